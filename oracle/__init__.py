@@ -1,0 +1,146 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP library and its Python binding
+never import it, and they share no code with it.
+
+``liboracle.so`` is built from ``oracle.c`` (plain C, fp64, OpenMP). It computes
+the textbook definition of attention, materialising S and P for every query row.
+The FlashAttention pages say the tiled online algorithm reproduces that
+definition exactly (mlapandio "FlashAttention: IO-aware exact attention",
+Definition and "Four ideas"). ``online.py`` is a separate fp64 model of the
+tiled recurrence in the pages' notation; the tests pin it to the definition.
+
+Every array here is numpy float64, contiguous [B, H, N, d]; LSE and D are
+[B, Hq, N].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH, build
+
+_f64p = ctypes.POINTER(ctypes.c_double)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_f64p)
+
+
+def _c64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+class Oracle:
+    """ctypes front end of one build of the oracle library.
+
+    ``lib_path`` defaults to the in-tree ``liboracle.so``; tests pass other builds
+    (for example deliberately broken ones) to check that the pins catch them."""
+
+    def __init__(self, lib_path: str | None = None):
+        path = lib_path or LIB_PATH
+        if lib_path is None and not os.path.exists(path):
+            build()
+        lib = ctypes.CDLL(path)
+        lib.oracle_attn_fwd.restype = ctypes.c_int
+        lib.oracle_attn_fwd.argtypes = [_f64p, _f64p, _f64p, _f64p, _f64p] + [ctypes.c_int] * 6 + [
+            _i64p, ctypes.c_int, ctypes.c_double]
+        lib.oracle_attn_probs.restype = ctypes.c_int
+        lib.oracle_attn_probs.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int] * 6 + [
+            _i64p, ctypes.c_int, ctypes.c_double]
+        lib.oracle_attn_bwd.restype = ctypes.c_int
+        lib.oracle_attn_bwd.argtypes = [_f64p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_double]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        self.lib = lib
+
+    @staticmethod
+    def _dims(q, k):
+        B, Hq, Nq, d = q.shape
+        Bk, Hkv, Nk, dk = k.shape
+        if Bk != B or dk != d:
+            raise ValueError("q and k disagree on batch or head dim")
+        return B, Hq, Hkv, Nq, Nk, d
+
+    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None):
+        """O [B,Hq,Nq,d] and LSE [B,Hq,Nq]. ``qpos`` (int64 [Nq]) places query
+        rows among the keys for the causal mask (default: row i is position i)."""
+        q, k, v = _c64(q), _c64(k), _c64(v)
+        B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
+        o = np.empty_like(q)
+        lse = np.empty((B, Hq, Nq), dtype=np.float64)
+        qp = None
+        if qpos is not None:
+            qpos = np.ascontiguousarray(qpos, dtype=np.int64)
+            if qpos.shape != (Nq,):
+                raise ValueError("qpos must have one entry per query row")
+            qp = qpos.ctypes.data_as(_i64p)
+        rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
+                                      Nk, d, qp, int(bool(causal)), float(scale))
+        if rc != 0:
+            raise ValueError("oracle_attn_fwd rejected its arguments")
+        return o, lse
+
+    def probs(self, q, k, causal: bool, scale: float, qpos=None):
+        """Full probability matrix P [B,Hq,Nq,Nk] (small sizes only)."""
+        q, k = _c64(q), _c64(k)
+        B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
+        p = np.empty((B, Hq, Nq, Nk), dtype=np.float64)
+        qp = None
+        if qpos is not None:
+            qpos = np.ascontiguousarray(qpos, dtype=np.int64)
+            qp = qpos.ctypes.data_as(_i64p)
+        rc = self.lib.oracle_attn_probs(_ptr(q), _ptr(k), _ptr(p), B, Hq, Hkv, Nq, Nk, d, qp,
+                                        int(bool(causal)), float(scale))
+        if rc != 0:
+            raise ValueError("oracle_attn_probs rejected its arguments")
+        return p
+
+    def bwd(self, q, k, v, do, causal: bool, scale: float):
+        """Gradients of sum(do * O): returns dict dq, dk, dv, o, lse, D."""
+        q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
+        B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
+        if Nq != Nk:
+            raise ValueError("backward needs queries and keys of one sequence")
+        if do.shape != q.shape:
+            raise ValueError("do must be shaped like q")
+        dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+        o = np.empty_like(q)
+        lse = np.empty((B, Hq, Nq), dtype=np.float64)
+        D = np.empty_like(lse)
+        rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
+                                      _ptr(dv), _ptr(o), _ptr(lse), _ptr(D), B, Hq, Hkv, Nq, d,
+                                      int(bool(causal)), float(scale))
+        if rc != 0:
+            raise ValueError("oracle_attn_bwd rejected its arguments")
+        return dict(dq=dq, dk=dk, dv=dv, o=o, lse=lse, D=D)
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def fwd(q, k, v, causal, scale, qpos=None):
+    return default().fwd(q, k, v, causal, scale, qpos)
+
+
+def bwd(q, k, v, do, causal, scale):
+    return default().bwd(q, k, v, do, causal, scale)
+
+
+def probs(q, k, causal, scale, qpos=None):
+    return default().probs(q, k, causal, scale, qpos)

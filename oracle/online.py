@@ -1,0 +1,65 @@
+"""fp64 model of the tiled online-softmax recurrence -- TEST INFRASTRUCTURE ONLY.
+
+This follows the "FLASH" half of the naive-vs-flash diagram on the mlapandio
+page "FlashAttention: IO-aware exact attention". For each block of query rows,
+the running output O, max m and sum l start at 0, -inf and 0. Each streamed
+key/value block then updates them:
+
+    m_new = max(m, rowmax(S_tile))
+    l     = e^(m - m_new) * l + rowsum(e^(S_tile - m_new))
+    O     = e^(m - m_new) * O + e^(S_tile - m_new) V_block
+    m     = m_new
+
+The diagram stops at "write O once" plus a logsumexp per row. It leaves the
+last step open. The reading used here is the only one under which the result
+equals the textbook softmax: O is divided by l, and LSE = m + ln l.
+
+``tau`` models a lazily updated reference max. The reference m moves only when
+a block's row max exceeds it by more than ``tau`` (natural-log units). The HIP
+forward kernel uses this variant. Any reference value cancels in O / l and in
+m + ln l, so the result is the same; the tests check that in fp64.
+
+The model is numpy fp64 with a numpy matmul as its product step. It serves
+only to pin the algorithm's order of steps against the definition.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def online_attention(q, k, v, causal: bool, scale: float, block_rows: int, block_cols: int,
+                     tau: float = 0.0):
+    """q [Nq, d], k/v [Nk, d] float64 for one head (queries at positions 0..Nq-1).
+    Returns O [Nq, d], LSE [Nq]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    Nq, d = q.shape
+    Nk = k.shape[0]
+    O_out = np.zeros((Nq, d))
+    L_out = np.zeros(Nq)
+    for r0 in range(0, Nq, block_rows):
+        rows = np.arange(r0, min(r0 + block_rows, Nq))
+        Qb = q[rows]
+        O = np.zeros((len(rows), d))
+        m = np.full(len(rows), -np.inf)
+        l = np.zeros(len(rows))
+        for c0 in range(0, Nk, block_cols):
+            cols = np.arange(c0, min(c0 + block_cols, Nk))
+            S = scale * (Qb @ k[cols].T)
+            if causal:
+                S = np.where(cols[None, :] <= rows[:, None], S, -np.inf)
+            rowmax = S.max(axis=1)
+            # lazy reference: move m only when the block max clears it by more than tau
+            move = (rowmax > m + tau) | np.isneginf(m)
+            m_new = np.where(move, np.maximum(m, rowmax), m)
+            # a row with no visible key so far keeps m = -inf; its terms are all zero
+            safe = np.where(np.isneginf(m_new), 0.0, m_new)
+            alpha = np.where(np.isneginf(m), 0.0, np.exp(m - safe))
+            E = np.exp(S - safe[:, None])
+            l = alpha * l + E.sum(axis=1)
+            O = alpha[:, None] * O + E @ v[cols]
+            m = m_new
+        O_out[rows] = O / l[:, None]
+        L_out[rows] = m + np.log(l)
+    return O_out, L_out

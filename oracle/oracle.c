@@ -1,0 +1,261 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for exact attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library. The HIP path never calls it, and the
+ * two share no code.
+ *
+ * What it computes: the textbook definition the FlashAttention pages say the
+ * tiled algorithm reproduces exactly. The mlapandio page "FlashAttention:
+ * IO-aware exact attention" (Definition; "Four ideas", online softmax item)
+ * says the result is exact and ends equal to the ordinary softmax. The
+ * wishwiki "FlashAttention" page ("The IO-Aware Insight") calls the outputs
+ * identical to standard attention. So this file does not use the online
+ * recurrence. For every query row it materialises the score row S and the
+ * probability row P in full, as the "NAIVE" half of the mlapandio naive-vs-flash
+ * diagram does, and takes the softmax in two passes (max, then sum).
+ *
+ *   scores   S_ij = s * sum_c q_ic k_jc            for visible keys j
+ *   softmax  m_i = max_j S_ij,  e_ij = exp(S_ij - m_i),  l_i = sum_j e_ij
+ *            P_ij = e_ij / l_i   (0 for masked keys)
+ *   output   O_i = sum_j P_ij v_j
+ *   LSE      L_i = m_i + ln l_i  (natural log of sum_j exp(S_ij))
+ *
+ * Key j is visible to query i when the mask is off, or when j <= pos_i under
+ * the causal mask. pos_i is the query's position among the keys (pos_i = i when
+ * queries and keys are the same sequence). Query head h reads key/value head
+ * h / (Hq / Hkv) (grouped-query attention, mlapandio "Two notes").
+ *
+ * Backward: the pages say only that the backward pass rebuilds P from the
+ * stored logsumexp (mlapandio "Four ideas", recomputation item; techtrendtracker
+ * "Recomputation in the Backward Pass"). The gradients below are the chain rule
+ * of the definition for the loss sum(dO * O):
+ *   D_i   = sum_c dO_ic O_ic
+ *   dP_ij = sum_c dO_ic v_jc
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = s sum_j dS_ij k_j
+ *   dK_j  = s sum_{heads in group} sum_i dS_ij q_i
+ *   dV_j  =   sum_{heads in group} sum_i P_ij dO_i
+ *
+ * Layout: every tensor is contiguous [B, H, N, d] float64 (d fastest);
+ * LSE and D are [B, Hq, N]. Functions return 0, or -1 on bad arguments or
+ * allocation failure.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static int thread_id(void) {
+#ifdef _OPENMP
+    return omp_get_thread_num();
+#else
+    return 0;
+#endif
+}
+
+static double dot(const double* a, const double* b, int d) {
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += a[c] * b[c];
+    return acc;
+}
+
+static int is_visible(int64_t pos_i, int j, int causal) {
+    return !causal || (int64_t)j <= pos_i;
+}
+
+/*
+ * One query row against one key/value head.
+ *   qi[d], kh[Nk*d], vh[Nk*d]  -> S[Nk], P[Nk] (scratch, filled), oi[d], *lse_i
+ * Returns the number of visible keys.
+ */
+static int attend_row(const double* qi, const double* kh, const double* vh, int Nk, int d,
+                      int64_t pos_i, int causal, double s, double* S, double* P, double* oi,
+                      double* lse_i) {
+    int visible = 0;
+    double m = -INFINITY;
+    for (int j = 0; j < Nk; ++j) {
+        if (is_visible(pos_i, j, causal)) {
+            S[j] = s * dot(qi, kh + (size_t)j * d, d);
+            if (S[j] > m) m = S[j];
+            ++visible;
+        } else {
+            S[j] = -INFINITY;
+        }
+    }
+    for (int c = 0; c < d; ++c) oi[c] = 0.0;
+    if (visible == 0) {          /* no visible key: empty sum */
+        for (int j = 0; j < Nk; ++j) P[j] = 0.0;
+        *lse_i = -INFINITY;
+        return 0;
+    }
+    double l = 0.0;
+    for (int j = 0; j < Nk; ++j) {
+        P[j] = is_visible(pos_i, j, causal) ? exp(S[j] - m) : 0.0;
+        l += P[j];
+    }
+    for (int j = 0; j < Nk; ++j) P[j] /= l;
+    for (int j = 0; j < Nk; ++j) {
+        if (P[j] == 0.0) continue;
+        const double* vj = vh + (size_t)j * d;
+        for (int c = 0; c < d; ++c) oi[c] += P[j] * vj[c];
+    }
+    *lse_i = m + log(l);
+    return visible;
+}
+
+static int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return -1;
+    if (Hq % Hkv != 0) return -1;
+    return 0;
+}
+
+/*
+ * Forward. q [B,Hq,Nq,d], k,v [B,Hkv,Nk,d] -> o [B,Hq,Nq,d], lse [B,Hq,Nq].
+ * qpos[Nq] gives each query row's position for the causal mask (NULL: row i
+ * is position i).
+ */
+int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int d, const int64_t* qpos,
+                    int causal, double scale) {
+    if (!q || !k || !v || !o || !lse || check_shape(B, Hq, Hkv, Nq, Nk, d)) return -1;
+    const int G = Hq / Hkv;
+    const int nt = max_threads();
+    double* scratch = (double*)malloc(sizeof(double) * 2 * (size_t)Nk * nt);
+    if (!scratch) return -1;
+    const int64_t rows = (int64_t)B * Hq * Nq;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int i = (int)(r % Nq);
+        const int h = (int)((r / Nq) % Hq);
+        const int b = (int)(r / ((int64_t)Nq * Hq));
+        const int hk = h / G;
+        const double* kh = k + ((size_t)b * Hkv + hk) * (size_t)Nk * d;
+        const double* vh = v + ((size_t)b * Hkv + hk) * (size_t)Nk * d;
+        double* S = scratch + (size_t)thread_id() * 2 * Nk;
+        double* P = S + Nk;
+        attend_row(q + (size_t)r * d, kh, vh, Nk, d, qpos ? qpos[i] : i, causal, scale, S, P,
+                   o + (size_t)r * d, lse + r);
+    }
+    free(scratch);
+    return 0;
+}
+
+/*
+ * Probability matrix, for checking invariants at small sizes:
+ * p [B,Hq,Nq,Nk] = softmax rows (0 on masked keys).
+ */
+int oracle_attn_probs(const double* q, const double* k, double* p, int B, int Hq, int Hkv, int Nq,
+                      int Nk, int d, const int64_t* qpos, int causal, double scale) {
+    if (!q || !k || !p || check_shape(B, Hq, Hkv, Nq, Nk, d)) return -1;
+    const int G = Hq / Hkv;
+    double* S = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    double* zeros = (double*)calloc((size_t)Nk * d, sizeof(double));
+    if (!S || !o || !zeros) { free(S); free(o); free(zeros); return -1; }
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < Hq; ++h)
+            for (int i = 0; i < Nq; ++i) {
+                const size_t r = ((size_t)b * Hq + h) * Nq + i;
+                const double* kh = k + ((size_t)b * Hkv + h / G) * (size_t)Nk * d;
+                double lse;
+                attend_row(q + r * d, kh, zeros, Nk, d, qpos ? qpos[i] : i, causal, scale, S,
+                           p + r * Nk, o, &lse);
+            }
+    free(S); free(o); free(zeros);
+    return 0;
+}
+
+/*
+ * Backward for the loss sum(dout * O), queries and keys the same sequence (N).
+ * Inputs q, dout [B,Hq,N,d]; k, v [B,Hkv,N,d].
+ * Outputs dq [B,Hq,N,d]; dk, dv [B,Hkv,N,d]; optional (may be NULL): o [B,Hq,N,d],
+ * lse and D [B,Hq,N].
+ * Rows are split over threads; each thread sums its dK/dV contributions in a
+ * private buffer, and the buffers are added in thread order afterwards.
+ */
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    double* dq, double* dk, double* dv, double* o_out, double* lse_out,
+                    double* D_out, int B, int Hq, int Hkv, int N, int d, int causal,
+                    double scale) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || check_shape(B, Hq, Hkv, N, N, d))
+        return -1;
+    const int G = Hq / Hkv;
+    const int nt = max_threads();
+    const size_t head = (size_t)N * d;
+    double* priv = (double*)calloc((size_t)nt * 2 * head, sizeof(double));
+    double* rowbuf = (double*)malloc(sizeof(double) * (size_t)nt * (3 * (size_t)N + d));
+    if (!priv || !rowbuf) { free(priv); free(rowbuf); return -1; }
+    int status = 0;
+    for (int b = 0; b < B; ++b) {
+        for (int hk = 0; hk < Hkv; ++hk) {
+            const double* kh = k + ((size_t)b * Hkv + hk) * head;
+            const double* vh = v + ((size_t)b * Hkv + hk) * head;
+            memset(priv, 0, sizeof(double) * (size_t)nt * 2 * head);
+            const int64_t rows = (int64_t)G * N;
+#pragma omp parallel for schedule(static)
+            for (int64_t r = 0; r < rows; ++r) {
+                const int g = (int)(r / N), i = (int)(r % N);
+                const int h = hk * G + g;
+                const size_t ri = (((size_t)b * Hq + h) * N + i);
+                const double* qi = q + ri * d;
+                const double* doi = dout + ri * d;
+                const int t = thread_id();
+                double* S = rowbuf + (size_t)t * (3 * (size_t)N + d);
+                double* P = S + N;
+                double* dS = P + N;
+                double* oi = dS + N;
+                double* dk_t = priv + (size_t)t * 2 * head;
+                double* dv_t = dk_t + head;
+                double lse_i;
+                attend_row(qi, kh, vh, N, d, i, causal, scale, S, P, oi, &lse_i);
+                const double Di = dot(doi, oi, d);
+                if (o_out) memcpy(o_out + ri * d, oi, sizeof(double) * d);
+                if (lse_out) lse_out[ri] = lse_i;
+                if (D_out) D_out[ri] = Di;
+                for (int j = 0; j < N; ++j) {
+                    if (!is_visible(i, j, causal)) { dS[j] = 0.0; continue; }
+                    const double dPij = dot(doi, vh + (size_t)j * d, d);
+                    dS[j] = P[j] * (dPij - Di);
+                }
+                double* dqi = dq + ri * d;
+                for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+                for (int j = 0; j < N; ++j) {
+                    if (!is_visible(i, j, causal)) continue;
+                    const double* kj = kh + (size_t)j * d;
+                    double* dkj = dk_t + (size_t)j * d;
+                    double* dvj = dv_t + (size_t)j * d;
+                    for (int c = 0; c < d; ++c) {
+                        dqi[c] += scale * dS[j] * kj[c];
+                        dkj[c] += scale * dS[j] * qi[c];
+                        dvj[c] += P[j] * doi[c];
+                    }
+                }
+            }
+            double* dkh = dk + ((size_t)b * Hkv + hk) * head;
+            double* dvh = dv + ((size_t)b * Hkv + hk) * head;
+            for (size_t e = 0; e < head; ++e) { dkh[e] = 0.0; dvh[e] = 0.0; }
+            for (int t = 0; t < nt; ++t) {
+                const double* dk_t = priv + (size_t)t * 2 * head;
+                const double* dv_t = dk_t + head;
+                for (size_t e = 0; e < head; ++e) { dkh[e] += dk_t[e]; dvh[e] += dv_t[e]; }
+            }
+        }
+    }
+    free(priv);
+    free(rowbuf);
+    return status;
+}
+
+int oracle_num_threads(void) { return max_threads(); }

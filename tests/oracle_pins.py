@@ -1,0 +1,368 @@
+"""Pins for the fp64 oracle: checks against facts other than the oracle itself.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees with a closed form, a hand formula, an invariant, an independent
+library implementation, finite differences, or high-precision arithmetic.
+``tests/test_oracle_pins.py`` runs them on the in-tree oracle, and
+``tests/test_oracle_mutants.py`` runs them on deliberately broken oracle builds.
+A mistake planted anywhere in the oracle should trip at least one pin.
+
+Sources of the facts: the FlashAttention pages say the method computes exact
+softmax attention (mlapandio "FlashAttention: IO-aware exact attention",
+Definition and "Four ideas"; wishwiki "FlashAttention", "The IO-Aware
+Insight"). Everything else follows from the algebra of that definition.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand(shape, seed, scale=1.0):
+    return _rng(seed).standard_normal(shape) * scale
+
+
+def _close(a, b, tol=TOL, what=""):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+
+
+# ------------------------------------------------------------------ tiny hand cases
+def pin_one_token(orc):
+    """N = 1: the only key has probability 1, so O = v, LSE = s q.k, dV = dO, dQ = dK = 0."""
+    d = 5
+    q, k, v, do = (_rand((1, 1, 1, d), s) for s in (1, 2, 3, 4))
+    s = 0.37
+    for causal in (False, True):
+        o, lse = orc.fwd(q, k, v, causal, s)
+        _close(o, v, what="N=1 O")
+        _close(lse[0, 0, 0], s * float(q[0, 0, 0] @ k[0, 0, 0]), what="N=1 LSE")
+        g = orc.bwd(q, k, v, do, causal, s)
+        _close(g["dv"], do, what="N=1 dV")
+        _close(g["dq"], 0 * q, what="N=1 dQ")
+        _close(g["dk"], 0 * k, what="N=1 dK")
+
+
+def pin_two_tokens(orc):
+    """N = 2, by the logistic form of a two-way softmax: p = sigmoid(S_0 - S_1).
+
+    O_i = p v_0 + (1 - p) v_1, LSE_i = max + log1p(exp(-|S_0 - S_1|)),
+    dS_i0 = p (1 - p) dO_i.(v_0 - v_1) = -dS_i1, dQ_i = s dS_i0 (k_0 - k_1),
+    dK_1 = -dK_0, dV_0 = sum_i p_i dO_i, dV_1 = sum_i (1 - p_i) dO_i.
+    Causal: row 0 sees only key 0."""
+    d = 3
+    q, k, v, do = (_rand((1, 1, 2, d), s) for s in (11, 12, 13, 14))
+    s = 0.8
+    qq, kk, vv, dd = q[0, 0], k[0, 0], v[0, 0], do[0, 0]
+    for causal in (False, True):
+        o, lse = orc.fwd(q, k, v, causal, s)
+        g = orc.bwd(q, k, v, do, causal, s)
+        dq_ref = np.zeros((2, d))
+        dk_ref = np.zeros((2, d))
+        dv_ref = np.zeros((2, d))
+        for i in range(2):
+            S0, S1 = s * (qq[i] @ kk[0]), s * (qq[i] @ kk[1])
+            if causal and i == 0:
+                _close(o[0, 0, 0], vv[0], what="N=2 causal row 0 O")
+                _close(lse[0, 0, 0], S0, what="N=2 causal row 0 LSE")
+                dv_ref[0] += dd[0]
+                continue
+            p = 1.0 / (1.0 + math.exp(-(S0 - S1)))
+            _close(o[0, 0, i], p * vv[0] + (1 - p) * vv[1], what=f"N=2 O row {i}")
+            _close(lse[0, 0, i], max(S0, S1) + math.log1p(math.exp(-abs(S0 - S1))),
+                   what=f"N=2 LSE row {i}")
+            dS0 = p * (1 - p) * (dd[i] @ (vv[0] - vv[1]))
+            dq_ref[i] = s * dS0 * (kk[0] - kk[1])
+            dk_ref[0] += s * dS0 * qq[i]
+            dk_ref[1] -= s * dS0 * qq[i]
+            dv_ref[0] += p * dd[i]
+            dv_ref[1] += (1 - p) * dd[i]
+        _close(g["dq"][0, 0], dq_ref, what="N=2 dQ")
+        _close(g["dk"][0, 0], dk_ref, what="N=2 dK")
+        _close(g["dv"][0, 0], dv_ref, what="N=2 dV")
+
+
+def pin_three_four_tokens_mp(orc):
+    """N = 3 and 4 with explicit exp sums in 50-digit arithmetic (mpmath), using
+    the ratio form O_i = sum_j v_j / sum_k exp(S_ik - S_ij)."""
+    import mpmath as mp
+    mp.mp.dps = 50
+    for N in (3, 4):
+        d = 3
+        q, k, v = (_rand((1, 1, N, d), 20 + N * 3 + t) for t in range(3))
+        s = 0.9
+        for causal in (False, True):
+            o, lse = orc.fwd(q, k, v, causal, s)
+            for i in range(N):
+                vis = [j for j in range(N) if (not causal or j <= i)]
+                S = {j: mp.mpf(s) * mp.fsum(mp.mpf(q[0, 0, i, c]) * mp.mpf(k[0, 0, j, c]) for c in range(d))
+                     for j in vis}
+                for c in range(d):
+                    ref = mp.fsum(mp.mpf(v[0, 0, j, c]) / mp.fsum(mp.exp(S[kk] - S[j]) for kk in vis) for j in vis)
+                    _close(o[0, 0, i, c], float(ref), what=f"N={N} O[{i},{c}]")
+                _close(lse[0, 0, i], float(mp.log(mp.fsum(mp.exp(S[j]) for j in vis))), what=f"N={N} LSE[{i}]")
+
+
+# ------------------------------------------------------------------ closed forms / invariants
+def pin_constant_v(orc):
+    """All v_j equal to one vector v: O_i = v for every row; in the backward
+    dQ = dK = 0 and dV_j = sum_i P_ij dO_i."""
+    B, H, N, d = 1, 2, 9, 4
+    q, k, do = _rand((B, H, N, d), 31), _rand((B, H, N, d), 32), _rand((B, H, N, d), 34)
+    vrow = _rand((d,), 33)
+    v = np.broadcast_to(vrow, (B, H, N, d)).copy()
+    for causal in (False, True):
+        o, _ = orc.fwd(q, k, v, causal, 0.6)
+        _close(o, np.broadcast_to(vrow, o.shape), what="constant V O")
+        g = orc.bwd(q, k, v, do, causal, 0.6)
+        _close(g["dq"], 0 * q, tol=1e-11, what="constant V dQ")
+        _close(g["dk"], 0 * k, tol=1e-11, what="constant V dK")
+        P = orc.probs(q, k, causal, 0.6)
+        _close(g["dv"], np.einsum("bhij,bhid->bhjd", P, do), what="constant V dV")
+
+
+def pin_causal_row_zero(orc):
+    """Causal row 0 sees key 0 only: O_0 = v_0, LSE_0 = s q_0.k_0, dQ_0 = 0."""
+    B, H, N, d = 2, 2, 7, 6
+    q, k, v, do = (_rand((B, H, N, d), 40 + t) for t in range(4))
+    s = 0.45
+    o, lse = orc.fwd(q, k, v, True, s)
+    _close(o[:, :, 0], v[:, :, 0], what="causal row 0 O")
+    _close(lse[:, :, 0], s * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]), what="causal row 0 LSE")
+    g = orc.bwd(q, k, v, do, True, s)
+    _close(g["dq"][:, :, 0], 0 * q[:, :, 0], what="causal row 0 dQ")
+
+
+def pin_uniform_scale_zero(orc):
+    """scale = 0 makes every visible key equally likely: non-causal O_i = mean_j v_j
+    and LSE_i = ln N; causal O_i = prefix mean over j <= i and LSE_i = ln(i+1)."""
+    B, H, N, d = 1, 2, 11, 4
+    q, k, v = (_rand((B, H, N, d), 50 + t) for t in range(3))
+    o, lse = orc.fwd(q, k, v, False, 0.0)
+    _close(o, np.broadcast_to(v.mean(axis=2, keepdims=True), o.shape), what="uniform O")
+    _close(lse, np.full(lse.shape, math.log(N)), what="uniform LSE")
+    o, lse = orc.fwd(q, k, v, True, 0.0)
+    counts = np.arange(1, N + 1, dtype=np.float64)
+    _close(o, np.cumsum(v, axis=2) / counts[None, None, :, None], what="prefix-mean O")
+    _close(lse, np.broadcast_to(np.log(counts), lse.shape), what="prefix-mean LSE")
+
+
+def pin_probability_rows(orc):
+    """Rows of P are a probability distribution over the visible keys: entries
+    >= 0, exactly 0 on masked keys, summing to 1. O is P times V."""
+    B, H, N, d = 1, 3, 12, 5
+    q, k, v = (_rand((B, H, N, d), 60 + t, 1.5) for t in range(3))
+    for causal in (False, True):
+        P = orc.probs(q, k, causal, 0.7)
+        assert np.all(P >= 0), "negative probability"
+        _close(P.sum(axis=-1), np.ones((B, H, N)), what="P row sums")
+        if causal:
+            assert np.all(P[..., np.triu_indices(N, 1)[0], np.triu_indices(N, 1)[1]] == 0), "masked P != 0"
+        o, _ = orc.fwd(q, k, v, causal, 0.7)
+        _close(o, P @ v, what="O = P V")
+
+
+def pin_key_translation(orc):
+    """Adding one vector c to every key leaves O unchanged and shifts LSE_i by s q_i.c."""
+    B, H, N, d = 1, 2, 10, 4
+    q, k, v = (_rand((B, H, N, d), 70 + t) for t in range(3))
+    c = _rand((d,), 74)
+    s = 0.5
+    for causal in (False, True):
+        o1, l1 = orc.fwd(q, k, v, causal, s)
+        o2, l2 = orc.fwd(q, k + c, v, causal, s)
+        _close(o2, o1, tol=1e-11, what="translation O")
+        _close(l2 - l1, s * (q @ c), tol=1e-11, what="translation LSE")
+
+
+def pin_gqa_equals_repeated_mha(orc):
+    """Grouped-query attention equals multi-head attention with each K/V head
+    repeated G times in order; dK/dV are the group sums of the repeated-head ones."""
+    B, Hq, Hkv, N, d = 2, 6, 2, 8, 4
+    G = Hq // Hkv
+    q, do = _rand((B, Hq, N, d), 80), _rand((B, Hq, N, d), 83)
+    k, v = _rand((B, Hkv, N, d), 81), _rand((B, Hkv, N, d), 82)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    for causal in (False, True):
+        o1, l1 = orc.fwd(q, k, v, causal, 0.5)
+        o2, l2 = orc.fwd(q, kr, vr, causal, 0.5)
+        _close(o1, o2, what="GQA O")
+        _close(l1, l2, what="GQA LSE")
+        g1 = orc.bwd(q, k, v, do, causal, 0.5)
+        g2 = orc.bwd(q, kr, vr, do, causal, 0.5)
+        _close(g1["dq"], g2["dq"], what="GQA dQ")
+        _close(g1["dk"], g2["dk"].reshape(B, Hkv, G, N, d).sum(2), what="GQA dK")
+        _close(g1["dv"], g2["dv"].reshape(B, Hkv, G, N, d).sum(2), what="GQA dV")
+
+
+def pin_head_permutation(orc):
+    """Heads and batch entries are independent: permuting them permutes the outputs."""
+    B, H, N, d = 2, 3, 6, 4
+    q, k, v, do = (_rand((B, H, N, d), 90 + t) for t in range(4))
+    perm_b, perm_h = [1, 0], [2, 0, 1]
+
+    def p(x):
+        return x[perm_b][:, perm_h]
+
+    o1, l1 = orc.fwd(q, k, v, True, 0.4)
+    o2, l2 = orc.fwd(p(q), p(k), p(v), True, 0.4)
+    _close(o2, p(o1), what="permuted O")
+    _close(l2, p(l1), what="permuted LSE")
+    g1 = orc.bwd(q, k, v, do, True, 0.4)
+    g2 = orc.bwd(p(q), p(k), p(v), p(do), True, 0.4)
+    for key in ("dq", "dk", "dv"):
+        _close(g2[key], p(g1[key]), what=f"permuted {key}")
+
+
+def pin_last_row_and_positions(orc):
+    """The causal last row sees every key, so it equals the non-causal last row.
+    Query rows given with explicit positions give the same rows as the full run."""
+    B, H, N, d = 1, 2, 13, 4
+    q, k, v = (_rand((B, H, N, d), 100 + t) for t in range(3))
+    oc, lc = orc.fwd(q, k, v, True, 0.6)
+    on, ln = orc.fwd(q, k, v, False, 0.6)
+    _close(oc[:, :, -1], on[:, :, -1], what="last row O")
+    _close(lc[:, :, -1], ln[:, :, -1], what="last row LSE")
+    rows = np.array([0, 4, 12], dtype=np.int64)
+    os_, ls_ = orc.fwd(q[:, :, rows], k, v, True, 0.6, qpos=rows)
+    _close(os_, oc[:, :, rows], what="row-subset O")
+    _close(ls_, lc[:, :, rows], what="row-subset LSE")
+
+
+def pin_gradient_sums(orc):
+    """Each row of dS sums to 0, so sum_j dK_j = 0 per KV head; rows of P sum to 1,
+    so sum_j dV_j = sum over the group's heads and rows of dO."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 10, 5
+    q, do = _rand((B, Hq, N, d), 110), _rand((B, Hq, N, d), 113)
+    k, v = _rand((B, Hkv, N, d), 111), _rand((B, Hkv, N, d), 112)
+    for causal in (False, True):
+        g = orc.bwd(q, k, v, do, causal, 0.7)
+        _close(g["dk"].sum(axis=2), np.zeros((B, Hkv, d)), tol=1e-11, what="sum dK")
+        _close(g["dv"].sum(axis=2), do.reshape(B, Hkv, Hq // Hkv, N, d).sum(axis=(2, 3)), tol=1e-11,
+               what="sum dV")
+
+
+def pin_large_logits(orc):
+    """Scores near +-700 (exp would overflow fp64 without a max shift): O and
+    LSE must match 50-digit arithmetic."""
+    import mpmath as mp
+    mp.mp.dps = 50
+    N, d = 6, 2
+    q = np.array([[30.0, -20.0]] * N)[None, None]
+    k = _rand((1, 1, N, d), 120) * 25.0
+    v = _rand((1, 1, N, d), 121)
+    s = 1.0
+    o, lse = orc.fwd(q, k, v, False, s)
+    for i in range(N):
+        S = [mp.mpf(s) * (mp.mpf(q[0, 0, i, 0]) * mp.mpf(k[0, 0, j, 0]) + mp.mpf(q[0, 0, i, 1]) * mp.mpf(k[0, 0, j, 1]))
+             for j in range(N)]
+        Z = mp.fsum(mp.exp(x) for x in S)
+        _close(lse[0, 0, i], float(mp.log(Z)), tol=1e-9, what="large-logit LSE")
+        for c in range(d):
+            _close(o[0, 0, i, c], float(mp.fsum(mp.exp(S[j]) * mp.mpf(v[0, 0, j, c]) for j in range(N)) / Z),
+                   what="large-logit O")
+
+
+# ------------------------------------------------------------------ independent implementations
+def pin_torch_sdpa(orc):
+    """torch's own fp64 CPU attention (its math path) and autograd agree with the
+    oracle on O and on the gradients of sum(dO * O); LSE against torch.logsumexp."""
+    import torch
+    torch.manual_seed(0)
+    B, Hq, Hkv, N, d = 2, 4, 2, 17, 8
+    G = Hq // Hkv
+    q, do = _rand((B, Hq, N, d), 130), _rand((B, Hq, N, d), 133)
+    k, v = _rand((B, Hkv, N, d), 131), _rand((B, Hkv, N, d), 132)
+    s = 1.0 / math.sqrt(d)
+    for causal in (False, True):
+        tq = torch.tensor(q, requires_grad=True)
+        tk = torch.tensor(k, requires_grad=True)
+        tv = torch.tensor(v, requires_grad=True)
+        to = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1), is_causal=causal, scale=s)
+        (to * torch.tensor(do)).sum().backward()
+        o, lse = orc.fwd(q, k, v, causal, s)
+        _close(o, to.detach().numpy(), tol=1e-12, what="SDPA O")
+        g = orc.bwd(q, k, v, do, causal, s)
+        _close(g["dq"], tq.grad.numpy(), tol=1e-11, what="autograd dQ")
+        _close(g["dk"], tk.grad.numpy(), tol=1e-11, what="autograd dK")
+        _close(g["dv"], tv.grad.numpy(), tol=1e-11, what="autograd dV")
+        scores = torch.tensor(q) @ torch.tensor(k).repeat_interleave(G, 1).transpose(-1, -2) * s
+        if causal:
+            scores = scores.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+        _close(lse, torch.logsumexp(scores, -1).numpy(), what="logsumexp LSE")
+
+
+def pin_finite_differences(orc):
+    """Central differences of the loss sum(dO * O(Q, K, V)) match the analytic
+    gradients (N <= 6, d <= 3, both masks, groups of 1 and 2 heads)."""
+    h = 1e-6
+    for (Hq, Hkv, causal) in ((1, 1, False), (2, 1, True), (2, 2, True), (2, 1, False)):
+        B, N, d = 1, 5, 3
+        q, do = _rand((B, Hq, N, d), 140 + Hq), _rand((B, Hq, N, d), 143)
+        k, v = _rand((B, Hkv, N, d), 141 + Hkv), _rand((B, Hkv, N, d), 142)
+        s = 0.7
+        g = orc.bwd(q, k, v, do, causal, s)
+
+        def loss(q_, k_, v_):
+            o, _ = orc.fwd(q_, k_, v_, causal, s)
+            return float((o * do).sum())
+
+        for name, arr in (("dq", q), ("dk", k), ("dv", v)):
+            num = np.zeros_like(arr)
+            it = np.nditer(arr, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                plus, minus = arr.copy(), arr.copy()
+                plus[idx] += h
+                minus[idx] -= h
+                args_p = {"dq": (plus, k, v), "dk": (q, plus, v), "dv": (q, k, plus)}[name]
+                args_m = {"dq": (minus, k, v), "dk": (q, minus, v), "dv": (q, k, minus)}[name]
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            _close(g[name], num, tol=1e-7, what=f"finite-difference {name} (Hq={Hq},Hkv={Hkv},causal={causal})")
+
+
+def pin_online_recurrence(orc):
+    """The tiled online recurrence in fp64 (any block sizes, ragged edges, lazy
+    reference max) reproduces the oracle's definition."""
+    from oracle.online import online_attention
+    N, d = 37, 6
+    q, k, v = (_rand((1, 1, N, d), 150 + t, 1.5) for t in range(3))
+    k[0, 0, 5] *= 4.0
+    for causal in (False, True):
+        o, lse = orc.fwd(q, k, v, causal, 0.6)
+        for br, bc, tau in ((1, 1, 0.0), (3, 5, 0.0), (16, 16, 0.0), (7, 64, 0.0), (8, 4, 8 * math.log(2)),
+                            (5, 3, 2.0)):
+            om, lm = online_attention(q[0, 0], k[0, 0], v[0, 0], causal, 0.6, br, bc, tau)
+            _close(om, o[0, 0], what=f"online O ({br}x{bc}, tau={tau:.2f})")
+            _close(lm, lse[0, 0], what=f"online LSE ({br}x{bc}, tau={tau:.2f})")
+
+
+PINS = [
+    pin_one_token,
+    pin_two_tokens,
+    pin_three_four_tokens_mp,
+    pin_constant_v,
+    pin_causal_row_zero,
+    pin_uniform_scale_zero,
+    pin_probability_rows,
+    pin_key_translation,
+    pin_gqa_equals_repeated_mha,
+    pin_head_permutation,
+    pin_last_row_and_positions,
+    pin_gradient_sums,
+    pin_large_logits,
+    pin_torch_sdpa,
+    pin_finite_differences,
+    pin_online_recurrence,
+]

@@ -1,0 +1,64 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pins catch every one of them.
+
+Each mutant replaces one snippet of ``oracle/oracle.c``; the snippet must occur
+exactly once, so an edit to the oracle that removes it fails loudly here rather
+than silently weakening the check. The mutated source is compiled into a
+temporary directory; the in-tree oracle is never touched.
+"""
+import os
+import tempfile
+
+import pytest
+
+from oracle import Oracle
+from oracle.build import SRC, compile_oracle
+from tests.oracle_pins import PINS
+
+MUTANTS = {
+    "score scale dropped": ("S[j] = s * dot(qi, kh", "S[j] = dot(qi, kh"),
+    "causal mask off by one": ("(int64_t)j <= pos_i", "(int64_t)j < pos_i"),
+    "causal mask flipped": ("(int64_t)j <= pos_i", "(int64_t)j >= pos_i"),
+    "max shift dropped": ("exp(S[j] - m)", "exp(S[j])"),
+    "no normalisation": ("for (int j = 0; j < Nk; ++j) P[j] /= l;", ""),
+    "O uses K for V": ("const double* vj = vh + (size_t)j * d;", "const double* vj = kh + (size_t)j * d;"),
+    "LSE in log2": ("*lse_i = m + log(l);", "*lse_i = m + log2(l);"),
+    "LSE drops max": ("*lse_i = m + log(l);", "*lse_i = log(l);"),
+    "fwd GQA map modulo": ("const int hk = h / G;\n        const double* kh", "const int hk = h % Hkv;\n        const double* kh"),
+    "fwd row position ignored": ("qpos ? qpos[i] : i, causal, scale, S, P,", "qpos ? qpos[i] : 0, causal, scale, S, P,"),
+    "D uses dO.dO": ("const double Di = dot(doi, oi, d);", "const double Di = dot(doi, doi, d);"),
+    "D term dropped": ("dS[j] = P[j] * (dPij - Di);", "dS[j] = P[j] * dPij;"),
+    "dS sign flipped": ("dS[j] = P[j] * (dPij - Di);", "dS[j] = P[j] * (Di - dPij);"),
+    "dP uses K": ("const double dPij = dot(doi, vh + (size_t)j * d, d);", "const double dPij = dot(doi, kh + (size_t)j * d, d);"),
+    "dQ uses Q": ("dqi[c] += scale * dS[j] * kj[c];", "dqi[c] += scale * dS[j] * qi[c];"),
+    "dK scale dropped": ("dkj[c] += scale * dS[j] * qi[c];", "dkj[c] += dS[j] * qi[c];"),
+    "dV uses dS": ("dvj[c] += P[j] * doi[c];", "dvj[c] += dS[j] * doi[c];"),
+    "bwd KV head ignored": ("const double* kh = k + ((size_t)b * Hkv + hk) * head;", "const double* kh = k + ((size_t)b * Hkv) * head;"),
+    "bwd head in group wrong": ("const int h = hk * G + g;", "const int h = hk + g * Hkv;"),
+    "bwd reduction drops a thread": ("for (int t = 0; t < nt; ++t) {\n                const double* dk_t", "for (int t = 1; t < nt; ++t) {\n                const double* dk_t"),
+}
+
+
+def _pins_fail(orc):
+    failed = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError, FloatingPointError) as e:
+            failed.append((pin.__name__, str(e).splitlines()[0][:120]))
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for '{name}' not found exactly once"
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "oracle_mutant.c")
+        with open(path, "w") as f:
+            f.write(src.replace(old, new))
+        lib = os.path.join(tmp, "liboracle_mutant.so")
+        compile_oracle(path, lib)
+        failed = _pins_fail(Oracle(lib))
+    assert failed, f"no pin caught the planted mistake '{name}'"
