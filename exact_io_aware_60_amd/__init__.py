@@ -1,0 +1,149 @@
+"""Exact attention on AMD MI355X: Python binding of ``libflashattn.so``.
+
+This module only marshals arguments. torch provides device memory and the
+current stream; every step of the computation runs in the library's HIP
+kernels. If the library is missing, ``lib()`` raises: there is no other
+implementation to fall back to.
+
+    o, lse = fwd(q, k, v, causal=True)                  # q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+
+The entry points mirror ``include/flash_attn.h`` one to one.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflashattn.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCALE = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+
+EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
+            "flash_attn_version")
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"flash_attn status {status}: {text}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with exact_io_aware_60_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.flash_attn_fwd.restype = _i
+        L.flash_attn_fwd.argtypes = [_vp] * 5 + [_i] * 6 + [ctypes.c_float, _vp]
+        L.flash_attn_bwd.restype = _i
+        L.flash_attn_bwd.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
+        L.flash_attn_bwd_workspace_size.argtypes = [_i] * 6
+        L.flash_attn_strerror.restype = ctypes.c_char_p
+        L.flash_attn_strerror.argtypes = [_i]
+        L.flash_attn_version.restype = ctypes.c_char_p
+        L.flash_attn_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().flash_attn_strerror(int(status)).decode()
+
+
+def version() -> str:
+    return lib().flash_attn_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        raise FlashAttnError(status, strerror(status))
+
+
+# ------------------------------------------------------------------ raw C entry points
+def fwd_raw(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream=None) -> int:
+    """flash_attn_fwd on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale), stream)
+
+
+def bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace, workspace_bytes,
+            stream=None) -> int:
+    """flash_attn_bwd on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), float(scale),
+                                workspace, workspace_bytes, stream)
+
+
+def bwd_workspace_size(B, Hq, Hkv, N, d, causal) -> int:
+    return int(lib().flash_attn_bwd_workspace_size(B, Hq, Hkv, N, d, int(causal)))
+
+
+# ------------------------------------------------------------------ torch front end
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d):
+        raise ValueError("q and k/v must agree on B, N and d")
+    return B, Hq, Hkv, N, d
+
+
+def _checked(t, name):
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 tensor on the GPU")
+    return t
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None):
+    """Forward pass. Returns (o bf16 [B,Hq,N,d], lse fp32 [B,Hq,N])."""
+    import torch
+    B, Hq, Hkv, N, d = _dims(q, k)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _checked(t, name)
+    if v.shape != k.shape:
+        raise ValueError("v must be shaped like k")
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                   causal, scale, _stream(q)))
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, workspace=None):
+    """Backward pass for the loss sum(do * O). Returns (dq, dk, dv), bf16."""
+    import torch
+    B, Hq, Hkv, N, d = _dims(q, k)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _checked(t, name)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be contiguous float32 [B, Hq, N]")
+    scale = default_scale(d) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bwd_workspace_size(B, Hq, Hkv, N, d, causal)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    _check(bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, causal, scale,
+                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv

@@ -1,0 +1,141 @@
+// fa_api.cpp -- the C ABI: argument validation, launch parameters, status codes.
+//
+// Every entry point checks its arguments before any HIP call, so an invalid
+// call enqueues nothing; the checks need no GPU. Kernels are enqueued on the
+// caller's stream; nothing here allocates, frees or synchronises.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/flash_attn.h"
+#include "fa_params.h"
+
+namespace {
+
+thread_local char g_hip_text[256] = "";
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int Hq, int Hkv, int N, int d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    // element counts and the largest launch grid must fit the kernels' index types
+    const long double elems = (long double)B * Hq * N * d;
+    if (elems >= 4.0e18L) return FA_ERR_SHAPE;
+    const long double grid = (long double)B * Hq * ((N + 63) / 64);
+    if (grid >= 2147483647.0L) return FA_ERR_SHAPE;
+    if ((long double)N * d >= 2147483647.0L) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+int check_scale(float scale) {
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+    return FA_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return FA_OK;
+    std::snprintf(g_hip_text, sizeof(g_hip_text), "HIP launch failed: %s", hipGetErrorString(e));
+    return FA_ERR_HIP;
+}
+
+void log_config(const char* pass, int B, int Hq, int Hkv, int N, int d, int causal) {
+    static const bool enabled = [] {
+        const char* e = std::getenv("FLASH_ATTN_LOG");
+        return e && e[0] == '1';
+    }();
+    if (!enabled) return;
+    const fa::Geometry g = fa::fwd_geometry(B, Hq, N, d, causal);
+    std::fprintf(stderr,
+                 "[flash_attn] %s B=%d Hq=%d Hkv=%d N=%d d=%d causal=%d: block_m=%d block_n=%d "
+                 "threads=%d grid=%d lds=%dB\n",
+                 pass, B, Hq, Hkv, N, d, causal, g.block_m, g.block_n, g.threads, g.grid, g.lds_bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                   int Hkv, int N, int d, int causal, float scale, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    int st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_ALIGN;
+    log_config("fwd", B, Hq, Hkv, N, d, causal);
+    fa::FwdParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d; p.G = Hq / Hkv;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal) {
+    (void)causal;
+    if (check_shape(B, Hq, Hkv, N, d) != FA_OK) return 0;
+    const size_t bytes = sizeof(float) * (size_t)B * Hq * N;
+    return (bytes + 255) & ~(size_t)255;
+}
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                   int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    int st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+        return FA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < flash_attn_bwd_workspace_size(B, Hq, Hkv, N, d, causal))
+        return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    log_config("bwd", B, Hq, Hkv, N, d, causal);
+    fa::BwdParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<const uint16_t*>(o);
+    p.lse = lse;
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.dq = static_cast<uint16_t*>(dq);
+    p.dk = static_cast<uint16_t*>(dk);
+    p.dv = static_cast<uint16_t*>(dv);
+    p.delta = static_cast<float*>(workspace);
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d; p.G = Hq / Hkv;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
+const char* flash_attn_strerror(int status) {
+    switch (status) {
+        case FA_OK: return "success";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "unsupported shape: B, Hq, Hkv, N must be >= 1, Hq % Hkv == 0, sizes in range";
+        case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
+        case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case FA_ERR_WORKSPACE: return "backward workspace is NULL or too small";
+        case FA_ERR_HIP: return g_hip_text[0] ? g_hip_text : "HIP launch failed";
+        case FA_ERR_SCALE: return "scale must be finite and >= 0";
+        default: return "unknown status";
+    }
+}
+
+const char* flash_attn_version(void) { return "0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// fa_device.h -- device-side building blocks for the gfx950 attention kernels.
+//
+// MFMA operand layouts (v_mfma_f32_32x32x16_bf16, checked on gfx950):
+//   A (32 x 16): lane l holds row l % 32, k = (l / 32) * 8 + s for slot s = 0..7
+//   B (16 x 32): lane l holds col l % 32, k = (l / 32) * 8 + s
+//   C (32 x 32): lane l holds col l % 32, rows (i / 4) * 8 + (l / 32) * 4 + (i % 4), i = 0..15
+// The k order inside one MFMA is free as long as A and B agree, and the kernels
+// use that freedom. They feed the fp32 accumulator rows of one product, in
+// register order, straight into the k slots of the next product. The other
+// operand is then read in the same permuted key order.
+//
+// LDS transpose read (ds_read_b64_tr_b16, checked on gfx950): in each 16-lane
+// group, lane i supplies the address of 4 consecutive bf16 values, namely
+// row (i % 16) / 4 and columns 4 * (i % 4) .. +3 of a 4 x 16 block. Lane j then
+// receives column j % 16 of that block, rows 0..3. This turns a row-major
+// [key][d] tile into an operand that holds consecutive keys at a fixed d.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// 16-byte LDS read / write at an element (bf16) offset into an LDS array.
+__device__ __forceinline__ u32x4 lds_read16(const FA_LDS uint16_t* base, int elem) {
+    return *reinterpret_cast<const FA_LDS u32x4*>(base + elem);
+}
+__device__ __forceinline__ void lds_write16(FA_LDS uint16_t* base, int elem, const u32x4& v) {
+    *reinterpret_cast<FA_LDS u32x4*>(base + elem) = v;
+}
+// Transposed 8-byte LDS read (see the header comment).
+__device__ __forceinline__ u32x2 lds_read_tr(const FA_LDS uint16_t* base, int elem) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<FA_LDS s16x4*>(const_cast<FA_LDS uint16_t*>(base + elem)));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) {
+    u32x4 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
+    return r;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
+// The data of lane i lands at lds_wave_base + 16 * i bytes; lds_wave_base must
+// be the same for the whole wave. Completion is tracked by vmcnt: wait with
+// wait_vmem() and then a barrier before another wave reads the bytes.
+__device__ __forceinline__ void gload_lds16(const uint16_t* g, FA_LDS uint16_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
+                                     (FA_LDS void*)(lds_wave_base), 16, 0, 0);
+}
+// s_waitcnt vmcnt(0): all of this wave's vector-memory loads have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Inverse of swz(): the (row, logical chunk) stored at 16-byte slot `slot` of a tile.
+template <int D, int MODE>
+__device__ __forceinline__ void unswz(int slot, int& row, int& c);
+
+// Global 16-byte load; returns zeros when !valid (ragged tails).
+__device__ __forceinline__ u32x4 gload16(const uint16_t* p, bool valid) {
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (valid) r = *reinterpret_cast<const u32x4*>(p);
+    return r;
+}
+
+// Exchange with the lane 32 apart: returns the value held by lane l ^ 32.
+__device__ __forceinline__ float swap_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    // lanes 0..31 find the partner's value in r[1], lanes 32..63 in r[0]
+    return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even float -> bf16 pair packed into one dword (lo in bits 0..15).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const f32x2v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));  // v_cvt_pk_bf16_f32
+}
+
+// Swizzled position of 16-byte chunk `c` of row `row` in an LDS tile of
+// D-element rows; returns an element offset. The XOR keeps the reads each kernel
+// issues spread over the LDS banks. MODE 0 suits row-parallel 16-byte reads
+// (lane = row); MODE 1 suits the transposed reads (4 rows x 4 chunks per half-wave).
+template <int D, int MODE>
+__device__ __forceinline__ int swz(int row, int c) {
+    int x;
+    if constexpr (D == 128) x = MODE == 0 ? (row & 15) : ((row & 3) << 2);
+    else x = MODE == 0 ? ((row >> 1) & 7) : (((row >> 1) & 1) << 2);
+    return row * D + ((c ^ x) << 3);
+}
+
+template <int D, int MODE>
+__device__ __forceinline__ void unswz(int slot, int& row, int& c) {
+    row = slot / (D / 8);
+    const int cp = slot % (D / 8);
+    int x;
+    if constexpr (D == 128) x = MODE == 0 ? (row & 15) : ((row & 3) << 2);
+    else x = MODE == 0 ? ((row >> 1) & 7) : (((row >> 1) & 1) << 2);
+    c = cp ^ x;
+}
+
+}  // namespace fa

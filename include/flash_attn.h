@@ -1,0 +1,115 @@
+/*
+ * flash_attn.h -- C ABI of an exact-attention library for AMD MI355X (gfx950).
+ *
+ * Operation. For each batch entry b and query head h:
+ *
+ *     O = softmax(scale * Q K^T [+ causal mask]) V
+ *
+ * Query head h reads key/value head h / (Hq / Hkv) (grouped-query attention;
+ * Hq / Hkv consecutive query heads share one K/V head). Under the causal mask,
+ * query row i sees key j iff j <= i. The forward pass also stores one
+ * logsumexp value per query row,
+ *
+ *     LSE_i = ln sum_{visible j} exp(scale * q_i . k_j),
+ *
+ * and the backward pass rebuilds the probabilities from it, never from a stored
+ * score matrix. The N x N score matrix is never written to device memory.
+ * Sources: mlapandio "FlashAttention: IO-aware exact attention" (Definition;
+ * the naive-vs-flash diagram, flash half; "Four ideas", recomputation item;
+ * "Two notes" for grouped-query attention) and techtrendtracker "Flash
+ * Attention: memory-efficient transformers" ("Recomputation in the Backward
+ * Pass"). The scale, the mask convention and the head mapping are readings
+ * of those pages; the pages fix none of them.
+ *
+ * Layout. Every tensor is contiguous, row-major [B, H, N, d] (d fastest) in
+ * bfloat16, with H = Hq for q/o/dout/dq and H = Hkv for k/v/dk/dv. LSE is
+ * contiguous [B, Hq, N] float32 (natural log). There are no stride arguments.
+ *
+ * Supported shapes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128};
+ * B*Hq*N*d < 2^62. scale must be finite and >= 0. Other shapes return an error;
+ * there is no fallback path.
+ *
+ * Pointers are device pointers (hipMalloc'd or equivalent), 16-byte aligned.
+ * `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
+ * work on `stream` and return at once; results are valid once the stream has
+ * been synchronised. The library never allocates, frees or synchronises, keeps
+ * no pointer after a call returns, and holds no mutable global state, so calls
+ * from several host threads are safe. Calls on one stream run in order; the
+ * caller orders calls on different streams that share buffers.
+ *
+ * Errors. Every entry point returns FA_OK (0) or a negative status and never
+ * aborts. Arguments are checked before any HIP call, so an invalid call
+ * enqueues nothing. FA_ERR_HIP means a launch failed; flash_attn_strerror()
+ * then also carries the HIP error text of the calling thread's last failure.
+ */
+#ifndef FLASH_ATTN_H
+#define FLASH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,      /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow */
+    FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
+    FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+    FA_ERR_WORKSPACE = -5, /* backward workspace NULL or smaller than required */
+    FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
+    FA_ERR_SCALE = -7      /* scale is negative, NaN or infinite */
+};
+
+/*
+ * Forward pass.
+ *   q    in   bf16 [B, Hq,  N, d]
+ *   k    in   bf16 [B, Hkv, N, d]
+ *   v    in   bf16 [B, Hkv, N, d]
+ *   o    out  bf16 [B, Hq,  N, d]   normalised output
+ *   lse  out  fp32 [B, Hq,  N]      natural-log logsumexp of the scaled, masked scores
+ * causal: 0 or 1. scale: the factor on q.k before the softmax (usually 1/sqrt(d)).
+ * Inputs and outputs must not overlap.
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   void* stream);
+
+/*
+ * Bytes of device workspace flash_attn_bwd needs for these arguments: room for
+ * D = rowsum(dout * o), fp32 [B, Hq, N], rounded up to 256 bytes. Returns 0 for
+ * shapes the backward rejects.
+ */
+size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal);
+
+/*
+ * Backward pass for the loss sum(dout * O): given the forward's o and lse,
+ * writes the gradients with respect to q, k and v.
+ *   q, k, v, o, lse, dout   in   as in flash_attn_fwd; dout shaped like o
+ *   dq                      out  bf16 [B, Hq,  N, d]
+ *   dk, dv                  out  bf16 [B, Hkv, N, d]   summed over each K/V head's query group
+ *   workspace               scratch, device memory of workspace_bytes >=
+ *                           flash_attn_bwd_workspace_size(...); contents on
+ *                           entry are ignored and on return are unspecified
+ * Outputs must not overlap inputs or each other. Runs three kernels in order on
+ * `stream`: the row-dot D, then dK/dV, then dQ. Deterministic: the same inputs
+ * give bit-identical outputs (no atomics).
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
+ * error string of the calling thread's last failed launch. Never NULL. */
+const char* flash_attn_strerror(int status);
+
+/* Library version and the GPU target it was compiled for, e.g. "0.1.0 gfx950". */
+const char* flash_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H */

@@ -1,0 +1,169 @@
+"""GPU forward pass against the fp64 oracle on identical seeded bf16 inputs.
+
+Tolerances: max abs error on O <= 1e-2 beyond the rounding of the bf16 output
+(half a bf16 ulp at the oracle's value), and on the fp32 LSE <= 1e-3. Small
+cases are compared element by element on every output.
+Full-size workloads are compared on seeded samples of query rows that the oracle
+computes one by one. Closed forms (constant V, causal row 0, uniform attention
+at scale 0) are checked on every row.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from tests.gpu_util import TOL_LSE, TOL_O, excess_err, f64, from_dev_bf16, from_dev_f32, max_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import exact_io_aware_60_amd as fa
+    fa.lib()
+    return fa
+
+
+def run_fwd(fa, inp, causal, scale):
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    return from_dev_bf16(o), from_dev_f32(lse)
+
+
+def check_full(fa, inp, causal, scale, tag):
+    say(f"fwd {tag}")
+    o, lse = run_fwd(fa, inp, causal, scale)
+    ro, rl = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), causal, scale)
+    eo, el = excess_err(o, ro), max_err(lse, rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"{tag}: O err {eo:.2e}, LSE err {el:.2e}"
+    return eo, el
+
+
+def test_tiny_workload(fa):
+    """The 1-head, N = 256, d = 64, non-causal workload with fp32-drawn inputs
+    rounded to bf16; both sides see the same rounded values."""
+    w = ai.WORKLOADS["tiny"]
+    inp = ai.make_inputs(w)
+    check_full(fa, inp, w.causal, w.scale, "tiny")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 3, 17, 63, 64, 65, 255, 256, 257, 300, 700])
+def test_ragged(fa, d, causal, N):
+    inp = ai.make_case(1, 2, 2, N, d, seed=N * 7 + d + int(causal), with_grad=False)
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"ragged N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_gqa_small(fa, d):
+    inp = ai.make_case(2, 8, 2, 333, d, seed=400 + d, with_grad=False)
+    check_full(fa, inp, True, 1.0 / math.sqrt(d), f"gqa d={d}")
+    check_full(fa, inp, False, 1.0 / math.sqrt(d), f"gqa d={d} noncausal")
+
+
+def test_head_count_multiple_of_eight(fa):
+    """Head counts that are a multiple of 8 take the XCD-grouped workgroup order."""
+    inp = ai.make_case(2, 8, 4, 520, 128, seed=77, with_grad=False)
+    check_full(fa, inp, True, 0.0883883, "heads%8==0")
+
+
+def test_large_logits(fa):
+    """Scores spread by a factor of 4 on some keys and a larger scale: exercises
+    the lazy reference-max rescale."""
+    inp = ai.make_case(1, 4, 4, 1000, 128, seed=5, with_grad=False, dist_scale=2.0)
+    check_full(fa, inp, True, 0.2, "large logits")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v(fa, causal):
+    """Every v_j equal: O_i = v exactly for every row."""
+    inp = ai.make_case(1, 2, 2, 500, 128, seed=11, with_grad=False)
+    inp["v"] = np.broadcast_to(inp["v"][:, :, :1], inp["v"].shape).copy()
+    say(f"fwd constant V causal={causal}")
+    o, _ = run_fwd(fa, inp, causal, 0.0883883)
+    assert excess_err(o, np.broadcast_to(f64(inp["v"][:, :, :1]), o.shape)) <= TOL_O
+
+
+def test_causal_row_zero(fa):
+    """Causal row 0 attends only to key 0: O_0 = v_0, LSE_0 = s q_0.k_0."""
+    inp = ai.make_case(2, 4, 4, 300, 64, seed=12, with_grad=False)
+    s = 0.125
+    say("fwd causal row 0")
+    o, lse = run_fwd(fa, inp, True, s)
+    q, k, v = f64(inp["q"]), f64(inp["k"]), f64(inp["v"])
+    assert excess_err(o[:, :, 0], v[:, :, 0]) <= TOL_O
+    assert max_err(lse[:, :, 0], s * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])) <= TOL_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_uniform_scale_zero(fa, d):
+    """scale = 0: causal O_i is the prefix mean of V and LSE_i = ln(i + 1)."""
+    inp = ai.make_case(1, 2, 1, 777, d, seed=13, with_grad=False)
+    say(f"fwd scale 0 d={d}")
+    o, lse = run_fwd(fa, inp, True, 0.0)
+    v = f64(inp["v"])
+    G = 2
+    ref = np.repeat(np.cumsum(v, axis=2) / np.arange(1, 778)[None, None, :, None], G, axis=1)
+    assert excess_err(o, ref) <= TOL_O
+    assert max_err(lse, np.broadcast_to(np.log(np.arange(1, 778)), lse.shape)) <= TOL_LSE
+
+
+def test_deterministic(fa):
+    inp = ai.make_case(1, 4, 2, 1000, 128, seed=21, with_grad=False)
+    say("fwd determinism")
+    o1, l1 = run_fwd(fa, inp, True, 0.0883883)
+    o2, l2 = run_fwd(fa, inp, True, 0.0883883)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------------ full-size workloads
+def sampled_check(fa, w, inp, rows, heads_b=None):
+    """Run the full GPU forward, then compare the sampled query rows (all heads, or
+    the (b, kv-head) groups listed) with the oracle."""
+    import torch
+    say(f"fwd workload {w.name} (full size on GPU, {len(rows)} sampled rows)")
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    rows_t = torch.as_tensor(rows, device=o.device)
+    o_s = from_dev_bf16(o.index_select(2, rows_t))
+    l_s = from_dev_f32(lse.index_select(2, rows_t))
+    del q, k, v, o, lse
+    ro, rl = oracle.fwd(f64(inp["q"][:, :, rows]), f64(inp["k"]), f64(inp["v"]), w.causal, w.scale, qpos=rows)
+    eo, el = excess_err(o_s, ro), max_err(l_s, rl)
+    assert eo <= TOL_O and el <= TOL_LSE, f"{w.name}: O err {eo:.2e}, LSE err {el:.2e}"
+
+
+@pytest.mark.parametrize("name", ["mha2k", "spiky8k", "gqa16k", "long128k"])
+def test_workload_sampled(fa, name):
+    w = ai.WORKLOADS[name]
+    inp = ai.make_inputs(w, with_grad=False)
+    rows = ai.sample_rows(w.N, 256 if name != "mha2k" else w.N, w.cfg_id)
+    sampled_check(fa, w, inp, rows)
+
+
+def test_long_context_every_row_uniform(fa):
+    """N = 131072, 8 heads, d = 128, causal, Q = 0: every row's output is the
+    prefix mean of V and LSE_i = ln(i + 1). This checks all rows at full length."""
+    import torch
+    w = ai.WORKLOADS["long128k"]
+    inp = ai.make_inputs(w, with_grad=False)
+    say("fwd long128k with Q = 0 (all rows)")
+    q = torch.zeros((w.B, w.Hq, w.N, w.d), dtype=torch.bfloat16, device="cuda")
+    k, v = to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = fa.fwd(q, k, v, causal=True, scale=w.scale)
+    vf = v.float()
+    ref = torch.cumsum(vf.double(), dim=2) / torch.arange(1, w.N + 1, device=v.device, dtype=torch.float64)[None, None, :, None]
+    half_ulp = torch.exp2(torch.floor(torch.log2(ref.abs().clamp_min(2.0 ** -126))) - 8)
+    err_o = ((o.double() - ref).abs() - half_ulp).max().item()
+    err_l = (lse.double() - torch.log(torch.arange(1, w.N + 1, device=v.device, dtype=torch.float64))).abs().max().item()
+    assert err_o <= TOL_O, err_o
+    assert err_l <= TOL_LSE, err_l
