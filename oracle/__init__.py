@@ -56,6 +56,9 @@ class Oracle:
             _i64p, ctypes.c_int, ctypes.c_double]
         lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_attn_bwd.argtypes = [_f64p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_double]
+        lib.oracle_attn_bwd_sampled.restype = ctypes.c_int
+        lib.oracle_attn_bwd_sampled.argtypes = [_f64p] * 4 + [_i64p, ctypes.c_int, _i64p, ctypes.c_int] + [
+            _f64p] * 3 + [ctypes.c_int] * 6 + [ctypes.c_double]
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
 
@@ -120,6 +123,26 @@ class Oracle:
             raise ValueError("oracle_attn_bwd rejected its arguments")
         return dict(dq=dq, dk=dk, dv=dv, o=o, lse=lse, D=D)
 
+    def bwd_sampled(self, q, k, v, do, causal: bool, scale: float, rows, keys):
+        """dQ of the listed query rows [B,Hq,len(rows),d] and dK/dV of the listed
+        keys [B,Hkv,len(keys),d]; every row still runs its full softmax."""
+        q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
+        B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
+        if Nq != Nk or do.shape != q.shape:
+            raise ValueError("backward needs one sequence and do shaped like q")
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        keys = np.ascontiguousarray(keys, dtype=np.int64)
+        dq = np.empty((B, Hq, len(rows), d))
+        dk = np.empty((B, Hkv, len(keys), d))
+        dv = np.empty((B, Hkv, len(keys), d))
+        rc = self.lib.oracle_attn_bwd_sampled(_ptr(q), _ptr(k), _ptr(v), _ptr(do), rows.ctypes.data_as(_i64p),
+                                              len(rows), keys.ctypes.data_as(_i64p), len(keys), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, d, int(bool(causal)),
+                                              float(scale))
+        if rc != 0:
+            raise ValueError("oracle_attn_bwd_sampled rejected its arguments")
+        return dict(dq=dq, dk=dk, dv=dv)
+
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
@@ -140,6 +163,10 @@ def fwd(q, k, v, causal, scale, qpos=None):
 
 def bwd(q, k, v, do, causal, scale):
     return default().bwd(q, k, v, do, causal, scale)
+
+
+def bwd_sampled(q, k, v, do, causal, scale, rows, keys):
+    return default().bwd_sampled(q, k, v, do, causal, scale, rows, keys)
 
 
 def probs(q, k, causal, scale, qpos=None):

@@ -178,84 +178,148 @@ int oracle_attn_probs(const double* q, const double* k, double* p, int B, int Hq
 }
 
 /*
- * Backward for the loss sum(dout * O), queries and keys the same sequence (N).
- * Inputs q, dout [B,Hq,N,d]; k, v [B,Hkv,N,d].
- * Outputs dq [B,Hq,N,d]; dk, dv [B,Hkv,N,d]; optional (may be NULL): o [B,Hq,N,d],
- * lse and D [B,Hq,N].
- * Rows are split over threads; each thread sums its dK/dV contributions in a
- * private buffer, and the buffers are added in thread order afterwards.
+ * Gradient contributions of one query row i against one key/value head, for
+ * the loss sum(dout * O) (definition in the header comment).
+ *   fills S, P (scratch, length N), oi[d], *lse_i, *D_i
+ *   dqi: receives dQ_i when not NULL
+ *   dK_j, dV_j contributions are added to dk_acc / dv_acc at row slot[j];
+ *   slot == NULL means slot j for every key, slot[j] < 0 skips key j.
  */
-int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
-                    double* dq, double* dk, double* dv, double* o_out, double* lse_out,
-                    double* D_out, int B, int Hq, int Hkv, int N, int d, int causal,
-                    double scale) {
-    if (!q || !k || !v || !dout || !dq || !dk || !dv || check_shape(B, Hq, Hkv, N, N, d))
-        return -1;
+static void bwd_row(const double* qi, const double* doi, const double* kh, const double* vh,
+                    int N, int d, int i, int causal, double scale, double* S, double* P,
+                    double* oi, double* lse_i, double* D_i, double* dqi, const int* slot,
+                    double* dk_acc, double* dv_acc) {
+    attend_row(qi, kh, vh, N, d, i, causal, scale, S, P, oi, lse_i);
+    const double Di = dot(doi, oi, d);
+    *D_i = Di;
+    if (dqi)
+        for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+    for (int j = 0; j < N; ++j) {
+        if (!is_visible(i, j, causal)) continue;
+        const int sj = slot ? slot[j] : j;
+        if (!dqi && sj < 0) continue;
+        const double dPij = dot(doi, vh + (size_t)j * d, d);
+        const double dSij = P[j] * (dPij - Di);
+        const double* kj = kh + (size_t)j * d;
+        if (dqi)
+            for (int c = 0; c < d; ++c) dqi[c] += scale * dSij * kj[c];
+        if (sj >= 0) {
+            double* dkj = dk_acc + (size_t)sj * d;
+            double* dvj = dv_acc + (size_t)sj * d;
+            for (int c = 0; c < d; ++c) {
+                dkj[c] += scale * dSij * qi[c];
+                dvj[c] += P[j] * doi[c];
+            }
+        }
+    }
+}
+
+/*
+ * Backward, optionally restricted to some outputs, queries and keys the same
+ * sequence (N). Inputs q, dout [B,Hq,N,d]; k, v [B,Hkv,N,d].
+ *  rows (nrows entries, ascending, or NULL = every row): dq [B,Hq,nrows,d] gets
+ *      dQ of those rows;
+ *  keys (nkeys entries, or NULL = every key): dk, dv [B,Hkv,nkeys,d] get dK, dV
+ *      of those keys (summed over the K/V head's query group);
+ *  optional (may be NULL, only with rows == NULL): o [B,Hq,N,d], lse and D [B,Hq,N].
+ * Every query row of every head still runs its full softmax, because dK_j and
+ * dV_j sum over all rows. Rows are split over threads; each thread sums its
+ * dK/dV contributions in a private buffer, and the buffers are added in thread
+ * order afterwards.
+ */
+static int bwd_impl(const double* q, const double* k, const double* v, const double* dout,
+                    const int64_t* rows, int nrows, const int64_t* keys, int nkeys, double* dq,
+                    double* dk, double* dv, double* o_out, double* lse_out, double* D_out, int B,
+                    int Hq, int Hkv, int N, int d, int causal, double scale) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || check_shape(B, Hq, Hkv, N, N, d)) return -1;
+    if (!rows) nrows = N;
+    if (!keys) nkeys = N;
+    if (nrows < 0 || nkeys < 0 || (rows && (o_out || lse_out || D_out))) return -1;
     const int G = Hq / Hkv;
     const int nt = max_threads();
-    const size_t head = (size_t)N * d;
-    double* priv = (double*)calloc((size_t)nt * 2 * head, sizeof(double));
-    double* rowbuf = (double*)malloc(sizeof(double) * (size_t)nt * (3 * (size_t)N + d));
-    if (!priv || !rowbuf) { free(priv); free(rowbuf); return -1; }
-    int status = 0;
+    const size_t head = (size_t)N * d, kout = (size_t)nkeys * d;
+    int* slot = NULL;   /* key j -> output row, or -1 */
+    int* rslot = NULL;  /* row i -> dq output row, or -1 */
+    if (keys) {
+        slot = (int*)malloc(sizeof(int) * (size_t)N);
+        if (!slot) return -1;
+        for (int j = 0; j < N; ++j) slot[j] = -1;
+        for (int t = 0; t < nkeys; ++t) {
+            if (keys[t] < 0 || keys[t] >= N) { free(slot); return -1; }
+            slot[keys[t]] = t;
+        }
+    }
+    if (rows) {
+        rslot = (int*)malloc(sizeof(int) * (size_t)N);
+        if (!rslot) { free(slot); return -1; }
+        for (int i = 0; i < N; ++i) rslot[i] = -1;
+        for (int t = 0; t < nrows; ++t) {
+            if (rows[t] < 0 || rows[t] >= N) { free(slot); free(rslot); return -1; }
+            rslot[rows[t]] = t;
+        }
+    }
+    double* priv = (double*)calloc((size_t)nt * 2 * kout + 1, sizeof(double));
+    double* rowbuf = (double*)malloc(sizeof(double) * (size_t)nt * (2 * (size_t)N + d));
+    if (!priv || !rowbuf) { free(priv); free(rowbuf); free(slot); free(rslot); return -1; }
     for (int b = 0; b < B; ++b) {
         for (int hk = 0; hk < Hkv; ++hk) {
             const double* kh = k + ((size_t)b * Hkv + hk) * head;
             const double* vh = v + ((size_t)b * Hkv + hk) * head;
-            memset(priv, 0, sizeof(double) * (size_t)nt * 2 * head);
-            const int64_t rows = (int64_t)G * N;
+            memset(priv, 0, sizeof(double) * (size_t)nt * 2 * kout);
+            const int64_t nr = (int64_t)G * N;
 #pragma omp parallel for schedule(static)
-            for (int64_t r = 0; r < rows; ++r) {
+            for (int64_t r = 0; r < nr; ++r) {
                 const int g = (int)(r / N), i = (int)(r % N);
                 const int h = hk * G + g;
                 const size_t ri = (((size_t)b * Hq + h) * N + i);
-                const double* qi = q + ri * d;
-                const double* doi = dout + ri * d;
                 const int t = thread_id();
-                double* S = rowbuf + (size_t)t * (3 * (size_t)N + d);
+                double* S = rowbuf + (size_t)t * (2 * (size_t)N + d);
                 double* P = S + N;
-                double* dS = P + N;
-                double* oi = dS + N;
-                double* dk_t = priv + (size_t)t * 2 * head;
-                double* dv_t = dk_t + head;
-                double lse_i;
-                attend_row(qi, kh, vh, N, d, i, causal, scale, S, P, oi, &lse_i);
-                const double Di = dot(doi, oi, d);
+                double* oi = P + N;
+                double* dqi = NULL;
+                if (!rows) dqi = dq + ri * d;
+                else if (rslot[i] >= 0) dqi = dq + (((size_t)b * Hq + h) * nrows + rslot[i]) * d;
+                double lse_i, D_i;
+                bwd_row(q + ri * d, dout + ri * d, kh, vh, N, d, i, causal, scale, S, P, oi, &lse_i,
+                        &D_i, dqi, slot, priv + (size_t)t * 2 * kout, priv + (size_t)t * 2 * kout + kout);
                 if (o_out) memcpy(o_out + ri * d, oi, sizeof(double) * d);
                 if (lse_out) lse_out[ri] = lse_i;
-                if (D_out) D_out[ri] = Di;
-                for (int j = 0; j < N; ++j) {
-                    if (!is_visible(i, j, causal)) { dS[j] = 0.0; continue; }
-                    const double dPij = dot(doi, vh + (size_t)j * d, d);
-                    dS[j] = P[j] * (dPij - Di);
-                }
-                double* dqi = dq + ri * d;
-                for (int c = 0; c < d; ++c) dqi[c] = 0.0;
-                for (int j = 0; j < N; ++j) {
-                    if (!is_visible(i, j, causal)) continue;
-                    const double* kj = kh + (size_t)j * d;
-                    double* dkj = dk_t + (size_t)j * d;
-                    double* dvj = dv_t + (size_t)j * d;
-                    for (int c = 0; c < d; ++c) {
-                        dqi[c] += scale * dS[j] * kj[c];
-                        dkj[c] += scale * dS[j] * qi[c];
-                        dvj[c] += P[j] * doi[c];
-                    }
-                }
+                if (D_out) D_out[ri] = D_i;
             }
-            double* dkh = dk + ((size_t)b * Hkv + hk) * head;
-            double* dvh = dv + ((size_t)b * Hkv + hk) * head;
-            for (size_t e = 0; e < head; ++e) { dkh[e] = 0.0; dvh[e] = 0.0; }
+            double* dkh = dk + ((size_t)b * Hkv + hk) * kout;
+            double* dvh = dv + ((size_t)b * Hkv + hk) * kout;
+            for (size_t e = 0; e < kout; ++e) { dkh[e] = 0.0; dvh[e] = 0.0; }
             for (int t = 0; t < nt; ++t) {
-                const double* dk_t = priv + (size_t)t * 2 * head;
-                const double* dv_t = dk_t + head;
-                for (size_t e = 0; e < head; ++e) { dkh[e] += dk_t[e]; dvh[e] += dv_t[e]; }
+                const double* dk_t = priv + (size_t)t * 2 * kout;
+                const double* dv_t = dk_t + kout;
+                for (size_t e = 0; e < kout; ++e) { dkh[e] += dk_t[e]; dvh[e] += dv_t[e]; }
             }
         }
     }
     free(priv);
     free(rowbuf);
-    return status;
+    free(slot);
+    free(rslot);
+    return 0;
+}
+
+/* Full backward: every dQ row and every dK/dV key, plus O, LSE and D (optional). */
+int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
+                    double* dq, double* dk, double* dv, double* o_out, double* lse_out,
+                    double* D_out, int B, int Hq, int Hkv, int N, int d, int causal,
+                    double scale) {
+    return bwd_impl(q, k, v, dout, NULL, 0, NULL, 0, dq, dk, dv, o_out, lse_out, D_out, B, Hq, Hkv,
+                    N, d, causal, scale);
+}
+
+/* Sampled backward: dQ of the listed rows, dK/dV of the listed keys. */
+int oracle_attn_bwd_sampled(const double* q, const double* k, const double* v, const double* dout,
+                            const int64_t* rows, int nrows, const int64_t* keys, int nkeys,
+                            double* dq_rows, double* dk_keys, double* dv_keys, int B, int Hq,
+                            int Hkv, int N, int d, int causal, double scale) {
+    if (!rows || !keys) return -1;
+    return bwd_impl(q, k, v, dout, rows, nrows, keys, nkeys, dq_rows, dk_keys, dv_keys, NULL, NULL,
+                    NULL, B, Hq, Hkv, N, d, causal, scale);
 }
 
 int oracle_num_threads(void) { return max_threads(); }

@@ -348,6 +348,22 @@ def pin_online_recurrence(orc):
             _close(lm, lse[0, 0], what=f"online LSE ({br}x{bc}, tau={tau:.2f})")
 
 
+def pin_sampled_backward(orc):
+    """The sampled backward (dQ of chosen rows, dK/dV of chosen keys) equals the
+    same rows and keys of the full backward, with GQA and both masks."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 23, 6
+    q, do = _rand((B, Hq, N, d), 160), _rand((B, Hq, N, d), 163)
+    k, v = _rand((B, Hkv, N, d), 161), _rand((B, Hkv, N, d), 162)
+    rows = np.array([0, 3, 4, 11, 22], dtype=np.int64)
+    keys = np.array([22, 1, 0, 9], dtype=np.int64)
+    for causal in (False, True):
+        full = orc.bwd(q, k, v, do, causal, 0.4)
+        smp = orc.bwd_sampled(q, k, v, do, causal, 0.4, rows, keys)
+        _close(smp["dq"], full["dq"][:, :, rows], what="sampled dQ")
+        _close(smp["dk"], full["dk"][:, :, keys], what="sampled dK")
+        _close(smp["dv"], full["dv"][:, :, keys], what="sampled dV")
+
+
 PINS = [
     pin_one_token,
     pin_two_tokens,
@@ -365,4 +381,5 @@ PINS = [
     pin_torch_sdpa,
     pin_finite_differences,
     pin_online_recurrence,
+    pin_sampled_backward,
 ]

@@ -27,14 +27,16 @@ MUTANTS = {
     "fwd GQA map modulo": ("const int hk = h / G;\n        const double* kh", "const int hk = h % Hkv;\n        const double* kh"),
     "fwd row position ignored": ("qpos ? qpos[i] : i, causal, scale, S, P,", "qpos ? qpos[i] : 0, causal, scale, S, P,"),
     "D uses dO.dO": ("const double Di = dot(doi, oi, d);", "const double Di = dot(doi, doi, d);"),
-    "D term dropped": ("dS[j] = P[j] * (dPij - Di);", "dS[j] = P[j] * dPij;"),
-    "dS sign flipped": ("dS[j] = P[j] * (dPij - Di);", "dS[j] = P[j] * (Di - dPij);"),
+    "D term dropped": ("const double dSij = P[j] * (dPij - Di);", "const double dSij = P[j] * dPij;"),
+    "dS sign flipped": ("const double dSij = P[j] * (dPij - Di);", "const double dSij = P[j] * (Di - dPij);"),
     "dP uses K": ("const double dPij = dot(doi, vh + (size_t)j * d, d);", "const double dPij = dot(doi, kh + (size_t)j * d, d);"),
-    "dQ uses Q": ("dqi[c] += scale * dS[j] * kj[c];", "dqi[c] += scale * dS[j] * qi[c];"),
-    "dK scale dropped": ("dkj[c] += scale * dS[j] * qi[c];", "dkj[c] += dS[j] * qi[c];"),
-    "dV uses dS": ("dvj[c] += P[j] * doi[c];", "dvj[c] += dS[j] * doi[c];"),
+    "dQ uses Q": ("dqi[c] += scale * dSij * kj[c];", "dqi[c] += scale * dSij * qi[c];"),
+    "dK scale dropped": ("dkj[c] += scale * dSij * qi[c];", "dkj[c] += dSij * qi[c];"),
+    "dV uses dS": ("dvj[c] += P[j] * doi[c];", "dvj[c] += dSij * doi[c];"),
     "bwd KV head ignored": ("const double* kh = k + ((size_t)b * Hkv + hk) * head;", "const double* kh = k + ((size_t)b * Hkv) * head;"),
     "bwd head in group wrong": ("const int h = hk * G + g;", "const int h = hk + g * Hkv;"),
+    "sampled key slot wrong": ("slot[keys[t]] = t;", "slot[keys[t]] = 0;"),
+    "sampled row slot wrong": ("rslot[rows[t]] = t;", "rslot[rows[t]] = nrows - 1 - t;"),
     "bwd reduction drops a thread": ("for (int t = 0; t < nt; ++t) {\n                const double* dk_t", "for (int t = 1; t < nt; ++t) {\n                const double* dk_t"),
 }
 
