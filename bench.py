@@ -1,0 +1,203 @@
+"""Benchmark: causal bf16 exact attention, forward + backward, on one MI355X.
+
+One step is the whole hot path over one batch of synthetic input: the forward
+kernel (O and LSE), then the three backward kernels (row dot, dK/dV, dQ). The
+workload is B=2, Hq=32, Hkv=8 (grouped-query attention), N=16384, d=128,
+causal, bf16 inputs ~ N(0, 1) from a fixed seed, dO ~ N(0, 1).
+
+Throughput counts 4*B*Hq*N^2*d FLOP for the forward, halved under the causal
+mask, and 2.5 times that for the backward. Inputs are resident in device memory
+before the timed region; each kernel is bracketed by HIP events on the stream
+it runs on. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import attn_inputs as ai  # noqa: E402
+
+METRIC = "attention fwd/bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
+WORKLOAD = "gqa16k"
+# MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP per clock per CU.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0
+KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+
+
+def pair_count(w) -> float:
+    """(query, key) pairs per query head as the FLOP formula counts them: N^2, halved when causal."""
+    return w.N * w.N / (2.0 if w.causal else 1.0)
+
+
+def algorithmic(w) -> dict:
+    """Algorithmic work per launch of each kernel.
+
+    fwd:      S = QK^T and O += PV, 4*d FLOP per visible pair.
+    bwd_dkdv: S (rebuilt), dP = dO V^T, dV += P^T dO, dK += dS^T Q, 8*d FLOP per pair.
+    bwd_dq:   dQ += dS K, 2*d FLOP per pair (its S and dP are a second evaluation
+              of the same products, so they are not counted again).
+    bwd_pre:  reads O and dO (bf16) and LSE, writes D and the log2-scaled LSE.
+    """
+    heads = w.B * w.Hq
+    pairs = heads * pair_count(w)
+    rows = heads * w.N
+    return {
+        "fwd": ("flop", 4 * w.d * pairs),
+        "bwd_dkdv": ("flop", 8 * w.d * pairs),
+        "bwd_dq": ("flop", 2 * w.d * pairs),
+        "bwd_pre": ("bytes", rows * (2 * 2 * w.d + 4 + 4 + 4)),
+    }
+
+
+def cpu_baseline(w) -> dict:
+    """The fp64 oracle timed on the host cores on a bounded sample: the first
+    (batch, K/V head) group (its G query heads) restricted to the first
+    `n` positions, forward and backward. Under the causal mask that prefix is a
+    self-contained problem of the same shape family."""
+    import oracle
+    n = int(os.environ.get("BENCH_CPU_SAMPLE_N", "6144"))
+    n = min(n, w.N)
+    inp = ai.make_inputs(w)
+    G = w.G
+    q = ai.bf16_bits_to_f64(inp["q"][0:1, 0:G, :n])
+    k = ai.bf16_bits_to_f64(inp["k"][0:1, 0:1, :n])
+    v = ai.bf16_bits_to_f64(inp["v"][0:1, 0:1, :n])
+    do = ai.bf16_bits_to_f64(inp["do"][0:1, 0:G, :n])
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    orc.fwd(q, k, v, w.causal, w.scale)
+    orc.bwd(q, k, v, do, w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    flop = 3.5 * 4 * G * n * n / (2.0 if w.causal else 1.0) * w.d
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"fp64 forward + backward of batch 0, K/V head 0 ({G} query heads), first {n} of "
+                      f"{w.N} positions (causal prefix); {dt:.1f} s",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: the attention path here is single-GPU (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_io_aware_60_amd as fa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    fa.lib()
+    w = ai.WORKLOADS[WORKLOAD]
+    B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
+    inp = ai.make_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.bwd_workspace_size(B, Hq, Hkv, N, d, w.causal)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    ptrs = [t.data_ptr() for t in (q, k, v, o, lse, do, dq, dk, dv)]
+
+    def call(i: int) -> None:
+        if i == 0:
+            st = fa.fwd_raw(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], B, Hq, Hkv, N, d, w.causal, w.scale, sp)
+        else:
+            st = fa.bwd_stage_raw(i - 1, *ptrs, B, Hq, Hkv, N, d, w.causal, w.scale, ws.data_ptr(), ws_bytes, sp)
+        if st != 0:
+            raise RuntimeError(f"{KERNELS[i]}: {fa.strerror(st)}")
+
+    for _ in range(args.warmup):
+        for i in range(4):
+            call(i)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i in range(4):
+            call(i)
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ktime = {name: 0.0 for name in KERNELS}
+    for s in range(args.steps):
+        for i, name in enumerate(KERNELS):
+            ktime[name] += ev[s][i].elapsed_time(ev[s][i + 1])
+    kavg = {name: t / args.steps for name, t in ktime.items()}
+    step_ms = sum(ev[s][0].elapsed_time(ev[s][4]) for s in range(args.steps)) / args.steps
+    fwd_flop = 4.0 * B * Hq * N * N * d / (2.0 if w.causal else 1.0)
+    bwd_flop = 2.5 * fwd_flop
+    fwd_ms = kavg["fwd"]
+    bwd_ms = kavg["bwd_pre"] + kavg["bwd_dkdv"] + kavg["bwd_dq"]
+    value = (fwd_flop + bwd_flop) / step_ms / 1e9
+
+    alg = algorithmic(w)
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kavg[n])
+    kind, amount = alg[dom]
+    achieved = amount / (kavg[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_ms": kavg[dom], "algorithmic_flop_per_launch": amount}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": w.causal,
+                   "passes": "fwd+bwd"},
+        "passes": {
+            "fwd": {"ms": fwd_ms, "tflops": fwd_flop / fwd_ms / 1e9,
+                    "frac_of_peak": fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS},
+            "bwd": {"ms": bwd_ms, "tflops": bwd_flop / bwd_ms / 1e9,
+                    "frac_of_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS},
+        },
+        "kernel_ms": kavg,
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "roofline": roofline,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

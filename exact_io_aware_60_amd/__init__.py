@@ -23,7 +23,8 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE
     0, -1, -2, -3, -4, -5, -6, -7)
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
-            "flash_attn_version")
+            "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq")
+BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -45,8 +46,10 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.flash_attn_fwd.restype = _i
         L.flash_attn_fwd.argtypes = [_vp] * 5 + [_i] * 6 + [ctypes.c_float, _vp]
-        L.flash_attn_bwd.restype = _i
-        L.flash_attn_bwd.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        for name in ("flash_attn_bwd",) + BWD_STAGES:
+            fn = getattr(L, name)
+            fn.restype = _i
+            fn.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_bwd_workspace_size.argtypes = [_i] * 6
         L.flash_attn_strerror.restype = ctypes.c_char_p
@@ -81,6 +84,14 @@ def bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, wo
     """flash_attn_bwd on raw addresses (ints); returns the status code."""
     return lib().flash_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), float(scale),
                                 workspace, workspace_bytes, stream)
+
+
+def bwd_stage_raw(stage: int, q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
+                  workspace_bytes, stream=None) -> int:
+    """One backward stage (0 = preprocess, 1 = dkdv, 2 = dq) on raw addresses; returns the status."""
+    fn = getattr(lib(), BWD_STAGES[stage])
+    return fn(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), float(scale), workspace,
+              workspace_bytes, stream)
 
 
 def bwd_workspace_size(B, Hq, Hkv, N, d, causal) -> int:

@@ -85,14 +85,19 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal) {
     (void)causal;
     if (check_shape(B, Hq, Hkv, N, d) != FA_OK) return 0;
-    const size_t bytes = sizeof(float) * (size_t)B * Hq * N;
-    return (bytes + 255) & ~(size_t)255;
+    return fa::bwd_workspace_bytes((long long)B * Hq * N);
 }
 
-int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
-                   int d, int causal, float scale, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by flash_attn_bwd and its stage entry points: validate, fill the
+// parameter block, enqueue stages [first, last].
+int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+               int causal, float scale, void* workspace, size_t workspace_bytes, void* stream,
+               int first, int last) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_shape(B, Hq, Hkv, N, d);
     if (st != FA_OK) return st;
@@ -103,7 +108,7 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
     if (!workspace || workspace_bytes < flash_attn_bwd_workspace_size(B, Hq, Hkv, N, d, causal))
         return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    log_config("bwd", B, Hq, Hkv, N, d, causal);
+    if (first == 0) log_config("bwd", B, Hq, Hkv, N, d, causal);
     fa::BwdParams p;
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
@@ -115,11 +120,54 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
     p.dk = static_cast<uint16_t*>(dk);
     p.dv = static_cast<uint16_t*>(dv);
     p.delta = static_cast<float*>(workspace);
+    p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      fa::bwd_workspace_bytes((long long)B * Hq * N) / 2);
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d; p.G = Hq / Hkv;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
-    return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int stage = first; stage <= last; ++stage) {
+        st = hip_status(fa::launch_bwd_stage(p, stage, s));
+        if (st != FA_OK) return st;
+    }
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                   int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
+                      workspace_bytes, stream, 0, 2);
+}
+
+int flash_attn_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
+                      workspace_bytes, stream, 0, 0);
+}
+
+int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                        int N, int d, int causal, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
+                      workspace_bytes, stream, 1, 1);
+}
+
+int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                      int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
+                      workspace_bytes, stream, 2, 2);
 }
 
 const char* flash_attn_strerror(int status) {
@@ -136,6 +184,6 @@ const char* flash_attn_strerror(int status) {
     }
 }
 
-const char* flash_attn_version(void) { return "0.1.0 gfx950"; }
+const char* flash_attn_version(void) { return "0.2.0 gfx950"; }
 
 }  // extern "C"

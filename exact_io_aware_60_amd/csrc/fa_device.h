@@ -24,6 +24,7 @@ namespace fa {
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
@@ -72,12 +73,14 @@ __device__ __forceinline__ void gload_lds16(const uint16_t* g, FA_LDS uint16_t* 
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
                                      (FA_LDS void*)(lds_wave_base), 16, 0, 0);
 }
+// Direct global -> LDS copy of 4 bytes per lane (global_load_lds_dword): lane i's
+// dword lands at lds_wave_base + 4 * i bytes. Same completion rules as above.
+__device__ __forceinline__ void gload_lds4(const float* g, FA_LDS float* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
+                                     (FA_LDS void*)(lds_wave_base), 4, 0, 0);
+}
 // s_waitcnt vmcnt(0): all of this wave's vector-memory loads have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Inverse of swz(): the (row, logical chunk) stored at 16-byte slot `slot` of a tile.
-template <int D, int MODE>
-__device__ __forceinline__ void unswz(int slot, int& row, int& c);
 
 // Global 16-byte load; returns zeros when !valid (ragged tails).
 __device__ __forceinline__ u32x4 gload16(const uint16_t* p, bool valid) {
@@ -105,24 +108,35 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // Swizzled position of 16-byte chunk `c` of row `row` in an LDS tile of
 // D-element rows; returns an element offset. The XOR keeps the reads each kernel
-// issues spread over the LDS banks. MODE 0 suits row-parallel 16-byte reads
-// (lane = row); MODE 1 suits the transposed reads (4 rows x 4 chunks per half-wave).
+// issues spread over the LDS banks (64 banks of 4 bytes: 256 bytes per bank
+// line). MODE 0 suits row-parallel 16-byte reads (lane = row): 16 consecutive
+// rows put one logical chunk at 16 distinct 16-byte slots of a bank line.
+// MODE 1 suits the transposed reads, where a 16-lane group reads 4 consecutive
+// rows x 2 consecutive chunks: those 8 chunks land in distinct slots. MODE 2
+// satisfies both conditions at once, for tiles read both ways.
+template <int D, int MODE>
+__device__ __forceinline__ int swz_key(int row) {
+    if constexpr (D == 128) {
+        if constexpr (MODE == 0) return row & 15;
+        else if constexpr (MODE == 1) return (row & 3) << 2;
+        else return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
+    } else {
+        const int x = (row >> 1) & 7;
+        if constexpr (MODE == 0) return x;
+        else if constexpr (MODE == 1) return (x & 1) << 2;
+        else return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
+    }
+}
+
 template <int D, int MODE>
 __device__ __forceinline__ int swz(int row, int c) {
-    int x;
-    if constexpr (D == 128) x = MODE == 0 ? (row & 15) : ((row & 3) << 2);
-    else x = MODE == 0 ? ((row >> 1) & 7) : (((row >> 1) & 1) << 2);
-    return row * D + ((c ^ x) << 3);
+    return row * D + ((c ^ swz_key<D, MODE>(row)) << 3);
 }
 
 template <int D, int MODE>
 __device__ __forceinline__ void unswz(int slot, int& row, int& c) {
     row = slot / (D / 8);
-    const int cp = slot % (D / 8);
-    int x;
-    if constexpr (D == 128) x = MODE == 0 ? (row & 15) : ((row & 3) << 2);
-    else x = MODE == 0 ? ((row >> 1) & 7) : (((row >> 1) & 1) << 2);
-    c = cp ^ x;
+    c = (slot % (D / 8)) ^ swz_key<D, MODE>(row);
 }
 
 }  // namespace fa

@@ -29,6 +29,7 @@ struct BwdParams {
     uint16_t* dk;
     uint16_t* dv;
     float* delta;        // fp32 [B, Hq, N] workspace: rowsum(dout * o)
+    float* lse2;         // fp32 [B, Hq, N] workspace: lse * log2(e)
     int B, Hq, Hkv, N, d, G;
     int causal;
     float scale;
@@ -39,6 +40,8 @@ struct BwdParams {
 // stream; they return the HIP status of the launch.
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+// One backward stage: 0 = row dot D (and log2-scaled LSE), 1 = dK/dV, 2 = dQ.
+hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream);
 
 // Launch geometry, exposed for logging and tests of the host logic.
 struct Geometry {
@@ -49,5 +52,9 @@ struct Geometry {
     int lds_bytes;    // LDS per workgroup
 };
 Geometry fwd_geometry(int B, int Hq, int N, int d, int causal);
+
+// Bytes of backward workspace: D and the log2-scaled LSE, one fp32 each per
+// query row, each array starting on a 256-byte boundary.
+size_t bwd_workspace_bytes(long long rows);
 
 }  // namespace fa

@@ -77,15 +77,18 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
- * Bytes of device workspace flash_attn_bwd needs for these arguments: room for
- * D = rowsum(dout * o), fp32 [B, Hq, N], rounded up to 256 bytes. Returns 0 for
- * shapes the backward rejects.
+ * Bytes of device workspace flash_attn_bwd needs for these arguments: two fp32
+ * arrays of one value per query row, D = rowsum(dout * o) and LSE * log2(e),
+ * each rounded up to 256 bytes. Returns 0 for shapes the backward rejects.
  */
 size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal);
 
 /*
  * Backward pass for the loss sum(dout * O): given the forward's o and lse,
- * writes the gradients with respect to q, k and v.
+ * writes the gradients with respect to q, k and v (mlapandio "FlashAttention:
+ * IO-aware exact attention", "Four ideas", recomputation item: P is rebuilt
+ * from the stored logsumexp; techtrendtracker "Flash Attention:
+ * memory-efficient transformers", "Recomputation in the Backward Pass").
  *   q, k, v, o, lse, dout   in   as in flash_attn_fwd; dout shaped like o
  *   dq                      out  bf16 [B, Hq,  N, d]
  *   dk, dv                  out  bf16 [B, Hkv, N, d]   summed over each K/V head's query group
@@ -93,7 +96,7 @@ size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int c
  *                           flash_attn_bwd_workspace_size(...); contents on
  *                           entry are ignored and on return are unspecified
  * Outputs must not overlap inputs or each other. Runs three kernels in order on
- * `stream`: the row-dot D, then dK/dV, then dQ. Deterministic: the same inputs
+ * `stream`: the row dot D, then dK/dV, then dQ. Deterministic: the same inputs
  * give bit-identical outputs (no atomics).
  */
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -101,11 +104,35 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The three stages of flash_attn_bwd, one kernel each, with its argument list
+ * and checks. flash_attn_bwd is exactly preprocess, dkdv, dq in that order on
+ * one stream. They exist so that a caller can time or schedule the kernels
+ * separately (for example dkdv and dq on two streams once preprocess is done).
+ *   preprocess  reads o, dout, lse; writes the workspace
+ *   dkdv        reads q, k, v, dout and the workspace; writes dk, dv
+ *   dq          reads q, k, v, dout and the workspace; writes dq
+ * dkdv and dq need the workspace that preprocess wrote for the same o, dout
+ * and lse; pointers a stage does not use must still be valid and aligned.
+ */
+int flash_attn_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
 
-/* Library version and the GPU target it was compiled for, e.g. "0.1.0 gfx950". */
+/* Library version and the GPU target it was compiled for, e.g. "0.2.0 gfx950". */
 const char* flash_attn_version(void);
 
 #ifdef __cplusplus

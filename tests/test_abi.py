@@ -106,10 +106,29 @@ def test_bwd_checks():
 @pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 1, 1, 1, 64), (4, 16, 16, 2048, 64), (2, 32, 8, 16384, 128),
                                           (1, 8, 8, 131072, 128), (3, 5, 5, 77, 128)])
 def test_workspace_size(B, Hq, Hkv, N, d):
-    # D = rowsum(dO * O): one fp32 per query row, rounded up to 256 bytes
+    # D = rowsum(dO * O) and the log2-scaled LSE: one fp32 each per query row,
+    # each array rounded up to 256 bytes
     got = fa.bwd_workspace_size(B, Hq, Hkv, N, d, 1)
-    need = 4 * B * Hq * N
-    assert got >= need and got % 256 == 0 and got - need < 256
+    one = 4 * B * Hq * N
+    assert got % 256 == 0 and got == 2 * (one + (-one) % 256)
+
+
+@pytest.mark.parametrize("stage", [0, 1, 2])
+def test_bwd_stages_validate(stage):
+    """The stage entry points take flash_attn_bwd's arguments and checks."""
+    a = dict(B=1, Hq=4, Hkv=2, N=128, d=128)
+    need = fa.bwd_workspace_size(1, 4, 2, 128, 128, 1)
+    args = [P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], 1,
+            0.088, P[9], need]
+    bad = list(args)
+    bad[0] = None
+    assert fa.bwd_stage_raw(stage, *bad) == fa.FA_ERR_NULL
+    bad = list(args)
+    bad[17] = need - 1
+    assert fa.bwd_stage_raw(stage, *bad) == fa.FA_ERR_WORKSPACE
+    bad = list(args)
+    bad[13] = 80
+    assert fa.bwd_stage_raw(stage, *bad) == fa.FA_ERR_HEADDIM
 
 
 def test_workspace_size_rejects_bad_shapes():

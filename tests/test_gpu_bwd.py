@@ -1,0 +1,189 @@
+"""GPU backward pass against the fp64 oracle on identical seeded bf16 inputs.
+
+The GPU backward is fed the GPU forward's own O and LSE, as a caller would; the
+oracle computes everything from the inputs in fp64. Tolerance: max abs error on
+dQ, dK and dV <= 2e-2 beyond the rounding of the bf16 output (half a bf16 ulp at
+the oracle's value). Small cases are compared element by element on every
+output; full-size workloads on seeded samples of query rows (dQ) and keys
+(dK, dV) that the oracle computes one by one, over all heads or, for the GQA
+workload, over two seeded (batch, K/V head) groups.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from tests.gpu_util import TOL_GRAD, excess_err, f64, from_dev_bf16, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import exact_io_aware_60_amd as fa
+    fa.lib()
+    return fa
+
+
+def run_fwd_bwd(fa, inp, causal, scale):
+    """GPU forward then backward on the same device tensors; returns host fp64 arrays."""
+    import torch
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return from_dev_bf16(dq), from_dev_bf16(dk), from_dev_bf16(dv)
+
+
+def check_full(fa, inp, causal, scale, tag):
+    say(f"bwd {tag}")
+    dq, dk, dv = run_fwd_bwd(fa, inp, causal, scale)
+    ref = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), causal, scale)
+    errs = {n: excess_err(g, ref[n]) for n, g in (("dq", dq), ("dk", dk), ("dv", dv))}
+    assert all(e <= TOL_GRAD for e in errs.values()), f"{tag}: {errs}"
+    return errs
+
+
+def test_workload_mha2k_full(fa):
+    """B=4, H=16, N=2048, d=64, causal: every gradient element against the oracle."""
+    w = ai.WORKLOADS["mha2k"]
+    inp = ai.make_inputs(w)
+    check_full(fa, inp, w.causal, w.scale, "mha2k (all elements)")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 2, 3, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 700])
+def test_ragged(fa, d, causal, N):
+    inp = ai.make_case(1, 2, 2, N, d, seed=N * 11 + d + int(causal))
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"ragged N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_small(fa, d, causal):
+    """Four query heads per K/V head: dK and dV sum over the group."""
+    inp = ai.make_case(2, 8, 2, 333, d, seed=500 + d + int(causal))
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"gqa d={d} causal={causal}")
+
+
+def test_head_count_multiple_of_eight(fa):
+    """Unit counts that are a multiple of 8 take the XCD-grouped workgroup order
+    (B*Hkv = 8 for the dK/dV kernel, B*Hq = 16 for the dQ kernel)."""
+    inp = ai.make_case(2, 8, 4, 520, 128, seed=78)
+    check_full(fa, inp, True, 0.0883883, "units%8==0")
+
+
+def test_large_logits(fa):
+    inp = ai.make_case(1, 4, 4, 1000, 128, seed=6, dist_scale=2.0)
+    check_full(fa, inp, True, 0.2, "large logits")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v(fa, causal):
+    """Every v_j equal: dP_ij = D_i, so dS = 0 and dQ = dK = 0 exactly in exact
+    arithmetic; dV_j = sum_i P_ij dO_i (checked against the oracle)."""
+    inp = ai.make_case(1, 2, 2, 500, 128, seed=14)
+    inp["v"] = np.broadcast_to(inp["v"][:, :, :1], inp["v"].shape).copy()
+    say(f"bwd constant V causal={causal}")
+    dq, dk, dv = run_fwd_bwd(fa, inp, causal, 0.0883883)
+    ref = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), causal, 0.0883883)
+    assert np.max(np.abs(dq)) <= TOL_GRAD and np.max(np.abs(dk)) <= TOL_GRAD
+    assert excess_err(dv, ref["dv"]) <= TOL_GRAD
+
+
+def test_causal_row_zero_and_sums(fa):
+    """Causal row 0 has one visible key, so dQ_0 = 0. Rows of dS sum to zero, so
+    sum_j dK_j = 0; rows of P sum to one, so sum_j dV_j = sum over the group of dO."""
+    inp = ai.make_case(1, 4, 2, 640, 64, seed=15)
+    say("bwd causal row 0 and gradient sums")
+    dq, dk, dv = run_fwd_bwd(fa, inp, True, 0.125)
+    assert np.max(np.abs(dq[:, :, 0])) <= TOL_GRAD
+    do = f64(inp["do"])
+    sum_dv = dv.sum(axis=2)
+    ref_dv = do.reshape(1, 2, 2, 640, 64).sum(axis=(2, 3))
+    scale_ref = np.sqrt(640 * 2)   # the sums run over 1280 terms of unit size
+    assert np.max(np.abs(sum_dv - ref_dv)) <= 2e-2 * scale_ref
+    assert np.max(np.abs(dk.sum(axis=2))) <= 2e-2 * scale_ref
+
+
+def test_deterministic(fa):
+    inp = ai.make_case(1, 4, 2, 1000, 128, seed=22)
+    say("bwd determinism")
+    a = run_fwd_bwd(fa, inp, True, 0.0883883)
+    b = run_fwd_bwd(fa, inp, True, 0.0883883)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_stages_equal_full_call(fa):
+    """preprocess, dkdv, dq called one by one give flash_attn_bwd's bits."""
+    import torch
+    inp = ai.make_case(1, 4, 2, 300, 64, seed=23)
+    say("bwd stages vs full call")
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    o, lse = fa.fwd(q, k, v, causal=True, scale=0.125)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=True, scale=0.125)
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    ws_bytes = fa.bwd_workspace_size(1, 4, 2, 300, 64, 1)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream().cuda_stream
+    for stage in range(3):
+        st = fa.bwd_stage_raw(stage, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              do.data_ptr(), dq2.data_ptr(), dk2.data_ptr(), dv2.data_ptr(), 1, 4, 2, 300, 64, 1,
+                              0.125, ws.data_ptr(), ws_bytes, stream)
+        assert st == 0
+    torch.cuda.synchronize()
+    for x, y in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+# ------------------------------------------------------------------ full-size workloads
+def sampled_bwd_check(fa, w, inp, groups):
+    """Full GPU forward + backward, then compare sampled dQ rows and dK/dV keys of
+    the listed (b, kv-head) groups with the oracle."""
+    import torch
+    say(f"bwd workload {w.name} (full size on GPU, groups {groups})")
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = ai.sample_rows(w.N, 256, w.cfg_id)
+    keys = ai.sample_rows(w.N, 256, w.cfg_id + 100)
+    rt, kt = torch.as_tensor(rows, device=q.device), torch.as_tensor(keys, device=q.device)
+    G = w.G
+    for (b, h) in groups:
+        hs = slice(h * G, (h + 1) * G)
+        g_dq = from_dev_bf16(dq[b:b + 1, hs].index_select(2, rt))
+        g_dk = from_dev_bf16(dk[b:b + 1, h:h + 1].index_select(2, kt))
+        g_dv = from_dev_bf16(dv[b:b + 1, h:h + 1].index_select(2, kt))
+        ref = oracle.bwd_sampled(f64(inp["q"][b:b + 1, hs]), f64(inp["k"][b:b + 1, h:h + 1]),
+                                 f64(inp["v"][b:b + 1, h:h + 1]), f64(inp["do"][b:b + 1, hs]), w.causal, w.scale,
+                                 rows, keys)
+        errs = {n: excess_err(g, ref[n]) for n, g in (("dq", g_dq), ("dk", g_dk), ("dv", g_dv))}
+        assert all(e <= TOL_GRAD for e in errs.values()), f"{w.name} group {(b, h)}: {errs}"
+
+
+def seeded_groups(w, count):
+    rng = ai.rng_for(w.cfg_id, 7)
+    flat = rng.choice(w.B * w.Hkv, size=min(count, w.B * w.Hkv), replace=False)
+    return [(int(f) // w.Hkv, int(f) % w.Hkv) for f in sorted(flat)]
+
+
+def test_workload_spiky8k(fa):
+    """N=8192, d=128, causal, K rows x4 at 5% of positions; 4 seeded heads."""
+    w = ai.WORKLOADS["spiky8k"]
+    inp = ai.make_inputs(w)
+    sampled_bwd_check(fa, w, inp, seeded_groups(w, 4))
+
+
+def test_workload_gqa16k(fa):
+    """B=2, Hq=32, Hkv=8, N=16384, d=128, causal; two seeded (b, kv-head) groups."""
+    w = ai.WORKLOADS["gqa16k"]
+    inp = ai.make_inputs(w)
+    sampled_bwd_check(fa, w, inp, seeded_groups(w, w.oracle_groups))
