@@ -55,10 +55,12 @@ class Oracle:
         lib.oracle_attn_probs.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int] * 6 + [
             _i64p, ctypes.c_int, ctypes.c_double]
         lib.oracle_attn_bwd.restype = ctypes.c_int
-        lib.oracle_attn_bwd.argtypes = [_f64p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_double]
+        lib.oracle_attn_bwd.argtypes = [_f64p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_bwd_sampled.restype = ctypes.c_int
         lib.oracle_attn_bwd_sampled.argtypes = [_f64p] * 4 + [_i64p, ctypes.c_int, _i64p, ctypes.c_int] + [
-            _f64p] * 3 + [ctypes.c_int] * 6 + [ctypes.c_double]
+            _f64p] * 3 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
+        lib.oracle_round_bf16.restype = ctypes.c_int
+        lib.oracle_round_bf16.argtypes = [_f64p, _f64p, ctypes.c_int64]
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
 
@@ -104,8 +106,11 @@ class Oracle:
             raise ValueError("oracle_attn_probs rejected its arguments")
         return p
 
-    def bwd(self, q, k, v, do, causal: bool, scale: float):
-        """Gradients of sum(do * O): returns dict dq, dk, dv, o, lse, D."""
+    def bwd(self, q, k, v, do, causal: bool, scale: float, o_bf16: bool = False):
+        """Gradients of sum(do * O): returns dict dq, dk, dv, o, lse, D.
+
+        ``o_bf16``: form D = rowsum(do * O) from O rounded to bfloat16, the
+        format the forward stores O in; every other quantity stays exact."""
         q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
         B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
         if Nq != Nk:
@@ -118,12 +123,12 @@ class Oracle:
         D = np.empty_like(lse)
         rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
                                       _ptr(dv), _ptr(o), _ptr(lse), _ptr(D), B, Hq, Hkv, Nq, d,
-                                      int(bool(causal)), float(scale))
+                                      int(bool(causal)), float(scale), int(bool(o_bf16)))
         if rc != 0:
             raise ValueError("oracle_attn_bwd rejected its arguments")
         return dict(dq=dq, dk=dk, dv=dv, o=o, lse=lse, D=D)
 
-    def bwd_sampled(self, q, k, v, do, causal: bool, scale: float, rows, keys):
+    def bwd_sampled(self, q, k, v, do, causal: bool, scale: float, rows, keys, o_bf16: bool = False):
         """dQ of the listed query rows [B,Hq,len(rows),d] and dK/dV of the listed
         keys [B,Hkv,len(keys),d]; every row still runs its full softmax."""
         q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
@@ -138,10 +143,18 @@ class Oracle:
         rc = self.lib.oracle_attn_bwd_sampled(_ptr(q), _ptr(k), _ptr(v), _ptr(do), rows.ctypes.data_as(_i64p),
                                               len(rows), keys.ctypes.data_as(_i64p), len(keys), _ptr(dq),
                                               _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, d, int(bool(causal)),
-                                              float(scale))
+                                              float(scale), int(bool(o_bf16)))
         if rc != 0:
             raise ValueError("oracle_attn_bwd_sampled rejected its arguments")
         return dict(dq=dq, dk=dk, dv=dv)
+
+    def round_bf16(self, x):
+        """Round float64 values to the nearest bfloat16 value (ties to even)."""
+        x = _c64(x)
+        y = np.empty_like(x)
+        if self.lib.oracle_round_bf16(_ptr(x), _ptr(y), x.size) != 0:
+            raise ValueError("oracle_round_bf16 rejected its arguments")
+        return y
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
@@ -161,12 +174,12 @@ def fwd(q, k, v, causal, scale, qpos=None):
     return default().fwd(q, k, v, causal, scale, qpos)
 
 
-def bwd(q, k, v, do, causal, scale):
-    return default().bwd(q, k, v, do, causal, scale)
+def bwd(q, k, v, do, causal, scale, o_bf16=False):
+    return default().bwd(q, k, v, do, causal, scale, o_bf16)
 
 
-def bwd_sampled(q, k, v, do, causal, scale, rows, keys):
-    return default().bwd_sampled(q, k, v, do, causal, scale, rows, keys)
+def bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16=False):
+    return default().bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16)
 
 
 def probs(q, k, causal, scale, qpos=None):

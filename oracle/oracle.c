@@ -36,6 +36,12 @@
  *   dQ_i  = s sum_j dS_ij k_j
  *   dK_j  = s sum_{heads in group} sum_i dS_ij q_i
  *   dV_j  =   sum_{heads in group} sum_i P_ij dO_i
+ * D_i is the row dot of dO with the forward's output. The backward's caller
+ * hands in O as the forward stored it, and the interface stores O in bfloat16.
+ * The backward functions therefore take a flag, o_bf16. When it is set, D_i is
+ * formed from O_i rounded to bfloat16 (round to nearest, ties to even),
+ * which models that storage step. When it is clear, D_i uses the exact fp64
+ * O_i. Everything else stays exact fp64 in both modes.
  *
  * Layout: every tensor is contiguous [B, H, N, d] float64 (d fastest);
  * LSE and D are [B, Hq, N]. Functions return 0, or -1 on bad arguments or
@@ -69,6 +75,18 @@ static double dot(const double* a, const double* b, int d) {
     double acc = 0.0;
     for (int c = 0; c < d; ++c) acc += a[c] * b[c];
     return acc;
+}
+
+/* x rounded to the nearest bfloat16 value (8 significant bits), ties to even.
+ * frexp gives x = m * 2^e with 0.5 <= |m| < 1, so m * 2^8 holds the 8 kept
+ * bits left of the point; nearbyint rounds it to nearest, ties to even, in the
+ * default rounding mode. Normal bfloat16 range only (the attention outputs
+ * here are far from its limits). */
+static double round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    const double m = frexp(x, &e);
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);
 }
 
 static int is_visible(int64_t pos_i, int j, int causal) {
@@ -188,9 +206,10 @@ int oracle_attn_probs(const double* q, const double* k, double* p, int B, int Hq
 static void bwd_row(const double* qi, const double* doi, const double* kh, const double* vh,
                     int N, int d, int i, int causal, double scale, double* S, double* P,
                     double* oi, double* lse_i, double* D_i, double* dqi, const int* slot,
-                    double* dk_acc, double* dv_acc) {
+                    double* dk_acc, double* dv_acc, int o_bf16, double* ostore) {
     attend_row(qi, kh, vh, N, d, i, causal, scale, S, P, oi, lse_i);
-    const double Di = dot(doi, oi, d);
+    for (int c = 0; c < d; ++c) ostore[c] = o_bf16 ? round_bf16(oi[c]) : oi[c];
+    const double Di = dot(doi, ostore, d);
     *D_i = Di;
     if (dqi)
         for (int c = 0; c < d; ++c) dqi[c] = 0.0;
@@ -230,7 +249,7 @@ static void bwd_row(const double* qi, const double* doi, const double* kh, const
 static int bwd_impl(const double* q, const double* k, const double* v, const double* dout,
                     const int64_t* rows, int nrows, const int64_t* keys, int nkeys, double* dq,
                     double* dk, double* dv, double* o_out, double* lse_out, double* D_out, int B,
-                    int Hq, int Hkv, int N, int d, int causal, double scale) {
+                    int Hq, int Hkv, int N, int d, int causal, double scale, int o_bf16) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || check_shape(B, Hq, Hkv, N, N, d)) return -1;
     if (!rows) nrows = N;
     if (!keys) nkeys = N;
@@ -259,7 +278,7 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
         }
     }
     double* priv = (double*)calloc((size_t)nt * 2 * kout + 1, sizeof(double));
-    double* rowbuf = (double*)malloc(sizeof(double) * (size_t)nt * (2 * (size_t)N + d));
+    double* rowbuf = (double*)malloc(sizeof(double) * (size_t)nt * (2 * (size_t)N + 2 * (size_t)d));
     if (!priv || !rowbuf) { free(priv); free(rowbuf); free(slot); free(rslot); return -1; }
     for (int b = 0; b < B; ++b) {
         for (int hk = 0; hk < Hkv; ++hk) {
@@ -273,15 +292,17 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
                 const int h = hk * G + g;
                 const size_t ri = (((size_t)b * Hq + h) * N + i);
                 const int t = thread_id();
-                double* S = rowbuf + (size_t)t * (2 * (size_t)N + d);
+                double* S = rowbuf + (size_t)t * (2 * (size_t)N + 2 * (size_t)d);
                 double* P = S + N;
                 double* oi = P + N;
+                double* ostore = oi + d;
                 double* dqi = NULL;
                 if (!rows) dqi = dq + ri * d;
                 else if (rslot[i] >= 0) dqi = dq + (((size_t)b * Hq + h) * nrows + rslot[i]) * d;
                 double lse_i, D_i;
                 bwd_row(q + ri * d, dout + ri * d, kh, vh, N, d, i, causal, scale, S, P, oi, &lse_i,
-                        &D_i, dqi, slot, priv + (size_t)t * 2 * kout, priv + (size_t)t * 2 * kout + kout);
+                        &D_i, dqi, slot, priv + (size_t)t * 2 * kout, priv + (size_t)t * 2 * kout + kout,
+                        o_bf16, ostore);
                 if (o_out) memcpy(o_out + ri * d, oi, sizeof(double) * d);
                 if (lse_out) lse_out[ri] = lse_i;
                 if (D_out) D_out[ri] = D_i;
@@ -303,23 +324,31 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
     return 0;
 }
 
-/* Full backward: every dQ row and every dK/dV key, plus O, LSE and D (optional). */
+/* Full backward: every dQ row and every dK/dV key, plus O, LSE and D (optional).
+ * o_bf16: form D from O rounded to bfloat16 (see the header comment). */
 int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
                     double* dq, double* dk, double* dv, double* o_out, double* lse_out,
                     double* D_out, int B, int Hq, int Hkv, int N, int d, int causal,
-                    double scale) {
+                    double scale, int o_bf16) {
     return bwd_impl(q, k, v, dout, NULL, 0, NULL, 0, dq, dk, dv, o_out, lse_out, D_out, B, Hq, Hkv,
-                    N, d, causal, scale);
+                    N, d, causal, scale, o_bf16);
 }
 
 /* Sampled backward: dQ of the listed rows, dK/dV of the listed keys. */
 int oracle_attn_bwd_sampled(const double* q, const double* k, const double* v, const double* dout,
                             const int64_t* rows, int nrows, const int64_t* keys, int nkeys,
                             double* dq_rows, double* dk_keys, double* dv_keys, int B, int Hq,
-                            int Hkv, int N, int d, int causal, double scale) {
+                            int Hkv, int N, int d, int causal, double scale, int o_bf16) {
     if (!rows || !keys) return -1;
     return bwd_impl(q, k, v, dout, rows, nrows, keys, nkeys, dq_rows, dk_keys, dv_keys, NULL, NULL,
-                    NULL, B, Hq, Hkv, N, d, causal, scale);
+                    NULL, B, Hq, Hkv, N, d, causal, scale, o_bf16);
+}
+
+/* The bfloat16 rounding the stored-O mode applies, exposed so tests can pin it. */
+int oracle_round_bf16(const double* x, double* y, int64_t n) {
+    if ((!x || !y) && n > 0) return -1;
+    for (int64_t t = 0; t < n; ++t) y[t] = round_bf16(x[t]);
+    return 0;
 }
 
 int oracle_num_threads(void) { return max_threads(); }

@@ -364,6 +364,62 @@ def pin_sampled_backward(orc):
         _close(smp["dv"], full["dv"][:, :, keys], what="sampled dV")
 
 
+def pin_round_bf16(orc):
+    """The oracle's bfloat16 rounding agrees with torch's float32 -> bfloat16
+    conversion (round to nearest, ties to even) on random values, on values
+    exactly halfway between two bfloat16 neighbours, and on powers of two."""
+    import torch
+    rng = _rng(170)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-20, 20, 20000))).astype(np.float32)
+    base = x.view(np.uint32) & np.uint32(0xFFFF0000)
+    ties = (base | np.uint32(0x8000)).view(np.float32)          # exactly half a bf16 ulp above base
+    pow2 = np.exp2(np.arange(-30, 30)).astype(np.float32)
+    for arr in (x, ties, -ties, pow2):
+        want = torch.from_numpy(arr).to(torch.bfloat16).to(torch.float64).numpy()
+        got = orc.round_bf16(arr.astype(np.float64))
+        assert np.array_equal(got, want), "bf16 rounding disagrees with torch"
+    assert orc.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    assert orc.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+
+
+def pin_stored_o_mode(orc):
+    """Forming D from O rounded to bfloat16 changes D to rowsum(dO * bf16(O)) and
+    nothing else. dS is linear in D, so with dD = D_stored - D_exact:
+    dQ_i moves by -s dD_i sum_j P_ij k_j, dK_j by -s sum_i P_ij dD_i q_i, dV
+    not at all. When O is already a bfloat16 value (constant bf16 V), both
+    modes agree exactly."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 4, 2, 13, 6
+    G = Hq // Hkv
+    q, do = _rand((B, Hq, N, d), 180, 1.3), _rand((B, Hq, N, d), 183)
+    k, v = _rand((B, Hkv, N, d), 181, 1.3), _rand((B, Hkv, N, d), 182)
+    s = 0.6
+    for causal in (False, True):
+        ex = orc.bwd(q, k, v, do, causal, s, o_bf16=False)
+        st = orc.bwd(q, k, v, do, causal, s, o_bf16=True)
+        o_b = torch.from_numpy(ex["o"]).to(torch.bfloat16).to(torch.float64).numpy()
+        _close(st["D"], (do * o_b).sum(-1), what="stored-O D")
+        _close(st["o"], ex["o"], what="stored-O mode keeps the exact O output")
+        dD = st["D"] - ex["D"]
+        P = orc.probs(q, k, causal, s)
+        kr, qr = np.repeat(k, G, axis=1), q
+        dq_shift = -s * dD[..., None] * (P @ kr)
+        dk_shift = (-s * np.einsum("bhij,bhi,bhic->bhjc", P, dD, qr)).reshape(B, Hkv, G, N, d).sum(2)
+        _close(st["dq"], ex["dq"] + dq_shift, tol=1e-11, what="stored-O dQ shift")
+        _close(st["dk"], ex["dk"] + dk_shift, tol=1e-11, what="stored-O dK shift")
+        _close(st["dv"], ex["dv"], what="stored-O dV unchanged")
+        rows = np.array([0, 5, 12], dtype=np.int64)
+        keys = np.array([12, 3], dtype=np.int64)
+        sm = orc.bwd_sampled(q, k, v, do, causal, s, rows, keys, o_bf16=True)
+        _close(sm["dq"], st["dq"][:, :, rows], what="stored-O sampled dQ")
+        _close(sm["dk"], st["dk"][:, :, keys], what="stored-O sampled dK")
+    vb = np.broadcast_to(orc.round_bf16(_rand((d,), 184)), (B, Hkv, N, d)).copy()
+    a = orc.bwd(q, k, vb, do, True, s, o_bf16=False)
+    b = orc.bwd(q, k, vb, do, True, s, o_bf16=True)
+    for key in ("dq", "dk", "dv", "D"):
+        _close(a[key], b[key], tol=1e-13, what=f"bf16-exact O: {key}")
+
+
 PINS = [
     pin_one_token,
     pin_two_tokens,
@@ -382,4 +438,6 @@ PINS = [
     pin_finite_differences,
     pin_online_recurrence,
     pin_sampled_backward,
+    pin_round_bf16,
+    pin_stored_o_mode,
 ]

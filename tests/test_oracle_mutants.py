@@ -26,7 +26,7 @@ MUTANTS = {
     "LSE drops max": ("*lse_i = m + log(l);", "*lse_i = log(l);"),
     "fwd GQA map modulo": ("const int hk = h / G;\n        const double* kh", "const int hk = h % Hkv;\n        const double* kh"),
     "fwd row position ignored": ("qpos ? qpos[i] : i, causal, scale, S, P,", "qpos ? qpos[i] : 0, causal, scale, S, P,"),
-    "D uses dO.dO": ("const double Di = dot(doi, oi, d);", "const double Di = dot(doi, doi, d);"),
+    "D uses dO.dO": ("const double Di = dot(doi, ostore, d);", "const double Di = dot(doi, doi, d);"),
     "D term dropped": ("const double dSij = P[j] * (dPij - Di);", "const double dSij = P[j] * dPij;"),
     "dS sign flipped": ("const double dSij = P[j] * (dPij - Di);", "const double dSij = P[j] * (Di - dPij);"),
     "dP uses K": ("const double dPij = dot(doi, vh + (size_t)j * d, d);", "const double dPij = dot(doi, kh + (size_t)j * d, d);"),
@@ -37,6 +37,9 @@ MUTANTS = {
     "bwd head in group wrong": ("const int h = hk * G + g;", "const int h = hk + g * Hkv;"),
     "sampled key slot wrong": ("slot[keys[t]] = t;", "slot[keys[t]] = 0;"),
     "sampled row slot wrong": ("rslot[rows[t]] = t;", "rslot[rows[t]] = nrows - 1 - t;"),
+    "stored O not rounded": ("ostore[c] = o_bf16 ? round_bf16(oi[c]) : oi[c];", "ostore[c] = oi[c];"),
+    "stored O rounded to 9 bits": ("ldexp(nearbyint(ldexp(m, 8)), e - 8)", "ldexp(nearbyint(ldexp(m, 9)), e - 9)"),
+    "stored O rounding truncates": ("ldexp(nearbyint(ldexp(m, 8)), e - 8)", "ldexp(trunc(ldexp(m, 8)), e - 8)"),
     "bwd reduction drops a thread": ("for (int t = 0; t < nt; ++t) {\n                const double* dk_t", "for (int t = 1; t < nt; ++t) {\n                const double* dk_t"),
 }
 
