@@ -1,7 +1,8 @@
 """Benchmark: causal bf16 exact attention, forward + backward, on one MI355X.
 
 One step is the whole hot path over one batch of synthetic input: the forward
-kernel (O and LSE), then the three backward kernels (row dot, dK/dV, dQ). The
+kernel (O and LSE), then the backward: preparation (two small kernels), dQ
+(which also forms the exact row dot D), dK/dV. The
 workload is B=2, Hq=32, Hkv=8 (grouped-query attention), N=16384, d=128,
 causal, bf16 inputs ~ N(0, 1) from a fixed seed, dO ~ N(0, 1).
 
@@ -32,7 +33,7 @@ WORKLOAD = "gqa16k"
 # MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP per clock per CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 PEAK_HBM_GBS = 8000.0
-KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+KERNELS = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv")
 
 
 def pair_count(w) -> float:
@@ -46,8 +47,10 @@ def algorithmic(w) -> dict:
     fwd:      S = QK^T and O += PV, 4*d FLOP per visible pair.
     bwd_dkdv: S (rebuilt), dP = dO V^T, dV += P^T dO, dK += dS^T Q, 8*d FLOP per pair.
     bwd_dq:   dQ += dS K, 2*d FLOP per pair (its S and dP are a second evaluation
-              of the same products, so they are not counted again).
-    bwd_pre:  reads O and dO (bf16) and LSE, writes D and the log2-scaled LSE.
+              of the same products, and its P K product only corrects dQ for
+              the exact row dot, so neither is counted again).
+    bwd_pre:  reads Q, K, V, dO (max pass), then Q, K, V, dO, O and LSE, writes the
+              fp16 copies, D and the log2-scaled LSE.
     """
     heads = w.B * w.Hq
     pairs = heads * pair_count(w)
@@ -56,7 +59,8 @@ def algorithmic(w) -> dict:
         "fwd": ("flop", 4 * w.d * pairs),
         "bwd_dkdv": ("flop", 8 * w.d * pairs),
         "bwd_dq": ("flop", 2 * w.d * pairs),
-        "bwd_pre": ("bytes", rows * (2 * 2 * w.d + 4 + 4 + 4)),
+        "bwd_pre": ("bytes", 2 * 2 * (2 * w.B * w.Hq + 2 * w.B * w.Hkv) * w.N * w.d
+                    + rows * (2 * 2 * w.d + 4 + 4 + 4)),
     }
 
 

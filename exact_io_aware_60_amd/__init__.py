@@ -24,7 +24,7 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
             "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq")
-BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq")
+BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -88,7 +88,7 @@ def bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, wo
 
 def bwd_stage_raw(stage: int, q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
                   workspace_bytes, stream=None) -> int:
-    """One backward stage (0 = preprocess, 1 = dkdv, 2 = dq) on raw addresses; returns the status."""
+    """One backward stage (0 = preprocess, 1 = dq, 2 = dkdv) on raw addresses; returns the status."""
     fn = getattr(lib(), BWD_STAGES[stage])
     return fn(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), float(scale), workspace,
               workspace_bytes, stream)

@@ -85,7 +85,7 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal) {
     (void)causal;
     if (check_shape(B, Hq, Hkv, N, d) != FA_OK) return 0;
-    return fa::bwd_workspace_bytes((long long)B * Hq * N);
+    return fa::bwd_workspace_layout(B, Hq, Hkv, N, d).total;
 }
 
 }  // extern "C"
@@ -119,9 +119,17 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
     p.dq = static_cast<uint16_t*>(dq);
     p.dk = static_cast<uint16_t*>(dk);
     p.dv = static_cast<uint16_t*>(dv);
-    p.delta = static_cast<float*>(workspace);
-    p.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      fa::bwd_workspace_bytes((long long)B * Hq * N) / 2);
+    const fa::BwdWorkspace w = fa::bwd_workspace_layout(B, Hq, Hkv, N, d);
+    char* ws = static_cast<char*>(workspace);
+    p.delta = reinterpret_cast<float*>(ws + w.delta);
+    p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
+    p.q16 = reinterpret_cast<uint16_t*>(ws + w.q16);
+    p.k16 = reinterpret_cast<uint16_t*>(ws + w.k16);
+    p.v16 = reinterpret_cast<uint16_t*>(ws + w.v16);
+    p.do16 = reinterpret_cast<uint16_t*>(ws + w.do16);
+    p.part = reinterpret_cast<uint32_t*>(ws + w.part);
+    p.scales = reinterpret_cast<float*>(ws + w.scales);
+    p.npart = w.npart;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d; p.G = Hq / Hkv;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
@@ -159,7 +167,7 @@ int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void*
                         int N, int d, int causal, float scale, void* workspace,
                         size_t workspace_bytes, void* stream) {
     return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
-                      workspace_bytes, stream, 1, 1);
+                      workspace_bytes, stream, 2, 2);
 }
 
 int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -167,7 +175,7 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
                       int d, int causal, float scale, void* workspace, size_t workspace_bytes,
                       void* stream) {
     return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, workspace,
-                      workspace_bytes, stream, 2, 2);
+                      workspace_bytes, stream, 1, 1);
 }
 
 const char* flash_attn_strerror(int status) {

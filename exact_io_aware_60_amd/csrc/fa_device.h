@@ -38,6 +38,14 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// The same product on fp16 operands (v_mfma_f32_32x32x16_f16: identical
+// operand and accumulator layouts, identical rate).
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+__device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
@@ -104,6 +112,13 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     const f32x2v v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));  // v_cvt_pk_bf16_f32
+}
+
+// Round-to-nearest-even float -> fp16 pair packed into one dword (v_cvt_pk_f16_f32).
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+    const f32x2v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
 }
 
 // Swizzled position of 16-byte chunk `c` of row `row` in an LDS tile of

@@ -19,28 +19,45 @@ struct FwdParams {
 };
 
 struct BwdParams {
-    const uint16_t* q;
+    const uint16_t* q;   // bf16 inputs, as in FwdParams
     const uint16_t* k;
     const uint16_t* v;
     const uint16_t* o;
     const float* lse;
     const uint16_t* dout;
-    uint16_t* dq;
+    uint16_t* dq;        // bf16 outputs
     uint16_t* dk;
     uint16_t* dv;
-    float* delta;        // fp32 [B, Hq, N] workspace: rowsum(dout * o)
-    float* lse2;         // fp32 [B, Hq, N] workspace: lse * log2(e)
+    // Workspace (device memory the caller provides; layout in bwd_workspace_layout):
+    float* delta;        // fp32 [B, Hq, N]: rowsum(dout * o), times the dS scale
+    float* lse2;         // fp32 [B, Hq, N]: lse * log2(e)
+    uint16_t* q16;       // fp16 copies of q, k, v, dout, each scaled by a power of two
+    uint16_t* k16;
+    uint16_t* v16;
+    uint16_t* do16;
+    uint32_t* part;      // [4][npart] partial max |x| of q, k, v, dout (bf16 magnitude bits)
+    float* scales;       // [8] derived constants, written by the preparation kernel
+    int npart;           // workgroups of the max-reduction kernel
     int B, Hq, Hkv, N, d, G;
     int causal;
     float scale;
     float scale_log2;
 };
 
+// Byte offsets of the backward workspace arrays; every array starts on a
+// 256-byte boundary.
+struct BwdWorkspace {
+    size_t delta, lse2, q16, k16, v16, do16, part, scales, total;
+    int npart;
+};
+BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d);
+
 // Launchers (defined next to their kernels). They only enqueue work on the
 // stream; they return the HIP status of the launch.
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
-// One backward stage: 0 = row dot D (and log2-scaled LSE), 1 = dK/dV, 2 = dQ.
+// One backward stage: 0 = preparation (scales, fp16 copies, row dot D,
+// log2-scaled LSE), 1 = dK/dV, 2 = dQ.
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream);
 
 // Launch geometry, exposed for logging and tests of the host logic.
@@ -52,9 +69,5 @@ struct Geometry {
     int lds_bytes;    // LDS per workgroup
 };
 Geometry fwd_geometry(int B, int Hq, int N, int d, int causal);
-
-// Bytes of backward workspace: D and the log2-scaled LSE, one fp32 each per
-// query row, each array starting on a 256-byte boundary.
-size_t bwd_workspace_bytes(long long rows);
 
 }  // namespace fa

@@ -77,9 +77,12 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
- * Bytes of device workspace flash_attn_bwd needs for these arguments: two fp32
- * arrays of one value per query row, D = rowsum(dout * o) and LSE * log2(e),
- * each rounded up to 256 bytes. Returns 0 for shapes the backward rejects.
+ * Bytes of device workspace flash_attn_bwd needs for these arguments, or 0 for
+ * shapes the backward rejects. The workspace holds two fp32 values per query
+ * row (D = rowsum(dout * o) and LSE * log2(e)), fp16 copies of q, k, v and
+ * dout scaled by powers of two (the operands of the backward's products), and
+ * a few KiB of reduction scratch: about 2 * (|q| + |k| + |v| + |dout|) bytes
+ * plus 8 bytes per query row.
  */
 size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal);
 
@@ -95,9 +98,14 @@ size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int c
  *   workspace               scratch, device memory of workspace_bytes >=
  *                           flash_attn_bwd_workspace_size(...); contents on
  *                           entry are ignored and on return are unspecified
- * Outputs must not overlap inputs or each other. Runs three kernels in order on
- * `stream`: the row dot D, then dK/dV, then dQ. Deterministic: the same inputs
- * give bit-identical outputs (no atomics).
+ * Outputs must not overlap inputs or each other. Runs four kernels in order on
+ * `stream`: max |x| of q, k, v, dout; preparation (scaled fp16 copies, the row
+ * dot D from o, the log2-scaled LSE); dQ, which also forms the exact row dot
+ * D_i = sum_j P_ij dP_ij from the rebuilt probabilities, corrects its own
+ * result with it and stores it; dK/dV, which uses that exact D. Deterministic:
+ * the same inputs give bit-identical outputs (no atomics). Inputs must be
+ * finite, with max|dout| * max|v| < 2^100 (the dS scale is derived from their
+ * product).
  */
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -105,15 +113,16 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The three stages of flash_attn_bwd, one kernel each, with its argument list
- * and checks. flash_attn_bwd is exactly preprocess, dkdv, dq in that order on
- * one stream. They exist so that a caller can time or schedule the kernels
- * separately (for example dkdv and dq on two streams once preprocess is done).
- *   preprocess  reads o, dout, lse; writes the workspace
- *   dkdv        reads q, k, v, dout and the workspace; writes dk, dv
- *   dq          reads q, k, v, dout and the workspace; writes dq
- * dkdv and dq need the workspace that preprocess wrote for the same o, dout
- * and lse; pointers a stage does not use must still be valid and aligned.
+ * The three stages of flash_attn_bwd, with its argument list and checks.
+ * flash_attn_bwd is exactly preprocess (two kernels), dq, dkdv in that order
+ * on one stream. They exist so that a caller can time or schedule the kernels
+ * separately.
+ *   preprocess  reads q, k, v, o, dout, lse; writes the workspace
+ *   dq          reads the workspace (and lse); writes dq and the exact row dot
+ *               into the workspace
+ *   dkdv        reads the workspace; writes dk, dv
+ * Each stage needs the workspace the previous stages wrote for the same
+ * inputs; pointers a stage does not use must still be valid and aligned.
  */
 int flash_attn_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
                               const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -1,7 +1,8 @@
 """GPU backward pass against the fp64 oracle on identical seeded bf16 inputs.
 
 The GPU backward is fed the GPU forward's own O and LSE, as a caller would; the
-oracle computes everything from the inputs in fp64. Tolerance: max abs error on
+oracle computes everything from the inputs in fp64 (exact D). Tolerance: max
+abs error on
 dQ, dK and dV <= 2e-2 beyond the rounding of the bf16 output (half a bf16 ulp at
 the oracle's value). Small cases are compared element by element on every
 output; full-size workloads on seeded samples of query rows (dQ) and keys
@@ -119,6 +120,32 @@ def test_deterministic(fa):
     b = run_fwd_bwd(fa, inp, True, 0.0883883)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_power_of_two_homogeneity(fa, d):
+    """Scaling inputs by powers of two scales the gradients exactly: the kernels
+    re-derive their fp16 scales, so every intermediate has the same bits.
+    V * 2^12 and dO * 2^-20 give dQ, dK * 2^-8 and dV * 2^-20; Q * 2^9 with
+    K * 2^-9 give dQ * 2^-9 and dK * 2^9."""
+    import torch
+    inp = ai.make_case(1, 4, 2, 700, d, seed=24 + d)
+    say(f"bwd power-of-two homogeneity d={d}")
+    s = 1.0 / math.sqrt(d)
+    base = run_fwd_bwd(fa, inp, True, s)
+
+    def scaled(name, e):
+        x = torch.from_numpy(f64(inp[name]) * 2.0 ** e).to(torch.bfloat16)
+        return x.view(torch.int16).numpy().view(np.uint16)
+
+    inp2 = dict(inp, v=scaled("v", 12), do=scaled("do", -20))
+    dq, dk, dv = run_fwd_bwd(fa, inp2, True, s)
+    assert np.array_equal(dq, base[0] * 2.0 ** -8) and np.array_equal(dk, base[1] * 2.0 ** -8)
+    assert np.array_equal(dv, base[2] * 2.0 ** -20)
+    inp3 = dict(inp, q=scaled("q", 9), k=scaled("k", -9))
+    dq, dk, dv = run_fwd_bwd(fa, inp3, True, s)
+    assert np.array_equal(dq, base[0] * 2.0 ** -9) and np.array_equal(dk, base[1] * 2.0 ** 9)
+    assert np.array_equal(dv, base[2])
 
 
 def test_stages_equal_full_call(fa):
