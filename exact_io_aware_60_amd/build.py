@@ -18,15 +18,19 @@ SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
 # v_*_f32 instruction.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         # keep MFMA accumulators in VGPRs (AGPRs then serve as extra storage);
-         # without it the softmax reads every score back out of AGPRs
-         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
+# Per-source extra flags: MFMA accumulators in VGPRs, so that the softmax and
+# gradient VALU work reads the scores without copies out of AGPRs (AGPRs then
+# serve as extra storage for long-lived values).
+SOURCE_FLAGS = {
+    "fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -154,4 +154,55 @@ __device__ __forceinline__ void unswz(int slot, int& row, int& c) {
     c = (slot % (D / 8)) ^ swz_key<D, MODE>(row);
 }
 
+// ---- padded LDS tiles ----
+// A padded tile stores row r of a [rows x D] 16-bit tile at byte r * STRIDE, so
+// every fragment address is (lane base) + (compile-time offset): no per-read
+// swizzle arithmetic. The padding is chosen for the read pattern:
+//  * row tiles (16-byte reads, 16 lanes = 16 consecutive rows at one column):
+//    STRIDE = 2D + 16, so the 16 rows start 16 bytes apart modulo the 256-byte
+//    bank line and hit distinct banks;
+//  * transposed tiles (ds_read_b64_tr_b16: 32 lanes read 4 consecutive rows x
+//    64 bytes): STRIDE = 2D + 64 (2D is 128 or 256), so the 4 rows land on
+//    distinct 64-byte quarters of the bank line.
+template <int D> struct RowPad { static constexpr int STRIDE = 2 * D + 16; };
+template <int D> struct TrPad { static constexpr int STRIDE = 2 * D + 64; };
+
+// Bytes a padded tile of ROWS rows occupies, rounded up to whole 1 KiB blocks
+// (the unit one wave's global->LDS copy writes).
+template <int STRIDE, int ROWS>
+constexpr int padded_tile_bytes() { return (ROWS * STRIDE + 1023) / 1024 * 1024; }
+
+// Copy rows [row0, row0 + ROWS) of a row-major [N x D] 16-bit tensor into a
+// padded tile, with NW waves sharing the work. Block u (1 KiB) is written by one
+// wave instruction: lane i fills 16-byte slot u*64 + i. Slots that fall in the
+// padding, or past the last row, receive a copy of a valid 16-byte piece and are
+// never read. Rows past N read row N-1 (finite data; the kernels mask them).
+template <int D, int STRIDE, int ROWS, int NW>
+__device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ g, int row0, int N,
+                                          FA_LDS uint8_t* __restrict__ tile, int w, int lane) {
+    constexpr int SPR = STRIDE / 16;                       // 16-byte slots per padded row
+    constexpr int NB = padded_tile_bytes<STRIDE, ROWS>() / 1024;
+#pragma unroll
+    for (int u = w; u < NB; u += NW) {
+        const int slot = u * 64 + lane;
+        int row = slot / SPR, c = slot - (slot / SPR) * SPR;
+        if (c >= D / 8 || row >= ROWS) {
+            c = 0;
+            row = row < ROWS ? row : ROWS - 1;
+        }
+        const int gr = row0 + row < N ? row0 + row : N - 1;
+        gload_lds16(g + (size_t)gr * D + c * 8, (FA_LDS uint16_t*)(tile + u * 1024));
+    }
+}
+
+// 16-byte and transposed 8-byte reads at a byte offset into a padded tile.
+__device__ __forceinline__ u32x4 lds_read16b(const FA_LDS uint8_t* base, int byte_off) {
+    return *reinterpret_cast<const FA_LDS u32x4*>(base + byte_off);
+}
+__device__ __forceinline__ u32x2 lds_read_trb(const FA_LDS uint8_t* base, int byte_off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<FA_LDS s16x4*>(const_cast<FA_LDS uint8_t*>(base + byte_off)));
+    return __builtin_bit_cast(u32x2, r);
+}
+
 }  // namespace fa

@@ -8,15 +8,20 @@
 // once, plus the logsumexp m + ln l. No score ever reaches device memory.
 //
 // gfx950 design (prior art on the pages targets A100/H100; these choices are
-// this kernel's own):
-//  * One workgroup = 4 waves = 256 query rows. Each wave owns 64 rows, and one
-//    wave runs per SIMD with up to 512 registers. 64 rows per wave halve the LDS
-//    bytes per MFMA flop against 32-row waves. That matters because every wave
-//    reads the whole K and V tile out of LDS.
-//  * Keys are streamed in tiles of 64. K and V tiles are double-buffered in LDS
-//    (64 KiB at d = 128). The next tile is loaded into registers while the
-//    current one is computed, then written to the other buffer. One barrier per
-//    tile.
+// this kernel's own, backed by measurements on MI355X):
+//  * The softmax is vector-ALU work that must overlap the MFMAs. One wave per
+//    SIMD hides only about 2 VALU instructions under each 32x32x16 MFMA; two
+//    waves per SIMD hide most of them. So a workgroup is 8 waves (2 per SIMD),
+//    each owning 32 query rows (256 rows per workgroup, at most 256 registers
+//    per wave).
+//  * Keys are streamed in tiles of 64 through LDS with direct global->LDS
+//    loads: K in 3 buffers, V in 2, one barrier per tile. Tiles are stored with
+//    padded rows (fa_device.h), which keeps every read bank-conflict-free and
+//    makes every fragment address a lane base plus a constant.
+//  * Inside each wave the work runs in chunks of 32 keys, software-pipelined by
+//    hand: the MFMAs for the scores of chunk c+1 are interleaved with the exp /
+//    sum / pack work of chunk c, and the P.V MFMAs of chunk c with the row max
+//    of chunk c+1.
 //  * The scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16. A lane then holds one query row and 16 keys per
 //    32 x 32 block. The row max needs a single cross-lane step (lane l with
@@ -24,11 +29,11 @@
 //    bf16, the B operand of O^T += V^T P^T with no data movement. V^T is read
 //    with ds_read_b64_tr_b16 in the matching key order.
 //  * exp2 with scale * log2(e) folded into one FMA. The reference max moves
-//    only when a tile's max exceeds it by more than 2^8; otherwise the rescale
+//    only when a chunk's max exceeds it by more than 2^8; otherwise the rescale
 //    of O is skipped. Any reference value cancels in O / l and m + ln l, so the
 //    result is the same (the fp64 model in oracle/online.py checks this).
-//  * Causal: tiles above a wave's diagonal are skipped; the diagonal tile and
-//    the ragged last tile are masked element-wise. Workgroups run heaviest
+//  * Causal: chunks above a wave's diagonal are skipped; the diagonal chunk and
+//    the ragged last chunk are masked element-wise. Workgroups run heaviest
 //    q-tile first (longest-processing-time order). Workgroups of one head set
 //    map to one XCD, so their K/V re-reads hit the same L2.
 #include "fa_device.h"
@@ -38,10 +43,21 @@ namespace fa {
 namespace {
 
 constexpr int kBM = 256;       // query rows per workgroup
-constexpr int kWM = 64;        // query rows per wave
-constexpr int kBN = 64;        // keys per tile
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kWM = 32;        // query rows per wave
+constexpr int kBN = 64;        // keys per LDS tile
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr float kTau = 8.0f;   // lazy-max threshold, log2 units
+
+template <int D>
+struct FwdCfg {
+    static constexpr int DS = D / 16, DB = D / 32;
+    static constexpr int SK = RowPad<D>::STRIDE;                 // K rows: 16-byte reads
+    static constexpr int SV = TrPad<D>::STRIDE;                  // V rows: transposed reads
+    static constexpr int KT = padded_tile_bytes<SK, kBN>();
+    static constexpr int VT = padded_tile_bytes<SV, kBN>();
+    static constexpr int LDS = 3 * KT + 2 * VT;
+};
 
 // Workgroup id -> (rank, bh). Workgroups are handed to the 8 XCDs round-robin,
 // so when the head count is a multiple of 8 each XCD gets a contiguous block of
@@ -57,219 +73,297 @@ __device__ __forceinline__ void unmap_block(int bid, int nbh, int& rank, int& bh
     }
 }
 
-// One key tile for one wave: S^T = K Q^T, mask, online-softmax update, O^T += V^T P^T.
-// `masked` (uniform over the wave) is set for the diagonal tile under the causal
-// mask and for the ragged last tile. Masked scores become -inf; with a positive
-// scale_log2 (the host keeps it >= 1e-30) they turn into exact zeros.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_tile(const FA_LDS uint16_t* Kt, const FA_LDS uint16_t* Vt,
-                                         const u32x4 (&qf)[2][D / 16], f32x16 (&o)[D / 32][2],
-                                         float (&m)[2], float (&l)[2], bool masked, int key0, int r0,
-                                         int N, float sl2, int lane) {
-    constexpr int DS = D / 16, DB = D / 32;
-    const int l32 = lane & 31, hh = lane >> 5;
+// ---- per-wave pieces of one 32-key chunk (32 query rows per wave) ----
+// A chunk is half h of a 64-key tile. Scores S^T = K Q^T: lane holds query
+// column l32 and keys (i/4)*8 + hh*4 + i%4 of register i.
+//
+// Lane bases (bytes): kbase = l32 * SK + hh * 16 for K fragments;
+// vbase = ((lane & 15) >> 2 + 4 * hh) * SV + ((g & 1) * 16 + 4 * (lane & 3)) * 2
+// for V^T fragments, g = lane >> 4.
 
-    f32x16 s[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = zero16();
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-            const u32x4 a = lds_read16(Kt, swz<D, 0>(kb * 32 + l32, ds * 2 + hh));
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mfma32(a, qf[qb][ds], s[kb][qb]);
-        }
-
-    if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-                    const int qrow = r0 + qb * 32 + l32;
-                    if (key >= N || (CAUSAL && key > qrow)) s[kb][qb][i] = -INFINITY;
-                }
-    }
-
-    // Row max of this tile, in log2 units; every active tile has a visible key per row.
-    float mc[2];
-    bool need[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float mx = s[0][qb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-        mx = fmaxf(mx, swap_half(mx));
-        mc[qb] = mx * sl2;
-        need[qb] = mc[qb] > m[qb] + kTau;
-    }
-    if (__ballot(need[0] || need[1])) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float mn = need[qb] ? mc[qb] : m[qb];
-            const float alpha = fast_exp2(m[qb] - mn);
-            l[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[db][qb][i] *= alpha;
-            m[qb] = mn;
-        }
-    }
-
-    // P~ = exp2(scale*log2e*S - m), row sums, and the bf16 B operand of the next product.
-    u32x4 pp[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float ls = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float x = fast_exp2(fmaf(s[kb][qb][i], sl2, -m[qb]));
-                s[kb][qb][i] = x;
-                ls += x;
-            }
-        l[qb] += ls;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                pp[qb][kc][t] = pack_bf16(s[kc >> 1][qb][(kc & 1) * 8 + 2 * t],
-                                          s[kc >> 1][qb][(kc & 1) * 8 + 2 * t + 1]);
-    }
-
-    // O^T += V^T P^T. k slot s of chunk kc is key kc*16 + (s/4)*8 + hh*4 + s%4.
-    const int g = lane >> 4;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int dcol = db * 32 + (g & 1) * 16 + 4 * (lane & 3);
-            const int krow = kc * 16 + (g >> 1) * 4 + ((lane & 15) >> 2);
-            const u32x2 t0 = lds_read_tr(Vt, swz<D, 1>(krow, dcol >> 3) + (dcol & 7));
-            const u32x2 t1 = lds_read_tr(Vt, swz<D, 1>(krow + 8, dcol >> 3) + (dcol & 7));
-            const u32x4 a = cat(t0, t1);
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma32(a, pp[qb][kc], o[db][qb]);
-        }
+// K fragment ds of chunk half h: the A operand of the score MFMAs (row l32,
+// d = ds*16 + hh*8 .. +7).
+template <int D>
+__device__ __forceinline__ u32x4 k_frag(const FA_LDS uint8_t* __restrict__ Kt, int kbase, int h, int ds) {
+    return lds_read16b(Kt, kbase + h * 32 * FwdCfg<D>::SK + ds * 32);
 }
 
-template <int D, bool CAUSAL>
+// V^T fragment f = (kc, db) of chunk half h: the A operand of the P.V MFMAs,
+// read transposed so that its k slots run over keys in the order the P operand
+// uses: slot hh*8 + t holds key kc*16 + (t/4)*8 + hh*4 + t%4.
+template <int D>
+__device__ __forceinline__ u32x4 v_frag(const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h, int f) {
+    constexpr int DB = FwdCfg<D>::DB, SV = FwdCfg<D>::SV;
+    const int kc = f / DB, db = f % DB;
+    const int off = vbase + (h * 32 + kc * 16) * SV + db * 64;
+    return cat(lds_read_trb(Vt, off), lds_read_trb(Vt, off + 8 * SV));
+}
+
+template <int D>
+__device__ __forceinline__ f32x16 scores(const FA_LDS uint8_t* __restrict__ Kt, int kbase, int h,
+                                         const u32x4 (&qf)[D / 16]) {
+    f32x16 s = zero16();
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) s = mfma32(k_frag<D>(Kt, kbase, h, ds), qf[ds], s);
+    return s;
+}
+
+// Diagonal or ragged chunk: scores of invisible keys become -inf. With a
+// positive scale_log2 (the host keeps it >= 1e-30) they turn into exact zeros.
+__device__ __forceinline__ void mask_scores(f32x16& s, int key0, int qrow, int N, bool causal, int hh) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int key = key0 + (i >> 2) * 8 + hh * 4 + (i & 3);
+        if (key >= N || (causal && key > qrow)) s[i] = -INFINITY;
+    }
+}
+
+// Row max of a chunk in log2 units. Every chunk a wave computes has a visible
+// key in every row, or the row is past N (finite scores, never stored).
+__device__ __forceinline__ float chunk_max(const f32x16& s, float sl2) {
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    return fmaxf(mx, swap_half(mx)) * sl2;
+}
+
+// Lazy reference max: m moves only when a chunk's max exceeds it by more than
+// kTau (log2 units); O and l are then rescaled by 2^(m_old - m_new). Any
+// reference cancels in O / l and m + ln l, so the result is unchanged.
+template <int D>
+__device__ __forceinline__ void maybe_rescale(float mc, float& m, float& l, f32x16 (&o)[D / 32]) {
+    const bool need = mc > m + kTau;
+    if (__ballot(need)) {
+        const float mn = need ? mc : m;
+        const float alpha = fast_exp2(m - mn);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        m = mn;
+    }
+}
+
+// P~ = exp2(S*sl2 - m) for pack pi = 0..7 of a chunk (16-key half kc = pi / 4,
+// dword t = pi % 4): registers kc*8 + 2t and +1, rounded to a bf16 pair, which
+// is k slot pair (2t, 2t+1) of the P^T operand of half kc.
+__device__ __forceinline__ void exp_pack_one(const f32x16& s, float m, float sl2, int pi, float& ls,
+                                             u32x4 (&pp)[2]) {
+    const int kc = pi >> 2, t = pi & 3, i = kc * 8 + 2 * t;
+    const float x0 = fast_exp2(fmaf(s[i], sl2, -m));
+    const float x1 = fast_exp2(fmaf(s[i + 1], sl2, -m));
+    ls += x0 + x1;
+    pp[kc][t] = pack_bf16(x0, x1);
+}
+
+// Softmax and O^T += V^T P^T for one chunk (not pipelined: a wave's last chunk).
+template <int D>
+__device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
+                                           const f32x16& s, float m, float& l, float sl2,
+                                           f32x16 (&o)[D / 32]) {
+    constexpr int DB = D / 32;
+    u32x4 pp[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int pi = 0; pi < 8; ++pi) exp_pack_one(s, m, sl2, pi, ls, pp);
+    l += ls;
+#pragma unroll
+    for (int f = 0; f < 2 * DB; ++f) o[f % DB] = mfma32(v_frag<D>(Vt, vbase, h, f), pp[f / DB], o[f % DB]);
+}
+
+// One pipelined chunk, interleaved by hand. Each step is closed by a scheduling
+// barrier, so the compiler keeps the order written here and only reorders
+// inside a step.
+//   phase 1 (DS steps): scores of the next chunk (one MFMA per K fragment, each
+//            fragment read two steps ahead) with the exp / row sum / bf16 pack
+//            of the current chunk; step r also reads V^T fragment r of the
+//            current chunk, which phase 2 consumes at least DS steps later;
+//   phase 2 (2*DB = DS steps): O^T += V^T P^T of the current chunk with the row
+//            max of the next chunk.
+template <int D>
+__device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict__ Kn, int kbase, int hn,
+                                                const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
+                                                const u32x4 (&qf)[D / 16], const f32x16& sc, f32x16& sn,
+                                                float m, float& l, float sl2, f32x16 (&o)[D / 32],
+                                                float& mc) {
+    constexpr int DS = D / 16, DB = D / 32, NF = 2 * DB;
+    constexpr int PPS = 8 / DS;      // packs per phase-1 step
+    constexpr int EPS = 16 / NF;     // score registers folded into the max per phase-2 step
+    static_assert(NF == DS, "one V^T fragment read per phase-1 step");
+    u32x4 pp[2];
+    u32x4 vf[NF];
+    float ls = 0.f;
+    sn = zero16();
+    u32x4 a0 = k_frag<D>(Kn, kbase, hn, 0);
+    u32x4 a1 = k_frag<D>(Kn, kbase, hn, 1);
+#pragma unroll
+    for (int r = 0; r < DS; ++r) {
+        u32x4 a2 = a1;
+        if (r + 2 < DS) a2 = k_frag<D>(Kn, kbase, hn, r + 2);
+        vf[r] = v_frag<D>(Vt, vbase, h, r);
+        sn = mfma32(a0, qf[r], sn);
+#pragma unroll
+        for (int c = 0; c < PPS; ++c) exp_pack_one(sc, m, sl2, r * PPS + c, ls, pp);
+        asm volatile("" : "+v"(ls));
+        __builtin_amdgcn_sched_barrier(0);
+        a0 = a1;
+        a1 = a2;
+    }
+    l += ls;
+    float mx = sn[0];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        o[f % DB] = mfma32(vf[f], pp[f / DB], o[f % DB]);
+#pragma unroll
+        for (int c = 0; c < EPS; ++c)
+            if (f * EPS + c > 0) mx = fmaxf(mx, sn[f * EPS + c]);
+        asm volatile("" : "+v"(mx));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    mc = fmaxf(mx, swap_half(mx)) * sl2;
+}
+
+// Per-wave state of the forward loop.
+template <int D>
+struct FwdState {
+    u32x4 qf[D / 16];          // Q as the B operand
+    f32x16 o[D / 32];          // O^T accumulators
+    f32x16 sA, sB;             // scores of the current / next chunk (alternating)
+    float m, l, mc;            // reference max, row sum, current chunk's log2 max
+};
+
+// Chunk c = 2j + h. sc holds its scores; the next chunk's go to sn.
+// Kn: the K tile holding the next chunk; Vt: this chunk's V tile.
+template <int D>
+__device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, int h, f32x16& sc, f32x16& sn,
+                                          const FA_LDS uint8_t* __restrict__ Kn,
+                                          const FA_LDS uint8_t* __restrict__ Vt, int kbase, int vbase,
+                                          bool causal, int qrow, int N, int lastc, float sl2, int hh) {
+    if (c > lastc) return;
+    if ((causal && c * 32 + 31 > qrow - (qrow & 31)) || (c * 32 + 32 > N)) {
+        mask_scores(sc, c * 32, qrow, N, causal, hh);
+        st.mc = chunk_max(sc, sl2);
+    }
+    maybe_rescale<D>(st.mc, st.m, st.l, st.o);
+    if (c < lastc)
+        pipelined_chunk<D>(Kn, kbase, h ^ 1, Vt, vbase, h, st.qf, sc, sn, st.m, st.l, sl2, st.o, st.mc);
+    else
+        softmax_pv<D>(Vt, vbase, h, sc, st.m, st.l, sl2, st.o);
+}
+
+// One 64-key tile j: start the copies of K tile j+2 (into Kw) and V tile j+1
+// (into Vw), then compute chunks 2j and 2j+1 from K tiles j, j+1 (Kr0, Kr1)
+// and V tile j (Vr). All five buffers are distinct during the iteration; the
+// __restrict__ qualifiers say so, which lets the compiler see that the LDS
+// reads do not touch the LDS the in-flight global->LDS copies write, so it does
+// not wait for those copies before each read.
+template <int D>
+__device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, const uint16_t* Kg,
+                                              const uint16_t* Vg, FA_LDS uint8_t* __restrict__ Kw,
+                                              FA_LDS uint8_t* __restrict__ Vw,
+                                              const FA_LDS uint8_t* __restrict__ Kr0,
+                                              const FA_LDS uint8_t* __restrict__ Kr1,
+                                              const FA_LDS uint8_t* __restrict__ Vr, int kbase, int vbase,
+                                              bool valid, bool causal, int qrow, int N, int lastc,
+                                              float sl2, int w, int lane) {
+    using C = FwdCfg<D>;
+    if (j + 2 < nt) copy_tile<D, C::SK, kBN, kWaves>(Kg, (j + 2) * kBN, N, Kw, w, lane);
+    if (j + 1 < nt) copy_tile<D, C::SV, kBN, kWaves>(Vg, (j + 1) * kBN, N, Vw, w, lane);
+    if (valid) {
+        const int hh = lane >> 5;
+        fwd_chunk<D>(st, 2 * j, 0, st.sA, st.sB, Kr0, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh);
+        fwd_chunk<D>(st, 2 * j + 1, 1, st.sB, st.sA, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh);
+    }
+}
+
+// The causal flag is a run-time argument: it only changes the tile ranges and
+// the mask of each wave's last chunk, so one instance per head dimension
+// serves both cases.
+template <int D>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
-    constexpr int CPR = D / 8;                   // 16-byte chunks per row
-    constexpr int DS = D / 16, DB = D / 32;
-    constexpr int TILE = kBN * D;                // elements per K or V tile
-    constexpr int LCH = kBN * CPR / kThreads;    // chunks each thread copies per tile
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
-    FA_LDS uint16_t* Ks = (FA_LDS uint16_t*)smem;
-    FA_LDS uint16_t* Vs = Ks + 2 * TILE;
+    using C = FwdCfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+    FA_LDS uint8_t* Ks = (FA_LDS uint8_t*)smem;          // 3 K tiles
+    FA_LDS uint8_t* Vs = Ks + 3 * C::KT;                   // 2 V tiles
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
+    const int l32 = lane & 31, hh = lane >> 5, g = lane >> 4;
     const int N = p.N;
+    const bool causal = p.causal != 0;
     const int nqt = (N + kBM - 1) / kBM;
     int rank, bh;
     unmap_block(blockIdx.x, p.B * p.Hq, rank, bh);
-    const int qt = CAUSAL ? nqt - 1 - rank : rank;
+    const int qt = causal ? nqt - 1 - rank : rank;
     const int b = bh / p.Hq, hq = bh - b * p.Hq, hkv = hq / p.G;
     const uint16_t* Qg = p.q + (size_t)bh * N * D;
     const uint16_t* Kg = p.k + ((size_t)b * p.Hkv + hkv) * N * D;
     const uint16_t* Vg = p.v + ((size_t)b * p.Hkv + hkv) * N * D;
 
     const int q0 = qt * kBM;
-    const int r0 = q0 + w * kWM;
+    const int r0 = q0 + w * kWM;                 // this wave's first query row
+    const int qrow = r0 + l32;                   // this lane's query row
     const int ntk = (N + kBN - 1) / kBN;
-    const int nt = CAUSAL ? min(ntk, (q0 + kBM - 1) / kBN + 1) : ntk;
+    const int nt = causal ? min(ntk, (q0 + kBM - 1) / kBN + 1) : ntk;
     const bool wave_valid = r0 < N;
-    const int wave_last = CAUSAL ? min(ntk - 1, r0 / kBN) : ntk - 1;
+    // last 32-key chunk this wave computes (causal: the diagonal chunk, keys r0 .. r0+31)
+    const int nck = (N + 31) / 32;
+    const int lastc = causal ? min(nck - 1, r0 / 32) : nck - 1;
+    const float sl2 = p.scale_log2;
+    const int kbase = l32 * C::SK + hh * 16;
+    const int vbase = (((lane & 15) >> 2) + 4 * hh) * C::SV + ((g & 1) * 16 + 4 * (lane & 3)) * 2;
 
-    // Copy K/V tile j into LDS buffer `buf`. Thread chunk u fills 16-byte slot
-    // u*256 + tid; the global chunk is the one the swizzle puts there. Rows past
-    // N read row N-1 (finite data, and their scores are masked).
-    auto issue_tile = [&](int j, int buf) {
+    FwdState<D> st;
 #pragma unroll
-        for (int u = 0; u < LCH; ++u) {
-            const int slot = u * kThreads + tid;
-            FA_LDS uint16_t* kdst = Ks + buf * TILE + (u * kThreads + w * 64) * 8;
-            FA_LDS uint16_t* vdst = Vs + buf * TILE + (u * kThreads + w * 64) * 8;
-            int row, c;
-            unswz<D, 0>(slot, row, c);
-            gload_lds16(Kg + (size_t)min(j * kBN + row, N - 1) * D + c * 8, kdst);
-            unswz<D, 1>(slot, row, c);
-            gload_lds16(Vg + (size_t)min(j * kBN + row, N - 1) * D + c * 8, vdst);
-        }
-    };
+    for (int ds = 0; ds < DS; ++ds) st.qf[ds] = gload16(Qg + (size_t)qrow * D + ds * 16 + hh * 8, qrow < N);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) st.o[db] = zero16();
+    st.m = -INFINITY;
+    st.l = 0.f;
+    st.mc = 0.f;
 
-    u32x4 qf[2][DS];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qrow = r0 + qb * 32 + l32;
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-            qf[qb][ds] = gload16(Qg + (size_t)qrow * D + ds * 16 + hh * 8, qrow < N);
-    }
-
-    f32x16 o[DB][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) o[db][qb] = zero16();
-    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
-
-    issue_tile(0, 0);
+    // K tiles 0, 1 and V tile 0 before the loop.
+    copy_tile<D, C::SK, kBN, kWaves>(Kg, 0, N, Ks, w, lane);
+    if (nt > 1) copy_tile<D, C::SK, kBN, kWaves>(Kg, kBN, N, Ks + C::KT, w, lane);
+    copy_tile<D, C::SV, kBN, kWaves>(Vg, 0, N, Vs, w, lane);
     wait_vmem();
     __syncthreads();
+
+    if (wave_valid) {
+        st.sA = scores<D>(Ks, kbase, 0, st.qf);
+        st.mc = chunk_max(st.sA, sl2);
+    }
     for (int j = 0; j < nt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nt) issue_tile(j + 1, buf ^ 1);
-        if (wave_valid && j <= wave_last) {
-            const int key0 = j * kBN;
-            const bool masked = (CAUSAL && key0 + kBN - 1 > r0) || (key0 + kBN > N);
-            fwd_tile<D, CAUSAL>(Ks + buf * TILE, Vs + buf * TILE, qf, o, m, l, masked, key0, r0, N,
-                                p.scale_log2, lane);
-        }
+        fwd_iteration<D>(st, j, nt, Kg, Vg, Ks + ((j + 2) % 3) * C::KT, Vs + ((j + 1) & 1) * C::VT,
+                         Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT, Vs + (j & 1) * C::VT, kbase,
+                         vbase, wave_valid, causal, qrow, N, lastc, sl2, w, lane);
         wait_vmem();
         __syncthreads();
     }
 
-    if (wave_valid) {
-        uint16_t* Og = p.o + (size_t)bh * N * D;
-        float* Lg = p.lse + (size_t)bh * N;
+    if (wave_valid && qrow < N) {
+        uint16_t* Og = p.o + (size_t)bh * N * D + (size_t)qrow * D;
+        const float lt = st.l + swap_half(st.l);
+        const float inv = 1.f / lt;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const float lt = l[qb] + swap_half(l[qb]);
-            const float inv = 1.f / lt;
-            const int qrow = r0 + qb * 32 + l32;
-            if (qrow < N) {
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        u32x2 val;
-                        val[0] = pack_bf16(o[db][qb][u * 4 + 0] * inv, o[db][qb][u * 4 + 1] * inv);
-                        val[1] = pack_bf16(o[db][qb][u * 4 + 2] * inv, o[db][qb][u * 4 + 3] * inv);
-                        *reinterpret_cast<u32x2*>(Og + (size_t)qrow * D + db * 32 + u * 8 + hh * 4) = val;
-                    }
-                if (hh == 0) Lg[qrow] = (m[qb] + __log2f(lt)) * kLn2;
+            for (int u = 0; u < 4; ++u) {
+                u32x2 val;
+                val[0] = pack_bf16(st.o[db][u * 4 + 0] * inv, st.o[db][u * 4 + 1] * inv);
+                val[1] = pack_bf16(st.o[db][u * 4 + 2] * inv, st.o[db][u * 4 + 3] * inv);
+                *reinterpret_cast<u32x2*>(Og + db * 32 + u * 8 + hh * 4) = val;
             }
-        }
+        if (hh == 0) p.lse[(size_t)bh * N + qrow] = (st.m + __log2f(lt)) * kLn2;
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     const int nqt = (p.N + kBM - 1) / kBM;
     const int grid = p.B * p.Hq * nqt;
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -282,13 +376,12 @@ Geometry fwd_geometry(int B, int Hq, int N, int d, int causal) {
     g.block_n = kBN;
     g.threads = kThreads;
     g.grid = B * Hq * ((N + kBM - 1) / kBM);
-    g.lds_bytes = 4 * kBN * d * 2;
+    g.lds_bytes = d == 128 ? FwdCfg<128>::LDS : FwdCfg<64>::LDS;
     return g;
 }
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
-    if (p.d == 128) return p.causal ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
-    return p.causal ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
+    return p.d == 128 ? launch_fwd_t<128>(p, stream) : launch_fwd_t<64>(p, stream);
 }
 
 }  // namespace fa
