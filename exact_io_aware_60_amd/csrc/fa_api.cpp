@@ -28,7 +28,11 @@ int check_shape(int B, int Hq, int Hkv, int N, int d) {
     if (elems >= 4.0e18L) return FA_ERR_SHAPE;
     const long double grid = (long double)B * Hq * ((N + 63) / 64);
     if (grid >= 2147483647.0L) return FA_ERR_SHAPE;
-    if ((long double)N * d >= 2147483647.0L) return FA_ERR_SHAPE;
+    // per-head element offsets of the (padded) backward copies are 32-bit, and
+    // the bytes of one group of query heads sharing a K/V head fit a 32-bit
+    // buffer range
+    if ((long double)(N + fa::kRowPad) * d >= 2147483647.0L) return FA_ERR_SHAPE;
+    if ((long double)(Hq / Hkv) * (N + fa::kRowPad) * d * 2 >= 4294967295.0L) return FA_ERR_SHAPE;
     return FA_OK;
 }
 
@@ -127,10 +131,14 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
     p.k16 = reinterpret_cast<uint16_t*>(ws + w.k16);
     p.v16 = reinterpret_cast<uint16_t*>(ws + w.v16);
     p.do16 = reinterpret_cast<uint16_t*>(ws + w.do16);
+    p.qT16 = reinterpret_cast<uint16_t*>(ws + w.qT16);
+    p.doT16 = reinterpret_cast<uint16_t*>(ws + w.doT16);
+    p.kT16 = reinterpret_cast<uint16_t*>(ws + w.kT16);
     p.part = reinterpret_cast<uint32_t*>(ws + w.part);
     p.scales = reinterpret_cast<float*>(ws + w.scales);
     p.npart = w.npart;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d; p.G = Hq / Hkv;
+    p.Np = w.Np;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);

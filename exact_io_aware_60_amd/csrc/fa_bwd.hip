@@ -7,20 +7,20 @@
 // Attention: memory-efficient transformers", "Recomputation in the Backward
 // Pass"). The gradient formulas are the chain rule of softmax attention for the
 // loss sum(dO * O):
-//   D_i   = sum_c dO_ic O_ic                 (row dot, first kernel)
+//   D_i   = sum_c dO_ic O_ic                 (row dot)
 //   dP_ij = dO_i . v_j,  dS_ij = P_ij (dP_ij - D_i)
-//   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i   (second kernel)
-//   dQ_i  = scale sum_j dS_ij k_j                              (third kernel)
+//   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i   (dK/dV kernel)
+//   dQ_i  = scale sum_j dS_ij k_j                              (dQ kernel)
 // dK and dV sum over the query heads that share the K/V head.
 //
 // Precision. The four products that take P or dS as an operand run on fp16
 // MFMA operands. fp16 keeps 11 significant bits where bf16 keeps 8, at the same
-// MFMA rate, so rounding P and dS costs 8x less accuracy. The first kernel
-// finds max |x| of q, k, v and dout. A preparation kernel then writes fp16
-// copies of them scaled by powers of two (max |x| * scale lies in
-// [2^13, 2^14)), so every bf16 value converts exactly. It also derives a scale
-// for dS from the bound |dS_ij| <= 2 d max|dO| max|V|. The scales are undone
-// in fp32 in each epilogue.
+// MFMA rate, so rounding P and dS costs 8x less accuracy. A first kernel finds
+// max |x| of q, k, v and dout. The preparation kernel then writes fp16 copies
+// of them scaled by powers of two (max |x| * scale lies in [2^13, 2^14)), so
+// every bf16 value converts exactly. It also derives a scale for dS from the
+// bound |dS_ij| <= 2 d max|dO| max|V|. The scales are undone in fp32 in each
+// epilogue.
 //
 // The row dot D. The forward stores O in bf16, and its P.V product rounds P to
 // bf16, so a D formed from the stored O is off by about one bf16 ulp of O per
@@ -36,29 +36,50 @@
 // output element is written once, so results are bit-reproducible. The cost is
 // recomputing S and dP in the dQ pass.
 //
-// Data flow per kernel, using 32x32x16 MFMA for every product (the
-// operand layouts are listed in fa_device.h):
-//  * dQ: a workgroup of 4 waves owns 256 query rows (64 per wave). Their Q and
-//    dO rows sit in LDS for the whole kernel, and 32-key tiles of K and V
-//    stream through double-buffered LDS. S^T = K Q^T and dP^T = V dO^T leave
-//    one query row per lane, and dS^T and P^T in fp16 feed dQ^T += K^T dS^T and
-//    PK^T += K^T P^T, with K^T from the LDS transpose read.
-//  * dK/dV: a workgroup of 4 waves owns 128 keys, 32 per wave, held in
-//    registers as MFMA operands. Per step it streams 64 query rows of Q and dO
-//    (plus their LSE and D) through double-buffered LDS. S = Q K^T and
-//    dP = dO V^T leave one key per lane and 16 query rows per lane, which after
-//    rounding to fp16 are directly the operands of dV^T += dO^T P and
-//    dK^T += Q^T dS. dO^T and Q^T come from the LDS transpose read.
-// Both kernels skip the tiles that the causal mask hides completely, mask the
-// diagonal and ragged tiles element-wise, and run the heaviest workgroups
-// first.
+// Operand layouts. All products use v_mfma_f32_32x32x16_f16 (layouts in
+// fa_device.h), and every operand is read from LDS with conflict-free 16-byte
+// row reads (ds_read_b128 delivers about 220 B/clk per CU on MI355X, the
+// transposing ds_read_b64_tr_b16 at most about 145 and only 70 with four
+// waves). The contractions over query rows (dV, dK) and over keys (dQ) need an
+// operand with consecutive rows at a fixed column, so the preparation kernel
+// writes transposed copies of q, dout and k ([d][rows] per head). Their rows
+// are stored in the k order of the operand they meet: the fp32 accumulator of
+// S or dP, reused in register order as the other operand, holds in slot s of
+// lane half hh the row 16c + 8(s/4) + 4hh + s%4, so position p of every group
+// of 16 holds row p with bits 2 and 3 swapped. All copies are padded to a
+// multiple of 128 rows with zero data, D = 0 and LSE = +inf, so no tile reads
+// past an array and padding rows carry P = 0.
+//
+// Data flow (four waves per workgroup, one per SIMD):
+//  * dQ: a workgroup owns 128 query rows, 32 per wave, whose Q and dO rows
+//    stay in registers as MFMA operands. Tiles of 64 keys (K and V rows, K^T)
+//    stream through three LDS stages. S^T = K Q^T and dP^T = V dO^T leave one
+//    query row per lane; P^T and dS^T in fp16 feed dQ^T += K^T dS^T and
+//    PK^T += K^T P^T. The loop is software-pipelined across tiles: the MFMAs of
+//    tile j's scores run beside the dQ products of tile j-1, and the exp / dS
+//    work of tile j spreads over the slots in between, so the vector ALU work
+//    of one tile overlaps a whole tile of MFMAs.
+//  * dK/dV: a workgroup owns 128 keys, 32 per wave, held in registers as MFMA
+//    operands. Each step streams 64 query rows of one query head of the group
+//    (Q and dO rows, their transposes, LSE and D) through two LDS stages. The
+//    steps walk the row blocks from the last one down, all heads of the group
+//    per block, so workgroups running side by side read the same rows from L2.
+//    S = Q K^T and dP = dO V^T leave one key per lane; P and dS in fp16 feed
+//    dV^T += dO^T P and dK^T += Q^T dS. Inside a step the exp / dS work is
+//    interleaved by hand with the MFMAs.
+// Only tiles that cross the causal diagonal (and, in dQ, the ragged last key
+// tile) take an element-wise mask, on a plain unpipelined path.
 #include "fa_device.h"
 #include "fa_params.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;   // 4 waves, one per SIMD
+
+// Keeps a value in place: the compiler may not move its computation across a
+// scheduling barrier that follows.
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
 // Workgroup id -> (rank, unit). Workgroups are handed to the 8 XCDs
 // round-robin; when the unit count is a multiple of 8, each XCD gets a
@@ -77,6 +98,7 @@ __device__ __forceinline__ void unmap_block(int bid, int nunits, int& rank, int&
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
 
 // ---------------------------------------------------------------- preparation
 // Tensors the preparation kernels read, in this order: q, k, v, dout.
@@ -137,10 +159,67 @@ __device__ __forceinline__ int scale_exp(uint32_t mag_bits) {
     return 14 - e;
 }
 
-// Scales, fp16 copies, and per row D * 2^sS and LSE * log2(e).
+// Position of row r of a group of 16 in a transposed copy, and back (bits 2 and
+// 3 swapped: the map is its own inverse). Bits above 3 pass through.
+__device__ __forceinline__ int perm16(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Rows [row0, row0 + 64) of one head: the fp16 copy (x * f) and, when dstT is
+// set, the transposed copy of the same rows. Rows >= N are written as zeros.
+// `tr` is a [64][D/2 + 1]-word LDS buffer (odd row pitch: the column reads of
+// the transpose hit distinct banks).
+template <int D>
+__device__ __forceinline__ void conv_tile(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                          uint16_t* __restrict__ dstT, int row0, int N, int Np, float f,
+                                          uint32_t* tr) {
+    constexpr int CPR = D / 8;
+    constexpr int CH = 64 * CPR / kThreads;
+    constexpr int TW = D / 2 + 1;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+        const int chunk = u * kThreads + tid;
+        const int r = chunk / CPR, c = chunk % CPR;
+        const int row = row0 + r;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < N) x = *reinterpret_cast<const u32x4*>(src + (size_t)row * D + c * 8);
+        u32x4 y;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) y[t] = pack_f16(bf16_lo(x[t]) * f, bf16_hi(x[t]) * f);
+        *reinterpret_cast<u32x4*>(dst + (size_t)row * D + c * 8) = y;
+        if (dstT) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) tr[r * TW + c * 4 + t] = y[t];
+        }
+    }
+    if (dstT) {   // uniform over the workgroup
+        __syncthreads();
+        // [D][64] block: 8 chunks of 16 bytes per d row; chunk cc holds positions
+        // cc*8 .. cc*8+7, i.e. rows perm16(position).
+        constexpr int TCH = D * 8 / kThreads;
+#pragma unroll
+        for (int u = 0; u < TCH; ++u) {
+            const int idx = u * kThreads + tid;
+            const int dd = idx >> 3, cc = idx & 7;
+            const int sh = (dd & 1) * 16;
+            u32x4 z;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t lo = tr[perm16(cc * 8 + 2 * t) * TW + (dd >> 1)] >> sh;
+                const uint32_t hi = tr[perm16(cc * 8 + 2 * t + 1) * TW + (dd >> 1)] >> sh;
+                z[t] = (lo & 0xFFFFu) | (hi << 16);
+            }
+            *reinterpret_cast<u32x4*>(dstT + (size_t)dd * Np + row0 + cc * 8) = z;
+        }
+        __syncthreads();
+    }
+}
+
+// Scales; fp16 copies (row and transposed); per padded row D * 2^sS and
+// LSE * log2(e) (0 and +inf on padding rows).
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     __shared__ uint32_t red[4];
+    __shared__ uint32_t tr[64 * (D / 2 + 1)];
     int sx[4];
     uint32_t mags[4];
     for (int t = 0; t < 4; ++t) {
@@ -164,31 +243,43 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
         p.scales[6] = 0.f;
         p.scales[7] = 0.f;
     }
-    for (int t = 0; t < 4; ++t) {
+    const int N = p.N, Np = p.Np, nrb = Np / 64;
+    // Tiles of 64 rows: q, dout (with transposes), k (with transpose), v.
+    const long long tq = (long long)p.B * p.Hq * nrb, tk = (long long)p.B * p.Hkv * nrb;
+    const long long ntiles = 2 * tq + 2 * tk;
+    for (long long t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        int which;
+        long long r;
+        if (t < tq) { which = 0; r = t; }
+        else if (t < 2 * tq) { which = 3; r = t - tq; }
+        else if (t < 2 * tq + tk) { which = 1; r = t - 2 * tq; }
+        else { which = 2; r = t - 2 * tq - tk; }
+        const long long h = r / nrb;
+        const int rb = (int)(r - h * nrb);
         const uint16_t* src;
         uint16_t* dst;
-        long long chunks;
-        prep_tensor(p, t, src, dst, chunks);
-        const float f = ldexpf(1.f, sx[t]);
-        for (long long c = (long long)blockIdx.x * kThreads + threadIdx.x; c < chunks;
-             c += (long long)gridDim.x * kThreads) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(src + c * 8);
-            u32x4 y;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) y[u] = pack_f16(bf16_lo(x[u]) * f, bf16_hi(x[u]) * f);
-            *reinterpret_cast<u32x4*>(dst + c * 8) = y;
-        }
+        uint16_t* dstT;
+        if (which == 0) { src = p.q; dst = p.q16; dstT = p.qT16; }
+        else if (which == 1) { src = p.k; dst = p.k16; dstT = p.kT16; }
+        else if (which == 2) { src = p.v; dst = p.v16; dstT = nullptr; }
+        else { src = p.dout; dst = p.do16; dstT = p.doT16; }
+        conv_tile<D>(src + (size_t)h * N * D, dst + (size_t)h * Np * D,
+                     dstT ? dstT + (size_t)h * D * Np : nullptr, rb * 64, N, Np, ldexpf(1.f, sx[which]), tr);
     }
     // Row dot: D / 8 lanes share one row (16 bytes each).
     constexpr int LPR = D / 8;
     constexpr int RPB = kThreads / LPR;
     const float fS = ldexpf(1.f, sS);
-    const long long rows = (long long)p.B * p.Hq * p.N;
+    const long long rows = (long long)p.B * p.Hq * Np;
     const int sub = threadIdx.x % LPR;
     for (long long base = (long long)blockIdx.x * RPB; base < rows; base += (long long)gridDim.x * RPB) {
-        const long long row = base + threadIdx.x / LPR;
+        const long long rp = base + threadIdx.x / LPR;
+        const long long bh = rp / Np;
+        const int q = (int)(rp - bh * Np);
+        const bool real = rp < rows && q < N;
+        const long long row = bh * N + q;
         float acc = 0.f;
-        if (row < rows) {
+        if (real) {
             const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + sub * 8);
             const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + row * D + sub * 8);
 #pragma unroll
@@ -199,32 +290,163 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (row < rows && sub == 0) {
-            p.delta[row] = acc * fS;
-            p.lse2[row] = p.lse[row] * kLog2e;
+        if (rp < rows && sub == 0) {
+            p.delta[rp] = real ? acc * fS : 0.f;
+            p.lse2[rp] = real ? p.lse[row] * kLog2e : INFINITY;
         }
     }
 }
 
 // ---------------------------------------------------------------- dK / dV
-constexpr int kKV_WG = 128;  // keys per workgroup
-constexpr int kKV_W = 32;    // keys per wave
-constexpr int kKV_Q = 64;    // query rows per step
+constexpr int kKV_WG = 128;   // keys per workgroup
+constexpr int kKV_W = 32;     // keys per wave
+constexpr int kKV_Q = 64;     // query rows per step
 
-// One step for one wave: 64 query rows against the wave's 32 keys.
-// Qt/dOt: [64][D] bf16 tiles (swizzle mode 2), L2t/Dt: 64 floats.
-// `key` is this lane's key; `masked` is set when the step touches the causal
-// diagonal or a ragged edge.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_step(const FA_LDS uint16_t* Qt, const FA_LDS uint16_t* dOt,
-                                          const FA_LDS float* L2t, const FA_LDS float* Dt,
-                                          const u32x4 (&kf)[D / 16], const u32x4 (&vf)[D / 16],
-                                          f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], bool masked,
-                                          int q0, int key, int N, float sl2, float c1, int lane) {
-    constexpr int DS = D / 16, DB = D / 32;
-    const int l32 = lane & 31, hh = lane >> 5;
+template <int D>
+struct KvCfg {
+    static constexpr int DS = D / 16, DB = D / 32;
+    static constexpr int SR = RowPad<D>::STRIDE;       // Q, dO rows: [64][D]
+    static constexpr int ST = RowPad<kKV_Q>::STRIDE;   // Q^T, dO^T: [D][64]
+    static constexpr int RT = padded_tile_bytes<SR, kKV_Q>();
+    static constexpr int TT = padded_tile_bytes<ST, D>();
+    static constexpr int QR = 0, DOR = RT, QT = 2 * RT, DOT = 2 * RT + TT;
+    static constexpr int L2 = 2 * RT + 2 * TT, DD = L2 + 4 * kKV_Q;   // 64 floats each
+    static constexpr int STAGE = DD + 4 * kKV_Q;
+    static constexpr int LDS = 2 * STAGE;
+    // MFMA slots of a step, in order: S rows 0-31 (DS), dP rows 0-31 (DS),
+    // S rows 32-63, dP rows 32-63, dV chunks 0-1 (2 DB), dK chunks 0-1,
+    // dV chunks 2-3, dK chunks 2-3.
+    static constexpr int NS = 8 * DS;
+    // The 64 softmax tasks of a step (P of rows 0-31, dS of rows 0-31, P of
+    // rows 32-63, dS of rows 32-63; 16 registers each) are spread evenly over
+    // the slots [START, END): from two slots after the first S block is
+    // complete to the first slot of dK chunks 2-3. Each group starts after its
+    // inputs are complete and ends before the slot that consumes it.
+    static constexpr int START = DS + 1;
+    static constexpr int END = 4 * DS + 6 * DB;
+    using PlanR = CopyPlan<D, SR, kKV_Q, 4>;
+    using PlanT = CopyPlan<kKV_Q, ST, D, 4>;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
 
-    // S = Q K^T and dP = dO V^T: lane holds key column l32, rows qb*32 + (i/4)*8 + hh*4 + i%4.
+template <int D>
+__host__ __device__ constexpr int kv_task_begin(int n) {
+    const int t = (n - KvCfg<D>::START) * 64 / (KvCfg<D>::END - KvCfg<D>::START);
+    return t < 0 ? 0 : (t > 64 ? 64 : t);
+}
+
+template <int D>
+struct KvState {
+    u32x4 kf[D / 16], vf[D / 16];   // K, V as the B operand: lane holds key l32, d = ds*16 + hh*8 .. +7
+    f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: lane holds key l32, d rows db*32 + (i/4)*8 + hh*4 + i%4
+};
+
+// Lane bases (bytes): abase = l32 * SR + hh * 16 for the Q / dO row operands
+// (row qb*32 + l32, d = ds*16 + hh*8 ..); tbase = l32 * ST + hh * 16 for the
+// transposed operands (d row db*32 + l32, positions qc*16 + hh*8 ..);
+// lbase = hh * 16 for the per-row LSE / D values.
+
+// One unmasked step, interleaved by hand: MFMA slot n issues its MFMA, starts
+// the LDS read of slot n + 3's operand and runs its share of the softmax
+// tasks; a scheduling barrier closes every slot.
+template <int D>
+__device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S, int abase,
+                                        int tbase, int lbase, float sl2, float c1) {
+    using C = KvCfg<D>;
+    constexpr int DS = C::DS, DB = C::DB, NS = C::NS, PF = 3;
+    f32x16 s[2], dp[2];
+    u32x4 pp[4], dsp[4];
+    f32x4 lv[2][4], dv4[2][4];
+    u32x4 ring[PF + 1];
+
+    auto frag = [&](auto nc) -> u32x4 {
+        constexpr int n = decltype(nc)::value;
+        if constexpr (n < 4 * DS) {
+            constexpr int ph = n / DS, ds = n % DS, qb = ph >> 1;
+            constexpr int off = ((ph & 1) ? C::DOR : C::QR) + qb * 32 * C::SR + ds * 32;
+            return lds_read16b(st, abase + off);
+        } else {
+            constexpr int m = n - 4 * DS, grp = m / (2 * DB);
+            constexpr int qc = (grp >> 1) * 2 + (m % (2 * DB)) / DB, db = m % DB;
+            constexpr int off = ((grp & 1) ? C::QT : C::DOT) + db * 32 * C::ST + qc * 32;
+            return lds_read16b(st, tbase + off);
+        }
+    };
+    auto mfma_at = [&](auto nc, const u32x4& a) {
+        constexpr int n = decltype(nc)::value;
+        if constexpr (n < 4 * DS) {
+            constexpr int ph = n / DS, ds = n % DS, qb = ph >> 1;
+            if constexpr ((ph & 1) == 0)
+                s[qb] = mfma32h(a, S.kf[ds], ds == 0 ? zero16() : s[qb]);
+            else
+                dp[qb] = mfma32h(a, S.vf[ds], ds == 0 ? zero16() : dp[qb]);
+        } else {
+            constexpr int m = n - 4 * DS, grp = m / (2 * DB);
+            constexpr int qc = (grp >> 1) * 2 + (m % (2 * DB)) / DB, db = m % DB;
+            if constexpr ((grp & 1) == 0)
+                S.dv[db] = mfma32h(a, pp[qc], S.dv[db]);
+            else
+                S.dk[db] = mfma32h(a, dsp[qc], S.dk[db]);
+        }
+    };
+    // Task t: group t/16 (P rows 0-31, dS rows 0-31, P rows 32-63, dS rows
+    // 32-63), register i = t%16 of the half, which is row h*32 + (i/4)*8 +
+    // hh*4 + i%4. P = exp2(S' sl2 - LSE log2 e); dS 2^sS = P (dP' c1 - D 2^sS).
+    // Register pair (2w, 2w+1) of 16-row chunk qc is k-slot pair w of the
+    // chunk's B operand.
+    auto task = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int grp = t / 16, i = t % 16, h = grp >> 1;
+        constexpr int u = i / 4, e = i % 4, qc = 2 * h + i / 8, w = (i % 8) / 2;
+        if constexpr ((grp & 1) == 0) {
+            const float x = fast_exp2(fmaf(s[h][i], sl2, -lv[h][u][e]));
+            s[h][i] = x;
+            if constexpr (i & 1) {
+                uint32_t v = pack_f16(s[h][i - 1], x);
+                pin(v);
+                pp[qc][w] = v;
+            }
+        } else {
+            const float y = s[h][i] * fmaf(dp[h][i], c1, -dv4[h][u][e]);
+            dp[h][i] = y;
+            if constexpr (i & 1) {
+                uint32_t v = pack_f16(dp[h][i - 1], y);
+                pin(v);
+                dsp[qc][w] = v;
+            }
+        }
+    };
+
+    static_for<PF>([&](auto nc) { ring[decltype(nc)::value] = frag(nc); });
+    static_for<NS>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        mfma_at(nc, ring[n % (PF + 1)]);
+        if constexpr (n + PF < NS) ring[(n + PF) % (PF + 1)] = frag(std::integral_constant<int, n + PF>{});
+        if constexpr (n % DS == 0 && n < 4 * DS) {
+            // LSE of a half before its P tasks, D before its dS tasks
+            constexpr int ph = n / DS, h = ph >> 1;
+            const FA_LDS uint8_t* src = st + ((ph & 1) ? C::DD : C::L2) + lbase + h * 32 * 4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const f32x4 x = *reinterpret_cast<const FA_LDS f32x4*>(src + u * 32);
+                if constexpr (ph & 1) dv4[h][u] = x;
+                else lv[h][u] = x;
+            }
+        }
+        constexpr int t0 = kv_task_begin<D>(n), t1 = kv_task_begin<D>(n + 1);
+        static_for<t1 - t0>([&](auto k) { task(std::integral_constant<int, t0 + decltype(k)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// A step that crosses the causal diagonal: keys above a row get P = 0.
+// Unpipelined; at most one per head and wave.
+template <int D>
+__device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S,
+                                               int abase, int tbase, int lbase, int q0, int key, float sl2,
+                                               float c1, int hh) {
+    using C = KvCfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
     f32x16 s[2], dp[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -235,161 +457,199 @@ __device__ __forceinline__ void dkdv_step(const FA_LDS uint16_t* Qt, const FA_LD
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const int off = swz<D, 2>(qb * 32 + l32, ds * 2 + hh);
-            s[qb] = mfma32h(lds_read16(Qt, off), kf[ds], s[qb]);
-            dp[qb] = mfma32h(lds_read16(dOt, off), vf[ds], dp[qb]);
+            s[qb] = mfma32h(lds_read16b(st, abase + C::QR + qb * 32 * C::SR + ds * 32), S.kf[ds], s[qb]);
+            dp[qb] = mfma32h(lds_read16b(st, abase + C::DOR + qb * 32 * C::SR + ds * 32), S.vf[ds], dp[qb]);
         }
-
-    // P = exp2(S * scale * log2e - L2); dS * 2^sS = P (dP' * c1 - D * 2^sS).
+    u32x4 pp[4], dsp[4];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int r = qb * 32 + u * 8 + hh * 4;
-            const f32x4 lv = *reinterpret_cast<const FA_LDS f32x4*>(L2t + r);
-            const f32x4 dv4 = *reinterpret_cast<const FA_LDS f32x4*>(Dt + r);
+            const f32x4 lv = *reinterpret_cast<const FA_LDS f32x4*>(st + C::L2 + lbase + (qb * 32 + u * 8) * 4);
+            const f32x4 dv4 = *reinterpret_cast<const FA_LDS f32x4*>(st + C::DD + lbase + (qb * 32 + u * 8) * 4);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int i = u * 4 + t;
-                float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[t]));
-                if (masked) {
-                    const int q = q0 + r + t;
-                    if (key >= N || q >= N || (CAUSAL && key > q)) x = 0.f;
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int i = u * 4 + e;
+                const int q = q0 + qb * 32 + u * 8 + hh * 4 + e;
+                float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[e]));
+                if (key > q) x = 0.f;
                 s[qb][i] = x;
-                dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[t]);
+                dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[e]);
             }
         }
-
-    // fp16 operands. k slot t of chunk qc is query row qc*16 + (t/4)*8 + hh*4 + t%4,
-    // which is register (qc & 1) * 8 + t of block qc >> 1.
-    u32x4 pp[4], dsp[4];
 #pragma unroll
     for (int qc = 0; qc < 4; ++qc)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int i = (qc & 1) * 8 + 2 * t;
-            pp[qc][t] = pack_f16(s[qc >> 1][i], s[qc >> 1][i + 1]);
-            dsp[qc][t] = pack_f16(dp[qc >> 1][i], dp[qc >> 1][i + 1]);
+        for (int w = 0; w < 4; ++w) {
+            const int i = (qc & 1) * 8 + 2 * w;
+            pp[qc][w] = pack_f16(s[qc >> 1][i], s[qc >> 1][i + 1]);
+            dsp[qc][w] = pack_f16(dp[qc >> 1][i], dp[qc >> 1][i + 1]);
         }
-
-    // dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T read transposed in the same row order.
-    const int g = lane >> 4;
 #pragma unroll
     for (int qc = 0; qc < 4; ++qc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int dcol = db * 32 + (g & 1) * 16 + 4 * (lane & 3);
-            const int qrow = qc * 16 + (g >> 1) * 4 + ((lane & 15) >> 2);
-            const int o0 = swz<D, 2>(qrow, dcol >> 3) + (dcol & 7);
-            const int o1 = swz<D, 2>(qrow + 8, dcol >> 3) + (dcol & 7);
-            dv[db] = mfma32h(cat(lds_read_tr(dOt, o0), lds_read_tr(dOt, o1)), pp[qc], dv[db]);
-            dk[db] = mfma32h(cat(lds_read_tr(Qt, o0), lds_read_tr(Qt, o1)), dsp[qc], dk[db]);
+            const int off = db * 32 * C::ST + qc * 32;
+            S.dv[db] = mfma32h(lds_read16b(st, tbase + C::DOT + off), pp[qc], S.dv[db]);
+            S.dk[db] = mfma32h(lds_read16b(st, tbase + C::QT + off), dsp[qc], S.dk[db]);
         }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
-    constexpr int CPR = D / 8, DS = D / 16, DB = D / 32;
-    constexpr int QT = kKV_Q * D;                  // elements per Q or dO tile
-    constexpr int LCH = kKV_Q * CPR / kThreads;    // chunks each thread copies per tile
-    constexpr int STAGE = 2 * QT + 4 * kKV_Q;      // Q, dO, then 64 floats of L2 and of D
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+// Where one step's data sits: the byte offsets, in the resources of the K/V
+// head's query-head group, of 64 rows from q0 of group member g.
+struct KvRes {
+    BufRes q, dout, qt, dot, l2, dd;
+};
+struct KvSrc {
+    uint32_t rows;   // q16 / do16 rows
+    uint32_t tr;     // qT16 / doT16 columns
+    uint32_t row4;   // lse2 / delta
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+template <int D>
+__device__ __forceinline__ void kv_copy(const typename KvCfg<D>::PlanR& pr, const typename KvCfg<D>::PlanT& pt,
+                                        const KvRes& rs, const KvSrc& x, FA_LDS uint8_t* __restrict__ st, int w,
+                                        int lane) {
+    using C = KvCfg<D>;
+    pr.copy(rs.q, x.rows, st + C::QR, w);
+    pr.copy(rs.dout, x.rows, st + C::DOR, w);
+    pt.copy(rs.qt, x.tr, st + C::QT, w);
+    pt.copy(rs.dot, x.tr, st + C::DOT, w);
+    if (w == 0) bload_lds4(rs.l2, lane * 4, x.row4, st + C::L2);
+    if (w == 1) bload_lds4(rs.dd, lane * 4, x.row4, st + C::DD);
+}
+
+// Step j: start the copy of step j+1 into stage `wst` (if any), then compute
+// step j from stage `rst`. The two stages are distinct; the __restrict__
+// qualifiers tell the compiler so, and it then reads `rst` without waiting for
+// the copies into `wst`. mode: 0 idle, 1 unmasked, 2 diagonal.
+template <int D>
+__device__ __forceinline__ void kv_iteration(KvState<D>& S, const typename KvCfg<D>::PlanR& pr,
+                                             const typename KvCfg<D>::PlanT& pt, const KvRes& rs, bool issue,
+                                             const KvSrc& nx,
+                                             FA_LDS uint8_t* __restrict__ wst,
+                                             const FA_LDS uint8_t* __restrict__ rst, int mode, int q0, int key,
+                                             int abase, int tbase, int lbase, float sl2, float c1, int w,
+                                             int lane) {
+    if (issue) kv_copy<D>(pr, pt, rs, nx, wst, w, lane);
+    if (mode == 1)
+        kv_step<D>(rst, S, abase, tbase, lbase, sl2, c1);
+    else if (mode == 2)
+        kv_step_masked<D>(rst, S, abase, tbase, lbase, q0, key, sl2, c1, lane >> 5);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
+    using C = KvCfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
-    const int N = p.N, G = p.G;
-    const int nkt = (N + kKV_WG - 1) / kKV_WG;
+    const int N = p.N, Np = p.Np, G = p.G;
+    const bool causal = p.causal != 0;
     int kt, bkv;
-    unmap_block(blockIdx.x, p.B * p.Hkv, kt, bkv);  // kt = 0 first: the most query rows when causal
+    unmap_block(blockIdx.x, p.B * p.Hkv, kt, bkv);   // kt = 0 first: the most query rows when causal
     const int b = bkv / p.Hkv, hkv = bkv - b * p.Hkv;
-    (void)nkt;
     const int k0 = kt * kKV_WG;
     const int kw0 = k0 + w * kKV_W;
-    const int key = kw0 + l32;
-    const uint16_t* Kg = p.k16 + (size_t)bkv * N * D;
-    const uint16_t* Vg = p.v16 + (size_t)bkv * N * D;
+    const int key = kw0 + l32;                       // < Np: padded rows are zero
     const float sl2 = p.scales[0], c1 = p.scales[1];
 
-    // K and V as the B operand of S = Q K^T and dP = dO V^T: lane holds key
-    // column l32 and d = ds*16 + hh*8 .. +7. Keys past N read row N-1 (masked later).
-    u32x4 kf[DS], vf[DS];
+    KvState<D> S;
     {
-        const size_t kr = (size_t)min(key, N - 1) * D;
+        const uint16_t* Kg = p.k16 + ((size_t)bkv * Np + key) * D;
+        const uint16_t* Vg = p.v16 + ((size_t)bkv * Np + key) * D;
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-            kf[ds] = *reinterpret_cast<const u32x4*>(Kg + kr + ds * 16 + hh * 8);
-            vf[ds] = *reinterpret_cast<const u32x4*>(Vg + kr + ds * 16 + hh * 8);
+            S.kf[ds] = *reinterpret_cast<const u32x4*>(Kg + ds * 16 + hh * 8);
+            S.vf[ds] = *reinterpret_cast<const u32x4*>(Vg + ds * 16 + hh * 8);
         }
     }
-    f32x16 dk[DB], dv[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-        dk[db] = zero16();
-        dv[db] = zero16();
+        S.dk[db] = zero16();
+        S.dv[db] = zero16();
     }
 
-    const int qs = CAUSAL ? k0 : 0;                 // rows before the block's first key see none of it
-    const int nqs = (N - qs + kKV_Q - 1) / kKV_Q;   // query steps per head
-    const int nsteps = G * nqs;
-
-    // Copy step j (head g, rows q0..q0+63) into stage `buf`. Rows past N read
-    // row N-1; their probabilities are masked to zero.
-    auto issue = [&](int j, int buf) {
-        const int g = j / nqs;
-        const int q0 = qs + (j - g * nqs) * kKV_Q;
-        const size_t bh = (size_t)b * p.Hq + (size_t)hkv * G + g;
-        const uint16_t* Qg = p.q16 + bh * N * D;
-        const uint16_t* dOg = p.do16 + bh * N * D;
-        FA_LDS uint16_t* st = (FA_LDS uint16_t*)smem + buf * STAGE;
-#pragma unroll
-        for (int u = 0; u < LCH; ++u) {
-            const int slot = u * kThreads + tid;
-            int row, c;
-            unswz<D, 2>(slot, row, c);
-            const size_t src = (size_t)min(q0 + row, N - 1) * D + c * 8;
-            gload_lds16(Qg + src, st + (u * kThreads + w * 64) * 8);
-            gload_lds16(dOg + src, st + QT + (u * kThreads + w * 64) * 8);
-        }
-        const size_t r = bh * N + min(q0 + lane, N - 1);
-        if (w == 0) gload_lds4(p.lse2 + r, (FA_LDS float*)(st + 2 * QT));
-        if (w == 1) gload_lds4(p.delta + r, (FA_LDS float*)(st + 2 * QT) + kKV_Q);
+    // Steps: row blocks from the last one down to qs (rows before the block's
+    // first key see none of it under the causal mask), all G heads per block.
+    const int qs = causal ? k0 : 0;
+    const int nrb = (N - qs + kKV_Q - 1) / kKV_Q;
+    const int nsteps = G * nrb;
+    const int qtop = qs + (nrb - 1) * kKV_Q;
+    KvRes rs;
+    {
+        const size_t bh0 = (size_t)b * p.Hq + (size_t)hkv * G;   // first query head of the group
+        const uint32_t nrow = (uint32_t)G * Np;
+        rs.q = make_bufres(p.q16 + bh0 * Np * D, nrow * D * 2);
+        rs.dout = make_bufres(p.do16 + bh0 * Np * D, nrow * D * 2);
+        rs.qt = make_bufres(p.qT16 + bh0 * D * Np, nrow * D * 2);
+        rs.dot = make_bufres(p.doT16 + bh0 * D * Np, nrow * D * 2);
+        rs.l2 = make_bufres(p.lse2 + bh0 * Np, nrow * 4);
+        rs.dd = make_bufres(p.delta + bh0 * Np, nrow * 4);
+    }
+    auto src_of = [&](int j) {
+        const uint32_t g = j % G;
+        const uint32_t q0 = qtop - (j / G) * kKV_Q;
+        KvSrc x;
+        x.rows = (g * Np + q0) * D * 2;
+        x.tr = g * D * Np * 2 + q0 * 2;
+        x.row4 = (g * Np + q0) * 4;
+        return x;
     };
+    typename C::PlanR pr;
+    typename C::PlanT pt;
+    pr.init(w, lane, D);
+    pt.init(w, lane, Np);
+    const int abase = l32 * C::SR + hh * 16;
+    const int tbase = l32 * C::ST + hh * 16;
+    const int lbase = hh * 16;
+    FA_LDS uint8_t* st0 = (FA_LDS uint8_t*)smem;
 
-    issue(0, 0);
+    kv_copy<D>(pr, pt, rs, src_of(0), st0, w, lane);
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < nsteps; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nsteps) issue(j + 1, buf ^ 1);
-        const int g = j / nqs;
-        const int q0 = qs + (j - g * nqs) * kKV_Q;
-        const bool active = kw0 < N && (!CAUSAL || q0 + kKV_Q - 1 >= kw0);
-        if (active) {
-            const bool masked = (CAUSAL && kw0 + kKV_W - 1 > q0) || (q0 + kKV_Q > N) || (kw0 + kKV_W > N);
-            const FA_LDS uint16_t* st = (const FA_LDS uint16_t*)smem + buf * STAGE;
-            const FA_LDS float* lt = (const FA_LDS float*)(st + 2 * QT);
-            dkdv_step<D, CAUSAL>(st, st + QT, lt, lt + kKV_Q, kf, vf, dk, dv, masked, q0, key, N,
-                                 sl2, c1, lane);
-        }
+    // Steps with q0 >= k0 + 128 (all but the last two row blocks when causal)
+    // are unmasked for every wave, and run on one code path. A wave whose keys
+    // lie past N runs them too (its keys are zero padding; never stored).
+    const int nsteady = causal ? G * max(0, nrb - 2) : nsteps;
+    for (int j = 0; j < nsteady; ++j) {
+        const KvSrc nx = src_of(j + 1 < nsteps ? j + 1 : j);
+        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
+        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
+        kv_iteration<D>(S, pr, pt, rs, j + 1 < nsteps, nx, wst, rst, 1, 0, key, abase, tbase, lbase, sl2, c1, w, lane);
+        wait_vmem();
+        __syncthreads();
+    }
+    for (int j = nsteady; j < nsteps; ++j) {
+        const int q0 = qtop - (j / G) * kKV_Q;
+        const bool active = kw0 < N && (!causal || q0 + kKV_Q - 1 >= kw0);
+        const int mode = !active ? 0 : ((causal && q0 < kw0 + kKV_W - 1) ? 2 : 1);
+        const bool issue = j + 1 < nsteps;
+        const KvSrc nx = src_of(issue ? j + 1 : j);
+        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
+        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
+        kv_iteration<D>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, abase, tbase, lbase, sl2, c1, w, lane);
         wait_vmem();
         __syncthreads();
     }
 
     // dK^T / dV^T blocks: lane holds key l32, d rows db*32 + u*8 + hh*4 + 0..3.
     if (key < N) {
-        uint16_t* dKg = p.dk + (size_t)bkv * N * D + (size_t)key * D;
-        uint16_t* dVg = p.dv + (size_t)bkv * N * D + (size_t)key * D;
+        uint16_t* dKg = p.dk + ((size_t)bkv * N + key) * D;
+        uint16_t* dVg = p.dv + ((size_t)bkv * N + key) * D;
         const float fk = p.scales[3], fv = p.scales[2];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 u32x2 a, c;
-                a[0] = pack_bf16(dk[db][u * 4 + 0] * fk, dk[db][u * 4 + 1] * fk);
-                a[1] = pack_bf16(dk[db][u * 4 + 2] * fk, dk[db][u * 4 + 3] * fk);
-                c[0] = pack_bf16(dv[db][u * 4 + 0] * fv, dv[db][u * 4 + 1] * fv);
-                c[1] = pack_bf16(dv[db][u * 4 + 2] * fv, dv[db][u * 4 + 3] * fv);
+                a[0] = pack_bf16(S.dk[db][u * 4 + 0] * fk, S.dk[db][u * 4 + 1] * fk);
+                a[1] = pack_bf16(S.dk[db][u * 4 + 2] * fk, S.dk[db][u * 4 + 3] * fk);
+                c[0] = pack_bf16(S.dv[db][u * 4 + 0] * fv, S.dv[db][u * 4 + 1] * fv);
+                c[1] = pack_bf16(S.dv[db][u * 4 + 2] * fv, S.dv[db][u * 4 + 3] * fv);
                 *reinterpret_cast<u32x2*>(dKg + db * 32 + u * 8 + hh * 4) = a;
                 *reinterpret_cast<u32x2*>(dVg + db * 32 + u * 8 + hh * 4) = c;
             }
@@ -397,207 +657,371 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
-constexpr int kQ_WG = 256;  // query rows per workgroup
-constexpr int kQ_W = 64;    // query rows per wave
-constexpr int kQ_N = 32;    // keys per tile
+constexpr int kQ_WG = 128;   // query rows per workgroup
+constexpr int kQ_W = 32;     // query rows per wave
+constexpr int kQ_N = 64;     // keys per tile
 
-// One key tile for one wave: S^T = K Q^T, dP^T = V dO^T, then
-//   dQ^T += K^T dS^T   with dS formed from the preparation's D (from the stored O),
-//   PK^T += K^T P^T    and D'_i += sum_j P_ij dP_ij (the exact row dot).
-// The epilogue corrects dQ by (D - D') PK, which is exact because dS is linear in D.
-// Q and dO are read from the workgroup's LDS copies (Qw, dOw).
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void dq_tile(const FA_LDS uint16_t* Kt, const FA_LDS uint16_t* Vt,
-                                        const FA_LDS uint16_t* dOw, const FA_LDS uint16_t* Qw,
-                                        f32x16 (&dq)[D / 32][2], f32x16 (&pk)[D / 32][2],
-                                        float (&dacc)[2], const float (&l2)[2], const float (&dd)[2],
-                                        bool masked, int key0, int r0, int wrow0, int N, float sl2,
-                                        float c1, int lane) {
-    constexpr int DS = D / 16, DB = D / 32;
-    const int l32 = lane & 31, hh = lane >> 5;
+template <int D>
+struct QCfg {
+    static constexpr int DS = D / 16, DB = D / 32;
+    static constexpr int SR = RowPad<D>::STRIDE;      // K, V rows: [64][D]
+    static constexpr int ST = RowPad<kQ_N>::STRIDE;   // K^T: [D][64]
+    static constexpr int RT = padded_tile_bytes<SR, kQ_N>();
+    static constexpr int TT = padded_tile_bytes<ST, D>();
+    static constexpr int KR = 0, VR = RT, KT = 2 * RT;
+    static constexpr int STAGE = 2 * RT + TT;
+    static constexpr int LDS = 3 * STAGE;             // tiles j-1 (K^T), j, j+1
+    // MFMA slots of a pipelined tile, DS each, in order: dQ/PK products of the
+    // previous tile for key chunk 0, chunk 1; S^T keys 0-31; dP^T keys 0-31;
+    // products of the previous tile for chunks 2, 3; S^T keys 32-63; dP^T keys
+    // 32-63. A product slot pair (2m, 2m+1) shares one K^T operand.
+    static constexpr int NS = 8 * DS;
+    // The 64 softmax tasks of a tile start two slots after its first S^T block
+    // is complete and run one per NS/64 slots; the last ones fall into the next
+    // tile's first slots. Each group of 16 starts after its inputs are complete
+    // and ends before the product that consumes it.
+    static constexpr int START = 3 * DS + 1;
+    using PlanR = CopyPlan<D, SR, kQ_N, 4>;
+    using PlanT = CopyPlan<kQ_N, ST, D, 4>;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
 
-    // lane holds query column l32 of block qb, keys (i/4)*8 + hh*4 + i%4.
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = zero16();
-        dp[qb] = zero16();
-    }
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-        const u32x4 ka = lds_read16(Kt, swz<D, 2>(l32, ds * 2 + hh));
-        const u32x4 va = lds_read16(Vt, swz<D, 0>(l32, ds * 2 + hh));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int off = swz<D, 0>(wrow0 + qb * 32 + l32, ds * 2 + hh);
-            s[qb] = mfma32h(ka, lds_read16(Qw, off), s[qb]);
-            dp[qb] = mfma32h(va, lds_read16(dOw, off), dp[qb]);
+// First softmax task of linear slot x (x counts from the tile's slot 0 and
+// runs past NS into the next tile).
+template <int D>
+__host__ __device__ constexpr int dq_task_begin(int x) {
+    const int t = (x - QCfg<D>::START) * 64 / QCfg<D>::NS;
+    return t < 0 ? 0 : (t > 64 ? 64 : t);
+}
+
+template <int D>
+struct QState {
+    u32x4 qf[D / 16], dof[D / 16];   // Q, dO as the B operand: lane holds row l32, d = ds*16 + hh*8 ..
+    f32x16 dq[D / 32], pk[D / 32];   // dQ^T, PK^T: lane holds row l32, d rows db*32 + (i/4)*8 + hh*4 + i%4
+    f32x16 s[2], dp[2];              // S^T, dP^T of keys kb*32 + (i/4)*8 + hh*4 + i%4
+    u32x4 pp[4], dsp[4];             // fp16 P^T, dS^T per 16-key chunk, as the B operand
+    float l2, dd, dacc;              // LSE log2 e, D 2^sS, running sum of P dP'
+};
+
+// Softmax task t of the tile whose S^T / dP^T are in S.s / S.dp: group t/16
+// (P keys 0-31, dS keys 0-31, P keys 32-63, dS keys 32-63), register i = t%16.
+template <int D, int t>
+__device__ __forceinline__ void dq_task(QState<D>& S, float sl2, float c1) {
+    constexpr int grp = t / 16, i = t % 16, h = grp >> 1;
+    constexpr int kc = 2 * h + i / 8, w = (i % 8) / 2;
+    if constexpr ((grp & 1) == 0) {
+        const float x = fast_exp2(fmaf(S.s[h][i], sl2, -S.l2));
+        S.s[h][i] = x;
+        if constexpr (i & 1) {
+            uint32_t v = pack_f16(S.s[h][i - 1], x);
+            pin(v);
+            S.pp[kc][w] = v;
+        }
+    } else {
+        const float dpv = S.dp[h][i];
+        S.dacc = fmaf(S.s[h][i], dpv, S.dacc);
+        const float y = S.s[h][i] * fmaf(dpv, c1, -S.dd);
+        S.dp[h][i] = y;
+        if constexpr (i & 1) {
+            uint32_t v = pack_f16(S.dp[h][i - 1], y);
+            pin(v);
+            S.dsp[kc][w] = v;
         }
     }
+}
 
-    // P and dS, packed to fp16 pairs as soon as each pair is ready.
-    u32x4 dsp[2][2], pp[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int q = r0 + qb * 32 + l32;
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-            float x[2], y[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                float xe = fast_exp2(fmaf(s[qb][i + e], sl2, -l2[qb]));
-                if (masked) {
-                    const int kk = key0 + ((i + e) >> 2) * 8 + hh * 4 + ((i + e) & 3);
-                    if (kk >= N || (CAUSAL && kk > q)) xe = 0.f;
-                }
-                const float t = dp[qb][i + e] * c1;     // dP * 2^sS
-                acc = fmaf(xe, t, acc);
-                x[e] = xe;
-                y[e] = xe * (t - dd[qb]);
-            }
-            pp[qb][i >> 3][(i & 7) >> 1] = pack_f16(x[0], x[1]);
-            dsp[qb][i >> 3][(i & 7) >> 1] = pack_f16(y[0], y[1]);
+// One pipelined tile: `cur` holds tile j (K, V rows), `prv` tile j-1 (K^T).
+// PREV = false for a wave's first tile (no previous products or tasks).
+// Lane bases: abase = l32 * SR + hh * 16, tbase = l32 * ST + hh * 16.
+template <int D, bool PREV>
+__device__ __forceinline__ void dq_pipe(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
+                                        const FA_LDS uint8_t* __restrict__ prv, int abase, int tbase,
+                                        float sl2, float c1) {
+    using C = QCfg<D>;
+    constexpr int DS = C::DS, NS = C::NS, PF = 3, START = C::START;
+    // product group g -> key chunk of the previous tile
+    constexpr int kc_of[8] = {0, 1, -1, -1, 2, 3, -1, -1};
+    u32x4 ring[PF + 1];
+
+    auto has_read = [](auto nc) constexpr {
+        constexpr int n = decltype(nc)::value;
+        constexpr int g = n / DS, m = n % DS;
+        constexpr bool prod = g == 0 || g == 1 || g == 4 || g == 5;
+        return prod ? (PREV && m % 2 == 0) : true;
+    };
+    auto frag = [&](auto nc) -> u32x4 {
+        constexpr int n = decltype(nc)::value;
+        constexpr int g = n / DS, m = n % DS;
+        if constexpr (kc_of[g] >= 0) {
+            constexpr int db = m / 2;
+            return lds_read16b(prv, tbase + C::KT + db * 32 * C::ST + kc_of[g] * 32);
+        } else {
+            constexpr int kb = g >= 6 ? 1 : 0;
+            constexpr int off = ((g & 1) ? C::VR : C::KR) + kb * 32 * C::SR + m * 32;
+            return lds_read16b(cur, abase + off);
         }
-        dacc[qb] += acc;
-    }
-
-    const int g = lane >> 4;
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-            const int dcol = db * 32 + (g & 1) * 16 + 4 * (lane & 3);
-            const int krow = kc * 16 + (g >> 1) * 4 + ((lane & 15) >> 2);
-            const u32x4 a = cat(lds_read_tr(Kt, swz<D, 2>(krow, dcol >> 3) + (dcol & 7)),
-                                lds_read_tr(Kt, swz<D, 2>(krow + 8, dcol >> 3) + (dcol & 7)));
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                dq[db][qb] = mfma32h(a, dsp[qb][kc], dq[db][qb]);
-                pk[db][qb] = mfma32h(a, pp[qb][kc], pk[db][qb]);
+    };
+    auto mfma_at = [&](auto nc, const u32x4& a) {
+        constexpr int n = decltype(nc)::value;
+        constexpr int g = n / DS, m = n % DS;
+        if constexpr (kc_of[g] >= 0) {
+            if constexpr (PREV) {
+                constexpr int db = m / 2, kc = kc_of[g];
+                if constexpr (m % 2 == 0) S.pk[db] = mfma32h(a, S.pp[kc], S.pk[db]);
+                else S.dq[db] = mfma32h(a, S.dsp[kc], S.dq[db]);
             }
+        } else {
+            constexpr int kb = g >= 6 ? 1 : 0;
+            if constexpr ((g & 1) == 0) S.s[kb] = mfma32h(a, S.qf[m], m == 0 ? zero16() : S.s[kb]);
+            else S.dp[kb] = mfma32h(a, S.dof[m], m == 0 ? zero16() : S.dp[kb]);
+        }
+    };
+
+    // operand reads of slots 0 .. PF-1
+    static_for<PF>([&](auto nc) {
+        if constexpr (has_read(nc)) ring[decltype(nc)::value % (PF + 1)] = frag(nc);
+    });
+    static_for<NS>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        // a product slot without a read of its own uses its pair's operand
+        constexpr int src = has_read(nc) ? n : n - 1;
+        if constexpr (!(kc_of[n / DS] >= 0) || PREV) mfma_at(nc, ring[src % (PF + 1)]);
+        if constexpr (n + PF < NS) {
+            using NX = std::integral_constant<int, n + PF>;
+            if constexpr (has_read(NX{})) ring[(n + PF) % (PF + 1)] = frag(NX{});
+        }
+        if constexpr (n < START) {
+            if constexpr (PREV) {
+                constexpr int t0 = dq_task_begin<D>(n + NS), t1 = dq_task_begin<D>(n + NS + 1);
+                static_for<t1 - t0>([&](auto k) { dq_task<D, t0 + decltype(k)::value>(S, sl2, c1); });
+            }
+        } else {
+            constexpr int t0 = dq_task_begin<D>(n), t1 = dq_task_begin<D>(n + 1);
+            static_for<t1 - t0>([&](auto k) { dq_task<D, t0 + decltype(k)::value>(S, sl2, c1); });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// Finish the last pipelined tile: its remaining softmax tasks, then all of its
+// dQ / PK products (K^T from `prv`).
+template <int D>
+__device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __restrict__ prv, int tbase,
+                                         float sl2, float c1) {
+    using C = QCfg<D>;
+    constexpr int t0 = dq_task_begin<D>(C::NS);
+    static_for<64 - t0>([&](auto k) { dq_task<D, t0 + decltype(k)::value>(S, sl2, c1); });
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const u32x4 a = lds_read16b(prv, tbase + C::KT + db * 32 * C::ST + kc * 32);
+            S.pk[db] = mfma32h(a, S.pp[kc], S.pk[db]);
+            S.dq[db] = mfma32h(a, S.dsp[kc], S.dq[db]);
         }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
-    constexpr int CPR = D / 8, DS = D / 16, DB = D / 32;
-    constexpr int TILE = kQ_N * D;
-    constexpr int LCH = kQ_N * CPR / kThreads;
-    constexpr int OCH = kQ_WG * CPR / kThreads;    // dO chunks per thread
-    __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + 2 * kQ_WG * D];
-    FA_LDS uint16_t* Ks = (FA_LDS uint16_t*)smem;
-    FA_LDS uint16_t* Vs = Ks + 2 * TILE;
-    FA_LDS uint16_t* dOs = Ks + 4 * TILE;
-    FA_LDS uint16_t* Qs = dOs + kQ_WG * D;
+// A tile with masked entries (the causal diagonal or keys >= N), complete and
+// unpipelined. Keys past N are zero rows in the copies but would still get
+// P = exp2(-LSE), so they are masked like the ones above the diagonal.
+template <int D>
+__device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur, int abase,
+                                          int tbase, int key0, int qrow, int N, bool causal, float sl2,
+                                          float c1, int hh) {
+    using C = QCfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        S.s[kb] = zero16();
+        S.dp[kb] = zero16();
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            S.s[kb] = mfma32h(lds_read16b(cur, abase + C::KR + kb * 32 * C::SR + ds * 32), S.qf[ds], S.s[kb]);
+            S.dp[kb] = mfma32h(lds_read16b(cur, abase + C::VR + kb * 32 * C::SR + ds * 32), S.dof[ds], S.dp[kb]);
+        }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kk = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+            float x = fast_exp2(fmaf(S.s[kb][i], sl2, -S.l2));
+            if (kk >= N || (causal && kk > qrow)) x = 0.f;
+            const float dpv = S.dp[kb][i];
+            S.dacc = fmaf(x, dpv, S.dacc);
+            S.s[kb][i] = x;
+            S.dp[kb][i] = x * fmaf(dpv, c1, -S.dd);
+        }
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int i = (kc & 1) * 8 + 2 * w;
+            S.pp[kc][w] = pack_f16(S.s[kc >> 1][i], S.s[kc >> 1][i + 1]);
+            S.dsp[kc][w] = pack_f16(S.dp[kc >> 1][i], S.dp[kc >> 1][i + 1]);
+        }
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const u32x4 a = lds_read16b(cur, tbase + C::KT + db * 32 * C::ST + kc * 32);
+            S.pk[db] = mfma32h(a, S.pp[kc], S.pk[db]);
+            S.dq[db] = mfma32h(a, S.dsp[kc], S.dq[db]);
+        }
+}
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// Tile j of the workgroup loop: start the copy of tile j+1 into `wst` (if
+// any), then this wave's work on tile j (`cur`; tile j-1 in `prv`). The three
+// stages are distinct (the __restrict__ qualifiers say so).
+// Tiles [0, jfull) are unmasked for this wave and pipelined, tiles
+// [jfull, jlast] are masked, later tiles leave the wave idle.
+template <int D>
+__device__ __forceinline__ void dq_copy(const typename QCfg<D>::PlanR& pr, const typename QCfg<D>::PlanT& pt,
+                                        BufRes rk, BufRes rv, BufRes rkt, int j, FA_LDS uint8_t* __restrict__ st,
+                                        int w) {
+    using C = QCfg<D>;
+    const uint32_t rows = (uint32_t)j * kQ_N * D * 2, tr = (uint32_t)j * kQ_N * 2;
+    pr.copy(rk, rows, st + C::KR, w);
+    pr.copy(rv, rows, st + C::VR, w);
+    pt.copy(rkt, tr, st + C::KT, w);
+}
+
+template <int D>
+__device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D>::PlanR& pr,
+                                             const typename QCfg<D>::PlanT& pt, bool issue, BufRes rk,
+                                             BufRes rv, BufRes rkt, int jn,
+                                             FA_LDS uint8_t* __restrict__ wst,
+                                             const FA_LDS uint8_t* __restrict__ cur,
+                                             const FA_LDS uint8_t* __restrict__ prv, int j, int jfull,
+                                             int jlast, int abase, int tbase, int qrow, int N, bool causal,
+                                             float sl2, float c1, int w) {
+    if (issue) dq_copy<D>(pr, pt, rk, rv, rkt, jn, wst, w);
+    if (j < jfull) {
+        if (j == 0) dq_pipe<D, false>(S, cur, prv, abase, tbase, sl2, c1);
+        else dq_pipe<D, true>(S, cur, prv, abase, tbase, sl2, c1);
+    } else {
+        if (j == jfull && j > 0) dq_drain<D>(S, prv, tbase, sl2, c1);
+        if (j <= jlast) dq_masked<D>(S, cur, abase, tbase, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+    using C = QCfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
-    const int N = p.N;
+    const int N = p.N, Np = p.Np;
+    const bool causal = p.causal != 0;
     const int nqt = (N + kQ_WG - 1) / kQ_WG;
     int rank, bh;
     unmap_block(blockIdx.x, p.B * p.Hq, rank, bh);
-    const int qt = CAUSAL ? nqt - 1 - rank : rank;
-    const int b = bh / p.Hq, hq = bh - b * p.Hq, hkv = hq / p.G;
-    const uint16_t* Qg = p.q16 + (size_t)bh * N * D;
-    const uint16_t* dOg = p.do16 + (size_t)bh * N * D;
-    const uint16_t* Kg = p.k16 + ((size_t)b * p.Hkv + hkv) * N * D;
-    const uint16_t* Vg = p.v16 + ((size_t)b * p.Hkv + hkv) * N * D;
+    const int qt = causal ? nqt - 1 - rank : rank;   // heaviest first when causal
+    const int b = bh / p.Hq, hq = bh - b * p.Hq;
+    const size_t bkv = (size_t)b * p.Hkv + hq / p.G;
+    const BufRes rk = make_bufres(p.k16 + bkv * Np * D, (uint32_t)Np * D * 2);
+    const BufRes rv = make_bufres(p.v16 + bkv * Np * D, (uint32_t)Np * D * 2);
+    const BufRes rkt = make_bufres(p.kT16 + bkv * D * Np, (uint32_t)Np * D * 2);
     const float sl2 = p.scales[0], c1 = p.scales[1];
 
     const int q0 = qt * kQ_WG;
     const int r0 = q0 + w * kQ_W;
+    const int qrow = r0 + l32;                       // < Np: padded rows are zero
     const int ntk = (N + kQ_N - 1) / kQ_N;
-    const int nt = CAUSAL ? min(ntk, (q0 + kQ_WG - 1) / kQ_N + 1) : ntk;
-    const bool wave_valid = r0 < N;
-    const int wave_last = CAUSAL ? min(ntk - 1, (r0 + kQ_W - 1) / kQ_N) : ntk - 1;
-
-    auto issue_tile = [&](int j, int buf) {
-#pragma unroll
-        for (int u = 0; u < LCH; ++u) {
-            const int slot = u * kThreads + tid;
-            int row, c;
-            unswz<D, 2>(slot, row, c);
-            gload_lds16(Kg + (size_t)min(j * kQ_N + row, N - 1) * D + c * 8,
-                        Ks + buf * TILE + (u * kThreads + w * 64) * 8);
-            unswz<D, 0>(slot, row, c);
-            gload_lds16(Vg + (size_t)min(j * kQ_N + row, N - 1) * D + c * 8,
-                        Vs + buf * TILE + (u * kThreads + w * 64) * 8);
-        }
-    };
-
-    // The workgroup's Q and dO rows, once (rows past N read row N-1; never stored).
-    // Both are read as the B operand: lane holds query column l32 of a 32-row
-    // block, d = ds*16 + hh*8 .. +7.
-#pragma unroll
-    for (int u = 0; u < OCH; ++u) {
-        const int slot = u * kThreads + tid;
-        int row, c;
-        unswz<D, 0>(slot, row, c);
-        const size_t src = (size_t)min(q0 + row, N - 1) * D + c * 8;
-        gload_lds16(dOg + src, dOs + (u * kThreads + w * 64) * 8);
-        gload_lds16(Qg + src, Qs + (u * kThreads + w * 64) * 8);
+    const int nt = causal ? min(ntk, (q0 + kQ_WG - 1) / kQ_N + 1) : ntk;
+    const int nfull = N / kQ_N;                      // key tiles with no key >= N
+    // Tiles [0, jfull) are unmasked for this wave, [jfull, jlast] masked.
+    // jA (wave 0's jfull) <= every wave's jfull: tiles below it run one code
+    // path on all waves. A wave past N runs those too (its rows are zero
+    // padding with P = 0) and then idles.
+    const int jA = causal ? min(nfull, q0 / kQ_N) : nfull;
+    int jfull = causal ? min(nfull, r0 / kQ_N) : nfull;
+    int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ_N) : ntk - 1;
+    if (r0 >= N) {
+        jfull = jA;
+        jlast = -1;
     }
 
-    float l2[2], dd[2], dacc[2] = {0.f, 0.f};
+    QState<D> S;
+    {
+        const size_t ro = ((size_t)bh * Np + qrow) * D;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int qrow = r0 + qb * 32 + l32;
-        const bool ok = qrow < N;
-        l2[qb] = ok ? p.lse2[(size_t)bh * N + qrow] : 0.f;
-        dd[qb] = ok ? p.delta[(size_t)bh * N + qrow] : 0.f;
-    }
-    f32x16 dq[DB][2], pk[DB][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            dq[db][qb] = zero16();
-            pk[db][qb] = zero16();
+        for (int ds = 0; ds < DS; ++ds) {
+            S.qf[ds] = *reinterpret_cast<const u32x4*>(p.q16 + ro + ds * 16 + hh * 8);
+            S.dof[ds] = *reinterpret_cast<const u32x4*>(p.do16 + ro + ds * 16 + hh * 8);
         }
+        S.l2 = p.lse2[(size_t)bh * Np + qrow];
+        S.dd = p.delta[(size_t)bh * Np + qrow];
+        S.dacc = 0.f;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        S.dq[db] = zero16();
+        S.pk[db] = zero16();
+    }
+    typename C::PlanR pr;
+    typename C::PlanT pt;
+    pr.init(w, lane, D);
+    pt.init(w, lane, Np);
+    const int abase = l32 * C::SR + hh * 16;
+    const int tbase = l32 * C::ST + hh * 16;
+    FA_LDS uint8_t* st0 = (FA_LDS uint8_t*)smem;
 
-    issue_tile(0, 0);
+    dq_copy<D>(pr, pt, rk, rv, rkt, 0, st0, w);
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < nt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nt) issue_tile(j + 1, buf ^ 1);
-        if (wave_valid && j <= wave_last) {
-            const int key0 = j * kQ_N;
-            const bool masked = (CAUSAL && key0 + kQ_N - 1 > r0) || (key0 + kQ_N > N);
-            dq_tile<D, CAUSAL>(Ks + buf * TILE, Vs + buf * TILE, dOs, Qs, dq, pk, dacc, l2, dd, masked,
-                               key0, r0, w * kQ_W, N, sl2, c1, lane);
-        }
+    // tile 0
+    dq_iteration<D>(S, pr, pt, nt > 1, rk, rv, rkt, 1, st0 + C::STAGE, st0, st0 + 2 * C::STAGE, 0, jfull, jlast,
+                    abase, tbase, qrow, N, causal, sl2, c1, w);
+    wait_vmem();
+    __syncthreads();
+    // steady state: every wave pipelines, and there is a next tile to copy
+    const int jS = min(jA, nt - 1);
+    for (int j = 1; j < jS; ++j) {
+        FA_LDS uint8_t* wst = st0 + ((j + 1) % 3) * C::STAGE;
+        const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
+        const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
+        dq_copy<D>(pr, pt, rk, rv, rkt, j + 1, wst, w);
+        dq_pipe<D, true>(S, cur, prv, abase, tbase, sl2, c1);
         wait_vmem();
         __syncthreads();
     }
+    // the diagonal / ragged tiles, where waves differ
+    for (int j = max(1, jS); j < nt; ++j) {
+        FA_LDS uint8_t* wst = st0 + ((j + 1) % 3) * C::STAGE;
+        const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
+        const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
+        dq_iteration<D>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, wst, cur, prv, j, jfull, jlast, abase, tbase,
+                        qrow, N, causal, sl2, c1, w);
+        wait_vmem();
+        __syncthreads();
+    }
+    if (jfull == nt && nt > 0) dq_drain<D>(S, st0 + ((nt - 1) % 3) * C::STAGE, tbase, sl2, c1);
 
-    if (wave_valid) {
-        uint16_t* dQg = p.dq + (size_t)bh * N * D;
+    // exact row dot (the lane halves hold half of the keys each), in units of 2^sS
+    const float dx = (S.dacc + swap_half(S.dacc)) * c1;
+    if (r0 < N && qrow < N) {
+        uint16_t* dQg = p.dq + ((size_t)bh * N + qrow) * D;
         const float sc = p.scales[4];
+        const float corr = S.dd - dx;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            const int qrow = r0 + qb * 32 + l32;
-            // exact row dot (both lane halves hold half of the keys), in units of 2^sS
-            const float dx = dacc[qb] + swap_half(dacc[qb]);
-            const float corr = dd[qb] - dx;
-            if (qrow < N) {
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
+            for (int u = 0; u < 4; ++u) {
+                float v4[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        float v4[4];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            v4[t] = fmaf(corr, pk[db][qb][u * 4 + t], dq[db][qb][u * 4 + t]) * sc;
-                        u32x2 val;
-                        val[0] = pack_bf16(v4[0], v4[1]);
-                        val[1] = pack_bf16(v4[2], v4[3]);
-                        *reinterpret_cast<u32x2*>(dQg + (size_t)qrow * D + db * 32 + u * 8 + hh * 4) = val;
-                    }
-                if (hh == 0) p.delta[(size_t)bh * N + qrow] = dx;   // for the dK/dV kernel
+                for (int t = 0; t < 4; ++t) v4[t] = fmaf(corr, S.pk[db][u * 4 + t], S.dq[db][u * 4 + t]) * sc;
+                u32x2 val;
+                val[0] = pack_bf16(v4[0], v4[1]);
+                val[1] = pack_bf16(v4[2], v4[3]);
+                *reinterpret_cast<u32x2*>(dQg + db * 32 + u * 8 + hh * 4) = val;
             }
-        }
+        if (hh == 0) p.delta[(size_t)bh * Np + qrow] = dx;   // for the dK/dV kernel
     }
 }
 
@@ -607,24 +1031,23 @@ hipError_t launch_prep_t(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_max_kernel, dim3(p.npart), dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long chunks = (long long)p.B * p.Hq * p.N * D / 8;
-    const long long want = (chunks + kThreads - 1) / kThreads;
-    const int grid = (int)(want < 4096 ? want : 4096);
+    const long long tiles = 2LL * p.B * (p.Hq + p.Hkv) * (p.Np / 64);
+    const int grid = (int)(tiles < 8192 ? tiles : 8192);
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D>
 hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
     const int grid = p.B * p.Hkv * ((p.N + kKV_WG - 1) / kKV_WG);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
     const int grid = p.B * p.Hq * ((p.N + kQ_WG - 1) / kQ_WG);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -632,10 +1055,11 @@ hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
 
 BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t rows = (size_t)B * Hq * N;
-    const size_t nq = rows * d, nk = (size_t)B * Hkv * N * d;
     BwdWorkspace w;
-    const size_t chunks = nq / 8;
+    w.Np = (N + kRowPad - 1) / kRowPad * kRowPad;
+    const size_t rows = (size_t)B * Hq * w.Np;
+    const size_t nq = rows * d, nk = (size_t)B * Hkv * w.Np * d;
+    const size_t chunks = (size_t)B * Hq * N * d / 8;
     const size_t want = (chunks + kThreads - 1) / kThreads;
     w.npart = (int)(want < 1024 ? (want > 0 ? want : 1) : 1024);
     size_t off = 0;
@@ -645,6 +1069,9 @@ BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d) {
     w.k16 = off; off += up(nk * 2);
     w.v16 = off; off += up(nk * 2);
     w.do16 = off; off += up(nq * 2);
+    w.qT16 = off; off += up(nq * 2);
+    w.doT16 = off; off += up(nq * 2);
+    w.kT16 = off; off += up(nk * 2);
     w.part = off; off += up((size_t)4 * w.npart * 4);
     w.scales = off; off += 256;
     w.total = off;
@@ -652,14 +1079,9 @@ BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d) {
 }
 
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream) {
-    const bool c = p.causal != 0;
     if (stage == 0) return p.d == 128 ? launch_prep_t<128>(p, stream) : launch_prep_t<64>(p, stream);
-    if (stage == 1) {
-        if (p.d == 128) return c ? launch_dq_t<128, true>(p, stream) : launch_dq_t<128, false>(p, stream);
-        return c ? launch_dq_t<64, true>(p, stream) : launch_dq_t<64, false>(p, stream);
-    }
-    if (p.d == 128) return c ? launch_dkdv_t<128, true>(p, stream) : launch_dkdv_t<128, false>(p, stream);
-    return c ? launch_dkdv_t<64, true>(p, stream) : launch_dkdv_t<64, false>(p, stream);
+    if (stage == 1) return p.d == 128 ? launch_dq_t<128>(p, stream) : launch_dq_t<64>(p, stream);
+    return p.d == 128 ? launch_dkdv_t<128>(p, stream) : launch_dkdv_t<64>(p, stream);
 }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {

@@ -19,7 +19,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that the body
+// can use i in constant expressions (fully unrolled schedules).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
@@ -45,6 +59,26 @@ __device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const 
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
+
+// acc += a * b on fp16 operands, with the accumulator in AGPRs. Meant for
+// accumulators that only MFMAs touch until an epilogue: they then stay out of
+// the 256 architectural VGPRs, which the operands and the vector-ALU work
+// need. The compiler does not look inside the asm, so the caller keeps the
+// hazard rules of gfx950 itself:
+//  * a vector-ALU write of a or b needs 2 wait states before this instruction
+//    (mfma32h_agpr_after_valu inserts them);
+//  * acc set by the vector ALU (zeroing) needs agpr_fence() before the first
+//    use, and any read of acc after the last MFMA needs agpr_fence() too.
+// Back-to-back accumulation into the same registers needs no wait states.
+__device__ __forceinline__ void mfma32h_agpr(f32x16& acc, const u32x4& a, const u32x4& b) {
+    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32h_agpr_after_valu(f32x16& acc, const u32x4& a, const u32x4& b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states: more than a 32x32 MFMA's result needs before other
+// instructions read it.
+__device__ __forceinline__ void agpr_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
@@ -87,6 +121,25 @@ __device__ __forceinline__ void gload_lds4(const float* g, FA_LDS float* lds_wav
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
                                      (FA_LDS void*)(lds_wave_base), 4, 0, 0);
 }
+// Buffer resources and buffer -> LDS copies. A raw resource (stride 0) covers
+// [base, base + bytes); loads outside it return zeros. Word 3 selects the
+// 32-bit data format that raw buffer loads on gfx9-family chips expect.
+// buffer_load ... lds is the MUBUF twin of global_load_lds: lane i's bytes from
+// offset voff + soff land at lds_wave_base + size * i, counted by vmcnt. The
+// compiler treats an in-flight global (FLAT) LDS load as a possible
+// out-of-order LDS access and then waits for every outstanding LDS read
+// (lgkmcnt(0)) before each use; with the buffer form its waits stay exact.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+__device__ __forceinline__ BufRes make_bufres(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void bload_lds16(BufRes r, uint32_t voff, uint32_t soff, FA_LDS void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bload_lds4(BufRes r, uint32_t voff, uint32_t soff, FA_LDS void* lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 4, voff, soff, 0, 0);
+}
+
 // s_waitcnt vmcnt(0): all of this wave's vector-memory loads have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -194,6 +247,44 @@ __device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ g, int ro
         gload_lds16(g + (size_t)gr * D + c * 8, (FA_LDS uint16_t*)(tile + u * 1024));
     }
 }
+
+// Copy of a padded tile through a buffer resource, with each lane's source
+// offsets computed once. Source row r of the tile starts `pitch` elements
+// after row r - 1 and holds ELEMS 16-bit values; the tile has ROWS rows of
+// STRIDE bytes. Rows past the resource's end read as zeros. Every wave issues
+// exactly NT loads per copy (a wave with no block left re-copies the tile's
+// last block: the same bytes to the same place).
+template <int ELEMS, int STRIDE, int ROWS, int NW>
+struct CopyPlan {
+    static constexpr int SPR = STRIDE / 16;
+    static constexpr int NB = padded_tile_bytes<STRIDE, ROWS>() / 1024;
+    static constexpr int NT = (NB + NW - 1) / NW;
+    uint32_t off[NT];   // byte offset of this lane's 16 bytes of block min(w + NW*t, NB - 1)
+
+    __device__ __forceinline__ void init(int w, int lane, int pitch) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int u = w + NW * t < NB ? w + NW * t : NB - 1;
+            const int slot = u * 64 + lane;
+            int row = slot / SPR, c = slot - (slot / SPR) * SPR;
+            if (c >= ELEMS / 8 || row >= ROWS) {   // padding slot: any in-tile source
+                c = 0;
+                row = row < ROWS ? row : ROWS - 1;
+            }
+            off[t] = (uint32_t)(row * pitch + c * 8) * 2u;
+        }
+    }
+    // soff: byte offset of the tile's first row in the resource (uniform);
+    // w: the wave index (uniform).
+    __device__ __forceinline__ void copy(BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile,
+                                         int w) const {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int u = w + NW * t < NB ? w + NW * t : NB - 1;
+            bload_lds16(r, off[t], soff, tile + u * 1024);
+        }
+    }
+};
 
 // 16-byte and transposed 8-byte reads at a byte offset into a padded tile.
 __device__ __forceinline__ u32x4 lds_read16b(const FA_LDS uint8_t* base, int byte_off) {

@@ -28,27 +28,37 @@ struct BwdParams {
     uint16_t* dq;        // bf16 outputs
     uint16_t* dk;
     uint16_t* dv;
-    // Workspace (device memory the caller provides; layout in bwd_workspace_layout):
-    float* delta;        // fp32 [B, Hq, N]: rowsum(dout * o), times the dS scale
-    float* lse2;         // fp32 [B, Hq, N]: lse * log2(e)
-    uint16_t* q16;       // fp16 copies of q, k, v, dout, each scaled by a power of two
-    uint16_t* k16;
+    // Workspace (device memory the caller provides; layout in bwd_workspace_layout).
+    // Per-row arrays and the fp16 copies hold Np = N rounded up to a multiple of
+    // kRowPad rows per head; rows N .. Np-1 are padding the preparation writes
+    // (zero data, D = 0, LSE = +inf), so tiles never read past an array.
+    float* delta;        // fp32 [B, Hq, Np]: row dot D times the dS scale
+    float* lse2;         // fp32 [B, Hq, Np]: lse * log2(e)
+    uint16_t* q16;       // fp16 [B, Hq, Np, d] copies of q, k, v, dout, each scaled by a power of two
+    uint16_t* k16;       // fp16 [B, Hkv, Np, d]
     uint16_t* v16;
     uint16_t* do16;
+    uint16_t* qT16;      // fp16 [B, Hq, d, Np] transposed copies of q, dout and k; inside every
+    uint16_t* doT16;     // group of 16 rows the row order is permuted (bits 2 and 3 of the row
+    uint16_t* kT16;      // index swapped), the k order of the MFMA operand they feed
     uint32_t* part;      // [4][npart] partial max |x| of q, k, v, dout (bf16 magnitude bits)
     float* scales;       // [8] derived constants, written by the preparation kernel
     int npart;           // workgroups of the max-reduction kernel
     int B, Hq, Hkv, N, d, G;
+    int Np;              // padded rows per head
     int causal;
     float scale;
     float scale_log2;
 };
 
+constexpr int kRowPad = 128;   // row padding unit of the backward workspace
+
 // Byte offsets of the backward workspace arrays; every array starts on a
 // 256-byte boundary.
 struct BwdWorkspace {
-    size_t delta, lse2, q16, k16, v16, do16, part, scales, total;
+    size_t delta, lse2, q16, k16, v16, do16, qT16, doT16, kT16, part, scales, total;
     int npart;
+    int Np;
 };
 BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d);
 
@@ -57,7 +67,7 @@ BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d);
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 // One backward stage: 0 = preparation (scales, fp16 copies, row dot D,
-// log2-scaled LSE), 1 = dK/dV, 2 = dQ.
+// log2-scaled LSE), 1 = dQ (and the exact row dot), 2 = dK/dV.
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream);
 
 // Launch geometry, exposed for logging and tests of the host logic.

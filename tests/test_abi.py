@@ -106,15 +106,17 @@ def test_bwd_checks():
 @pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 1, 1, 1, 64), (4, 16, 16, 2048, 64), (2, 32, 8, 16384, 128),
                                           (1, 8, 8, 131072, 128), (3, 5, 5, 77, 128)])
 def test_workspace_size(B, Hq, Hkv, N, d):
-    # D and the log2-scaled LSE (fp32 per query row), fp16 copies of q, k, v and
-    # dout, and at most 16 KiB of reduction scratch plus 256 bytes of constants;
-    # every array rounded up to 256 bytes
+    # Per head, rows padded to Np = N rounded up to 128: D and the log2-scaled
+    # LSE (fp32 per query row), fp16 copies of q, k, v and dout, transposed
+    # fp16 copies of q, dout and k, and at most 16 KiB of reduction scratch plus
+    # 256 bytes of constants; every array rounded up to 256 bytes
     got = fa.bwd_workspace_size(B, Hq, Hkv, N, d, 1)
 
     def up(x):
         return x + (-x) % 256
-    rows, nq, nk = B * Hq * N, B * Hq * N * d, B * Hkv * N * d
-    core = 2 * up(4 * rows) + 2 * up(2 * nq) + 2 * up(2 * nk)
+    Np = -(-N // 128) * 128
+    rows, nq, nk = B * Hq * Np, B * Hq * Np * d, B * Hkv * Np * d
+    core = 2 * up(4 * rows) + 4 * up(2 * nq) + 3 * up(2 * nk)
     assert got % 256 == 0 and core + 256 < got <= core + 256 + up(16 * 1024)
 
 
