@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int N = p.N, Np = p.Np, G = p.G;
     const bool causal = p.causal != 0;
@@ -914,7 +914,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int N = p.N, Np = p.Np;
     const bool causal = p.causal != 0;

@@ -275,13 +275,45 @@ struct CopyPlan {
         }
     }
     // soff: byte offset of the tile's first row in the resource (uniform);
-    // w: the wave index (uniform).
+    // w: the wave index. It is made scalar here, at the copy, rather than once
+    // per kernel: a scalar wave index held across the whole kernel has been
+    // seen to make the register allocator copy accumulators around.
+    __device__ __forceinline__ void copy(BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile,
+                                         int w) const {
+        const int ws = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int u = ws + NW * t < NB ? ws + NW * t : NB - 1;
+            bload_lds16(r, off[t], soff, tile + u * 1024);
+        }
+    }
+};
+
+// The same copy with the per-lane offsets recomputed at every copy (a few
+// vector-ALU instructions per 1 KiB block) instead of held in registers, for
+// kernels short of registers.
+template <int ELEMS, int STRIDE, int ROWS, int NW>
+struct CopyPlanLite {
+    static constexpr int SPR = STRIDE / 16;
+    static constexpr int NB = padded_tile_bytes<STRIDE, ROWS>() / 1024;
+    static constexpr int NT = (NB + NW - 1) / NW;
+    int lane_, pitch_;
+    __device__ __forceinline__ void init(int, int lane, int pitch) {
+        lane_ = lane;
+        pitch_ = pitch;
+    }
     __device__ __forceinline__ void copy(BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile,
                                          int w) const {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int u = w + NW * t < NB ? w + NW * t : NB - 1;
-            bload_lds16(r, off[t], soff, tile + u * 1024);
+            const int slot = u * 64 + lane_;
+            int row = slot / SPR, c = slot - (slot / SPR) * SPR;
+            if (c >= ELEMS / 8 || row >= ROWS) {
+                c = 0;
+                row = row < ROWS ? row : ROWS - 1;
+            }
+            bload_lds16(r, (uint32_t)(row * pitch_ + c * 8) * 2u, soff, tile + u * 1024);
         }
     }
 };

@@ -57,6 +57,8 @@ struct FwdCfg {
     static constexpr int KT = padded_tile_bytes<SK, kBN>();
     static constexpr int VT = padded_tile_bytes<SV, kBN>();
     static constexpr int LDS = 3 * KT + 2 * VT;
+    using PlanK = CopyPlan<D, SK, kBN, kWaves>;
+    using PlanV = CopyPlan<D, SV, kBN, kWaves>;
 };
 
 // Workgroup id -> (rank, bh). Workgroups are handed to the 8 XCDs round-robin,
@@ -259,17 +261,17 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, int h, f32x16&
 // reads do not touch the LDS the in-flight global->LDS copies write, so it does
 // not wait for those copies before each read.
 template <int D>
-__device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, const uint16_t* Kg,
-                                              const uint16_t* Vg, FA_LDS uint8_t* __restrict__ Kw,
+__device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, const typename FwdCfg<D>::PlanK& pk,
+                                              const typename FwdCfg<D>::PlanV& pv, BufRes rk, BufRes rv,
+                                              FA_LDS uint8_t* __restrict__ Kw,
                                               FA_LDS uint8_t* __restrict__ Vw,
                                               const FA_LDS uint8_t* __restrict__ Kr0,
                                               const FA_LDS uint8_t* __restrict__ Kr1,
                                               const FA_LDS uint8_t* __restrict__ Vr, int kbase, int vbase,
                                               bool valid, bool causal, int qrow, int N, int lastc,
                                               float sl2, int w, int lane) {
-    using C = FwdCfg<D>;
-    if (j + 2 < nt) copy_tile<D, C::SK, kBN, kWaves>(Kg, (j + 2) * kBN, N, Kw, w, lane);
-    if (j + 1 < nt) copy_tile<D, C::SV, kBN, kWaves>(Vg, (j + 1) * kBN, N, Vw, w, lane);
+    if (j + 2 < nt) pk.copy(rk, (uint32_t)(j + 2) * kBN * D * 2, Kw, w);
+    if (j + 1 < nt) pv.copy(rv, (uint32_t)(j + 1) * kBN * D * 2, Vw, w);
     if (valid) {
         const int hh = lane >> 5;
         fwd_chunk<D>(st, 2 * j, 0, st.sA, st.sB, Kr0, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh);
@@ -288,7 +290,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     FA_LDS uint8_t* Ks = (FA_LDS uint8_t*)smem;          // 3 K tiles
     FA_LDS uint8_t* Vs = Ks + 3 * C::KT;                   // 2 V tiles
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5, g = lane >> 4;
     const int N = p.N;
     const bool causal = p.causal != 0;
@@ -323,10 +326,19 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     st.l = 0.f;
     st.mc = 0.f;
 
+    // K and V through buffer resources covering the head's N rows: rows of a
+    // ragged last tile past N read as zeros (their scores are masked).
+    const BufRes rk = make_bufres(Kg, (uint32_t)N * D * 2);
+    const BufRes rv = make_bufres(Vg, (uint32_t)N * D * 2);
+    typename C::PlanK pk;
+    typename C::PlanV pv;
+    pk.init(w, lane, D);
+    pv.init(w, lane, D);
+
     // K tiles 0, 1 and V tile 0 before the loop.
-    copy_tile<D, C::SK, kBN, kWaves>(Kg, 0, N, Ks, w, lane);
-    if (nt > 1) copy_tile<D, C::SK, kBN, kWaves>(Kg, kBN, N, Ks + C::KT, w, lane);
-    copy_tile<D, C::SV, kBN, kWaves>(Vg, 0, N, Vs, w, lane);
+    pk.copy(rk, 0, Ks, w);
+    if (nt > 1) pk.copy(rk, kBN * D * 2, Ks + C::KT, w);
+    pv.copy(rv, 0, Vs, w);
     wait_vmem();
     __syncthreads();
 
@@ -335,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         st.mc = chunk_max(st.sA, sl2);
     }
     for (int j = 0; j < nt; ++j) {
-        fwd_iteration<D>(st, j, nt, Kg, Vg, Ks + ((j + 2) % 3) * C::KT, Vs + ((j + 1) & 1) * C::VT,
+        fwd_iteration<D>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT, Vs + ((j + 1) & 1) * C::VT,
                          Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT, Vs + (j & 1) * C::VT, kbase,
                          vbase, wave_valid, causal, qrow, N, lastc, sl2, w, lane);
         wait_vmem();
