@@ -341,6 +341,55 @@ struct KvState {
     f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: lane holds key l32, d rows db*32 + (i/4)*8 + hh*4 + i%4
 };
 
+// Where one step's data sits: the byte offsets, in the resources of the K/V
+// head's query-head group, of 64 rows from q0 of group member g.
+struct KvRes {
+    BufRes q, dout, qt, dot, l2, dd;
+};
+struct KvSrc {
+    uint32_t rows;   // q16 / do16 rows
+    uint32_t tr;     // qT16 / doT16 columns
+    uint32_t row4;   // lse2 / delta
+};
+
+// The copy of the next step, spread over the MFMA slots of a pipelined step.
+// A wave waits at each direct-to-LDS load until the memory pipeline accepts it
+// (about 1 KiB per 20 cycles per CU), so loads issued back to back stall it for
+// a long stretch; one load every few MFMAs hides under them.
+template <int D>
+struct KvNext {
+    const typename KvCfg<D>::PlanR& pr;
+    const typename KvCfg<D>::PlanT& pt;
+    const KvRes& rs;
+    KvSrc x;
+    int ws;     // wave index (scalar)
+    int lane;
+};
+
+// Copy item c of a step: [0, NT) Q rows, [NT, 2NT) dO rows, [2NT, 3NT) Q^T,
+// [3NT, 4NT) dO^T (one 1 KiB block per wave each), 4NT the LSE and D rows
+// (waves 0 and 2 copy LSE, 1 and 3 copy D: the same bytes twice).
+template <int D, int c>
+__device__ __forceinline__ void kv_copy_item(const KvNext<D>& nx, FA_LDS uint8_t* __restrict__ st) {
+    using C = KvCfg<D>;
+    using PR = typename C::PlanR;
+    using PT = typename C::PlanT;
+    constexpr int NT = PR::NT;
+    static_assert(PT::NT == NT, "row and transposed tiles take the same number of loads");
+    if constexpr (c < 2 * NT) {
+        constexpr int t = c % NT;
+        const int u = min(nx.ws + 4 * t, PR::NB - 1);
+        bload_lds16(c < NT ? nx.rs.q : nx.rs.dout, nx.pr.off[t], nx.x.rows, st + (c < NT ? C::QR : C::DOR) + u * 1024);
+    } else if constexpr (c < 4 * NT) {
+        constexpr int t = c % NT;
+        const int u = min(nx.ws + 4 * t, PT::NB - 1);
+        bload_lds16(c < 3 * NT ? nx.rs.qt : nx.rs.dot, nx.pt.off[t], nx.x.tr, st + (c < 3 * NT ? C::QT : C::DOT) + u * 1024);
+    } else {
+        const bool odd = nx.ws & 1;
+        bload_lds4(odd ? nx.rs.dd : nx.rs.l2, nx.lane * 4, nx.x.row4, st + (odd ? C::DD : C::L2));
+    }
+}
+
 // Lane bases (bytes): abase = l32 * SR + hh * 16 for the Q / dO row operands
 // (row qb*32 + l32, d = ds*16 + hh*8 ..); tbase = l32 * ST + hh * 16 for the
 // transposed operands (d row db*32 + l32, positions qc*16 + hh*8 ..);
@@ -349,11 +398,16 @@ struct KvState {
 // One unmasked step, interleaved by hand: MFMA slot n issues its MFMA, starts
 // the LDS read of slot n + 3's operand and runs its share of the softmax
 // tasks; a scheduling barrier closes every slot.
-template <int D>
+// With COPY, the next step's copy into `wst` is issued item by item, one item
+// every SP slots.
+template <int D, bool COPY>
 __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S, int abase,
-                                        int tbase, int lbase, float sl2, float c1) {
+                                        int tbase, int lbase, float sl2, float c1, const KvNext<D>* nx,
+                                        FA_LDS uint8_t* __restrict__ wst) {
     using C = KvCfg<D>;
     constexpr int DS = C::DS, DB = C::DB, NS = C::NS, PF = 3;
+    constexpr int NITEM = 4 * C::PlanR::NT + 1, SP = NS / NITEM;
+    static_assert(SP >= 1 && 1 + (NITEM - 1) * SP < NS, "copy items fit the slots");
     f32x16 s[2], dp[2];
     u32x4 pp[4], dsp[4];
     f32x4 lv[2][4], dv4[2][4];
@@ -433,6 +487,8 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
                 else lv[h][u] = x;
             }
         }
+        if constexpr (COPY && n >= 1 && (n - 1) % SP == 0 && (n - 1) / SP < NITEM)
+            kv_copy_item<D, (n - 1) / SP>(*nx, wst);
         constexpr int t0 = kv_task_begin<D>(n), t1 = kv_task_begin<D>(n + 1);
         static_for<t1 - t0>([&](auto k) { task(std::integral_constant<int, t0 + decltype(k)::value>{}); });
         __builtin_amdgcn_sched_barrier(0);
@@ -495,17 +551,6 @@ __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict_
         }
 }
 
-// Where one step's data sits: the byte offsets, in the resources of the K/V
-// head's query-head group, of 64 rows from q0 of group member g.
-struct KvRes {
-    BufRes q, dout, qt, dot, l2, dd;
-};
-struct KvSrc {
-    uint32_t rows;   // q16 / do16 rows
-    uint32_t tr;     // qT16 / doT16 columns
-    uint32_t row4;   // lse2 / delta
-};
-
 template <int D>
 __device__ __forceinline__ void kv_copy(const typename KvCfg<D>::PlanR& pr, const typename KvCfg<D>::PlanT& pt,
                                         const KvRes& rs, const KvSrc& x, FA_LDS uint8_t* __restrict__ st, int w,
@@ -533,7 +578,7 @@ __device__ __forceinline__ void kv_iteration(KvState<D>& S, const typename KvCfg
                                              int lane) {
     if (issue) kv_copy<D>(pr, pt, rs, nx, wst, w, lane);
     if (mode == 1)
-        kv_step<D>(rst, S, abase, tbase, lbase, sl2, c1);
+        kv_step<D, false>(rst, S, abase, tbase, lbase, sl2, c1, nullptr, nullptr);
     else if (mode == 2)
         kv_step_masked<D>(rst, S, abase, tbase, lbase, q0, key, sl2, c1, lane >> 5);
 }
@@ -614,12 +659,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     // Steps with q0 >= k0 + 128 (all but the last two row blocks when causal)
     // are unmasked for every wave, and run on one code path. A wave whose keys
     // lie past N runs them too (its keys are zero padding; never stored).
-    const int nsteady = causal ? G * max(0, nrb - 2) : nsteps;
+    const int nsteady = causal ? G * max(0, nrb - 2) : nsteps - 1;   // each has a next step to copy
     for (int j = 0; j < nsteady; ++j) {
-        const KvSrc nx = src_of(j + 1 < nsteps ? j + 1 : j);
+        const KvNext<D> nx{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane};
         FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
         const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
-        kv_iteration<D>(S, pr, pt, rs, j + 1 < nsteps, nx, wst, rst, 1, 0, key, abase, tbase, lbase, sl2, c1, w, lane);
+        kv_step<D, true>(rst, S, abase, tbase, lbase, sl2, c1, &nx, wst);
         wait_vmem();
         __syncthreads();
     }
@@ -730,15 +775,46 @@ __device__ __forceinline__ void dq_task(QState<D>& S, float sl2, float c1) {
     }
 }
 
+// The copy of the next tile, spread over the MFMA slots of a pipelined tile
+// (see KvNext): items [0, NT) K rows, [NT, 2NT) V rows, [2NT, 3NT) K^T.
+template <int D>
+struct QNext {
+    const typename QCfg<D>::PlanR& pr;
+    const typename QCfg<D>::PlanT& pt;
+    BufRes rk, rv, rkt;
+    uint32_t rows, tr;   // byte offsets of the tile in the row / transposed copies
+    int ws;              // wave index (scalar)
+};
+
+template <int D, int c>
+__device__ __forceinline__ void dq_copy_item(const QNext<D>& nx, FA_LDS uint8_t* __restrict__ st) {
+    using C = QCfg<D>;
+    using PR = typename C::PlanR;
+    using PT = typename C::PlanT;
+    constexpr int NT = PR::NT;
+    static_assert(PT::NT == NT, "row and transposed tiles take the same number of loads");
+    constexpr int t = c % NT;
+    if constexpr (c < 2 * NT) {
+        const int u = min(nx.ws + 4 * t, PR::NB - 1);
+        bload_lds16(c < NT ? nx.rk : nx.rv, nx.pr.off[t], nx.rows, st + (c < NT ? C::KR : C::VR) + u * 1024);
+    } else {
+        const int u = min(nx.ws + 4 * t, PT::NB - 1);
+        bload_lds16(nx.rkt, nx.pt.off[t], nx.tr, st + C::KT + u * 1024);
+    }
+}
+
 // One pipelined tile: `cur` holds tile j (K, V rows), `prv` tile j-1 (K^T).
 // PREV = false for a wave's first tile (no previous products or tasks).
 // Lane bases: abase = l32 * SR + hh * 16, tbase = l32 * ST + hh * 16.
-template <int D, bool PREV>
+// With COPY, the next tile's copy into `wst` is issued one item every SP slots.
+template <int D, bool PREV, bool COPY>
 __device__ __forceinline__ void dq_pipe(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
                                         const FA_LDS uint8_t* __restrict__ prv, int abase, int tbase,
-                                        float sl2, float c1) {
+                                        float sl2, float c1, const QNext<D>* nx, FA_LDS uint8_t* __restrict__ wst) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, NS = C::NS, PF = 3, START = C::START;
+    constexpr int NITEM = 3 * C::PlanR::NT, SP = NS / NITEM;
+    static_assert(SP >= 1 && 1 + (NITEM - 1) * SP < NS, "copy items fit the slots");
     // product group g -> key chunk of the previous tile
     constexpr int kc_of[8] = {0, 1, -1, -1, 2, 3, -1, -1};
     u32x4 ring[PF + 1];
@@ -790,6 +866,8 @@ __device__ __forceinline__ void dq_pipe(QState<D>& S, const FA_LDS uint8_t* __re
             using NX = std::integral_constant<int, n + PF>;
             if constexpr (has_read(NX{})) ring[(n + PF) % (PF + 1)] = frag(NX{});
         }
+        if constexpr (COPY && n >= 1 && (n - 1) % SP == 0 && (n - 1) / SP < NITEM)
+            dq_copy_item<D, (n - 1) / SP>(*nx, wst);
         if constexpr (n < START) {
             if constexpr (PREV) {
                 constexpr int t0 = dq_task_begin<D>(n + NS), t1 = dq_task_begin<D>(n + NS + 1);
@@ -899,8 +977,8 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
                                              float sl2, float c1, int w) {
     if (issue) dq_copy<D>(pr, pt, rk, rv, rkt, jn, wst, w);
     if (j < jfull) {
-        if (j == 0) dq_pipe<D, false>(S, cur, prv, abase, tbase, sl2, c1);
-        else dq_pipe<D, true>(S, cur, prv, abase, tbase, sl2, c1);
+        if (j == 0) dq_pipe<D, false, false>(S, cur, prv, abase, tbase, sl2, c1, nullptr, nullptr);
+        else dq_pipe<D, true, false>(S, cur, prv, abase, tbase, sl2, c1, nullptr, nullptr);
     } else {
         if (j == jfull && j > 0) dq_drain<D>(S, prv, tbase, sl2, c1);
         if (j <= jlast) dq_masked<D>(S, cur, abase, tbase, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1);
@@ -986,8 +1064,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         FA_LDS uint8_t* wst = st0 + ((j + 1) % 3) * C::STAGE;
         const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
         const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
-        dq_copy<D>(pr, pt, rk, rv, rkt, j + 1, wst, w);
-        dq_pipe<D, true>(S, cur, prv, abase, tbase, sl2, c1);
+        const QNext<D> nx{pr, pt, rk, rv, rkt, (uint32_t)(j + 1) * kQ_N * D * 2, (uint32_t)(j + 1) * kQ_N * 2,
+                          __builtin_amdgcn_readfirstlane(w)};
+        dq_pipe<D, true, true>(S, cur, prv, abase, tbase, sl2, c1, &nx, wst);
         wait_vmem();
         __syncthreads();
     }
