@@ -16,8 +16,10 @@ it runs on. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -64,6 +66,39 @@ def algorithmic(w) -> dict:
     }
 
 
+# Sources each timed kernel is built from (hashed to tie a traffic record to the kernel it measured).
+KERNEL_SOURCES = {
+    "fwd": ("fa_fwd.hip", "fa_device.h", "fa_params.h"),
+    "bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_params.h"),
+    "bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_params.h"),
+}
+
+
+def sources_sha256(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_io_aware_60_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic_<workload>.md: FETCH_SIZE and WRITE_SIZE, each scaled by what
+    the counter reads for a 1 GiB device copy), or None when there is no record or
+    the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.md")
+    if not os.path.exists(path):
+        return None
+    want = sources_sha256(kernel)
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"traffic-record: kernel=(\w+) bytes=(\d+) sources_sha256=(\w+)", line.strip())
+            if m and m.group(1) == kernel and m.group(3) == want:
+                return int(m.group(2))
+    return None
+
+
 def cpu_baseline(w) -> dict:
     """The fp64 oracle timed on the host cores on a bounded sample: the first
     (batch, K/V head) group (its G query heads) restricted to the first
@@ -96,6 +131,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (3 times) after the timed steps, so that one "
+                         "profiled run holds the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the attention path here is single-GPU (asked for --gpus {args.gpus}).",
@@ -163,12 +201,23 @@ def main() -> int:
     bwd_ms = kavg["bwd_pre"] + kavg["bwd_dkdv"] + kavg["bwd_dq"]
     value = (fwd_flop + bwd_flop) / step_ms / 1e9
 
+    if args.copy_calibration > 0:
+        # reads and writes exactly copy_calibration MiB per launch
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=q.device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     alg = algorithmic(w)
     dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kavg[n])
     kind, amount = alg[dom]
     achieved = amount / (kavg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
+                "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
                 "avg_launch_ms": kavg[dom], "algorithmic_flop_per_launch": amount}
 
     out = {

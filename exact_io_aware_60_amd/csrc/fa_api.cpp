@@ -200,6 +200,6 @@ const char* flash_attn_strerror(int status) {
     }
 }
 
-const char* flash_attn_version(void) { return "0.2.0 gfx950"; }
+const char* flash_attn_version(void) { return "0.3.0 gfx950"; }
 
 }  // extern "C"

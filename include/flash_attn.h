@@ -26,8 +26,9 @@
  * contiguous [B, Hq, N] float32 (natural log). There are no stride arguments.
  *
  * Supported shapes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128};
- * B*Hq*N*d < 2^62. scale must be finite and >= 0. Other shapes return an error;
- * there is no fallback path.
+ * B*Hq*N*d < 2^62; (N + 128) * d < 2^31 and (Hq / Hkv) * (N + 128) * d * 2 <
+ * 2^32 (32-bit offsets inside one head and one query-head group). scale must
+ * be finite and >= 0. Other shapes return an error; there is no fallback path.
  *
  * Pointers are device pointers (hipMalloc'd or equivalent), 16-byte aligned.
  * `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
@@ -78,11 +79,13 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for these arguments, or 0 for
- * shapes the backward rejects. The workspace holds two fp32 values per query
- * row (D = rowsum(dout * o) and LSE * log2(e)), fp16 copies of q, k, v and
- * dout scaled by powers of two (the operands of the backward's products), and
- * a few KiB of reduction scratch: about 2 * (|q| + |k| + |v| + |dout|) bytes
- * plus 8 bytes per query row.
+ * shapes the backward rejects. Per head, rows are padded to Np = N rounded up
+ * to a multiple of 128. The workspace holds two fp32 values per padded query
+ * row (D = rowsum(dout * o) and LSE * log2(e)); fp16 copies of q, k, v and dout
+ * scaled by powers of two, [.., Np, d]; transposed fp16 copies of q, dout and
+ * k, [.., d, Np] (the operands of the backward's products); and a few KiB of
+ * reduction scratch. In all, about 4 * |q| + 3 * |k| bytes for the bf16 sizes
+ * |q| = B*Hq*N*d*2 and |k| = B*Hkv*N*d*2, plus 8 bytes per query row.
  */
 size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal);
 
@@ -99,8 +102,9 @@ size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int c
  *                           flash_attn_bwd_workspace_size(...); contents on
  *                           entry are ignored and on return are unspecified
  * Outputs must not overlap inputs or each other. Runs four kernels in order on
- * `stream`: max |x| of q, k, v, dout; preparation (scaled fp16 copies, the row
- * dot D from o, the log2-scaled LSE); dQ, which also forms the exact row dot
+ * `stream`: max |x| of q, k, v, dout; preparation (scaled fp16 copies and
+ * transposed copies, the row dot D from o, the log2-scaled LSE); dQ, which
+ * also forms the exact row dot
  * D_i = sum_j P_ij dP_ij from the rebuilt probabilities, corrects its own
  * result with it and stores it; dK/dV, which uses that exact D. Deterministic:
  * the same inputs give bit-identical outputs (no atomics). Inputs must be
@@ -141,7 +145,7 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
 
-/* Library version and the GPU target it was compiled for, e.g. "0.2.0 gfx950". */
+/* Library version and the GPU target it was compiled for, e.g. "0.3.0 gfx950". */
 const char* flash_attn_version(void);
 
 #ifdef __cplusplus
