@@ -77,6 +77,24 @@ namespace {
 
 constexpr int kThreads = 256;   // 4 waves, one per SIMD
 
+// Per-lane fragment addresses in a stage of either backward kernel. Row tiles
+// ([64 x D], padded rows of SR bytes) are read at one lane base plus constants:
+// row(b, ds) is row b*32 + l32, d = ds*16 + hh*8 ... Transposed tiles
+// ([D x 64]) are read through T (Swz128 or PadRows): t.read(tile, b*32, c) is
+// d row b*32 + l32, positions c*16 + hh*8 ... Swizzled row tiles would need a
+// table of eight lane offsets, which the register budget of these kernels does
+// not have.
+template <int SR, class T>
+struct LaneAddr {
+    int rbase;          // l32 * SR + hh * 16
+    T t;
+    __device__ __forceinline__ void init(int l32, int hh) {
+        rbase = l32 * SR + hh * 16;
+        t.init(l32, hh);
+    }
+    __device__ __forceinline__ int row(int b, int ds) const { return rbase + b * 32 * SR + ds * 32; }
+};
+
 // Keeps a value in place: the compiler may not move its computation across a
 // scheduling barrier that follows.
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
@@ -305,10 +323,9 @@ constexpr int kKV_Q = 64;     // query rows per step
 template <int D>
 struct KvCfg {
     static constexpr int DS = D / 16, DB = D / 32;
-    static constexpr int SR = RowPad<D>::STRIDE;       // Q, dO rows: [64][D]
-    static constexpr int ST = RowPad<kKV_Q>::STRIDE;   // Q^T, dO^T: [D][64]
+    static constexpr int SR = RowPad<D>::STRIDE;       // Q, dO rows: [64][D], padded rows
     static constexpr int RT = padded_tile_bytes<SR, kKV_Q>();
-    static constexpr int TT = padded_tile_bytes<ST, D>();
+    static constexpr int TT = D * 2 * kKV_Q;            // Q^T, dO^T: [D][64], swizzled
     static constexpr int QR = 0, DOR = RT, QT = 2 * RT, DOT = 2 * RT + TT;
     static constexpr int L2 = 2 * RT + 2 * TT, DD = L2 + 4 * kKV_Q;   // 64 floats each
     static constexpr int STAGE = DD + 4 * kKV_Q;
@@ -325,8 +342,10 @@ struct KvCfg {
     static constexpr int START = DS + 1;
     static constexpr int END = 4 * DS + 6 * DB;
     using PlanR = CopyPlan<D, SR, kKV_Q, 4>;
-    using PlanT = CopyPlan<kKV_Q, ST, D, 4>;
+    using PlanT = CopyPlanSwz<2 * kKV_Q, D, 4>;
+    using Addr = LaneAddr<SR, Swz128>;
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(QT % 128 == 0 && DOT % 128 == 0 && STAGE % 128 == 0, "swizzled tiles start on 128 bytes");
 };
 
 template <int D>
@@ -366,34 +385,27 @@ struct KvNext {
     int lane;
 };
 
-// Copy item c of a step: [0, NT) Q rows, [NT, 2NT) dO rows, [2NT, 3NT) Q^T,
-// [3NT, 4NT) dO^T (one 1 KiB block per wave each), 4NT the LSE and D rows
-// (waves 0 and 2 copy LSE, 1 and 3 copy D: the same bytes twice).
+// Copy item c of a step (one 1 KiB block per wave each): [0, NR) Q rows,
+// [NR, 2NR) dO rows, then NT blocks of Q^T and NT of dO^T, and last the LSE
+// and D rows (waves 0 and 2 copy LSE, 1 and 3 copy D: the same bytes twice).
 template <int D, int c>
 __device__ __forceinline__ void kv_copy_item(const KvNext<D>& nx, FA_LDS uint8_t* __restrict__ st) {
     using C = KvCfg<D>;
-    using PR = typename C::PlanR;
-    using PT = typename C::PlanT;
-    constexpr int NT = PR::NT;
-    static_assert(PT::NT == NT, "row and transposed tiles take the same number of loads");
-    if constexpr (c < 2 * NT) {
-        constexpr int t = c % NT;
-        const int u = min(nx.ws + 4 * t, PR::NB - 1);
-        bload_lds16(c < NT ? nx.rs.q : nx.rs.dout, nx.pr.off[t], nx.x.rows, st + (c < NT ? C::QR : C::DOR) + u * 1024);
-    } else if constexpr (c < 4 * NT) {
-        constexpr int t = c % NT;
-        const int u = min(nx.ws + 4 * t, PT::NB - 1);
-        bload_lds16(c < 3 * NT ? nx.rs.qt : nx.rs.dot, nx.pt.off[t], nx.x.tr, st + (c < 3 * NT ? C::QT : C::DOT) + u * 1024);
+    constexpr int NR = C::PlanR::NT, NT = C::PlanT::NT;
+    if constexpr (c < 2 * NR) {
+        nx.pr.copy_one(c % NR, c < NR ? nx.rs.q : nx.rs.dout, nx.x.rows, st + (c < NR ? C::QR : C::DOR), nx.ws);
+    } else if constexpr (c < 2 * NR + 2 * NT) {
+        constexpr int k = c - 2 * NR;
+        nx.pt.copy_one(k % NT, k < NT ? nx.rs.qt : nx.rs.dot, nx.x.tr, st + (k < NT ? C::QT : C::DOT), nx.ws);
     } else {
         const bool odd = nx.ws & 1;
         bload_lds4(odd ? nx.rs.dd : nx.rs.l2, nx.lane * 4, nx.x.row4, st + (odd ? C::DD : C::L2));
     }
 }
 
-// Lane bases (bytes): abase = l32 * SR + hh * 16 for the Q / dO row operands
-// (row qb*32 + l32, d = ds*16 + hh*8 ..); tbase = l32 * ST + hh * 16 for the
-// transposed operands (d row db*32 + l32, positions qc*16 + hh*8 ..);
-// lbase = hh * 16 for the per-row LSE / D values.
+// Fragment addresses: la.row(qb, ds) for the Q / dO row operands,
+// la.t.read(tile, db*32, qc) for the transposed ones; lbase = hh * 16 for the per-row
+// LSE / D values.
 
 // One unmasked step, interleaved by hand: MFMA slot n issues its MFMA, starts
 // the LDS read of slot n + 3's operand and runs its share of the softmax
@@ -401,12 +413,12 @@ __device__ __forceinline__ void kv_copy_item(const KvNext<D>& nx, FA_LDS uint8_t
 // With COPY, the next step's copy into `wst` is issued item by item, one item
 // every SP slots.
 template <int D, bool COPY>
-__device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S, int abase,
-                                        int tbase, int lbase, float sl2, float c1, const KvNext<D>* nx,
+__device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S,
+                                        const typename KvCfg<D>::Addr& la, int lbase, float sl2, float c1, const KvNext<D>* nx,
                                         FA_LDS uint8_t* __restrict__ wst) {
     using C = KvCfg<D>;
     constexpr int DS = C::DS, DB = C::DB, NS = C::NS, PF = 3;
-    constexpr int NITEM = 4 * C::PlanR::NT + 1, SP = NS / NITEM;
+    constexpr int NITEM = 2 * C::PlanR::NT + 2 * C::PlanT::NT + 1, SP = NS / NITEM;
     static_assert(SP >= 1 && 1 + (NITEM - 1) * SP < NS, "copy items fit the slots");
     f32x16 s[2], dp[2];
     u32x4 pp[4], dsp[4];
@@ -417,13 +429,11 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
         constexpr int n = decltype(nc)::value;
         if constexpr (n < 4 * DS) {
             constexpr int ph = n / DS, ds = n % DS, qb = ph >> 1;
-            constexpr int off = ((ph & 1) ? C::DOR : C::QR) + qb * 32 * C::SR + ds * 32;
-            return lds_read16b(st, abase + off);
+            return lds_read16b(st, la.row(qb, ds) + ((ph & 1) ? C::DOR : C::QR));
         } else {
             constexpr int m = n - 4 * DS, grp = m / (2 * DB);
             constexpr int qc = (grp >> 1) * 2 + (m % (2 * DB)) / DB, db = m % DB;
-            constexpr int off = ((grp & 1) ? C::QT : C::DOT) + db * 32 * C::ST + qc * 32;
-            return lds_read16b(st, tbase + off);
+            return la.t.read(st + ((grp & 1) ? C::QT : C::DOT), db * 32, qc);
         }
     };
     auto mfma_at = [&](auto nc, const u32x4& a) {
@@ -499,7 +509,7 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
 // Unpipelined; at most one per head and wave.
 template <int D>
 __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S,
-                                               int abase, int tbase, int lbase, int q0, int key, float sl2,
+                                               const typename KvCfg<D>::Addr& la, int lbase, int q0, int key, float sl2,
                                                float c1, int hh) {
     using C = KvCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
@@ -513,8 +523,8 @@ __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict_
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = mfma32h(lds_read16b(st, abase + C::QR + qb * 32 * C::SR + ds * 32), S.kf[ds], s[qb]);
-            dp[qb] = mfma32h(lds_read16b(st, abase + C::DOR + qb * 32 * C::SR + ds * 32), S.vf[ds], dp[qb]);
+            s[qb] = mfma32h(lds_read16b(st, la.row(qb, ds) + C::QR), S.kf[ds], s[qb]);
+            dp[qb] = mfma32h(lds_read16b(st, la.row(qb, ds) + C::DOR), S.vf[ds], dp[qb]);
         }
     u32x4 pp[4], dsp[4];
 #pragma unroll
@@ -545,9 +555,8 @@ __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict_
     for (int qc = 0; qc < 4; ++qc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int off = db * 32 * C::ST + qc * 32;
-            S.dv[db] = mfma32h(lds_read16b(st, tbase + C::DOT + off), pp[qc], S.dv[db]);
-            S.dk[db] = mfma32h(lds_read16b(st, tbase + C::QT + off), dsp[qc], S.dk[db]);
+            S.dv[db] = mfma32h(la.t.read(st + C::DOT, db * 32, qc), pp[qc], S.dv[db]);
+            S.dk[db] = mfma32h(la.t.read(st + C::QT, db * 32, qc), dsp[qc], S.dk[db]);
         }
 }
 
@@ -574,13 +583,13 @@ __device__ __forceinline__ void kv_iteration(KvState<D>& S, const typename KvCfg
                                              const KvSrc& nx,
                                              FA_LDS uint8_t* __restrict__ wst,
                                              const FA_LDS uint8_t* __restrict__ rst, int mode, int q0, int key,
-                                             int abase, int tbase, int lbase, float sl2, float c1, int w,
+                                             const typename KvCfg<D>::Addr& la, int lbase, float sl2, float c1, int w,
                                              int lane) {
     if (issue) kv_copy<D>(pr, pt, rs, nx, wst, w, lane);
     if (mode == 1)
-        kv_step<D, false>(rst, S, abase, tbase, lbase, sl2, c1, nullptr, nullptr);
+        kv_step<D, false>(rst, S, la, lbase, sl2, c1, nullptr, nullptr);
     else if (mode == 2)
-        kv_step_masked<D>(rst, S, abase, tbase, lbase, q0, key, sl2, c1, lane >> 5);
+        kv_step_masked<D>(rst, S, la, lbase, q0, key, sl2, c1, lane >> 5);
 }
 
 template <int D>
@@ -648,8 +657,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     typename C::PlanT pt;
     pr.init(w, lane, D);
     pt.init(w, lane, Np);
-    const int abase = l32 * C::SR + hh * 16;
-    const int tbase = l32 * C::ST + hh * 16;
+    typename C::Addr la;
+    la.init(l32, hh);
     const int lbase = hh * 16;
     FA_LDS uint8_t* st0 = (FA_LDS uint8_t*)smem;
 
@@ -664,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
         const KvNext<D> nx{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane};
         FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
         const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
-        kv_step<D, true>(rst, S, abase, tbase, lbase, sl2, c1, &nx, wst);
+        kv_step<D, true>(rst, S, la, lbase, sl2, c1, &nx, wst);
         wait_vmem();
         __syncthreads();
     }
@@ -676,7 +685,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
         const KvSrc nx = src_of(issue ? j + 1 : j);
         FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
         const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
-        kv_iteration<D>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, abase, tbase, lbase, sl2, c1, w, lane);
+        kv_iteration<D>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, la, lbase, sl2, c1, w, lane);
         wait_vmem();
         __syncthreads();
     }
@@ -709,9 +718,9 @@ constexpr int kQ_N = 64;     // keys per tile
 template <int D>
 struct QCfg {
     static constexpr int DS = D / 16, DB = D / 32;
-    static constexpr int SR = RowPad<D>::STRIDE;      // K, V rows: [64][D]
-    static constexpr int ST = RowPad<kQ_N>::STRIDE;   // K^T: [D][64]
+    static constexpr int SR = RowPad<D>::STRIDE;      // K, V rows: [64][D], padded rows
     static constexpr int RT = padded_tile_bytes<SR, kQ_N>();
+    static constexpr int ST = RowPad<kQ_N>::STRIDE;   // K^T: [D][64], padded rows
     static constexpr int TT = padded_tile_bytes<ST, D>();
     static constexpr int KR = 0, VR = RT, KT = 2 * RT;
     static constexpr int STAGE = 2 * RT + TT;
@@ -726,8 +735,11 @@ struct QCfg {
     // tile's first slots. Each group of 16 starts after its inputs are complete
     // and ends before the product that consumes it.
     static constexpr int START = 3 * DS + 1;
+    // K^T keeps padded rows here: swizzled ones, which copy no pad bytes and no
+    // duplicate blocks, measured slower in this kernel.
     using PlanR = CopyPlan<D, SR, kQ_N, 4>;
     using PlanT = CopyPlan<kQ_N, ST, D, 4>;
+    using Addr = LaneAddr<SR, PadRows<ST>>;
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -776,7 +788,7 @@ __device__ __forceinline__ void dq_task(QState<D>& S, float sl2, float c1) {
 }
 
 // The copy of the next tile, spread over the MFMA slots of a pipelined tile
-// (see KvNext): items [0, NT) K rows, [NT, 2NT) V rows, [2NT, 3NT) K^T.
+// (see KvNext): NR items of K rows, NR of V rows, then NT of K^T.
 template <int D>
 struct QNext {
     const typename QCfg<D>::PlanR& pr;
@@ -789,31 +801,24 @@ struct QNext {
 template <int D, int c>
 __device__ __forceinline__ void dq_copy_item(const QNext<D>& nx, FA_LDS uint8_t* __restrict__ st) {
     using C = QCfg<D>;
-    using PR = typename C::PlanR;
-    using PT = typename C::PlanT;
-    constexpr int NT = PR::NT;
-    static_assert(PT::NT == NT, "row and transposed tiles take the same number of loads");
-    constexpr int t = c % NT;
-    if constexpr (c < 2 * NT) {
-        const int u = min(nx.ws + 4 * t, PR::NB - 1);
-        bload_lds16(c < NT ? nx.rk : nx.rv, nx.pr.off[t], nx.rows, st + (c < NT ? C::KR : C::VR) + u * 1024);
-    } else {
-        const int u = min(nx.ws + 4 * t, PT::NB - 1);
-        bload_lds16(nx.rkt, nx.pt.off[t], nx.tr, st + C::KT + u * 1024);
-    }
+    constexpr int NR = C::PlanR::NT;
+    if constexpr (c < 2 * NR)
+        nx.pr.copy_one(c % NR, c < NR ? nx.rk : nx.rv, nx.rows, st + (c < NR ? C::KR : C::VR), nx.ws);
+    else
+        nx.pt.copy_one(c - 2 * NR, nx.rkt, nx.tr, st + C::KT, nx.ws);
 }
 
 // One pipelined tile: `cur` holds tile j (K, V rows), `prv` tile j-1 (K^T).
 // PREV = false for a wave's first tile (no previous products or tasks).
-// Lane bases: abase = l32 * SR + hh * 16, tbase = l32 * ST + hh * 16.
+// Fragment addresses: la.row(kb, ds) for K / V rows, la.t.read(tile, db*32, kc) for K^T.
 // With COPY, the next tile's copy into `wst` is issued one item every SP slots.
 template <int D, bool PREV, bool COPY>
 __device__ __forceinline__ void dq_pipe(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
-                                        const FA_LDS uint8_t* __restrict__ prv, int abase, int tbase,
+                                        const FA_LDS uint8_t* __restrict__ prv, const typename QCfg<D>::Addr& la,
                                         float sl2, float c1, const QNext<D>* nx, FA_LDS uint8_t* __restrict__ wst) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, NS = C::NS, PF = 3, START = C::START;
-    constexpr int NITEM = 3 * C::PlanR::NT, SP = NS / NITEM;
+    constexpr int NITEM = 2 * C::PlanR::NT + C::PlanT::NT, SP = NS / NITEM;
     static_assert(SP >= 1 && 1 + (NITEM - 1) * SP < NS, "copy items fit the slots");
     // product group g -> key chunk of the previous tile
     constexpr int kc_of[8] = {0, 1, -1, -1, 2, 3, -1, -1};
@@ -830,11 +835,10 @@ __device__ __forceinline__ void dq_pipe(QState<D>& S, const FA_LDS uint8_t* __re
         constexpr int g = n / DS, m = n % DS;
         if constexpr (kc_of[g] >= 0) {
             constexpr int db = m / 2;
-            return lds_read16b(prv, tbase + C::KT + db * 32 * C::ST + kc_of[g] * 32);
+            return la.t.read(prv + C::KT, db * 32, kc_of[g]);
         } else {
             constexpr int kb = g >= 6 ? 1 : 0;
-            constexpr int off = ((g & 1) ? C::VR : C::KR) + kb * 32 * C::SR + m * 32;
-            return lds_read16b(cur, abase + off);
+            return lds_read16b(cur, la.row(kb, m) + ((g & 1) ? C::VR : C::KR));
         }
     };
     auto mfma_at = [&](auto nc, const u32x4& a) {
@@ -884,7 +888,7 @@ __device__ __forceinline__ void dq_pipe(QState<D>& S, const FA_LDS uint8_t* __re
 // Finish the last pipelined tile: its remaining softmax tasks, then all of its
 // dQ / PK products (K^T from `prv`).
 template <int D>
-__device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __restrict__ prv, int tbase,
+__device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __restrict__ prv, const typename QCfg<D>::Addr& la,
                                          float sl2, float c1) {
     using C = QCfg<D>;
     constexpr int t0 = dq_task_begin<D>(C::NS);
@@ -893,7 +897,7 @@ __device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __r
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-            const u32x4 a = lds_read16b(prv, tbase + C::KT + db * 32 * C::ST + kc * 32);
+            const u32x4 a = la.t.read(prv + C::KT, db * 32, kc);
             S.pk[db] = mfma32h(a, S.pp[kc], S.pk[db]);
             S.dq[db] = mfma32h(a, S.dsp[kc], S.dq[db]);
         }
@@ -903,8 +907,8 @@ __device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __r
 // unpipelined. Keys past N are zero rows in the copies but would still get
 // P = exp2(-LSE), so they are masked like the ones above the diagonal.
 template <int D>
-__device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur, int abase,
-                                          int tbase, int key0, int qrow, int N, bool causal, float sl2,
+__device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
+                                          const typename QCfg<D>::Addr& la, int key0, int qrow, int N, bool causal, float sl2,
                                           float c1, int hh) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
@@ -917,8 +921,8 @@ __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            S.s[kb] = mfma32h(lds_read16b(cur, abase + C::KR + kb * 32 * C::SR + ds * 32), S.qf[ds], S.s[kb]);
-            S.dp[kb] = mfma32h(lds_read16b(cur, abase + C::VR + kb * 32 * C::SR + ds * 32), S.dof[ds], S.dp[kb]);
+            S.s[kb] = mfma32h(lds_read16b(cur, la.row(kb, ds) + C::KR), S.qf[ds], S.s[kb]);
+            S.dp[kb] = mfma32h(lds_read16b(cur, la.row(kb, ds) + C::VR), S.dof[ds], S.dp[kb]);
         }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -944,7 +948,7 @@ __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const u32x4 a = lds_read16b(cur, tbase + C::KT + db * 32 * C::ST + kc * 32);
+            const u32x4 a = la.t.read(cur + C::KT, db * 32, kc);
             S.pk[db] = mfma32h(a, S.pp[kc], S.pk[db]);
             S.dq[db] = mfma32h(a, S.dsp[kc], S.dq[db]);
         }
@@ -973,15 +977,15 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
                                              FA_LDS uint8_t* __restrict__ wst,
                                              const FA_LDS uint8_t* __restrict__ cur,
                                              const FA_LDS uint8_t* __restrict__ prv, int j, int jfull,
-                                             int jlast, int abase, int tbase, int qrow, int N, bool causal,
+                                             int jlast, const typename QCfg<D>::Addr& la, int qrow, int N, bool causal,
                                              float sl2, float c1, int w) {
     if (issue) dq_copy<D>(pr, pt, rk, rv, rkt, jn, wst, w);
     if (j < jfull) {
-        if (j == 0) dq_pipe<D, false, false>(S, cur, prv, abase, tbase, sl2, c1, nullptr, nullptr);
-        else dq_pipe<D, true, false>(S, cur, prv, abase, tbase, sl2, c1, nullptr, nullptr);
+        if (j == 0) dq_pipe<D, false, false>(S, cur, prv, la, sl2, c1, nullptr, nullptr);
+        else dq_pipe<D, true, false>(S, cur, prv, la, sl2, c1, nullptr, nullptr);
     } else {
-        if (j == jfull && j > 0) dq_drain<D>(S, prv, tbase, sl2, c1);
-        if (j <= jlast) dq_masked<D>(S, cur, abase, tbase, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1);
+        if (j == jfull && j > 0) dq_drain<D>(S, prv, la, sl2, c1);
+        if (j <= jlast) dq_masked<D>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1);
     }
 }
 
@@ -1046,8 +1050,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     typename C::PlanT pt;
     pr.init(w, lane, D);
     pt.init(w, lane, Np);
-    const int abase = l32 * C::SR + hh * 16;
-    const int tbase = l32 * C::ST + hh * 16;
+    typename C::Addr la;
+    la.init(l32, hh);
     FA_LDS uint8_t* st0 = (FA_LDS uint8_t*)smem;
 
     dq_copy<D>(pr, pt, rk, rv, rkt, 0, st0, w);
@@ -1055,7 +1059,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
     // tile 0
     dq_iteration<D>(S, pr, pt, nt > 1, rk, rv, rkt, 1, st0 + C::STAGE, st0, st0 + 2 * C::STAGE, 0, jfull, jlast,
-                    abase, tbase, qrow, N, causal, sl2, c1, w);
+                    la, qrow, N, causal, sl2, c1, w);
     wait_vmem();
     __syncthreads();
     // steady state: every wave pipelines, and there is a next tile to copy
@@ -1066,7 +1070,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
         const QNext<D> nx{pr, pt, rk, rv, rkt, (uint32_t)(j + 1) * kQ_N * D * 2, (uint32_t)(j + 1) * kQ_N * 2,
                           __builtin_amdgcn_readfirstlane(w)};
-        dq_pipe<D, true, true>(S, cur, prv, abase, tbase, sl2, c1, &nx, wst);
+        dq_pipe<D, true, true>(S, cur, prv, la, sl2, c1, &nx, wst);
         wait_vmem();
         __syncthreads();
     }
@@ -1075,12 +1079,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         FA_LDS uint8_t* wst = st0 + ((j + 1) % 3) * C::STAGE;
         const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
         const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
-        dq_iteration<D>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, wst, cur, prv, j, jfull, jlast, abase, tbase,
+        dq_iteration<D>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, wst, cur, prv, j, jfull, jlast, la,
                         qrow, N, causal, sl2, c1, w);
         wait_vmem();
         __syncthreads();
     }
-    if (jfull == nt && nt > 0) dq_drain<D>(S, st0 + ((nt - 1) % 3) * C::STAGE, tbase, sl2, c1);
+    if (jfull == nt && nt > 0) dq_drain<D>(S, st0 + ((nt - 1) % 3) * C::STAGE, la, sl2, c1);
 
     // exact row dot (the lane halves hold half of the keys each), in units of 2^sS
     const float dx = (S.dacc + swap_half(S.dacc)) * c1;

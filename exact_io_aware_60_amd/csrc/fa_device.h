@@ -60,45 +60,11 @@ __device__ __forceinline__ f32x16 mfma32h(const u32x4& a, const u32x4& b, const 
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// acc += a * b on fp16 operands, with the accumulator in AGPRs. Meant for
-// accumulators that only MFMAs touch until an epilogue: they then stay out of
-// the 256 architectural VGPRs, which the operands and the vector-ALU work
-// need. The compiler does not look inside the asm, so the caller keeps the
-// hazard rules of gfx950 itself:
-//  * a vector-ALU write of a or b needs 2 wait states before this instruction
-//    (mfma32h_agpr_after_valu inserts them);
-//  * acc set by the vector ALU (zeroing) needs agpr_fence() before the first
-//    use, and any read of acc after the last MFMA needs agpr_fence() too.
-// Back-to-back accumulation into the same registers needs no wait states.
-__device__ __forceinline__ void mfma32h_agpr(f32x16& acc, const u32x4& a, const u32x4& b) {
-    asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma32h_agpr_after_valu(f32x16& acc, const u32x4& a, const u32x4& b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// 24 wait states: more than a 32x32 MFMA's result needs before other
-// instructions read it.
-__device__ __forceinline__ void agpr_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
-
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = 0.f;
     return z;
-}
-
-// 16-byte LDS read / write at an element (bf16) offset into an LDS array.
-__device__ __forceinline__ u32x4 lds_read16(const FA_LDS uint16_t* base, int elem) {
-    return *reinterpret_cast<const FA_LDS u32x4*>(base + elem);
-}
-__device__ __forceinline__ void lds_write16(FA_LDS uint16_t* base, int elem, const u32x4& v) {
-    *reinterpret_cast<FA_LDS u32x4*>(base + elem) = v;
-}
-// Transposed 8-byte LDS read (see the header comment).
-__device__ __forceinline__ u32x2 lds_read_tr(const FA_LDS uint16_t* base, int elem) {
-    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        reinterpret_cast<FA_LDS s16x4*>(const_cast<FA_LDS uint16_t*>(base + elem)));
-    return __builtin_bit_cast(u32x2, r);
 }
 
 __device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) {
@@ -107,20 +73,6 @@ __device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) {
     return r;
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
-// The data of lane i lands at lds_wave_base + 16 * i bytes; lds_wave_base must
-// be the same for the whole wave. Completion is tracked by vmcnt: wait with
-// wait_vmem() and then a barrier before another wave reads the bytes.
-__device__ __forceinline__ void gload_lds16(const uint16_t* g, FA_LDS uint16_t* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
-                                     (FA_LDS void*)(lds_wave_base), 16, 0, 0);
-}
-// Direct global -> LDS copy of 4 bytes per lane (global_load_lds_dword): lane i's
-// dword lands at lds_wave_base + 4 * i bytes. Same completion rules as above.
-__device__ __forceinline__ void gload_lds4(const float* g, FA_LDS float* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g),
-                                     (FA_LDS void*)(lds_wave_base), 4, 0, 0);
-}
 // Buffer resources and buffer -> LDS copies. A raw resource (stride 0) covers
 // [base, base + bytes); loads outside it return zeros. Word 3 selects the
 // 32-bit data format that raw buffer loads on gfx9-family chips expect.
@@ -174,39 +126,6 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
 }
 
-// Swizzled position of 16-byte chunk `c` of row `row` in an LDS tile of
-// D-element rows; returns an element offset. The XOR keeps the reads each kernel
-// issues spread over the LDS banks (64 banks of 4 bytes: 256 bytes per bank
-// line). MODE 0 suits row-parallel 16-byte reads (lane = row): 16 consecutive
-// rows put one logical chunk at 16 distinct 16-byte slots of a bank line.
-// MODE 1 suits the transposed reads, where a 16-lane group reads 4 consecutive
-// rows x 2 consecutive chunks: those 8 chunks land in distinct slots. MODE 2
-// satisfies both conditions at once, for tiles read both ways.
-template <int D, int MODE>
-__device__ __forceinline__ int swz_key(int row) {
-    if constexpr (D == 128) {
-        if constexpr (MODE == 0) return row & 15;
-        else if constexpr (MODE == 1) return (row & 3) << 2;
-        else return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8);
-    } else {
-        const int x = (row >> 1) & 7;
-        if constexpr (MODE == 0) return x;
-        else if constexpr (MODE == 1) return (x & 1) << 2;
-        else return ((x & 1) << 1) | ((x >> 1) & 1) | (x & 4);
-    }
-}
-
-template <int D, int MODE>
-__device__ __forceinline__ int swz(int row, int c) {
-    return row * D + ((c ^ swz_key<D, MODE>(row)) << 3);
-}
-
-template <int D, int MODE>
-__device__ __forceinline__ void unswz(int slot, int& row, int& c) {
-    row = slot / (D / 8);
-    c = (slot % (D / 8)) ^ swz_key<D, MODE>(row);
-}
-
 // ---- padded LDS tiles ----
 // A padded tile stores row r of a [rows x D] 16-bit tile at byte r * STRIDE, so
 // every fragment address is (lane base) + (compile-time offset): no per-read
@@ -224,29 +143,6 @@ template <int D> struct TrPad { static constexpr int STRIDE = 2 * D + 64; };
 // (the unit one wave's global->LDS copy writes).
 template <int STRIDE, int ROWS>
 constexpr int padded_tile_bytes() { return (ROWS * STRIDE + 1023) / 1024 * 1024; }
-
-// Copy rows [row0, row0 + ROWS) of a row-major [N x D] 16-bit tensor into a
-// padded tile, with NW waves sharing the work. Block u (1 KiB) is written by one
-// wave instruction: lane i fills 16-byte slot u*64 + i. Slots that fall in the
-// padding, or past the last row, receive a copy of a valid 16-byte piece and are
-// never read. Rows past N read row N-1 (finite data; the kernels mask them).
-template <int D, int STRIDE, int ROWS, int NW>
-__device__ __forceinline__ void copy_tile(const uint16_t* __restrict__ g, int row0, int N,
-                                          FA_LDS uint8_t* __restrict__ tile, int w, int lane) {
-    constexpr int SPR = STRIDE / 16;                       // 16-byte slots per padded row
-    constexpr int NB = padded_tile_bytes<STRIDE, ROWS>() / 1024;
-#pragma unroll
-    for (int u = w; u < NB; u += NW) {
-        const int slot = u * 64 + lane;
-        int row = slot / SPR, c = slot - (slot / SPR) * SPR;
-        if (c >= D / 8 || row >= ROWS) {
-            c = 0;
-            row = row < ROWS ? row : ROWS - 1;
-        }
-        const int gr = row0 + row < N ? row0 + row : N - 1;
-        gload_lds16(g + (size_t)gr * D + c * 8, (FA_LDS uint16_t*)(tile + u * 1024));
-    }
-}
 
 // Copy of a padded tile through a buffer resource, with each lane's source
 // offsets computed once. Source row r of the tile starts `pitch` elements
@@ -274,6 +170,12 @@ struct CopyPlan {
             off[t] = (uint32_t)(row * pitch + c * 8) * 2u;
         }
     }
+    // Block t of wave ws (a scalar wave index).
+    __device__ __forceinline__ void copy_one(int t, BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile,
+                                             int ws) const {
+        const int u = ws + NW * t < NB ? ws + NW * t : NB - 1;
+        bload_lds16(r, off[t], soff, tile + u * 1024);
+    }
     // soff: byte offset of the tile's first row in the resource (uniform);
     // w: the wave index. It is made scalar here, at the copy, rather than once
     // per kernel: a scalar wave index held across the whole kernel has been
@@ -282,39 +184,94 @@ struct CopyPlan {
                                          int w) const {
         const int ws = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int u = ws + NW * t < NB ? ws + NW * t : NB - 1;
-            bload_lds16(r, off[t], soff, tile + u * 1024);
-        }
+        for (int t = 0; t < NT; ++t) copy_one(t, r, soff, tile, ws);
     }
 };
 
-// The same copy with the per-lane offsets recomputed at every copy (a few
-// vector-ALU instructions per 1 KiB block) instead of held in registers, for
-// kernels short of registers.
-template <int ELEMS, int STRIDE, int ROWS, int NW>
-struct CopyPlanLite {
-    static constexpr int SPR = STRIDE / 16;
-    static constexpr int NB = padded_tile_bytes<STRIDE, ROWS>() / 1024;
-    static constexpr int NT = (NB + NW - 1) / NW;
-    int lane_, pitch_;
-    __device__ __forceinline__ void init(int, int lane, int pitch) {
-        lane_ = lane;
-        pitch_ = pitch;
-    }
-    __device__ __forceinline__ void copy(BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile,
-                                         int w) const {
+// ---- swizzled LDS tiles ----
+// A swizzled tile stores a [ROWS x L bytes] 16-bit tile densely (row r at byte
+// r * L) and puts 16-byte chunk c of row r at chunk position c ^ key(r):
+//   L = 256 (16 chunks): key(r) = r & 15;
+//   L = 128 (8 chunks):  key(r) = (r >> 1) & 7.
+// A 16-byte row read in which 16 lanes take 16 consecutive rows (starting at a
+// multiple of 16) at one logical chunk then touches 16 distinct 16-byte bank
+// groups: with L = 256 the positions differ, with L = 128 rows of one parity
+// do and the parities fill the two halves of the 256-byte bank line. (Measured
+// on MI355X with the MFMA operand lane pattern, row l32 and half hh: both
+// layouts read at 223-230 B/clk per CU, as fast as the padded rows.) Unlike
+// padding, the tile is whole 1 KiB blocks of data only, so a copy moves no pad
+// bytes and splits evenly over 4 or 8 waves.
+template <int L>
+__host__ __device__ constexpr int swz_key(int r) {
+    static_assert(L == 256 || L == 128, "swizzled rows are 128 or 256 bytes");
+    return L == 256 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Copy of a swizzled [ROWS x L] tile through a buffer resource: wave w copies
+// 1 KiB blocks w, w + NW, ... (NT of them, the same count on every wave).
+// Source row r starts `pitch` elements after row r - 1; rows past the
+// resource's end read as zeros. Each lane's source offsets are computed once.
+template <int L, int ROWS, int NW>
+struct CopyPlanSwz {
+    static constexpr int NB = ROWS * L / 1024;
+    static constexpr int NT = NB / NW;
+    static_assert(NB % NW == 0, "the tile splits evenly over the waves");
+    uint32_t off[NT];
+    __device__ __forceinline__ void init(int w, int lane, int pitch) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int u = w + NW * t < NB ? w + NW * t : NB - 1;
-            const int slot = u * 64 + lane_;
-            int row = slot / SPR, c = slot - (slot / SPR) * SPR;
-            if (c >= ELEMS / 8 || row >= ROWS) {
-                c = 0;
-                row = row < ROWS ? row : ROWS - 1;
-            }
-            bload_lds16(r, (uint32_t)(row * pitch_ + c * 8) * 2u, soff, tile + u * 1024);
+            const int pos = (w + NW * t) * 1024 + lane * 16;
+            const int row = pos / L, phys = (pos % L) / 16;
+            const int c = phys ^ swz_key<L>(row);
+            off[t] = (uint32_t)(row * pitch + c * 8) * 2u;
         }
+    }
+    // Block t of wave ws (a scalar wave index).
+    __device__ __forceinline__ void copy_one(int t, BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile,
+                                             int ws) const {
+        bload_lds16(r, off[t], soff, tile + (ws + NW * t) * 1024);
+    }
+    __device__ __forceinline__ void copy(BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile, int w) const {
+        const int ws = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) copy_one(t, r, soff, tile, ws);
+    }
+};
+
+// ---- per-lane fragment reads ----
+// Both structs read the A-operand fragment of a 32-row block: chunk pair c
+// (16-bit elements c*16 + hh*8 ..) of row R0 + l32, R0 a multiple of 32 known
+// at compile time. They share one interface, so a kernel can take either
+// layout for a tile.
+
+// Padded rows, STRIDE bytes apart.
+template <int STRIDE>
+struct PadRows {
+    int b0;
+    __device__ __forceinline__ void init(int l32, int hh) { b0 = l32 * STRIDE + hh * 16; }
+    __device__ __forceinline__ u32x4 read(const FA_LDS uint8_t* tile, int R0, int c) const {
+        return *reinterpret_cast<const FA_LDS u32x4*>(tile + b0 + R0 * STRIDE + c * 32);
+    }
+};
+
+// 128-byte rows swizzled with swz_key<128>, from one register per lane: the
+// pair sits at b0 ^ (c << 5), plus R0 * 128 (key bits 1-2 flip the pair index,
+// bit 0 the half; R0 leaves the key unchanged). The XOR is applied to the whole
+// LDS address, so the tile must start on a 128-byte boundary. It is an asm
+// statement at each read, which the compiler may not hoist out of a loop, so
+// the four offsets do not hold four registers, and R0 * 128 folds into the
+// read's offset field.
+struct Swz128 {
+    int b0;
+    __device__ __forceinline__ void init(int l32, int hh) {
+        const int key = swz_key<128>(l32);
+        b0 = l32 * 128 + ((hh ^ (key & 1)) << 4) + ((key >> 1) << 5);
+    }
+    __device__ __forceinline__ u32x4 read(const FA_LDS uint8_t* tile, int R0, int c) const {
+        const uint32_t a = (uint32_t)(uintptr_t)tile + (uint32_t)b0;
+        uint32_t x = a;
+        if (c != 0) asm volatile("v_xor_b32 %0, %1, %2" : "=v"(x) : "i"(c << 5), "v"(a));
+        return *reinterpret_cast<const FA_LDS u32x4*>((const FA_LDS uint8_t*)(uintptr_t)x + R0 * 128);
     }
 };
 
