@@ -74,7 +74,11 @@ __device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) {
 }
 
 // Buffer resources and buffer -> LDS copies. A raw resource (stride 0) covers
-// [base, base + bytes); loads outside it return zeros. Word 3 selects the
+// [base, base + bytes); loads outside it return zeros. The range check covers
+// the whole offset, scalar part included (checked on MI355X: a load whose
+// soffset alone passes the end returns zeros, and a wave straddling the end
+// gets zeros exactly in the lanes past it), so a tile offset may be passed as
+// soffset. Word 3 selects the
 // 32-bit data format that raw buffer loads on gfx9-family chips expect.
 // buffer_load ... lds is the MUBUF twin of global_load_lds: lane i's bytes from
 // offset voff + soff land at lds_wave_base + size * i, counted by vmcnt. The

@@ -174,6 +174,46 @@ __device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt
     for (int f = 0; f < 2 * DB; ++f) o[f % DB] = mfma32(v_frag<D>(Vt, vbase, h, f), pp[f / DB], o[f % DB]);
 }
 
+// The global->LDS copies of one tile iteration (K tile j+2, V tile j+1). When
+// the iteration's first chunk is pipelined they go out one 1 KiB load at a time
+// inside its MFMA steps (2 * D/16 of them): item i at step 1 + i * SP. A wave
+// waits at each such load until the memory pipeline takes it, so a burst of
+// loads before the MFMAs stalls both waves of a SIMD together right after the
+// tile barrier; spread out, each load costs about one issue slot. Otherwise
+// (the chunk is the wave's last, or past it) `bulk` issues them all at once.
+// ON = false issues nothing.
+template <int D, bool ON>
+struct FwdCopies {
+    using PlanK = typename FwdCfg<D>::PlanK;
+    using PlanV = typename FwdCfg<D>::PlanV;
+    static constexpr int NK = PlanK::NT, NI = PlanK::NT + PlanV::NT, SP = 2 * (D / 16) / NI;
+    static_assert(SP >= 1, "copy items fit the steps");
+    const PlanK* pk;
+    const PlanV* pv;
+    BufRes rk, rv;
+    uint32_t koff, voff;
+    FA_LDS uint8_t* Kw;
+    FA_LDS uint8_t* Vw;
+    int w;
+    template <int step>
+    __device__ __forceinline__ void at() const {
+        if constexpr (ON && step >= 1 && (step - 1) % SP == 0 && (step - 1) / SP < NI) {
+            constexpr int i = (step - 1) / SP;
+            const int ws = __builtin_amdgcn_readfirstlane(w);
+            if constexpr (i < NK)
+                pk->copy_one(i, rk, koff, Kw, ws);
+            else
+                pv->copy_one(i - NK, rv, voff, Vw, ws);
+        }
+    }
+    __device__ __forceinline__ void bulk() const {
+        if constexpr (ON) {
+            pk->copy(rk, koff, Kw, w);
+            pv->copy(rv, voff, Vw, w);
+        }
+    }
+};
+
 // One pipelined chunk, interleaved by hand. Each step is closed by a scheduling
 // barrier, so the compiler keeps the order written here and only reorders
 // inside a step.
@@ -183,12 +223,13 @@ __device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt
 //            current chunk, which phase 2 consumes at least DS steps later;
 //   phase 2 (2*DB = DS steps): O^T += V^T P^T of the current chunk with the row
 //            max of the next chunk.
-template <int D>
+// cp issues its copy items at step r of phase 1 and step DS + f of phase 2.
+template <int D, int H, class CP>
 __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict__ Kn, int kbase, int hn,
                                                 const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
                                                 const u32x4 (&qf)[D / 16], const f32x16& sc, f32x16& sn,
                                                 float m, float& l, float sl2, f32x16 (&o)[D / 32],
-                                                float& mc) {
+                                                float& mc, const CP& cp) {
     constexpr int DS = D / 16, DB = D / 32, NF = 2 * DB;
     constexpr int PPS = 8 / DS;      // packs per phase-1 step
     constexpr int EPS = 16 / NF;     // score registers folded into the max per phase-2 step
@@ -199,30 +240,32 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
     sn = zero16();
     u32x4 a0 = k_frag<D>(Kn, kbase, hn, 0);
     u32x4 a1 = k_frag<D>(Kn, kbase, hn, 1);
-#pragma unroll
-    for (int r = 0; r < DS; ++r) {
+    static_for<DS>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
         u32x4 a2 = a1;
-        if (r + 2 < DS) a2 = k_frag<D>(Kn, kbase, hn, r + 2);
+        if constexpr (r + 2 < DS) a2 = k_frag<D>(Kn, kbase, hn, r + 2);
         vf[r] = v_frag<D>(Vt, vbase, h, r);
         sn = mfma32(a0, qf[r], sn);
 #pragma unroll
         for (int c = 0; c < PPS; ++c) exp_pack_one(sc, m, sl2, r * PPS + c, ls, pp);
+        cp.template at<r>();
         asm volatile("" : "+v"(ls));
         __builtin_amdgcn_sched_barrier(0);
         a0 = a1;
         a1 = a2;
-    }
+    });
     l += ls;
     float mx = sn[0];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
+    static_for<NF>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
         o[f % DB] = mfma32(vf[f], pp[f / DB], o[f % DB]);
 #pragma unroll
         for (int c = 0; c < EPS; ++c)
             if (f * EPS + c > 0) mx = fmaxf(mx, sn[f * EPS + c]);
+        cp.template at<DS + f>();
         asm volatile("" : "+v"(mx));
         __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     mc = fmaxf(mx, swap_half(mx)) * sl2;
 }
 
@@ -235,23 +278,30 @@ struct FwdState {
     float m, l, mc;            // reference max, row sum, current chunk's log2 max
 };
 
-// Chunk c = 2j + h. sc holds its scores; the next chunk's go to sn.
-// Kn: the K tile holding the next chunk; Vt: this chunk's V tile.
-template <int D>
-__device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, int h, f32x16& sc, f32x16& sn,
+// Chunk c = 2j + H. sc holds its scores; the next chunk's go to sn.
+// Kn: the K tile holding the next chunk; Vt: this chunk's V tile. cp carries
+// the iteration's copies (first chunk only).
+template <int D, int H, bool CP>
+__device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f32x16& sn,
                                           const FA_LDS uint8_t* __restrict__ Kn,
                                           const FA_LDS uint8_t* __restrict__ Vt, int kbase, int vbase,
-                                          bool causal, int qrow, int N, int lastc, float sl2, int hh) {
-    if (c > lastc) return;
+                                          bool causal, int qrow, int N, int lastc, float sl2, int hh,
+                                          const FwdCopies<D, CP>& cp) {
+    if (c > lastc) {
+        cp.bulk();
+        return;
+    }
     if ((causal && c * 32 + 31 > qrow - (qrow & 31)) || (c * 32 + 32 > N)) {
         mask_scores(sc, c * 32, qrow, N, causal, hh);
         st.mc = chunk_max(sc, sl2);
     }
     maybe_rescale<D>(st.mc, st.m, st.l, st.o);
-    if (c < lastc)
-        pipelined_chunk<D>(Kn, kbase, h ^ 1, Vt, vbase, h, st.qf, sc, sn, st.m, st.l, sl2, st.o, st.mc);
-    else
-        softmax_pv<D>(Vt, vbase, h, sc, st.m, st.l, sl2, st.o);
+    if (c < lastc) {
+        pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, sl2, st.o, st.mc, cp);
+    } else {
+        cp.bulk();
+        softmax_pv<D>(Vt, vbase, H, sc, st.m, st.l, sl2, st.o);
+    }
 }
 
 // One 64-key tile j: start the copies of K tile j+2 (into Kw) and V tile j+1
@@ -270,12 +320,18 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, co
                                               const FA_LDS uint8_t* __restrict__ Vr, int kbase, int vbase,
                                               bool valid, bool causal, int qrow, int N, int lastc,
                                               float sl2, int w, int lane) {
-    if (j + 2 < nt) pk.copy(rk, (uint32_t)(j + 2) * kBN * D * 2, Kw, w);
-    if (j + 1 < nt) pv.copy(rv, (uint32_t)(j + 1) * kBN * D * 2, Vw, w);
+    // Tiles j + 1 and j + 2 may lie past the last one: their copies then read
+    // past the resource (zeros) into buffers no chunk reads any more (those of
+    // tiles j - 1 and j - 2).
+    const FwdCopies<D, true> cp{&pk, &pv, rk, rv, (uint32_t)(j + 2) * kBN * D * 2,
+                                (uint32_t)(j + 1) * kBN * D * 2, Kw, Vw, w};
     if (valid) {
         const int hh = lane >> 5;
-        fwd_chunk<D>(st, 2 * j, 0, st.sA, st.sB, Kr0, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh);
-        fwd_chunk<D>(st, 2 * j + 1, 1, st.sB, st.sA, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh);
+        fwd_chunk<D, 0>(st, 2 * j, st.sA, st.sB, Kr0, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh, cp);
+        fwd_chunk<D, 1>(st, 2 * j + 1, st.sB, st.sA, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh,
+                        FwdCopies<D, false>{});
+    } else {
+        cp.bulk();
     }
 }
 
