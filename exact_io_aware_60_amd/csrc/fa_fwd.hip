@@ -28,10 +28,15 @@
 //    l ^ 32), and the fp32 accumulator registers become, after rounding to
 //    bf16, the B operand of O^T += V^T P^T with no data movement. V^T is read
 //    with ds_read_b64_tr_b16 in the matching key order.
-//  * exp2 with scale * log2(e) folded into one FMA. The reference max moves
-//    only when a chunk's max exceeds it by more than 2^8; otherwise the rescale
-//    of O is skipped. Any reference value cancels in O / l and m + ln l, so the
-//    result is the same (the fp64 model in oracle/online.py checks this).
+//  * exp2 with scale * log2(e) folded into one FMA, x = S * scale * log2(e) - m,
+//    computed for the next chunk beside the P.V MFMAs of the current one. The
+//    reference m is not the running max: it starts at the first chunk's max
+//    and moves only when a chunk's probabilities under it grow too large (a
+//    lane's 16 values sum past 2^8, or overflow). That chunk is then redone
+//    with the exact max, O and l rescaled. So no row max is computed for the
+//    other chunks, and every P stays at most 2^8. Any reference value cancels
+//    in O / l and m + ln l, so the result is the same (the fp64 model in
+//    oracle/online.py checks this rule).
 //  * Causal: chunks above a wave's diagonal are skipped; the diagonal chunk and
 //    the ragged last chunk are masked element-wise. Workgroups run heaviest
 //    q-tile first (longest-processing-time order). Workgroups of one head set
@@ -47,7 +52,7 @@ constexpr int kWM = 32;        // query rows per wave
 constexpr int kBN = 64;        // keys per LDS tile
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kTau = 8.0f;   // lazy-max threshold, log2 units
+constexpr float kSumMax = 256.0f;   // largest partial sum of P accepted without a new reference
 
 template <int D>
 struct FwdCfg {
@@ -110,8 +115,8 @@ __device__ __forceinline__ f32x16 scores(const FA_LDS uint8_t* __restrict__ Kt, 
     return s;
 }
 
-// Diagonal or ragged chunk: scores of invisible keys become -inf. With a
-// positive scale_log2 (the host keeps it >= 1e-30) they turn into exact zeros.
+// Diagonal or ragged chunk: scores (or x values) of invisible keys become -inf,
+// so their probabilities are exact zeros.
 __device__ __forceinline__ void mask_scores(f32x16& s, int key0, int qrow, int N, bool causal, int hh) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -121,7 +126,8 @@ __device__ __forceinline__ void mask_scores(f32x16& s, int key0, int qrow, int N
 }
 
 // Row max of a chunk in log2 units. Every chunk a wave computes has a visible
-// key in every row, or the row is past N (finite scores, never stored).
+// key in every row, or the row is past N (finite scores, never stored). With a
+// positive scale_log2 (the host keeps it >= 1e-30) the max commutes with it.
 __device__ __forceinline__ float chunk_max(const f32x16& s, float sl2) {
     float mx = s[0];
 #pragma unroll
@@ -129,46 +135,55 @@ __device__ __forceinline__ float chunk_max(const f32x16& s, float sl2) {
     return fmaxf(mx, swap_half(mx)) * sl2;
 }
 
-// Lazy reference max: m moves only when a chunk's max exceeds it by more than
-// kTau (log2 units); O and l are then rescaled by 2^(m_old - m_new). Any
-// reference cancels in O / l and m + ln l, so the result is unchanged.
+// P~ = exp2(x) for pack pi = 0..7 of a chunk holding x = S*sl2 - m (16-key
+// half kc = pi / 4, dword t = pi % 4): registers kc*8 + 2t and +1, rounded to a
+// bf16 pair, which is k slot pair (2t, 2t+1) of the P^T operand of half kc.
+__device__ __forceinline__ void exp_pack_one(const f32x16& x, int pi, float& ls, u32x4 (&pp)[2]) {
+    const int kc = pi >> 2, t = pi & 3, i = kc * 8 + 2 * t;
+    const float p0 = fast_exp2(x[i]);
+    const float p1 = fast_exp2(x[i + 1]);
+    ls += p0 + p1;
+    pp[kc][t] = pack_bf16(p0, p1);
+}
+
+// The reference check after a chunk's exps (ls: this lane's sum, pp: packs).
+// Unless some lane's sum exceeds kSumMax or is not finite, every P of the chunk
+// is at most kSumMax and nothing happens. Otherwise the wave moves m up to the
+// exact running max (m + the chunk's max of x, both lane halves), rescales O
+// and l by 2^(m_old - m_new), shifts x and redoes the exps.
 template <int D>
-__device__ __forceinline__ void maybe_rescale(float mc, float& m, float& l, f32x16 (&o)[D / 32]) {
-    const bool need = mc > m + kTau;
-    if (__ballot(need)) {
-        const float mn = need ? mc : m;
-        const float alpha = fast_exp2(m - mn);
+__device__ __forceinline__ void check_reference(f32x16& x, float& m, float& l, f32x16 (&o)[D / 32],
+                                                float& ls, u32x4 (&pp)[2]) {
+    if (__ballot(!(ls <= kSumMax))) {
+        float mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+        const float delta = fmaxf(fmaxf(mx, swap_half(mx)), 0.f);
+        const float alpha = fast_exp2(-delta);
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-        m = mn;
+        m += delta;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] -= delta;
+        ls = 0.f;
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) exp_pack_one(x, pi, ls, pp);
     }
-}
-
-// P~ = exp2(S*sl2 - m) for pack pi = 0..7 of a chunk (16-key half kc = pi / 4,
-// dword t = pi % 4): registers kc*8 + 2t and +1, rounded to a bf16 pair, which
-// is k slot pair (2t, 2t+1) of the P^T operand of half kc.
-__device__ __forceinline__ void exp_pack_one(const f32x16& s, float m, float sl2, int pi, float& ls,
-                                             u32x4 (&pp)[2]) {
-    const int kc = pi >> 2, t = pi & 3, i = kc * 8 + 2 * t;
-    const float x0 = fast_exp2(fmaf(s[i], sl2, -m));
-    const float x1 = fast_exp2(fmaf(s[i + 1], sl2, -m));
-    ls += x0 + x1;
-    pp[kc][t] = pack_bf16(x0, x1);
 }
 
 // Softmax and O^T += V^T P^T for one chunk (not pipelined: a wave's last chunk).
 template <int D>
 __device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
-                                           const f32x16& s, float m, float& l, float sl2,
-                                           f32x16 (&o)[D / 32]) {
+                                           f32x16& x, float& m, float& l, f32x16 (&o)[D / 32]) {
     constexpr int DB = D / 32;
     u32x4 pp[2];
     float ls = 0.f;
 #pragma unroll
-    for (int pi = 0; pi < 8; ++pi) exp_pack_one(s, m, sl2, pi, ls, pp);
+    for (int pi = 0; pi < 8; ++pi) exp_pack_one(x, pi, ls, pp);
+    check_reference<D>(x, m, l, o, ls, pp);
     l += ls;
 #pragma unroll
     for (int f = 0; f < 2 * DB; ++f) o[f % DB] = mfma32(v_frag<D>(Vt, vbase, h, f), pp[f / DB], o[f % DB]);
@@ -221,22 +236,28 @@ struct FwdCopies {
 //            fragment read two steps ahead) with the exp / row sum / bf16 pack
 //            of the current chunk; step r also reads V^T fragment r of the
 //            current chunk, which phase 2 consumes at least DS steps later;
-//   phase 2 (2*DB = DS steps): O^T += V^T P^T of the current chunk with the row
-//            max of the next chunk.
+//   then the reference check (check_reference);
+//   phase 2 (2*DB = DS steps): O^T += V^T P^T of the current chunk with
+//            x = S*sl2 - m of the next chunk, in place.
 // cp issues its copy items at step r of phase 1 and step DS + f of phase 2.
 template <int D, int H, class CP>
 __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict__ Kn, int kbase, int hn,
                                                 const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
-                                                const u32x4 (&qf)[D / 16], const f32x16& sc, f32x16& sn,
-                                                float m, float& l, float sl2, f32x16 (&o)[D / 32],
-                                                float& mc, const CP& cp) {
+                                                const u32x4 (&qf)[D / 16], f32x16& sc, f32x16& sn,
+                                                float& m, float& l, float sl2, f32x16 (&o)[D / 32],
+                                                const CP& cp) {
     constexpr int DS = D / 16, DB = D / 32, NF = 2 * DB;
     constexpr int PPS = 8 / DS;      // packs per phase-1 step
-    constexpr int EPS = 16 / NF;     // score registers folded into the max per phase-2 step
+    constexpr int EPS = 16 / NF;     // next-chunk registers turned into x per phase-2 step
     static_assert(NF == DS, "one V^T fragment read per phase-1 step");
     u32x4 pp[2];
     u32x4 vf[NF];
     float ls = 0.f;
+    // The last chunk exponentiates the same x values; an empty asm statement
+    // marks them as changed here, so the compiler cannot hoist this chunk's
+    // exps above the branch between the two, out of the MFMA steps below.
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) asm volatile("" : "+v"(sc[i]), "+v"(sc[i + 1]));
     sn = zero16();
     u32x4 a0 = k_frag<D>(Kn, kbase, hn, 0);
     u32x4 a1 = k_frag<D>(Kn, kbase, hn, 1);
@@ -247,26 +268,23 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
         vf[r] = v_frag<D>(Vt, vbase, h, r);
         sn = mfma32(a0, qf[r], sn);
 #pragma unroll
-        for (int c = 0; c < PPS; ++c) exp_pack_one(sc, m, sl2, r * PPS + c, ls, pp);
+        for (int c = 0; c < PPS; ++c) exp_pack_one(sc, r * PPS + c, ls, pp);
         cp.template at<r>();
         asm volatile("" : "+v"(ls));
         __builtin_amdgcn_sched_barrier(0);
         a0 = a1;
         a1 = a2;
     });
+    check_reference<D>(sc, m, l, o, ls, pp);
     l += ls;
-    float mx = sn[0];
     static_for<NF>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         o[f % DB] = mfma32(vf[f], pp[f / DB], o[f % DB]);
 #pragma unroll
-        for (int c = 0; c < EPS; ++c)
-            if (f * EPS + c > 0) mx = fmaxf(mx, sn[f * EPS + c]);
+        for (int c = 0; c < EPS; ++c) sn[f * EPS + c] = fmaf(sn[f * EPS + c], sl2, -m);
         cp.template at<DS + f>();
-        asm volatile("" : "+v"(mx));
         __builtin_amdgcn_sched_barrier(0);
     });
-    mc = fmaxf(mx, swap_half(mx)) * sl2;
 }
 
 // Per-wave state of the forward loop.
@@ -274,8 +292,8 @@ template <int D>
 struct FwdState {
     u32x4 qf[D / 16];          // Q as the B operand
     f32x16 o[D / 32];          // O^T accumulators
-    f32x16 sA, sB;             // scores of the current / next chunk (alternating)
-    float m, l, mc;            // reference max, row sum, current chunk's log2 max
+    f32x16 sA, sB;             // x = S*sl2 - m of the current chunk / scores of the next (alternating)
+    float m, l;                // reference (log2 units), this lane's share of the row sum
 };
 
 // Chunk c = 2j + H. sc holds its scores; the next chunk's go to sn.
@@ -291,16 +309,13 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
         cp.bulk();
         return;
     }
-    if ((causal && c * 32 + 31 > qrow - (qrow & 31)) || (c * 32 + 32 > N)) {
+    if ((causal && c * 32 + 31 > qrow - (qrow & 31)) || (c * 32 + 32 > N))
         mask_scores(sc, c * 32, qrow, N, causal, hh);
-        st.mc = chunk_max(sc, sl2);
-    }
-    maybe_rescale<D>(st.mc, st.m, st.l, st.o);
     if (c < lastc) {
-        pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, sl2, st.o, st.mc, cp);
+        pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, sl2, st.o, cp);
     } else {
         cp.bulk();
-        softmax_pv<D>(Vt, vbase, H, sc, st.m, st.l, sl2, st.o);
+        softmax_pv<D>(Vt, vbase, H, sc, st.m, st.l, st.o);
     }
 }
 
@@ -378,9 +393,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     for (int ds = 0; ds < DS; ++ds) st.qf[ds] = gload16(Qg + (size_t)qrow * D + ds * 16 + hh * 8, qrow < N);
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.o[db] = zero16();
-    st.m = -INFINITY;
+    st.m = 0.f;
     st.l = 0.f;
-    st.mc = 0.f;
 
     // K and V through buffer resources covering the head's N rows: rows of a
     // ragged last tile past N read as zeros (their scores are masked).
@@ -399,8 +413,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     __syncthreads();
 
     if (wave_valid) {
+        // The first reference is chunk 0's exact (masked) max, so every row has
+        // l >= 1 from then on; chunk 0 then holds x.
         st.sA = scores<D>(Ks, kbase, 0, st.qf);
-        st.mc = chunk_max(st.sA, sl2);
+        if ((causal && 31 > r0) || 32 > N) mask_scores(st.sA, 0, qrow, N, causal, hh);
+        st.m = chunk_max(st.sA, sl2);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.sA[i] = fmaf(st.sA[i], sl2, -st.m);
     }
     for (int j = 0; j < nt; ++j) {
         fwd_iteration<D>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT, Vs + ((j + 1) & 1) * C::VT,

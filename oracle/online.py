@@ -15,9 +15,16 @@ last step open. The reading used here is the only one under which the result
 equals the textbook softmax: O is divided by l, and LSE = m + ln l.
 
 ``tau`` models a lazily updated reference max. The reference m moves only when
-a block's row max exceeds it by more than ``tau`` (natural-log units). The HIP
-forward kernel uses this variant. Any reference value cancels in O / l and in
-m + ln l, so the result is the same; the tests check that in fp64.
+a block's row max exceeds it by more than ``tau`` (natural-log units).
+
+``sum_max`` models the rule the HIP forward kernel uses instead. The reference
+starts at the first key block's row max. For each later block the
+probabilities e^(S - m) are formed under the old reference; only when some row
+of the row block sums past ``sum_max`` (or overflows) does the whole row block
+move to m = max(m, rowmax). No row max is needed for the other blocks.
+
+Any reference value cancels in O / l and in m + ln l, so the result is the
+same under every rule; the tests check that in fp64.
 
 The model is numpy fp64 with a numpy matmul as its product step. It serves
 only to pin the algorithm's order of steps against the definition.
@@ -28,7 +35,7 @@ import numpy as np
 
 
 def online_attention(q, k, v, causal: bool, scale: float, block_rows: int, block_cols: int,
-                     tau: float = 0.0):
+                     tau: float = 0.0, sum_max: float | None = None):
     """q [Nq, d], k/v [Nk, d] float64 for one head (queries at positions 0..Nq-1).
     Returns O [Nq, d], LSE [Nq]."""
     q = np.asarray(q, np.float64)
@@ -50,8 +57,16 @@ def online_attention(q, k, v, causal: bool, scale: float, block_rows: int, block
             if causal:
                 S = np.where(cols[None, :] <= rows[:, None], S, -np.inf)
             rowmax = S.max(axis=1)
-            # lazy reference: move m only when the block max clears it by more than tau
-            move = (rowmax > m + tau) | np.isneginf(m)
+            if sum_max is None:
+                # lazy reference: move m only when the block max clears it by more than tau
+                move = (rowmax > m + tau) | np.isneginf(m)
+            else:
+                # move the whole row block when some row's probabilities under the
+                # old reference sum past sum_max (the first block always moves)
+                with np.errstate(over="ignore", invalid="ignore"):
+                    sums = np.exp(S - m[:, None]).sum(axis=1)
+                grow = bool(np.any(~(sums <= sum_max))) or bool(np.any(np.isneginf(m)))
+                move = np.full(len(rows), grow)
             m_new = np.where(move, np.maximum(m, rowmax), m)
             # a row with no visible key so far keeps m = -inf; its terms are all zero
             safe = np.where(np.isneginf(m_new), 0.0, m_new)

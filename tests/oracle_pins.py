@@ -334,7 +334,8 @@ def pin_finite_differences(orc):
 
 def pin_online_recurrence(orc):
     """The tiled online recurrence in fp64 (any block sizes, ragged edges, lazy
-    reference max) reproduces the oracle's definition."""
+    reference max or the sum-triggered reference) reproduces the oracle's
+    definition."""
     from oracle.online import online_attention
     N, d = 37, 6
     q, k, v = (_rand((1, 1, N, d), 150 + t, 1.5) for t in range(3))
@@ -346,6 +347,12 @@ def pin_online_recurrence(orc):
             om, lm = online_attention(q[0, 0], k[0, 0], v[0, 0], causal, 0.6, br, bc, tau)
             _close(om, o[0, 0], what=f"online O ({br}x{bc}, tau={tau:.2f})")
             _close(lm, lse[0, 0], what=f"online LSE ({br}x{bc}, tau={tau:.2f})")
+        # the sum-triggered reference: tight (moves often), the kernel's 2^8, and
+        # loose enough that it never moves after the first block
+        for br, bc, smax in ((4, 3, 1.5), (32, 32, 256.0), (6, 5, 1e30)):
+            om, lm = online_attention(q[0, 0], k[0, 0], v[0, 0], causal, 0.6, br, bc, sum_max=smax)
+            _close(om, o[0, 0], what=f"online O ({br}x{bc}, sum_max={smax:g})")
+            _close(lm, lse[0, 0], what=f"online LSE ({br}x{bc}, sum_max={smax:g})")
 
 
 def pin_sampled_backward(orc):
