@@ -211,11 +211,27 @@ __host__ __device__ constexpr int swz_key(int r) {
     return L == 256 ? (r & 15) : ((r >> 1) & 7);
 }
 
+// The same for tiles read with ds_read_b64_tr_b16, where 32 lanes read 4
+// consecutive rows (starting at a multiple of 4) x 64 bytes at one column: the
+// 64-byte quarters of a row are permuted instead, quarter q of row r stored at
+// quarter q ^ tr_key(r), so the 4 rows land on the 4 distinct 64-byte quarters
+// of the 256-byte bank line (L = 128: two rows share a line, and the key
+// separates the rows of one parity). In 16-byte chunk units the key is
+// tr_key(r) << 2.
+template <int L>
+__host__ __device__ constexpr int tr_key(int r) {
+    static_assert(L == 256 || L == 128, "swizzled rows are 128 or 256 bytes");
+    return L == 256 ? (r & 3) : ((r >> 1) & 1);
+}
+template <int L> struct RowKey { __host__ __device__ static constexpr int key(int r) { return swz_key<L>(r); } };
+template <int L> struct TrKey { __host__ __device__ static constexpr int key(int r) { return tr_key<L>(r) << 2; } };
+
 // Copy of a swizzled [ROWS x L] tile through a buffer resource: wave w copies
 // 1 KiB blocks w, w + NW, ... (NT of them, the same count on every wave).
-// Source row r starts `pitch` elements after row r - 1; rows past the
-// resource's end read as zeros. Each lane's source offsets are computed once.
-template <int L, int ROWS, int NW>
+// 16-byte chunk c of row r goes to chunk position c ^ Key::key(r). Source row
+// r starts `pitch` elements after row r - 1; rows past the resource's end read
+// as zeros. Each lane's source offsets are computed once.
+template <int L, int ROWS, int NW, class Key = RowKey<L>>
 struct CopyPlanSwz {
     static constexpr int NB = ROWS * L / 1024;
     static constexpr int NT = NB / NW;
@@ -226,7 +242,7 @@ struct CopyPlanSwz {
         for (int t = 0; t < NT; ++t) {
             const int pos = (w + NW * t) * 1024 + lane * 16;
             const int row = pos / L, phys = (pos % L) / 16;
-            const int c = phys ^ swz_key<L>(row);
+            const int c = phys ^ Key::key(row);
             off[t] = (uint32_t)(row * pitch + c * 8) * 2u;
         }
     }
@@ -258,26 +274,29 @@ struct PadRows {
     }
 };
 
-// 128-byte rows swizzled with swz_key<128>, from one register per lane: the
-// pair sits at b0 ^ (c << 5), plus R0 * 128 (key bits 1-2 flip the pair index,
-// bit 0 the half; R0 leaves the key unchanged). The XOR is applied to the whole
-// LDS address, so the tile must start on a 128-byte boundary. It is an asm
-// statement at each read, which the compiler may not hoist out of a loop, so
-// the four offsets do not hold four registers, and R0 * 128 folds into the
+// L-byte rows swizzled with swz_key<L>, from one register per lane: the pair
+// sits at b0 ^ (c << 5), plus R0 * L (key bit 0 flips the half, the higher key
+// bits the pair index; R0 leaves the key unchanged). The XOR is applied to the
+// whole LDS address, so the tile must start on an L-byte boundary. With PIN it
+// is an asm statement at each read, which the compiler may not hoist out of a
+// loop, so the offsets do not hold one register each; R0 * L folds into the
 // read's offset field.
-struct Swz128 {
+template <int L, bool PIN = true>
+struct SwzRowRead {
     int b0;
     __device__ __forceinline__ void init(int l32, int hh) {
-        const int key = swz_key<128>(l32);
-        b0 = l32 * 128 + ((hh ^ (key & 1)) << 4) + ((key >> 1) << 5);
+        const int key = swz_key<L>(l32);
+        b0 = l32 * L + ((hh ^ (key & 1)) << 4) + ((key >> 1) << 5);
     }
     __device__ __forceinline__ u32x4 read(const FA_LDS uint8_t* tile, int R0, int c) const {
         const uint32_t a = (uint32_t)(uintptr_t)tile + (uint32_t)b0;
-        uint32_t x = a;
-        if (c != 0) asm volatile("v_xor_b32 %0, %1, %2" : "=v"(x) : "i"(c << 5), "v"(a));
-        return *reinterpret_cast<const FA_LDS u32x4*>((const FA_LDS uint8_t*)(uintptr_t)x + R0 * 128);
+        uint32_t x = a ^ (uint32_t)(c << 5);
+        if constexpr (PIN)
+            if (c != 0) asm volatile("v_xor_b32 %0, %1, %2" : "=v"(x) : "i"(c << 5), "v"(a));
+        return *reinterpret_cast<const FA_LDS u32x4*>((const FA_LDS uint8_t*)(uintptr_t)x + R0 * L);
     }
 };
+using Swz128 = SwzRowRead<128>;
 
 // 16-byte and transposed 8-byte reads at a byte offset into a padded tile.
 __device__ __forceinline__ u32x4 lds_read16b(const FA_LDS uint8_t* base, int byte_off) {

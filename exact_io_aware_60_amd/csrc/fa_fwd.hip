@@ -15,9 +15,12 @@
 //    each owning 32 query rows (256 rows per workgroup, at most 256 registers
 //    per wave).
 //  * Keys are streamed in tiles of 64 through LDS with direct global->LDS
-//    loads: K in 3 buffers, V in 2, one barrier per tile. Tiles are stored with
-//    padded rows (fa_device.h), which keeps every read bank-conflict-free and
-//    makes every fragment address a lane base plus a constant.
+//    loads: K in 3 buffers, V in 2, one barrier per tile. Tiles are stored
+//    densely with XOR-swizzled 16-byte chunks (fa_device.h): K by row for the
+//    16-byte row reads, V by 64-byte quarter for the transposing reads. Every
+//    read stays bank-conflict-free, and a copy moves whole 1 KiB blocks of data
+//    only: 2 loads per wave per tile for each of K and V at d = 128 (padded
+//    rows took 3 each, part of them duplicates).
 //  * Inside each wave the work runs in chunks of 32 keys, software-pipelined by
 //    hand: the MFMAs for the scores of chunk c+1 are interleaved with the exp /
 //    sum / pack work of chunk c, and the P.V MFMAs of chunk c with the row max
@@ -57,13 +60,11 @@ constexpr float kSumMax = 256.0f;   // largest partial sum of P accepted without
 template <int D>
 struct FwdCfg {
     static constexpr int DS = D / 16, DB = D / 32;
-    static constexpr int SK = RowPad<D>::STRIDE;                 // K rows: 16-byte reads
-    static constexpr int SV = TrPad<D>::STRIDE;                  // V rows: transposed reads
-    static constexpr int KT = padded_tile_bytes<SK, kBN>();
-    static constexpr int VT = padded_tile_bytes<SV, kBN>();
+    static constexpr int L = 2 * D;                              // bytes per K / V row
+    static constexpr int KT = kBN * L, VT = kBN * L;
     static constexpr int LDS = 3 * KT + 2 * VT;
-    using PlanK = CopyPlan<D, SK, kBN, kWaves>;
-    using PlanV = CopyPlan<D, SV, kBN, kWaves>;
+    using PlanK = CopyPlanSwz<L, kBN, kWaves, RowKey<L>>;
+    using PlanV = CopyPlanSwz<L, kBN, kWaves, TrKey<L>>;
 };
 
 // Workgroup id -> (rank, bh). Workgroups are handed to the 8 XCDs round-robin,
@@ -84,15 +85,21 @@ __device__ __forceinline__ void unmap_block(int bid, int nbh, int& rank, int& bh
 // A chunk is half h of a 64-key tile. Scores S^T = K Q^T: lane holds query
 // column l32 and keys (i/4)*8 + hh*4 + i%4 of register i.
 //
-// Lane bases (bytes): kbase = l32 * SK + hh * 16 for K fragments;
-// vbase = ((lane & 15) >> 2 + 4 * hh) * SV + ((g & 1) * 16 + 4 * (lane & 3)) * 2
-// for V^T fragments, g = lane >> 4.
+// Lane bases (bytes, swizzle folded in; L = 2D bytes per row):
+//   K: kbase = l32 * L + ((hh ^ k0) << 4) + ((key >> 1) << 5), key = swz_key(l32),
+//      k0 = key & 1; chunk pair ds of the row is at (tile + kbase) ^ (ds << 5);
+//   V: vbase = vr * L + (tr_key(vr) << 6) + ((g & 1) * 16 + 4 * (lane & 3)) * 2
+//      with vr = (lane & 15) >> 2 + 4 * hh, g = lane >> 4; the 64-byte quarter
+//      db is at (tile + vbase) ^ (db << 6).
+// Row offsets that are multiples of 8 leave both keys unchanged, and tiles
+// start on L-byte boundaries, so the XOR can act on the whole address.
 
 // K fragment ds of chunk half h: the A operand of the score MFMAs (row l32,
 // d = ds*16 + hh*8 .. +7).
 template <int D>
 __device__ __forceinline__ u32x4 k_frag(const FA_LDS uint8_t* __restrict__ Kt, int kbase, int h, int ds) {
-    return lds_read16b(Kt, kbase + h * 32 * FwdCfg<D>::SK + ds * 32);
+    const uint32_t a = ((uint32_t)(uintptr_t)Kt + (uint32_t)kbase) ^ (uint32_t)(ds << 5);
+    return *reinterpret_cast<const FA_LDS u32x4*>((const FA_LDS uint8_t*)(uintptr_t)a + h * 32 * FwdCfg<D>::L);
 }
 
 // V^T fragment f = (kc, db) of chunk half h: the A operand of the P.V MFMAs,
@@ -100,10 +107,11 @@ __device__ __forceinline__ u32x4 k_frag(const FA_LDS uint8_t* __restrict__ Kt, i
 // uses: slot hh*8 + t holds key kc*16 + (t/4)*8 + hh*4 + t%4.
 template <int D>
 __device__ __forceinline__ u32x4 v_frag(const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h, int f) {
-    constexpr int DB = FwdCfg<D>::DB, SV = FwdCfg<D>::SV;
+    constexpr int DB = FwdCfg<D>::DB, L = FwdCfg<D>::L;
     const int kc = f / DB, db = f % DB;
-    const int off = vbase + (h * 32 + kc * 16) * SV + db * 64;
-    return cat(lds_read_trb(Vt, off), lds_read_trb(Vt, off + 8 * SV));
+    const uint32_t a = ((uint32_t)(uintptr_t)Vt + (uint32_t)vbase) ^ (uint32_t)(db << 6);
+    const FA_LDS uint8_t* p = (const FA_LDS uint8_t*)(uintptr_t)a + (h * 32 + kc * 16) * L;
+    return cat(lds_read_trb(p, 0), lds_read_trb(p, 8 * L));
 }
 
 template <int D>
@@ -239,13 +247,17 @@ struct FwdCopies {
 //   then the reference check (check_reference);
 //   phase 2 (2*DB = DS steps): O^T += V^T P^T of the current chunk with
 //            x = S*sl2 - m of the next chunk, in place.
+// ka holds the first two K fragments of this chunk's score MFMAs on entry;
+// phase 2 reads those of the following chunk into it (half hnn of tile Knn),
+// so no chunk starts by waiting for its first LDS reads.
 // cp issues its copy items at step r of phase 1 and step DS + f of phase 2.
 template <int D, int H, class CP>
 __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict__ Kn, int kbase, int hn,
+                                                const FA_LDS uint8_t* __restrict__ Knn, int hnn,
                                                 const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
                                                 const u32x4 (&qf)[D / 16], f32x16& sc, f32x16& sn,
                                                 float& m, float& l, float sl2, f32x16 (&o)[D / 32],
-                                                const CP& cp) {
+                                                u32x4 (&ka)[2], const CP& cp) {
     constexpr int DS = D / 16, DB = D / 32, NF = 2 * DB;
     constexpr int PPS = 8 / DS;      // packs per phase-1 step
     constexpr int EPS = 16 / NF;     // next-chunk registers turned into x per phase-2 step
@@ -259,8 +271,8 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
 #pragma unroll
     for (int i = 0; i < 16; i += 2) asm volatile("" : "+v"(sc[i]), "+v"(sc[i + 1]));
     sn = zero16();
-    u32x4 a0 = k_frag<D>(Kn, kbase, hn, 0);
-    u32x4 a1 = k_frag<D>(Kn, kbase, hn, 1);
+    u32x4 a0 = ka[0];
+    u32x4 a1 = ka[1];
     static_for<DS>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
         u32x4 a2 = a1;
@@ -282,6 +294,7 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
         o[f % DB] = mfma32(vf[f], pp[f / DB], o[f % DB]);
 #pragma unroll
         for (int c = 0; c < EPS; ++c) sn[f * EPS + c] = fmaf(sn[f * EPS + c], sl2, -m);
+        if constexpr (f == 2 || f == 3) ka[f - 2] = k_frag<D>(Knn, kbase, hnn, f - 2);
         cp.template at<DS + f>();
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -293,15 +306,18 @@ struct FwdState {
     u32x4 qf[D / 16];          // Q as the B operand
     f32x16 o[D / 32];          // O^T accumulators
     f32x16 sA, sB;             // x = S*sl2 - m of the current chunk / scores of the next (alternating)
+    u32x4 ka[2];               // first two K fragments of the next pipelined chunk's score MFMAs
     float m, l;                // reference (log2 units), this lane's share of the row sum
 };
 
 // Chunk c = 2j + H. sc holds its scores; the next chunk's go to sn.
-// Kn: the K tile holding the next chunk; Vt: this chunk's V tile. cp carries
-// the iteration's copies (first chunk only).
+// Kn: the K tile holding the next chunk; Kr1: K tile j+1, which holds chunk
+// c+2 (half H); Vt: this chunk's V tile. cp carries the iteration's copies
+// (first chunk only).
 template <int D, int H, bool CP>
 __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f32x16& sn,
                                           const FA_LDS uint8_t* __restrict__ Kn,
+                                          const FA_LDS uint8_t* __restrict__ Kr1,
                                           const FA_LDS uint8_t* __restrict__ Vt, int kbase, int vbase,
                                           bool causal, int qrow, int N, int lastc, float sl2, int hh,
                                           const FwdCopies<D, CP>& cp) {
@@ -312,7 +328,8 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
     if ((causal && c * 32 + 31 > qrow - (qrow & 31)) || (c * 32 + 32 > N))
         mask_scores(sc, c * 32, qrow, N, causal, hh);
     if (c < lastc) {
-        pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, sl2, st.o, cp);
+        pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Kr1, H, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, sl2, st.o,
+                              st.ka, cp);
     } else {
         cp.bulk();
         softmax_pv<D>(Vt, vbase, H, sc, st.m, st.l, st.o);
@@ -342,8 +359,9 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, co
                                 (uint32_t)(j + 1) * kBN * D * 2, Kw, Vw, w};
     if (valid) {
         const int hh = lane >> 5;
-        fwd_chunk<D, 0>(st, 2 * j, st.sA, st.sB, Kr0, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh, cp);
-        fwd_chunk<D, 1>(st, 2 * j + 1, st.sB, st.sA, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh,
+        fwd_chunk<D, 0>(st, 2 * j, st.sA, st.sB, Kr0, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh,
+                        cp);
+        fwd_chunk<D, 1>(st, 2 * j + 1, st.sB, st.sA, Kr1, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh,
                         FwdCopies<D, false>{});
     } else {
         cp.bulk();
@@ -385,8 +403,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const int nck = (N + 31) / 32;
     const int lastc = causal ? min(nck - 1, r0 / 32) : nck - 1;
     const float sl2 = p.scale_log2;
-    const int kbase = l32 * C::SK + hh * 16;
-    const int vbase = (((lane & 15) >> 2) + 4 * hh) * C::SV + ((g & 1) * 16 + 4 * (lane & 3)) * 2;
+    const int kkey = swz_key<C::L>(l32);
+    const int kbase = l32 * C::L + ((hh ^ (kkey & 1)) << 4) + ((kkey >> 1) << 5);
+    const int vr = ((lane & 15) >> 2) + 4 * hh;
+    const int vbase = vr * C::L + (tr_key<C::L>(vr) << 6) + ((g & 1) * 16 + 4 * (lane & 3)) * 2;
 
     FwdState<D> st;
 #pragma unroll
@@ -416,6 +436,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
         // The first reference is chunk 0's exact (masked) max, so every row has
         // l >= 1 from then on; chunk 0 then holds x.
         st.sA = scores<D>(Ks, kbase, 0, st.qf);
+        st.ka[0] = k_frag<D>(Ks, kbase, 1, 0);   // chunk 1's keys: tile 0, second half
+        st.ka[1] = k_frag<D>(Ks, kbase, 1, 1);
         if ((causal && 31 > r0) || 32 > N) mask_scores(st.sA, 0, qrow, N, causal, hh);
         st.m = chunk_max(st.sA, sl2);
 #pragma unroll
