@@ -273,6 +273,12 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
     sn = zero16();
     u32x4 a0 = ka[0];
     u32x4 a1 = ka[1];
+    // Phase 1 (score MFMAs interleaved with the softmax) runs at a raised wave
+    // priority, phase 2 at the normal one: when the two waves of a SIMD want to
+    // issue at once, the one in phase 1 goes first. Measured on MI355X: about
+    // 4% less forward time than equal priorities (any raised level alike, and
+    // raising phase 2 instead gains half as much).
+    __builtin_amdgcn_s_setprio(1);
     static_for<DS>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
         u32x4 a2 = a1;
@@ -289,6 +295,7 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
     });
     check_reference<D>(sc, m, l, o, ls, pp);
     l += ls;
+    __builtin_amdgcn_s_setprio(0);
     static_for<NF>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         o[f % DB] = mfma32(vf[f], pp[f / DB], o[f % DB]);
