@@ -424,6 +424,12 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
     u32x4 pp[4], dsp[4];
     f32x4 lv[2][4], dv4[2][4];
     u32x4 ring[PF + 1];
+    // Transposed operands: chunk pair qc of d rows db*32 + l32 lies at
+    // ((st + b0) ^ (qc << 5)) + tile + db*32*128. The address of pair qc is
+    // formed once, at its first read, and serves the 2*DB reads of that pair in
+    // the dO^T and Q^T tiles (tile offsets are multiples of 128 bytes).
+    const uint32_t tb = (uint32_t)(uintptr_t)st + (uint32_t)la.t.b0;
+    uint32_t tx[4];
 
     auto frag = [&](auto nc) -> u32x4 {
         constexpr int n = decltype(nc)::value;
@@ -433,7 +439,12 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
         } else {
             constexpr int m = n - 4 * DS, grp = m / (2 * DB);
             constexpr int qc = (grp >> 1) * 2 + (m % (2 * DB)) / DB, db = m % DB;
-            return la.t.read(st + ((grp & 1) ? C::QT : C::DOT), db * 32, qc);
+            if constexpr ((grp & 1) == 0 && db == 0) {
+                if constexpr (qc == 0) tx[0] = tb;
+                else asm volatile("v_xor_b32 %0, %1, %2" : "=v"(tx[qc]) : "i"(qc << 5), "v"(tb));
+            }
+            const FA_LDS uint8_t* a = (const FA_LDS uint8_t*)(uintptr_t)tx[qc];
+            return *reinterpret_cast<const FA_LDS u32x4*>(a + ((grp & 1) ? C::QT : C::DOT) + db * 32 * 128);
         }
     };
     auto mfma_at = [&](auto nc, const u32x4& a) {
