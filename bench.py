@@ -105,7 +105,7 @@ def cpu_baseline(w) -> dict:
     `n` positions, forward and backward. Under the causal mask that prefix is a
     self-contained problem of the same shape family."""
     import oracle
-    n = int(os.environ.get("BENCH_CPU_SAMPLE_N", "6144"))
+    n = int(os.environ.get("BENCH_CPU_SAMPLE_N", "13312"))
     n = min(n, w.N)
     inp = ai.make_inputs(w)
     G = w.G
