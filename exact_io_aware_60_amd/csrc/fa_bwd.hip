@@ -482,10 +482,12 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
                 pp[qc][w] = v;
             }
         } else {
-            const float y = s[h][i] * fmaf(dp[h][i], c1, -dv4[h][u][e]);
-            dp[h][i] = y;
+            // dS = P (dP c1 - D): the difference in fp32, the product of the fp16
+            // pair with the P pair already packed for the dV MFMA (v_pk_mul_f16)
+            const float t = fmaf(dp[h][i], c1, -dv4[h][u][e]);
+            dp[h][i] = t;
             if constexpr (i & 1) {
-                uint32_t v = pack_f16(dp[h][i - 1], y);
+                uint32_t v = mul_f16x2(pp[qc][w], pack_f16(dp[h][i - 1], t));
                 pin(v);
                 dsp[qc][w] = v;
             }

@@ -130,6 +130,12 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2v));
 }
 
+// Elementwise product of two packed fp16 pairs, rounded to fp16 (v_pk_mul_f16).
+__device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
+    const f16x2v x = __builtin_bit_cast(f16x2v, a), y = __builtin_bit_cast(f16x2v, b);
+    return __builtin_bit_cast(uint32_t, x * y);
+}
+
 // ---- padded LDS tiles ----
 // A padded tile stores row r of a [rows x D] 16-bit tile at byte r * STRIDE, so
 // every fragment address is (lane base) + (compile-time offset): no per-read
