@@ -427,6 +427,68 @@ def pin_stored_o_mode(orc):
         _close(a[key], b[key], tol=1e-13, what=f"bf16-exact O: {key}")
 
 
+def pin_decode_positions(orc):
+    """Short query blocks at the end of a long key sequence (decode): with row i
+    placed at position Nk - Nq + i, the oracle equals (a) torch's fp64 SDPA with
+    that bottom-right causal mask written out, (b) the last Nq rows of the
+    square causal run whose final query rows are these queries, and (c) for a
+    single query, the unmasked run (it sees every key)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = 2, 6, 2, 3, 19, 8
+    G = Hq // Hkv
+    q = _rand((B, Hq, Nq, d), 190)
+    k, v = _rand((B, Hkv, Nk, d), 191), _rand((B, Hkv, Nk, d), 192)
+    s = 0.45
+    pos = Nk - Nq + np.arange(Nq, dtype=np.int64)
+    o, lse = orc.fwd(q, k, v, True, s, qpos=pos)
+    mask = torch.tensor(np.arange(Nk)[None, :] <= pos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q), torch.tensor(k).repeat_interleave(G, 1), torch.tensor(v).repeat_interleave(G, 1),
+        attn_mask=mask, scale=s)
+    _close(o, ref.numpy(), tol=1e-12, what="decode O vs SDPA with explicit mask")
+    sc = (torch.tensor(q) @ torch.tensor(k).repeat_interleave(G, 1).transpose(-1, -2) * s).masked_fill(~mask, float("-inf"))
+    _close(lse, torch.logsumexp(sc, -1).numpy(), tol=1e-12, what="decode LSE vs logsumexp")
+    qf = _rand((B, Hq, Nk, d), 193)
+    qf[:, :, Nk - Nq:] = q
+    of, lf = orc.fwd(qf, k, v, True, s)
+    _close(o, of[:, :, Nk - Nq:], what="decode rows vs square causal rows")
+    _close(lse, lf[:, :, Nk - Nq:], what="decode LSE vs square causal LSE")
+    o1, l1 = orc.fwd(q[:, :, -1:], k, v, True, s, qpos=np.array([Nk - 1], dtype=np.int64))
+    on, ln = orc.fwd(q[:, :, -1:], k, v, False, s)
+    _close(o1, on, what="single decode row vs unmasked")
+    _close(l1, ln, what="single decode LSE vs unmasked")
+
+
+def pin_split_merge(orc):
+    """Keys split into disjoint ranges: the per-range (O, LSE) pairs merge into the
+    full result by LSE = ln sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r. This
+    holds only if LSE is the full log-sum-exp (max included) and O the
+    normalised output. With the causal decode mask, a range a row cannot see has
+    LSE = -inf and weight 0."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 4, 23, 6
+    q = _rand((B, Hq, Nq, d), 195, 1.5)
+    k, v = _rand((B, Hkv, Nk, d), 196, 1.5), _rand((B, Hkv, Nk, d), 197)
+    s = 0.7
+    pos = Nk - Nq + np.arange(Nq, dtype=np.int64)
+    cuts = [0, 7, 16, 21, Nk]          # the last range [21, 23) is beyond row 0's position 19
+    for causal in (False, True):
+        qp = pos if causal else None
+        o, lse = orc.fwd(q, k, v, causal, s, qpos=qp)
+        parts = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            rp = (pos - a) if causal else None
+            parts.append(orc.fwd(q, k[:, :, a:b], v[:, :, a:b], causal, s, qpos=rp))
+        L = np.stack([p[1] for p in parts])
+        if causal:
+            assert np.isneginf(L[-1][..., 0]).all(), "a range after a row's position must have LSE = -inf"
+        top = L.max(0)
+        wsum = np.exp(L - top).sum(0)
+        Lm = top + np.log(wsum)
+        Om = sum(np.exp(Lr - Lm)[..., None] * p[0] for Lr, p in zip(L, parts))
+        _close(Lm, lse, what=f"merged LSE causal={causal}")
+        _close(Om, o, what=f"merged O causal={causal}")
+
+
 PINS = [
     pin_one_token,
     pin_two_tokens,
@@ -447,4 +509,6 @@ PINS = [
     pin_sampled_backward,
     pin_round_bf16,
     pin_stored_o_mode,
+    pin_decode_positions,
+    pin_split_merge,
 ]
