@@ -179,3 +179,61 @@ def make_case(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int, with_grad: b
     if with_grad:
         out["do"] = bf16_round_bits(normal_f32(qs, cid, TENSOR_DO))
     return out
+
+
+# ---------------------------------------------------------------- decode workloads
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq new query rows per head against a cache of Nk keys and values (the
+    decode step of generation). The cache shapes are those of the long-sequence
+    workloads above; the queries are the sequence's last Nq tokens."""
+    cfg_id: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool = True
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def describe(self) -> dict:
+        return dict(workload=self.name, B=self.B, Hq=self.Hq, Hkv=self.Hkv, Nq=self.Nq, Nk=self.Nk, d=self.d,
+                    causal=self.causal, passes="decode")
+
+
+DECODE_WORKLOADS = {
+    "decode_gqa16k": DecodeWorkload(5, "decode_gqa16k", 2, 32, 8, 1, 16384, 128),
+    "decode_gqa16k_q16": DecodeWorkload(6, "decode_gqa16k_q16", 2, 32, 8, 16, 16384, 128),
+    "decode_long128k": DecodeWorkload(7, "decode_long128k", 1, 8, 8, 1, 131072, 128),
+    "decode_batch64": DecodeWorkload(8, "decode_batch64", 64, 32, 8, 1, 4096, 128),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload) -> dict:
+    """q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d], N(0, 1) rounded to bf16 (uint16 bits)."""
+    return {
+        "q": normal_bf16((w.B, w.Hq, w.Nq, w.d), w.cfg_id, TENSOR_Q),
+        "k": normal_bf16((w.B, w.Hkv, w.Nk, w.d), w.cfg_id, TENSOR_K),
+        "v": normal_bf16((w.B, w.Hkv, w.Nk, w.d), w.cfg_id, TENSOR_V),
+    }
+
+
+def make_decode_case(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: int,
+                     dist_scale: float = 1.0) -> dict:
+    """Small seeded decode case (cfg_id space 3000 + seed)."""
+    cid = 3000 + seed
+    f = np.float32(dist_scale)
+    return {
+        "q": bf16_round_bits(normal_f32((B, Hq, Nq, d), cid, TENSOR_Q) * f),
+        "k": bf16_round_bits(normal_f32((B, Hkv, Nk, d), cid, TENSOR_K) * f),
+        "v": bf16_round_bits(normal_f32((B, Hkv, Nk, d), cid, TENSOR_V)),
+    }

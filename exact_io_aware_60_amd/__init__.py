@@ -7,6 +7,7 @@ implementation to fall back to.
 
     o, lse = fwd(q, k, v, causal=True)                  # q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+    o, lse = decode(q, k, v, causal=True)               # q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d]
 
 The entry points mirror ``include/flash_attn.h`` one to one.
 """
@@ -23,7 +24,8 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE
     0, -1, -2, -3, -4, -5, -6, -7)
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
-            "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq")
+            "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
+            "flash_attn_decode", "flash_attn_decode_workspace_size")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -52,6 +54,10 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_bwd_workspace_size.argtypes = [_i] * 6
+        L.flash_attn_decode.restype = _i
+        L.flash_attn_decode.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.flash_attn_decode_workspace_size.restype = ctypes.c_size_t
+        L.flash_attn_decode_workspace_size.argtypes = [_i] * 7
         L.flash_attn_strerror.restype = ctypes.c_char_p
         L.flash_attn_strerror.argtypes = [_i]
         L.flash_attn_version.restype = ctypes.c_char_p
@@ -96,6 +102,17 @@ def bwd_stage_raw(stage: int, q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d,
 
 def bwd_workspace_size(B, Hq, Hkv, N, d, causal) -> int:
     return int(lib().flash_attn_bwd_workspace_size(B, Hq, Hkv, N, d, int(causal)))
+
+
+def decode_raw(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
+               stream=None) -> int:
+    """flash_attn_decode on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale), workspace,
+                                   workspace_bytes, stream)
+
+
+def decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal) -> int:
+    return int(lib().flash_attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(causal)))
 
 
 # ------------------------------------------------------------------ torch front end
@@ -158,3 +175,30 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, wo
                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, causal, scale,
                    workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
     return dq, dk, dv
+
+
+def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=None, out=None, lse=None):
+    """Attention of the newest Nq query rows over a cache of Nk keys.
+
+    q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16. Causal: row i is token
+    Nk - Nq + i. Returns (o bf16 [B,Hq,Nq,d], lse fp32 [B,Hq,Nq])."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("q and k/v must agree on B and d, and v must be shaped like k")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _checked(t, name)
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws_bytes = decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk,
+                      d, causal, scale, ws_ptr, ws_len, _stream(q)))
+    return o, lse

@@ -186,6 +186,65 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
                       workspace_bytes, stream, 1, 1);
 }
 
+namespace {
+
+int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (causal && Nq > Nk) return FA_ERR_SHAPE;
+    // one K/V head fits a 32-bit buffer range with room for a ragged tile
+    if ((long double)Nk * d * 2 >= 2147483648.0L) return FA_ERR_SHAPE;
+    // rows of one group and their offsets, element counts, grids
+    if ((long double)(Hq / Hkv) * Nq * d >= 2147483647.0L) return FA_ERR_SHAPE;
+    if ((long double)B * Hq * Nq * d >= 4.0e18L || (long double)B * Hkv * Nk * d >= 4.0e18L) return FA_ERR_SHAPE;
+    const long double rows = (long double)B * Hq * Nq;
+    if (rows / 4 >= 2147483647.0L) return FA_ERR_SHAPE;
+    const long double nrb = ((long double)(Hq / Hkv) * Nq + 127) / 128;
+    if ((long double)B * Hkv * (nrb + 1) * 512 >= 2147483647.0L) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+}  // namespace
+
+size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+    if (check_decode_shape(B, Hq, Hkv, Nq, Nk, d, causal) != FA_OK) return 0;
+    return fa::dec_plan(B, Hq, Hkv, Nq, Nk, d).total;
+}
+
+int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                      int Hkv, int Nq, int Nk, int d, int causal, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    int st = check_decode_shape(B, Hq, Hkv, Nq, Nk, d, causal);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_ALIGN;
+    const fa::DecPlan pl = fa::dec_plan(B, Hq, Hkv, Nq, Nk, d);
+    if (pl.total > 0) {
+        if (!workspace || workspace_bytes < pl.total) return FA_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    }
+    fa::DecParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    char* ws = static_cast<char*>(workspace);
+    p.part_lse = pl.total ? reinterpret_cast<float*>(ws + pl.part_lse) : nullptr;
+    p.part_o = pl.total ? reinterpret_cast<float*>(ws + pl.part_o) : nullptr;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d; p.G = Hq / Hkv; p.M = pl.M;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    p.nrb = pl.nrb;
+    p.nsplit = pl.nsplit;
+    p.tps = pl.tps;
+    p.pair = pl.pair;
+    return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
 const char* flash_attn_strerror(int status) {
     switch (status) {
         case FA_OK: return "success";
@@ -193,13 +252,13 @@ const char* flash_attn_strerror(int status) {
         case FA_ERR_SHAPE: return "unsupported shape: B, Hq, Hkv, N must be >= 1, Hq % Hkv == 0, sizes in range";
         case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
         case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
-        case FA_ERR_WORKSPACE: return "backward workspace is NULL or too small";
+        case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
         case FA_ERR_HIP: return g_hip_text[0] ? g_hip_text : "HIP launch failed";
         case FA_ERR_SCALE: return "scale must be finite and >= 0";
         default: return "unknown status";
     }
 }
 
-const char* flash_attn_version(void) { return "0.3.0 gfx950"; }
+const char* flash_attn_version(void) { return "0.4.0 gfx950"; }
 
 }  // extern "C"

@@ -51,6 +51,38 @@ struct BwdParams {
     float scale_log2;
 };
 
+// Decode: a few query rows against a long key/value sequence. The M = G * Nq
+// query rows that share a K/V head (a "group", index b * Hkv + hkv) are
+// contiguous in q, o and lse. The keys of a group are split into nsplit ranges
+// of tps 64-key tiles; a workgroup handles one (group, 128-row block, range)
+// and, unless there is a single range, leaves a partial result that the merge
+// kernel combines.
+struct DecParams {
+    const uint16_t* q;   // bf16 [B, Hq, Nq, d]
+    const uint16_t* k;   // bf16 [B, Hkv, Nk, d]
+    const uint16_t* v;   // bf16 [B, Hkv, Nk, d]
+    uint16_t* o;         // bf16 [B, Hq, Nq, d]
+    float* lse;          // fp32 [B, Hq, Nq]
+    float* part_lse;     // fp32 [groups][nsplit][M]: log2 of the range's sum of exp2 (-inf: no key seen)
+    float* part_o;       // fp32 [groups][nsplit][M][d]: the range's normalised output (0: no key seen)
+    int B, Hq, Hkv, Nq, Nk, d, G, M;
+    int causal;
+    float scale_log2;
+    int nrb;             // 128-row blocks per group
+    int nsplit;          // key ranges per group
+    int tps;             // 64-key tiles per range
+    int pair;            // 1: two waves share each 32-row block, one per 32-key half of a tile
+};
+
+// Split plan and workspace layout of the decode (workspace offsets are
+// 256-byte aligned; total = 0 when nsplit == 1 and the range kernel writes o
+// and lse itself).
+struct DecPlan {
+    int M, nrb, nsplit, tps, pair;
+    size_t part_lse, part_o, total;
+};
+DecPlan dec_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
 constexpr int kRowPad = 128;   // row padding unit of the backward workspace
 
 // Byte offsets of the backward workspace arrays; every array starts on a
@@ -69,6 +101,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 // One backward stage: 0 = preparation (scales, fp16 copies, row dot D,
 // log2-scaled LSE), 1 = dQ (and the exact row dot), 2 = dK/dV.
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream);
+hipError_t launch_decode(const DecParams& p, hipStream_t stream);
 
 // Launch geometry, exposed for logging and tests of the host logic.
 struct Geometry {

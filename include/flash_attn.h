@@ -58,7 +58,7 @@ enum fa_status {
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow */
     FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
     FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
-    FA_ERR_WORKSPACE = -5, /* backward workspace NULL or smaller than required */
+    FA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
     FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
     FA_ERR_SCALE = -7      /* scale is negative, NaN or infinite */
 };
@@ -141,11 +141,53 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Attention of a few query rows over a long key/value sequence: the decode
+ * step of generation, where each new token (or a short block of them) attends
+ * to the whole key/value cache. The mlapandio page "FlashAttention: IO-aware
+ * exact attention" notes that tiling does not speed this case up: it is bound
+ * by reading the cache from memory ("Two notes"; end of the naive-vs-flash
+ * diagram). So this entry point splits the keys of every K/V head into
+ * ranges read by separate workgroups, which keeps the whole GPU reading, and
+ * merges the per-range results by their logsumexp.
+ *   q    in   bf16 [B, Hq,  Nq, d]    the newest Nq query rows
+ *   k    in   bf16 [B, Hkv, Nk, d]    the key/value cache
+ *   v    in   bf16 [B, Hkv, Nk, d]
+ *   o    out  bf16 [B, Hq,  Nq, d]
+ *   lse  out  fp32 [B, Hq,  Nq]       natural-log logsumexp, as in flash_attn_fwd
+ * causal: query row i is token Nk - Nq + i of the sequence the keys belong to
+ * (the queries are its last Nq tokens) and sees keys j <= Nk - Nq + i; this
+ * needs Nq <= Nk. causal = 0: every row sees all Nk keys. With Nq = Nk and
+ * causal = 1 the result is that of flash_attn_fwd.
+ * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {64, 128};
+ * Nk * d * 2 < 2^31 bytes per K/V head. Any Nq is accepted; the path is made
+ * for (Hq / Hkv) * Nq <= 128 query rows per K/V head, and larger counts read
+ * the cache once per 128 rows. Inputs and outputs must not overlap.
+ * workspace: device memory of workspace_bytes >=
+ * flash_attn_decode_workspace_size(...) for the per-range partial results;
+ * NULL is accepted when that size is 0. Contents on entry are ignored and on
+ * return are unspecified. Runs two kernels on `stream` (the range kernel and
+ * the merge), or one when the shape needs a single range per head. Results do
+ * not depend on the stream or on earlier calls (no atomics).
+ */
+int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace flash_attn_decode needs for these arguments, or 0
+ * when it needs none or rejects the shape. The workspace holds, for every
+ * key range of every K/V head and every query row, one fp32 logsumexp and d
+ * fp32 output values: about R * B * Hq * Nq * (d + 1) * 4 bytes for R ranges
+ * per head (R is chosen from the shape so that the grid fills the GPU).
+ */
+size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal);
+
 /* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
 
-/* Library version and the GPU target it was compiled for, e.g. "0.3.0 gfx950". */
+/* Library version and the GPU target it was compiled for, e.g. "0.4.0 gfx950". */
 const char* flash_attn_version(void);
 
 #ifdef __cplusplus

@@ -141,3 +141,58 @@ def test_bwd_stages_validate(stage):
 def test_workspace_size_rejects_bad_shapes():
     assert fa.bwd_workspace_size(1, 3, 2, 64, 128, 1) == 0
     assert fa.bwd_workspace_size(1, 4, 2, 64, 96, 1) == 0
+
+
+def dec_call(**over):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, Hq=32, Hkv=8, Nq=1, Nk=16384, d=128, causal=1,
+             scale=0.088, ws=P[9], ws_bytes=1 << 30)
+    a.update(over)
+    return fa.decode_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                         a["d"], a["causal"], a["scale"], a["ws"], a["ws_bytes"])
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
+def test_decode_null(name):
+    assert dec_call(**{name: None}) == fa.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(Hq=0), dict(Hkv=0), dict(Nq=0), dict(Nk=0), dict(Hq=6, Hkv=4),
+                                  dict(Nq=5, Nk=4), dict(Nk=1 << 23), dict(Hq=1 << 20, Hkv=1, Nq=1 << 12)])
+def test_decode_shape(over):
+    assert dec_call(**over) == fa.FA_ERR_SHAPE
+
+
+def test_decode_checks():
+    assert dec_call(d=96) == fa.FA_ERR_HEADDIM
+    assert dec_call(scale=-1.0) == fa.FA_ERR_SCALE
+    assert dec_call(o=P[3] + 2) == fa.FA_ERR_ALIGN
+    need = fa.decode_workspace_size(2, 32, 8, 1, 16384, 128, 1)
+    assert need > 0
+    assert dec_call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert dec_call(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert dec_call(ws=P[9] + 4, ws_bytes=need) == fa.FA_ERR_ALIGN
+    # more query rows than keys is only an error under the causal mask
+    assert fa.decode_workspace_size(1, 4, 2, 9, 8, 64, 1) == 0
+    assert fa.decode_workspace_size(1, 4, 2, 9, 8, 64, 0) == 0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d", [(2, 32, 8, 1, 16384, 128), (2, 32, 8, 16, 16384, 128),
+                                               (1, 8, 8, 1, 131072, 128), (1, 4, 1, 3, 1000, 64),
+                                               (1, 16, 1, 20, 5000, 128)])
+def test_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d):
+    """With R key ranges per K/V head the workspace is one fp32 logsumexp and d
+    fp32 outputs per (range, query row), each array rounded up to 256 bytes;
+    the ranges are whole 64-key tiles, at most one range per tile."""
+    got = fa.decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, 1)
+    rows = B * Hq * Nq
+
+    def up(x):
+        return x + (-x) % 256
+    ranges = [R for R in range(2, -(-Nk // 64) + 1) if up(4 * rows * R) + up(4 * rows * R * d) == got]
+    assert len(ranges) == 1, got
+
+
+def test_decode_single_range_needs_no_workspace():
+    """A grid that already fills the GPU (B * Hkv >= 512 groups) reads each head
+    in one range and writes the output directly."""
+    assert fa.decode_workspace_size(64, 32, 8, 1, 8192, 128, 1) == 0
