@@ -12,6 +12,13 @@ before the timed region; each kernel is bracketed by HIP events on the stream
 it runs on. Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
+
+With --decode NAME it measures instead the decode path (a few query rows over
+a long key/value cache) on one of the decode workloads, against the HBM
+roofline: the bytes the step must move (K and V once, Q, O and LSE) over the
+time of one call (range kernel and merge). Before each timed call a 512 MiB
+read evicts the cache from the 256 MB last-level cache, so K and V come from
+HBM.
 """
 from __future__ import annotations
 
@@ -68,6 +75,7 @@ def algorithmic(w) -> dict:
 
 # Sources each timed kernel is built from (hashed to tie a traffic record to the kernel it measured).
 KERNEL_SOURCES = {
+    "decode": ("fa_decode.hip", "fa_device.h", "fa_params.h"),
     "fwd": ("fa_fwd.hip", "fa_device.h", "fa_params.h"),
     "bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_params.h"),
     "bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_params.h"),
@@ -82,12 +90,12 @@ def sources_sha256(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, workload: str = WORKLOAD):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (profiles/traffic_<workload>.md: FETCH_SIZE and WRITE_SIZE, each scaled by what
     the counter reads for a 1 GiB device copy), or None when there is no record or
     the kernel's sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     want = sources_sha256(kernel)
@@ -125,6 +133,111 @@ def cpu_baseline(w) -> dict:
             "seconds": dt}
 
 
+def decode_bytes(w) -> int:
+    """Bytes a decode step must move: K and V once, Q read, O written (bf16), LSE (fp32)."""
+    return 2 * 2 * w.B * w.Hkv * w.Nk * w.d + 2 * 2 * w.B * w.Hq * w.Nq * w.d + 4 * w.B * w.Hq * w.Nq
+
+
+def decode_cpu_baseline(w) -> dict:
+    """The fp64 oracle on the whole decode workload (it runs in seconds)."""
+    import oracle
+    inp = ai.make_decode_inputs(w)
+    q, k, v = (ai.bf16_bits_to_f64(inp[t]) for t in ("q", "k", "v"))
+    pos = w.Nk - w.Nq + np.arange(w.Nq, dtype=np.int64)
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    orc.fwd(q, k, v, w.causal, w.scale, qpos=pos if w.causal else None)
+    dt = time.perf_counter() - t0
+    return {"value": decode_bytes(w) / dt / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"the whole {w.name} step in fp64 (the bytes of its bf16 inputs and outputs per second); "
+                      f"{dt:.2f} s", "seconds": dt}
+
+
+def decode_main(args) -> int:
+    import torch
+    import exact_io_aware_60_amd as fa
+
+    fa.lib()
+    w = ai.DECODE_WORKLOADS[args.decode]
+    inp = ai.make_decode_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=q.device)
+    ws_bytes = fa.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    # 512 MiB of floats, summed (read once, nothing written back) before each call
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nk,
+              w.d, w.causal, w.scale, ws.data_ptr(), ws_bytes, sp)
+
+    def call():
+        st = fa.decode_raw(*args_c)
+        if st != 0:
+            raise RuntimeError(f"decode: {fa.strerror(st)}")
+
+    for _ in range(args.warmup):
+        flush.sum()
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        flush.sum()
+        ev[s][0].record(stream)
+        call()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = [a.elapsed_time(b) for a, b in ev]
+    ms = sum(times) / len(times)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=q.device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    nbytes = decode_bytes(w)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "decode step HBM throughput (bf16 K/V cache read once)",
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "passes": "decode"},
+        "ms_min": min(times),
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "roofline": {"bound": "hbm", "kernel": "decode (range kernel + merge)", "achieved": gbs,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": measured_traffic("decode", w.name),
+                     "traffic_unit": "bytes per call (HBM read + write, rocprofv3 counters)",
+                     "avg_launch_ms": ms, "algorithmic_bytes_per_launch": nbytes},
+        "workspace_bytes": ws_bytes,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = decode_cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,11 +247,19 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (3 times) after the timed steps, so that one "
                          "profiled run holds the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--decode", choices=sorted(ai.DECODE_WORKLOADS), default=None,
+                    help="measure the decode path on this workload instead of the forward + backward step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the attention path here is single-GPU (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
+    if args.decode:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            return 2
+        return decode_main(args)
 
     import torch
     import exact_io_aware_60_amd as fa

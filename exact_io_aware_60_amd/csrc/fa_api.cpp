@@ -199,7 +199,7 @@ int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
     if ((long double)(Hq / Hkv) * Nq * d >= 2147483647.0L) return FA_ERR_SHAPE;
     if ((long double)B * Hq * Nq * d >= 4.0e18L || (long double)B * Hkv * Nk * d >= 4.0e18L) return FA_ERR_SHAPE;
     const long double rows = (long double)B * Hq * Nq;
-    if (rows / 4 >= 2147483647.0L) return FA_ERR_SHAPE;
+    if (rows >= 2147483647.0L) return FA_ERR_SHAPE;
     const long double nrb = ((long double)(Hq / Hkv) * Nq + 127) / 128;
     if ((long double)B * Hkv * (nrb + 1) * 512 >= 2147483647.0L) return FA_ERR_SHAPE;
     return FA_OK;

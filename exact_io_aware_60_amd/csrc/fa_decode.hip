@@ -12,10 +12,11 @@
 // gfx950 design:
 //  * The bound is HBM bandwidth, so the kernel's job is to keep every CU
 //    reading. The keys of each K/V head are split into ranges of whole 64-key
-//    tiles, enough ranges that the grid holds about two workgroups per CU; a
-//    workgroup streams its range once through LDS with direct global->LDS
-//    loads (tile j+1 in flight while tile j is used) and leaves a partial
-//    result. A second kernel merges the ranges by their logsumexp.
+//    tiles, enough ranges that the grid holds about one workgroup per CU; a
+//    workgroup streams its range once through a ring of LDS stages filled by
+//    direct global->LDS loads (three tiles in flight while one is used: one
+//    tile in flight left each CU waiting on memory latency) and leaves a
+//    partial result. A second kernel merges the ranges by their logsumexp.
 //  * The G = Hq / Hkv query heads that share a K/V head read it together: the
 //    G * Nq rows of such a group (contiguous in q, o and lse) form the MFMA
 //    row dimension, so the cache is read once per group, not once per head.
@@ -372,43 +373,61 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     if (hh == 0) p.part_lse[slot] = lt > 0.f ? st.m + __log2f(lt) : -INFINITY;
 }
 
-// Merge of the key ranges: one wave per query row. With L_r the ranges' log2
-// sums and mx = max_r L_r, weights w_r = exp2(L_r - mx); O = sum w_r O_r /
+// Merge of the key ranges: one workgroup per query row. With L_r the ranges'
+// log2 sums and mx = max_r L_r, weights w_r = exp2(L_r - mx); O = sum w_r O_r /
 // sum w_r and LSE = (mx + log2 sum w_r) * ln 2. Every row sees key 0, so some
-// range has a finite L_r.
+// range has a finite L_r. Thread t takes 4 output values (column c) of the
+// ranges r = g, g + SG, ... (group g): the loads of all ranges go out
+// together instead of one range after another.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
-    constexpr int E = D / 64;            // output values per lane
-    const int lane = threadIdx.x & 63;
-    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (long long)p.B * p.Hq * p.Nq) return;
-    const int grp = (int)(row / p.M), r = (int)(row - (long long)grp * p.M);
-    const int S = p.nsplit, M = p.M;
+    constexpr int C4 = D / 4;             // 4-value columns of a row
+    constexpr int SG = 256 / C4;          // range groups
+    __shared__ f32x4 part[256];
+    __shared__ float wpart[SG];
+    __shared__ float wmax[4];
+    const int t = threadIdx.x, c = t % C4, g = t / C4;
+    const long long row = blockIdx.x;
+    const int M = p.M, S = p.nsplit;
+    const int grp = (int)(row / M), r = (int)(row - (long long)grp * M);
     const float* pl = p.part_lse + (size_t)grp * S * M + r;
-    const float* po = p.part_o + ((size_t)grp * S * M + r) * D + lane * E;
+    const float* po = p.part_o + ((size_t)grp * S * M + r) * D + c * 4;
     float mx = -INFINITY;
-    for (int s = lane; s < S; s += 64) mx = fmaxf(mx, pl[(size_t)s * M]);
+    for (int s = t; s < S; s += 256) mx = fmaxf(mx, pl[(size_t)s * M]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    if ((t & 63) == 0) wmax[t >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    for (int s = 0; s < S; ++s) {
+#pragma unroll 4
+    for (int s = g; s < S; s += SG) {
         const float wt = fast_exp2(pl[(size_t)s * M] - mx);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(po + (size_t)s * M * D);
         wsum += wt;
-        const float* src = po + (size_t)s * M * D;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(wt, src[e], acc[e]);
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(wt, x[e], acc[e]);
     }
-    const float inv = 1.f / wsum;
-    uint16_t* Og = p.o + (size_t)row * D + lane * E;
-    if constexpr (E == 2) {
-        *reinterpret_cast<uint32_t*>(Og) = pack_bf16(acc[0] * inv, acc[1] * inv);
-    } else {
-        Og[0] = (uint16_t)(pack_bf16(acc[0] * inv, 0.f) & 0xffffu);
+    part[t] = acc;
+    if (c == 0) wpart[g] = wsum;
+    __syncthreads();
+    if (g != 0) return;
+#pragma unroll
+    for (int k = 1; k < SG; ++k) {
+        const f32x4 x = part[k * C4 + c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += x[e];
     }
-    if (lane == 0) p.lse[row] = (mx + __log2f(wsum)) * kLn2;
+    float wt = 0.f;
+#pragma unroll
+    for (int k = 0; k < SG; ++k) wt += wpart[k];
+    const float inv = 1.f / wt;
+    u32x2 val;
+    val[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
+    val[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(p.o + (size_t)row * D + c * 4) = val;
+    if (c == 0) p.lse[row] = (mx + __log2f(wt)) * kLn2;
 }
 
 template <int D>
@@ -418,7 +437,7 @@ hipError_t launch_decode_t(const DecParams& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     const long long rows = (long long)p.B * p.Hq * p.Nq;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
