@@ -12,7 +12,7 @@ No dataset is used; every tensor is N(0, 1) from a counter-based seed.
 
 Seeding: tensor t of workload c is drawn from numpy's PCG64 seeded with
 ``SeedSequence([2026, c, t])``. Tensor ids: Q = 0, K = 1, V = 2, dO = 3, spike
-positions = 4, row sample = 5. Each tensor has its own stream, so regenerating
+positions = 4, row sample = 5, per-sequence cache lengths = 6. Each tensor has its own stream, so regenerating
 one tensor never changes another.
 """
 from __future__ import annotations
@@ -22,7 +22,7 @@ import math
 
 import numpy as np
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DO, TENSOR_SPIKE, TENSOR_ROWS = range(6)
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DO, TENSOR_SPIKE, TENSOR_ROWS, TENSOR_LENS = range(7)
 ROOT_SEED = 2026
 
 
@@ -196,6 +196,7 @@ class DecodeWorkload:
     Nk: int
     d: int
     causal: bool = True
+    ragged: bool = False     # per-sequence cache lengths, uniform in [Nk / 16, Nk]
 
     @property
     def G(self) -> int:
@@ -207,7 +208,14 @@ class DecodeWorkload:
 
     def describe(self) -> dict:
         return dict(workload=self.name, B=self.B, Hq=self.Hq, Hkv=self.Hkv, Nq=self.Nq, Nk=self.Nk, d=self.d,
-                    causal=self.causal, passes="decode")
+                    causal=self.causal, ragged=self.ragged, passes="decode")
+
+
+def decode_seqlens(w: DecodeWorkload) -> np.ndarray | None:
+    """Cache rows in use per batch entry (int32 [B]) for a ragged decode workload, else None."""
+    if not w.ragged:
+        return None
+    return rng_for(w.cfg_id, TENSOR_LENS).integers(w.Nk // 16, w.Nk, size=w.B, endpoint=True).astype(np.int32)
 
 
 DECODE_WORKLOADS = {
@@ -215,6 +223,7 @@ DECODE_WORKLOADS = {
     "decode_gqa16k_q16": DecodeWorkload(6, "decode_gqa16k_q16", 2, 32, 8, 16, 16384, 128),
     "decode_long128k": DecodeWorkload(7, "decode_long128k", 1, 8, 8, 1, 131072, 128),
     "decode_batch64": DecodeWorkload(8, "decode_batch64", 64, 32, 8, 1, 4096, 128),
+    "decode_ragged64": DecodeWorkload(9, "decode_ragged64", 64, 32, 8, 1, 8192, 128, ragged=True),
 }
 
 

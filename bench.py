@@ -134,20 +134,30 @@ def cpu_baseline(w) -> dict:
 
 
 def decode_bytes(w) -> int:
-    """Bytes a decode step must move: K and V once, Q read, O written (bf16), LSE (fp32)."""
-    return 2 * 2 * w.B * w.Hkv * w.Nk * w.d + 2 * 2 * w.B * w.Hq * w.Nq * w.d + 4 * w.B * w.Hq * w.Nq
+    """Bytes a decode step must move: the K and V rows in use once, Q read, O written (bf16), LSE (fp32)."""
+    lens = ai.decode_seqlens(w)
+    keys = w.B * w.Nk if lens is None else int(lens.sum())
+    return 2 * 2 * w.Hkv * keys * w.d + 2 * 2 * w.B * w.Hq * w.Nq * w.d + 4 * w.B * w.Hq * w.Nq
 
 
 def decode_cpu_baseline(w) -> dict:
     """The fp64 oracle on the whole decode workload (it runs in seconds)."""
     import oracle
     inp = ai.make_decode_inputs(w)
-    q, k, v = (ai.bf16_bits_to_f64(inp[t]) for t in ("q", "k", "v"))
-    pos = w.Nk - w.Nq + np.arange(w.Nq, dtype=np.int64)
+    lens = ai.decode_seqlens(w)
+    if lens is None:
+        lens = np.full(w.B, w.Nk)
     orc = oracle.default()
-    t0 = time.perf_counter()
-    orc.fwd(q, k, v, w.causal, w.scale, qpos=pos if w.causal else None)
-    dt = time.perf_counter() - t0
+    dt = 0.0
+    for b in range(w.B):
+        L = int(lens[b])
+        q = ai.bf16_bits_to_f64(inp["q"][b:b + 1])
+        k = ai.bf16_bits_to_f64(inp["k"][b:b + 1, :, :L])
+        v = ai.bf16_bits_to_f64(inp["v"][b:b + 1, :, :L])
+        pos = L - w.Nq + np.arange(w.Nq, dtype=np.int64)
+        t0 = time.perf_counter()
+        orc.fwd(q, k, v, w.causal, w.scale, qpos=pos if w.causal else None)
+        dt += time.perf_counter() - t0
     return {"value": decode_bytes(w) / dt / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
             "sample": f"the whole {w.name} step in fp64 (the bytes of its bf16 inputs and outputs per second); "
                       f"{dt:.2f} s", "seconds": dt}
@@ -166,6 +176,8 @@ def decode_main(args) -> int:
 
     q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
     del inp
+    lens = ai.decode_seqlens(w)
+    sl = None if lens is None else torch.as_tensor(lens).cuda()
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=q.device)
     ws_bytes = fa.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal)
@@ -174,7 +186,8 @@ def decode_main(args) -> int:
     flush = torch.zeros(128 << 20, dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nk,
+    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+              None if sl is None else sl.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nk,
               w.d, w.causal, w.scale, ws.data_ptr(), ws_bytes, sp)
 
     def call():
@@ -221,7 +234,8 @@ def decode_main(args) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "passes": "decode"},
+                   "causal": w.causal, "passes": "decode",
+                   "keys_in_use": None if lens is None else int(lens.sum())},
         "ms_min": min(times),
         "wall_ms_per_step": wall / args.steps * 1e3,
         "roofline": {"bound": "hbm", "kernel": "decode (range kernel + merge)", "achieved": gbs,

@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_bwd_workspace_size.argtypes = [_i] * 6
         L.flash_attn_decode.restype = _i
-        L.flash_attn_decode.argtypes = [_vp] * 5 + [_i] * 7 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.flash_attn_decode.argtypes = [_vp] * 6 + [_i] * 7 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_decode_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_decode_workspace_size.argtypes = [_i] * 7
         L.flash_attn_strerror.restype = ctypes.c_char_p
@@ -104,11 +104,11 @@ def bwd_workspace_size(B, Hq, Hkv, N, d, causal) -> int:
     return int(lib().flash_attn_bwd_workspace_size(B, Hq, Hkv, N, d, int(causal)))
 
 
-def decode_raw(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
+def decode_raw(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
                stream=None) -> int:
-    """flash_attn_decode on raw addresses (ints); returns the status code."""
-    return lib().flash_attn_decode(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale), workspace,
-                                   workspace_bytes, stream)
+    """flash_attn_decode on raw addresses (ints; seqlens_k may be None); returns the status code."""
+    return lib().flash_attn_decode(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale),
+                                   workspace, workspace_bytes, stream)
 
 
 def decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal) -> int:
@@ -177,11 +177,14 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, wo
     return dq, dk, dv
 
 
-def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=None, out=None, lse=None):
+def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=None, out=None, lse=None,
+           seqlens_k=None):
     """Attention of the newest Nq query rows over a cache of Nk keys.
 
-    q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16. Causal: row i is token
-    Nk - Nq + i. Returns (o bf16 [B,Hq,Nq,d], lse fp32 [B,Hq,Nq])."""
+    q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16. seqlens_k: optional int32
+    device tensor [B], the cache rows in use per batch entry (default: all
+    Nk). Causal: row i is token L_b - Nq + i. Returns (o bf16 [B,Hq,Nq,d],
+    lse fp32 [B,Hq,Nq])."""
     import torch
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
@@ -191,6 +194,12 @@ def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=N
         raise ValueError("q and k/v must agree on B and d, and v must be shaped like k")
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _checked(t, name)
+    sl_ptr = None
+    if seqlens_k is not None:
+        if (seqlens_k.dtype != torch.int32 or not seqlens_k.is_cuda or not seqlens_k.is_contiguous()
+                or tuple(seqlens_k.shape) != (B,)):
+            raise ValueError("seqlens_k must be a contiguous int32 GPU tensor of shape [B]")
+        sl_ptr = seqlens_k.data_ptr()
     scale = default_scale(d) if scale is None else scale
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -199,6 +208,6 @@ def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=N
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Nq, Nk,
-                      d, causal, scale, ws_ptr, ws_len, _stream(q)))
+    _check(decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sl_ptr, B, Hq, Hkv,
+                      Nq, Nk, d, causal, scale, ws_ptr, ws_len, _stream(q)))
     return o, lse

@@ -212,14 +212,15 @@ size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, 
     return fa::dec_plan(B, Hq, Hkv, Nq, Nk, d).total;
 }
 
-int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                      int Hkv, int Nq, int Nk, int d, int causal, float scale, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     int st = check_decode_shape(B, Hq, Hkv, Nq, Nk, d, causal);
     if (st != FA_OK) return st;
     if ((st = check_scale(scale)) != FA_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0)
         return FA_ERR_ALIGN;
     const fa::DecPlan pl = fa::dec_plan(B, Hq, Hkv, Nq, Nk, d);
     if (pl.total > 0) {
@@ -235,6 +236,7 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
     char* ws = static_cast<char*>(workspace);
     p.part_lse = pl.total ? reinterpret_cast<float*>(ws + pl.part_lse) : nullptr;
     p.part_o = pl.total ? reinterpret_cast<float*>(ws + pl.part_o) : nullptr;
+    p.seqlens_k = seqlens_k;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d; p.G = Hq / Hkv; p.M = pl.M;
     p.causal = causal ? 1 : 0;
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
@@ -251,7 +253,7 @@ const char* flash_attn_strerror(int status) {
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "unsupported shape: B, Hq, Hkv, N must be >= 1, Hq % Hkv == 0, sizes in range";
         case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
-        case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned (seqlens_k: 4-byte)";
         case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
         case FA_ERR_HIP: return g_hip_text[0] ? g_hip_text : "HIP launch failed";
         case FA_ERR_SCALE: return "scale must be finite and >= 0";

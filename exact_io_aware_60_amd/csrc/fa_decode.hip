@@ -222,6 +222,9 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     const int rest = blockIdx.x / p.nsplit;
     const int rblk = rest % p.nrb, grp = rest / p.nrb;
     const int M = p.M, Nk = p.Nk;
+    // keys in use for this batch entry: the first L of its Nk cache rows
+    int L = Nk;
+    if (p.seqlens_k) L = min(max(p.seqlens_k[grp / p.Hkv], 0), Nk);
 
     // waves -> (32-row block, key half)
     const int rows_here = min(kDRows, M - rblk * kDRows);
@@ -240,12 +243,15 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     const int h0 = p.pair ? kw : 0, h1 = p.pair ? kw + 1 : 2;
     const int r = rblk * kDRows + rb * 32 + l32;          // this lane's row in the group
     const bool row_ok = active && r < M;
-    // causal: row r is token Nk - Nq + (r % Nq); keys after it are invisible
-    const int pos = (p.causal && row_ok) ? Nk - p.Nq + r % p.Nq : 0x7fffffff;
+    // causal: row r is token L - Nq + (r % Nq); keys after it are invisible
+    // (a negative position: the row sees no key)
+    const int pos = (p.causal && row_ok) ? L - p.Nq + r % p.Nq : 0x7fffffff;
     // chunks ending after mfrom may hold invisible keys
-    const int mfrom = p.causal ? Nk - p.Nq + 1 : Nk;
+    const int mfrom = p.causal ? L - p.Nq + 1 : L;
 
-    const int ntile = (Nk + kDBN - 1) / kDBN;
+    // this range's tiles that hold keys in use (none: the range reports an
+    // empty result)
+    const int ntile = (L + kDBN - 1) / kDBN;
     const int t0 = split * p.tps;
     const int nt = min(p.tps, ntile - t0);
 
@@ -280,6 +286,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     pk.init(w, lane, D);
     pv.init(w, lane, D);
     constexpr uint32_t kTileBytes = kDBN * D * 2;
+    if (nt > 0) {
     // Ring of NS stages: tiles j+1 .. j+NS-2 stay in flight while tile j is
     // used, and tile j+NS-1 goes into the stage tile j-1 used. The first NS-1
     // copies are issued unconditionally (a range shorter than that re-copies
@@ -304,7 +311,8 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
         const int jn = j + NS - 1;
         dec_iteration<D>(st, pk, pv, rk, rv, jn < nt, (uint32_t)(t0 + jn) * kTileBytes,
                          ring + (jn % NS) * C::STAGE, ring + (j % NS) * C::STAGE, w, active, h0, h1,
-                         (t0 + j) * kDBN, Nk, pos, mfrom, sl2, kbase, vbase, hh);
+                         (t0 + j) * kDBN, L, pos, mfrom, sl2, kbase, vbase, hh);
+    }
     }
 
     if (p.pair) {
@@ -341,9 +349,10 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     const float lt = st.l + swap_half(st.l);
     if (r >= M) return;
     if (p.nsplit == 1) {
-        // a single range: the final result (every row sees key 0, so lt >= 1)
+        // a single range: the final result (a row that sees no key gets
+        // O = 0 and LSE = -inf)
         uint16_t* Og = p.o + ((size_t)grp * M + r) * D;
-        const float inv = 1.f / lt;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -353,7 +362,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
                 val[1] = pack_bf16(st.o[db][u * 4 + 2] * inv, st.o[db][u * 4 + 3] * inv);
                 *reinterpret_cast<u32x2*>(Og + db * 32 + u * 8 + hh * 4) = val;
             }
-        if (hh == 0) p.lse[(size_t)grp * M + r] = (st.m + __log2f(lt)) * kLn2;
+        if (hh == 0) p.lse[(size_t)grp * M + r] = lt > 0.f ? (st.m + __log2f(lt)) * kLn2 : -INFINITY;
         return;
     }
     // partial result of this range: normalised O and log2 of the sum (a row
@@ -375,8 +384,8 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
 
 // Merge of the key ranges: one workgroup per query row. With L_r the ranges'
 // log2 sums and mx = max_r L_r, weights w_r = exp2(L_r - mx); O = sum w_r O_r /
-// sum w_r and LSE = (mx + log2 sum w_r) * ln 2. Every row sees key 0, so some
-// range has a finite L_r. Thread t takes 4 output values (column c) of the
+// sum w_r and LSE = (mx + log2 sum w_r) * ln 2. A row with no finite L_r saw
+// no key at all: O = 0 and LSE = -inf. Thread t takes 4 output values (column c) of the
 // ranges r = g, g + SG, ... (group g): the loads of all ranges go out
 // together instead of one range after another.
 template <int D>
@@ -399,11 +408,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     if ((t & 63) == 0) wmax[t >> 6] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float mref = mx == -INFINITY ? 0.f : mx;       // all weights 0 then, not NaN
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
 #pragma unroll 4
     for (int s = g; s < S; s += SG) {
-        const float wt = fast_exp2(pl[(size_t)s * M] - mx);
+        const float wt = fast_exp2(pl[(size_t)s * M] - mref);
         const f32x4 x = *reinterpret_cast<const f32x4*>(po + (size_t)s * M * D);
         wsum += wt;
 #pragma unroll
@@ -422,12 +432,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     float wt = 0.f;
 #pragma unroll
     for (int k = 0; k < SG; ++k) wt += wpart[k];
-    const float inv = 1.f / wt;
+    const float inv = wt > 0.f ? 1.f / wt : 0.f;
     u32x2 val;
     val[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
     val[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
     *reinterpret_cast<u32x2*>(p.o + (size_t)row * D + c * 4) = val;
-    if (c == 0) p.lse[row] = (mx + __log2f(wt)) * kLn2;
+    if (c == 0) p.lse[row] = wt > 0.f ? (mx + __log2f(wt)) * kLn2 : -INFINITY;
 }
 
 template <int D>

@@ -65,6 +65,7 @@ struct DecParams {
     float* lse;          // fp32 [B, Hq, Nq]
     float* part_lse;     // fp32 [groups][nsplit][M]: log2 of the range's sum of exp2 (-inf: no key seen)
     float* part_o;       // fp32 [groups][nsplit][M][d]: the range's normalised output (0: no key seen)
+    const int* seqlens_k;  // int32 [B] keys in use per batch entry (clamped to [0, Nk]), or null: all Nk
     int B, Hq, Hkv, Nq, Nk, d, G, M;
     int causal;
     float scale_log2;

@@ -57,7 +57,7 @@ enum fa_status {
     FA_ERR_NULL = -1,      /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow */
     FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
-    FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+    FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned (seqlens_k: 4-byte) */
     FA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
     FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
     FA_ERR_SCALE = -7      /* scale is negative, NaN or infinite */
@@ -150,17 +150,22 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
  * diagram). So this entry point splits the keys of every K/V head into
  * ranges read by separate workgroups, which keeps the whole GPU reading, and
  * merges the per-range results by their logsumexp.
- *   q    in   bf16 [B, Hq,  Nq, d]    the newest Nq query rows
- *   k    in   bf16 [B, Hkv, Nk, d]    the key/value cache
- *   v    in   bf16 [B, Hkv, Nk, d]
- *   o    out  bf16 [B, Hq,  Nq, d]
- *   lse  out  fp32 [B, Hq,  Nq]       natural-log logsumexp, as in flash_attn_fwd
- * causal: query row i is token Nk - Nq + i of the sequence the keys belong to
- * (the queries are its last Nq tokens) and sees keys j <= Nk - Nq + i; this
- * needs Nq <= Nk. causal = 0: every row sees all Nk keys. With Nq = Nk and
- * causal = 1 the result is that of flash_attn_fwd.
- * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {64, 128};
- * Nk * d * 2 < 2^31 bytes per K/V head. Any Nq is accepted; the path is made
+ *   q          in   bf16 [B, Hq,  Nq, d]    the newest Nq query rows
+ *   k          in   bf16 [B, Hkv, Nk, d]    the key/value cache, Nk rows per head
+ *   v          in   bf16 [B, Hkv, Nk, d]
+ *   o          out  bf16 [B, Hq,  Nq, d]
+ *   lse        out  fp32 [B, Hq,  Nq]       natural-log logsumexp, as in flash_attn_fwd
+ *   seqlens_k  in   int32 [B] device array, or NULL: batch entry b uses the
+ *              first L_b = seqlens_k[b] rows of its cache (clamped to
+ *              [0, Nk]; rows past L_b are never read into the result). NULL:
+ *              L_b = Nk for every entry.
+ * causal: query row i is token L_b - Nq + i of the sequence the keys belong to
+ * (the queries are its last Nq tokens) and sees keys j <= L_b - Nq + i.
+ * causal = 0: every row sees all L_b keys. With Nq = Nk = L_b and causal = 1
+ * the result is that of flash_attn_fwd. A row that sees no key at all (L_b =
+ * 0, or L_b - Nq + i < 0) gets O = 0 and LSE = -inf.
+ * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {64, 128}; Nq <= Nk
+ * when causal; Nk * d * 2 < 2^31 bytes per K/V head. Any Nq is accepted; the path is made
  * for (Hq / Hkv) * Nq <= 128 query rows per K/V head, and larger counts read
  * the cache once per 128 rows. Inputs and outputs must not overlap.
  * workspace: device memory of workspace_bytes >=
@@ -171,12 +176,14 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
  * not depend on the stream or on earlier calls (no atomics).
  */
 int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      int causal, float scale, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /*
  * Bytes of device workspace flash_attn_decode needs for these arguments, or 0
- * when it needs none or rejects the shape. The workspace holds, for every
+ * when it needs none or rejects the shape. It depends on the cache capacity
+ * Nk, not on seqlens_k. The workspace holds, for every
  * key range of every K/V head and every query row, one fp32 logsumexp and d
  * fp32 output values: about R * B * Hq * Nq * (d + 1) * 4 bytes for R ranges
  * per head (R is chosen from the shape so that the grid fills the GPU).

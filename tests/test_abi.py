@@ -144,11 +144,11 @@ def test_workspace_size_rejects_bad_shapes():
 
 
 def dec_call(**over):
-    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=2, Hq=32, Hkv=8, Nq=1, Nk=16384, d=128, causal=1,
-             scale=0.088, ws=P[9], ws_bytes=1 << 30)
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], sl=None, B=2, Hq=32, Hkv=8, Nq=1, Nk=16384, d=128,
+             causal=1, scale=0.088, ws=P[9], ws_bytes=1 << 30)
     a.update(over)
-    return fa.decode_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
-                         a["d"], a["causal"], a["scale"], a["ws"], a["ws_bytes"])
+    return fa.decode_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                         a["Nk"], a["d"], a["causal"], a["scale"], a["ws"], a["ws_bytes"])
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse"])
@@ -166,6 +166,7 @@ def test_decode_checks():
     assert dec_call(d=96) == fa.FA_ERR_HEADDIM
     assert dec_call(scale=-1.0) == fa.FA_ERR_SCALE
     assert dec_call(o=P[3] + 2) == fa.FA_ERR_ALIGN
+    assert dec_call(sl=P[11] + 2) == fa.FA_ERR_ALIGN
     need = fa.decode_workspace_size(2, 32, 8, 1, 16384, 128, 1)
     assert need > 0
     assert dec_call(ws=None) == fa.FA_ERR_WORKSPACE

@@ -9,7 +9,9 @@ The cases cover the kernel's layouts: one or two 32-row blocks per K/V head
 (two waves per block, one per half tile), three and four blocks (one wave
 each), more than 128 rows (several row blocks), a single key range (output
 written directly) and many ranges (partial results merged by logsumexp), ragged
-and tiny caches, both head dimensions and both masks.
+and tiny caches, both head dimensions and both masks, and per-sequence cache
+lengths (seqlens_k), including entries with no key at all and rows that see
+none (their O is 0 and LSE -inf, as in the oracle).
 """
 import math
 
@@ -33,12 +35,44 @@ def fa():
     return fa
 
 
-def run_decode(fa, inp, causal, scale):
+def run_decode(fa, inp, causal, scale, seqlens=None):
     import torch
     q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
-    o, lse = fa.decode(q, k, v, causal=causal, scale=scale)
+    sl = None if seqlens is None else torch.as_tensor(np.asarray(seqlens, np.int32)).cuda()
+    o, lse = fa.decode(q, k, v, causal=causal, scale=scale, seqlens_k=sl)
     torch.cuda.synchronize()
     return from_dev_bf16(o), from_dev_f32(lse)
+
+
+def oracle_decode_ragged(inp, causal, scale, seqlens):
+    """Per batch entry b, the oracle over the first L_b = clamp(seqlens[b], 0, Nk)
+    cache rows; an entry with no key gives O = 0 and LSE = -inf on every row."""
+    B, Hq, Nq, d = inp["q"].shape
+    Nk = inp["k"].shape[2]
+    o = np.zeros((B, Hq, Nq, d))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        L = int(min(max(int(seqlens[b]), 0), Nk))
+        if L == 0:
+            continue
+        pos = L - Nq + np.arange(Nq, dtype=np.int64) if causal else None
+        o[b:b + 1], lse[b:b + 1] = oracle.fwd(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1, :, :L]),
+                                              f64(inp["v"][b:b + 1, :, :L]), causal, scale, qpos=pos)
+    return o, lse
+
+
+def check_ragged(fa, inp, causal, scale, seqlens, tag):
+    B, Hq, Nq, d = inp["q"].shape
+    _, Hkv, Nk, _ = inp["k"].shape
+    say(f"decode {tag}: B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} causal={causal} seqlens={list(seqlens)[:8]}")
+    o, lse = run_decode(fa, inp, causal, scale, seqlens)
+    ro, rl = oracle_decode_ragged(inp, causal, scale, seqlens)
+    empty = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), empty), f"{tag}: rows without keys differ"
+    assert np.all(o[empty] == 0.0), f"{tag}: rows without keys must give O = 0"
+    eo = excess_err(o, ro)
+    el = max_err(lse[~empty], rl[~empty]) if (~empty).any() else 0.0
+    assert eo <= TOL_O and el <= TOL_LSE, f"{tag}: O err {eo:.2e}, LSE err {el:.2e}"
 
 
 def oracle_decode(inp, causal, scale):
@@ -149,9 +183,50 @@ def test_deterministic(fa):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_seqlens_ragged(fa, causal, d):
+    """Entries with 0, 1, 2, 65 and all cache rows, one past the capacity
+    (clamped) and a negative length (clamped to 0); with Nq = 3 and the causal
+    mask the 1- and 2-key entries have rows that see no key."""
+    inp = ai.make_decode_case(7, 4, 2, 3, 700, d, seed=97 + d + int(causal))
+    check_ragged(fa, inp, causal, 1.0 / math.sqrt(d), [0, 1, 2, 65, 700, 5000, -3], "seqlens ragged")
+
+
+def test_seqlens_many_ranges(fa):
+    """Few groups, so the keys split into many ranges; the short entry leaves
+    most of its ranges empty, which the merge must weigh 0."""
+    inp = ai.make_decode_case(2, 8, 1, 2, 9000, 128, seed=98)
+    check_ragged(fa, inp, True, 0.0883883, [150, 8999], "seqlens many ranges")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_seqlens_direct(fa, d):
+    """512 groups, one range each (no merge), random lengths including 0."""
+    B, Hq, Hkv, Nq, Nk = 64, 16, 8, 1, 300
+    assert fa.decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, 1) == 0
+    inp = ai.make_decode_case(B, Hq, Hkv, Nq, Nk, d, seed=99 + d)
+    lens = np.random.default_rng(99 + d).integers(0, Nk, size=B, endpoint=True)
+    lens[:3] = (0, 1, Nk)
+    check_ragged(fa, inp, True, 1.0 / math.sqrt(d), lens, "seqlens direct")
+
+
+def test_seqlens_full_is_default(fa):
+    """seqlens_k equal to the capacity gives bit-identical results to no seqlens_k."""
+    inp = ai.make_decode_case(3, 8, 2, 2, 3000, 128, seed=100)
+    say("decode seqlens = Nk vs none")
+    o1, l1 = run_decode(fa, inp, True, 0.0883883)
+    o2, l2 = run_decode(fa, inp, True, 0.0883883, [3000, 3000, 3000])
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 @pytest.mark.parametrize("name", sorted(ai.DECODE_WORKLOADS))
 def test_workload(fa, name):
     """The measured decode workloads at full size, every row against the oracle."""
     w = ai.DECODE_WORKLOADS[name]
     inp = ai.make_decode_inputs(w)
-    check(fa, inp, w.causal, w.scale, name)
+    lens = ai.decode_seqlens(w)
+    if lens is None:
+        check(fa, inp, w.causal, w.scale, name)
+    else:
+        check_ragged(fa, inp, w.causal, w.scale, lens, name)
