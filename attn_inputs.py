@@ -246,3 +246,67 @@ def make_decode_case(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, seed: 
         "k": bf16_round_bits(normal_f32((B, Hkv, Nk, d), cid, TENSOR_K) * f),
         "v": bf16_round_bits(normal_f32((B, Hkv, Nk, d), cid, TENSOR_V)),
     }
+
+
+# ---------------------------------------------------------------- packed (variable-length) workloads
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """B sequences of different lengths packed head by head: q [Hq, total, d],
+    k/v [Hkv, total, d]; lengths uniform in [min_len, max_len] (seeded)."""
+    cfg_id: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    min_len: int
+    max_len: int
+    d: int
+    causal: bool = True
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    def lengths(self) -> np.ndarray:
+        return rng_for(self.cfg_id, TENSOR_LENS).integers(self.min_len, self.max_len, size=self.B,
+                                                          endpoint=True).astype(np.int64)
+
+    def describe(self) -> dict:
+        return dict(workload=self.name, B=self.B, Hq=self.Hq, Hkv=self.Hkv, min_len=self.min_len,
+                    max_len=self.max_len, d=self.d, causal=self.causal, passes="fwd (packed sequences)")
+
+
+VARLEN_WORKLOADS = {
+    # a prefill batch of 16 prompts of 512 .. 16384 tokens, with the GQA heads of the gqa16k workload
+    "varlen_mix": VarlenWorkload(10, "varlen_mix", 16, 32, 8, 512, 16384, 128),
+}
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """int32 [B + 1] offsets of packed sequences."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))]).astype(np.int32)
+
+
+def make_varlen_inputs(w: VarlenWorkload) -> dict:
+    lens = w.lengths()
+    total = int(lens.sum())
+    return {
+        "q": normal_bf16((w.Hq, total, w.d), w.cfg_id, TENSOR_Q),
+        "k": normal_bf16((w.Hkv, total, w.d), w.cfg_id, TENSOR_K),
+        "v": normal_bf16((w.Hkv, total, w.d), w.cfg_id, TENSOR_V),
+        "lengths": lens,
+        "cu_seqlens": cu_seqlens(lens),
+    }
+
+
+def make_varlen_case(lengths, Hq: int, Hkv: int, d: int, seed: int) -> dict:
+    """Small packed case (cfg_id space 4000 + seed)."""
+    cid = 4000 + seed
+    total = int(np.sum(lengths))
+    return {
+        "q": normal_bf16((Hq, total, d), cid, TENSOR_Q),
+        "k": normal_bf16((Hkv, total, d), cid, TENSOR_K),
+        "v": normal_bf16((Hkv, total, d), cid, TENSOR_V),
+        "lengths": np.asarray(lengths, np.int64),
+        "cu_seqlens": cu_seqlens(lengths),
+    }

@@ -13,6 +13,10 @@ it runs on. Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
 
+With --varlen NAME it measures the forward pass over packed sequences of
+different lengths (flash_attn_fwd_varlen) against the MFMA roofline, counting
+4*Hq*d FLOP per visible (query, key) pair of every sequence.
+
 With --decode NAME it measures instead the decode path (a few query rows over
 a long key/value cache) on one of the decode workloads, against the HBM
 roofline: the bytes the step must move (K and V once, Q, O and LSE) over the
@@ -252,6 +256,75 @@ def decode_main(args) -> int:
     return 0
 
 
+def varlen_main(args) -> int:
+    import torch
+    import exact_io_aware_60_amd as fa
+
+    fa.lib()
+    w = ai.VARLEN_WORKLOADS[args.varlen]
+    inp = ai.make_varlen_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    lens = inp["lengths"]
+    cu = torch.as_tensor(inp["cu_seqlens"]).cuda()
+    del inp
+    total, ms = int(lens.sum()), int(lens.max())
+    o = torch.empty_like(q)
+    lse = torch.empty((w.Hq, total), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu.data_ptr(), len(lens), ms,
+              total, w.Hq, w.Hkv, w.d, w.causal, w.scale, sp)
+
+    def call():
+        st = fa.fwd_varlen_raw(*args_c)
+        if st != 0:
+            raise RuntimeError(f"fwd_varlen: {fa.strerror(st)}")
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record(stream)
+        call()
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = [a.elapsed_time(b) for a, b in ev]
+    ms_avg = sum(times) / len(times)
+    pairs = float(sum(int(n) * int(n) for n in lens)) / (2.0 if w.causal else 1.0)
+    flop = 4.0 * w.Hq * w.d * pairs
+    tflops = flop / (ms_avg * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd TFLOP/s over packed sequences (bf16) and % of MI355X bf16 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_avg,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "total": total, "max_seqlen": ms,
+                   "min_len": int(lens.min()), "d": w.d, "causal": w.causal, "passes": "fwd (packed sequences)"},
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel (packed)", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "avg_launch_ms": ms_avg, "algorithmic_flop_per_launch": flop},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +336,8 @@ def main() -> int:
                          "profiled run holds the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--decode", choices=sorted(ai.DECODE_WORKLOADS), default=None,
                     help="measure the decode path on this workload instead of the forward + backward step")
+    ap.add_argument("--varlen", choices=sorted(ai.VARLEN_WORKLOADS), default=None,
+                    help="measure the forward pass over this packed variable-length workload instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the attention path here is single-GPU (asked for --gpus {args.gpus}).",
@@ -274,6 +349,12 @@ def main() -> int:
             print("bench.py needs a GPU", file=sys.stderr)
             return 2
         return decode_main(args)
+    if args.varlen:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            return 2
+        return varlen_main(args)
 
     import torch
     import exact_io_aware_60_amd as fa

@@ -25,7 +25,7 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
             "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
-            "flash_attn_decode", "flash_attn_decode_workspace_size")
+            "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_bwd_workspace_size.argtypes = [_i] * 6
+        L.flash_attn_fwd_varlen.restype = _i
+        L.flash_attn_fwd_varlen.argtypes = [_vp] * 6 + [_i] * 7 + [ctypes.c_float, _vp]
         L.flash_attn_decode.restype = _i
         L.flash_attn_decode.argtypes = [_vp] * 6 + [_i] * 7 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_decode_workspace_size.restype = ctypes.c_size_t
@@ -102,6 +104,13 @@ def bwd_stage_raw(stage: int, q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d,
 
 def bwd_workspace_size(B, Hq, Hkv, N, d, causal) -> int:
     return int(lib().flash_attn_bwd_workspace_size(B, Hq, Hkv, N, d, int(causal)))
+
+
+def fwd_varlen_raw(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total, Hq, Hkv, d, causal, scale,
+                   stream=None) -> int:
+    """flash_attn_fwd_varlen on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total, Hq, Hkv, d, int(causal),
+                                       float(scale), stream)
 
 
 def decode_raw(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
@@ -210,4 +219,30 @@ def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=N
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sl_ptr, B, Hq, Hkv,
                       Nq, Nk, d, causal, scale, ws_ptr, ws_len, _stream(q)))
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None, out=None,
+               lse=None):
+    """Forward pass over packed sequences: q [Hq, total, d], k/v [Hkv, total, d] bf16,
+    cu_seqlens int32 [B + 1] on the GPU (sequence b is rows cu_seqlens[b] ..
+    cu_seqlens[b+1]-1). Returns (o bf16 [Hq, total, d], lse fp32 [Hq, total])."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [Hq, total, d] and k, v [Hkv, total, d]")
+    Hq, total, d = q.shape
+    Hkv = k.shape[0]
+    if k.shape[1:] != (total, d):
+        raise ValueError("q and k/v must agree on total and d")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _checked(t, name)
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or not cu_seqlens.is_contiguous() \
+            or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a contiguous int32 GPU tensor of shape [B + 1]")
+    B = cu_seqlens.numel() - 1
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, total), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(fwd_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          cu_seqlens.data_ptr(), B, int(max_seqlen), total, Hq, Hkv, d, causal, scale, _stream(q)))
     return o, lse

@@ -83,6 +83,35 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
     p.causal = causal ? 1 : 0;
     p.scale = scale;
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    p.cu_seqlens = nullptr;
+    p.total = 0;
+    return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* cu_seqlens, int B, int max_seqlen, int total, int Hq, int Hkv, int d,
+                          int causal, float scale, void* stream) {
+    if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
+    int st = check_shape(B, Hq, Hkv, max_seqlen, d);
+    if (st != FA_OK) return st;
+    if (total < 1 || (long double)Hq * total * d >= 4.0e18L) return FA_ERR_SHAPE;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return FA_ERR_ALIGN;
+    log_config("fwd_varlen", B, Hq, Hkv, max_seqlen, d, causal);
+    fa::FwdParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = max_seqlen; p.d = d; p.G = Hq / Hkv;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    p.cu_seqlens = cu_seqlens;
+    p.total = total;
     return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -253,7 +282,7 @@ const char* flash_attn_strerror(int status) {
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "unsupported shape: B, Hq, Hkv, N must be >= 1, Hq % Hkv == 0, sizes in range";
         case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128";
-        case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned (seqlens_k: 4-byte)";
+        case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned (int32 length arrays: 4-byte)";
         case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
         case FA_ERR_HIP: return g_hip_text[0] ? g_hip_text : "HIP launch failed";
         case FA_ERR_SCALE: return "scale must be finite and >= 0";

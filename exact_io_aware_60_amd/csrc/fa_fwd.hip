@@ -389,18 +389,40 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5, g = lane >> 4;
-    const int N = p.N;
     const bool causal = p.causal != 0;
-    const int nqt = (N + kBM - 1) / kBM;
+    const int nqt = (p.N + kBM - 1) / kBM;
     int rank, bh;
     unmap_block(blockIdx.x, p.B * p.Hq, rank, bh);
+    // Causal: the heaviest q-tiles first. The work of a tile depends only on
+    // its index, so with packed sequences this order is heaviest first too.
     const int qt = causal ? nqt - 1 - rank : rank;
+    if (p.cu_seqlens) {
+        // Packed sequences differ in length, so an XCD must not own whole
+        // sequences: read the index K/V-head-major, (hkv, b, g), so that each
+        // XCD's block of indices is one K/V head (its G query heads) of every
+        // sequence. The load is then even over the XCDs and a K/V head's
+        // re-reads stay in one L2.
+        const int g = bh % p.G, u = bh / p.G;
+        const int bb = u % p.B, kv = u / p.B;
+        bh = bb * p.Hq + kv * p.G + g;
+    }
     const int b = bh / p.Hq, hq = bh - b * p.Hq, hkv = hq / p.G;
-    const uint16_t* Qg = p.q + (size_t)bh * N * D;
-    const uint16_t* Kg = p.k + ((size_t)b * p.Hkv + hkv) * N * D;
-    const uint16_t* Vg = p.v + ((size_t)b * p.Hkv + hkv) * N * D;
-
+    int N = p.N;
+    size_t qrow0 = (size_t)bh * N, kvrow0 = ((size_t)b * p.Hkv + hkv) * N;   // first row of the head
+    if (p.cu_seqlens) {
+        // packed: this sequence's rows; the bounds are clamped so that any
+        // cu_seqlens keeps every access inside the [H, total] arrays
+        const int s0 = min(max(p.cu_seqlens[b], 0), p.total);
+        N = min(max(p.cu_seqlens[b + 1] - s0, 0), min(p.N, p.total - s0));
+        qrow0 = (size_t)hq * p.total + s0;
+        kvrow0 = (size_t)hkv * p.total + s0;
+    }
     const int q0 = qt * kBM;
+    if (q0 >= N) return;          // a q-tile past a shorter packed sequence (whole workgroup)
+    const uint16_t* Qg = p.q + qrow0 * D;
+    const uint16_t* Kg = p.k + kvrow0 * D;
+    const uint16_t* Vg = p.v + kvrow0 * D;
+
     const int r0 = q0 + w * kWM;                 // this wave's first query row
     const int qrow = r0 + l32;                   // this lane's query row
     const int ntk = (N + kBN - 1) / kBN;
@@ -459,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     }
 
     if (wave_valid && qrow < N) {
-        uint16_t* Og = p.o + (size_t)bh * N * D + (size_t)qrow * D;
+        uint16_t* Og = p.o + (qrow0 + qrow) * D;
         const float lt = st.l + swap_half(st.l);
         const float inv = 1.f / lt;
 #pragma unroll
@@ -471,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
                 val[1] = pack_bf16(st.o[db][u * 4 + 2] * inv, st.o[db][u * 4 + 3] * inv);
                 *reinterpret_cast<u32x2*>(Og + db * 32 + u * 8 + hh * 4) = val;
             }
-        if (hh == 0) p.lse[(size_t)bh * N + qrow] = (st.m + __log2f(lt)) * kLn2;
+        if (hh == 0) p.lse[qrow0 + qrow] = (st.m + __log2f(lt)) * kLn2;
     }
 }
 

@@ -16,6 +16,12 @@ struct FwdParams {
     int causal;
     float scale;         // softmax scale
     float scale_log2;    // scale * log2(e)
+    // Packed sequences of different lengths (null: every sequence has N rows).
+    // Then q/o are [Hq, total, d], k/v [Hkv, total, d], lse [Hq, total];
+    // sequence b holds rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head,
+    // and N is the longest sequence (it sizes the grid).
+    const int* cu_seqlens;
+    int total;
 };
 
 struct BwdParams {

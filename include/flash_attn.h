@@ -57,7 +57,7 @@ enum fa_status {
     FA_ERR_NULL = -1,      /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow */
     FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
-    FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned (seqlens_k: 4-byte) */
+    FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned (int32 length arrays: 4-byte) */
     FA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
     FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
     FA_ERR_SCALE = -7      /* scale is negative, NaN or infinite */
@@ -76,6 +76,29 @@ enum fa_status {
 int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                    void* stream);
+
+/*
+ * Forward pass over packed sequences of different lengths (one launch for a
+ * batch of prompts, no padding). Same computation as flash_attn_fwd for each
+ * sequence on its own; the sequences share heads and nothing else.
+ *   q           in   bf16 [Hq,  total, d]   sequence b is rows cu_seqlens[b] ..
+ *   k, v        in   bf16 [Hkv, total, d]   cu_seqlens[b+1]-1 of every head
+ *   o           out  bf16 [Hq,  total, d]
+ *   lse         out  fp32 [Hq,  total]
+ *   cu_seqlens  in   int32 [B + 1] device array: 0 = cu_seqlens[0] <= ... <=
+ *                    cu_seqlens[B] = total, every length <= max_seqlen
+ * max_seqlen sizes the grid (workgroups of q-tiles past a shorter sequence
+ * exit at once). causal: within each sequence, row i sees keys j <= i.
+ * Supported: B, max_seqlen, total, Hq, Hkv >= 1 and the limits of
+ * flash_attn_fwd with N = max_seqlen. cu_seqlens is device data and is not
+ * read on the host: offsets and lengths that break the rules above are
+ * clamped in the kernel to [0, total] and [0, min(max_seqlen, total - offset)],
+ * so no access leaves the arrays, but the affected sequences' results are
+ * then unspecified. cu_seqlens must be 4-byte aligned.
+ */
+int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int* cu_seqlens, int B, int max_seqlen, int total, int Hq, int Hkv,
+                          int d, int causal, float scale, void* stream);
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for these arguments, or 0 for

@@ -197,3 +197,27 @@ def test_decode_single_range_needs_no_workspace():
     """A grid that already fills the GPU (B * Hkv >= 512 groups) reads each head
     in one range and writes the output directly."""
     assert fa.decode_workspace_size(64, 32, 8, 1, 8192, 128, 1) == 0
+
+
+def varlen_call(**over):
+    a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], cu=P[5], B=4, ms=4096, total=9000, Hq=32, Hkv=8, d=128,
+             causal=1, scale=0.088)
+    a.update(over)
+    return fa.fwd_varlen_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["ms"], a["total"],
+                             a["Hq"], a["Hkv"], a["d"], a["causal"], a["scale"])
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "lse", "cu"])
+def test_varlen_null(name):
+    assert varlen_call(**{name: None}) == fa.FA_ERR_NULL
+
+
+def test_varlen_checks():
+    assert varlen_call(B=0) == fa.FA_ERR_SHAPE
+    assert varlen_call(ms=0) == fa.FA_ERR_SHAPE
+    assert varlen_call(total=0) == fa.FA_ERR_SHAPE
+    assert varlen_call(Hq=6, Hkv=4) == fa.FA_ERR_SHAPE
+    assert varlen_call(d=96) == fa.FA_ERR_HEADDIM
+    assert varlen_call(scale=float("nan")) == fa.FA_ERR_SCALE
+    assert varlen_call(cu=P[5] + 2) == fa.FA_ERR_ALIGN
+    assert varlen_call(o=P[3] + 8) == fa.FA_ERR_ALIGN

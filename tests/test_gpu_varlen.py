@@ -1,0 +1,109 @@
+"""GPU forward over packed sequences of different lengths against the fp64 oracle.
+
+Each sequence is an independent attention problem, so the oracle runs the
+textbook definition on each sequence's rows alone. Tolerances are the forward
+pass's (O <= 1e-2 beyond the bf16 output rounding, LSE <= 1e-3). Small cases
+compare every element; the full-size packed workload compares seeded samples
+of query rows in every sequence, which the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from tests.gpu_util import TOL_LSE, TOL_O, excess_err, f64, from_dev_bf16, from_dev_f32, max_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import exact_io_aware_60_amd as fa
+    fa.lib()
+    return fa
+
+
+def run_varlen(fa, inp, causal, scale, max_seqlen=None):
+    import torch
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    cu = torch.as_tensor(inp["cu_seqlens"]).cuda()
+    ms = int(max(inp["lengths"].max(), 1)) if max_seqlen is None else max_seqlen
+    o, lse = fa.fwd_varlen(q, k, v, cu, ms, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return from_dev_bf16(o), from_dev_f32(lse)
+
+
+def check(fa, inp, causal, scale, tag, rows_per_seq=None, max_seqlen=None):
+    lens, cu = inp["lengths"], inp["cu_seqlens"]
+    Hq, total, d = inp["q"].shape
+    say(f"varlen {tag}: B={len(lens)} Hq={Hq} Hkv={inp['k'].shape[0]} total={total} d={d} causal={causal}")
+    o, lse = run_varlen(fa, inp, causal, scale, max_seqlen)
+    eo = el = 0.0
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        rows = np.arange(n, dtype=np.int64) if rows_per_seq is None else ai.sample_rows(int(n), rows_per_seq, 50 + b)
+        qs = f64(inp["q"][None, :, s0:s1][:, :, rows])
+        ks, vs = f64(inp["k"][None, :, s0:s1]), f64(inp["v"][None, :, s0:s1])
+        ro, rl = oracle.fwd(qs, ks, vs, causal, scale, qpos=rows)
+        eo = max(eo, excess_err(o[None, :, s0:s1][:, :, rows], ro))
+        el = max(el, max_err(lse[None, :, s0:s1][:, :, rows], rl))
+    assert eo <= TOL_O and el <= TOL_LSE, f"{tag}: O err {eo:.2e}, LSE err {el:.2e}"
+
+
+LENGTHS = [
+    [1],
+    [300],
+    [1, 17, 256, 257, 700],
+    [0, 64, 0, 513, 5],          # empty sequences in between
+    [1000, 999, 3, 1024],
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("lens", LENGTHS, ids=["-".join(map(str, x)) for x in LENGTHS])
+def test_lengths(fa, lens, causal, d):
+    inp = ai.make_varlen_case(lens, 4, 2, d, seed=sum(lens) % 997 + d + int(causal))
+    check(fa, inp, causal, 1.0 / math.sqrt(d), f"lengths {lens}")
+
+
+def test_grid_larger_than_longest(fa):
+    """max_seqlen above every length: the extra q-tiles exit at once."""
+    inp = ai.make_varlen_case([100, 333], 8, 2, 128, seed=7)
+    check(fa, inp, True, 0.0883883, "max_seqlen 2000", max_seqlen=2000)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_equal_lengths_match_fixed(fa, causal):
+    """B sequences of one length N give bit-identical results to flash_attn_fwd
+    on the [B, H, N, d] layout of the same data."""
+    import torch
+    B, Hq, Hkv, N, d = 3, 8, 2, 600, 128
+    inp = ai.make_varlen_case([N] * B, Hq, Hkv, d, seed=8 + int(causal))
+    say(f"varlen equal lengths vs fixed causal={causal}")
+    o_v, l_v = run_varlen(fa, inp, causal, 0.0883883)
+
+    def fixed(x, H):
+        return np.ascontiguousarray(x.reshape(H, B, N, d).transpose(1, 0, 2, 3))
+    q, k, v = to_dev(fixed(inp["q"], Hq)), to_dev(fixed(inp["k"], Hkv)), to_dev(fixed(inp["v"], Hkv))
+    o_f, l_f = fa.fwd(q, k, v, causal=causal, scale=0.0883883)
+    torch.cuda.synchronize()
+    o_f = from_dev_bf16(o_f).transpose(1, 0, 2, 3).reshape(Hq, B * N, d)
+    l_f = from_dev_f32(l_f).transpose(1, 0, 2).reshape(Hq, B * N)
+    assert np.array_equal(o_v, o_f) and np.array_equal(l_v, l_f)
+
+
+@pytest.mark.parametrize("name", sorted(ai.VARLEN_WORKLOADS))
+def test_workload_sampled(fa, name):
+    """The measured packed workload at full size; 64 seeded rows per sequence
+    (always the first and last) against the oracle."""
+    w = ai.VARLEN_WORKLOADS[name]
+    inp = ai.make_varlen_inputs(w)
+    check(fa, inp, w.causal, w.scale, name, rows_per_seq=64)
