@@ -50,10 +50,10 @@ class Oracle:
         lib = ctypes.CDLL(path)
         lib.oracle_attn_fwd.restype = ctypes.c_int
         lib.oracle_attn_fwd.argtypes = [_f64p, _f64p, _f64p, _f64p, _f64p] + [ctypes.c_int] * 6 + [
-            _i64p, ctypes.c_int, ctypes.c_double]
+            _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.oracle_attn_probs.restype = ctypes.c_int
         lib.oracle_attn_probs.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int] * 6 + [
-            _i64p, ctypes.c_int, ctypes.c_double]
+            _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.oracle_attn_bwd.restype = ctypes.c_int
         lib.oracle_attn_bwd.argtypes = [_f64p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_bwd_sampled.restype = ctypes.c_int
@@ -72,9 +72,10 @@ class Oracle:
             raise ValueError("q and k disagree on batch or head dim")
         return B, Hq, Hkv, Nq, Nk, d
 
-    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None):
+    def fwd(self, q, k, v, causal: bool, scale: float, qpos=None, window: int = 0):
         """O [B,Hq,Nq,d] and LSE [B,Hq,Nq]. ``qpos`` (int64 [Nq]) places query
-        rows among the keys for the causal mask (default: row i is position i)."""
+        rows among the keys for the causal mask (default: row i is position i);
+        ``window`` > 0 keeps only a causal row's `window` most recent positions."""
         q, k, v = _c64(q), _c64(k), _c64(v)
         B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
         o = np.empty_like(q)
@@ -86,12 +87,12 @@ class Oracle:
                 raise ValueError("qpos must have one entry per query row")
             qp = qpos.ctypes.data_as(_i64p)
         rc = self.lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
-                                      Nk, d, qp, int(bool(causal)), float(scale))
+                                      Nk, d, qp, int(bool(causal)), int(window), float(scale))
         if rc != 0:
             raise ValueError("oracle_attn_fwd rejected its arguments")
         return o, lse
 
-    def probs(self, q, k, causal: bool, scale: float, qpos=None):
+    def probs(self, q, k, causal: bool, scale: float, qpos=None, window: int = 0):
         """Full probability matrix P [B,Hq,Nq,Nk] (small sizes only)."""
         q, k = _c64(q), _c64(k)
         B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
@@ -101,7 +102,7 @@ class Oracle:
             qpos = np.ascontiguousarray(qpos, dtype=np.int64)
             qp = qpos.ctypes.data_as(_i64p)
         rc = self.lib.oracle_attn_probs(_ptr(q), _ptr(k), _ptr(p), B, Hq, Hkv, Nq, Nk, d, qp,
-                                        int(bool(causal)), float(scale))
+                                        int(bool(causal)), int(window), float(scale))
         if rc != 0:
             raise ValueError("oracle_attn_probs rejected its arguments")
         return p
@@ -170,8 +171,8 @@ def default() -> Oracle:
     return _default
 
 
-def fwd(q, k, v, causal, scale, qpos=None):
-    return default().fwd(q, k, v, causal, scale, qpos)
+def fwd(q, k, v, causal, scale, qpos=None, window=0):
+    return default().fwd(q, k, v, causal, scale, qpos, window)
 
 
 def bwd(q, k, v, do, causal, scale, o_bf16=False):
@@ -182,5 +183,5 @@ def bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16=False):
     return default().bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16)
 
 
-def probs(q, k, causal, scale, qpos=None):
-    return default().probs(q, k, causal, scale, qpos)
+def probs(q, k, causal, scale, qpos=None, window=0):
+    return default().probs(q, k, causal, scale, qpos, window)

@@ -22,7 +22,8 @@
  *   LSE      L_i = m_i + ln l_i  (natural log of sum_j exp(S_ij))
  *
  * Key j is visible to query i when the mask is off, or when j <= pos_i under
- * the causal mask. pos_i is the query's position among the keys (pos_i = i when
+ * the causal mask; a sliding window W > 0 (local attention) also hides keys
+ * j <= pos_i - W, leaving the W most recent positions. pos_i is the query's position among the keys (pos_i = i when
  * queries and keys are the same sequence). Query head h reads key/value head
  * h / (Hq / Hkv) (grouped-query attention, mlapandio "Two notes").
  *
@@ -89,8 +90,8 @@ static double round_bf16(double x) {
     return ldexp(nearbyint(ldexp(m, 8)), e - 8);
 }
 
-static int is_visible(int64_t pos_i, int j, int causal) {
-    return !causal || (int64_t)j <= pos_i;
+static int is_visible(int64_t pos_i, int j, int causal, int window) {
+    return !causal || ((int64_t)j <= pos_i && (window <= 0 || (int64_t)j > pos_i - window));
 }
 
 /*
@@ -99,12 +100,12 @@ static int is_visible(int64_t pos_i, int j, int causal) {
  * Returns the number of visible keys.
  */
 static int attend_row(const double* qi, const double* kh, const double* vh, int Nk, int d,
-                      int64_t pos_i, int causal, double s, double* S, double* P, double* oi,
-                      double* lse_i) {
+                      int64_t pos_i, int causal, int window, double s, double* S, double* P,
+                      double* oi, double* lse_i) {
     int visible = 0;
     double m = -INFINITY;
     for (int j = 0; j < Nk; ++j) {
-        if (is_visible(pos_i, j, causal)) {
+        if (is_visible(pos_i, j, causal, window)) {
             S[j] = s * dot(qi, kh + (size_t)j * d, d);
             if (S[j] > m) m = S[j];
             ++visible;
@@ -120,7 +121,7 @@ static int attend_row(const double* qi, const double* kh, const double* vh, int 
     }
     double l = 0.0;
     for (int j = 0; j < Nk; ++j) {
-        P[j] = is_visible(pos_i, j, causal) ? exp(S[j] - m) : 0.0;
+        P[j] = is_visible(pos_i, j, causal, window) ? exp(S[j] - m) : 0.0;
         l += P[j];
     }
     for (int j = 0; j < Nk; ++j) P[j] /= l;
@@ -142,11 +143,12 @@ static int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 /*
  * Forward. q [B,Hq,Nq,d], k,v [B,Hkv,Nk,d] -> o [B,Hq,Nq,d], lse [B,Hq,Nq].
  * qpos[Nq] gives each query row's position for the causal mask (NULL: row i
- * is position i).
+ * is position i); window > 0 limits a causal row to its `window` most recent
+ * positions (0: no limit).
  */
 int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
                     int B, int Hq, int Hkv, int Nq, int Nk, int d, const int64_t* qpos,
-                    int causal, double scale) {
+                    int causal, int window, double scale) {
     if (!q || !k || !v || !o || !lse || check_shape(B, Hq, Hkv, Nq, Nk, d)) return -1;
     const int G = Hq / Hkv;
     const int nt = max_threads();
@@ -163,7 +165,7 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o
         const double* vh = v + ((size_t)b * Hkv + hk) * (size_t)Nk * d;
         double* S = scratch + (size_t)thread_id() * 2 * Nk;
         double* P = S + Nk;
-        attend_row(q + (size_t)r * d, kh, vh, Nk, d, qpos ? qpos[i] : i, causal, scale, S, P,
+        attend_row(q + (size_t)r * d, kh, vh, Nk, d, qpos ? qpos[i] : i, causal, window, scale, S, P,
                    o + (size_t)r * d, lse + r);
     }
     free(scratch);
@@ -175,7 +177,7 @@ int oracle_attn_fwd(const double* q, const double* k, const double* v, double* o
  * p [B,Hq,Nq,Nk] = softmax rows (0 on masked keys).
  */
 int oracle_attn_probs(const double* q, const double* k, double* p, int B, int Hq, int Hkv, int Nq,
-                      int Nk, int d, const int64_t* qpos, int causal, double scale) {
+                      int Nk, int d, const int64_t* qpos, int causal, int window, double scale) {
     if (!q || !k || !p || check_shape(B, Hq, Hkv, Nq, Nk, d)) return -1;
     const int G = Hq / Hkv;
     double* S = (double*)malloc(sizeof(double) * (size_t)Nk);
@@ -188,7 +190,7 @@ int oracle_attn_probs(const double* q, const double* k, double* p, int B, int Hq
                 const size_t r = ((size_t)b * Hq + h) * Nq + i;
                 const double* kh = k + ((size_t)b * Hkv + h / G) * (size_t)Nk * d;
                 double lse;
-                attend_row(q + r * d, kh, zeros, Nk, d, qpos ? qpos[i] : i, causal, scale, S,
+                attend_row(q + r * d, kh, zeros, Nk, d, qpos ? qpos[i] : i, causal, window, scale, S,
                            p + r * Nk, o, &lse);
             }
     free(S); free(o); free(zeros);
@@ -207,14 +209,14 @@ static void bwd_row(const double* qi, const double* doi, const double* kh, const
                     int N, int d, int i, int causal, double scale, double* S, double* P,
                     double* oi, double* lse_i, double* D_i, double* dqi, const int* slot,
                     double* dk_acc, double* dv_acc, int o_bf16, double* ostore) {
-    attend_row(qi, kh, vh, N, d, i, causal, scale, S, P, oi, lse_i);
+    attend_row(qi, kh, vh, N, d, i, causal, 0, scale, S, P, oi, lse_i);
     for (int c = 0; c < d; ++c) ostore[c] = o_bf16 ? round_bf16(oi[c]) : oi[c];
     const double Di = dot(doi, ostore, d);
     *D_i = Di;
     if (dqi)
         for (int c = 0; c < d; ++c) dqi[c] = 0.0;
     for (int j = 0; j < N; ++j) {
-        if (!is_visible(i, j, causal)) continue;
+        if (!is_visible(i, j, causal, 0)) continue;
         const int sj = slot ? slot[j] : j;
         if (!dqi && sj < 0) continue;
         const double dPij = dot(doi, vh + (size_t)j * d, d);

@@ -489,6 +489,44 @@ def pin_split_merge(orc):
         _close(Om, o, what=f"merged O causal={causal}")
 
 
+def pin_sliding_window(orc):
+    """Local (sliding-window) causal attention: row i keeps keys i - W < j <= i.
+    (a) W >= every position is plain causal; (b) W = 1 leaves only the diagonal
+    key, so O_i = v_i and LSE_i = s q_i.k_i; (c) torch's fp64 SDPA with the band
+    mask written out, also for decode rows placed at the end of the keys; (d) the
+    probabilities vanish outside the band and sum to 1 inside it."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 4, 2, 23, 6
+    G = Hq // Hkv
+    q = _rand((B, Hq, N, d), 200)
+    k, v = _rand((B, Hkv, N, d), 201), _rand((B, Hkv, N, d), 202)
+    s = 0.55
+    oc, lc = orc.fwd(q, k, v, True, s)
+    ow, lw = orc.fwd(q, k, v, True, s, window=N)
+    _close(ow, oc, what="window N O")
+    _close(lw, lc, what="window N LSE")
+    o1, l1 = orc.fwd(q, k, v, True, s, window=1)
+    _close(o1, np.repeat(v, G, axis=1), what="window 1 O")
+    _close(l1, s * np.einsum("bhnd,bhnd->bhn", q, np.repeat(k, G, axis=1)), what="window 1 LSE")
+    for W, Nq in ((5, N), (5, 3), (9, 1)):
+        pos = N - Nq + np.arange(Nq, dtype=np.int64)
+        qq = q[:, :, N - Nq:]
+        o, lse = orc.fwd(qq, k, v, True, s, qpos=pos, window=W)
+        j = np.arange(N)[None, :]
+        band = (j <= pos[:, None]) & (j > pos[:, None] - W)
+        mask = torch.tensor(band)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(qq), torch.tensor(k).repeat_interleave(G, 1), torch.tensor(v).repeat_interleave(G, 1),
+            attn_mask=mask, scale=s)
+        _close(o, ref.numpy(), tol=1e-12, what=f"window {W} Nq {Nq} O vs SDPA")
+        sc = (torch.tensor(qq) @ torch.tensor(k).repeat_interleave(G, 1).transpose(-1, -2) * s).masked_fill(
+            ~mask, float("-inf"))
+        _close(lse, torch.logsumexp(sc, -1).numpy(), tol=1e-12, what=f"window {W} Nq {Nq} LSE")
+        P = orc.probs(qq, k, True, s, qpos=pos, window=W)
+        assert np.all(P[..., ~band] == 0.0), "probability outside the window"
+        _close(P.sum(-1), np.ones(P.shape[:-1]), what="window rows sum to 1")
+
+
 PINS = [
     pin_one_token,
     pin_two_tokens,
@@ -511,4 +549,5 @@ PINS = [
     pin_stored_o_mode,
     pin_decode_positions,
     pin_split_merge,
+    pin_sliding_window,
 ]

@@ -25,7 +25,9 @@ MUTANTS = {
     "LSE in log2": ("*lse_i = m + log(l);", "*lse_i = m + log2(l);"),
     "LSE drops max": ("*lse_i = m + log(l);", "*lse_i = log(l);"),
     "fwd GQA map modulo": ("const int hk = h / G;\n        const double* kh", "const int hk = h % Hkv;\n        const double* kh"),
-    "fwd row position ignored": ("qpos ? qpos[i] : i, causal, scale, S, P,", "qpos ? qpos[i] : 0, causal, scale, S, P,"),
+    "window keeps one key too many": ("(int64_t)j > pos_i - window", "(int64_t)j >= pos_i - window"),
+    "window ignored": ("(window <= 0 ||", "(1 ||"),
+    "fwd row position ignored": ("qpos ? qpos[i] : i, causal, window, scale, S, P,", "qpos ? qpos[i] : 0, causal, window, scale, S, P,"),
     "D uses dO.dO": ("const double Di = dot(doi, ostore, d);", "const double Di = dot(doi, doi, d);"),
     "D term dropped": ("const double dSij = P[j] * (dPij - Di);", "const double dSij = P[j] * dPij;"),
     "dS sign flipped": ("const double dSij = P[j] * (dPij - Di);", "const double dSij = P[j] * (Di - dPij);"),
