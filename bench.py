@@ -17,6 +17,10 @@ With --varlen NAME it measures the forward pass over packed sequences of
 different lengths (flash_attn_fwd_varlen) against the MFMA roofline, counting
 4*Hq*d FLOP per visible (query, key) pair of every sequence.
 
+With --window W it measures the forward pass of the same workload under a
+sliding-window causal mask of W keys (flash_attn_fwd_window), counting 4*d FLOP
+per visible pair: sum over rows of min(i + 1, W) pairs per head.
+
 With --decode NAME it measures instead the decode path (a few query rows over
 a long key/value cache) on one of the decode workloads, against the HBM
 roofline: the bytes the step must move (K and V once, Q, O and LSE) over the
@@ -256,6 +260,74 @@ def decode_main(args) -> int:
     return 0
 
 
+def window_main(args) -> int:
+    import torch
+    import exact_io_aware_60_amd as fa
+
+    fa.lib()
+    w = ai.WORKLOADS[WORKLOAD]
+    W = int(args.window)
+    inp = ai.make_inputs(w, with_grad=False)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, W,
+              w.scale, sp)
+
+    def call():
+        st = fa.fwd_window_raw(*args_c)
+        if st != 0:
+            raise RuntimeError(f"fwd_window: {fa.strerror(st)}")
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record(stream)
+        call()
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = [a.elapsed_time(b) for a, b in ev]
+    ms_avg = sum(times) / len(times)
+    n = np.arange(w.N, dtype=np.float64)
+    pairs = w.B * w.Hq * float(np.minimum(n + 1, W).sum())
+    flop = 4.0 * w.d * pairs
+    tflops = flop / (ms_avg * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd TFLOP/s with a sliding-window causal mask (bf16) and % of MI355X bf16 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_avg,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "window": W,
+                   "passes": "fwd (sliding window)"},
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "roofline": {"bound": "mfma", "kernel": "fwd_kernel (window)", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "avg_launch_ms": ms_avg, "algorithmic_flop_per_launch": flop},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def varlen_main(args) -> int:
     import torch
     import exact_io_aware_60_amd as fa
@@ -336,6 +408,8 @@ def main() -> int:
                          "profiled run holds the reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--decode", choices=sorted(ai.DECODE_WORKLOADS), default=None,
                     help="measure the decode path on this workload instead of the forward + backward step")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="measure the gqa16k forward under a sliding-window causal mask of W keys instead")
     ap.add_argument("--varlen", choices=sorted(ai.VARLEN_WORKLOADS), default=None,
                     help="measure the forward pass over this packed variable-length workload instead")
     args = ap.parse_args()
@@ -349,6 +423,12 @@ def main() -> int:
             print("bench.py needs a GPU", file=sys.stderr)
             return 2
         return decode_main(args)
+    if args.window > 0:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            return 2
+        return window_main(args)
     if args.varlen:
         import torch
         if not torch.cuda.is_available():

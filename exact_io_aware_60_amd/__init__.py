@@ -25,7 +25,8 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
             "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
-            "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen")
+            "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen",
+            "flash_attn_fwd_window")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_bwd_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_bwd_workspace_size.argtypes = [_i] * 6
+        L.flash_attn_fwd_window.restype = _i
+        L.flash_attn_fwd_window.argtypes = [_vp] * 5 + [_i] * 6 + [ctypes.c_float, _vp]
         L.flash_attn_fwd_varlen.restype = _i
         L.flash_attn_fwd_varlen.argtypes = [_vp] * 6 + [_i] * 7 + [ctypes.c_float, _vp]
         L.flash_attn_decode.restype = _i
@@ -104,6 +107,11 @@ def bwd_stage_raw(stage: int, q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d,
 
 def bwd_workspace_size(B, Hq, Hkv, N, d, causal) -> int:
     return int(lib().flash_attn_bwd_workspace_size(B, Hq, Hkv, N, d, int(causal)))
+
+
+def fwd_window_raw(q, k, v, o, lse, B, Hq, Hkv, N, d, window, scale, stream=None) -> int:
+    """flash_attn_fwd_window on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_fwd_window(q, k, v, o, lse, B, Hq, Hkv, N, d, int(window), float(scale), stream)
 
 
 def fwd_varlen_raw(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total, Hq, Hkv, d, causal, scale,
@@ -164,6 +172,23 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check(fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
                    causal, scale, _stream(q)))
+    return o, lse
+
+
+def fwd_window(q, k, v, window: int, scale: float | None = None, out=None, lse=None):
+    """Forward pass with a sliding-window causal mask (row i sees keys i - window < j <= i).
+    Returns (o bf16 [B,Hq,N,d], lse fp32 [B,Hq,N])."""
+    import torch
+    B, Hq, Hkv, N, d = _dims(q, k)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _checked(t, name)
+    if v.shape != k.shape:
+        raise ValueError("v must be shaped like k")
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(fwd_window_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                          window, scale, _stream(q)))
     return o, lse
 
 

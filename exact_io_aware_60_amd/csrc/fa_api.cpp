@@ -85,6 +85,33 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
     p.cu_seqlens = nullptr;
     p.total = 0;
+    p.window = 0;
+    return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                          int Hkv, int N, int d, int window, float scale, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    int st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    if (window < 1) return FA_ERR_SHAPE;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_ALIGN;
+    log_config("fwd_window", B, Hq, Hkv, N, d, 1);
+    fa::FwdParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d; p.G = Hq / Hkv;
+    p.causal = 1;
+    p.scale = scale;
+    p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    p.cu_seqlens = nullptr;
+    p.total = 0;
+    p.window = window;
     return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
 }
 
@@ -112,6 +139,7 @@ int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
     p.cu_seqlens = cu_seqlens;
     p.total = total;
+    p.window = 0;
     return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -124,12 +124,16 @@ __device__ __forceinline__ f32x16 scores(const FA_LDS uint8_t* __restrict__ Kt, 
 }
 
 // Diagonal or ragged chunk: scores (or x values) of invisible keys become -inf,
-// so their probabilities are exact zeros.
-__device__ __forceinline__ void mask_scores(f32x16& s, int key0, int qrow, int N, bool causal, int hh) {
+// so their probabilities are exact zeros. With a sliding window (WIN) the keys
+// at or before qrow - win are invisible too.
+template <bool WIN = false>
+__device__ __forceinline__ void mask_scores(f32x16& s, int key0, int qrow, int N, bool causal, int hh,
+                                            int win = 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int key = key0 + (i >> 2) * 8 + hh * 4 + (i & 3);
-        if (key >= N || (causal && key > qrow)) s[i] = -INFINITY;
+        // (rows past N, never stored, keep all keys below N so their max stays finite)
+        if (key >= N || (causal && key > qrow) || (WIN && qrow < N && key <= qrow - win)) s[i] = -INFINITY;
     }
 }
 
@@ -317,23 +321,59 @@ struct FwdState {
     float m, l;                // reference (log2 units), this lane's share of the row sum
 };
 
+// Sliding window: where a wave's keys start. A wave skips the chunks before
+// its first one (firstc) and, at that chunk, takes as its reference the exact
+// max over it and the next chunk: together they hold a visible key for every
+// row of the wave (the first row's window starts in chunk firstc, so the last
+// row's starts at most 31 keys later, and the diagonal chunk has each row's own
+// key), while one chunk alone may hold none for some rows.
+struct Window {
+    int firstc;   // first chunk with a visible key for some row of the wave
+    int win;      // window size
+    int r0;       // the wave's first row
+};
+
 // Chunk c = 2j + H. sc holds its scores; the next chunk's go to sn.
-// Kn: the K tile holding the next chunk; Kr1: K tile j+1, which holds chunk
-// c+2 (half H); Vt: this chunk's V tile. cp carries the iteration's copies
-// (first chunk only).
-template <int D, int H, bool CP>
+// Kc: the K tile holding this chunk; Kn: the K tile holding the next chunk;
+// Kr1: K tile j+1, which holds chunk c+2 (half H); Vt: this chunk's V tile.
+// cp carries the iteration's copies (first chunk only).
+template <int D, int H, bool CP, bool WIN>
 __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f32x16& sn,
+                                          const FA_LDS uint8_t* __restrict__ Kc,
                                           const FA_LDS uint8_t* __restrict__ Kn,
                                           const FA_LDS uint8_t* __restrict__ Kr1,
                                           const FA_LDS uint8_t* __restrict__ Vt, int kbase, int vbase,
                                           bool causal, int qrow, int N, int lastc, float sl2, int hh,
-                                          const FwdCopies<D, CP>& cp) {
+                                          const FwdCopies<D, CP>& cp, const Window& wd) {
     if (c > lastc) {
         cp.bulk();
         return;
     }
+    if constexpr (WIN) {
+        if (c < wd.firstc) {
+            cp.bulk();
+            return;
+        }
+        if (c == wd.firstc) {
+            sc = scores<D>(Kc, kbase, H, st.qf);
+            mask_scores<true>(sc, c * 32, qrow, N, true, hh, wd.win);
+            float mx = chunk_max(sc, sl2);
+            if (c < lastc) {
+                f32x16 s1 = scores<D>(Kn, kbase, H ^ 1, st.qf);
+                mask_scores<true>(s1, c * 32 + 32, qrow, N, true, hh, wd.win);
+                mx = fmaxf(mx, chunk_max(s1, sl2));
+                st.ka[0] = k_frag<D>(Kn, kbase, H ^ 1, 0);
+                st.ka[1] = k_frag<D>(Kn, kbase, H ^ 1, 1);
+            }
+            st.m = mx;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[i] = fmaf(sc[i], sl2, -st.m);
+        }
+    }
     if ((causal && c * 32 + 31 > qrow - (qrow & 31)) || (c * 32 + 32 > N))
-        mask_scores(sc, c * 32, qrow, N, causal, hh);
+        mask_scores<WIN>(sc, c * 32, qrow, N, causal, hh, wd.win);
+    else if (WIN && c * 32 < wd.r0 + 32 - wd.win)
+        mask_scores<true>(sc, c * 32, qrow, N, causal, hh, wd.win);
     if (c < lastc) {
         pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Kr1, H, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, sl2, st.o,
                               st.ka, cp);
@@ -349,7 +389,7 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
 // __restrict__ qualifiers say so, which lets the compiler see that the LDS
 // reads do not touch the LDS the in-flight global->LDS copies write, so it does
 // not wait for those copies before each read.
-template <int D>
+template <int D, bool WIN>
 __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, const typename FwdCfg<D>::PlanK& pk,
                                               const typename FwdCfg<D>::PlanV& pv, BufRes rk, BufRes rv,
                                               FA_LDS uint8_t* __restrict__ Kw,
@@ -358,7 +398,7 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, co
                                               const FA_LDS uint8_t* __restrict__ Kr1,
                                               const FA_LDS uint8_t* __restrict__ Vr, int kbase, int vbase,
                                               bool valid, bool causal, int qrow, int N, int lastc,
-                                              float sl2, int w, int lane) {
+                                              float sl2, int w, int lane, const Window& wd) {
     // Tiles j + 1 and j + 2 may lie past the last one: their copies then read
     // past the resource (zeros) into buffers no chunk reads any more (those of
     // tiles j - 1 and j - 2).
@@ -366,10 +406,10 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, co
                                 (uint32_t)(j + 1) * kBN * D * 2, Kw, Vw, w};
     if (valid) {
         const int hh = lane >> 5;
-        fwd_chunk<D, 0>(st, 2 * j, st.sA, st.sB, Kr0, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh,
-                        cp);
-        fwd_chunk<D, 1>(st, 2 * j + 1, st.sB, st.sA, Kr1, Kr1, Vr, kbase, vbase, causal, qrow, N, lastc, sl2, hh,
-                        FwdCopies<D, false>{});
+        fwd_chunk<D, 0, true, WIN>(st, 2 * j, st.sA, st.sB, Kr0, Kr0, Kr1, Vr, kbase, vbase, causal, qrow, N,
+                                   lastc, sl2, hh, cp, wd);
+        fwd_chunk<D, 1, false, WIN>(st, 2 * j + 1, st.sB, st.sA, Kr0, Kr1, Kr1, Vr, kbase, vbase, causal, qrow, N,
+                                    lastc, sl2, hh, FwdCopies<D, false>{}, wd);
     } else {
         cp.bulk();
     }
@@ -378,7 +418,7 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, co
 // The causal flag is a run-time argument: it only changes the tile ranges and
 // the mask of each wave's last chunk, so one instance per head dimension
 // serves both cases.
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     using C = FwdCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
@@ -427,6 +467,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const int qrow = r0 + l32;                   // this lane's query row
     const int ntk = (N + kBN - 1) / kBN;
     const int nt = causal ? min(ntk, (q0 + kBM - 1) / kBN + 1) : ntk;
+    // sliding window: the workgroup's first tile, and this wave's first chunk
+    const int win = WIN ? p.window : 0;
+    const int js = WIN ? max(0, q0 - win + 1) / kBN : 0;
+    const Window wd{WIN ? max(0, r0 - win + 1) / 32 : 0, win, r0};
     const bool wave_valid = r0 < N;
     // last 32-key chunk this wave computes (causal: the diagonal chunk, keys r0 .. r0+31)
     const int nck = (N + 31) / 32;
@@ -454,14 +498,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     pk.init(w, lane, D);
     pv.init(w, lane, D);
 
-    // K tiles 0, 1 and V tile 0 before the loop.
-    pk.copy(rk, 0, Ks, w);
-    if (nt > 1) pk.copy(rk, kBN * D * 2, Ks + C::KT, w);
-    pv.copy(rv, 0, Vs, w);
+    // K tiles js, js+1 and V tile js before the loop (js = 0 without a window),
+    // in the buffers the loop's index arithmetic expects for them.
+    pk.copy(rk, (uint32_t)js * kBN * D * 2, Ks + (js % 3) * C::KT, w);
+    if (nt > js + 1) pk.copy(rk, (uint32_t)(js + 1) * kBN * D * 2, Ks + ((js + 1) % 3) * C::KT, w);
+    pv.copy(rv, (uint32_t)js * kBN * D * 2, Vs + (js & 1) * C::VT, w);
     wait_vmem();
     __syncthreads();
 
-    if (wave_valid) {
+    if (!WIN && wave_valid) {
         // The first reference is chunk 0's exact (masked) max, so every row has
         // l >= 1 from then on; chunk 0 then holds x.
         st.sA = scores<D>(Ks, kbase, 0, st.qf);
@@ -472,10 +517,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) st.sA[i] = fmaf(st.sA[i], sl2, -st.m);
     }
-    for (int j = 0; j < nt; ++j) {
-        fwd_iteration<D>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT, Vs + ((j + 1) & 1) * C::VT,
-                         Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT, Vs + (j & 1) * C::VT, kbase,
-                         vbase, wave_valid, causal, qrow, N, lastc, sl2, w, lane);
+    for (int j = js; j < nt; ++j) {
+        fwd_iteration<D, WIN>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT, Vs + ((j + 1) & 1) * C::VT,
+                              Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT, Vs + (j & 1) * C::VT, kbase,
+                              vbase, wave_valid, causal, qrow, N, lastc, sl2, w, lane, wd);
         wait_vmem();
         __syncthreads();
     }
@@ -501,7 +546,10 @@ template <int D>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     const int nqt = (p.N + kBM - 1) / kBM;
     const int grid = p.B * p.Hq * nqt;
-    hipLaunchKernelGGL((fwd_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (p.window > 0)
+        hipLaunchKernelGGL((fwd_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fwd_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

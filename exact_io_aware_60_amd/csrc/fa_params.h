@@ -22,6 +22,9 @@ struct FwdParams {
     // and N is the longest sequence (it sizes the grid).
     const int* cu_seqlens;
     int total;
+    // Sliding window (local attention, with the causal mask): row i keeps keys
+    // i - window < j <= i. 0: no window.
+    int window;
 };
 
 struct BwdParams {

@@ -78,6 +78,19 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
+ * Forward pass with a sliding-window (local) causal mask: query row i sees keys
+ * i - window < j <= i, its `window` most recent positions. Arguments, layout
+ * and outputs as in flash_attn_fwd (causal is implied); window >= 1, and
+ * window >= N gives the plain causal result. The mlapandio page
+ * "FlashAttention: IO-aware exact attention" ("Honest limits") notes that such
+ * masks need implementations of their own: here the causal tile skip is
+ * extended to the band, so keys before a q-tile's window are never read.
+ */
+int flash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int N, int d, int window, float scale,
+                          void* stream);
+
+/*
  * Forward pass over packed sequences of different lengths (one launch for a
  * batch of prompts, no padding). Same computation as flash_attn_fwd for each
  * sequence on its own; the sequences share heads and nothing else.

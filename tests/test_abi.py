@@ -221,3 +221,18 @@ def test_varlen_checks():
     assert varlen_call(scale=float("nan")) == fa.FA_ERR_SCALE
     assert varlen_call(cu=P[5] + 2) == fa.FA_ERR_ALIGN
     assert varlen_call(o=P[3] + 8) == fa.FA_ERR_ALIGN
+
+
+def test_window_checks():
+    def call(**over):
+        a = dict(q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, Hq=4, Hkv=2, N=128, d=128, W=64, scale=0.088)
+        a.update(over)
+        return fa.fwd_window_raw(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["N"],
+                                 a["d"], a["W"], a["scale"])
+    assert call(q=None) == fa.FA_ERR_NULL
+    assert call(W=0) == fa.FA_ERR_SHAPE
+    assert call(W=-4) == fa.FA_ERR_SHAPE
+    assert call(Hq=3) == fa.FA_ERR_SHAPE
+    assert call(d=32) == fa.FA_ERR_HEADDIM
+    assert call(scale=-1.0) == fa.FA_ERR_SCALE
+    assert call(lse=P[4] + 4) == fa.FA_ERR_ALIGN
