@@ -60,9 +60,9 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_fwd_varlen.restype = _i
         L.flash_attn_fwd_varlen.argtypes = [_vp] * 6 + [_i] * 7 + [ctypes.c_float, _vp]
         L.flash_attn_decode.restype = _i
-        L.flash_attn_decode.argtypes = [_vp] * 6 + [_i] * 7 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.flash_attn_decode.argtypes = [_vp] * 6 + [_i] * 8 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_decode_workspace_size.restype = ctypes.c_size_t
-        L.flash_attn_decode_workspace_size.argtypes = [_i] * 7
+        L.flash_attn_decode_workspace_size.argtypes = [_i] * 8
         L.flash_attn_strerror.restype = ctypes.c_char_p
         L.flash_attn_strerror.argtypes = [_i]
         L.flash_attn_version.restype = ctypes.c_char_p
@@ -122,14 +122,14 @@ def fwd_varlen_raw(q, k, v, o, lse, cu_seqlens, B, max_seqlen, total, Hq, Hkv, d
 
 
 def decode_raw(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
-               stream=None) -> int:
+               stream=None, window: int = 0) -> int:
     """flash_attn_decode on raw addresses (ints; seqlens_k may be None); returns the status code."""
-    return lib().flash_attn_decode(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale),
-                                   workspace, workspace_bytes, stream)
+    return lib().flash_attn_decode(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, int(causal), int(window),
+                                   float(scale), workspace, workspace_bytes, stream)
 
 
-def decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal) -> int:
-    return int(lib().flash_attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(causal)))
+def decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window: int = 0) -> int:
+    return int(lib().flash_attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(causal), int(window)))
 
 
 # ------------------------------------------------------------------ torch front end
@@ -212,13 +212,13 @@ def bwd(q, k, v, o, lse, do, causal: bool = True, scale: float | None = None, wo
 
 
 def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=None, out=None, lse=None,
-           seqlens_k=None):
+           seqlens_k=None, window: int = 0):
     """Attention of the newest Nq query rows over a cache of Nk keys.
 
     q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d] bf16. seqlens_k: optional int32
     device tensor [B], the cache rows in use per batch entry (default: all
-    Nk). Causal: row i is token L_b - Nq + i. Returns (o bf16 [B,Hq,Nq,d],
-    lse fp32 [B,Hq,Nq])."""
+    Nk). Causal: row i is token L_b - Nq + i; window > 0 keeps its `window`
+    most recent keys. Returns (o bf16 [B,Hq,Nq,d], lse fp32 [B,Hq,Nq])."""
     import torch
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
@@ -237,13 +237,13 @@ def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=N
     scale = default_scale(d) if scale is None else scale
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    ws_bytes = decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal)
+    ws_bytes = decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sl_ptr, B, Hq, Hkv,
-                      Nq, Nk, d, causal, scale, ws_ptr, ws_len, _stream(q)))
+                      Nq, Nk, d, causal, scale, ws_ptr, ws_len, _stream(q), window))
     return o, lse
 
 

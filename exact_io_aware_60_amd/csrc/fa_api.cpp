@@ -264,22 +264,25 @@ int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
 
 }  // namespace
 
-size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                                        int window) {
     if (check_decode_shape(B, Hq, Hkv, Nq, Nk, d, causal) != FA_OK) return 0;
-    return fa::dec_plan(B, Hq, Hkv, Nq, Nk, d).total;
+    if (window < 0 || (window > 0 && !causal)) return 0;
+    return fa::dec_plan(B, Hq, Hkv, Nq, Nk, d, window).total;
 }
 
 int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                       const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
-                      float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                      int window, float scale, void* workspace, size_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     int st = check_decode_shape(B, Hq, Hkv, Nq, Nk, d, causal);
     if (st != FA_OK) return st;
+    if (window < 0 || (window > 0 && !causal)) return FA_ERR_SHAPE;
     if ((st = check_scale(scale)) != FA_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
         (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0)
         return FA_ERR_ALIGN;
-    const fa::DecPlan pl = fa::dec_plan(B, Hq, Hkv, Nq, Nk, d);
+    const fa::DecPlan pl = fa::dec_plan(B, Hq, Hkv, Nq, Nk, d, window);
     if (pl.total > 0) {
         if (!workspace || workspace_bytes < pl.total) return FA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return FA_ERR_ALIGN;
@@ -294,6 +297,7 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
     p.part_lse = pl.total ? reinterpret_cast<float*>(ws + pl.part_lse) : nullptr;
     p.part_o = pl.total ? reinterpret_cast<float*>(ws + pl.part_o) : nullptr;
     p.seqlens_k = seqlens_k;
+    p.window = window;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.d = d; p.G = Hq / Hkv; p.M = pl.M;
     p.causal = causal ? 1 : 0;
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);

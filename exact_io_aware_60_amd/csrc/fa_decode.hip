@@ -34,6 +34,9 @@
 //    memory time, so the forward's rarer reference moves buy nothing here.
 #include <math.h>
 
+#include <algorithm>
+#include <climits>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -117,11 +120,12 @@ __device__ __forceinline__ u32x4 dec_v_frag(const FA_LDS uint8_t* Vc, int vbase)
 
 // One 32-key chunk starting at key0: scores, mask, online softmax, P.V.
 // pos: the lane's row position (keys > pos are invisible); Nk: keys past it
-// are invisible; mask: whether any key of the chunk can be invisible.
+// are invisible; lo: keys <= lo are invisible (a sliding window; INT_MIN
+// without one); mask: whether any key of the chunk can be invisible.
 template <int D>
 __device__ __forceinline__ void dec_chunk(DecWave<D>& st, const FA_LDS uint8_t* __restrict__ Kc,
                                           const FA_LDS uint8_t* __restrict__ Vc, int kbase, int vbase,
-                                          int key0, int Nk, int pos, bool mask, float sl2, int hh) {
+                                          int key0, int Nk, int pos, int lo, bool mask, float sl2, int hh) {
     constexpr int DS = D / 16, DB = D / 32;
     // All fragment reads go out first: the K reads feed the score MFMAs, the
     // V^T reads land while the softmax runs.
@@ -141,7 +145,7 @@ __device__ __forceinline__ void dec_chunk(DecWave<D>& st, const FA_LDS uint8_t* 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = key0 + (i >> 2) * 8 + hh * 4 + (i & 3);
-            if (key >= Nk || key > pos) s[i] = -INFINITY;
+            if (key >= Nk || key > pos || key <= lo) s[i] = -INFINITY;
         }
     }
     float mx = s[0];
@@ -193,8 +197,8 @@ __device__ __forceinline__ void dec_iteration(DecWave<D>& st, const typename Dec
                                               const typename DecCfg<D>::PlanV& pv, BufRes rk, BufRes rv,
                                               bool copy_next, uint32_t noff, FA_LDS uint8_t* __restrict__ W,
                                               const FA_LDS uint8_t* __restrict__ R, int w, bool active,
-                                              int h0, int h1, int key0, int Nk, int pos, int mfrom, float sl2,
-                                              int kbase, int vbase, int hh) {
+                                              int h0, int h1, int key0, int Nk, int pos, int lo, int mfrom,
+                                              int mto, float sl2, int kbase, int vbase, int hh) {
     using C = DecCfg<D>;
     if (copy_next) {
         pk.copy(rk, noff, W, w);
@@ -204,8 +208,8 @@ __device__ __forceinline__ void dec_iteration(DecWave<D>& st, const typename Dec
     for (int h = h0; h < h1; ++h) {
         const int kc = key0 + 32 * h;
         if (kc >= Nk) break;
-        dec_chunk<D>(st, R + h * 32 * C::L, R + C::KT + h * 32 * C::L, kbase, vbase, kc, Nk, pos,
-                     kc + 32 > mfrom, sl2, hh);
+        dec_chunk<D>(st, R + h * 32 * C::L, R + C::KT + h * 32 * C::L, kbase, vbase, kc, Nk, pos, lo,
+                     kc + 32 > mfrom || kc <= mto, sl2, hh);
     }
 }
 
@@ -246,13 +250,19 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     // causal: row r is token L - Nq + (r % Nq); keys after it are invisible
     // (a negative position: the row sees no key)
     const int pos = (p.causal && row_ok) ? L - p.Nq + r % p.Nq : 0x7fffffff;
-    // chunks ending after mfrom may hold invisible keys
+    // sliding window: keys at or before lo are invisible to this row
+    const int lo = (p.window > 0 && row_ok) ? pos - p.window : INT_MIN;
+    // chunks ending after mfrom, or starting at or before mto, may hold
+    // invisible keys (mto: the last row's window start - 1)
     const int mfrom = p.causal ? L - p.Nq + 1 : L;
+    const int mto = p.window > 0 ? L - 1 - p.window : INT_MIN;
 
     // this range's tiles that hold keys in use (none: the range reports an
-    // empty result)
+    // empty result). With a window the ranges start at the tile of the first
+    // row's first visible key, so earlier tiles are never read.
     const int ntile = (L + kDBN - 1) / kDBN;
-    const int t0 = split * p.tps;
+    const int tf = p.window > 0 ? max(0, L - p.Nq - p.window + 1) / kDBN : 0;
+    const int t0 = tf + split * p.tps;
     const int nt = min(p.tps, ntile - t0);
 
     const float sl2 = p.scale_log2;
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
         const int jn = j + NS - 1;
         dec_iteration<D>(st, pk, pv, rk, rv, jn < nt, (uint32_t)(t0 + jn) * kTileBytes,
                          ring + (jn % NS) * C::STAGE, ring + (j % NS) * C::STAGE, w, active, h0, h1,
-                         (t0 + j) * kDBN, L, pos, mfrom, sl2, kbase, vbase, hh);
+                         (t0 + j) * kDBN, L, pos, lo, mfrom, mto, sl2, kbase, vbase, hh);
     }
     }
 
@@ -455,13 +465,16 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-DecPlan dec_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+DecPlan dec_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int window) {
     DecPlan pl{};
     const int G = Hq / Hkv;
     pl.M = G * Nq;
     pl.nrb = (pl.M + kDRows - 1) / kDRows;
     pl.pair = pl.M <= 64 ? 1 : 0;
-    const long long ntile = (Nk + kDBN - 1) / kDBN;
+    // tiles a row group can need: all of them, or with a window the tiles
+    // from the first row's first visible key to the end of the cache
+    long long ntile = (Nk + kDBN - 1) / kDBN;
+    if (window > 0) ntile = std::min(ntile, ((long long)Nq + window - 1 + kDBN - 1) / kDBN + 1);
     const long long base = (long long)B * Hkv * pl.nrb;
     long long tps = (ntile * base + kDTarget - 1) / kDTarget;
     tps = tps < 1 ? 1 : (tps > ntile ? ntile : tps);

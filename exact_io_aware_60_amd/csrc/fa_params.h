@@ -75,6 +75,7 @@ struct DecParams {
     float* part_lse;     // fp32 [groups][nsplit][M]: log2 of the range's sum of exp2 (-inf: no key seen)
     float* part_o;       // fp32 [groups][nsplit][M][d]: the range's normalised output (0: no key seen)
     const int* seqlens_k;  // int32 [B] keys in use per batch entry (clamped to [0, Nk]), or null: all Nk
+    int window;            // causal sliding window: row at position p sees keys p - window < j <= p (0: none)
     int B, Hq, Hkv, Nq, Nk, d, G, M;
     int causal;
     float scale_log2;
@@ -91,7 +92,7 @@ struct DecPlan {
     int M, nrb, nsplit, tps, pair;
     size_t part_lse, part_o, total;
 };
-DecPlan dec_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+DecPlan dec_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int window);
 
 constexpr int kRowPad = 128;   // row padding unit of the backward workspace
 

@@ -198,8 +198,11 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
  * causal: query row i is token L_b - Nq + i of the sequence the keys belong to
  * (the queries are its last Nq tokens) and sees keys j <= L_b - Nq + i.
  * causal = 0: every row sees all L_b keys. With Nq = Nk = L_b and causal = 1
- * the result is that of flash_attn_fwd. A row that sees no key at all (L_b =
- * 0, or L_b - Nq + i < 0) gets O = 0 and LSE = -inf.
+ * the result is that of flash_attn_fwd. window > 0 (causal only) adds a
+ * sliding window: row i also loses keys j <= L_b - Nq + i - window (as in
+ * flash_attn_fwd_window), and only the cache tiles the window covers are
+ * read. window = 0: no window. A row that sees no key at all (L_b = 0, or
+ * L_b - Nq + i < 0) gets O = 0 and LSE = -inf.
  * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {64, 128}; Nq <= Nk
  * when causal; Nk * d * 2 < 2^31 bytes per K/V head. Any Nq is accepted; the path is made
  * for (Hq / Hkv) * Nq <= 128 query rows per K/V head, and larger counts read
@@ -213,18 +216,20 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
  */
 int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                       const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                      int causal, float scale, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      int causal, int window, float scale, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace flash_attn_decode needs for these arguments, or 0
- * when it needs none or rejects the shape. It depends on the cache capacity
- * Nk, not on seqlens_k. The workspace holds, for every
+ * when it needs none or rejects the shape (including window < 0, or a window
+ * without the causal mask). It depends on the cache capacity Nk and the
+ * window, not on seqlens_k. The workspace holds, for every
  * key range of every K/V head and every query row, one fp32 logsumexp and d
  * fp32 output values: about R * B * Hq * Nq * (d + 1) * 4 bytes for R ranges
  * per head (R is chosen from the shape so that the grid fills the GPU).
  */
-size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal);
+size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                                        int window);
 
 /* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
  * error string of the calling thread's last failed launch. Never NULL. */

@@ -172,6 +172,14 @@ def test_decode_checks():
     assert dec_call(ws=None) == fa.FA_ERR_WORKSPACE
     assert dec_call(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
     assert dec_call(ws=P[9] + 4, ws_bytes=need) == fa.FA_ERR_ALIGN
+    assert fa.decode_raw(P[0], P[1], P[2], P[3], P[4], None, 2, 32, 8, 1, 16384, 128, 1, 0.088, P[9], 1 << 30,
+                         window=-1) == fa.FA_ERR_SHAPE
+    assert fa.decode_raw(P[0], P[1], P[2], P[3], P[4], None, 2, 32, 8, 1, 16384, 128, 0, 0.088, P[9], 1 << 30,
+                         window=64) == fa.FA_ERR_SHAPE
+    assert fa.decode_workspace_size(2, 32, 8, 1, 16384, 128, 0, 64) == 0
+    # a window shrinks the ranges to the tiles it covers
+    assert 0 < fa.decode_workspace_size(1, 8, 8, 1, 131072, 128, 1, 4096) < fa.decode_workspace_size(
+        1, 8, 8, 1, 131072, 128, 1)
     # more query rows than keys is only an error under the causal mask
     assert fa.decode_workspace_size(1, 4, 2, 9, 8, 64, 1) == 0
     assert fa.decode_workspace_size(1, 4, 2, 9, 8, 64, 0) == 0

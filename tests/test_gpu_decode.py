@@ -230,3 +230,53 @@ def test_workload(fa, name):
         check(fa, inp, w.causal, w.scale, name)
     else:
         check_ragged(fa, inp, w.causal, w.scale, lens, name)
+
+
+def check_window(fa, inp, W, scale, tag, seqlens=None):
+    import torch
+    B, Hq, Nq, d = inp["q"].shape
+    Nk = inp["k"].shape[2]
+    say(f"decode window {tag}: B={B} Hq={Hq} Nq={Nq} Nk={Nk} d={d} W={W} seqlens={seqlens}")
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    sl = None if seqlens is None else torch.as_tensor(np.asarray(seqlens, np.int32)).cuda()
+    o, lse = fa.decode(q, k, v, causal=True, scale=scale, seqlens_k=sl, window=W)
+    torch.cuda.synchronize()
+    o, lse = from_dev_bf16(o), from_dev_f32(lse)
+    lens = [Nk] * B if seqlens is None else [int(min(max(x, 0), Nk)) for x in seqlens]
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+            continue
+        pos = L - Nq + np.arange(Nq, dtype=np.int64)
+        ro, rl = oracle.fwd(f64(inp["q"][b:b + 1]), f64(inp["k"][b:b + 1, :, :L]), f64(inp["v"][b:b + 1, :, :L]),
+                            True, scale, qpos=pos, window=W)
+        empty = np.isneginf(rl)
+        assert np.array_equal(np.isneginf(lse[b:b + 1]), empty)
+        eo = excess_err(o[b:b + 1], ro)
+        el = max_err(lse[b:b + 1][~empty], rl[~empty]) if (~empty).any() else 0.0
+        assert eo <= TOL_O and el <= TOL_LSE, f"{tag} b={b}: O err {eo:.2e}, LSE err {el:.2e}"
+
+
+@pytest.mark.parametrize("W", [1, 63, 64, 65, 100, 1000, 4999, 6000])
+def test_window(fa, W):
+    """Sliding window over a 5000-key cache: the window's first key falls in
+    the middle of a tile, on a tile edge, or before the cache (W >= Nk)."""
+    inp = ai.make_decode_case(2, 8, 2, 1, 5000, 128, seed=110 + W)
+    check_window(fa, inp, W, 0.0883883, "W")
+
+
+def test_window_short_queries_ragged(fa):
+    """Nq = 4 rows with a 37-key window over ragged caches (lengths 0, 3, 500,
+    3000), d = 64: rows whose window starts before the cache, inside it, and
+    entries with no key."""
+    inp = ai.make_decode_case(4, 8, 2, 4, 3000, 64, seed=120)
+    check_window(fa, inp, 37, 0.125, "ragged", seqlens=[0, 3, 500, 3000])
+
+
+def test_window_many_ranges(fa):
+    """Few groups and a 4096-key window over a 60000-key cache: the ranges cover
+    only the window's tiles."""
+    inp = ai.make_decode_case(1, 4, 1, 2, 60000, 128, seed=121)
+    assert fa.decode_workspace_size(1, 4, 1, 2, 60000, 128, 1, 4096) < fa.decode_workspace_size(1, 4, 1, 2, 60000,
+                                                                                                 128, 1)
+    check_window(fa, inp, 4096, 0.0883883, "many ranges")
