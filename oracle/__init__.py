@@ -55,10 +55,10 @@ class Oracle:
         lib.oracle_attn_probs.argtypes = [_f64p, _f64p, _f64p] + [ctypes.c_int] * 6 + [
             _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_double]
         lib.oracle_attn_bwd.restype = ctypes.c_int
-        lib.oracle_attn_bwd.argtypes = [_f64p] * 10 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
+        lib.oracle_attn_bwd.argtypes = [_f64p] * 10 + [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int]
         lib.oracle_attn_bwd_sampled.restype = ctypes.c_int
         lib.oracle_attn_bwd_sampled.argtypes = [_f64p] * 4 + [_i64p, ctypes.c_int, _i64p, ctypes.c_int] + [
-            _f64p] * 3 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int]
+            _f64p] * 3 + [ctypes.c_int] * 7 + [ctypes.c_double, ctypes.c_int]
         lib.oracle_round_bf16.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [_f64p, _f64p, ctypes.c_int64]
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -107,11 +107,12 @@ class Oracle:
             raise ValueError("oracle_attn_probs rejected its arguments")
         return p
 
-    def bwd(self, q, k, v, do, causal: bool, scale: float, o_bf16: bool = False):
+    def bwd(self, q, k, v, do, causal: bool, scale: float, o_bf16: bool = False, window: int = 0):
         """Gradients of sum(do * O): returns dict dq, dk, dv, o, lse, D.
 
         ``o_bf16``: form D = rowsum(do * O) from O rounded to bfloat16, the
-        format the forward stores O in; every other quantity stays exact."""
+        format the forward stores O in; every other quantity stays exact.
+        ``window``: sliding-window causal mask, as in ``fwd``."""
         q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
         B, Hq, Hkv, Nq, Nk, d = self._dims(q, k)
         if Nq != Nk:
@@ -124,12 +125,13 @@ class Oracle:
         D = np.empty_like(lse)
         rc = self.lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dq), _ptr(dk),
                                       _ptr(dv), _ptr(o), _ptr(lse), _ptr(D), B, Hq, Hkv, Nq, d,
-                                      int(bool(causal)), float(scale), int(bool(o_bf16)))
+                                      int(bool(causal)), int(window), float(scale), int(bool(o_bf16)))
         if rc != 0:
             raise ValueError("oracle_attn_bwd rejected its arguments")
         return dict(dq=dq, dk=dk, dv=dv, o=o, lse=lse, D=D)
 
-    def bwd_sampled(self, q, k, v, do, causal: bool, scale: float, rows, keys, o_bf16: bool = False):
+    def bwd_sampled(self, q, k, v, do, causal: bool, scale: float, rows, keys, o_bf16: bool = False,
+                    window: int = 0):
         """dQ of the listed query rows [B,Hq,len(rows),d] and dK/dV of the listed
         keys [B,Hkv,len(keys),d]; every row still runs its full softmax."""
         q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
@@ -144,7 +146,7 @@ class Oracle:
         rc = self.lib.oracle_attn_bwd_sampled(_ptr(q), _ptr(k), _ptr(v), _ptr(do), rows.ctypes.data_as(_i64p),
                                               len(rows), keys.ctypes.data_as(_i64p), len(keys), _ptr(dq),
                                               _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, d, int(bool(causal)),
-                                              float(scale), int(bool(o_bf16)))
+                                              int(window), float(scale), int(bool(o_bf16)))
         if rc != 0:
             raise ValueError("oracle_attn_bwd_sampled rejected its arguments")
         return dict(dq=dq, dk=dk, dv=dv)
@@ -175,12 +177,12 @@ def fwd(q, k, v, causal, scale, qpos=None, window=0):
     return default().fwd(q, k, v, causal, scale, qpos, window)
 
 
-def bwd(q, k, v, do, causal, scale, o_bf16=False):
-    return default().bwd(q, k, v, do, causal, scale, o_bf16)
+def bwd(q, k, v, do, causal, scale, o_bf16=False, window=0):
+    return default().bwd(q, k, v, do, causal, scale, o_bf16, window)
 
 
-def bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16=False):
-    return default().bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16)
+def bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16=False, window=0):
+    return default().bwd_sampled(q, k, v, do, causal, scale, rows, keys, o_bf16, window)
 
 
 def probs(q, k, causal, scale, qpos=None, window=0):

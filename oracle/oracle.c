@@ -206,17 +206,17 @@ int oracle_attn_probs(const double* q, const double* k, double* p, int B, int Hq
  *   slot == NULL means slot j for every key, slot[j] < 0 skips key j.
  */
 static void bwd_row(const double* qi, const double* doi, const double* kh, const double* vh,
-                    int N, int d, int i, int causal, double scale, double* S, double* P,
+                    int N, int d, int i, int causal, int window, double scale, double* S, double* P,
                     double* oi, double* lse_i, double* D_i, double* dqi, const int* slot,
                     double* dk_acc, double* dv_acc, int o_bf16, double* ostore) {
-    attend_row(qi, kh, vh, N, d, i, causal, 0, scale, S, P, oi, lse_i);
+    attend_row(qi, kh, vh, N, d, i, causal, window, scale, S, P, oi, lse_i);
     for (int c = 0; c < d; ++c) ostore[c] = o_bf16 ? round_bf16(oi[c]) : oi[c];
     const double Di = dot(doi, ostore, d);
     *D_i = Di;
     if (dqi)
         for (int c = 0; c < d; ++c) dqi[c] = 0.0;
     for (int j = 0; j < N; ++j) {
-        if (!is_visible(i, j, causal, 0)) continue;
+        if (!is_visible(i, j, causal, window)) continue;
         const int sj = slot ? slot[j] : j;
         if (!dqi && sj < 0) continue;
         const double dPij = dot(doi, vh + (size_t)j * d, d);
@@ -251,7 +251,7 @@ static void bwd_row(const double* qi, const double* doi, const double* kh, const
 static int bwd_impl(const double* q, const double* k, const double* v, const double* dout,
                     const int64_t* rows, int nrows, const int64_t* keys, int nkeys, double* dq,
                     double* dk, double* dv, double* o_out, double* lse_out, double* D_out, int B,
-                    int Hq, int Hkv, int N, int d, int causal, double scale, int o_bf16) {
+                    int Hq, int Hkv, int N, int d, int causal, int window, double scale, int o_bf16) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv || check_shape(B, Hq, Hkv, N, N, d)) return -1;
     if (!rows) nrows = N;
     if (!keys) nkeys = N;
@@ -302,7 +302,7 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
                 if (!rows) dqi = dq + ri * d;
                 else if (rslot[i] >= 0) dqi = dq + (((size_t)b * Hq + h) * nrows + rslot[i]) * d;
                 double lse_i, D_i;
-                bwd_row(q + ri * d, dout + ri * d, kh, vh, N, d, i, causal, scale, S, P, oi, &lse_i,
+                bwd_row(q + ri * d, dout + ri * d, kh, vh, N, d, i, causal, window, scale, S, P, oi, &lse_i,
                         &D_i, dqi, slot, priv + (size_t)t * 2 * kout, priv + (size_t)t * 2 * kout + kout,
                         o_bf16, ostore);
                 if (o_out) memcpy(o_out + ri * d, oi, sizeof(double) * d);
@@ -327,23 +327,24 @@ static int bwd_impl(const double* q, const double* k, const double* v, const dou
 }
 
 /* Full backward: every dQ row and every dK/dV key, plus O, LSE and D (optional).
- * o_bf16: form D from O rounded to bfloat16 (see the header comment). */
+ * o_bf16: form D from O rounded to bfloat16 (see the header comment); window:
+ * as in oracle_attn_fwd. */
 int oracle_attn_bwd(const double* q, const double* k, const double* v, const double* dout,
                     double* dq, double* dk, double* dv, double* o_out, double* lse_out,
-                    double* D_out, int B, int Hq, int Hkv, int N, int d, int causal,
+                    double* D_out, int B, int Hq, int Hkv, int N, int d, int causal, int window,
                     double scale, int o_bf16) {
     return bwd_impl(q, k, v, dout, NULL, 0, NULL, 0, dq, dk, dv, o_out, lse_out, D_out, B, Hq, Hkv,
-                    N, d, causal, scale, o_bf16);
+                    N, d, causal, window, scale, o_bf16);
 }
 
 /* Sampled backward: dQ of the listed rows, dK/dV of the listed keys. */
 int oracle_attn_bwd_sampled(const double* q, const double* k, const double* v, const double* dout,
                             const int64_t* rows, int nrows, const int64_t* keys, int nkeys,
                             double* dq_rows, double* dk_keys, double* dv_keys, int B, int Hq,
-                            int Hkv, int N, int d, int causal, double scale, int o_bf16) {
+                            int Hkv, int N, int d, int causal, int window, double scale, int o_bf16) {
     if (!rows || !keys) return -1;
     return bwd_impl(q, k, v, dout, rows, nrows, keys, nkeys, dq_rows, dk_keys, dv_keys, NULL, NULL,
-                    NULL, B, Hq, Hkv, N, d, causal, scale, o_bf16);
+                    NULL, B, Hq, Hkv, N, d, causal, window, scale, o_bf16);
 }
 
 /* The bfloat16 rounding the stored-O mode applies, exposed so tests can pin it. */

@@ -527,6 +527,50 @@ def pin_sliding_window(orc):
         _close(P.sum(-1), np.ones(P.shape[:-1]), what="window rows sum to 1")
 
 
+def pin_sliding_window_backward(orc):
+    """Gradients under the sliding-window mask: torch's fp64 autograd through SDPA
+    with the band mask written out, central finite differences on a tiny case,
+    W >= N equal to plain causal, and the sampled backward equal to the full one."""
+    import torch
+    B, Hq, Hkv, N, d = 1, 4, 2, 19, 5
+    G = Hq // Hkv
+    q, do = _rand((B, Hq, N, d), 210), _rand((B, Hq, N, d), 213)
+    k, v = _rand((B, Hkv, N, d), 211), _rand((B, Hkv, N, d), 212)
+    s = 0.6
+    for W in (1, 4, 7):
+        j = np.arange(N)
+        band = torch.tensor((j[None, :] <= j[:, None]) & (j[None, :] > j[:, None] - W))
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        to = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(G, 1), tv.repeat_interleave(G, 1), attn_mask=band, scale=s)
+        (to * torch.tensor(do)).sum().backward()
+        g = orc.bwd(q, k, v, do, True, s, window=W)
+        _close(g["o"], to.detach().numpy(), tol=1e-12, what=f"window {W} O")
+        _close(g["dq"], tq.grad.numpy(), tol=1e-11, what=f"window {W} dQ")
+        _close(g["dk"], tk.grad.numpy(), tol=1e-11, what=f"window {W} dK")
+        _close(g["dv"], tv.grad.numpy(), tol=1e-11, what=f"window {W} dV")
+        rows, keys = np.array([0, 6, 18], dtype=np.int64), np.array([17, 2], dtype=np.int64)
+        sm = orc.bwd_sampled(q, k, v, do, True, s, rows, keys, window=W)
+        _close(sm["dq"], g["dq"][:, :, rows], what=f"window {W} sampled dQ")
+        _close(sm["dk"], g["dk"][:, :, keys], what=f"window {W} sampled dK")
+    gw, gc = orc.bwd(q, k, v, do, True, s, window=N), orc.bwd(q, k, v, do, True, s)
+    for key in ("dq", "dk", "dv"):
+        _close(gw[key], gc[key], what=f"window N {key}")
+    # finite differences of sum(dO * O) in one K and one V entry, W = 3
+    h, W = 1e-6, 3
+    g = orc.bwd(q, k, v, do, True, s, window=W)
+    for name, arr, idx in (("k", k, (0, 1, 9, 2)), ("v", v, (0, 0, 4, 3)), ("q", q, (0, 3, 12, 1))):
+        xp, xm = arr.copy(), arr.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        args_p = {"q": q, "k": k, "v": v}
+        args_m = dict(args_p)
+        args_p[name], args_m[name] = xp, xm
+        fp = float((orc.fwd(args_p["q"], args_p["k"], args_p["v"], True, s, window=W)[0] * do).sum())
+        fm = float((orc.fwd(args_m["q"], args_m["k"], args_m["v"], True, s, window=W)[0] * do).sum())
+        _close((fp - fm) / (2 * h), g["d" + name][idx], tol=1e-7, what=f"window FD d{name}")
+
+
 PINS = [
     pin_one_token,
     pin_two_tokens,
@@ -550,4 +594,5 @@ PINS = [
     pin_decode_positions,
     pin_split_merge,
     pin_sliding_window,
+    pin_sliding_window_backward,
 ]
