@@ -27,7 +27,7 @@ MUTANTS = {
     "fwd GQA map modulo": ("const int hk = h / G;\n        const double* kh", "const int hk = h % Hkv;\n        const double* kh"),
     "window keeps one key too many": ("(int64_t)j > pos_i - window", "(int64_t)j >= pos_i - window"),
     "window ignored": ("(window <= 0 ||", "(1 ||"),
-    "bwd window ignored": ("if (!is_visible(i, j, causal, window)) continue;", "if (!is_visible(i, j, causal, 0)) continue;"),
+    "bwd softmax ignores window": ("attend_row(qi, kh, vh, N, d, i, causal, window, scale,", "attend_row(qi, kh, vh, N, d, i, causal, 0, scale,"),
     "fwd row position ignored": ("qpos ? qpos[i] : i, causal, window, scale, S, P,", "qpos ? qpos[i] : 0, causal, window, scale, S, P,"),
     "D uses dO.dO": ("const double Di = dot(doi, ostore, d);", "const double Di = dot(doi, doi, d);"),
     "D term dropped": ("const double dSij = P[j] * (dPij - Di);", "const double dSij = P[j] * dPij;"),
