@@ -17,9 +17,10 @@ With --varlen NAME it measures the forward pass over packed sequences of
 different lengths (flash_attn_fwd_varlen) against the MFMA roofline, counting
 4*Hq*d FLOP per visible (query, key) pair of every sequence.
 
-With --window W it measures the forward pass of the same workload under a
-sliding-window causal mask of W keys (flash_attn_fwd_window), counting 4*d FLOP
-per visible pair: sum over rows of min(i + 1, W) pairs per head.
+With --window W it measures the forward and backward passes of the same
+workload under a sliding-window causal mask of W keys (flash_attn_fwd_window,
+flash_attn_bwd_window), counting 4*d FLOP per visible pair for the forward and
+2.5 times that for the backward: sum over rows of min(i + 1, W) pairs per head.
 
 With --decode NAME it measures instead the decode path (a few query rows over
 a long key/value cache) on one of the decode workloads, against the HBM
@@ -267,45 +268,60 @@ def window_main(args) -> int:
     fa.lib()
     w = ai.WORKLOADS[WORKLOAD]
     W = int(args.window)
-    inp = ai.make_inputs(w, with_grad=False)
+    inp = ai.make_inputs(w)
 
     def dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
     del inp
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.bwd_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.d, True)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d, W,
-              w.scale, sp)
+    P = [t.data_ptr() for t in (q, k, v, o, lse, do, dq, dk, dv)]
 
-    def call():
-        st = fa.fwd_window_raw(*args_c)
+    def fwd():
+        st = fa.fwd_window_raw(P[0], P[1], P[2], P[3], P[4], w.B, w.Hq, w.Hkv, w.N, w.d, W, w.scale, sp)
         if st != 0:
             raise RuntimeError(f"fwd_window: {fa.strerror(st)}")
 
+    def bwd():
+        st = fa.bwd_window_raw(*P, w.B, w.Hq, w.Hkv, w.N, w.d, W, w.scale, ws.data_ptr(), ws_bytes, sp)
+        if st != 0:
+            raise RuntimeError(f"bwd_window: {fa.strerror(st)}")
+
     for _ in range(args.warmup):
-        call()
+        fwd()
+        bwd()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s_ in range(args.steps):
         ev[s_][0].record(stream)
-        call()
+        fwd()
         ev[s_][1].record(stream)
+        bwd()
+        ev[s_][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    times = [a.elapsed_time(b) for a, b in ev]
-    ms_avg = sum(times) / len(times)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_avg = fwd_ms + bwd_ms
     n = np.arange(w.N, dtype=np.float64)
     pairs = w.B * w.Hq * float(np.minimum(n + 1, W).sum())
     flop = 4.0 * w.d * pairs
-    tflops = flop / (ms_avg * 1e-3) / 1e12
+    tflops = flop / (fwd_ms * 1e-3) / 1e12
+    step_tflops = 3.5 * flop / (ms_avg * 1e-3) / 1e12
     out = {
-        "metric": "attention fwd TFLOP/s with a sliding-window causal mask (bf16) and % of MI355X bf16 MFMA peak",
-        "value": tflops,
+        "metric": "attention fwd/bwd TFLOP/s with a sliding-window causal mask (bf16) and % of MI355X bf16 MFMA peak",
+        "value": step_tflops,
+        "passes": {"fwd": {"ms": fwd_ms, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS},
+                   "bwd": {"ms": bwd_ms, "tflops": 2.5 * flop / (bwd_ms * 1e-3) / 1e12,
+                           "frac_of_peak": 2.5 * flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}},
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -317,11 +333,11 @@ def window_main(args) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "window": W,
-                   "passes": "fwd (sliding window)"},
+                   "passes": "fwd+bwd (sliding window)"},
         "wall_ms_per_step": wall / args.steps * 1e3,
         "roofline": {"bound": "mfma", "kernel": "fwd_kernel (window)", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "avg_launch_ms": ms_avg, "algorithmic_flop_per_launch": flop},
+                     "avg_launch_ms": fwd_ms, "algorithmic_flop_per_launch": flop},
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -158,7 +158,7 @@ namespace {
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
                int causal, float scale, void* workspace, size_t workspace_bytes, void* stream,
-               int first, int last) {
+               int first, int last, int window = 0) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_shape(B, Hq, Hkv, N, d);
     if (st != FA_OK) return st;
@@ -199,6 +199,7 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
     p.causal = causal ? 1 : 0;
     p.scale = scale;
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    p.window = window;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     for (int stage = first; stage <= last; ++stage) {
         st = hip_status(fa::launch_bwd_stage(p, stage, s));
@@ -306,6 +307,15 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
     p.tps = pl.tps;
     p.pair = pl.pair;
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N,
+                          int d, int window, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (window < 1) return FA_ERR_SHAPE;
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, 1, scale, workspace,
+                      workspace_bytes, stream, 0, 2, window);
 }
 
 const char* flash_attn_strerror(int status) {

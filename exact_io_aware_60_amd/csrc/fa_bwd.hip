@@ -518,12 +518,13 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
     });
 }
 
-// A step that crosses the causal diagonal: keys above a row get P = 0.
-// Unpipelined; at most one per head and wave.
-template <int D>
+// A step that crosses the causal diagonal: keys above a row get P = 0. With a
+// sliding window (WIN) so do keys at or before row - win (rows at or past
+// key + win). Unpipelined; a few per head and wave.
+template <int D, bool WIN>
 __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S,
                                                const typename KvCfg<D>::Addr& la, int lbase, int q0, int key, float sl2,
-                                               float c1, int hh) {
+                                               float c1, int hh, int win) {
     using C = KvCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
     f32x16 s[2], dp[2];
@@ -551,7 +552,7 @@ __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict_
                 const int i = u * 4 + e;
                 const int q = q0 + qb * 32 + u * 8 + hh * 4 + e;
                 float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[e]));
-                if (key > q) x = 0.f;
+                if (key > q || (WIN && q >= key + win)) x = 0.f;
                 s[qb][i] = x;
                 dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[e]);
             }
@@ -590,22 +591,22 @@ __device__ __forceinline__ void kv_copy(const typename KvCfg<D>::PlanR& pr, cons
 // step j from stage `rst`. The two stages are distinct; the __restrict__
 // qualifiers tell the compiler so, and it then reads `rst` without waiting for
 // the copies into `wst`. mode: 0 idle, 1 unmasked, 2 diagonal.
-template <int D>
+template <int D, bool WIN>
 __device__ __forceinline__ void kv_iteration(KvState<D>& S, const typename KvCfg<D>::PlanR& pr,
                                              const typename KvCfg<D>::PlanT& pt, const KvRes& rs, bool issue,
                                              const KvSrc& nx,
                                              FA_LDS uint8_t* __restrict__ wst,
                                              const FA_LDS uint8_t* __restrict__ rst, int mode, int q0, int key,
                                              const typename KvCfg<D>::Addr& la, int lbase, float sl2, float c1, int w,
-                                             int lane) {
+                                             int lane, int win) {
     if (issue) kv_copy<D>(pr, pt, rs, nx, wst, w, lane);
     if (mode == 1)
         kv_step<D, false>(rst, S, la, lbase, sl2, c1, nullptr, nullptr);
     else if (mode == 2)
-        kv_step_masked<D>(rst, S, la, lbase, q0, key, sl2, c1, lane >> 5);
+        kv_step_masked<D, WIN>(rst, S, la, lbase, q0, key, sl2, c1, lane >> 5, win);
 }
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     using C = KvCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
@@ -642,8 +643,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // Steps: row blocks from the last one down to qs (rows before the block's
     // first key see none of it under the causal mask), all G heads per block.
+    // With a sliding window only rows below qe see a key of this workgroup.
+    const int win = WIN ? p.window : 0;
     const int qs = causal ? k0 : 0;
-    const int nrb = (N - qs + kKV_Q - 1) / kKV_Q;
+    const int qe = WIN ? min(N, k0 + kKV_WG - 1 + win) : N;
+    const int nrb = (qe - qs + kKV_Q - 1) / kKV_Q;
     const int nsteps = G * nrb;
     const int qtop = qs + (nrb - 1) * kKV_Q;
     KvRes rs;
@@ -681,8 +685,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     // Steps with q0 >= k0 + 128 (all but the last two row blocks when causal)
     // are unmasked for every wave, and run on one code path. A wave whose keys
     // lie past N runs them too (its keys are zero padding; never stored).
-    const int nsteady = causal ? G * max(0, nrb - 2) : nsteps - 1;   // each has a next step to copy
-    for (int j = 0; j < nsteady; ++j) {
+    // With a window the top row blocks t >= win / 64 (q0 = qs + 64 t) hold rows
+    // past some key's window; they come first (jT steps, per wave), and the
+    // steady blocks are t in [2, win / 64).
+    const int nfar = WIN ? max(0, nrb - win / kKV_Q) : 0;
+    const int jT = G * nfar;
+    const int nsteady = WIN ? G * max(0, min(win / kKV_Q, nrb) - 2)
+                            : (causal ? G * max(0, nrb - 2) : nsteps - 1);   // each has a next step to copy
+    auto per_wave_step = [&](int j) {
+        const int q0 = qtop - (j / G) * kKV_Q;
+        const bool active = kw0 < N && (!causal || q0 + kKV_Q - 1 >= kw0) && (!WIN || q0 <= kw0 + kKV_W - 2 + win);
+        const int mode = !active ? 0
+                                 : (((causal && q0 < kw0 + kKV_W - 1) || (WIN && q0 + kKV_Q - 1 >= kw0 + win)) ? 2 : 1);
+        const bool issue = j + 1 < nsteps;
+        const KvSrc nx = src_of(issue ? j + 1 : j);
+        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
+        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
+        kv_iteration<D, WIN>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, la, lbase, sl2, c1, w, lane, win);
+        wait_vmem();
+        __syncthreads();
+    };
+    for (int j = 0; j < jT; ++j) per_wave_step(j);
+    for (int j = jT; j < jT + nsteady; ++j) {
         const KvNext<D> nx{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane};
         FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
         const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
@@ -690,18 +714,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
         wait_vmem();
         __syncthreads();
     }
-    for (int j = nsteady; j < nsteps; ++j) {
-        const int q0 = qtop - (j / G) * kKV_Q;
-        const bool active = kw0 < N && (!causal || q0 + kKV_Q - 1 >= kw0);
-        const int mode = !active ? 0 : ((causal && q0 < kw0 + kKV_W - 1) ? 2 : 1);
-        const bool issue = j + 1 < nsteps;
-        const KvSrc nx = src_of(issue ? j + 1 : j);
-        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
-        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
-        kv_iteration<D>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, la, lbase, sl2, c1, w, lane);
-        wait_vmem();
-        __syncthreads();
-    }
+    for (int j = jT + nsteady; j < nsteps; ++j) per_wave_step(j);
 
     // dK^T / dV^T blocks: lane holds key l32, d rows db*32 + u*8 + hh*4 + 0..3.
     if (key < N) {
@@ -919,10 +932,10 @@ __device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __r
 // A tile with masked entries (the causal diagonal or keys >= N), complete and
 // unpipelined. Keys past N are zero rows in the copies but would still get
 // P = exp2(-LSE), so they are masked like the ones above the diagonal.
-template <int D>
+template <int D, bool WIN>
 __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
                                           const typename QCfg<D>::Addr& la, int key0, int qrow, int N, bool causal, float sl2,
-                                          float c1, int hh) {
+                                          float c1, int hh, int win) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
 #pragma unroll
@@ -943,7 +956,7 @@ __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __
         for (int i = 0; i < 16; ++i) {
             const int kk = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
             float x = fast_exp2(fmaf(S.s[kb][i], sl2, -S.l2));
-            if (kk >= N || (causal && kk > qrow)) x = 0.f;
+            if (kk >= N || (causal && kk > qrow) || (WIN && kk <= qrow - win)) x = 0.f;
             const float dpv = S.dp[kb][i];
             S.dacc = fmaf(x, dpv, S.dacc);
             S.s[kb][i] = x;
@@ -970,8 +983,10 @@ __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __
 // Tile j of the workgroup loop: start the copy of tile j+1 into `wst` (if
 // any), then this wave's work on tile j (`cur`; tile j-1 in `prv`). The three
 // stages are distinct (the __restrict__ qualifiers say so).
-// Tiles [0, jfull) are unmasked for this wave and pipelined, tiles
-// [jfull, jlast] are masked, later tiles leave the wave idle.
+// Tiles [jw1, jfull) are unmasked for this wave and pipelined, tiles
+// [jfull, jlast] are masked, later tiles leave the wave idle. Without a window
+// jw0 = jw1 = 0; with one, tiles before jw0 hold no visible key for the wave
+// and tiles [jw0, jw1) cross its rows' window starts (masked).
 template <int D>
 __device__ __forceinline__ void dq_copy(const typename QCfg<D>::PlanR& pr, const typename QCfg<D>::PlanT& pt,
                                         BufRes rk, BufRes rv, BufRes rkt, int j, FA_LDS uint8_t* __restrict__ st,
@@ -983,7 +998,7 @@ __device__ __forceinline__ void dq_copy(const typename QCfg<D>::PlanR& pr, const
     pt.copy(rkt, tr, st + C::KT, w);
 }
 
-template <int D>
+template <int D, bool WIN>
 __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D>::PlanR& pr,
                                              const typename QCfg<D>::PlanT& pt, bool issue, BufRes rk,
                                              BufRes rv, BufRes rkt, int jn,
@@ -991,18 +1006,20 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
                                              const FA_LDS uint8_t* __restrict__ cur,
                                              const FA_LDS uint8_t* __restrict__ prv, int j, int jfull,
                                              int jlast, const typename QCfg<D>::Addr& la, int qrow, int N, bool causal,
-                                             float sl2, float c1, int w) {
+                                             float sl2, float c1, int w, int jw0, int jw1, int win) {
     if (issue) dq_copy<D>(pr, pt, rk, rv, rkt, jn, wst, w);
-    if (j < jfull) {
-        if (j == 0) dq_pipe<D, false, false>(S, cur, prv, la, sl2, c1, nullptr, nullptr);
+    if (WIN && j < jw0) return;
+    if (j >= jw1 && j < jfull) {
+        if (j == jw1) dq_pipe<D, false, false>(S, cur, prv, la, sl2, c1, nullptr, nullptr);
         else dq_pipe<D, true, false>(S, cur, prv, la, sl2, c1, nullptr, nullptr);
     } else {
-        if (j == jfull && j > 0) dq_drain<D>(S, prv, la, sl2, c1);
-        if (j <= jlast) dq_masked<D>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1);
+        if (j == jfull && jfull > jw1) dq_drain<D>(S, prv, la, sl2, c1);
+        if (j <= jlast)
+            dq_masked<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1, win);
     }
 }
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
@@ -1037,9 +1054,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     const int jA = causal ? min(nfull, q0 / kQ_N) : nfull;
     int jfull = causal ? min(nfull, r0 / kQ_N) : nfull;
     int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ_N) : ntk - 1;
+    // Sliding window: tiles before jw0 hold no visible key of the wave, tiles
+    // [jw0, jw1) cross its rows' window starts; the loop starts at wave 0's
+    // jw0, and the uniform pipelined tiles start after every wave's jw1.
+    const int win = WIN ? p.window : 0;
+    auto jw1_of = [&](int r) { return r + kQ_W - win > 0 ? (r + kQ_W - win + kQ_N - 1) / kQ_N : 0; };
+    int jw0 = WIN ? max(0, r0 - win + 1) / kQ_N : 0;
+    int jw1 = WIN ? jw1_of(r0) : 0;
+    const int jst = WIN ? max(0, q0 - win + 1) / kQ_N : 0;
+    const int jU0 = WIN ? jw1_of(q0 + kQ_WG - kQ_W) + 1 : 1;
     if (r0 >= N) {
         jfull = jA;
         jlast = -1;
+        jw0 = jw1 = WIN ? jw1_of(q0) : 0;
     }
 
     QState<D> S;
@@ -1067,17 +1094,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     la.init(l32, hh);
     FA_LDS uint8_t* st0 = (FA_LDS uint8_t*)smem;
 
-    dq_copy<D>(pr, pt, rk, rv, rkt, 0, st0, w);
+    dq_copy<D>(pr, pt, rk, rv, rkt, jst, st0 + (jst % 3) * C::STAGE, w);
     wait_vmem();
     __syncthreads();
-    // tile 0
-    dq_iteration<D>(S, pr, pt, nt > 1, rk, rv, rkt, 1, st0 + C::STAGE, st0, st0 + 2 * C::STAGE, 0, jfull, jlast,
-                    la, qrow, N, causal, sl2, c1, w);
-    wait_vmem();
-    __syncthreads();
+    // first tiles, where waves start their pipelines: tile 0 without a window
+    if constexpr (!WIN) {
+        dq_iteration<D, WIN>(S, pr, pt, nt > 1, rk, rv, rkt, 1, st0 + C::STAGE, st0, st0 + 2 * C::STAGE, 0, jfull,
+                             jlast, la, qrow, N, causal, sl2, c1, w, 0, 0, 0);
+        wait_vmem();
+        __syncthreads();
+    } else {
+        for (int j = jst; j < min(jU0, nt); ++j) {
+            dq_iteration<D, WIN>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, st0 + ((j + 1) % 3) * C::STAGE,
+                                 st0 + (j % 3) * C::STAGE, st0 + ((j + 2) % 3) * C::STAGE, j, jfull, jlast, la, qrow,
+                                 N, causal, sl2, c1, w, jw0, jw1, win);
+            wait_vmem();
+            __syncthreads();
+        }
+    }
     // steady state: every wave pipelines, and there is a next tile to copy
     const int jS = min(jA, nt - 1);
-    for (int j = 1; j < jS; ++j) {
+    for (int j = jU0; j < jS; ++j) {
         FA_LDS uint8_t* wst = st0 + ((j + 1) % 3) * C::STAGE;
         const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
         const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
@@ -1088,16 +1125,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         __syncthreads();
     }
     // the diagonal / ragged tiles, where waves differ
-    for (int j = max(1, jS); j < nt; ++j) {
+    for (int j = max(jU0, jS); j < nt; ++j) {
         FA_LDS uint8_t* wst = st0 + ((j + 1) % 3) * C::STAGE;
         const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
         const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
-        dq_iteration<D>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, wst, cur, prv, j, jfull, jlast, la,
-                        qrow, N, causal, sl2, c1, w);
+        dq_iteration<D, WIN>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, wst, cur, prv, j, jfull, jlast, la,
+                             qrow, N, causal, sl2, c1, w, jw0, jw1, win);
         wait_vmem();
         __syncthreads();
     }
-    if (jfull == nt && nt > 0) dq_drain<D>(S, st0 + ((nt - 1) % 3) * C::STAGE, la, sl2, c1);
+    if (jfull == nt && nt > jw1) dq_drain<D>(S, st0 + ((nt - 1) % 3) * C::STAGE, la, sl2, c1);
 
     // exact row dot (the lane halves hold half of the keys each), in units of 2^sS
     const float dx = (S.dacc + swap_half(S.dacc)) * c1;
@@ -1136,14 +1173,20 @@ hipError_t launch_prep_t(const BwdParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
     const int grid = p.B * p.Hkv * ((p.N + kKV_WG - 1) / kKV_WG);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (p.window > 0)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
     const int grid = p.B * p.Hq * ((p.N + kQ_WG - 1) / kQ_WG);
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, p);
+    if (p.window > 0)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

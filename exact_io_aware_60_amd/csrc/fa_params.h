@@ -58,6 +58,7 @@ struct BwdParams {
     int causal;
     float scale;
     float scale_log2;
+    int window;          // sliding window with the causal mask (0: none), as in FwdParams
 };
 
 // Decode: a few query rows against a long key/value sequence. The M = G * Nq

@@ -231,6 +231,19 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
 size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                                         int window);
 
+/*
+ * Backward pass of flash_attn_fwd_window: the gradients of sum(dout * O) under
+ * the sliding-window causal mask (row i sees keys i - window < j <= i).
+ * Arguments, workspace (flash_attn_bwd_workspace_size with causal = 1) and
+ * behaviour as in flash_attn_bwd with causal = 1; o and lse must come from
+ * flash_attn_fwd_window with the same window. window >= 1. Key tiles before a
+ * row block's window and row blocks past a key block's window are not read.
+ */
+int flash_attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int N, int d, int window, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);

@@ -244,3 +244,17 @@ def test_window_checks():
     assert call(d=32) == fa.FA_ERR_HEADDIM
     assert call(scale=-1.0) == fa.FA_ERR_SCALE
     assert call(lse=P[4] + 4) == fa.FA_ERR_ALIGN
+
+
+def test_bwd_window_checks():
+    need = fa.bwd_workspace_size(1, 4, 2, 128, 128, 1)
+    args = [P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 4, 2, 128, 128, 64, 0.088, P[9], need]
+    bad = list(args)
+    bad[14] = 0
+    assert fa.bwd_window_raw(*bad) == fa.FA_ERR_SHAPE
+    bad = list(args)
+    bad[0] = None
+    assert fa.bwd_window_raw(*bad) == fa.FA_ERR_NULL
+    bad = list(args)
+    bad[17] = need - 1
+    assert fa.bwd_window_raw(*bad) == fa.FA_ERR_WORKSPACE

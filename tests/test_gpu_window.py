@@ -100,3 +100,86 @@ def test_full_size_sampled(fa):
     ro, rl = oracle.fwd(f64(inp["q"][:, :, rows]), f64(inp["k"]), f64(inp["v"]), True, w.scale, qpos=rows, window=W)
     eo, el = excess_err(o_s, ro), max_err(l_s, rl)
     assert eo <= TOL_O and el <= TOL_LSE, f"O err {eo:.2e}, LSE err {el:.2e}"
+
+
+# ------------------------------------------------------------------ backward
+TOL_GRAD = 2e-2
+
+
+def check_bwd(fa, inp, W, scale, tag):
+    import torch
+    B, Hq, N, d = inp["q"].shape
+    say(f"bwd window {tag}: B={B} Hq={Hq} Hkv={inp['k'].shape[1]} N={N} d={d} W={W}")
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    o, lse = fa.fwd_window(q, k, v, W, scale=scale)
+    dq, dk, dv = fa.bwd_window(q, k, v, o, lse, do, W, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), True, scale, window=W)
+    errs = {n: excess_err(from_dev_bf16(g), ref[n]) for n, g in (("dq", dq), ("dk", dk), ("dv", dv))}
+    assert all(e <= TOL_GRAD for e in errs.values()), f"{tag} W={W}: {errs}"
+
+
+BWD_CASES = [(300, W) for W in (1, 31, 64, 100, 300)] + \
+            [(1000, W) for W in (63, 64, 65, 127, 128, 129, 192, 256, 700)] + [(2049, 200), (2049, 1500)]
+
+
+@pytest.mark.parametrize("N,W", BWD_CASES, ids=[f"N{n}-W{w}" for n, w in BWD_CASES])
+def test_bwd_windows(fa, N, W):
+    """Window edges against the backward's 64-row steps, 128-key workgroups and
+    64-key dQ tiles: masked first tiles, a uniform middle and masked ends."""
+    inp = ai.make_case(1, 4, 2, N, 128, seed=N + 5 * W)
+    check_bwd(fa, inp, W, 0.0883883, "window")
+
+
+@pytest.mark.parametrize("W", [33, 500])
+def test_bwd_windows_d64(fa, W):
+    inp = ai.make_case(2, 4, 4, 1100, 64, seed=40 + W)
+    check_bwd(fa, inp, W, 0.125, "d64")
+
+
+def test_bwd_large_logits(fa):
+    inp = ai.make_case(1, 4, 2, 1500, 128, seed=41, dist_scale=2.0)
+    check_bwd(fa, inp, 333, 0.2, "large logits")
+
+
+def test_bwd_window_covering_everything_is_causal(fa):
+    """W >= N: the same gradients as the plain causal backward (within rounding)."""
+    import torch
+    inp = ai.make_case(1, 4, 2, 700, 128, seed=42)
+    say("bwd window >= N vs causal")
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    o, lse = fa.fwd(q, k, v, causal=True)
+    g1 = fa.bwd_window(q, k, v, o, lse, do, 700)
+    g2 = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, b_ in zip(g1, g2):
+        assert (a.float() - b_.float()).abs().max().item() <= TOL_GRAD
+
+
+def test_bwd_full_size_sampled(fa):
+    """gqa16k shapes with a 4096-key window: full GPU forward and backward, then
+    256 sampled dQ rows and dK/dV keys of one seeded (b, kv-head) group against
+    the oracle."""
+    import torch
+    w = ai.WORKLOADS["gqa16k"]
+    W = 4096
+    inp = ai.make_inputs(w)
+    say("bwd window gqa16k W=4096 (full size on GPU, one group)")
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    o, lse = fa.fwd_window(q, k, v, W, scale=w.scale)
+    dq, dk, dv = fa.bwd_window(q, k, v, o, lse, do, W, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = ai.sample_rows(w.N, 256, w.cfg_id)
+    keys = ai.sample_rows(w.N, 256, w.cfg_id + 100)
+    rt, kt = torch.as_tensor(rows, device=q.device), torch.as_tensor(keys, device=q.device)
+    b, h, G = 1, 5, w.G
+    hs = slice(h * G, (h + 1) * G)
+    g = {"dq": from_dev_bf16(dq[b:b + 1, hs].index_select(2, rt)),
+         "dk": from_dev_bf16(dk[b:b + 1, h:h + 1].index_select(2, kt)),
+         "dv": from_dev_bf16(dv[b:b + 1, h:h + 1].index_select(2, kt))}
+    del q, k, v, do, o, lse, dq, dk, dv
+    ref = oracle.bwd_sampled(f64(inp["q"][b:b + 1, hs]), f64(inp["k"][b:b + 1, h:h + 1]),
+                             f64(inp["v"][b:b + 1, h:h + 1]), f64(inp["do"][b:b + 1, hs]), True, w.scale, rows, keys,
+                             window=W)
+    errs = {n: excess_err(g[n], ref[n]) for n in g}
+    assert all(e <= TOL_GRAD for e in errs.values()), errs
