@@ -13,9 +13,10 @@ it runs on. Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
 
-With --varlen NAME it measures the forward pass over packed sequences of
-different lengths (flash_attn_fwd_varlen) against the MFMA roofline, counting
-4*Hq*d FLOP per visible (query, key) pair of every sequence.
+With --varlen NAME it measures the forward and backward passes over packed
+sequences of different lengths (flash_attn_fwd_varlen, flash_attn_bwd_varlen)
+against the MFMA roofline, counting 4*Hq*d FLOP per visible (query, key) pair of
+every sequence for the forward and 2.5 times that for the backward.
 
 With --window W it measures the forward and backward passes of the same
 workload under a sliding-window causal mask of W keys (flash_attn_fwd_window,
@@ -356,41 +357,60 @@ def varlen_main(args) -> int:
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
     q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    do = torch.randn_like(q)
     lens = inp["lengths"]
     cu = torch.as_tensor(inp["cu_seqlens"]).cuda()
     del inp
     total, ms = int(lens.sum()), int(lens.max())
     o = torch.empty_like(q)
     lse = torch.empty((w.Hq, total), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = fa.bwd_workspace_size(1, w.Hq, w.Hkv, total, w.d, True)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu.data_ptr(), len(lens), ms,
               total, w.Hq, w.Hkv, w.d, w.causal, w.scale, sp)
+    args_b = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+              dk.data_ptr(), dv.data_ptr(), cu.data_ptr(), len(lens), ms, total, w.Hq, w.Hkv, w.d, w.causal, w.scale,
+              ws.data_ptr(), ws_bytes, sp)
 
     def call():
         st = fa.fwd_varlen_raw(*args_c)
         if st != 0:
             raise RuntimeError(f"fwd_varlen: {fa.strerror(st)}")
 
+    def call_b():
+        st = fa.bwd_varlen_raw(*args_b)
+        if st != 0:
+            raise RuntimeError(f"bwd_varlen: {fa.strerror(st)}")
+
     for _ in range(args.warmup):
         call()
+        call_b()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s_ in range(args.steps):
         ev[s_][0].record(stream)
         call()
         ev[s_][1].record(stream)
+        call_b()
+        ev[s_][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    times = [a.elapsed_time(b) for a, b in ev]
-    ms_avg = sum(times) / len(times)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    ms_avg = fwd_ms + bwd_ms
     pairs = float(sum(int(n) * int(n) for n in lens)) / (2.0 if w.causal else 1.0)
     flop = 4.0 * w.Hq * w.d * pairs
-    tflops = flop / (ms_avg * 1e-3) / 1e12
+    tflops = flop / (fwd_ms * 1e-3) / 1e12
     out = {
-        "metric": "attention fwd TFLOP/s over packed sequences (bf16) and % of MI355X bf16 MFMA peak",
-        "value": tflops,
+        "metric": "attention fwd/bwd TFLOP/s over packed sequences (bf16) and % of MI355X bf16 MFMA peak",
+        "value": 3.5 * flop / (ms_avg * 1e-3) / 1e12,
+        "passes": {"fwd": {"ms": fwd_ms, "tflops": tflops, "frac_of_peak": tflops / PEAK_BF16_TFLOPS},
+                   "bwd": {"ms": bwd_ms, "tflops": 2.5 * flop / (bwd_ms * 1e-3) / 1e12,
+                           "frac_of_peak": 2.5 * flop / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}},
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -402,11 +422,11 @@ def varlen_main(args) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "total": total, "max_seqlen": ms,
-                   "min_len": int(lens.min()), "d": w.d, "causal": w.causal, "passes": "fwd (packed sequences)"},
+                   "min_len": int(lens.min()), "d": w.d, "causal": w.causal, "passes": "fwd+bwd (packed sequences)"},
         "wall_ms_per_step": wall / args.steps * 1e3,
         "roofline": {"bound": "mfma", "kernel": "fwd_kernel (packed)", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "avg_launch_ms": ms_avg, "algorithmic_flop_per_launch": flop},
+                     "avg_launch_ms": fwd_ms, "algorithmic_flop_per_launch": flop},
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

@@ -26,7 +26,7 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
             "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
             "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen",
-            "flash_attn_fwd_window", "flash_attn_bwd_window")
+            "flash_attn_fwd_window", "flash_attn_bwd_window", "flash_attn_bwd_varlen")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.flash_attn_fwd.restype = _i
         L.flash_attn_fwd.argtypes = [_vp] * 5 + [_i] * 6 + [ctypes.c_float, _vp]
+        L.flash_attn_bwd_varlen.restype = _i
+        L.flash_attn_bwd_varlen.argtypes = [_vp] * 10 + [_i] * 7 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_bwd_window.restype = _i
         L.flash_attn_bwd_window.argtypes = [_vp] * 9 + [_i] * 6 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         for name in ("flash_attn_bwd",) + BWD_STAGES:
@@ -105,6 +107,13 @@ def bwd_stage_raw(stage: int, q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d,
     fn = getattr(lib(), BWD_STAGES[stage])
     return fn(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, int(causal), float(scale), workspace,
               workspace_bytes, stream)
+
+
+def bwd_varlen_raw(q, k, v, o, lse, do, dq, dk, dv, cu_seqlens, B, max_seqlen, total, Hq, Hkv, d, causal, scale,
+                   workspace, workspace_bytes, stream=None) -> int:
+    """flash_attn_bwd_varlen on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_bwd_varlen(q, k, v, o, lse, do, dq, dk, dv, cu_seqlens, B, max_seqlen, total, Hq, Hkv,
+                                       d, int(causal), float(scale), workspace, workspace_bytes, stream)
 
 
 def bwd_window_raw(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, window, scale, workspace, workspace_bytes,
@@ -298,4 +307,31 @@ def bwd_window(q, k, v, o, lse, do, window: int, scale: float | None = None, wor
     _check(bwd_window_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, window, scale,
                           workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None,
+               workspace=None):
+    """Backward pass of fwd_varlen (causal): q/o/do [Hq, total, d], k/v [Hkv, total, d], lse [Hq, total].
+    Returns (dq, dk, dv), bf16, in the same packed layout."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [Hq, total, d] and k, v [Hkv, total, d]")
+    Hq, total, d = q.shape
+    Hkv = k.shape[0]
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _checked(t, name)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (Hq, total):
+        raise ValueError("lse must be contiguous float32 [Hq, total]")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be an int32 GPU tensor of shape [B + 1]")
+    scale = default_scale(d) if scale is None else scale
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_bytes = bwd_workspace_size(1, Hq, Hkv, total, d, True)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    _check(bwd_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1,
+                          int(max_seqlen), total, Hq, Hkv, d, causal, scale, workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream(q)))
     return dq, dk, dv

@@ -158,7 +158,7 @@ namespace {
 int bwd_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
                int causal, float scale, void* workspace, size_t workspace_bytes, void* stream,
-               int first, int last, int window = 0) {
+               int first, int last, int window = 0, const int* cu_seqlens = nullptr, int nseq = 0) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_shape(B, Hq, Hkv, N, d);
     if (st != FA_OK) return st;
@@ -200,6 +200,8 @@ int bwd_common(const void* q, const void* k, const void* v, const void* o, const
     p.scale = scale;
     p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
     p.window = window;
+    p.cu_seqlens = cu_seqlens;
+    p.nseq = nseq;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     for (int stage = first; stage <= last; ++stage) {
         st = hip_status(fa::launch_bwd_stage(p, stage, s));
@@ -316,6 +318,17 @@ int flash_attn_bwd_window(const void* q, const void* k, const void* v, const voi
     if (window < 1) return FA_ERR_SHAPE;
     return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N, d, 1, scale, workspace,
                       workspace_bytes, stream, 0, 2, window);
+}
+
+int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, const int* cu_seqlens, int B,
+                          int max_seqlen, int total, int Hq, int Hkv, int d, int causal, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens) return FA_ERR_NULL;
+    if (B < 1 || max_seqlen < 1 || !causal) return FA_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return FA_ERR_ALIGN;
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, 1, Hq, Hkv, total, d, 1, scale, workspace,
+                      workspace_bytes, stream, 0, 2, 0, cu_seqlens, B);
 }
 
 const char* flash_attn_strerror(int status) {

@@ -99,6 +99,34 @@ struct LaneAddr {
 // scheduling barrier that follows.
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// Bounded masks (sliding window or packed sequences), as the first key a row
+// sees and the first row that no longer sees a key. Window W: rows r see keys
+// r - W + 1 .. r. Packed sequences: the keys of the row's own sequence up to
+// the row. Offsets are clamped to [0, N], so any cu_seqlens keeps every bound
+// inside the arrays; rows and keys at or past N get N.
+struct Bounds {
+    const int* cu;   // packed offsets (nseq + 1 entries), or null for a window
+    int nseq, win, N;
+    // index s with cu[s] <= x < cu[s+1] (the last such s when sequences are empty)
+    __device__ __forceinline__ int seq_of(int x) const {
+        int lo = 0, hi = nseq - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (min(max(cu[mid], 0), N) <= x) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+    __device__ __forceinline__ int first_key(int r) const {      // of row r
+        if (!cu) return r - win + 1;
+        return r >= N ? N : min(max(cu[seq_of(r)], 0), N);
+    }
+    __device__ __forceinline__ int row_end(int k) const {        // first row past key k's reach
+        if (!cu) return k + win;
+        return k >= N ? N : min(max(cu[seq_of(k) + 1], 0), N);
+    }
+};
+
 // Workgroup id -> (rank, unit). Workgroups are handed to the 8 XCDs
 // round-robin; when the unit count is a multiple of 8, each XCD gets a
 // contiguous block of units and walks them in rank order, so the units that
@@ -519,12 +547,13 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
 }
 
 // A step that crosses the causal diagonal: keys above a row get P = 0. With a
-// sliding window (WIN) so do keys at or before row - win (rows at or past
-// key + win). Unpipelined; a few per head and wave.
+// bounded mask (WIN: sliding window or packed sequences) so do rows at or past
+// kend, the first row that no longer sees this lane's key. Unpipelined; a few
+// per head and wave.
 template <int D, bool WIN>
 __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S,
                                                const typename KvCfg<D>::Addr& la, int lbase, int q0, int key, float sl2,
-                                               float c1, int hh, int win) {
+                                               float c1, int hh, int kend) {
     using C = KvCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
     f32x16 s[2], dp[2];
@@ -552,7 +581,7 @@ __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict_
                 const int i = u * 4 + e;
                 const int q = q0 + qb * 32 + u * 8 + hh * 4 + e;
                 float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[e]));
-                if (key > q || (WIN && q >= key + win)) x = 0.f;
+                if (key > q || (WIN && q >= kend)) x = 0.f;
                 s[qb][i] = x;
                 dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[e]);
             }
@@ -598,12 +627,12 @@ __device__ __forceinline__ void kv_iteration(KvState<D>& S, const typename KvCfg
                                              FA_LDS uint8_t* __restrict__ wst,
                                              const FA_LDS uint8_t* __restrict__ rst, int mode, int q0, int key,
                                              const typename KvCfg<D>::Addr& la, int lbase, float sl2, float c1, int w,
-                                             int lane, int win) {
+                                             int lane, int kend) {
     if (issue) kv_copy<D>(pr, pt, rs, nx, wst, w, lane);
     if (mode == 1)
         kv_step<D, false>(rst, S, la, lbase, sl2, c1, nullptr, nullptr);
     else if (mode == 2)
-        kv_step_masked<D, WIN>(rst, S, la, lbase, q0, key, sl2, c1, lane >> 5, win);
+        kv_step_masked<D, WIN>(rst, S, la, lbase, q0, key, sl2, c1, lane >> 5, kend);
 }
 
 template <int D, bool WIN>
@@ -643,10 +672,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // Steps: row blocks from the last one down to qs (rows before the block's
     // first key see none of it under the causal mask), all G heads per block.
-    // With a sliding window only rows below qe see a key of this workgroup.
-    const int win = WIN ? p.window : 0;
+    // With a bounded mask only rows below qe see a key of this workgroup.
+    const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
+    const int kend = WIN ? bd.row_end(key) : 0;     // this lane's key
     const int qs = causal ? k0 : 0;
-    const int qe = WIN ? min(N, k0 + kKV_WG - 1 + win) : N;
+    const int qe = WIN ? min(N, bd.row_end(k0 + kKV_WG - 1)) : N;
     const int nrb = (qe - qs + kKV_Q - 1) / kKV_Q;
     const int nsteps = G * nrb;
     const int qtop = qs + (nrb - 1) * kKV_Q;
@@ -685,23 +715,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     // Steps with q0 >= k0 + 128 (all but the last two row blocks when causal)
     // are unmasked for every wave, and run on one code path. A wave whose keys
     // lie past N runs them too (its keys are zero padding; never stored).
-    // With a window the top row blocks t >= win / 64 (q0 = qs + 64 t) hold rows
-    // past some key's window; they come first (jT steps, per wave), and the
-    // steady blocks are t in [2, win / 64).
-    const int nfar = WIN ? max(0, nrb - win / kKV_Q) : 0;
+    // With a bounded mask the top row blocks t >= tfar (q0 = qs + 64 t) hold
+    // rows past some key's reach (the workgroup's first key reaches least far);
+    // they come first (jT steps, per wave), and the steady blocks are t in
+    // [2, tfar).
+    const int tfar = WIN ? max(0, bd.row_end(k0) - k0) / kKV_Q : 0;
+    const int nfar = WIN ? max(0, nrb - tfar) : 0;
     const int jT = G * nfar;
-    const int nsteady = WIN ? G * max(0, min(win / kKV_Q, nrb) - 2)
+    const int nsteady = WIN ? G * max(0, min(tfar, nrb) - 2)
                             : (causal ? G * max(0, nrb - 2) : nsteps - 1);   // each has a next step to copy
+    const int kend_w0 = WIN ? bd.row_end(kw0) : 0, kend_w31 = WIN ? bd.row_end(kw0 + kKV_W - 1) : 0;
     auto per_wave_step = [&](int j) {
         const int q0 = qtop - (j / G) * kKV_Q;
-        const bool active = kw0 < N && (!causal || q0 + kKV_Q - 1 >= kw0) && (!WIN || q0 <= kw0 + kKV_W - 2 + win);
+        const bool active = kw0 < N && (!causal || q0 + kKV_Q - 1 >= kw0) && (!WIN || q0 < kend_w31);
         const int mode = !active ? 0
-                                 : (((causal && q0 < kw0 + kKV_W - 1) || (WIN && q0 + kKV_Q - 1 >= kw0 + win)) ? 2 : 1);
+                                 : (((causal && q0 < kw0 + kKV_W - 1) || (WIN && q0 + kKV_Q - 1 >= kend_w0)) ? 2 : 1);
         const bool issue = j + 1 < nsteps;
         const KvSrc nx = src_of(issue ? j + 1 : j);
         FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
         const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
-        kv_iteration<D, WIN>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, la, lbase, sl2, c1, w, lane, win);
+        kv_iteration<D, WIN>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, la, lbase, sl2, c1, w, lane, kend);
         wait_vmem();
         __syncthreads();
     };
@@ -935,7 +968,7 @@ __device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __r
 template <int D, bool WIN>
 __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
                                           const typename QCfg<D>::Addr& la, int key0, int qrow, int N, bool causal, float sl2,
-                                          float c1, int hh, int win) {
+                                          float c1, int hh, int lbq) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
 #pragma unroll
@@ -956,7 +989,7 @@ __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __
         for (int i = 0; i < 16; ++i) {
             const int kk = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
             float x = fast_exp2(fmaf(S.s[kb][i], sl2, -S.l2));
-            if (kk >= N || (causal && kk > qrow) || (WIN && kk <= qrow - win)) x = 0.f;
+            if (kk >= N || (causal && kk > qrow) || (WIN && kk < lbq)) x = 0.f;
             const float dpv = S.dp[kb][i];
             S.dacc = fmaf(x, dpv, S.dacc);
             S.s[kb][i] = x;
@@ -1006,7 +1039,7 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
                                              const FA_LDS uint8_t* __restrict__ cur,
                                              const FA_LDS uint8_t* __restrict__ prv, int j, int jfull,
                                              int jlast, const typename QCfg<D>::Addr& la, int qrow, int N, bool causal,
-                                             float sl2, float c1, int w, int jw0, int jw1, int win) {
+                                             float sl2, float c1, int w, int jw0, int jw1, int lbq) {
     if (issue) dq_copy<D>(pr, pt, rk, rv, rkt, jn, wst, w);
     if (WIN && j < jw0) return;
     if (j >= jw1 && j < jfull) {
@@ -1015,7 +1048,7 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
     } else {
         if (j == jfull && jfull > jw1) dq_drain<D>(S, prv, la, sl2, c1);
         if (j <= jlast)
-            dq_masked<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1, win);
+            dq_masked<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1, lbq);
     }
 }
 
@@ -1054,14 +1087,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     const int jA = causal ? min(nfull, q0 / kQ_N) : nfull;
     int jfull = causal ? min(nfull, r0 / kQ_N) : nfull;
     int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ_N) : ntk - 1;
-    // Sliding window: tiles before jw0 hold no visible key of the wave, tiles
-    // [jw0, jw1) cross its rows' window starts; the loop starts at wave 0's
-    // jw0, and the uniform pipelined tiles start after every wave's jw1.
-    const int win = WIN ? p.window : 0;
-    auto jw1_of = [&](int r) { return r + kQ_W - win > 0 ? (r + kQ_W - win + kQ_N - 1) / kQ_N : 0; };
-    int jw0 = WIN ? max(0, r0 - win + 1) / kQ_N : 0;
+    // Bounded mask (sliding window or packed sequences): tiles before jw0 hold
+    // no visible key of the wave, tiles [jw0, jw1) cross its rows' first keys;
+    // the loop starts at wave 0's jw0, and the uniform pipelined tiles start
+    // after every wave's jw1. A row's first key never decreases along the rows.
+    const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
+    const int lbq = WIN ? bd.first_key(qrow) : 0;   // this lane's row
+    auto jw1_of = [&](int r) {                       // first tile the wave of rows r.. sees in full
+        const int f = bd.first_key(r + kQ_W - 1);
+        return f > 0 ? (f + kQ_N - 1) / kQ_N : 0;
+    };
+    int jw0 = WIN ? max(0, bd.first_key(r0)) / kQ_N : 0;
     int jw1 = WIN ? jw1_of(r0) : 0;
-    const int jst = WIN ? max(0, q0 - win + 1) / kQ_N : 0;
+    const int jst = WIN ? max(0, bd.first_key(q0)) / kQ_N : 0;
     const int jU0 = WIN ? jw1_of(q0 + kQ_WG - kQ_W) + 1 : 1;
     if (r0 >= N) {
         jfull = jA;
@@ -1107,7 +1145,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         for (int j = jst; j < min(jU0, nt); ++j) {
             dq_iteration<D, WIN>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, st0 + ((j + 1) % 3) * C::STAGE,
                                  st0 + (j % 3) * C::STAGE, st0 + ((j + 2) % 3) * C::STAGE, j, jfull, jlast, la, qrow,
-                                 N, causal, sl2, c1, w, jw0, jw1, win);
+                                 N, causal, sl2, c1, w, jw0, jw1, lbq);
             wait_vmem();
             __syncthreads();
         }
@@ -1130,7 +1168,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
         const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
         dq_iteration<D, WIN>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, wst, cur, prv, j, jfull, jlast, la,
-                             qrow, N, causal, sl2, c1, w, jw0, jw1, win);
+                             qrow, N, causal, sl2, c1, w, jw0, jw1, lbq);
         wait_vmem();
         __syncthreads();
     }
@@ -1173,7 +1211,7 @@ hipError_t launch_prep_t(const BwdParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
     const int grid = p.B * p.Hkv * ((p.N + kKV_WG - 1) / kKV_WG);
-    if (p.window > 0)
+    if (p.window > 0 || p.cu_seqlens)
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
@@ -1183,7 +1221,7 @@ hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
     const int grid = p.B * p.Hq * ((p.N + kQ_WG - 1) / kQ_WG);
-    if (p.window > 0)
+    if (p.window > 0 || p.cu_seqlens)
         hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);

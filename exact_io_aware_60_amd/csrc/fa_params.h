@@ -59,6 +59,12 @@ struct BwdParams {
     float scale;
     float scale_log2;
     int window;          // sliding window with the causal mask (0: none), as in FwdParams
+    // Packed sequences (null: none): the arrays are one sequence of N = total
+    // rows per head, and sequence s holds rows cu_seqlens[s] .. cu_seqlens[s+1]-1.
+    // With the causal mask a row then sees the keys from its sequence's start
+    // to itself, a key is seen by the rows from itself to its sequence's end.
+    const int* cu_seqlens;
+    int nseq;
 };
 
 // Decode: a few query rows against a long key/value sequence. The M = G * Nq

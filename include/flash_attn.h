@@ -244,6 +244,26 @@ int flash_attn_bwd_window(const void* q, const void* k, const void* v, const voi
                           int B, int Hq, int Hkv, int N, int d, int window, float scale,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward pass of flash_attn_fwd_varlen (causal only): the gradients of
+ * sum(dout * O) for packed sequences, every sequence on its own.
+ *   q, k, v, o, dout, dq, dk, dv   [H, total, d] as in flash_attn_fwd_varlen
+ *   lse                            fp32 [Hq, total] from flash_attn_fwd_varlen
+ *   cu_seqlens                     int32 [B + 1] device array, as there
+ * workspace: flash_attn_bwd_workspace_size(1, Hq, Hkv, total, d, 1) bytes (the
+ * packed arrays are one sequence of `total` rows to the preparation and the
+ * workspace). causal must be 1 (the non-causal packed backward is not built:
+ * FA_ERR_SHAPE). Each row's keys run from its sequence's start to itself, and
+ * the gradient kernels read only those, as in flash_attn_bwd_window with a
+ * per-row first key. max_seqlen is checked (>= 1) but not otherwise needed.
+ * Offsets are clamped in the kernels as in flash_attn_fwd_varlen.
+ */
+int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          const int* cu_seqlens, int B, int max_seqlen, int total, int Hq, int Hkv,
+                          int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);

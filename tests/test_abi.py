@@ -258,3 +258,21 @@ def test_bwd_window_checks():
     bad = list(args)
     bad[17] = need - 1
     assert fa.bwd_window_raw(*bad) == fa.FA_ERR_WORKSPACE
+
+
+def test_bwd_varlen_checks():
+    need = fa.bwd_workspace_size(1, 4, 2, 1000, 128, 1)
+    args = [P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9], 3, 512, 1000, 4, 2, 128, 1, 0.088, P[10],
+            need]
+    bad = list(args)
+    bad[9] = None
+    assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_NULL
+    bad = list(args)
+    bad[16] = 0
+    assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_SHAPE      # the packed backward is causal only
+    bad = list(args)
+    bad[9] = P[9] + 2
+    assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_ALIGN
+    bad = list(args)
+    bad[19] = need - 1
+    assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_WORKSPACE

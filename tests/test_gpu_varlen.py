@@ -107,3 +107,84 @@ def test_workload_sampled(fa, name):
     w = ai.VARLEN_WORKLOADS[name]
     inp = ai.make_varlen_inputs(w)
     check(fa, inp, w.causal, w.scale, name, rows_per_seq=64)
+
+
+# ------------------------------------------------------------------ backward
+TOL_GRAD = 2e-2
+
+
+def make_grad_case(lengths, Hq, Hkv, d, seed):
+    inp = ai.make_varlen_case(lengths, Hq, Hkv, d, seed)
+    inp["do"] = ai.normal_bf16(inp["q"].shape, 4000 + seed, ai.TENSOR_DO)
+    return inp
+
+
+def check_bwd(fa, inp, scale, tag, seqs=None, sample=None):
+    """GPU forward + backward on the packed batch, then per sequence (all, or
+    the listed ones) the oracle's gradients of that sequence alone; `sample`
+    rows/keys per sequence when given (sampled oracle), else every element."""
+    import torch
+    lens, cu = inp["lengths"], inp["cu_seqlens"]
+    Hq, total, d = inp["q"].shape
+    Hkv = inp["k"].shape[0]
+    say(f"bwd varlen {tag}: B={len(lens)} Hq={Hq} Hkv={Hkv} total={total} d={d}")
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    cud = torch.as_tensor(cu).cuda()
+    ms = int(max(lens.max(), 1))
+    o, lse = fa.fwd_varlen(q, k, v, cud, ms, causal=True, scale=scale)
+    dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cud, ms, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = from_dev_bf16(dq), from_dev_bf16(dk), from_dev_bf16(dv)
+    errs = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in (range(len(lens)) if seqs is None else seqs):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        qs, ks, vs, ds = (f64(inp[t][None, :, s0:s1]) for t in ("q", "k", "v", "do"))
+        if sample is None:
+            ref = oracle.bwd(qs, ks, vs, ds, True, scale)
+            got = {"dq": dq[None, :, s0:s1], "dk": dk[None, :, s0:s1], "dv": dv[None, :, s0:s1]}
+        else:
+            rows = ai.sample_rows(n, sample, 60 + b)
+            keys = ai.sample_rows(n, sample, 160 + b)
+            ref = oracle.bwd_sampled(qs, ks, vs, ds, True, scale, rows, keys)
+            got = {"dq": dq[None, :, s0:s1][:, :, rows], "dk": dk[None, :, s0:s1][:, :, keys],
+                   "dv": dv[None, :, s0:s1][:, :, keys]}
+        for key in errs:
+            errs[key] = max(errs[key], excess_err(got[key], ref[key]))
+    assert all(e <= TOL_GRAD for e in errs.values()), f"{tag}: {errs}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("lens", LENGTHS, ids=["-".join(map(str, x)) for x in LENGTHS])
+def test_bwd_lengths(fa, lens, d):
+    """Sequence boundaries inside 32-row waves, 64-key tiles and 128-key
+    workgroups, with empty sequences between them."""
+    inp = make_grad_case(lens, 4, 2, d, seed=sum(lens) % 991 + d)
+    check_bwd(fa, inp, 1.0 / math.sqrt(d), f"lengths {lens}")
+
+
+def test_bwd_many_short(fa):
+    """40 sequences of 1..200 tokens: most tiles cross a boundary."""
+    lens = np.random.default_rng(5).integers(1, 200, size=40)
+    inp = make_grad_case(lens, 4, 2, 128, seed=77)
+    check_bwd(fa, inp, 0.0883883, "many short")
+
+
+def test_bwd_large_logits(fa):
+    inp = ai.make_varlen_case([700, 1300, 90], 4, 4, 128, seed=78)
+    inp["q"] = ai.bf16_round_bits(f64(inp["q"]).astype(np.float32) * 2)
+    inp["k"] = ai.bf16_round_bits(f64(inp["k"]).astype(np.float32) * 2)
+    inp["do"] = ai.normal_bf16(inp["q"].shape, 4078, ai.TENSOR_DO)
+    check_bwd(fa, inp, 0.2, "large logits")
+
+
+def test_bwd_workload_sampled(fa):
+    """The packed workload (16 prompts of 512..16384 tokens) at full size; the
+    shortest and the longest sequence checked on 128 sampled rows and keys."""
+    w = ai.VARLEN_WORKLOADS["varlen_mix"]
+    inp = ai.make_varlen_inputs(w)
+    inp["do"] = ai.normal_bf16(inp["q"].shape, w.cfg_id, ai.TENSOR_DO)
+    lens = inp["lengths"]
+    check_bwd(fa, inp, w.scale, "varlen_mix", seqs=[int(np.argmin(lens)), int(np.argmax(lens))], sample=128)
