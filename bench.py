@@ -50,7 +50,8 @@ import attn_inputs as ai  # noqa: E402
 METRIC = "attention fwd/bwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak"
 WORKLOAD = "gqa16k"
 # MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP per clock per CU.
-PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+RATED_MHZ = 2400.0
+PEAK_BF16_TFLOPS = 256 * RATED_MHZ * 1e6 * 4096 / 1e12
 PEAK_HBM_GBS = 8000.0
 KERNELS = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv")
 
@@ -115,6 +116,60 @@ def measured_traffic(kernel: str, workload: str = WORKLOAD):
             if m and m.group(1) == kernel and m.group(3) == want:
                 return int(m.group(2))
     return None
+
+
+class ClockSampler:
+    """Samples the GPU's current engine clock from sysfs (pp_dpm_sclk, the line
+    marked '*') every `period` seconds on a host thread, between start() and
+    stop(). The rated peak assumes 2.4 GHz; under sustained MFMA load the clock
+    runs lower, and the peak scaled by the sampled mean is the clock-adjusted
+    peak. Returns None where the file is not readable."""
+
+    def __init__(self, period: float = 0.002):
+        import glob
+        import threading
+        self.period = period
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples: list[float] = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for path in self.paths:
+            try:
+                with open(path) as fh:
+                    for line in fh:
+                        if line.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                return float(m.group(1))
+            except OSError:
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            mhz = self._read()
+            if mhz is not None:
+                self.samples.append(mhz)
+            time.sleep(self.period)
+
+    def start(self) -> "ClockSampler":
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        if not self.paths:
+            return None
+        self._stop.set()
+        self._thread.join()
+        if not self.samples:
+            return None
+        xs = self.samples
+        return {"source": "sysfs pp_dpm_sclk (current engine clock), sampled every 2 ms over the timed steps",
+                "mean_mhz": sum(xs) / len(xs), "min_mhz": min(xs), "max_mhz": max(xs), "samples": len(xs),
+                "rated_mhz": RATED_MHZ}
 
 
 def cpu_baseline(w) -> dict:
@@ -512,6 +567,7 @@ def main() -> int:
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
+    clk = ClockSampler().start()
     t0 = time.perf_counter()
     for s in range(args.steps):
         ev[s][0].record(stream)
@@ -520,6 +576,7 @@ def main() -> int:
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock = clk.stop()
 
     ktime = {name: 0.0 for name in KERNELS}
     for s in range(args.steps):
@@ -551,6 +608,10 @@ def main() -> int:
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
                 "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
                 "avg_launch_ms": kavg[dom], "algorithmic_flop_per_launch": amount}
+    # fraction of the peak at the clock the GPU actually ran at (sampled mean)
+    adj = (clock["mean_mhz"] / RATED_MHZ) if clock else None
+    if adj:
+        roofline["frac_clock_adjusted"] = roofline["frac"] / adj
 
     out = {
         "metric": METRIC,
@@ -569,10 +630,13 @@ def main() -> int:
                    "passes": "fwd+bwd"},
         "passes": {
             "fwd": {"ms": fwd_ms, "tflops": fwd_flop / fwd_ms / 1e9,
-                    "frac_of_peak": fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS},
+                    "frac_of_peak": fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS,
+                    "frac_of_clock_adjusted_peak": fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS / adj if adj else None},
             "bwd": {"ms": bwd_ms, "tflops": bwd_flop / bwd_ms / 1e9,
-                    "frac_of_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS},
+                    "frac_of_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS,
+                    "frac_of_clock_adjusted_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS / adj if adj else None},
         },
+        "clock": clock,
         "kernel_ms": kavg,
         "wall_ms_per_step": wall / args.steps * 1e3,
         "roofline": roofline,
