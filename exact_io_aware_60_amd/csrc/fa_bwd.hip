@@ -142,6 +142,20 @@ __device__ __forceinline__ void unmap_block(int bid, int nunits, int& rank, int&
     }
 }
 
+// The same hand-out, unit-major: each XCD takes its units one after another,
+// all ranks of a unit in rank order, so the workgroups an XCD runs side by
+// side belong to one unit and read the same rows through its L2.
+__device__ __forceinline__ void unmap_block_unit_major(int bid, int nunits, int nranks, int& rank, int& unit) {
+    if ((nunits & 7) == 0) {
+        const int x = bid & 7, r = bid >> 3, upx = nunits >> 3;
+        const int u = r / nranks;
+        rank = r - u * nranks;
+        unit = x * upx + u;
+    } else {
+        unmap_block(bid, nunits, rank, unit);
+    }
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
@@ -647,7 +661,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int N = p.N, Np = p.Np, G = p.G;
     const bool causal = p.causal != 0;
     int kt, bkv;
-    unmap_block(blockIdx.x, p.B * p.Hkv, kt, bkv);   // kt = 0 first: the most query rows when causal
+    // kt = 0 first: the most query rows when causal
+    unmap_block_unit_major(blockIdx.x, p.B * p.Hkv, (N + kKV_WG - 1) / kKV_WG, kt, bkv);
     const int b = bkv / p.Hkv, hkv = bkv - b * p.Hkv;
     const int k0 = kt * kKV_WG;
     const int kw0 = k0 + w * kKV_W;
@@ -1065,7 +1080,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     const bool causal = p.causal != 0;
     const int nqt = (N + kQ_WG - 1) / kQ_WG;
     int rank, bh;
-    unmap_block(blockIdx.x, p.B * p.Hq, rank, bh);
+    unmap_block_unit_major(blockIdx.x, p.B * p.Hq, nqt, rank, bh);
     const int qt = causal ? nqt - 1 - rank : rank;   // heaviest first when causal
     const int b = bh / p.Hq, hq = bh - b * p.Hq;
     const size_t bkv = (size_t)b * p.Hkv + hq / p.G;
