@@ -167,7 +167,8 @@ class ClockSampler:
         if not self.samples:
             return None
         xs = self.samples
-        return {"source": "sysfs pp_dpm_sclk (current engine clock), sampled every 2 ms over the timed steps",
+        return {"source": "sysfs pp_dpm_sclk (the power manager's average engine clock), sampled every 2 ms over "
+                          "the timed steps; it reads low when its window holds idle time",
                 "mean_mhz": sum(xs) / len(xs), "min_mhz": min(xs), "max_mhz": max(xs), "samples": len(xs),
                 "rated_mhz": RATED_MHZ}
 
