@@ -279,6 +279,8 @@ class VarlenWorkload:
 VARLEN_WORKLOADS = {
     # a prefill batch of 16 prompts of 512 .. 16384 tokens, with the GQA heads of the gqa16k workload
     "varlen_mix": VarlenWorkload(10, "varlen_mix", 16, 32, 8, 512, 16384, 128),
+    # the same sequences and data without the causal mask (an encoder's packed batch)
+    "varlen_mix_noncausal": VarlenWorkload(10, "varlen_mix_noncausal", 16, 32, 8, 512, 16384, 128, causal=False),
 }
 
 

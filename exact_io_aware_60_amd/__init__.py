@@ -312,7 +312,7 @@ def bwd_window(q, k, v, o, lse, do, window: int, scale: float | None = None, wor
 
 def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None,
                workspace=None):
-    """Backward pass of fwd_varlen (causal): q/o/do [Hq, total, d], k/v [Hkv, total, d], lse [Hq, total].
+    """Backward pass of fwd_varlen (causal or not): q/o/do [Hq, total, d], k/v [Hkv, total, d], lse [Hq, total].
     Returns (dq, dk, dv), bf16, in the same packed layout."""
     import torch
     if q.dim() != 3 or k.dim() != 3:
@@ -327,7 +327,7 @@ def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, causal: bool = 
         raise ValueError("cu_seqlens must be an int32 GPU tensor of shape [B + 1]")
     scale = default_scale(d) if scale is None else scale
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_bytes = bwd_workspace_size(1, Hq, Hkv, total, d, True)
+    ws_bytes = bwd_workspace_size(1, Hq, Hkv, total, d, causal)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
     _check(bwd_varlen_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),

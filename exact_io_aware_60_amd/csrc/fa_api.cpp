@@ -325,9 +325,9 @@ int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const voi
                           int max_seqlen, int total, int Hq, int Hkv, int d, int causal, float scale,
                           void* workspace, size_t workspace_bytes, void* stream) {
     if (!cu_seqlens) return FA_ERR_NULL;
-    if (B < 1 || max_seqlen < 1 || !causal) return FA_ERR_SHAPE;
+    if (B < 1 || max_seqlen < 1) return FA_ERR_SHAPE;
     if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return FA_ERR_ALIGN;
-    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, 1, Hq, Hkv, total, d, 1, scale, workspace,
+    return bwd_common(q, k, v, o, lse, dout, dq, dk, dv, 1, Hq, Hkv, total, d, causal ? 1 : 0, scale, workspace,
                       workspace_bytes, stream, 0, 2, 0, cu_seqlens, B);
 }
 

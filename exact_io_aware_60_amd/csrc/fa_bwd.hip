@@ -562,12 +562,13 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
 
 // A step that crosses the causal diagonal: keys above a row get P = 0. With a
 // bounded mask (WIN: sliding window or packed sequences) so do rows at or past
-// kend, the first row that no longer sees this lane's key. Unpipelined; a few
-// per head and wave.
+// kend, the first row that no longer sees this lane's key, and rows before
+// kbeg, the first row that sees it (packed sequences without the causal mask:
+// its sequence's start). Unpipelined; a few per head and wave.
 template <int D, bool WIN>
 __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict__ st, KvState<D>& S,
                                                const typename KvCfg<D>::Addr& la, int lbase, int q0, int key, float sl2,
-                                               float c1, int hh, int kend) {
+                                               float c1, int hh, bool causal, int kbeg, int kend) {
     using C = KvCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
     f32x16 s[2], dp[2];
@@ -595,7 +596,7 @@ __device__ __forceinline__ void kv_step_masked(const FA_LDS uint8_t* __restrict_
                 const int i = u * 4 + e;
                 const int q = q0 + qb * 32 + u * 8 + hh * 4 + e;
                 float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[e]));
-                if (key > q || (WIN && q >= kend)) x = 0.f;
+                if ((causal && key > q) || (WIN && (q < kbeg || q >= kend))) x = 0.f;
                 s[qb][i] = x;
                 dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[e]);
             }
@@ -641,12 +642,12 @@ __device__ __forceinline__ void kv_iteration(KvState<D>& S, const typename KvCfg
                                              FA_LDS uint8_t* __restrict__ wst,
                                              const FA_LDS uint8_t* __restrict__ rst, int mode, int q0, int key,
                                              const typename KvCfg<D>::Addr& la, int lbase, float sl2, float c1, int w,
-                                             int lane, int kend) {
+                                             int lane, bool causal, int kbeg, int kend) {
     if (issue) kv_copy<D>(pr, pt, rs, nx, wst, w, lane);
     if (mode == 1)
         kv_step<D, false>(rst, S, la, lbase, sl2, c1, nullptr, nullptr);
     else if (mode == 2)
-        kv_step_masked<D, WIN>(rst, S, la, lbase, q0, key, sl2, c1, lane >> 5, kend);
+        kv_step_masked<D, WIN>(rst, S, la, lbase, q0, key, sl2, c1, lane >> 5, causal, kbeg, kend);
 }
 
 template <int D, bool WIN>
@@ -687,10 +688,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // Steps: row blocks from the last one down to qs (rows before the block's
     // first key see none of it under the causal mask), all G heads per block.
-    // With a bounded mask only rows below qe see a key of this workgroup.
+    // With a bounded mask only rows below qe see a key of this workgroup, and
+    // packed sequences without the causal mask start at the first key's
+    // sequence (qs, rounded down to a row block).
     const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
     const int kend = WIN ? bd.row_end(key) : 0;     // this lane's key
-    const int qs = causal ? k0 : 0;
+    const bool lbnd = WIN && !causal;
+    const int kbeg = lbnd ? bd.first_key(key) : 0;  // first row that sees this lane's key
+    const int qs = causal ? k0 : (lbnd ? bd.first_key(k0) / kKV_Q * kKV_Q : 0);
     const int qe = WIN ? min(N, bd.row_end(k0 + kKV_WG - 1)) : N;
     const int nrb = (qe - qs + kKV_Q - 1) / kKV_Q;
     const int nsteps = G * nrb;
@@ -733,23 +738,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     // With a bounded mask the top row blocks t >= tfar (q0 = qs + 64 t) hold
     // rows past some key's reach (the workgroup's first key reaches least far);
     // they come first (jT steps, per wave), and the steady blocks are t in
-    // [2, tfar).
-    const int tfar = WIN ? max(0, bd.row_end(k0) - k0) / kKV_Q : 0;
+    // [tnear, tfar). The bottom blocks t < tnear hold rows before some key's
+    // first row: the causal diagonal (two blocks), or, for packed sequences
+    // without the causal mask, rows before the last key's sequence start.
+    const int tfar = WIN ? max(0, bd.row_end(k0) - qs) / kKV_Q : 0;
+    const int tnear = lbnd ? (max(0, bd.first_key(min(k0 + kKV_WG - 1, N - 1)) - qs) + kKV_Q - 1) / kKV_Q : 2;
     const int nfar = WIN ? max(0, nrb - tfar) : 0;
     const int jT = G * nfar;
-    const int nsteady = WIN ? G * max(0, min(tfar, nrb) - 2)
-                            : (causal ? G * max(0, nrb - 2) : nsteps - 1);   // each has a next step to copy
+    int nsteady = WIN ? G * max(0, min(tfar, nrb) - tnear)
+                      : (causal ? G * max(0, nrb - 2) : nsteps - 1);   // each has a next step to copy
+    if (lbnd) nsteady = min(nsteady, max(0, nsteps - jT - 1));
     const int kend_w0 = WIN ? bd.row_end(kw0) : 0, kend_w31 = WIN ? bd.row_end(kw0 + kKV_W - 1) : 0;
+    const int kbeg_w0 = lbnd ? bd.first_key(kw0) : 0;
+    const int kbeg_w31 = lbnd ? bd.first_key(min(kw0 + kKV_W - 1, N - 1)) : 0;
     auto per_wave_step = [&](int j) {
         const int q0 = qtop - (j / G) * kKV_Q;
-        const bool active = kw0 < N && (!causal || q0 + kKV_Q - 1 >= kw0) && (!WIN || q0 < kend_w31);
+        const bool active = kw0 < N && (!causal || q0 + kKV_Q - 1 >= kw0) && (!WIN || q0 < kend_w31) &&
+                            (!lbnd || q0 + kKV_Q - 1 >= kbeg_w0);
         const int mode = !active ? 0
-                                 : (((causal && q0 < kw0 + kKV_W - 1) || (WIN && q0 + kKV_Q - 1 >= kend_w0)) ? 2 : 1);
+                                 : (((causal && q0 < kw0 + kKV_W - 1) || (WIN && q0 + kKV_Q - 1 >= kend_w0) ||
+                                     (lbnd && q0 < kbeg_w31)) ? 2 : 1);
         const bool issue = j + 1 < nsteps;
         const KvSrc nx = src_of(issue ? j + 1 : j);
         FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
         const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
-        kv_iteration<D, WIN>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, la, lbase, sl2, c1, w, lane, kend);
+        kv_iteration<D, WIN>(S, pr, pt, rs, issue, nx, wst, rst, mode, q0, key, la, lbase, sl2, c1, w, lane, causal,
+                             kbeg, kend);
         wait_vmem();
         __syncthreads();
     };
@@ -983,7 +997,7 @@ __device__ __forceinline__ void dq_drain(QState<D>& S, const FA_LDS uint8_t* __r
 template <int D, bool WIN>
 __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
                                           const typename QCfg<D>::Addr& la, int key0, int qrow, int N, bool causal, float sl2,
-                                          float c1, int hh, int lbq) {
+                                          float c1, int hh, int lbq, int ubq) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
 #pragma unroll
@@ -1004,7 +1018,7 @@ __device__ __forceinline__ void dq_masked(QState<D>& S, const FA_LDS uint8_t* __
         for (int i = 0; i < 16; ++i) {
             const int kk = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
             float x = fast_exp2(fmaf(S.s[kb][i], sl2, -S.l2));
-            if (kk >= N || (causal && kk > qrow) || (WIN && kk < lbq)) x = 0.f;
+            if (kk >= N || (causal && kk > qrow) || (WIN && (kk < lbq || kk >= ubq))) x = 0.f;
             const float dpv = S.dp[kb][i];
             S.dacc = fmaf(x, dpv, S.dacc);
             S.s[kb][i] = x;
@@ -1054,7 +1068,7 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
                                              const FA_LDS uint8_t* __restrict__ cur,
                                              const FA_LDS uint8_t* __restrict__ prv, int j, int jfull,
                                              int jlast, const typename QCfg<D>::Addr& la, int qrow, int N, bool causal,
-                                             float sl2, float c1, int w, int jw0, int jw1, int lbq) {
+                                             float sl2, float c1, int w, int jw0, int jw1, int lbq, int ubq) {
     if (issue) dq_copy<D>(pr, pt, rk, rv, rkt, jn, wst, w);
     if (WIN && j < jw0) return;
     if (j >= jw1 && j < jfull) {
@@ -1063,7 +1077,7 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
     } else {
         if (j == jfull && jfull > jw1) dq_drain<D>(S, prv, la, sl2, c1);
         if (j <= jlast)
-            dq_masked<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1, lbq);
+            dq_masked<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, (threadIdx.x >> 5) & 1, lbq, ubq);
     }
 }
 
@@ -1093,21 +1107,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     const int r0 = q0 + w * kQ_W;
     const int qrow = r0 + l32;                       // < Np: padded rows are zero
     const int ntk = (N + kQ_N - 1) / kQ_N;
-    const int nt = causal ? min(ntk, (q0 + kQ_WG - 1) / kQ_N + 1) : ntk;
     const int nfull = N / kQ_N;                      // key tiles with no key >= N
-    // Tiles [0, jfull) are unmasked for this wave, [jfull, jlast] masked.
-    // jA (wave 0's jfull) <= every wave's jfull: tiles below it run one code
-    // path on all waves. A wave past N runs those too (its rows are zero
-    // padding with P = 0) and then idles.
-    const int jA = causal ? min(nfull, q0 / kQ_N) : nfull;
-    int jfull = causal ? min(nfull, r0 / kQ_N) : nfull;
-    int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ_N) : ntk - 1;
     // Bounded mask (sliding window or packed sequences): tiles before jw0 hold
     // no visible key of the wave, tiles [jw0, jw1) cross its rows' first keys;
     // the loop starts at wave 0's jw0, and the uniform pipelined tiles start
     // after every wave's jw1. A row's first key never decreases along the rows.
+    // Packed sequences without the causal mask also end each row's keys at its
+    // sequence's end (ub, this bound never decreases along the rows either).
     const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
+    const bool ubnd = WIN && !causal;
+    auto ub_of = [&](int r) { return bd.row_end(min(r, N - 1)); };   // keys of row r end before this
+    const int nt = causal ? min(ntk, (q0 + kQ_WG - 1) / kQ_N + 1)
+                          : (ubnd ? max(1, min(ntk, (ub_of(q0 + kQ_WG - 1) + kQ_N - 1) / kQ_N)) : ntk);
+    // Tiles [0, jfull) are unmasked for this wave, [jfull, jlast] masked.
+    // jA (wave 0's jfull) <= every wave's jfull: tiles below it run one code
+    // path on all waves. A wave past N runs those too (its rows are zero
+    // padding with P = 0) and then idles.
+    const int jA = causal ? min(nfull, q0 / kQ_N) : (ubnd ? min(nfull, ub_of(q0) / kQ_N) : nfull);
+    int jfull = causal ? min(nfull, r0 / kQ_N) : (ubnd ? min(nfull, ub_of(r0) / kQ_N) : nfull);
+    int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ_N)
+                       : (ubnd ? min(ntk - 1, max(0, ub_of(r0 + kQ_W - 1) - 1) / kQ_N) : ntk - 1);
     const int lbq = WIN ? bd.first_key(qrow) : 0;   // this lane's row
+    const int ubq = ubnd ? bd.row_end(qrow) : N;
     auto jw1_of = [&](int r) {                       // first tile the wave of rows r.. sees in full
         const int f = bd.first_key(r + kQ_W - 1);
         return f > 0 ? (f + kQ_N - 1) / kQ_N : 0;
@@ -1153,14 +1174,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     // first tiles, where waves start their pipelines: tile 0 without a window
     if constexpr (!WIN) {
         dq_iteration<D, WIN>(S, pr, pt, nt > 1, rk, rv, rkt, 1, st0 + C::STAGE, st0, st0 + 2 * C::STAGE, 0, jfull,
-                             jlast, la, qrow, N, causal, sl2, c1, w, 0, 0, 0);
+                             jlast, la, qrow, N, causal, sl2, c1, w, 0, 0, 0, N);
         wait_vmem();
         __syncthreads();
     } else {
         for (int j = jst; j < min(jU0, nt); ++j) {
             dq_iteration<D, WIN>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, st0 + ((j + 1) % 3) * C::STAGE,
                                  st0 + (j % 3) * C::STAGE, st0 + ((j + 2) % 3) * C::STAGE, j, jfull, jlast, la, qrow,
-                                 N, causal, sl2, c1, w, jw0, jw1, lbq);
+                                 N, causal, sl2, c1, w, jw0, jw1, lbq, ubq);
             wait_vmem();
             __syncthreads();
         }
@@ -1183,7 +1204,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         const FA_LDS uint8_t* cur = st0 + (j % 3) * C::STAGE;
         const FA_LDS uint8_t* prv = st0 + ((j + 2) % 3) * C::STAGE;
         dq_iteration<D, WIN>(S, pr, pt, j + 1 < nt, rk, rv, rkt, j + 1, wst, cur, prv, j, jfull, jlast, la,
-                             qrow, N, causal, sl2, c1, w, jw0, jw1, lbq);
+                             qrow, N, causal, sl2, c1, w, jw0, jw1, lbq, ubq);
         wait_vmem();
         __syncthreads();
     }

@@ -245,17 +245,18 @@ int flash_attn_bwd_window(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward pass of flash_attn_fwd_varlen (causal only): the gradients of
- * sum(dout * O) for packed sequences, every sequence on its own.
+ * Backward pass of flash_attn_fwd_varlen: the gradients of sum(dout * O) for
+ * packed sequences, every sequence on its own.
  *   q, k, v, o, dout, dq, dk, dv   [H, total, d] as in flash_attn_fwd_varlen
  *   lse                            fp32 [Hq, total] from flash_attn_fwd_varlen
  *   cu_seqlens                     int32 [B + 1] device array, as there
- * workspace: flash_attn_bwd_workspace_size(1, Hq, Hkv, total, d, 1) bytes (the
- * packed arrays are one sequence of `total` rows to the preparation and the
- * workspace). causal must be 1 (the non-causal packed backward is not built:
- * FA_ERR_SHAPE). Each row's keys run from its sequence's start to itself, and
- * the gradient kernels read only those, as in flash_attn_bwd_window with a
- * per-row first key. max_seqlen is checked (>= 1) but not otherwise needed.
+ * workspace: flash_attn_bwd_workspace_size(1, Hq, Hkv, total, d, causal) bytes
+ * (the packed arrays are one sequence of `total` rows to the preparation and
+ * the workspace). With causal = 1 each row's keys run from its sequence's
+ * start to itself; with causal = 0, over its whole sequence. The gradient
+ * kernels read only those keys, as in flash_attn_bwd_window with a per-row
+ * first (and, non-causal, last) key. max_seqlen is checked (>= 1) but not
+ * otherwise needed.
  * Offsets are clamped in the kernels as in flash_attn_fwd_varlen.
  */
 int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,

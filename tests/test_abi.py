@@ -267,9 +267,14 @@ def test_bwd_varlen_checks():
     bad = list(args)
     bad[9] = None
     assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_NULL
+    for i in (10, 11):                                     # no sequences; max_seqlen < 1
+        bad = list(args)
+        bad[i] = 0
+        assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_SHAPE
     bad = list(args)
-    bad[16] = 0
-    assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_SHAPE      # the packed backward is causal only
+    bad[16] = 0                                            # non-causal: still checked before any launch
+    bad[9] = None
+    assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_NULL
     bad = list(args)
     bad[9] = P[9] + 2
     assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_ALIGN

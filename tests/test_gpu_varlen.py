@@ -119,7 +119,7 @@ def make_grad_case(lengths, Hq, Hkv, d, seed):
     return inp
 
 
-def check_bwd(fa, inp, scale, tag, seqs=None, sample=None):
+def check_bwd(fa, inp, scale, tag, seqs=None, sample=None, causal=True):
     """GPU forward + backward on the packed batch, then per sequence (all, or
     the listed ones) the oracle's gradients of that sequence alone; `sample`
     rows/keys per sequence when given (sampled oracle), else every element."""
@@ -127,12 +127,12 @@ def check_bwd(fa, inp, scale, tag, seqs=None, sample=None):
     lens, cu = inp["lengths"], inp["cu_seqlens"]
     Hq, total, d = inp["q"].shape
     Hkv = inp["k"].shape[0]
-    say(f"bwd varlen {tag}: B={len(lens)} Hq={Hq} Hkv={Hkv} total={total} d={d}")
+    say(f"bwd varlen {tag}: B={len(lens)} Hq={Hq} Hkv={Hkv} total={total} d={d} causal={causal}")
     q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
     cud = torch.as_tensor(cu).cuda()
     ms = int(max(lens.max(), 1))
-    o, lse = fa.fwd_varlen(q, k, v, cud, ms, causal=True, scale=scale)
-    dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cud, ms, causal=True, scale=scale)
+    o, lse = fa.fwd_varlen(q, k, v, cud, ms, causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cud, ms, causal=causal, scale=scale)
     torch.cuda.synchronize()
     dq, dk, dv = from_dev_bf16(dq), from_dev_bf16(dk), from_dev_bf16(dv)
     errs = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
@@ -143,12 +143,12 @@ def check_bwd(fa, inp, scale, tag, seqs=None, sample=None):
         s0, s1 = int(cu[b]), int(cu[b + 1])
         qs, ks, vs, ds = (f64(inp[t][None, :, s0:s1]) for t in ("q", "k", "v", "do"))
         if sample is None:
-            ref = oracle.bwd(qs, ks, vs, ds, True, scale)
+            ref = oracle.bwd(qs, ks, vs, ds, causal, scale)
             got = {"dq": dq[None, :, s0:s1], "dk": dk[None, :, s0:s1], "dv": dv[None, :, s0:s1]}
         else:
             rows = ai.sample_rows(n, sample, 60 + b)
             keys = ai.sample_rows(n, sample, 160 + b)
-            ref = oracle.bwd_sampled(qs, ks, vs, ds, True, scale, rows, keys)
+            ref = oracle.bwd_sampled(qs, ks, vs, ds, causal, scale, rows, keys)
             got = {"dq": dq[None, :, s0:s1][:, :, rows], "dk": dk[None, :, s0:s1][:, :, keys],
                    "dv": dv[None, :, s0:s1][:, :, keys]}
         for key in errs:
@@ -156,35 +156,68 @@ def check_bwd(fa, inp, scale, tag, seqs=None, sample=None):
     assert all(e <= TOL_GRAD for e in errs.values()), f"{tag}: {errs}"
 
 
+@pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("lens", LENGTHS, ids=["-".join(map(str, x)) for x in LENGTHS])
-def test_bwd_lengths(fa, lens, d):
+def test_bwd_lengths(fa, lens, d, causal):
     """Sequence boundaries inside 32-row waves, 64-key tiles and 128-key
     workgroups, with empty sequences between them."""
-    inp = make_grad_case(lens, 4, 2, d, seed=sum(lens) % 991 + d)
-    check_bwd(fa, inp, 1.0 / math.sqrt(d), f"lengths {lens}")
+    inp = make_grad_case(lens, 4, 2, d, seed=sum(lens) % 991 + d + 3 * int(not causal))
+    check_bwd(fa, inp, 1.0 / math.sqrt(d), f"lengths {lens}", causal=causal)
 
 
-def test_bwd_many_short(fa):
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_many_short(fa, causal):
     """40 sequences of 1..200 tokens: most tiles cross a boundary."""
     lens = np.random.default_rng(5).integers(1, 200, size=40)
     inp = make_grad_case(lens, 4, 2, 128, seed=77)
-    check_bwd(fa, inp, 0.0883883, "many short")
+    check_bwd(fa, inp, 0.0883883, "many short", causal=causal)
 
 
-def test_bwd_large_logits(fa):
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_large_logits(fa, causal):
     inp = ai.make_varlen_case([700, 1300, 90], 4, 4, 128, seed=78)
     inp["q"] = ai.bf16_round_bits(f64(inp["q"]).astype(np.float32) * 2)
     inp["k"] = ai.bf16_round_bits(f64(inp["k"]).astype(np.float32) * 2)
     inp["do"] = ai.normal_bf16(inp["q"].shape, 4078, ai.TENSOR_DO)
-    check_bwd(fa, inp, 0.2, "large logits")
+    check_bwd(fa, inp, 0.2, "large logits", causal=causal)
 
 
-def test_bwd_workload_sampled(fa):
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_workload_sampled(fa, causal):
     """The packed workload (16 prompts of 512..16384 tokens) at full size; the
     shortest and the longest sequence checked on 128 sampled rows and keys."""
     w = ai.VARLEN_WORKLOADS["varlen_mix"]
     inp = ai.make_varlen_inputs(w)
     inp["do"] = ai.normal_bf16(inp["q"].shape, w.cfg_id, ai.TENSOR_DO)
     lens = inp["lengths"]
-    check_bwd(fa, inp, w.scale, "varlen_mix", seqs=[int(np.argmin(lens)), int(np.argmax(lens))], sample=128)
+    check_bwd(fa, inp, w.scale, "varlen_mix", seqs=[int(np.argmin(lens)), int(np.argmax(lens))], sample=128,
+              causal=causal)
+
+
+def test_bwd_noncausal_equal_lengths_match_fixed(fa):
+    """Equal lengths without the causal mask: the packed backward and the
+    fixed-length non-causal backward (a separate kernel instantiation, itself
+    checked against the oracle) agree within the gradient tolerance."""
+    import torch
+    B, Hq, Hkv, N, d = 3, 4, 2, 320, 128
+    inp = make_grad_case([N] * B, Hq, Hkv, d, seed=91)
+    say(f"bwd varlen equal lengths vs fixed, non-causal: B={B} N={N}")
+    q, k, v, do = (to_dev(inp[t]) for t in ("q", "k", "v", "do"))
+    cud = torch.as_tensor(inp["cu_seqlens"]).cuda()
+    o, lse = fa.fwd_varlen(q, k, v, cud, N, causal=False, scale=0.0883883)
+    dq, dk, dv = fa.bwd_varlen(q, k, v, o, lse, do, cud, N, causal=False, scale=0.0883883)
+
+    def fixed(t):   # [H, B*N, d] -> [B, H, N, d]
+        return t.reshape(t.shape[0], B, N, *t.shape[2:]).transpose(0, 1).contiguous()
+
+    def packed(t):  # [B, H, N, d] -> [H, B*N, d]
+        return t.transpose(0, 1).reshape(t.shape[1], B * N, *t.shape[3:]).contiguous()
+
+    fq, fk, fv, fdo = fixed(q), fixed(k), fixed(v), fixed(do)
+    fo, flse = fa.fwd(fq, fk, fv, causal=False, scale=0.0883883)
+    gq, gk, gv = fa.bwd(fq, fk, fv, fo, flse, fdo, causal=False, scale=0.0883883)
+    torch.cuda.synchronize()
+    for a, b_, name in ((dq, packed(gq), "dq"), (dk, packed(gk), "dk"), (dv, packed(gv), "dv")):
+        err = (a.float() - b_.float()).abs().max().item()
+        assert err <= 2e-2, f"{name}: {err}"
