@@ -176,26 +176,32 @@ class ClockSampler:
 def cpu_baseline(w) -> dict:
     """The fp64 oracle timed on the host cores on a bounded sample: the first
     (batch, K/V head) group (its G query heads) restricted to the first
-    `n` positions, forward and backward. Under the causal mask that prefix is a
-    self-contained problem of the same shape family."""
+    `n` positions, forward and backward (forward alone for a workload without
+    a backward pass). Under the causal mask that prefix is a self-contained
+    problem of the same shape family."""
     import oracle
-    n = int(os.environ.get("BENCH_CPU_SAMPLE_N", "13312"))
+    fwd_only = not w.backward
+    n = int(os.environ.get("BENCH_CPU_SAMPLE_N", "32768" if fwd_only else "13312"))
     n = min(n, w.N)
     inp = ai.make_inputs(w)
     G = w.G
     q = ai.bf16_bits_to_f64(inp["q"][0:1, 0:G, :n])
     k = ai.bf16_bits_to_f64(inp["k"][0:1, 0:1, :n])
     v = ai.bf16_bits_to_f64(inp["v"][0:1, 0:1, :n])
-    do = ai.bf16_bits_to_f64(inp["do"][0:1, 0:G, :n])
+    do = None if fwd_only else ai.bf16_bits_to_f64(inp["do"][0:1, 0:G, :n])
+    del inp
     orc = oracle.default()
     t0 = time.perf_counter()
     orc.fwd(q, k, v, w.causal, w.scale)
-    orc.bwd(q, k, v, do, w.causal, w.scale)
+    if not fwd_only:
+        orc.bwd(q, k, v, do, w.causal, w.scale)
     dt = time.perf_counter() - t0
-    flop = 3.5 * 4 * G * n * n / (2.0 if w.causal else 1.0) * w.d
+    flop = (1.0 if fwd_only else 3.5) * 4 * G * n * n / (2.0 if w.causal else 1.0) * w.d
+    passes = "forward" if fwd_only else "forward + backward"
+    prefix = "causal prefix" if w.causal else "prefix"
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"fp64 forward + backward of batch 0, K/V head 0 ({G} query heads), first {n} of "
-                      f"{w.N} positions (causal prefix); {dt:.1f} s",
+            "sample": f"fp64 {passes} of batch 0, K/V head 0 ({G} query heads), first {n} of "
+                      f"{w.N} positions ({prefix}); {dt:.1f} s",
             "seconds": dt}
 
 
@@ -502,6 +508,9 @@ def main() -> int:
                     help="measure the decode path on this workload instead of the forward + backward step")
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="measure the gqa16k forward under a sliding-window causal mask of W keys instead")
+    ap.add_argument("--workload", choices=sorted(ai.WORKLOADS), default=WORKLOAD,
+                    help="the fixed-length workload of the step (default gqa16k); workloads without a backward "
+                         "pass time the forward alone")
     ap.add_argument("--varlen", choices=sorted(ai.VARLEN_WORKLOADS), default=None,
                     help="measure the forward pass over this packed variable-length workload instead")
     args = ap.parse_args()
@@ -535,19 +544,25 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     fa.lib()
-    w = ai.WORKLOADS[WORKLOAD]
+    w = ai.WORKLOADS[args.workload]
+    nk = 4 if w.backward else 1          # launches per step: fwd (+ bwd preparation, dQ, dK/dV)
     B, Hq, Hkv, N, d = w.B, w.Hq, w.Hkv, w.N, w.d
     inp = ai.make_inputs(w)
 
     def dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
-    q, k, v, do = dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["do"])
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    do = dev(inp["do"]) if w.backward else torch.empty_like(q)
     del inp
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws_bytes = fa.bwd_workspace_size(B, Hq, Hkv, N, d, w.causal)
+    if w.backward:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws_bytes = fa.bwd_workspace_size(B, Hq, Hkv, N, d, w.causal)
+    else:
+        dq = dk = dv = o                 # never written: the step is the forward alone
+        ws_bytes = 256
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -562,33 +577,33 @@ def main() -> int:
             raise RuntimeError(f"{KERNELS[i]}: {fa.strerror(st)}")
 
     for _ in range(args.warmup):
-        for i in range(4):
+        for i in range(nk):
             call(i)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     clk = ClockSampler().start()
     t0 = time.perf_counter()
     for s in range(args.steps):
         ev[s][0].record(stream)
-        for i in range(4):
+        for i in range(nk):
             call(i)
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     clock = clk.stop()
 
-    ktime = {name: 0.0 for name in KERNELS}
+    ktime = {name: 0.0 for name in KERNELS[:nk]}
     for s in range(args.steps):
-        for i, name in enumerate(KERNELS):
+        for i, name in enumerate(KERNELS[:nk]):
             ktime[name] += ev[s][i].elapsed_time(ev[s][i + 1])
     kavg = {name: t / args.steps for name, t in ktime.items()}
-    step_ms = sum(ev[s][0].elapsed_time(ev[s][4]) for s in range(args.steps)) / args.steps
+    step_ms = sum(ev[s][0].elapsed_time(ev[s][nk]) for s in range(args.steps)) / args.steps
     fwd_flop = 4.0 * B * Hq * N * N * d / (2.0 if w.causal else 1.0)
-    bwd_flop = 2.5 * fwd_flop
+    bwd_flop = 2.5 * fwd_flop if w.backward else 0.0
     fwd_ms = kavg["fwd"]
-    bwd_ms = kavg["bwd_pre"] + kavg["bwd_dkdv"] + kavg["bwd_dq"]
+    bwd_ms = kavg["bwd_pre"] + kavg["bwd_dkdv"] + kavg["bwd_dq"] if w.backward else None
     value = (fwd_flop + bwd_flop) / step_ms / 1e9
 
     if args.copy_calibration > 0:
@@ -602,11 +617,11 @@ def main() -> int:
         del src, dst
 
     alg = algorithmic(w)
-    dom = max(("fwd", "bwd_dkdv", "bwd_dq"), key=lambda n: kavg[n])
+    dom = max(("fwd", "bwd_dkdv", "bwd_dq")[:3 if w.backward else 1], key=lambda n: kavg[n])
     kind, amount = alg[dom]
     achieved = amount / (kavg[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom, w.name),
                 "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
                 "avg_launch_ms": kavg[dom], "algorithmic_flop_per_launch": amount}
     # fraction of the peak at the clock the GPU actually ran at (sampled mean)
@@ -628,14 +643,15 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": w.causal,
-                   "passes": "fwd+bwd"},
+                   "passes": "fwd+bwd" if w.backward else "fwd"},
         "passes": {
             "fwd": {"ms": fwd_ms, "tflops": fwd_flop / fwd_ms / 1e9,
                     "frac_of_peak": fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS,
                     "frac_of_clock_adjusted_peak": fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS / adj if adj else None},
-            "bwd": {"ms": bwd_ms, "tflops": bwd_flop / bwd_ms / 1e9,
-                    "frac_of_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS,
-                    "frac_of_clock_adjusted_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS / adj if adj else None},
+            "bwd": None if not w.backward else {
+                "ms": bwd_ms, "tflops": bwd_flop / bwd_ms / 1e9,
+                "frac_of_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS,
+                "frac_of_clock_adjusted_peak": bwd_flop / bwd_ms / 1e9 / PEAK_BF16_TFLOPS / adj if adj else None},
         },
         "clock": clock,
         "kernel_ms": kavg,
