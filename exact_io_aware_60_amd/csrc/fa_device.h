@@ -201,6 +201,9 @@ struct CopyPlan {
 // ---- swizzled LDS tiles ----
 // A swizzled tile stores a [ROWS x L bytes] 16-bit tile densely (row r at byte
 // r * L) and puts 16-byte chunk c of row r at chunk position c ^ key(r):
+//   L = 512 (32 chunks): key(r) = r & 15 (two bank lines per row: chunk c sits
+//                        in bank group c % 16 of its line whatever the row, so
+//                        the key alone spreads 16 rows over the 16 groups);
 //   L = 256 (16 chunks): key(r) = r & 15;
 //   L = 128 (8 chunks):  key(r) = (r >> 1) & 7.
 // A 16-byte row read in which 16 lanes take 16 consecutive rows (starting at a
@@ -213,21 +216,22 @@ struct CopyPlan {
 // bytes and splits evenly over 4 or 8 waves.
 template <int L>
 __host__ __device__ constexpr int swz_key(int r) {
-    static_assert(L == 256 || L == 128, "swizzled rows are 128 or 256 bytes");
-    return L == 256 ? (r & 15) : ((r >> 1) & 7);
+    static_assert(L == 512 || L == 256 || L == 128, "swizzled rows are 128, 256 or 512 bytes");
+    return L >= 256 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // The same for tiles read with ds_read_b64_tr_b16, where 32 lanes read 4
 // consecutive rows (starting at a multiple of 4) x 64 bytes at one column: the
 // 64-byte quarters of a row are permuted instead, quarter q of row r stored at
 // quarter q ^ tr_key(r), so the 4 rows land on the 4 distinct 64-byte quarters
-// of the 256-byte bank line (L = 128: two rows share a line, and the key
+// of the 256-byte bank line (L = 512 likewise: quarter q of any row is in
+// quarter q % 4 of its line; L = 128: two rows share a line, and the key
 // separates the rows of one parity). In 16-byte chunk units the key is
 // tr_key(r) << 2.
 template <int L>
 __host__ __device__ constexpr int tr_key(int r) {
-    static_assert(L == 256 || L == 128, "swizzled rows are 128 or 256 bytes");
-    return L == 256 ? (r & 3) : ((r >> 1) & 1);
+    static_assert(L == 512 || L == 256 || L == 128, "swizzled rows are 128, 256 or 512 bytes");
+    return L >= 256 ? (r & 3) : ((r >> 1) & 1);
 }
 template <int L> struct RowKey { __host__ __device__ static constexpr int key(int r) { return swz_key<L>(r); } };
 template <int L> struct TrKey { __host__ __device__ static constexpr int key(int r) { return tr_key<L>(r) << 2; } };

@@ -50,21 +50,25 @@
 namespace fa {
 namespace {
 
-constexpr int kBM = 256;       // query rows per workgroup
 constexpr int kWM = 32;        // query rows per wave
 constexpr int kBN = 64;        // keys per LDS tile
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr float kSumMax = 256.0f;   // largest partial sum of P accepted without a new reference
 
+// d = 64 and 128: 8 waves, two per SIMD (at most 256 registers each). d = 256:
+// a wave's Q and O alone take 192 registers, so 4 waves, one per SIMD (up to
+// 512 registers), and 128 rows per workgroup; its 3 K + 2 V tiles of 32 KiB
+// fill the 160 KiB of LDS.
 template <int D>
 struct FwdCfg {
     static constexpr int DS = D / 16, DB = D / 32;
+    static constexpr int WAVES = D == 256 ? 4 : 8;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BM = kWM * WAVES;                       // query rows per workgroup
     static constexpr int L = 2 * D;                              // bytes per K / V row
     static constexpr int KT = kBN * L, VT = kBN * L;
     static constexpr int LDS = 3 * KT + 2 * VT;
-    using PlanK = CopyPlanSwz<L, kBN, kWaves, RowKey<L>>;
-    using PlanV = CopyPlanSwz<L, kBN, kWaves, TrKey<L>>;
+    using PlanK = CopyPlanSwz<L, kBN, WAVES, RowKey<L>>;
+    using PlanV = CopyPlanSwz<L, kBN, WAVES, TrKey<L>>;
 };
 
 // Workgroup id -> (rank, bh). Workgroups are handed to the 8 XCDs round-robin,
@@ -263,7 +267,10 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
                                                 float& m, float& l, float sl2, f32x16 (&o)[D / 32],
                                                 u32x4 (&ka)[2], const CP& cp) {
     constexpr int DS = D / 16, DB = D / 32, NF = 2 * DB;
-    constexpr int PPS = 8 / DS;      // packs per phase-1 step
+    // the 8 packs of the current chunk over the DS phase-1 steps: PPS per step,
+    // on every PEVERY-th step (d = 256: one pack every other step)
+    constexpr int PPS = DS <= 8 ? 8 / DS : 1;
+    constexpr int PEVERY = DS <= 8 ? 1 : DS / 8;
     constexpr int EPS = 16 / NF;     // next-chunk registers turned into x per phase-2 step
     static_assert(NF == DS, "one V^T fragment read per phase-1 step");
     u32x4 pp[2];
@@ -289,8 +296,10 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
         if constexpr (r + 2 < DS) a2 = k_frag<D>(Kn, kbase, hn, r + 2);
         vf[r] = v_frag<D>(Vt, vbase, h, r);
         sn = mfma32(a0, qf[r], sn);
+        if constexpr (r % PEVERY == 0) {
 #pragma unroll
-        for (int c = 0; c < PPS; ++c) exp_pack_one(sc, r * PPS + c, ls, pp);
+            for (int c = 0; c < PPS; ++c) exp_pack_one(sc, (r / PEVERY) * PPS + c, ls, pp);
+        }
         cp.template at<r>();
         asm volatile("" : "+v"(ls));
         __builtin_amdgcn_sched_barrier(0);
@@ -419,7 +428,7 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, co
 // the mask of each wave's last chunk, so one instance per head dimension
 // serves both cases.
 template <int D, bool WIN>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p) {
     using C = FwdCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
@@ -430,6 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
     const int w = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5, g = lane >> 4;
     const bool causal = p.causal != 0;
+    constexpr int kBM = C::BM;
     const int nqt = (p.N + kBM - 1) / kBM;
     int rank, bh;
     unmap_block(blockIdx.x, p.B * p.Hq, rank, bh);
@@ -544,29 +554,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(FwdParams p) {
 
 template <int D>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-    const int nqt = (p.N + kBM - 1) / kBM;
+    using C = FwdCfg<D>;
+    const int nqt = (p.N + C::BM - 1) / C::BM;
     const int grid = p.B * p.Hq * nqt;
     if (p.window > 0)
-        hipLaunchKernelGGL((fwd_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, true>), dim3(grid), dim3(C::THREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, false>), dim3(grid), dim3(C::THREADS), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+Geometry geometry_t(int B, int Hq, int N) {
+    using C = FwdCfg<D>;
+    Geometry g;
+    g.block_m = C::BM;
+    g.block_n = kBN;
+    g.threads = C::THREADS;
+    g.grid = B * Hq * ((N + C::BM - 1) / C::BM);
+    g.lds_bytes = C::LDS;
+    return g;
 }
 
 }  // namespace
 
 Geometry fwd_geometry(int B, int Hq, int N, int d, int causal) {
     (void)causal;
-    Geometry g;
-    g.block_m = kBM;
-    g.block_n = kBN;
-    g.threads = kThreads;
-    g.grid = B * Hq * ((N + kBM - 1) / kBM);
-    g.lds_bytes = d == 128 ? FwdCfg<128>::LDS : FwdCfg<64>::LDS;
-    return g;
+    return d == 256 ? geometry_t<256>(B, Hq, N) : d == 128 ? geometry_t<128>(B, Hq, N) : geometry_t<64>(B, Hq, N);
 }
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+    if (p.d == 256) return launch_fwd_t<256>(p, stream);
     return p.d == 128 ? launch_fwd_t<128>(p, stream) : launch_fwd_t<64>(p, stream);
 }
 

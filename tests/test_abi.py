@@ -72,9 +72,20 @@ def test_fwd_shape(over):
     assert fwd_call(**over) == fa.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("d", [0, 16, 32, 63, 96, 129, 256])
+@pytest.mark.parametrize("d", [0, 16, 32, 63, 96, 129, 255, 257, 512])
 def test_fwd_headdim(d):
     assert fwd_call(d=d) == fa.FA_ERR_HEADDIM
+
+
+def test_d256_forward_only():
+    """d = 256 passes the forward passes' shape check (their next check, the
+    scale, is reached) and is refused by the backward and decode."""
+    assert fwd_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
+    assert fwd_call(d=256, o=P[3] + 2) == fa.FA_ERR_ALIGN
+    assert bwd_call(d=256) == fa.FA_ERR_HEADDIM
+    assert dec_call(d=256) == fa.FA_ERR_HEADDIM
+    assert varlen_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
+    assert fa.bwd_workspace_size(1, 4, 2, 128, 256, 1) == 0
 
 
 @pytest.mark.parametrize("scale", [-0.1, float("nan"), float("inf"), float("-inf")])
@@ -243,6 +254,7 @@ def test_window_checks():
     assert call(Hq=3) == fa.FA_ERR_SHAPE
     assert call(d=32) == fa.FA_ERR_HEADDIM
     assert call(scale=-1.0) == fa.FA_ERR_SCALE
+    assert call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert call(lse=P[4] + 4) == fa.FA_ERR_ALIGN
 
 

@@ -54,7 +54,7 @@ def test_tiny_workload(fa):
     check_full(fa, inp, w.causal, w.scale, "tiny")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 3, 17, 63, 64, 65, 255, 256, 257, 300, 700])
 def test_ragged(fa, d, causal, N):
@@ -62,7 +62,7 @@ def test_ragged(fa, d, causal, N):
     check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"ragged N={N} d={d} causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_gqa_small(fa, d):
     inp = ai.make_case(2, 8, 2, 333, d, seed=400 + d, with_grad=False)
     check_full(fa, inp, True, 1.0 / math.sqrt(d), f"gqa d={d}")
@@ -75,11 +75,19 @@ def test_head_count_multiple_of_eight(fa):
     check_full(fa, inp, True, 0.0883883, "heads%8==0")
 
 
-def test_large_logits(fa):
+@pytest.mark.parametrize("d", [128, 256])
+def test_large_logits(fa, d):
     """Scores spread by a factor of 4 on some keys and a larger scale: exercises
     the lazy reference-max rescale."""
-    inp = ai.make_case(1, 4, 4, 1000, 128, seed=5, with_grad=False, dist_scale=2.0)
-    check_full(fa, inp, True, 0.2, "large logits")
+    inp = ai.make_case(1, 4, 4, 1000, d, seed=5 + d, with_grad=False, dist_scale=2.0)
+    check_full(fa, inp, True, 0.2 * math.sqrt(128 / d), f"large logits d={d}")
+
+
+def test_d256_head_count_multiple_of_eight(fa):
+    """d = 256 (four waves, 128-row workgroups) with the XCD-grouped order."""
+    inp = ai.make_case(2, 8, 2, 600, 256, seed=78, with_grad=False)
+    check_full(fa, inp, True, 0.0625, "d=256 heads%8==0")
+    check_full(fa, inp, False, 0.0625, "d=256 heads%8==0 noncausal")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -103,7 +111,7 @@ def test_causal_row_zero(fa):
     assert max_err(lse[:, :, 0], s * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0])) <= TOL_LSE
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_uniform_scale_zero(fa, d):
     """scale = 0: causal O_i is the prefix mean of V and LSE_i = ln(i + 1)."""
     inp = ai.make_case(1, 2, 1, 777, d, seed=13, with_grad=False)
@@ -147,6 +155,15 @@ def test_workload_sampled(fa, name):
     w = ai.WORKLOADS[name]
     inp = ai.make_inputs(w, with_grad=False)
     rows = ai.sample_rows(w.N, 256 if name != "mha2k" else w.N, w.cfg_id)
+    sampled_check(fa, w, inp, rows)
+
+
+def test_d256_full_size_sampled(fa):
+    """d = 256 at a prefill size (B=2, Hq=16, Hkv=4, N=16384, causal) on 128
+    seeded rows of every head."""
+    w = ai.WORKLOADS["gqa16k_d256"]
+    inp = ai.make_inputs(w, with_grad=False)
+    rows = ai.sample_rows(w.N, 128, w.cfg_id)
     sampled_check(fa, w, inp, rows)
 
 

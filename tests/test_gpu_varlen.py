@@ -66,7 +66,7 @@ LENGTHS = [
 ]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("lens", LENGTHS, ids=["-".join(map(str, x)) for x in LENGTHS])
 def test_lengths(fa, lens, causal, d):

@@ -51,7 +51,7 @@ CASES = [(300, W) for W in (1, 2, 31, 32, 33, 100, 300)] + \
         [(1000, W) for W in (64, 255, 256, 257, 999)] + [(2049, 128), (2049, 700)]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("N,W", CASES, ids=[f"N{n}-W{w}" for n, w in CASES])
 def test_windows(fa, N, W, d):
     inp = ai.make_case(1, 2, 2, N, d, seed=N + 3 * W + d, with_grad=False)
