@@ -25,7 +25,8 @@
  * bfloat16, with H = Hq for q/o/dout/dq and H = Hkv for k/v/dk/dv. LSE is
  * contiguous [B, Hq, N] float32 (natural log). There are no stride arguments.
  *
- * Supported shapes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128};
+ * Supported shapes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}, and also
+ * d = 256 in the forward passes (flash_attn_fwd, _fwd_window, _fwd_varlen);
  * B*Hq*N*d < 2^62; (N + 128) * d < 2^31 and (Hq / Hkv) * (N + 128) * d * 2 <
  * 2^32 (32-bit offsets inside one head and one query-head group). scale must
  * be finite and >= 0. Other shapes return an error; there is no fallback path.
@@ -56,7 +57,7 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = -1,      /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow */
-    FA_ERR_HEADDIM = -3,   /* d not in {64, 128} */
+    FA_ERR_HEADDIM = -3,   /* d not in {64, 128} (forward passes: not in {64, 128, 256}) */
     FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned (int32 length arrays: 4-byte) */
     FA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
     FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
