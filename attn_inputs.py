@@ -226,6 +226,8 @@ DECODE_WORKLOADS = {
     "decode_long128k": DecodeWorkload(7, "decode_long128k", 1, 8, 8, 1, 131072, 128),
     "decode_batch64": DecodeWorkload(8, "decode_batch64", 64, 32, 8, 1, 4096, 128),
     "decode_ragged64": DecodeWorkload(9, "decode_ragged64", 64, 32, 8, 1, 8192, 128, ragged=True),
+    # decode_gqa16k's cache bytes at d = 256 (half the heads)
+    "decode_gqa16k_d256": DecodeWorkload(12, "decode_gqa16k_d256", 2, 16, 4, 1, 16384, 256),
 }
 
 

@@ -20,7 +20,8 @@ thread_local char g_hip_text[256] = "";
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Head dimensions: 64 and 128 everywhere; 256 in the forward passes only
-// (forward = true), whose kernel has a 256-wide instance.
+// (forward = true), whose kernel has a 256-wide instance (decode, checked
+// apart, has one too).
 int check_shape(int B, int Hq, int Hkv, int N, int d, bool forward = false) {
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_SHAPE;
@@ -253,7 +254,7 @@ namespace {
 int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
     if (causal && Nq > Nk) return FA_ERR_SHAPE;
     // one K/V head fits a 32-bit buffer range with room for a ragged tile
     if ((long double)Nk * d * 2 >= 2147483648.0L) return FA_ERR_SHAPE;
@@ -338,7 +339,7 @@ const char* flash_attn_strerror(int status) {
         case FA_OK: return "success";
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "unsupported shape: B, Hq, Hkv, N must be >= 1, Hq % Hkv == 0, sizes in range";
-        case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128 (or 256 in the forward passes)";
+        case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128 (or 256 in the forward passes and decode)";
         case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned (int32 length arrays: 4-byte)";
         case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
         case FA_ERR_HIP: return g_hip_text[0] ? g_hip_text : "HIP launch failed";

@@ -58,7 +58,9 @@ struct DecCfg {
     static constexpr int DS = D / 16, DB = D / 32, L = 2 * D;
     static constexpr int KT = kDBN * L;             // one K or V tile
     static constexpr int STAGE = 2 * KT;            // K tile, then V tile
-    static constexpr int NS = D == 128 ? 4 : 8;     // ring stages: 128 KiB of LDS
+    // ring stages: 128 KiB of LDS (d = 256: two stages of 64 KiB, one tile in
+    // flight while one is used)
+    static constexpr int NS = D == 256 ? 2 : D == 128 ? 4 : 8;
     static constexpr int LDS = NS * STAGE;
     using PlanK = CopyPlanSwz<L, kDBN, kDW, RowKey<L>>;
     using PlanV = CopyPlanSwz<L, kDBN, kDW, TrKey<L>>;
@@ -118,6 +120,26 @@ __device__ __forceinline__ u32x4 dec_v_frag(const FA_LDS uint8_t* Vc, int vbase)
     return cat(lds_tr_b64<kc * 16 * L>(a), lds_tr_b64<kc * 16 * L + 8 * L>(a));
 }
 
+// The d = 256 instance reads through the compiler's own LDS loads instead.
+// Its 48 fragment registers per chunk (128 registers) do not fit beside O
+// while asm loads are in flight: an asm load's output counts as written when
+// the statement ends, so the compiler may copy or reuse that register before
+// the data lands. With the builtins the compiler places every wait itself.
+// (With its two-stage ring, each wait for the copy in flight costs little.)
+template <int D>
+__device__ __forceinline__ u32x4 dec_k_frag_b(const FA_LDS uint8_t* Kc, int kbase, int ds) {
+    const uint32_t a = ((uint32_t)(uintptr_t)Kc + (uint32_t)kbase) ^ (uint32_t)(ds << 5);
+    return *reinterpret_cast<const FA_LDS u32x4*>((const FA_LDS uint8_t*)(uintptr_t)a);
+}
+template <int D, int F>
+__device__ __forceinline__ u32x4 dec_v_frag_b(const FA_LDS uint8_t* Vc, int vbase) {
+    constexpr int DB = D / 32, L = 2 * D;
+    constexpr int kc = F / DB, db = F % DB;
+    const uint32_t a = (((uint32_t)(uintptr_t)Vc + (uint32_t)vbase) ^ (uint32_t)(db << 6));
+    const FA_LDS uint8_t* p = (const FA_LDS uint8_t*)(uintptr_t)a;
+    return cat(lds_read_trb(p, kc * 16 * L), lds_read_trb(p, kc * 16 * L + 8 * L));
+}
+
 // One 32-key chunk starting at key0: scores, mask, online softmax, P.V.
 // pos: the lane's row position (keys > pos are invisible); Nk: keys past it
 // are invisible; lo: keys <= lo are invisible (a sliding window; INT_MIN
@@ -129,15 +151,19 @@ __device__ __forceinline__ void dec_chunk(DecWave<D>& st, const FA_LDS uint8_t* 
     constexpr int DS = D / 16, DB = D / 32;
     // All fragment reads go out first: the K reads feed the score MFMAs, the
     // V^T reads land while the softmax runs.
+    constexpr bool ASM = D != 256;
     u32x4 kf[DS], vf[2 * DB];
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) kf[ds] = dec_k_frag(Kc, kbase, ds);
+    for (int ds = 0; ds < DS; ++ds) kf[ds] = ASM ? dec_k_frag(Kc, kbase, ds) : dec_k_frag_b<D>(Kc, kbase, ds);
     static_for<2 * DB>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
-        vf[f] = dec_v_frag<D, f>(Vc, vbase);
+        if constexpr (ASM)
+            vf[f] = dec_v_frag<D, f>(Vc, vbase);
+        else
+            vf[f] = dec_v_frag_b<D, f>(Vc, vbase);
     });
     // K done; the V^T reads (2 per fragment) may still be in flight
-    lds_wait<(4 * DB < 15 ? 4 * DB : 15)>(kf);
+    if constexpr (ASM) lds_wait<(4 * DB < 15 ? 4 * DB : 15)>(kf);
     f32x16 s = zero16();
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) s = mfma32(kf[ds], st.qf[ds], s);
@@ -175,7 +201,7 @@ __device__ __forceinline__ void dec_chunk(DecWave<D>& st, const FA_LDS uint8_t* 
         pp[kc][t] = pack_bf16(p0, p1);
     }
     st.l += ls;
-    lds_wait<0>(vf);
+    if constexpr (ASM) lds_wait<0>(vf);
 #pragma unroll
     for (int f = 0; f < 2 * DB; ++f) st.o[f % DB] = mfma32(vf[f], pp[f / DB], st.o[f % DB]);
 }
@@ -490,6 +516,7 @@ DecPlan dec_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int window) {
 }
 
 hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
+    if (p.d == 256) return launch_decode_t<256>(p, stream);
     return p.d == 128 ? launch_decode_t<128>(p, stream) : launch_decode_t<64>(p, stream);
 }
 

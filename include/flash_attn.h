@@ -26,7 +26,8 @@
  * contiguous [B, Hq, N] float32 (natural log). There are no stride arguments.
  *
  * Supported shapes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}, and also
- * d = 256 in the forward passes (flash_attn_fwd, _fwd_window, _fwd_varlen);
+ * d = 256 in the forward passes (flash_attn_fwd, _fwd_window, _fwd_varlen) and
+ * in flash_attn_decode;
  * B*Hq*N*d < 2^62; (N + 128) * d < 2^31 and (Hq / Hkv) * (N + 128) * d * 2 <
  * 2^32 (32-bit offsets inside one head and one query-head group). scale must
  * be finite and >= 0. Other shapes return an error; there is no fallback path.
@@ -57,7 +58,7 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = -1,      /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow */
-    FA_ERR_HEADDIM = -3,   /* d not in {64, 128} (forward passes: not in {64, 128, 256}) */
+    FA_ERR_HEADDIM = -3,   /* d not in {64, 128} (forward passes, decode: not in {64, 128, 256}) */
     FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned (int32 length arrays: 4-byte) */
     FA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
     FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
@@ -204,7 +205,7 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
  * flash_attn_fwd_window), and only the cache tiles the window covers are
  * read. window = 0: no window. A row that sees no key at all (L_b = 0, or
  * L_b - Nq + i < 0) gets O = 0 and LSE = -inf.
- * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {64, 128}; Nq <= Nk
+ * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {64, 128, 256}; Nq <= Nk
  * when causal; Nk * d * 2 < 2^31 bytes per K/V head. Any Nq is accepted; the path is made
  * for (Hq / Hkv) * Nq <= 128 query rows per K/V head, and larger counts read
  * the cache once per 128 rows. Inputs and outputs must not overlap.

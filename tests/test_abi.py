@@ -78,12 +78,12 @@ def test_fwd_headdim(d):
 
 
 def test_d256_forward_only():
-    """d = 256 passes the forward passes' shape check (their next check, the
-    scale, is reached) and is refused by the backward and decode."""
+    """d = 256 passes the forward passes' and decode's shape checks (their next
+    check, the scale, is reached) and is refused by the backward."""
     assert fwd_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert fwd_call(d=256, o=P[3] + 2) == fa.FA_ERR_ALIGN
     assert bwd_call(d=256) == fa.FA_ERR_HEADDIM
-    assert dec_call(d=256) == fa.FA_ERR_HEADDIM
+    assert dec_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert varlen_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert fa.bwd_workspace_size(1, 4, 2, 128, 256, 1) == 0
 

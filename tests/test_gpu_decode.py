@@ -106,7 +106,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"B{s[0]}Hq{s[1]}Hkv{s[2]}Nq{s[3]}Nk{s[4]}" for s in SHAPES])
 def test_shapes(fa, shape, causal, d):
@@ -120,7 +120,7 @@ def test_more_rows_than_keys_noncausal(fa):
     check(fa, inp, False, 0.0883883, "Nq > Nk")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_single_range_direct_output(fa, d):
     """512 (b, kv-head) groups fill the grid with one range each: no merge."""
     B, Hq, Hkv, Nq, Nk = 64, 16, 8, 1, 200
@@ -183,7 +183,7 @@ def test_deterministic(fa):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_seqlens_ragged(fa, causal, d):
     """Entries with 0, 1, 2, 65 and all cache rows, one past the capacity
@@ -200,7 +200,7 @@ def test_seqlens_many_ranges(fa):
     check_ragged(fa, inp, True, 0.0883883, [150, 8999], "seqlens many ranges")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_seqlens_direct(fa, d):
     """512 groups, one range each (no merge), random lengths including 0."""
     B, Hq, Hkv, Nq, Nk = 64, 16, 8, 1, 300
