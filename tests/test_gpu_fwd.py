@@ -184,3 +184,34 @@ def test_long_context_every_row_uniform(fa):
     err_l = (lse.double() - torch.log(torch.arange(1, w.N + 1, device=v.device, dtype=torch.float64))).abs().max().item()
     assert err_o <= TOL_O, err_o
     assert err_l <= TOL_LSE, err_l
+
+
+def test_long_context_memory_footprint(fa):
+    """O(N d) memory at N = 131072, 8 heads, d = 128: the forward allocates no
+    device memory of its own (free device memory is the same before and after a
+    call), and the tensors in use are Q, K, V, O and LSE, about 1.08 GB, where
+    one bf16 score matrix per head would take 275 GB."""
+    import torch
+    w = ai.WORKLOADS["long128k"]
+    say("fwd long128k memory footprint")
+    q = torch.randn((w.B, w.Hq, w.N, w.d), device="cuda").bfloat16()
+    k = torch.randn((w.B, w.Hkv, w.N, w.d), device="cuda").bfloat16()
+    v = torch.randn((w.B, w.Hkv, w.N, w.d), device="cuda").bfloat16()
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hkv, w.N, w.d,
+            1, w.scale)
+    assert fa.fwd_raw(*args) == 0                  # first call: code objects load
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    torch.cuda.reset_peak_memory_stats()
+    held = torch.cuda.memory_allocated()
+    assert fa.fwd_raw(*args) == 0
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0, (free0, free1)          # no device allocation during the call
+    assert torch.cuda.max_memory_allocated() == held
+    tensors = sum(t.numel() * t.element_size() for t in (q, k, v, o, lse))
+    assert tensors == 4 * w.B * w.Hq * w.N * w.d * 2 + w.B * w.Hq * w.N * 4
+    assert round(tensors / 1e9, 2) == 1.08
+    assert w.B * w.Hq * w.N * w.N * 2 > 250 * tensors
