@@ -533,6 +533,9 @@ def main() -> int:
                     help="measure the decode path on this workload instead of the forward + backward step")
     ap.add_argument("--window", type=int, default=0, metavar="W",
                     help="measure the gqa16k forward under a sliding-window causal mask of W keys instead")
+    ap.add_argument("--flush-mib", type=int, default=0, metavar="MIB",
+                    help="before each timed step, write MIB MiB of scratch memory (outside the step's events), so "
+                         "that no input is still in the last-level cache; default 0: warm")
     ap.add_argument("--workload", choices=sorted(ai.WORKLOADS), default=WORKLOAD,
                     help="the fixed-length workload of the step (default gqa16k); workloads without a backward "
                          "pass time the forward alone")
@@ -607,9 +610,12 @@ def main() -> int:
     torch.cuda.synchronize()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nk + 1)] for _ in range(args.steps)]
+    scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=q.device) if args.flush_mib > 0 else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(s & 0xFF)
         ev[s][0].record(stream)
         for i in range(nk):
             call(i)
@@ -672,7 +678,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": w.causal,
-                   "passes": "fwd+bwd" if w.backward else "fwd"},
+                   "passes": "fwd+bwd" if w.backward else "fwd",
+                   "cache": f"flushed ({args.flush_mib} MiB written before each step)" if args.flush_mib else "warm"},
         "passes": {
             "fwd": {"ms": fwd_ms, "tflops": fwd_flop / fwd_ms / 1e9,
                     "frac_of_peak": fwd_flop / fwd_ms / 1e9 / PEAK_BF16_TFLOPS,
