@@ -195,6 +195,21 @@ def sustained_clock(step, step_ms: float, seconds: float = 1.2):
     return sampler.stop()
 
 
+def host_info() -> dict:
+    """The host the oracle ran on: CPU model, os.cpu_count() and the cores this
+    process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w) -> dict:
     """The fp64 oracle timed on the host cores on a bounded sample: the first
     (batch, K/V head) group (its G query heads) restricted to the first
@@ -222,6 +237,7 @@ def cpu_baseline(w) -> dict:
     passes = "forward" if fwd_only else "forward + backward"
     prefix = "causal prefix" if w.causal else "prefix"
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+            **host_info(),
             "sample": f"fp64 {passes} of batch 0, K/V head 0 ({G} query heads), first {n} of "
                       f"{w.N} positions ({prefix}); {dt:.1f} s",
             "seconds": dt}
@@ -253,6 +269,7 @@ def decode_cpu_baseline(w) -> dict:
         orc.fwd(q, k, v, w.causal, w.scale, qpos=pos if w.causal else None)
         dt += time.perf_counter() - t0
     return {"value": decode_bytes(w) / dt / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+            **host_info(),
             "sample": f"the whole {w.name} step in fp64 (the bytes of its bf16 inputs and outputs per second); "
                       f"{dt:.2f} s", "seconds": dt}
 
