@@ -75,3 +75,23 @@ def test_long_context_footprint():
     assert acc.flash_total_bytes(131072, 128, 8) == 4 * 8 * 131072 * 128 * 2 + 8 * 131072 * 4
     assert round(acc.flash_total_bytes(131072, 128, 8) / 1e9, 2) == 1.08
     assert round(acc.naive_score_bytes(131072, 8) / 1e9) == 275
+
+
+def test_tiny_input_rounding_deviation():
+    """For information (the tiny workload draws its inputs in fp32 and both
+    sides see them rounded to bf16): the fp64 oracle's output moves by about
+    1.7e-3 in O and 1.5e-3 in LSE between the unrounded fp32 draws and the
+    rounded inputs. That is the input rounding itself, not an error of either
+    side. The bounds only check the order of magnitude: half a bf16 ulp
+    (2^-9 relative) on each input."""
+    import numpy as np
+    import attn_inputs as ai
+    import oracle
+    w = ai.WORKLOADS["tiny"]
+    inp = ai.make_inputs(w)
+    f = ai.bf16_bits_to_f64
+    o_r, l_r = oracle.fwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), w.causal, w.scale)
+    o_u, l_u = oracle.fwd(*(inp[t].astype(np.float64) for t in ("q32", "k32", "v32")), w.causal, w.scale)
+    dev_o, dev_l = float(np.abs(o_r - o_u).max()), float(np.abs(l_r - l_u).max())
+    print(f"tiny: oracle deviation from bf16 input rounding: O {dev_o:.2e}, LSE {dev_l:.2e}")
+    assert 1e-4 < dev_o < 1e-2 and 1e-4 < dev_l < 1e-2
