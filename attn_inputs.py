@@ -128,6 +128,8 @@ WORKLOADS = {
     "spiky8k": Workload(2, "spiky8k", 1, 32, 32, 8192, 128, True, True, spike_frac=0.05, spike_factor=4.0),
     "gqa16k": Workload(3, "gqa16k", 2, 32, 8, 16384, 128, True, True, oracle_groups=2),
     "long128k": Workload(4, "long128k", 1, 8, 8, 131072, 128, True, False, oracle_rows=256),
+    # gqa16k's shape and FLOP count with d = 64 (twice the heads), forward and backward
+    "gqa16k_d64": Workload(13, "gqa16k_d64", 2, 64, 16, 16384, 64, True, True, oracle_rows=128),
     # gqa16k's shape and FLOP count with d = 256 (half the query heads), forward only
     "gqa16k_d256": Workload(11, "gqa16k_d256", 2, 16, 4, 16384, 256, True, False, oracle_rows=128),
 }
