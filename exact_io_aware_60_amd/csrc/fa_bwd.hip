@@ -863,12 +863,14 @@ __device__ __forceinline__ void dq_task(QState<D>& S, float sl2, float c1) {
             S.pp[kc][w] = v;
         }
     } else {
+        // dS = P (dP c1 - D): the difference in fp32, the product of the fp16
+        // pair with the P pair already packed for the PK MFMA (v_pk_mul_f16)
         const float dpv = S.dp[h][i];
         S.dacc = fmaf(S.s[h][i], dpv, S.dacc);
-        const float y = S.s[h][i] * fmaf(dpv, c1, -S.dd);
+        const float y = fmaf(dpv, c1, -S.dd);
         S.dp[h][i] = y;
         if constexpr (i & 1) {
-            uint32_t v = pack_f16(S.dp[h][i - 1], y);
+            uint32_t v = mul_f16x2(S.pp[kc][w], pack_f16(S.dp[h][i - 1], y));
             pin(v);
             S.dsp[kc][w] = v;
         }
