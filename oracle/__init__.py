@@ -62,6 +62,15 @@ class Oracle:
         lib.oracle_round_bf16.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [_f64p, _f64p, ctypes.c_int64]
         lib.oracle_num_threads.restype = ctypes.c_int
+        _u8p = ctypes.POINTER(ctypes.c_uint8)
+        _f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_e4m3_decode.restype = ctypes.c_int
+        lib.oracle_e4m3_decode.argtypes = [_u8p, _f64p, ctypes.c_int64]
+        lib.oracle_e4m3_encode.restype = ctypes.c_int
+        lib.oracle_e4m3_encode.argtypes = [_f32p, _u8p, ctypes.c_int64]
+        lib.oracle_quantize_e4m3_blocks.restype = ctypes.c_int
+        lib.oracle_quantize_e4m3_blocks.argtypes = [_f32p, _u8p, _f32p, ctypes.c_int64] + [ctypes.c_int] * 3
+        self._u8p, self._f32p = _u8p, _f32p
         self.lib = lib
 
     @staticmethod
@@ -158,6 +167,51 @@ class Oracle:
         if self.lib.oracle_round_bf16(_ptr(x), _ptr(y), x.size) != 0:
             raise ValueError("oracle_round_bf16 rejected its arguments")
         return y
+
+    # ---- 8-bit floating point with block scales (OCP E4M3; see oracle.c) ----
+
+    def e4m3_decode(self, codes):
+        """float64 values of E4M3 codes (uint8); the NaN codes give NaN."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        y = np.empty(c.shape, dtype=np.float64)
+        if self.lib.oracle_e4m3_decode(c.ctypes.data_as(self._u8p), _ptr(y), c.size) != 0:
+            raise ValueError("oracle_e4m3_decode rejected its arguments")
+        return y
+
+    def e4m3_encode(self, x):
+        """E4M3 codes of float32 values: nearest, ties to even, saturated at 448."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        c = np.empty(x.shape, dtype=np.uint8)
+        if self.lib.oracle_e4m3_encode(x.ctypes.data_as(self._f32p), c.ctypes.data_as(self._u8p), x.size) != 0:
+            raise ValueError("oracle_e4m3_encode rejected its arguments")
+        return c
+
+    def quantize_e4m3(self, x, rows: int):
+        """Block-quantise a float32 [B, H, N, d] tensor, one scale per `rows`
+        rows of each (b, h): returns (codes uint8 [B, H, N, d], scales float32
+        [B, H, ceil(N / rows)]) with x ~ code * scale."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        B, H, N, d = x.shape
+        nb = (N + rows - 1) // rows
+        c = np.empty(x.shape, dtype=np.uint8)
+        sc = np.empty((B, H, nb), dtype=np.float32)
+        rc = self.lib.oracle_quantize_e4m3_blocks(x.ctypes.data_as(self._f32p), c.ctypes.data_as(self._u8p),
+                                                  sc.ctypes.data_as(self._f32p), B * H, N, d, rows)
+        if rc != 0:
+            raise ValueError("oracle_quantize_e4m3_blocks rejected its arguments")
+        return c, sc
+
+    def dequantize_e4m3(self, codes, scales, rows: int):
+        """Exact float64 values code * scale (a 4-bit by 24-bit significand
+        product, exact in float64)."""
+        v = self.e4m3_decode(codes)
+        s = np.repeat(np.asarray(scales, dtype=np.float64), rows, axis=2)[:, :, :v.shape[2]]
+        return v * s[..., None]
+
+    def fwd_e4m3(self, q8, k8, v8, qs, ks, vs, rows: int, causal: bool, scale: float):
+        """The attention definition on the dequantised block-scaled inputs."""
+        return self.fwd(self.dequantize_e4m3(q8, qs, rows), self.dequantize_e4m3(k8, ks, rows),
+                        self.dequantize_e4m3(v8, vs, rows), causal, scale)
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

@@ -44,10 +44,16 @@
  * which models that storage step. When it is clear, D_i uses the exact fp64
  * O_i. Everything else stays exact fp64 in both modes.
  *
+ * 8-bit inputs (test infrastructure for an FP8 forward, which the pages credit
+ * to FlashAttention-3 with block scaling): an E4M3 codec and an fp32 block
+ * quantiser, below. The attention on such inputs is the definition above on
+ * the exactly dequantised values code * scale.
+ *
  * Layout: every tensor is contiguous [B, H, N, d] float64 (d fastest);
  * LSE and D are [B, Hq, N]. Functions return 0, or -1 on bad arguments or
  * allocation failure.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -351,6 +357,89 @@ int oracle_attn_bwd_sampled(const double* q, const double* k, const double* v, c
 int oracle_round_bf16(const double* x, double* y, int64_t n) {
     if ((!x || !y) && n > 0) return -1;
     for (int64_t t = 0; t < n; ++t) y[t] = round_bf16(x[t]);
+    return 0;
+}
+
+/* ---- 8-bit floating point (OCP E4M3, the "fn" variant) and block scaling ----
+ * FlashAttention-3 (Shah et al.) runs the forward in FP8 with block scaling;
+ * the pages fix neither the format nor the scaling, so this follows the OCP
+ * 8-bit floating point definition of E4M3: 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits, no infinities, and one NaN pattern per sign (all
+ * exponent and mantissa bits set). Exponent field 0 holds the subnormals
+ * m * 2^-9. The largest finite magnitude is 1.75 * 2^8 = 448. */
+static double e4m3_value(uint8_t c) {
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double a;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) a = ldexp((double)m, -9);
+    else a = ldexp(8.0 + m, e - 10);          /* (1 + m/8) * 2^(e-7) */
+    return s ? -a : a;
+}
+
+/* x rounded to the nearest E4M3 value, ties to even, magnitudes at or above
+ * 448 saturated to 448 (the reading taken for overflow; block scaling keeps
+ * every scaled value at or below 448 up to one fp32 rounding), NaN to 0x7F. */
+static uint8_t e4m3_code(float xf) {
+    const double x = (double)xf;
+    if (isnan(x)) return 0x7F;
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    const double a = fabs(x);
+    if (a >= 448.0) return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal spacing 2^-9; a count of 8 is the smallest normal, code 8 */
+        return sign | (uint8_t)nearbyint(ldexp(a, 9));
+    }
+    int E;
+    frexp(a, &E);                              /* a = f * 2^E, 0.5 <= f < 1 */
+    int ee = E - 1;                            /* a = (1.x) * 2^ee, ee in [-6, 8] */
+    double q = nearbyint(ldexp(a, 3 - ee));    /* 8 .. 16 eighths */
+    if (q == 16.0) { q = 8.0; ++ee; }
+    return sign | (uint8_t)(((ee + 7) << 3) | ((int)q - 8));
+}
+
+int oracle_e4m3_decode(const uint8_t* c, double* y, int64_t n) {
+    if ((!c || !y) && n > 0) return -1;
+    for (int64_t t = 0; t < n; ++t) y[t] = e4m3_value(c[t]);
+    return 0;
+}
+
+int oracle_e4m3_encode(const float* x, uint8_t* c, int64_t n) {
+    if ((!x || !c) && n > 0) return -1;
+    for (int64_t t = 0; t < n; ++t) c[t] = e4m3_code(x[t]);
+    return 0;
+}
+
+/* Block quantisation of a contiguous [BH, N, d] fp32 tensor: each run of R
+ * rows of one (b, h) slab (the last one ragged) gets one scale. In fp32, as a
+ * kernel would do it: amax = the largest |x| of the block, inv = 448 / amax
+ * (one rounded division), code = E4M3(x * inv) (one rounded product), and the
+ * stored dequantisation scale is amax / 448, so that x ~ code * scale. An
+ * all-zero block gets inv = scale = 1. Scales are [BH, ceil(N / R)]. */
+int oracle_quantize_e4m3_blocks(const float* x, uint8_t* codes, float* scales, int64_t BH, int N,
+                                int d, int R) {
+    if (!x || !codes || !scales || BH < 0 || N < 0 || d <= 0 || R <= 0) return -1;
+    const int nb = (N + R - 1) / R;
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        for (int b = 0; b < nb; ++b) {
+            const int r0 = b * R, r1 = r0 + R < N ? r0 + R : N;
+            const float* xb = x + (bh * N + r0) * (int64_t)d;
+            uint8_t* cb = codes + (bh * N + r0) * (int64_t)d;
+            const int64_t cnt = (int64_t)(r1 - r0) * d;
+            float amax = 0.0f;
+            for (int64_t t = 0; t < cnt; ++t) {
+                const float a = fabsf(xb[t]);
+                if (!(a <= FLT_MAX)) return -2;        /* NaN or infinite input */
+                if (a > amax) amax = a;
+            }
+            volatile float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+            volatile float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            for (int64_t t = 0; t < cnt; ++t) {
+                volatile float y = xb[t] * inv;
+                cb[t] = e4m3_code(y);
+            }
+            scales[bh * nb + b] = sc;
+        }
+    }
     return 0;
 }
 

@@ -571,6 +571,125 @@ def pin_sliding_window_backward(orc):
         _close((fp - fm) / (2 * h), g["d" + name][idx], tol=1e-7, what=f"window FD d{name}")
 
 
+
+# ---- 8-bit inputs: OCP E4M3 codes with fp32 block scales ----
+# The pages credit FlashAttention-3 with an FP8 forward using block scaling
+# (mlapandio "Generations"; wishwiki "FlashAttention", "Legacy and
+# Successors") and fix no format. These pins hold the oracle's E4M3 codec to
+# torch's float8_e4m3fn (an independent library implementation of the same OCP
+# format), to the format's closed forms, and its block quantiser to a
+# brute-force numpy float32 recomputation.
+
+def _torch_e4m3_values(codes):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8).copy()).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_e4m3_codes(x32):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32).copy()).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_codes(orc):
+    """Every code decodes as the library does; closed forms of the format."""
+    c = np.arange(256, dtype=np.uint8)
+    v = orc.e4m3_decode(c)
+    assert np.array_equal(v, _torch_e4m3_values(c), equal_nan=True), "E4M3 decode differs from float8_e4m3fn"
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0, "largest finite E4M3 magnitude is 1.75 * 2^8"
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9, "subnormals are m * 2^-9"
+    assert v[0x08] == 2.0 ** -6 and v[0x38] == 1.0 and v[0x40] == 2.0, "normals are (1 + m/8) 2^(e-7)"
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.isfinite(v).sum() == 254, "one NaN code per sign"
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0), "positive codes increase with their value"
+    assert np.array_equal(v[0x80:0xFF], -pos) and math.copysign(1.0, v[0x80]) < 0, "sign bit mirrors"
+    fin = c[np.isfinite(v)]
+    assert np.array_equal(orc.e4m3_encode(v[np.isfinite(v)].astype(np.float32)), fin), "encode(decode(c)) != c"
+
+
+def pin_e4m3_rounding(orc):
+    """Nearest value with ties to even, saturation at 448, NaN to the NaN code."""
+    v = orc.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mid = ((v[:-1] + v[1:]) / 2).astype(np.float32)           # 5 significant bits: exact in float32
+    assert np.array_equal(mid.astype(np.float64), (v[:-1] + v[1:]) / 2)
+    got = orc.e4m3_encode(mid)
+    lo = np.arange(0x7E, dtype=np.uint8)
+    want = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    assert np.array_equal(got, want), "a tie does not go to the even code"
+    up = np.nextafter(mid, np.float32(np.inf))
+    dn = np.nextafter(mid, np.float32(0))
+    assert np.array_equal(orc.e4m3_encode(up), lo + 1) and np.array_equal(orc.e4m3_encode(dn), lo), "not nearest"
+    rng = _rng(41)
+    x = np.concatenate([rng.standard_normal(20000) * 60, rng.standard_normal(20000) * 2.0 ** -7,
+                        rng.uniform(-464, 464, 20000)]).astype(np.float32)
+    assert np.array_equal(orc.e4m3_encode(x), _torch_e4m3_codes(x)), "encode differs from float8_e4m3fn"
+    big = np.array([448, 464, 480, 500, 1e6, 3e38, np.inf], dtype=np.float32)
+    assert np.all(orc.e4m3_encode(big) == 0x7E) and np.all(orc.e4m3_encode(-big) == 0xFE), "saturation"
+    assert orc.e4m3_encode(np.array([np.nan], dtype=np.float32))[0] & 0x7F == 0x7F, "NaN code"
+    assert orc.e4m3_encode(np.array([-0.0], dtype=np.float32))[0] == 0x80, "negative zero keeps its sign"
+
+
+def pin_e4m3_block_quantiser(orc):
+    """Blocks of rows, one scale each, against a numpy float32 recomputation."""
+    rng = _rng(43)
+    B, H, N, d, R = 2, 3, 300, 16, 128                        # ragged last block of 44 rows
+    x = (rng.standard_normal((B, H, N, d)) * rng.uniform(0.01, 30, (B, H, 1, 1))).astype(np.float32)
+    x[1, 2, 128:256] = 0.0                                     # an all-zero block
+    x[0, 1, 5, 3] = np.float32(1e4)                            # one outlier sets its block's scale
+    codes, scales = orc.quantize_e4m3(x, R)
+    nb = -(-N // R)
+    assert scales.shape == (B, H, nb)
+    for b in range(B):
+        for h in range(H):
+            for j in range(nb):
+                blk = x[b, h, j * R:(j + 1) * R]
+                amax = np.float32(np.abs(blk).max())
+                if amax == 0:
+                    inv, sc = np.float32(1), np.float32(1)
+                else:
+                    inv, sc = np.float32(448) / amax, amax / np.float32(448)
+                assert scales[b, h, j] == sc, f"scale of block {b, h, j}"
+                want = _torch_e4m3_codes((blk * inv).astype(np.float32))
+                assert np.array_equal(codes[b, h, j * R:(j + 1) * R], want), f"codes of block {b, h, j}"
+                if amax > 0:
+                    top = np.abs(blk) == amax
+                    assert np.all(codes[b, h, j * R:(j + 1) * R][top] & 0x7F == 0x7E), "amax maps to 448"
+    deq = orc.dequantize_e4m3(codes, scales, R)
+    assert np.array_equal(deq, _torch_e4m3_values(codes) * np.repeat(scales.astype(np.float64), R, axis=2)[
+        :, :, :N, None]), "dequantisation"
+    s_full = np.repeat(scales.astype(np.float64), R, axis=2)[:, :, :N, None]
+    y = np.abs(x.astype(np.float64)) / s_full
+    normal = y >= 2.0 ** -6
+    err = np.abs(deq - x)
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(x[normal]) * (1 + 1e-6)), "relative error of a normal code"
+    assert np.all(err[~normal] <= 2.0 ** -10 * s_full.repeat(d, axis=3)[~normal] * (1 + 1e-6)), "subnormal error"
+
+
+def pin_e4m3_forward(orc):
+    """The forward on 8-bit inputs is the definition on the dequantised values:
+    constant V codes give O = that value exactly; zero Q codes give the causal
+    prefix mean of the dequantised V with LSE = ln(i + 1)."""
+    rng = _rng(47)
+    B, Hq, Hkv, N, d, R = 1, 4, 2, 200, 32, 64
+    xq = rng.standard_normal((B, Hq, N, d)).astype(np.float32)
+    xk = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    q8, qs = orc.quantize_e4m3(xq, R)
+    k8, ks = orc.quantize_e4m3(xk, R)
+    v8 = np.full((B, Hkv, N, d), 0x3B, dtype=np.uint8)      # 1.375
+    vs = np.full((B, Hkv, -(-N // R)), 0.5, dtype=np.float32)
+    o, lse = orc.fwd_e4m3(q8, k8, v8, qs, ks, vs, R, causal=True, scale=d ** -0.5)
+    assert np.max(np.abs(o - 0.6875)) <= TOL, "constant V"
+    xv = rng.standard_normal((B, Hkv, N, d)).astype(np.float32)
+    v8, vs = orc.quantize_e4m3(xv, R)
+    o, lse = orc.fwd_e4m3(np.zeros_like(q8), k8, v8, qs, ks, vs, R, causal=True, scale=d ** -0.5)
+    vd = _torch_e4m3_values(v8) * np.repeat(vs.astype(np.float64), R, axis=2)[:, :, :N, None]
+    cnt = np.arange(1, N + 1, dtype=np.float64)
+    prefix = np.cumsum(vd, axis=2) / cnt[None, None, :, None]
+    assert np.max(np.abs(o - np.repeat(prefix, Hq // Hkv, axis=1))) <= 1e-12, "zero Q: prefix mean"
+    assert np.max(np.abs(lse - np.log(cnt))) <= 1e-12, "zero Q: LSE = ln(i + 1)"
+
+
 PINS = [
     pin_one_token,
     pin_two_tokens,
@@ -595,4 +714,8 @@ PINS = [
     pin_split_merge,
     pin_sliding_window,
     pin_sliding_window_backward,
+    pin_e4m3_codes,
+    pin_e4m3_rounding,
+    pin_e4m3_block_quantiser,
+    pin_e4m3_forward,
 ]

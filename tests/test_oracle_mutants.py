@@ -43,6 +43,14 @@ MUTANTS = {
     "stored O not rounded": ("ostore[c] = o_bf16 ? round_bf16(oi[c]) : oi[c];", "ostore[c] = oi[c];"),
     "stored O rounded to 9 bits": ("ldexp(nearbyint(ldexp(m, 8)), e - 8)", "ldexp(nearbyint(ldexp(m, 9)), e - 9)"),
     "stored O rounding truncates": ("ldexp(nearbyint(ldexp(m, 8)), e - 8)", "ldexp(trunc(ldexp(m, 8)), e - 8)"),
+    "e4m3 exponent bias 8": ("ldexp(8.0 + m, e - 10)", "ldexp(8.0 + m, e - 11)"),
+    "e4m3 subnormal spacing": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "e4m3 encode truncates": ("double q = nearbyint(ldexp(a, 3 - ee));", "double q = floor(ldexp(a, 3 - ee));"),
+    "e4m3 overflow to NaN": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
+    "e4m3 sign dropped": ("const uint8_t sign = signbit(x) ? 0x80 : 0;", "const uint8_t sign = 0;"),
+    "e4m3 subnormal rounding truncates": ("return sign | (uint8_t)nearbyint(ldexp(a, 9));", "return sign | (uint8_t)trunc(ldexp(a, 9));"),
+    "quantiser stores the inverse scale": ("volatile float sc = amax > 0.0f ? amax / 448.0f : 1.0f;", "volatile float sc = amax > 0.0f ? 448.0f / amax : 1.0f;"),
+    "quantiser amax of the first row": ("for (int64_t t = 0; t < cnt; ++t) {\n                const float a = fabsf(xb[t]);", "for (int64_t t = 0; t < d; ++t) {\n                const float a = fabsf(xb[t]);"),
     "bwd reduction drops a thread": ("for (int t = 0; t < nt; ++t) {\n                const double* dk_t", "for (int t = 1; t < nt; ++t) {\n                const double* dk_t"),
 }
 
