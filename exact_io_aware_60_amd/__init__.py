@@ -26,7 +26,8 @@ FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
             "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
             "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen",
-            "flash_attn_fwd_window", "flash_attn_bwd_window", "flash_attn_bwd_varlen")
+            "flash_attn_fwd_window", "flash_attn_bwd_window", "flash_attn_bwd_varlen",
+            "flash_attn_quantize_e4m3")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_decode.argtypes = [_vp] * 6 + [_i] * 8 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
         L.flash_attn_decode_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_decode_workspace_size.argtypes = [_i] * 8
+        L.flash_attn_quantize_e4m3.restype = _i
+        L.flash_attn_quantize_e4m3.argtypes = [_vp] * 3 + [_i] * 4 + [_vp]
         L.flash_attn_strerror.restype = ctypes.c_char_p
         L.flash_attn_strerror.argtypes = [_i]
         L.flash_attn_version.restype = ctypes.c_char_p
@@ -144,6 +147,11 @@ def decode_raw(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, scale,
     """flash_attn_decode on raw addresses (ints; seqlens_k may be None); returns the status code."""
     return lib().flash_attn_decode(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, int(causal), int(window),
                                    float(scale), workspace, workspace_bytes, stream)
+
+
+def quantize_e4m3_raw(x, codes, scales, BH, N, d, rows, stream=None) -> int:
+    """flash_attn_quantize_e4m3 on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_quantize_e4m3(x, codes, scales, BH, N, d, rows, stream)
 
 
 def decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window: int = 0) -> int:
@@ -335,3 +343,23 @@ def bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, causal: bool = 
                           int(max_seqlen), total, Hq, Hkv, d, causal, scale, workspace.data_ptr(),
                           workspace.numel() * workspace.element_size(), _stream(q)))
     return dq, dk, dv
+
+
+def quantize_e4m3(x, rows: int = 128):
+    """Block-quantise a contiguous bf16 [..., N, d] GPU tensor to OCP E4M3 codes
+    with one fp32 scale per run of `rows` rows of each leading slab (the last
+    run ragged): returns (codes uint8 [..., N, d], scales float32
+    [..., ceil(N / rows)]) with x ~ code * scale. See flash_attn_quantize_e4m3."""
+    import torch
+    _checked(x, "x")
+    if x.dim() < 2:
+        raise ValueError("x must be [..., N, d]")
+    N, d = x.shape[-2], x.shape[-1]
+    BH = x.numel() // max(N * d, 1)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    rows = int(rows)
+    nruns = -(-N // rows) if rows > 0 else 1          # rows < 1 is rejected by the library
+    scales = torch.empty((*x.shape[:-2], nruns), dtype=torch.float32, device=x.device)
+    _check(quantize_e4m3_raw(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), BH, N, d, rows,
+                             torch.cuda.current_stream().cuda_stream))
+    return codes, scales

@@ -13,6 +13,14 @@
 #include "../../include/flash_attn.h"
 #include "fa_params.h"
 
+namespace fa {
+// fa_quant.hip: block E4M3 quantisation of a bf16 [BH, N, d] tensor (d a
+// multiple of 8) into codes [BH, N, d] and one fp32 scale per run of `rows`
+// rows, [BH, ceil(N / rows)].
+hipError_t launch_quant_e4m3(const void* x, void* codes, float* scales, int BH, int N, int d, int rows,
+                             hipStream_t stream);
+}  // namespace fa
+
 namespace {
 
 thread_local char g_hip_text[256] = "";
@@ -312,6 +320,21 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
     p.tps = pl.tps;
     p.pair = pl.pair;
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_quantize_e4m3(const void* x, void* codes, float* scales, int BH, int N, int d, int rows,
+                             void* stream) {
+    if (!x || !codes || !scales) return FA_ERR_NULL;
+    if (BH < 1 || N < 1 || rows < 1) return FA_ERR_SHAPE;
+    if (d < 8 || d % 8 != 0) return FA_ERR_HEADDIM;
+    if (!aligned16(x) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+        return FA_ERR_ALIGN;
+    // one workgroup per run; a run's element count and the grid are 32-bit
+    const long long runs = (N + (long long)rows - 1) / rows;
+    if ((long double)BH * runs >= 2147483647.0L) return FA_ERR_SHAPE;
+    if ((long double)std::min(rows, N) * d >= 2147483647.0L) return FA_ERR_SHAPE;
+    if ((long double)BH * N * d >= 4.0e18L) return FA_ERR_SHAPE;
+    return hip_status(fa::launch_quant_e4m3(x, codes, scales, BH, N, d, rows, static_cast<hipStream_t>(stream)));
 }
 
 int flash_attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -267,6 +267,29 @@ int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const voi
                           int d, int causal, float scale, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Block quantisation of a bf16 tensor to 8-bit floating point codes, the input
+ * form of an FP8 forward. FlashAttention-3 runs its forward in FP8 with block
+ * scaling (mlapandio "FlashAttention: IO-aware exact attention", Generations;
+ * wishwiki "FlashAttention", Legacy and Successors); the pages fix no format.
+ *
+ *   x       bf16 [BH, N, d] contiguous (e.g. [B, H, N, d] with BH = B * H),
+ *           finite values (a NaN or infinity gives unspecified codes for its run)
+ *   codes   uint8 [BH, N, d]: OCP E4M3 codes (bias 7, 3 mantissa bits, no
+ *           infinities, largest finite 448; 0x7F / 0xFF are NaN and never written)
+ *   scales  fp32 [BH, ceil(N / rows)]: one per run of `rows` rows of a slab,
+ *           the last run of a slab ragged
+ *
+ * Per run, in fp32: amax = max |x|, inv = 448 / amax, code = E4M3(x * inv)
+ * rounded to nearest (ties to even) and saturated at 448, scale = amax / 448
+ * (both divisions correctly rounded); an all-zero run gets scale 1. Then
+ * x ~ code * scale, within 2^-4 relative for codes of magnitude >= 2^-6.
+ * d: a multiple of 8; rows >= 1. x and codes 16-byte aligned, scales 4-byte.
+ * The caller owns every buffer; the call is asynchronous on `stream`.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (BH, N, rows < 1, or the run count or the
+ * size beyond the 32-bit grid), FA_ERR_HEADDIM (d), FA_ERR_ALIGN, FA_ERR_HIP. */
+int flash_attn_quantize_e4m3(const void* x, void* codes, float* scales, int BH, int N, int d, int rows,
+                             void* stream);
+
 /* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
