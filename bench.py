@@ -52,6 +52,14 @@ WORKLOAD = "gqa16k"
 # MI355X dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP per clock per CU.
 RATED_MHZ = 2400.0
 PEAK_BF16_TFLOPS = 256 * RATED_MHZ * 1e6 * 4096 / 1e12
+# What the timed step computes in: bf16 tensors in and out, bf16 MFMA operands in
+# the forward, fp16 MFMA operands (power-of-two scaled copies of the bf16 inputs,
+# P and dS rounded to fp16) in the backward, fp32 accumulation and softmax.
+DTYPE_FWD_BWD = "bf16 fwd / fp16-operand bwd"
+PRECISION = {"io": "bf16 (LSE fp32)", "fwd_mfma": "bf16 x bf16 -> fp32",
+             "bwd_mfma": "fp16 x fp16 -> fp32 (scaled copies of the bf16 inputs; P, dS in fp16)",
+             "softmax": "fp32"}
+PRECISION_FWD = {"io": "bf16 (LSE fp32)", "fwd_mfma": "bf16 x bf16 -> fp32", "softmax": "fp32"}
 PEAK_HBM_GBS = 8000.0
 KERNELS = ("fwd", "bwd_pre", "bwd_dq", "bwd_dkdv")
 
@@ -432,7 +440,8 @@ def window_main(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_FWD_BWD,
+        "precision": PRECISION,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "window": W,
                    "passes": "fwd+bwd (sliding window)"},
@@ -520,7 +529,8 @@ def varlen_main(args) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_FWD_BWD,
+        "precision": PRECISION,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "total": total, "max_seqlen": ms,
                    "min_len": int(lens.min()), "d": w.d, "causal": w.causal, "passes": "fwd+bwd (packed sequences)"},
@@ -692,7 +702,8 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_FWD_BWD if w.backward else "bf16",
+        "precision": PRECISION if w.backward else PRECISION_FWD,
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": Hkv, "N": N, "d": d, "causal": w.causal,
                    "passes": "fwd+bwd" if w.backward else "fwd",

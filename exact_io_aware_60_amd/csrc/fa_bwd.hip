@@ -17,9 +17,15 @@
 // MFMA operands. fp16 keeps 11 significant bits where bf16 keeps 8, at the same
 // MFMA rate, so rounding P and dS costs 8x less accuracy. A first kernel finds
 // max |x| of q, k, v and dout. The preparation kernel then writes fp16 copies
-// of them scaled by powers of two (max |x| * scale lies in [2^13, 2^14)), so
-// every bf16 value converts exactly. It also derives a scale for dS from the
-// bound |dS_ij| <= 2 d max|dO| max|V|. The scales are undone in fp32 in each
+// of them scaled by powers of two (max |x| * scale lies in [2^13, 2^14)). A
+// bf16 value x converts exactly when |x| >= 2^-30 max |x| of its tensor (its
+// scaled value then keeps 8 significant bits above fp16's subnormal spacing
+// 2^-24); smaller values become fp16 subnormals or zero, off by at most
+// 2^-38 max |x|. It also derives a scale for dS from the bound
+// |dS_ij| <= 2 d max|dO| max|V|, so dS values far below that bound (for
+// example every dS of a head whose dO is 2^-20 times another head's) lose
+// relative precision in the same way; their absolute error stays below
+// 2^-25 times the bound's scale. The scales are undone in fp32 in each
 // epilogue.
 //
 // The row dot D. The forward stores O in bf16, and its P.V product rounds P to

@@ -2,7 +2,7 @@
 //
 // FlashAttention-3 runs its forward in FP8 with block scaling (the mlapandio
 // page "FlashAttention: IO-aware exact attention", "Generations"; the wishwiki
-// page "FlashAttention", "Legacy and Successors"). The pages give no format,
+// page "FlashAttention", "Evolution: FlashAttention-2 and -3"). The pages give no format,
 // so the codes follow the OCP 8-bit floating point E4M3 definition (sign, 4
 // exponent bits with bias 7, 3 mantissa bits, no infinities, largest finite
 // value 448), which is the FP8 format gfx950's matrix cores read.
@@ -11,7 +11,9 @@
 // In fp32: amax = max |x| over the run, inv = 448 / amax (correctly rounded),
 // code = E4M3(x * inv) rounded to nearest, ties to even, saturating at 448,
 // and the stored scale is amax / 448 (correctly rounded), so x ~ code * scale.
-// An all-zero run gets inv = scale = 1.
+// An all-zero run gets inv = scale = 1. A run whose amax is below 2^-64 is
+// multiplied by 2^64 first (exact), which keeps 448 / amax finite; its codes
+// are those of the scaled run and its scale is (2^64 amax / 448) * 2^-64.
 //
 // One workgroup per run: a first sweep takes amax from the bf16 magnitude bits
 // (integer max of finite values), a second re-reads the run (from L2) and
@@ -75,9 +77,15 @@ __global__ __launch_bounds__(kQThreads) void quant_e4m3_kernel(const uint16_t* _
     __syncthreads();
     m = max(max(red[0], red[1]), max(red[2], red[3]));
 
-    const float amax = __uint_as_float(m << 16);
+    // A run below 2^-64 (bf16 exponent field under 63) is taken times 2^64
+    // first, exactly, so that 448 / amax cannot overflow; its stored scale is
+    // scaled back by 2^-64.
+    const bool tiny = m < (63u << 7);
+    const float up = tiny ? 0x1p64f : 1.0f;
+    const float amax = __fmul_rn(__uint_as_float(m << 16), up);
     const float inv = m ? __fdiv_rn(448.0f, amax) : 1.0f;
-    if (threadIdx.x == 0) scales[bh * nruns + run] = m ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    if (threadIdx.x == 0)
+        scales[bh * nruns + run] = m ? __fmul_rn(__fdiv_rn(amax, 448.0f), tiny ? 0x1p-64f : 1.0f) : 1.0f;
 
     uint2* dst = reinterpret_cast<uint2*>(codes + base);
     for (int c = threadIdx.x; c < chunks; c += kQThreads) {
@@ -86,10 +94,10 @@ __global__ __launch_bounds__(kQThreads) void quant_e4m3_kernel(const uint16_t* _
         uint32_t out[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint32_t c0 = e4m3_code(__fmul_rn(bf16_lo_f(ws[2 * t]), inv));
-            const uint32_t c1 = e4m3_code(__fmul_rn(bf16_hi_f(ws[2 * t]), inv));
-            const uint32_t c2 = e4m3_code(__fmul_rn(bf16_lo_f(ws[2 * t + 1]), inv));
-            const uint32_t c3 = e4m3_code(__fmul_rn(bf16_hi_f(ws[2 * t + 1]), inv));
+            const uint32_t c0 = e4m3_code(__fmul_rn(__fmul_rn(bf16_lo_f(ws[2 * t]), up), inv));
+            const uint32_t c1 = e4m3_code(__fmul_rn(__fmul_rn(bf16_hi_f(ws[2 * t]), up), inv));
+            const uint32_t c2 = e4m3_code(__fmul_rn(__fmul_rn(bf16_lo_f(ws[2 * t + 1]), up), inv));
+            const uint32_t c3 = e4m3_code(__fmul_rn(__fmul_rn(bf16_hi_f(ws[2 * t + 1]), up), inv));
             out[t] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
         }
         dst[c] = make_uint2(out[0], out[1]);

@@ -270,7 +270,7 @@ int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const voi
 /* Block quantisation of a bf16 tensor to 8-bit floating point codes, the input
  * form of an FP8 forward. FlashAttention-3 runs its forward in FP8 with block
  * scaling (mlapandio "FlashAttention: IO-aware exact attention", Generations;
- * wishwiki "FlashAttention", Legacy and Successors); the pages fix no format.
+ * wishwiki "FlashAttention", "Evolution: FlashAttention-2 and -3"); the pages fix no format.
  *
  *   x       bf16 [BH, N, d] contiguous (e.g. [B, H, N, d] with BH = B * H),
  *           finite values (a NaN or infinity gives unspecified codes for its run)
@@ -281,8 +281,12 @@ int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const voi
  *
  * Per run, in fp32: amax = max |x|, inv = 448 / amax, code = E4M3(x * inv)
  * rounded to nearest (ties to even) and saturated at 448, scale = amax / 448
- * (both divisions correctly rounded); an all-zero run gets scale 1. Then
- * x ~ code * scale, within 2^-4 relative for codes of magnitude >= 2^-6.
+ * (both divisions correctly rounded); an all-zero run gets scale 1. A run
+ * with amax below 2^-64 is first multiplied by 2^64 (exact; 448 / amax would
+ * overflow otherwise): its codes are those of the scaled run and its scale is
+ * (2^64 amax / 448) * 2^-64. Then x ~ code * scale, within 2^-4 relative for
+ * codes of magnitude >= 2^-6 (an fp32-subnormal scale, for amax below about
+ * 2^-117, keeps at least 7 significant bits for any bf16 input).
  * d: a multiple of 8; rows >= 1. x and codes 16-byte aligned, scales 4-byte.
  * The caller owns every buffer; the call is asynchronous on `stream`.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE (BH, N, rows < 1, or the run count or the
@@ -294,7 +298,7 @@ int flash_attn_quantize_e4m3(const void* x, void* codes, float* scales, int BH, 
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
 
-/* Library version and the GPU target it was compiled for, e.g. "0.4.0 gfx950". */
+/* Library version and the GPU target it was compiled for, e.g. "0.6.0 gfx950". */
 const char* flash_attn_version(void);
 
 #ifdef __cplusplus

@@ -10,9 +10,11 @@ key/value block then updates them:
     O     = e^(m - m_new) * O + e^(S_tile - m_new) V_block
     m     = m_new
 
-The diagram stops at "write O once" plus a logsumexp per row. It leaves the
-last step open. The reading used here is the only one under which the result
-equals the textbook softmax: O is divided by l, and LSE = m + ln l.
+The diagram ends by storing the accumulated O and one logsumexp per row, and
+leaves the final normalisation open. The reading used here is the only one
+under which the running statistics reproduce the ordinary softmax, as the
+page's "Four ideas" section says they do: O is divided by l, and
+LSE = m + ln l.
 
 ``tau`` models a lazily updated reference max. The reference m moves only when
 a block's row max exceeds it by more than ``tau`` (natural-log units).

@@ -414,7 +414,10 @@ int oracle_e4m3_encode(const float* x, uint8_t* c, int64_t n) {
  * kernel would do it: amax = the largest |x| of the block, inv = 448 / amax
  * (one rounded division), code = E4M3(x * inv) (one rounded product), and the
  * stored dequantisation scale is amax / 448, so that x ~ code * scale. An
- * all-zero block gets inv = scale = 1. Scales are [BH, ceil(N / R)]. */
+ * all-zero block gets inv = scale = 1. A block with amax below 2^-64 is taken
+ * times 2^64 first (amax and every x; exact), so that 448 / amax stays finite,
+ * and its stored scale is (2^64 amax / 448) * 2^-64 (two roundings). The
+ * codes are then those of the block times 2^64. Scales are [BH, ceil(N / R)]. */
 int oracle_quantize_e4m3_blocks(const float* x, uint8_t* codes, float* scales, int64_t BH, int N,
                                 int d, int R) {
     if (!x || !codes || !scales || BH < 0 || N < 0 || d <= 0 || R <= 0) return -1;
@@ -431,12 +434,20 @@ int oracle_quantize_e4m3_blocks(const float* x, uint8_t* codes, float* scales, i
                 if (!(a <= FLT_MAX)) return -2;        /* NaN or infinite input */
                 if (a > amax) amax = a;
             }
-            volatile float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
-            volatile float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            /* below 2^-64, 448 / amax could overflow: the run is first scaled
+             * up by 2^64 (exact), and the stored scale scaled back down */
+            const int tiny = amax > 0.0f && amax < 0x1p-64f;
+            const float up = tiny ? 0x1p64f : 1.0f;
+            volatile float a = amax * up;
+            volatile float inv = amax > 0.0f ? 448.0f / a : 1.0f;
+            volatile float sc = amax > 0.0f ? a / 448.0f : 1.0f;
+            volatile float sc_out = sc * (tiny ? 0x1p-64f : 1.0f);
             for (int64_t t = 0; t < cnt; ++t) {
-                volatile float y = xb[t] * inv;
+                volatile float xs = xb[t] * up;
+                volatile float y = xs * inv;
                 cb[t] = e4m3_code(y);
             }
+            sc = sc_out;
             scales[bh * nb + b] = sc;
         }
     }

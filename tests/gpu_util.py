@@ -65,6 +65,30 @@ def excess_err(gpu, ref) -> float:
     return float(np.max(np.abs(gpu - ref) - bf16_half_ulp(ref)))
 
 
+def report(gpu, ref) -> str:
+    """Both error figures of one output: the plain max abs error and the error
+    beyond the bf16 output rounding (the quantity the tolerance applies to)."""
+    return f"max|gpu-ref| {max_err(gpu, ref):.3e}, beyond rounding {excess_err(gpu, ref):.3e}"
+
+
+def check_outputs(tag: str, pairs: dict, tol: dict) -> dict:
+    """Compare several outputs at once. ``pairs`` maps a name to (gpu, ref);
+    ``tol`` maps it to its bound. The LSE ("lse" in the name) is fp32 and is
+    compared plainly; bf16 outputs beyond their rounding. The assertion message
+    carries both figures of every output, so a failure shows how much of the
+    margin the rounding allowance took."""
+    errs, lines = {}, []
+    for name, (g, r) in pairs.items():
+        plain = max_err(g, r)
+        errs[name] = plain if "lse" in name else excess_err(g, r)
+        lines.append(f"{name}: max|gpu-ref| {plain:.3e}" + ("" if "lse" in name else
+                                                             f", beyond rounding {errs[name]:.3e}"))
+    say(f"{tag}: " + "; ".join(lines))
+    bad = [n for n, e in errs.items() if not e <= tol[n]]
+    assert not bad, f"{tag}: " + "; ".join(lines)
+    return errs
+
+
 # Tolerances for bf16 inputs/outputs with fp32 accumulation: max abs error beyond
 # the bf16 output rounding for O and the gradients; plain max abs error for the
 # fp32 LSE.

@@ -574,8 +574,8 @@ def pin_sliding_window_backward(orc):
 
 # ---- 8-bit inputs: OCP E4M3 codes with fp32 block scales ----
 # The pages credit FlashAttention-3 with an FP8 forward using block scaling
-# (mlapandio "Generations"; wishwiki "FlashAttention", "Legacy and
-# Successors") and fix no format. These pins hold the oracle's E4M3 codec to
+# (mlapandio "Generations"; wishwiki "FlashAttention", "Evolution:
+# FlashAttention-2 and -3") and fix no format. These pins hold the oracle's E4M3 codec to
 # torch's float8_e4m3fn (an independent library implementation of the same OCP
 # format), to the format's closed forms, and its block quantiser to a
 # brute-force numpy float32 recomputation.
@@ -666,6 +666,45 @@ def pin_e4m3_block_quantiser(orc):
     assert np.all(err[~normal] <= 2.0 ** -10 * s_full.repeat(d, axis=3)[~normal] * (1 + 1e-6)), "subnormal error"
 
 
+def pin_e4m3_tiny_runs(orc):
+    """Runs far below the normal range. A power-of-two factor on a run commutes
+    with the quantiser: the run times 2^-k gets the codes of the run itself and
+    its scale times 2^-k, as long as that scale stays a normal fp32 number. For
+    a run whose max is below 2^-64 (where 448 / amax would overflow fp32), the
+    codes still equal those of the run times 2^80, never hold a NaN pattern,
+    map the run's max to 448, and dequantise within 2^-4 relative."""
+    rng = _rng(53)
+    R, d = 16, 8
+    base = (rng.standard_normal((1, 4, 2 * R, d)) * 3).astype(np.float32)
+    base[0, 3, R:] = 0.0
+    base[0, 3, R, 0] = np.float32(0.75)                 # a run holding one nonzero value
+    c0, s0 = orc.quantize_e4m3(base, R)
+    for k in (20, 60, 100):                             # 2^-100 * 448 / 2^8.6 is still a normal scale
+        ck, sk = orc.quantize_e4m3((base * np.float32(2.0 ** -k)).astype(np.float32), R)
+        assert np.array_equal(ck, c0), f"codes of the run times 2^-{k}"
+        assert np.array_equal(sk.astype(np.float64), s0.astype(np.float64) * 2.0 ** -k), f"scale times 2^-{k}"
+    # the advisor's case: a run of [1e-37, 5e-38, 0, ...]
+    x = np.zeros((1, 1, R, d), dtype=np.float32)
+    x[0, 0, 0, 0], x[0, 0, 0, 1] = np.float32(1e-37), np.float32(5e-38)
+    c, sc = orc.quantize_e4m3(x, R)
+    c80, _ = orc.quantize_e4m3((x * np.float32(2.0 ** 80)).astype(np.float32), R)
+    assert np.array_equal(c, c80), "tiny run: codes of the run times 2^80"
+    assert c[0, 0, 0, 0] == 0x7E and np.all(c.reshape(-1)[2:] == 0), "max to 448, zeros to 0"
+    assert not np.any((c & 0x7F) == 0x7F), "no NaN code"
+    deq = orc.dequantize_e4m3(c, sc, R)
+    nz = x != 0
+    assert np.all(np.abs(deq[nz] - x[nz]) <= 2.0 ** -4 * np.abs(x[nz])), "tiny run dequantises within 2^-4"
+    # bf16 subnormal inputs: the smallest bf16 magnitudes, scale an fp32 subnormal
+    y = np.zeros((1, 1, R, d), dtype=np.float32)
+    y[0, 0, 0, :3] = np.array([2.0 ** -133, -3 * 2.0 ** -133, 2.0 ** -127], dtype=np.float32)
+    c, sc = orc.quantize_e4m3(y, R)
+    assert 0 < sc[0, 0, 0] < 2.0 ** -126, "the scale is an fp32 subnormal here"
+    assert c[0, 0, 0, 2] == 0x7E and not np.any((c & 0x7F) == 0x7F)
+    deq = orc.dequantize_e4m3(c, sc, R)
+    nz = y != 0
+    assert np.all(np.abs(deq[nz] - y[nz]) <= 2.0 ** -4 * np.abs(y[nz])), "subnormal-scale run within 2^-4"
+
+
 def pin_e4m3_forward(orc):
     """The forward on 8-bit inputs is the definition on the dequantised values:
     constant V codes give O = that value exactly; zero Q codes give the causal
@@ -717,5 +756,6 @@ PINS = [
     pin_e4m3_codes,
     pin_e4m3_rounding,
     pin_e4m3_block_quantiser,
+    pin_e4m3_tiny_runs,
     pin_e4m3_forward,
 ]

@@ -5,9 +5,11 @@ oracle computes everything from the inputs in fp64 (exact D). Tolerance: max
 abs error on
 dQ, dK and dV <= 2e-2 beyond the rounding of the bf16 output (half a bf16 ulp at
 the oracle's value). Small cases are compared element by element on every
-output; full-size workloads on seeded samples of query rows (dQ) and keys
-(dK, dV) that the oracle computes one by one, over all heads or, for the GQA
-workload, over two seeded (batch, K/V head) groups.
+output. The full-size workloads are compared on every element too: the spiky
+N = 8192 workload on all 32 heads, the GQA N = 16384 workload on two seeded
+(batch, K/V head) groups, each group's four query heads and one K/V head whole.
+Failure messages carry the plain max abs error beside the error beyond the
+output rounding.
 """
 import math
 
@@ -16,7 +18,8 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from tests.gpu_util import TOL_GRAD, excess_err, f64, from_dev_bf16, say, to_dev
+from tests.gpu_util import (TOL_GRAD, TOL_LSE, TOL_O, check_outputs, excess_err, f64, from_dev_bf16,
+                            say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,9 +48,8 @@ def check_full(fa, inp, causal, scale, tag):
     say(f"bwd {tag}")
     dq, dk, dv = run_fwd_bwd(fa, inp, causal, scale)
     ref = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), causal, scale)
-    errs = {n: excess_err(g, ref[n]) for n, g in (("dq", dq), ("dk", dk), ("dv", dv))}
-    assert all(e <= TOL_GRAD for e in errs.values()), f"{tag}: {errs}"
-    return errs
+    return check_outputs(tag, {"dq": (dq, ref["dq"]), "dk": (dk, ref["dk"]), "dv": (dv, ref["dv"])},
+                         dict(dq=TOL_GRAD, dk=TOL_GRAD, dv=TOL_GRAD))
 
 
 def test_workload_mha2k_full(fa):
@@ -171,29 +173,27 @@ def test_stages_equal_full_call(fa):
 
 
 # ------------------------------------------------------------------ full-size workloads
-def sampled_bwd_check(fa, w, inp, groups):
-    """Full GPU forward + backward, then compare sampled dQ rows and dK/dV keys of
-    the listed (b, kv-head) groups with the oracle."""
+def group_bwd_check(fa, w, inp, groups):
+    """Full GPU forward + backward at the workload's size, then every element of
+    O, LSE, dQ, dK and dV of the listed (b, kv-head) groups against the oracle's
+    full backward of those groups (every row, every key)."""
     import torch
-    say(f"bwd workload {w.name} (full size on GPU, groups {groups})")
+    say(f"bwd workload {w.name} (full size on GPU; oracle on groups {groups}, all rows and keys)")
     q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
-    rows = ai.sample_rows(w.N, 256, w.cfg_id)
-    keys = ai.sample_rows(w.N, 256, w.cfg_id + 100)
-    rt, kt = torch.as_tensor(rows, device=q.device), torch.as_tensor(keys, device=q.device)
     G = w.G
     for (b, h) in groups:
         hs = slice(h * G, (h + 1) * G)
-        g_dq = from_dev_bf16(dq[b:b + 1, hs].index_select(2, rt))
-        g_dk = from_dev_bf16(dk[b:b + 1, h:h + 1].index_select(2, kt))
-        g_dv = from_dev_bf16(dv[b:b + 1, h:h + 1].index_select(2, kt))
-        ref = oracle.bwd_sampled(f64(inp["q"][b:b + 1, hs]), f64(inp["k"][b:b + 1, h:h + 1]),
-                                 f64(inp["v"][b:b + 1, h:h + 1]), f64(inp["do"][b:b + 1, hs]), w.causal, w.scale,
-                                 rows, keys)
-        errs = {n: excess_err(g, ref[n]) for n, g in (("dq", g_dq), ("dk", g_dk), ("dv", g_dv))}
-        assert all(e <= TOL_GRAD for e in errs.values()), f"{w.name} group {(b, h)}: {errs}"
+        got = dict(o=from_dev_bf16(o[b:b + 1, hs]), lse=lse[b:b + 1, hs].double().cpu().numpy(),
+                   dq=from_dev_bf16(dq[b:b + 1, hs]), dk=from_dev_bf16(dk[b:b + 1, h:h + 1]),
+                   dv=from_dev_bf16(dv[b:b + 1, h:h + 1]))
+        say(f"oracle backward of group {(b, h)}")
+        ref = oracle.bwd(f64(inp["q"][b:b + 1, hs]), f64(inp["k"][b:b + 1, h:h + 1]),
+                         f64(inp["v"][b:b + 1, h:h + 1]), f64(inp["do"][b:b + 1, hs]), w.causal, w.scale)
+        check_outputs(f"{w.name} group {(b, h)}", {n: (got[n], ref[n]) for n in got},
+                      dict(o=TOL_O, lse=TOL_LSE, dq=TOL_GRAD, dk=TOL_GRAD, dv=TOL_GRAD))
 
 
 def seeded_groups(w, count):
@@ -203,14 +203,73 @@ def seeded_groups(w, count):
 
 
 def test_workload_spiky8k(fa):
-    """N=8192, d=128, causal, K rows x4 at 5% of positions; 4 seeded heads."""
+    """N=8192, d=128, causal, K rows x4 at 5% of positions: every element of
+    every output of all 32 heads (forward O and LSE included) against the
+    oracle's full backward."""
+    import torch
     w = ai.WORKLOADS["spiky8k"]
     inp = ai.make_inputs(w)
-    sampled_bwd_check(fa, w, inp, seeded_groups(w, 4))
+    say(f"bwd workload {w.name} (full size, every head, row and key)")
+    q, k, v, do = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]), to_dev(inp["do"])
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    got = dict(o=from_dev_bf16(o), lse=lse.double().cpu().numpy(), dq=from_dev_bf16(dq),
+               dk=from_dev_bf16(dk), dv=from_dev_bf16(dv))
+    del q, k, v, do, o, lse, dq, dk, dv
+    say("oracle backward of all 32 heads")
+    ref = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), w.causal, w.scale)
+    check_outputs(w.name, {n: (got[n], ref[n]) for n in got},
+                  dict(o=TOL_O, lse=TOL_LSE, dq=TOL_GRAD, dk=TOL_GRAD, dv=TOL_GRAD))
 
 
 def test_workload_gqa16k(fa):
-    """B=2, Hq=32, Hkv=8, N=16384, d=128, causal; two seeded (b, kv-head) groups."""
+    """B=2, Hq=32, Hkv=8, N=16384, d=128, causal: two seeded (b, kv-head) groups
+    (8 of the 32 query heads' rows, 2 of the 8 K/V heads' keys) on every
+    element of O, LSE, dQ, dK and dV."""
     w = ai.WORKLOADS["gqa16k"]
     inp = ai.make_inputs(w)
-    sampled_bwd_check(fa, w, inp, seeded_groups(w, w.oracle_groups))
+    group_bwd_check(fa, w, inp, seeded_groups(w, w.oracle_groups))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_dynamic_range_of_the_fp16_operands(fa, d):
+    """The backward's products take fp16 operands scaled by one power of two per
+    tensor (and one for dS, from the bound 2 d max|dO| max|V|). Four heads see
+    the same Q, K and V, and dO times 2^0, 2^-8, 2^-24 and 2^-40: a dynamic range
+    of 2^40 inside one dO tensor, beyond fp16's. The gradients are linear in dO,
+    so head h's gradients are 2^e_h times head 0's.
+      * Every head meets the absolute bound against the oracle.
+      * Heads at 2^0 and 2^-8, divided by their factor, meet it too: relative
+        accuracy holds there.
+      * Further down, dS falls below fp16's normal range (2^-14 after its scale)
+        and then below its subnormals, so dQ and dK of those heads lose their
+        relative accuracy (their absolute error stays below 2^-20); dV, whose
+        operands are P and dO alone, keeps it at 2^-24. The relative errors are
+        printed."""
+    import torch
+    Hq = 4
+    exps = (0, -8, -24, -40)
+    base = ai.make_case(1, 1, 1, 640, d, seed=3100 + d)
+    inp = {n: np.repeat(base[n], Hq, axis=1) for n in ("q", "k", "v", "do")}
+    do = torch.from_numpy(f64(inp["do"]))
+    for h, e in enumerate(exps):
+        do[:, h] *= 2.0 ** e
+    inp["do"] = do.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(f64(inp["do"][:, 1]) * 2.0 ** 8, f64(base["do"][:, 0])), "power-of-two scaling is exact"
+    s = 1.0 / math.sqrt(d)
+    say(f"bwd dynamic range of dO over heads d={d}")
+    dq, dk, dv = run_fwd_bwd(fa, inp, True, s)
+    ref = oracle.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]), True, s)
+    check_outputs(f"dynamic range d={d} (absolute, all heads)",
+                  {"dq": (dq, ref["dq"]), "dk": (dk, ref["dk"]), "dv": (dv, ref["dv"])},
+                  dict(dq=TOL_GRAD, dk=TOL_GRAD, dv=TOL_GRAD))
+    rel = {}
+    for h, e in enumerate(exps):
+        f = 2.0 ** -e
+        rel[e] = {n: excess_err(g[:, h] * f, ref[n][:, h] * f)
+                  for n, g in (("dq", dq), ("dk", dk), ("dv", dv))}
+    say(f"error beyond rounding, each head divided by its factor: {rel}")
+    for e in (0, -8):
+        assert all(x <= TOL_GRAD for x in rel[e].values()), f"head at 2^{e}: {rel[e]}"
+    assert np.max(np.abs(dq[:, 2:])) <= 2.0 ** -20 and np.max(np.abs(dk[:, 2:])) <= 2.0 ** -20

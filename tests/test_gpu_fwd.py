@@ -3,8 +3,11 @@
 Tolerances: max abs error on O <= 1e-2 beyond the rounding of the bf16 output
 (half a bf16 ulp at the oracle's value), and on the fp32 LSE <= 1e-3. Small
 cases are compared element by element on every output.
-Full-size workloads are compared on seeded samples of query rows that the oracle
-computes one by one. Closed forms (constant V, causal row 0, uniform attention
+The spiky N = 8192 workload is compared on every row of every head; the other
+full-size workloads on seeded samples of query rows that the oracle computes
+one by one (every row of the GQA workload's two seeded groups is checked in the
+backward tests). Failure messages carry the plain max abs error beside the error
+beyond the output rounding. Closed forms (constant V, causal row 0, uniform attention
 at scale 0) are checked on every row.
 """
 import math
@@ -14,7 +17,8 @@ import pytest
 
 import attn_inputs as ai
 import oracle
-from tests.gpu_util import TOL_LSE, TOL_O, excess_err, f64, from_dev_bf16, from_dev_f32, max_err, say, to_dev
+from tests.gpu_util import (TOL_LSE, TOL_O, check_outputs, excess_err, f64, from_dev_bf16, from_dev_f32, max_err,
+                            say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,9 +45,8 @@ def check_full(fa, inp, causal, scale, tag):
     say(f"fwd {tag}")
     o, lse = run_fwd(fa, inp, causal, scale)
     ro, rl = oracle.fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), causal, scale)
-    eo, el = excess_err(o, ro), max_err(lse, rl)
-    assert eo <= TOL_O and el <= TOL_LSE, f"{tag}: O err {eo:.2e}, LSE err {el:.2e}"
-    return eo, el
+    errs = check_outputs(tag, {"o": (o, ro), "lse": (lse, rl)}, dict(o=TOL_O, lse=TOL_LSE))
+    return errs["o"], errs["lse"]
 
 
 def test_tiny_workload(fa):
@@ -146,16 +149,26 @@ def sampled_check(fa, w, inp, rows, heads_b=None):
     l_s = from_dev_f32(lse.index_select(2, rows_t))
     del q, k, v, o, lse
     ro, rl = oracle.fwd(f64(inp["q"][:, :, rows]), f64(inp["k"]), f64(inp["v"]), w.causal, w.scale, qpos=rows)
-    eo, el = excess_err(o_s, ro), max_err(l_s, rl)
-    assert eo <= TOL_O and el <= TOL_LSE, f"{w.name}: O err {eo:.2e}, LSE err {el:.2e}"
+    check_outputs(f"{w.name} ({len(rows)} rows)", {"o": (o_s, ro), "lse": (l_s, rl)}, dict(o=TOL_O, lse=TOL_LSE))
 
 
 @pytest.mark.parametrize("name", ["mha2k", "spiky8k", "gqa16k", "long128k"])
 def test_workload_sampled(fa, name):
+    """The full-size forward on seeded rows of every head (every row at mha2k).
+    The spiky and GQA workloads' forward outputs are also checked on every
+    element of every head they cover in the backward tests."""
     w = ai.WORKLOADS[name]
     inp = ai.make_inputs(w, with_grad=False)
     rows = ai.sample_rows(w.N, 256 if name != "mha2k" else w.N, w.cfg_id)
     sampled_check(fa, w, inp, rows)
+
+
+def test_workload_spiky8k_every_row(fa):
+    """N = 8192, d = 128, causal, spiked K: O and LSE of every row of all 32
+    heads against the oracle."""
+    w = ai.WORKLOADS["spiky8k"]
+    inp = ai.make_inputs(w, with_grad=False)
+    check_full(fa, inp, w.causal, w.scale, "spiky8k (every row, every head)")
 
 
 def test_d256_full_size_sampled(fa):

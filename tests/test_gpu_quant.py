@@ -74,6 +74,27 @@ def test_quantize_matches_oracle(fa, orc, BH, N, d, rows):
     assert not np.any((c & 0x7F) == 0x7F), "a NaN code was written"
 
 
+@pytest.mark.parametrize("exp", [-64, -70, -100, -120, -126, -133])
+def test_quantize_tiny_runs(fa, orc, exp):
+    """Runs whose max is near or below 2^-64, where 448 / amax overflows fp32
+    unless the run is scaled up first, down to bf16 subnormals (2^-133): codes
+    and scales bit-exact with the oracle, no NaN code, the run's max at 448."""
+    import torch
+    say(f"quantize_e4m3 tiny runs 2^{exp}")
+    g = torch.Generator().manual_seed(900 + (-exp))
+    x = (torch.randn((3, 48, 64), generator=g) * 2.0 ** exp).to(torch.bfloat16)
+    x[1, :16] = 0.0                                   # an all-zero run
+    x[2, 32:] = (torch.randn((16, 64), generator=g) * 2.0 ** min(exp + 40, 0)).to(torch.bfloat16)
+    c = _compare(fa, orc, x, 16)
+    assert not np.any((c & 0x7F) == 0x7F), "a NaN code was written"
+    mags = x.float().abs().numpy().reshape(3, -1, 16 * 64)
+    codes = c.reshape(3, -1, 16 * 64)
+    for bh in range(3):
+        for r in range(mags.shape[1]):
+            if mags[bh, r].max() > 0:
+                assert np.all(codes[bh, r][mags[bh, r] == mags[bh, r].max()] & 0x7F == 0x7E)
+
+
 def test_quantize_full_size_q_of_gqa16k(fa, orc):
     """Q of the gqa16k workload (B = 2, Hq = 32, N = 16384, d = 128), 128-row runs, every code."""
     import torch

@@ -49,7 +49,9 @@ MUTANTS = {
     "e4m3 overflow to NaN": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
     "e4m3 sign dropped": ("const uint8_t sign = signbit(x) ? 0x80 : 0;", "const uint8_t sign = 0;"),
     "e4m3 subnormal rounding truncates": ("return sign | (uint8_t)nearbyint(ldexp(a, 9));", "return sign | (uint8_t)trunc(ldexp(a, 9));"),
-    "quantiser stores the inverse scale": ("volatile float sc = amax > 0.0f ? amax / 448.0f : 1.0f;", "volatile float sc = amax > 0.0f ? 448.0f / amax : 1.0f;"),
+    "quantiser stores the inverse scale": ("volatile float sc = amax > 0.0f ? a / 448.0f : 1.0f;", "volatile float sc = amax > 0.0f ? 448.0f / a : 1.0f;"),
+    "quantiser forgets the tiny-run factor on x": ("volatile float xs = xb[t] * up;", "volatile float xs = xb[t];"),
+    "quantiser keeps the scale of the scaled-up run": ("volatile float sc_out = sc * (tiny ? 0x1p-64f : 1.0f);", "volatile float sc_out = sc;"),
     "quantiser amax of the first row": ("for (int64_t t = 0; t < cnt; ++t) {\n                const float a = fabsf(xb[t]);", "for (int64_t t = 0; t < d; ++t) {\n                const float a = fabsf(xb[t]);"),
     "bwd reduction drops a thread": ("for (int t = 0; t < nt; ++t) {\n                const double* dk_t", "for (int t = 1; t < nt; ++t) {\n                const double* dk_t"),
 }
