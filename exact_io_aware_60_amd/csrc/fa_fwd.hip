@@ -39,7 +39,14 @@
 //    with the exact max, O and l rescaled. So no row max is computed for the
 //    other chunks, and every P stays at most 2^8. Any reference value cancels
 //    in O / l and m + ln l, so the result is the same (the fp64 model in
-//    oracle/online.py checks this rule).
+//    oracle/online.py checks this rule). In bf16, though, a stale reference
+//    leaves a peaked row's dominant probability at some 2^x with x > 0 that
+//    rounds by up to 2^-8 relative, about 0.01 on a value of 4. So O is
+//    divided by the sum of the bf16 probabilities themselves: the weights
+//    then sum to one as used, and the dominant value's rounding cancels. The
+//    matrix cores form that sum (two more MFMAs per chunk, ones * P^T): the
+//    forward is bound by its vector-ALU issue, and one v_dot2 per pair cost
+//    8.7% of its time. LSE keeps the fp32 sum.
 //  * Causal: chunks above a wave's diagonal are skipped; the diagonal chunk and
 //    the ragged last chunk are masked element-wise. Workgroups run heaviest
 //    q-tile first (longest-processing-time order). Workgroups of one head set
@@ -162,13 +169,21 @@ __device__ __forceinline__ void exp_pack_one(const f32x16& x, int pi, float& ls,
     pp[kc][t] = pack_bf16(p0, p1);
 }
 
+// The A operand of all-ones bf16 values: ones * P^T sums, for every query row
+// (lane column), the bf16 probabilities the P.V MFMA takes, over both lane
+// halves' keys. Every register of the accumulator then holds that row sum.
+__device__ __forceinline__ u32x4 ones_bf16() {
+    const uint32_t one2 = 0x3F803F80u;
+    return u32x4{one2, one2, one2, one2};
+}
+
 // The reference check after a chunk's exps (ls: this lane's sum, pp: packs).
 // Unless some lane's sum exceeds kSumMax or is not finite, every P of the chunk
 // is at most kSumMax and nothing happens. Otherwise the wave moves m up to the
 // exact running max (m + the chunk's max of x, both lane halves), rescales O
 // and l by 2^(m_old - m_new), shifts x and redoes the exps.
 template <int D>
-__device__ __forceinline__ void check_reference(f32x16& x, float& m, float& l, f32x16 (&o)[D / 32],
+__device__ __forceinline__ void check_reference(f32x16& x, float& m, float& l, f32x16& lsum, f32x16 (&o)[D / 32],
                                                 float& ls, u32x4 (&pp)[2]) {
     if (__ballot(!(ls <= kSumMax))) {
         float mx = x[0];
@@ -177,6 +192,7 @@ __device__ __forceinline__ void check_reference(f32x16& x, float& m, float& l, f
         const float delta = fmaxf(fmaxf(mx, swap_half(mx)), 0.f);
         const float alpha = fast_exp2(-delta);
         l *= alpha;
+        lsum[0] *= alpha;   // the only entry the epilogue reads
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -193,14 +209,16 @@ __device__ __forceinline__ void check_reference(f32x16& x, float& m, float& l, f
 // Softmax and O^T += V^T P^T for one chunk (not pipelined: a wave's last chunk).
 template <int D>
 __device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
-                                           f32x16& x, float& m, float& l, f32x16 (&o)[D / 32]) {
+                                           f32x16& x, float& m, float& l, f32x16& lsum, f32x16 (&o)[D / 32]) {
     constexpr int DB = D / 32;
     u32x4 pp[2];
     float ls = 0.f;
 #pragma unroll
     for (int pi = 0; pi < 8; ++pi) exp_pack_one(x, pi, ls, pp);
-    check_reference<D>(x, m, l, o, ls, pp);
+    check_reference<D>(x, m, l, lsum, o, ls, pp);
     l += ls;
+    lsum = mfma32(ones_bf16(), pp[0], lsum);
+    lsum = mfma32(ones_bf16(), pp[1], lsum);
 #pragma unroll
     for (int f = 0; f < 2 * DB; ++f) o[f % DB] = mfma32(v_frag<D>(Vt, vbase, h, f), pp[f / DB], o[f % DB]);
 }
@@ -264,7 +282,7 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
                                                 const FA_LDS uint8_t* __restrict__ Knn, int hnn,
                                                 const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
                                                 const u32x4 (&qf)[D / 16], f32x16& sc, f32x16& sn,
-                                                float& m, float& l, float sl2, f32x16 (&o)[D / 32],
+                                                float& m, float& l, f32x16& lsum, float sl2, f32x16 (&o)[D / 32],
                                                 u32x4 (&ka)[2], const CP& cp) {
     constexpr int DS = D / 16, DB = D / 32, NF = 2 * DB;
     // the 8 packs of the current chunk over the DS phase-1 steps: PPS per step,
@@ -306,12 +324,13 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
         a0 = a1;
         a1 = a2;
     });
-    check_reference<D>(sc, m, l, o, ls, pp);
+    check_reference<D>(sc, m, l, lsum, o, ls, pp);
     l += ls;
     __builtin_amdgcn_s_setprio(0);
     static_for<NF>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         o[f % DB] = mfma32(vf[f], pp[f / DB], o[f % DB]);
+        if constexpr (f == 1 || f == NF - 1) lsum = mfma32(ones_bf16(), pp[f == 1 ? 0 : 1], lsum);
 #pragma unroll
         for (int c = 0; c < EPS; ++c) sn[f * EPS + c] = fmaf(sn[f * EPS + c], sl2, -m);
         if constexpr (f == 2 || f == 3) ka[f - 2] = k_frag<D>(Knn, kbase, hnn, f - 2);
@@ -328,6 +347,7 @@ struct FwdState {
     f32x16 sA, sB;             // x = S*sl2 - m of the current chunk / scores of the next (alternating)
     u32x4 ka[2];               // first two K fragments of the next pipelined chunk's score MFMAs
     float m, l;                // reference (log2 units), this lane's share of the row sum
+    f32x16 lsum;               // ones * P^T: the row sum of the bf16 probabilities the P.V MFMA takes
 };
 
 // Sliding window: where a wave's keys start. A wave skips the chunks before
@@ -384,11 +404,11 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
     else if (WIN && c * 32 < wd.r0 + 32 - wd.win)
         mask_scores<true>(sc, c * 32, qrow, N, causal, hh, wd.win);
     if (c < lastc) {
-        pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Kr1, H, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, sl2, st.o,
-                              st.ka, cp);
+        pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Kr1, H, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, st.lsum, sl2,
+                              st.o, st.ka, cp);
     } else {
         cp.bulk();
-        softmax_pv<D>(Vt, vbase, H, sc, st.m, st.l, st.o);
+        softmax_pv<D>(Vt, vbase, H, sc, st.m, st.l, st.lsum, st.o);
     }
 }
 
@@ -498,6 +518,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
     for (int db = 0; db < DB; ++db) st.o[db] = zero16();
     st.m = 0.f;
     st.l = 0.f;
+    st.lsum = zero16();
 
     // K and V through buffer resources covering the head's N rows: rows of a
     // ragged last tile past N read as zeros (their scores are masked).
@@ -537,8 +558,13 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
 
     if (wave_valid && qrow < N) {
         uint16_t* Og = p.o + (qrow0 + qrow) * D;
+        // O is divided by the sum of the bf16 probabilities the P.V products
+        // took, so each row's weights sum to one as used: a peaked row keeps
+        // its dominant value's weight at 1 whatever that probability rounded
+        // to (the reference need not sit at the row's max). The logsumexp
+        // takes the fp32 sum.
         const float lt = st.l + swap_half(st.l);
-        const float inv = 1.f / lt;
+        const float inv = 1.f / st.lsum[0];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
