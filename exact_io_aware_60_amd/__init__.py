@@ -22,12 +22,13 @@ LIB_PATH = os.path.join(HERE, "libflashattn.so")
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCALE = (
     0, -1, -2, -3, -4, -5, -6, -7)
+FA_ERR_SCRATCH = -8
 
 EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_strerror",
             "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
             "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen",
             "flash_attn_fwd_window", "flash_attn_bwd_window", "flash_attn_bwd_varlen",
-            "flash_attn_quantize_e4m3")
+            "flash_attn_quantize_e4m3", "flash_attn_decode_noalloc", "flash_attn_decode_noalloc_max_bytes")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_fwd_varlen.argtypes = [_vp] * 6 + [_i] * 7 + [ctypes.c_float, _vp]
         L.flash_attn_decode.restype = _i
         L.flash_attn_decode.argtypes = [_vp] * 6 + [_i] * 8 + [ctypes.c_float, _vp, ctypes.c_size_t, _vp]
+        L.flash_attn_decode_noalloc.restype = _i
+        L.flash_attn_decode_noalloc.argtypes = [_vp] * 6 + [_i] * 8 + [ctypes.c_float, _vp]
+        L.flash_attn_decode_noalloc_max_bytes.restype = ctypes.c_size_t
+        L.flash_attn_decode_noalloc_max_bytes.argtypes = []
         L.flash_attn_decode_workspace_size.restype = ctypes.c_size_t
         L.flash_attn_decode_workspace_size.argtypes = [_i] * 8
         L.flash_attn_quantize_e4m3.restype = _i
@@ -147,6 +152,17 @@ def decode_raw(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, scale,
     """flash_attn_decode on raw addresses (ints; seqlens_k may be None); returns the status code."""
     return lib().flash_attn_decode(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, int(causal), int(window),
                                    float(scale), workspace, workspace_bytes, stream)
+
+
+def decode_noalloc_raw(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, scale, stream=None,
+                       window: int = 0) -> int:
+    """flash_attn_decode_noalloc on raw addresses (ints; seqlens_k may be None); returns the status code."""
+    return lib().flash_attn_decode_noalloc(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, int(causal),
+                                           int(window), float(scale), stream)
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(lib().flash_attn_decode_noalloc_max_bytes())
 
 
 def quantize_e4m3_raw(x, codes, scales, BH, N, d, rows, stream=None) -> int:
@@ -271,6 +287,38 @@ def decode(q, k, v, causal: bool = True, scale: float | None = None, workspace=N
     _check(decode_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), sl_ptr, B, Hq, Hkv,
                       Nq, Nk, d, causal, scale, ws_ptr, ws_len, _stream(q), window))
     return o, lse
+
+
+def decode_noalloc(q, k, v, out, lse, causal: bool = True, scale: float | None = None, seqlens_k=None,
+                   window: int = 0):
+    """decode() through flash_attn_decode_noalloc: the caller passes the outputs
+    (o bf16 [B,Hq,Nq,d], lse fp32 [B,Hq,Nq]); the partial results go to the
+    library's static per-GPU scratch, so nothing is allocated here or in the
+    library. Overlapping calls on one GPU race (the scratch is shared)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape != k.shape:
+        raise ValueError("q and k/v must agree on B and d, and v must be shaped like k")
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _checked(t, name)
+    if tuple(out.shape) != (B, Hq, Nq, d):
+        raise ValueError("out must be shaped like q")
+    if (lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous()
+            or tuple(lse.shape) != (B, Hq, Nq)):
+        raise ValueError("lse must be a contiguous float32 GPU tensor of shape [B, Hq, Nq]")
+    sl_ptr = None
+    if seqlens_k is not None:
+        if (seqlens_k.dtype != torch.int32 or not seqlens_k.is_cuda or not seqlens_k.is_contiguous()
+                or tuple(seqlens_k.shape) != (B,)):
+            raise ValueError("seqlens_k must be a contiguous int32 GPU tensor of shape [B]")
+        sl_ptr = seqlens_k.data_ptr()
+    scale = default_scale(d) if scale is None else scale
+    _check(decode_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), sl_ptr, B,
+                              Hq, Hkv, Nq, Nk, d, causal, scale, _stream(q), window))
+    return out, lse
 
 
 def fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None, out=None,

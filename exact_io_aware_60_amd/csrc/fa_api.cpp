@@ -285,9 +285,36 @@ size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, 
     return fa::dec_plan(B, Hq, Hkv, Nq, Nk, d, window).total;
 }
 
+namespace {
+
+// flash_attn_decode with the workspace checks done by the caller.
+int decode_common(const void* q, const void* k, const void* v, void* o, float* lse, const int* seqlens_k,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream, bool noalloc);
+
+}  // namespace
+
 int flash_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                       const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                       int window, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_common(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, workspace,
+                         workspace_bytes, stream, false);
+}
+
+int flash_attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                              int causal, int window, float scale, void* stream) {
+    return decode_common(q, k, v, o, lse, seqlens_k, B, Hq, Hkv, Nq, Nk, d, causal, window, scale, nullptr, 0,
+                         stream, true);
+}
+
+size_t flash_attn_decode_noalloc_max_bytes(void) { return fa::kDecodeScratchBytes; }
+
+namespace {
+
+int decode_common(const void* q, const void* k, const void* v, void* o, float* lse, const int* seqlens_k,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     int st = check_decode_shape(B, Hq, Hkv, Nq, Nk, d, causal);
     if (st != FA_OK) return st;
@@ -297,6 +324,15 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
         (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0)
         return FA_ERR_ALIGN;
     const fa::DecPlan pl = fa::dec_plan(B, Hq, Hkv, Nq, Nk, d, window);
+    if (noalloc) {
+        // the partial results go to this GPU's static scratch array
+        if (pl.total > fa::kDecodeScratchBytes) return FA_ERR_SCRATCH;
+        if (pl.total > 0) {
+            const hipError_t e = fa::decode_scratch(&workspace);
+            if (e != hipSuccess) return hip_status(e);
+            workspace_bytes = fa::kDecodeScratchBytes;
+        }
+    }
     if (pl.total > 0) {
         if (!workspace || workspace_bytes < pl.total) return FA_ERR_WORKSPACE;
         if (!aligned16(workspace)) return FA_ERR_ALIGN;
@@ -321,6 +357,8 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
     p.pair = pl.pair;
     return hip_status(fa::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
 
 int flash_attn_quantize_e4m3(const void* x, void* codes, float* scales, int BH, int N, int d, int rows,
                              void* stream) {
@@ -367,6 +405,9 @@ const char* flash_attn_strerror(int status) {
         case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
         case FA_ERR_HIP: return g_hip_text[0] ? g_hip_text : "HIP launch failed";
         case FA_ERR_SCALE: return "scale must be finite and >= 0";
+        case FA_ERR_SCRATCH:
+            return "the call needs more partial-result memory than the static scratch holds "
+                   "(flash_attn_decode_noalloc_max_bytes); use flash_attn_decode with a workspace";
         default: return "unknown status";
     }
 }

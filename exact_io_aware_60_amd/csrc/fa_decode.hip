@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 #include "fa_device.h"
 #include "fa_params.h"
@@ -519,5 +520,39 @@ hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
     if (p.d == 256) return launch_decode_t<256>(p, stream);
     return p.d == 128 ? launch_decode_t<128>(p, stream) : launch_decode_t<64>(p, stream);
 }
+
+// ---------------------------------------------------------------- static scratch
+// Device memory for the per-range partial results of callers that cannot
+// allocate (flash_attn_decode_noalloc). Every GPU the library runs on holds
+// its own copy until the process ends. In host code `scratch` names a host-side
+// stand-in, not the device array: kernels and copies only ever get the address
+// that hipGetSymbolAddress returns for the current device.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t decode_scratch(void** out) {
+    *out = nullptr;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    // once per device, with that device current (it is: hipGetDevice above)
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+    if (!g_scratch_ptr[dev]) return hipErrorInvalidSymbol;
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 
 }  // namespace fa

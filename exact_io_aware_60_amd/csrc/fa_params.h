@@ -121,6 +121,12 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, hipStream_t stream);
 
+// Size of the decode's static scratch array (one per GPU; flash_attn_decode_noalloc).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+// Device address of the current GPU's scratch array, looked up once per GPU
+// (hipGetSymbolAddress with that GPU current) and cached.
+hipError_t decode_scratch(void** out);
+
 // Launch geometry, exposed for logging and tests of the host logic.
 struct Geometry {
     int block_m;      // query rows per workgroup

@@ -36,8 +36,10 @@
  * `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
  * work on `stream` and return at once; results are valid once the stream has
  * been synchronised. The library never allocates, frees or synchronises, keeps
- * no pointer after a call returns, and holds no mutable global state, so calls
- * from several host threads are safe. Calls on one stream run in order; the
+ * no pointer after a call returns, and holds no mutable global state apart
+ * from the per-GPU address cache of flash_attn_decode_noalloc's static scratch
+ * (set once per GPU under a once-flag), so calls from several host threads are
+ * safe (flash_attn_decode_noalloc: see its sharing rule). Calls on one stream run in order; the
  * caller orders calls on different streams that share buffers.
  *
  * Errors. Every entry point returns FA_OK (0) or a negative status and never
@@ -62,7 +64,8 @@ enum fa_status {
     FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned (int32 length arrays: 4-byte) */
     FA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
     FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
-    FA_ERR_SCALE = -7      /* scale is negative, NaN or infinite */
+    FA_ERR_SCALE = -7,     /* scale is negative, NaN or infinite */
+    FA_ERR_SCRATCH = -8    /* flash_attn_decode_noalloc: more partial results than its static scratch holds */
 };
 
 /*
@@ -232,6 +235,34 @@ int flash_attn_decode(const void* q, const void* k, const void* v, void* o, floa
  */
 size_t flash_attn_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
                                         int window);
+
+/*
+ * flash_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks, kernels and results as flash_attn_decode, without
+ * the workspace: the per-range partial results go to a static device array of
+ * flash_attn_decode_noalloc_max_bytes() bytes (32 MiB) that the library holds
+ * on every GPU it runs on until the process ends. The call allocates and frees
+ * nothing. Its first call on a GPU looks up that GPU's copy of the array
+ * (hipGetSymbolAddress, with that GPU current) and caches the address; the
+ * runtime loads the library's code object for that GPU then if it has not yet.
+ *   Limit: shapes whose flash_attn_decode_workspace_size(...) exceeds the
+ *   array return FA_ERR_SCRATCH and enqueue nothing (the largest plans, near
+ *   67 MB, need 128 query rows per K/V head at d = 256 over few heads).
+ *   Sharing: every call on one GPU uses the same array, and the partial results
+ *   of a call live there from its range kernel to its merge kernel. Calls that
+ *   overlap on one GPU (different streams, or host threads each enqueueing on
+ *   its own stream) race and give unspecified results: the caller serialises
+ *   them, for example by enqueueing them on one stream. Nothing in the array
+ *   needs to start at zero (every partial slot a merge reads is written first
+ *   by the same call), and the array keeps the last call's contents.
+ */
+int flash_attn_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                              int causal, int window, float scale, void* stream);
+
+/* Bytes of the static scratch array flash_attn_decode_noalloc uses on each GPU. */
+size_t flash_attn_decode_noalloc_max_bytes(void);
 
 /*
  * Backward pass of flash_attn_fwd_window: the gradients of sum(dout * O) under

@@ -63,7 +63,11 @@ def kernels(asm):
     lines = asm.split("\n")
     starts = [i for i, l in enumerate(lines) if re.match(r"^_ZN\S+:", l)]
     for s in starts:
-        e = next(i for i in range(s, len(lines)) if "s_endpgm" in lines[i])
+        # the next label, so a data symbol (the static scratch array) is no kernel
+        nxt = next((i for i in range(s + 1, len(lines)) if re.match(r"^_ZN\S+:", lines[i])), len(lines))
+        e = next((i for i in range(s, nxt) if "s_endpgm" in lines[i]), None)
+        if e is None:
+            continue
         yield lines[s].split(":")[0], lines[s + 1:e + 1]
 
 
