@@ -131,7 +131,7 @@ WORKLOADS = {
     # gqa16k's shape and FLOP count with d = 64 (twice the heads), forward and backward
     "gqa16k_d64": Workload(13, "gqa16k_d64", 2, 64, 16, 16384, 64, True, True, oracle_rows=128),
     # gqa16k's shape and FLOP count with d = 256 (half the query heads), forward only
-    "gqa16k_d256": Workload(11, "gqa16k_d256", 2, 16, 4, 16384, 256, True, False, oracle_rows=128),
+    "gqa16k_d256": Workload(11, "gqa16k_d256", 2, 16, 4, 16384, 256, True, True, oracle_rows=128),
 }
 
 

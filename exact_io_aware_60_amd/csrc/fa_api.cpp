@@ -27,13 +27,15 @@ thread_local char g_hip_text[256] = "";
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Head dimensions: 64 and 128 everywhere; 256 in the forward passes only
-// (forward = true), whose kernel has a 256-wide instance (decode, checked
-// apart, has one too).
-int check_shape(int B, int Hq, int Hkv, int N, int d, bool forward = false) {
+// Head dimensions: multiples of 8 from 8 to 256 in every pass. A d below 64,
+// 128 or 256 runs on that instance with zero columns past d.
+bool headdim_ok(int d, int dmax) { return d >= 8 && d <= dmax && d % 8 == 0; }
+
+int check_shape(int B, int Hq, int Hkv, int N, int d) {
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128 && !(forward && d == 256)) return FA_ERR_HEADDIM;
+    if (!headdim_ok(d, 256)) return FA_ERR_HEADDIM;
+    d = fa::padded_dim(d);   // the width the copies and tiles use
     // element counts and the largest launch grid must fit the kernels' index types
     const long double elems = (long double)B * Hq * N * d;
     if (elems >= 4.0e18L) return FA_ERR_SHAPE;
@@ -78,7 +80,7 @@ extern "C" {
 int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                    int Hkv, int N, int d, int causal, float scale, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    int st = check_shape(B, Hq, Hkv, N, d, true);
+    int st = check_shape(B, Hq, Hkv, N, d);
     if (st != FA_OK) return st;
     if ((st = check_scale(scale)) != FA_OK) return st;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -103,7 +105,7 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 int flash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                           int Hkv, int N, int d, int window, float scale, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    int st = check_shape(B, Hq, Hkv, N, d, true);
+    int st = check_shape(B, Hq, Hkv, N, d);
     if (st != FA_OK) return st;
     if (window < 1) return FA_ERR_SHAPE;
     if ((st = check_scale(scale)) != FA_OK) return st;
@@ -130,7 +132,7 @@ int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
                           const int* cu_seqlens, int B, int max_seqlen, int total, int Hq, int Hkv, int d,
                           int causal, float scale, void* stream) {
     if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_NULL;
-    int st = check_shape(B, Hq, Hkv, max_seqlen, d, true);
+    int st = check_shape(B, Hq, Hkv, max_seqlen, d);
     if (st != FA_OK) return st;
     if (total < 1 || (long double)Hq * total * d >= 4.0e18L) return FA_ERR_SHAPE;
     if ((st = check_scale(scale)) != FA_OK) return st;
@@ -262,7 +264,8 @@ namespace {
 int check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-    if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
+    if (!headdim_ok(d, 256)) return FA_ERR_HEADDIM;
+    d = fa::padded_dim(d);
     if (causal && Nq > Nk) return FA_ERR_SHAPE;
     // one K/V head fits a 32-bit buffer range with room for a ragged tile
     if ((long double)Nk * d * 2 >= 2147483648.0L) return FA_ERR_SHAPE;
@@ -400,7 +403,8 @@ const char* flash_attn_strerror(int status) {
         case FA_OK: return "success";
         case FA_ERR_NULL: return "a required pointer is NULL";
         case FA_ERR_SHAPE: return "unsupported shape: B, Hq, Hkv, N must be >= 1, Hq % Hkv == 0, sizes in range";
-        case FA_ERR_HEADDIM: return "unsupported head dimension: d must be 64 or 128 (or 256 in the forward passes and decode)";
+        case FA_ERR_HEADDIM:
+            return "unsupported head dimension: d must be a multiple of 8 from 8 to 256";
         case FA_ERR_ALIGN: return "a pointer is not 16-byte aligned (int32 length arrays: 4-byte)";
         case FA_ERR_WORKSPACE: return "workspace is NULL or too small";
         case FA_ERR_HIP: return g_hip_text[0] ? g_hip_text : "HIP launch failed";

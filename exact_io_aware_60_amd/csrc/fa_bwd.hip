@@ -35,7 +35,9 @@
 // dot D'_i = sum_j P_ij dP_ij from the probabilities it rebuilds, together
 // with PK_i = sum_j P_ij k_j. dS is linear in D, so dQ computed with the
 // approximate D plus (D - D') PK equals dQ computed with D'. The dK/dV kernel
-// runs after it and uses D'.
+// runs after it and uses D'. (Forming D' instead as D + sum_j dS_ij, one
+// v_dot2_f32_f16 per packed dS pair in place of one FMA per element, measured
+// 3.7% slower: each dot2 waits for the packed product just before it.)
 //
 // Two passes, no atomics: the dQ kernel owns a block of query rows and walks the
 // keys; the dK/dV kernel owns a block of keys and walks the query rows. Each
@@ -230,13 +232,15 @@ __device__ __forceinline__ int scale_exp(uint32_t mag_bits) {
 __device__ __forceinline__ int perm16(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // Rows [row0, row0 + 64) of one head: the fp16 copy (x * f) and, when dstT is
-// set, the transposed copy of the same rows. Rows >= N are written as zeros.
+// set, the transposed copy of the same rows. Rows >= N are written as zeros,
+// and so are columns >= dr: source rows hold dr values (a multiple of 8, at
+// most D), the copies D.
 // `tr` is a [64][D/2 + 1]-word LDS buffer (odd row pitch: the column reads of
 // the transpose hit distinct banks).
 template <int D>
 __device__ __forceinline__ void conv_tile(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                                           uint16_t* __restrict__ dstT, int row0, int N, int Np, float f,
-                                          uint32_t* tr) {
+                                          uint32_t* tr, int dr) {
     constexpr int CPR = D / 8;
     constexpr int CH = 64 * CPR / kThreads;
     constexpr int TW = D / 2 + 1;
@@ -247,7 +251,7 @@ __device__ __forceinline__ void conv_tile(const uint16_t* __restrict__ src, uint
         const int r = chunk / CPR, c = chunk % CPR;
         const int row = row0 + r;
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < N) x = *reinterpret_cast<const u32x4*>(src + (size_t)row * D + c * 8);
+        if (row < N && c * 8 < dr) x = *reinterpret_cast<const u32x4*>(src + (size_t)row * dr + c * 8);
         u32x4 y;
 #pragma unroll
         for (int t = 0; t < 4; ++t) y[t] = pack_f16(bf16_lo(x[t]) * f, bf16_hi(x[t]) * f);
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
     }
     // |dS| <= |dP| + |D| <= 2 d max|dO| max|V| < 2^(1 + log2 d + eO + eV), with
     // max|X| < 2^eX = 2^(14 - sX).
-    constexpr int LOG2D = D == 128 ? 7 : 6;
+    constexpr int LOG2D = D == 256 ? 8 : (D == 128 ? 7 : 6);
     const int eO = 14 - sx[3], eV = 14 - sx[2];
     const int sS = (mags[3] == 0 || mags[2] == 0) ? 0 : 14 - (1 + LOG2D + eO + eV);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -329,8 +333,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
         else if (which == 1) { src = p.k; dst = p.k16; dstT = p.kT16; }
         else if (which == 2) { src = p.v; dst = p.v16; dstT = nullptr; }
         else { src = p.dout; dst = p.do16; dstT = p.doT16; }
-        conv_tile<D>(src + (size_t)h * N * D, dst + (size_t)h * Np * D,
-                     dstT ? dstT + (size_t)h * D * Np : nullptr, rb * 64, N, Np, ldexpf(1.f, sx[which]), tr);
+        conv_tile<D>(src + (size_t)h * N * p.d, dst + (size_t)h * Np * D,
+                     dstT ? dstT + (size_t)h * D * Np : nullptr, rb * 64, N, Np, ldexpf(1.f, sx[which]), tr, p.d);
     }
     // Row dot: D / 8 lanes share one row (16 bytes each).
     constexpr int LPR = D / 8;
@@ -342,12 +346,12 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p) {
         const long long rp = base + threadIdx.x / LPR;
         const long long bh = rp / Np;
         const int q = (int)(rp - bh * Np);
-        const bool real = rp < rows && q < N;
+        const bool real = rp < rows && q < N && sub * 8 < p.d;
         const long long row = bh * N + q;
         float acc = 0.f;
         if (real) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + sub * 8);
-            const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + row * D + sub * 8);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * p.d + sub * 8);
+            const u32x4 g = *reinterpret_cast<const u32x4*>(p.dout + row * p.d + sub * 8);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 acc = fmaf(bf16_lo(a[t]), bf16_lo(g[t]), acc);
@@ -786,8 +790,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 
     // dK^T / dV^T blocks: lane holds key l32, d rows db*32 + u*8 + hh*4 + 0..3.
     if (key < N) {
-        uint16_t* dKg = p.dk + ((size_t)bkv * N + key) * D;
-        uint16_t* dVg = p.dv + ((size_t)bkv * N + key) * D;
+        // rows of dr = p.d values (D, or fewer: the copies' columns past them are zero)
+        const int dr = p.d;
+        uint16_t* dKg = p.dk + ((size_t)bkv * N + key) * dr;
+        uint16_t* dVg = p.dv + ((size_t)bkv * N + key) * dr;
         const float fk = p.scales[3], fv = p.scales[2];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -798,8 +804,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
                 a[1] = pack_bf16(S.dk[db][u * 4 + 2] * fk, S.dk[db][u * 4 + 3] * fk);
                 c[0] = pack_bf16(S.dv[db][u * 4 + 0] * fv, S.dv[db][u * 4 + 1] * fv);
                 c[1] = pack_bf16(S.dv[db][u * 4 + 2] * fv, S.dv[db][u * 4 + 3] * fv);
-                *reinterpret_cast<u32x2*>(dKg + db * 32 + u * 8 + hh * 4) = a;
-                *reinterpret_cast<u32x2*>(dVg + db * 32 + u * 8 + hh * 4) = c;
+                if (db * 32 + u * 8 + hh * 4 < dr) {
+                    *reinterpret_cast<u32x2*>(dKg + db * 32 + u * 8 + hh * 4) = a;
+                    *reinterpret_cast<u32x2*>(dVg + db * 32 + u * 8 + hh * 4) = c;
+                }
             }
     }
 }
@@ -1221,7 +1229,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
     // exact row dot (the lane halves hold half of the keys each), in units of 2^sS
     const float dx = (S.dacc + swap_half(S.dacc)) * c1;
     if (r0 < N && qrow < N) {
-        uint16_t* dQg = p.dq + ((size_t)bh * N + qrow) * D;
+        const int dr = p.d;   // rows of dr values (D, or fewer: padded copies)
+        uint16_t* dQg = p.dq + ((size_t)bh * N + qrow) * dr;
         const float sc = p.scales[4];
         const float corr = S.dd - dx;
 #pragma unroll
@@ -1234,9 +1243,362 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
                 u32x2 val;
                 val[0] = pack_bf16(v4[0], v4[1]);
                 val[1] = pack_bf16(v4[2], v4[3]);
-                *reinterpret_cast<u32x2*>(dQg + db * 32 + u * 8 + hh * 4) = val;
+                if (db * 32 + u * 8 + hh * 4 < dr) *reinterpret_cast<u32x2*>(dQg + db * 32 + u * 8 + hh * 4) = val;
             }
         if (hh == 0) p.delta[(size_t)bh * Np + qrow] = dx;   // for the dK/dV kernel
+    }
+}
+
+// ---------------------------------------------------------------- d = 256: split head dimension
+// A wave's K and V (dK/dV pass) or Q and dO (dQ pass) over all 256 columns take
+// 128 registers, and the four accumulators of the full width 256 more: no room
+// for the scores. So each gradient pass runs two workgroups per tile, one per
+// half of the accumulated columns (kSplitDH = 128): both compute S and dP over
+// all 256 columns, and each accumulates its half of dK, dV (or dQ, PK). The
+// LDS then holds one stage (a row tile of 256 columns is 33 KiB), every step
+// runs the plain masked path, and no step overlaps the next one's copy. This
+// trades speed (S and dP are computed twice) for a register budget that fits.
+constexpr int kSplitDH = 128;
+
+template <int D>
+struct KvSplitCfg {
+    static constexpr int DS = D / 16, DBH = kSplitDH / 32;
+    static constexpr int SR = RowPad<D>::STRIDE;          // Q, dO rows: [64][D], padded rows
+    static constexpr int RT = padded_tile_bytes<SR, kKV_Q>();
+    static constexpr int TT = kSplitDH * 2 * kKV_Q;        // Q^T, dO^T of one half: [DH][64], swizzled
+    static constexpr int QR = 0, DOR = RT, QT = 2 * RT, DOT = 2 * RT + TT;
+    static constexpr int L2 = 2 * RT + 2 * TT, DD = L2 + 4 * kKV_Q;
+    static constexpr int LDS = DD + 4 * kKV_Q;             // one stage
+    using PlanR = CopyPlan<D, SR, kKV_Q, 4>;
+    using PlanT = CopyPlanSwz<2 * kKV_Q, kSplitDH, 4>;
+    using Addr = LaneAddr<SR, Swz128>;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(QT % 128 == 0 && DOT % 128 == 0, "swizzled tiles start on 128 bytes");
+};
+
+template <int D>
+struct KvSplitState {
+    u32x4 kf[D / 16], vf[D / 16];          // K, V as the B operand (all columns)
+    f32x16 dk[kSplitDH / 32], dv[kSplitDH / 32];   // dK^T, dV^T of this workgroup's half
+};
+
+// One step of 64 query rows against the wave's 32 keys, every entry masked
+// as in kv_step_masked (causal: keys above the row; bounded masks: rows
+// outside [kbeg, kend)); the transposed tiles hold this half's columns.
+template <int D, bool WIN>
+__device__ __forceinline__ void kv_split_step(const FA_LDS uint8_t* __restrict__ st, KvSplitState<D>& S,
+                                              const typename KvSplitCfg<D>::Addr& la, int lbase, int q0, int key,
+                                              float sl2, float c1, int hh, bool causal, int kbeg, int kend) {
+    using C = KvSplitCfg<D>;
+    constexpr int DS = C::DS, DBH = C::DBH;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = zero16();
+        dp[qb] = zero16();
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            s[qb] = mfma32h(lds_read16b(st, la.row(qb, ds) + C::QR), S.kf[ds], s[qb]);
+            dp[qb] = mfma32h(lds_read16b(st, la.row(qb, ds) + C::DOR), S.vf[ds], dp[qb]);
+        }
+    u32x4 pp[4], dsp[4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const f32x4 lv = *reinterpret_cast<const FA_LDS f32x4*>(st + C::L2 + lbase + (qb * 32 + u * 8) * 4);
+            const f32x4 dv4 = *reinterpret_cast<const FA_LDS f32x4*>(st + C::DD + lbase + (qb * 32 + u * 8) * 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = u * 4 + e;
+                const int q = q0 + qb * 32 + u * 8 + hh * 4 + e;
+                float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[e]));
+                if ((causal && key > q) || (WIN && (q < kbeg || q >= kend))) x = 0.f;
+                s[qb][i] = x;
+                dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[e]);
+            }
+        }
+#pragma unroll
+    for (int qc = 0; qc < 4; ++qc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int i = (qc & 1) * 8 + 2 * w;
+            pp[qc][w] = pack_f16(s[qc >> 1][i], s[qc >> 1][i + 1]);
+            dsp[qc][w] = pack_f16(dp[qc >> 1][i], dp[qc >> 1][i + 1]);
+        }
+#pragma unroll
+    for (int qc = 0; qc < 4; ++qc)
+#pragma unroll
+        for (int db = 0; db < DBH; ++db) {
+            S.dv[db] = mfma32h(la.t.read(st + C::DOT, db * 32, qc), pp[qc], S.dv[db]);
+            S.dk[db] = mfma32h(la.t.read(st + C::QT, db * 32, qc), dsp[qc], S.dk[db]);
+        }
+}
+
+template <int D, bool WIN>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_split_kernel(BwdParams p) {
+    using C = KvSplitCfg<D>;
+    constexpr int DS = C::DS, DBH = C::DBH;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+    FA_LDS uint8_t* st = (FA_LDS uint8_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int N = p.N, Np = p.Np, G = p.G;
+    const bool causal = p.causal != 0;
+    int kt, unit;
+    unmap_block_unit_major(blockIdx.x, p.B * p.Hkv * 2, (N + kKV_WG - 1) / kKV_WG, kt, unit);
+    const int half = unit & 1, bkv = unit >> 1;
+    const int b = bkv / p.Hkv, hkv = bkv - b * p.Hkv;
+    const int k0 = kt * kKV_WG, kw0 = k0 + w * kKV_W, key = kw0 + l32;   // key < Np: padded rows are zero
+    const float sl2 = p.scales[0], c1 = p.scales[1];
+
+    KvSplitState<D> S;
+    {
+        const uint16_t* Kg = p.k16 + ((size_t)bkv * Np + key) * D;
+        const uint16_t* Vg = p.v16 + ((size_t)bkv * Np + key) * D;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            S.kf[ds] = *reinterpret_cast<const u32x4*>(Kg + ds * 16 + hh * 8);
+            S.vf[ds] = *reinterpret_cast<const u32x4*>(Vg + ds * 16 + hh * 8);
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < DBH; ++db) {
+        S.dk[db] = zero16();
+        S.dv[db] = zero16();
+    }
+    // the row blocks that can see a key of this workgroup (as bwd_dkdv_kernel)
+    const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
+    const int kend = WIN ? bd.row_end(key) : 0;
+    const bool lbnd = WIN && !causal;
+    const int kbeg = lbnd ? bd.first_key(key) : 0;
+    const int qs = causal ? k0 : (lbnd ? bd.first_key(k0) / kKV_Q * kKV_Q : 0);
+    const int qe = WIN ? min(N, bd.row_end(k0 + kKV_WG - 1)) : N;
+    const int nrb = max(0, (qe - qs + kKV_Q - 1) / kKV_Q);
+    const int nsteps = G * nrb;
+
+    KvRes rs;
+    {
+        const size_t bh0 = (size_t)b * p.Hq + (size_t)hkv * G;
+        const uint32_t nrow = (uint32_t)G * Np;
+        rs.q = make_bufres(p.q16 + bh0 * Np * D, nrow * D * 2);
+        rs.dout = make_bufres(p.do16 + bh0 * Np * D, nrow * D * 2);
+        rs.qt = make_bufres(p.qT16 + bh0 * D * Np, nrow * D * 2);
+        rs.dot = make_bufres(p.doT16 + bh0 * D * Np, nrow * D * 2);
+        rs.l2 = make_bufres(p.lse2 + bh0 * Np, nrow * 4);
+        rs.dd = make_bufres(p.delta + bh0 * Np, nrow * 4);
+    }
+    typename C::PlanR pr;
+    typename C::PlanT pt;
+    pr.init(w, lane, D);
+    pt.init(w, lane, Np);
+    typename C::Addr la;
+    la.init(l32, hh);
+    const int lbase = hh * 16;
+    for (int j = 0; j < nsteps; ++j) {
+        const uint32_t g = j % G;
+        const int q0 = qs + (j / G) * kKV_Q;
+        const uint32_t rows = (g * Np + q0) * D * 2;
+        const uint32_t tr = (g * D + half * kSplitDH) * Np * 2 + q0 * 2;   // this half's d rows
+        const uint32_t row4 = (g * Np + q0) * 4;
+        pr.copy(rs.q, rows, st + C::QR, w);
+        pr.copy(rs.dout, rows, st + C::DOR, w);
+        pt.copy(rs.qt, tr, st + C::QT, w);
+        pt.copy(rs.dot, tr, st + C::DOT, w);
+        if (w == 0) bload_lds4(rs.l2, lane * 4, row4, st + C::L2);
+        if (w == 1) bload_lds4(rs.dd, lane * 4, row4, st + C::DD);
+        wait_vmem();
+        __syncthreads();
+        kv_split_step<D, WIN>(st, S, la, lbase, q0, key, sl2, c1, hh, causal, kbeg, kend);
+        __syncthreads();
+    }
+    if (key < N) {
+        const int dr = p.d;
+        uint16_t* dKg = p.dk + ((size_t)bkv * N + key) * dr + half * kSplitDH;
+        uint16_t* dVg = p.dv + ((size_t)bkv * N + key) * dr + half * kSplitDH;
+        const float fk = p.scales[3], fv = p.scales[2];
+#pragma unroll
+        for (int db = 0; db < DBH; ++db)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                u32x2 a, c;
+                a[0] = pack_bf16(S.dk[db][u * 4 + 0] * fk, S.dk[db][u * 4 + 1] * fk);
+                a[1] = pack_bf16(S.dk[db][u * 4 + 2] * fk, S.dk[db][u * 4 + 3] * fk);
+                c[0] = pack_bf16(S.dv[db][u * 4 + 0] * fv, S.dv[db][u * 4 + 1] * fv);
+                c[1] = pack_bf16(S.dv[db][u * 4 + 2] * fv, S.dv[db][u * 4 + 3] * fv);
+                if (half * kSplitDH + db * 32 + u * 8 + hh * 4 < dr) {
+                    *reinterpret_cast<u32x2*>(dKg + db * 32 + u * 8 + hh * 4) = a;
+                    *reinterpret_cast<u32x2*>(dVg + db * 32 + u * 8 + hh * 4) = c;
+                }
+            }
+    }
+}
+
+template <int D>
+struct QSplitCfg {
+    static constexpr int DS = D / 16, DBH = kSplitDH / 32;
+    static constexpr int SR = RowPad<D>::STRIDE;          // K, V rows: [64][D], padded rows
+    static constexpr int RT = padded_tile_bytes<SR, kQ_N>();
+    static constexpr int ST = RowPad<kQ_N>::STRIDE;       // K^T of one half: [DH][64], padded rows
+    static constexpr int TT = padded_tile_bytes<ST, kSplitDH>();
+    static constexpr int KR = 0, VR = RT, KT = 2 * RT;
+    static constexpr int LDS = 2 * RT + TT;               // one stage
+    using PlanR = CopyPlan<D, SR, kQ_N, 4>;
+    using PlanT = CopyPlan<kQ_N, ST, kSplitDH, 4>;
+    using Addr = LaneAddr<SR, PadRows<ST>>;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int D>
+struct QSplitState {
+    u32x4 qf[D / 16], dof[D / 16];                 // Q, dO as the B operand (all columns)
+    f32x16 dq[kSplitDH / 32], pk[kSplitDH / 32];   // dQ^T, PK^T of this workgroup's half
+    float l2, dd, dacc;                             // LSE log2 e, D 2^sS, running sum of P dP'
+};
+
+// One tile of 64 keys, every entry masked as in dq_masked; the exact row dot
+// sums over all columns of dP, so both halves form the same value.
+template <int D, bool WIN>
+__device__ __forceinline__ void dq_split_step(QSplitState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
+                                              const typename QSplitCfg<D>::Addr& la, int key0, int qrow, int N,
+                                              bool causal, float sl2, float c1, int hh, int lbq, int ubq) {
+    using C = QSplitCfg<D>;
+    constexpr int DS = C::DS, DBH = C::DBH;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = zero16();
+        dp[kb] = zero16();
+    }
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = mfma32h(lds_read16b(cur, la.row(kb, ds) + C::KR), S.qf[ds], s[kb]);
+            dp[kb] = mfma32h(lds_read16b(cur, la.row(kb, ds) + C::VR), S.dof[ds], dp[kb]);
+        }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kk = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+            float x = fast_exp2(fmaf(s[kb][i], sl2, -S.l2));
+            if (kk >= N || (causal && kk > qrow) || (WIN && (kk < lbq || kk >= ubq))) x = 0.f;
+            const float dpv = dp[kb][i];
+            S.dacc = fmaf(x, dpv, S.dacc);
+            s[kb][i] = x;
+            dp[kb][i] = x * fmaf(dpv, c1, -S.dd);
+        }
+    u32x4 pp[4], dsp[4];
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int i = (kc & 1) * 8 + 2 * w;
+            pp[kc][w] = pack_f16(s[kc >> 1][i], s[kc >> 1][i + 1]);
+            dsp[kc][w] = pack_f16(dp[kc >> 1][i], dp[kc >> 1][i + 1]);
+        }
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int db = 0; db < DBH; ++db) {
+            const u32x4 a = la.t.read(cur + C::KT, db * 32, kc);
+            S.pk[db] = mfma32h(a, pp[kc], S.pk[db]);
+            S.dq[db] = mfma32h(a, dsp[kc], S.dq[db]);
+        }
+}
+
+template <int D, bool WIN>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_split_kernel(BwdParams p) {
+    using C = QSplitCfg<D>;
+    constexpr int DS = C::DS, DBH = C::DBH;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+    FA_LDS uint8_t* cur = (FA_LDS uint8_t*)smem;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int N = p.N, Np = p.Np;
+    const bool causal = p.causal != 0;
+    const int nqt = (N + kQ_WG - 1) / kQ_WG;
+    int rank, unit;
+    unmap_block_unit_major(blockIdx.x, p.B * p.Hq * 2, nqt, rank, unit);
+    const int half = unit & 1, bh = unit >> 1;
+    const int qt = causal ? nqt - 1 - rank : rank;
+    const int b = bh / p.Hq, hq = bh - b * p.Hq;
+    const size_t bkv = (size_t)b * p.Hkv + hq / p.G;
+    const BufRes rk = make_bufres(p.k16 + bkv * Np * D, (uint32_t)Np * D * 2);
+    const BufRes rv = make_bufres(p.v16 + bkv * Np * D, (uint32_t)Np * D * 2);
+    const BufRes rkt = make_bufres(p.kT16 + (bkv * D + half * kSplitDH) * Np, (uint32_t)Np * kSplitDH * 2);
+    const float sl2 = p.scales[0], c1 = p.scales[1];
+
+    const int q0 = qt * kQ_WG, r0 = q0 + w * kQ_W, qrow = r0 + l32;   // qrow < Np
+    const int ntk = (N + kQ_N - 1) / kQ_N;
+    const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
+    const bool ubnd = WIN && !causal;
+    auto ub_of = [&](int r) { return bd.row_end(min(r, N - 1)); };
+    const int nt = causal ? min(ntk, (q0 + kQ_WG - 1) / kQ_N + 1)
+                          : (ubnd ? max(1, min(ntk, (ub_of(q0 + kQ_WG - 1) + kQ_N - 1) / kQ_N)) : ntk);
+    const int jst = WIN ? max(0, bd.first_key(q0)) / kQ_N : 0;
+    const int lbq = WIN ? bd.first_key(qrow) : 0;
+    const int ubq = ubnd ? bd.row_end(qrow) : N;
+
+    QSplitState<D> S;
+    {
+        const size_t ro = ((size_t)bh * Np + qrow) * D;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            S.qf[ds] = *reinterpret_cast<const u32x4*>(p.q16 + ro + ds * 16 + hh * 8);
+            S.dof[ds] = *reinterpret_cast<const u32x4*>(p.do16 + ro + ds * 16 + hh * 8);
+        }
+        S.l2 = p.lse2[(size_t)bh * Np + qrow];
+        S.dd = p.delta[(size_t)bh * Np + qrow];
+        S.dacc = 0.f;
+    }
+#pragma unroll
+    for (int db = 0; db < DBH; ++db) {
+        S.dq[db] = zero16();
+        S.pk[db] = zero16();
+    }
+    typename C::PlanR pr;
+    typename C::PlanT pt;
+    pr.init(w, lane, D);
+    pt.init(w, lane, Np);
+    typename C::Addr la;
+    la.init(l32, hh);
+    for (int j = jst; j < nt; ++j) {
+        pr.copy(rk, (uint32_t)j * kQ_N * D * 2, cur + C::KR, w);
+        pr.copy(rv, (uint32_t)j * kQ_N * D * 2, cur + C::VR, w);
+        pt.copy(rkt, (uint32_t)j * kQ_N * 2, cur + C::KT, w);
+        wait_vmem();
+        __syncthreads();
+        dq_split_step<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, hh, lbq, ubq);
+        __syncthreads();
+    }
+    const float dx = (S.dacc + swap_half(S.dacc)) * c1;
+    if (qrow < N) {
+        const int dr = p.d;
+        uint16_t* dQg = p.dq + ((size_t)bh * N + qrow) * dr + half * kSplitDH;
+        const float sc = p.scales[4];
+        const float corr = S.dd - dx;
+#pragma unroll
+        for (int db = 0; db < DBH; ++db)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float v4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v4[t] = fmaf(corr, S.pk[db][u * 4 + t], S.dq[db][u * 4 + t]) * sc;
+                u32x2 val;
+                val[0] = pack_bf16(v4[0], v4[1]);
+                val[1] = pack_bf16(v4[2], v4[3]);
+                if (half * kSplitDH + db * 32 + u * 8 + hh * 4 < dr)
+                    *reinterpret_cast<u32x2*>(dQg + db * 32 + u * 8 + hh * 4) = val;
+            }
+        // both halves form the same value; one stores it for the dK/dV kernel
+        if (hh == 0 && half == 0) p.delta[(size_t)bh * Np + qrow] = dx;
     }
 }
 
@@ -1272,6 +1634,26 @@ hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_dkdv_split_t(const BwdParams& p, hipStream_t stream) {
+    const int grid = p.B * p.Hkv * 2 * ((p.N + kKV_WG - 1) / kKV_WG);
+    if (p.window > 0 || p.cu_seqlens)
+        hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_split_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dq_split_t(const BwdParams& p, hipStream_t stream) {
+    const int grid = p.B * p.Hq * 2 * ((p.N + kQ_WG - 1) / kQ_WG);
+    if (p.window > 0 || p.cu_seqlens)
+        hipLaunchKernelGGL((bwd_dq_split_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((bwd_dq_split_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d) {
@@ -1279,7 +1661,8 @@ BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d) {
     BwdWorkspace w;
     w.Np = (N + kRowPad - 1) / kRowPad * kRowPad;
     const size_t rows = (size_t)B * Hq * w.Np;
-    const size_t nq = rows * d, nk = (size_t)B * Hkv * w.Np * d;
+    const size_t Dp = (size_t)padded_dim(d);   // the copies hold D = padded_dim(d) columns
+    const size_t nq = rows * Dp, nk = (size_t)B * Hkv * w.Np * Dp;
     const size_t chunks = (size_t)B * Hq * N * d / 8;
     const size_t want = (chunks + kThreads - 1) / kThreads;
     w.npart = (int)(want < 1024 ? (want > 0 ? want : 1) : 1024);
@@ -1300,9 +1683,15 @@ BwdWorkspace bwd_workspace_layout(int B, int Hq, int Hkv, int N, int d) {
 }
 
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream) {
-    if (stage == 0) return p.d == 128 ? launch_prep_t<128>(p, stream) : launch_prep_t<64>(p, stream);
-    if (stage == 1) return p.d == 128 ? launch_dq_t<128>(p, stream) : launch_dq_t<64>(p, stream);
-    return p.d == 128 ? launch_dkdv_t<128>(p, stream) : launch_dkdv_t<64>(p, stream);
+    if (padded_dim(p.d) == 256) {
+        if (stage == 0) return launch_prep_t<256>(p, stream);
+        if (stage == 1) return launch_dq_split_t<256>(p, stream);
+        return launch_dkdv_split_t<256>(p, stream);
+    }
+    const bool d128 = padded_dim(p.d) == 128;
+    if (stage == 0) return d128 ? launch_prep_t<128>(p, stream) : launch_prep_t<64>(p, stream);
+    if (stage == 1) return d128 ? launch_dq_t<128>(p, stream) : launch_dq_t<64>(p, stream);
+    return d128 ? launch_dkdv_t<128>(p, stream) : launch_dkdv_t<64>(p, stream);
 }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {

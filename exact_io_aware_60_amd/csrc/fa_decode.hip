@@ -54,7 +54,11 @@ constexpr int kDTarget = 256;          // workgroups the split aims for (one per
 // (-inf) give exact zeros under it.
 constexpr float kNoMax = -1e30f;
 
-template <int D>
+// PAD: tensor rows hold fewer than D values (a multiple of 8); tile columns
+// past them stay zero (CopyPlanSwz with PAD). Every tile row keeps at least
+// one source chunk, so each copy instruction still issues (with some lanes
+// off) and the vmcnt accounting of the ring holds.
+template <int D, bool PAD = false>
 struct DecCfg {
     static constexpr int DS = D / 16, DB = D / 32, L = 2 * D;
     static constexpr int KT = kDBN * L;             // one K or V tile
@@ -63,8 +67,8 @@ struct DecCfg {
     // flight while one is used)
     static constexpr int NS = D == 256 ? 2 : D == 128 ? 4 : 8;
     static constexpr int LDS = NS * STAGE;
-    using PlanK = CopyPlanSwz<L, kDBN, kDW, RowKey<L>>;
-    using PlanV = CopyPlanSwz<L, kDBN, kDW, TrKey<L>>;
+    using PlanK = CopyPlanSwz<L, kDBN, kDW, RowKey<L>, PAD>;
+    using PlanV = CopyPlanSwz<L, kDBN, kDW, TrKey<L>, PAD>;
     static constexpr int LOADS = PlanK::NT + PlanV::NT;   // copy loads per wave per tile
     static_assert((NS - 2) * LOADS <= 63, "the loads of the tiles in flight fit vmcnt");
     // per-lane state a wave hands to its partner in the final fold
@@ -219,9 +223,9 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 
 // One tile iteration: start the copy of a later tile (when there is one) into
 // stage W, then use the current tile from stage R.
-template <int D>
-__device__ __forceinline__ void dec_iteration(DecWave<D>& st, const typename DecCfg<D>::PlanK& pk,
-                                              const typename DecCfg<D>::PlanV& pv, BufRes rk, BufRes rv,
+template <int D, bool PAD>
+__device__ __forceinline__ void dec_iteration(DecWave<D>& st, const typename DecCfg<D, PAD>::PlanK& pk,
+                                              const typename DecCfg<D, PAD>::PlanV& pv, BufRes rk, BufRes rv,
                                               bool copy_next, uint32_t noff, FA_LDS uint8_t* __restrict__ W,
                                               const FA_LDS uint8_t* __restrict__ R, int w, bool active,
                                               int h0, int h1, int key0, int Nk, int pos, int lo, int mfrom,
@@ -240,9 +244,9 @@ __device__ __forceinline__ void dec_iteration(DecWave<D>& st, const typename Dec
     }
 }
 
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p) {
-    using C = DecCfg<D>;
+    using C = DecCfg<D, PAD>;
     constexpr int DB = C::DB, NS = C::NS;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
     FA_LDS uint8_t* ring = (FA_LDS uint8_t*)smem;
@@ -299,14 +303,19 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     const int vbase = vr * C::L + (tr_key<C::L>(vr) << 6) + ((g & 1) * 16 + 4 * (lane & 3)) * 2;
 
     DecWave<D> st;
+    // elements per row in the tensors: D, or with PAD the real head dimension
+    const int dr = PAD ? p.d : D;
     // Q through a buffer resource over this workgroup's rows: rows past the
-    // group's M (and lanes of idle waves) read zeros, with no branch.
+    // group's M (and lanes of idle waves) read zeros, with no branch; so do
+    // the padding columns (an offset past the resource, which is < 2^17 bytes).
     const int rq = active ? r : M;
-    const BufRes rq_res = make_bufres(p.q + ((size_t)grp * M + rblk * kDRows) * D, (uint32_t)rows_here * D * 2);
+    const BufRes rq_res = make_bufres(p.q + ((size_t)grp * M + rblk * kDRows) * dr, (uint32_t)rows_here * dr * 2);
 #pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds)
-        st.qf[ds] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                        rq_res, (uint32_t)((rq - rblk * kDRows) * D + ds * 16 + hh * 8) * 2u, 0, 0));
+    for (int ds = 0; ds < C::DS; ++ds) {
+        const int col = ds * 16 + hh * 8;
+        const uint32_t qoff = (!PAD || col < dr) ? (uint32_t)((rq - rblk * kDRows) * dr + col) * 2u : 0x7FFFFFF0u;
+        st.qf[ds] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq_res, qoff, 0, 0));
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.o[db] = zero16();
     st.m = kNoMax;
@@ -314,15 +323,19 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
 
     // K and V through buffer resources over the group's Nk rows: rows of a
     // ragged last tile past Nk read as zeros (and are masked).
-    const uint16_t* Kg = p.k + (size_t)grp * Nk * D;
-    const uint16_t* Vg = p.v + (size_t)grp * Nk * D;
-    const BufRes rk = make_bufres(Kg, (uint32_t)Nk * D * 2);
-    const BufRes rv = make_bufres(Vg, (uint32_t)Nk * D * 2);
+    const uint16_t* Kg = p.k + (size_t)grp * Nk * dr;
+    const uint16_t* Vg = p.v + (size_t)grp * Nk * dr;
+    const BufRes rk = make_bufres(Kg, (uint32_t)Nk * dr * 2);
+    const BufRes rv = make_bufres(Vg, (uint32_t)Nk * dr * 2);
     typename C::PlanK pk;
     typename C::PlanV pv;
-    pk.init(w, lane, D);
-    pv.init(w, lane, D);
-    constexpr uint32_t kTileBytes = kDBN * D * 2;
+    pk.init(w, lane, dr, dr);
+    pv.init(w, lane, dr, dr);
+    const uint32_t kTileBytes = kDBN * dr * 2;
+    if (PAD) {   // the columns no copy writes must read as zeros
+        lds_zero(ring, C::LDS, tid, kDThreads);
+        __syncthreads();
+    }
     if (nt > 0) {
     // Ring of NS stages: tiles j+1 .. j+NS-2 stay in flight while tile j is
     // used, and tile j+NS-1 goes into the stage tile j-1 used. The first NS-1
@@ -346,7 +359,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
         // wait for themselves, and the memory clobber keeps the copies in order.
         asm volatile("s_barrier" ::: "memory");
         const int jn = j + NS - 1;
-        dec_iteration<D>(st, pk, pv, rk, rv, jn < nt, (uint32_t)(t0 + jn) * kTileBytes,
+        dec_iteration<D, PAD>(st, pk, pv, rk, rv, jn < nt, (uint32_t)(t0 + jn) * kTileBytes,
                          ring + (jn % NS) * C::STAGE, ring + (j % NS) * C::STAGE, w, active, h0, h1,
                          (t0 + j) * kDBN, L, pos, lo, mfrom, mto, sl2, kbase, vbase, hh);
     }
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
     if (p.nsplit == 1) {
         // a single range: the final result (a row that sees no key gets
         // O = 0 and LSE = -inf)
-        uint16_t* Og = p.o + ((size_t)grp * M + r) * D;
+        uint16_t* Og = p.o + ((size_t)grp * M + r) * dr;
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -397,7 +410,8 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
                 u32x2 val;
                 val[0] = pack_bf16(st.o[db][u * 4 + 0] * inv, st.o[db][u * 4 + 1] * inv);
                 val[1] = pack_bf16(st.o[db][u * 4 + 2] * inv, st.o[db][u * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(Og + db * 32 + u * 8 + hh * 4) = val;
+                if (!PAD || db * 32 + u * 8 + hh * 4 < dr)
+                    *reinterpret_cast<u32x2*>(Og + db * 32 + u * 8 + hh * 4) = val;
             }
         if (hh == 0) p.lse[(size_t)grp * M + r] = lt > 0.f ? (st.m + __log2f(lt)) * kLn2 : -INFINITY;
         return;
@@ -425,7 +439,7 @@ __global__ __launch_bounds__(kDThreads, 1) void decode_split_kernel(DecParams p)
 // no key at all: O = 0 and LSE = -inf. Thread t takes 4 output values (column c) of the
 // ranges r = g, g + SG, ... (group g): the loads of all ranges go out
 // together instead of one range after another.
-template <int D>
+template <int D, bool PAD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     constexpr int C4 = D / 4;             // 4-value columns of a row
     constexpr int SG = 256 / C4;          // range groups
@@ -473,19 +487,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecParams p) {
     u32x2 val;
     val[0] = pack_bf16(acc[0] * inv, acc[1] * inv);
     val[1] = pack_bf16(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<u32x2*>(p.o + (size_t)row * D + c * 4) = val;
+    const int dr = PAD ? p.d : D;
+    if (!PAD || c * 4 < dr) *reinterpret_cast<u32x2*>(p.o + (size_t)row * dr + c * 4) = val;
     if (c == 0) p.lse[row] = wt > 0.f ? (mx + __log2f(wt)) * kLn2 : -INFINITY;
 }
 
-template <int D>
+template <int D, bool PAD>
 hipError_t launch_decode_t(const DecParams& p, hipStream_t stream) {
     const long long grid = (long long)p.B * p.Hkv * p.nrb * p.nsplit;
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)grid), dim3(kDThreads), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, PAD>), dim3((unsigned)grid), dim3(kDThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.nsplit == 1) return e;
     const long long rows = (long long)p.B * p.Hq * p.Nq;
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_merge_kernel<D, PAD>), dim3((unsigned)rows), dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecParams& p, hipStream_t stream) {
+    return p.d == D ? launch_decode_t<D, false>(p, stream) : launch_decode_t<D, true>(p, stream);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -511,14 +531,15 @@ DecPlan dec_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, int window) {
         const size_t n = (size_t)B * Hkv * pl.nsplit * pl.M;
         pl.part_lse = 0;
         pl.part_o = align256(n * 4);
-        pl.total = pl.part_o + align256(n * (size_t)d * 4);
+        pl.total = pl.part_o + align256(n * (size_t)padded_dim(d) * 4);   // partial O rows hold D values
     }
     return pl;
 }
 
 hipError_t launch_decode(const DecParams& p, hipStream_t stream) {
-    if (p.d == 256) return launch_decode_t<256>(p, stream);
-    return p.d == 128 ? launch_decode_t<128>(p, stream) : launch_decode_t<64>(p, stream);
+    const int D = padded_dim(p.d);
+    if (D == 256) return launch_decode_d<256>(p, stream);
+    return D == 128 ? launch_decode_d<128>(p, stream) : launch_decode_d<64>(p, stream);
 }
 
 // ---------------------------------------------------------------- static scratch
@@ -553,6 +574,5 @@ hipError_t decode_scratch(void** out) {
     *out = g_scratch_ptr[dev];
     return hipSuccess;
 }
-
 
 }  // namespace fa

@@ -241,25 +241,34 @@ template <int L> struct TrKey { __host__ __device__ static constexpr int key(int
 // 16-byte chunk c of row r goes to chunk position c ^ Key::key(r). Source row
 // r starts `pitch` elements after row r - 1; rows past the resource's end read
 // as zeros. Each lane's source offsets are computed once.
-template <int L, int ROWS, int NW, class Key = RowKey<L>>
+//
+// PAD: the source rows hold only the first `dr` (a multiple of 8, < L / 2)
+// 16-bit values of each tile row. Lanes whose chunk lies past them issue no
+// load, so their LDS bytes keep what the kernel put there (zeros; see
+// lds_zero): a tile row is then the source row followed by zero columns.
+template <int L, int ROWS, int NW, class Key = RowKey<L>, bool PAD = false>
 struct CopyPlanSwz {
     static constexpr int NB = ROWS * L / 1024;
     static constexpr int NT = NB / NW;
     static_assert(NB % NW == 0, "the tile splits evenly over the waves");
+    static_assert(NT <= 32, "one mask bit per block");
     uint32_t off[NT];
-    __device__ __forceinline__ void init(int w, int lane, int pitch) {
+    uint32_t vmask;   // PAD: bit t set when block t's chunk of this lane is a source chunk
+    __device__ __forceinline__ void init(int w, int lane, int pitch, int dr = 0) {
+        vmask = 0;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int pos = (w + NW * t) * 1024 + lane * 16;
             const int row = pos / L, phys = (pos % L) / 16;
             const int c = phys ^ Key::key(row);
             off[t] = (uint32_t)(row * pitch + c * 8) * 2u;
+            if (PAD && c * 8 < dr) vmask |= 1u << t;
         }
     }
     // Block t of wave ws (a scalar wave index).
     __device__ __forceinline__ void copy_one(int t, BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile,
                                              int ws) const {
-        bload_lds16(r, off[t], soff, tile + (ws + NW * t) * 1024);
+        if (!PAD || ((vmask >> t) & 1u)) bload_lds16(r, off[t], soff, tile + (ws + NW * t) * 1024);
     }
     __device__ __forceinline__ void copy(BufRes r, uint32_t soff, FA_LDS uint8_t* __restrict__ tile, int w) const {
         const int ws = __builtin_amdgcn_readfirstlane(w);
@@ -267,6 +276,14 @@ struct CopyPlanSwz {
         for (int t = 0; t < NT; ++t) copy_one(t, r, soff, tile, ws);
     }
 };
+
+// Zero `bytes` bytes of LDS from `base` (a multiple of 16 bytes), all threads
+// of the workgroup taking part; the caller synchronises before the bytes are
+// written again by global->LDS copies.
+__device__ __forceinline__ void lds_zero(FA_LDS uint8_t* base, int bytes, int tid, int nthreads) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int o = tid * 16; o < bytes; o += nthreads * 16) *reinterpret_cast<FA_LDS u32x4*>(base + o) = z;
+}
 
 // ---- per-lane fragment reads ----
 // Both structs read the A-operand fragment of a 32-row block: chunk pair c

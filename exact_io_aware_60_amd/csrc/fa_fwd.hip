@@ -65,7 +65,10 @@ constexpr float kSumMax = 256.0f;   // largest partial sum of P accepted without
 // a wave's Q and O alone take 192 registers, so 4 waves, one per SIMD (up to
 // 512 registers), and 128 rows per workgroup; its 3 K + 2 V tiles of 32 KiB
 // fill the 160 KiB of LDS.
-template <int D>
+// PAD: the tensors' rows hold fewer than D values (a multiple of 8); the
+// tiles' columns past them stay zero (CopyPlanSwz with PAD), so every product
+// over D columns equals the product over the real ones.
+template <int D, bool PAD = false>
 struct FwdCfg {
     static constexpr int DS = D / 16, DB = D / 32;
     static constexpr int WAVES = D == 256 ? 4 : 8;
@@ -74,8 +77,8 @@ struct FwdCfg {
     static constexpr int L = 2 * D;                              // bytes per K / V row
     static constexpr int KT = kBN * L, VT = kBN * L;
     static constexpr int LDS = 3 * KT + 2 * VT;
-    using PlanK = CopyPlanSwz<L, kBN, WAVES, RowKey<L>>;
-    using PlanV = CopyPlanSwz<L, kBN, WAVES, TrKey<L>>;
+    using PlanK = CopyPlanSwz<L, kBN, WAVES, RowKey<L>, PAD>;
+    using PlanV = CopyPlanSwz<L, kBN, WAVES, TrKey<L>, PAD>;
 };
 
 // Workgroup id -> (rank, bh). Workgroups are handed to the 8 XCDs round-robin,
@@ -231,10 +234,10 @@ __device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt
 // tile barrier; spread out, each load costs about one issue slot. Otherwise
 // (the chunk is the wave's last, or past it) `bulk` issues them all at once.
 // ON = false issues nothing.
-template <int D, bool ON>
+template <int D, bool ON, bool PAD = false>
 struct FwdCopies {
-    using PlanK = typename FwdCfg<D>::PlanK;
-    using PlanV = typename FwdCfg<D>::PlanV;
+    using PlanK = typename FwdCfg<D, PAD>::PlanK;
+    using PlanV = typename FwdCfg<D, PAD>::PlanV;
     static constexpr int NK = PlanK::NT, NI = PlanK::NT + PlanV::NT, SP = 2 * (D / 16) / NI;
     static_assert(SP >= 1, "copy items fit the steps");
     const PlanK* pk;
@@ -366,14 +369,14 @@ struct Window {
 // Kc: the K tile holding this chunk; Kn: the K tile holding the next chunk;
 // Kr1: K tile j+1, which holds chunk c+2 (half H); Vt: this chunk's V tile.
 // cp carries the iteration's copies (first chunk only).
-template <int D, int H, bool CP, bool WIN>
+template <int D, int H, bool CP, bool WIN, bool PAD>
 __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f32x16& sn,
                                           const FA_LDS uint8_t* __restrict__ Kc,
                                           const FA_LDS uint8_t* __restrict__ Kn,
                                           const FA_LDS uint8_t* __restrict__ Kr1,
                                           const FA_LDS uint8_t* __restrict__ Vt, int kbase, int vbase,
                                           bool causal, int qrow, int N, int lastc, float sl2, int hh,
-                                          const FwdCopies<D, CP>& cp, const Window& wd) {
+                                          const FwdCopies<D, CP, PAD>& cp, const Window& wd) {
     if (c > lastc) {
         cp.bulk();
         return;
@@ -418,27 +421,29 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
 // __restrict__ qualifiers say so, which lets the compiler see that the LDS
 // reads do not touch the LDS the in-flight global->LDS copies write, so it does
 // not wait for those copies before each read.
-template <int D, bool WIN>
-__device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, const typename FwdCfg<D>::PlanK& pk,
-                                              const typename FwdCfg<D>::PlanV& pv, BufRes rk, BufRes rv,
+template <int D, bool WIN, bool PAD>
+__device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt,
+                                              const typename FwdCfg<D, PAD>::PlanK& pk,
+                                              const typename FwdCfg<D, PAD>::PlanV& pv, BufRes rk, BufRes rv,
                                               FA_LDS uint8_t* __restrict__ Kw,
                                               FA_LDS uint8_t* __restrict__ Vw,
                                               const FA_LDS uint8_t* __restrict__ Kr0,
                                               const FA_LDS uint8_t* __restrict__ Kr1,
                                               const FA_LDS uint8_t* __restrict__ Vr, int kbase, int vbase,
                                               bool valid, bool causal, int qrow, int N, int lastc,
-                                              float sl2, int w, int lane, const Window& wd) {
+                                              float sl2, int w, int lane, const Window& wd, int dr) {
+    // dr: elements per row in the tensors (D, or fewer with PAD).
     // Tiles j + 1 and j + 2 may lie past the last one: their copies then read
     // past the resource (zeros) into buffers no chunk reads any more (those of
     // tiles j - 1 and j - 2).
-    const FwdCopies<D, true> cp{&pk, &pv, rk, rv, (uint32_t)(j + 2) * kBN * D * 2,
-                                (uint32_t)(j + 1) * kBN * D * 2, Kw, Vw, w};
+    const FwdCopies<D, true, PAD> cp{&pk, &pv, rk, rv, (uint32_t)(j + 2) * kBN * dr * 2,
+                                     (uint32_t)(j + 1) * kBN * dr * 2, Kw, Vw, w};
     if (valid) {
         const int hh = lane >> 5;
-        fwd_chunk<D, 0, true, WIN>(st, 2 * j, st.sA, st.sB, Kr0, Kr0, Kr1, Vr, kbase, vbase, causal, qrow, N,
+        fwd_chunk<D, 0, true, WIN, PAD>(st, 2 * j, st.sA, st.sB, Kr0, Kr0, Kr1, Vr, kbase, vbase, causal, qrow, N,
                                    lastc, sl2, hh, cp, wd);
-        fwd_chunk<D, 1, false, WIN>(st, 2 * j + 1, st.sB, st.sA, Kr0, Kr1, Kr1, Vr, kbase, vbase, causal, qrow, N,
-                                    lastc, sl2, hh, FwdCopies<D, false>{}, wd);
+        fwd_chunk<D, 1, false, WIN, PAD>(st, 2 * j + 1, st.sB, st.sA, Kr0, Kr1, Kr1, Vr, kbase, vbase, causal, qrow,
+                                         N, lastc, sl2, hh, FwdCopies<D, false, PAD>{}, wd);
     } else {
         cp.bulk();
     }
@@ -447,9 +452,9 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt, co
 // The causal flag is a run-time argument: it only changes the tile ranges and
 // the mask of each wave's last chunk, so one instance per head dimension
 // serves both cases.
-template <int D, bool WIN>
+template <int D, bool WIN, bool PAD>
 __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p) {
-    using C = FwdCfg<D>;
+    using C = FwdCfg<D, PAD>;
     constexpr int DS = C::DS, DB = C::DB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
     FA_LDS uint8_t* Ks = (FA_LDS uint8_t*)smem;          // 3 K tiles
@@ -489,9 +494,12 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
     }
     const int q0 = qt * kBM;
     if (q0 >= N) return;          // a q-tile past a shorter packed sequence (whole workgroup)
-    const uint16_t* Qg = p.q + qrow0 * D;
-    const uint16_t* Kg = p.k + kvrow0 * D;
-    const uint16_t* Vg = p.v + kvrow0 * D;
+    // elements per row in the tensors: D, or with PAD the real head dimension
+    // (a multiple of 8 below D); columns past it are zeros in every tile
+    const int dr = PAD ? p.d : D;
+    const uint16_t* Qg = p.q + qrow0 * dr;
+    const uint16_t* Kg = p.k + kvrow0 * dr;
+    const uint16_t* Vg = p.v + kvrow0 * dr;
 
     const int r0 = q0 + w * kWM;                 // this wave's first query row
     const int qrow = r0 + l32;                   // this lane's query row
@@ -513,7 +521,8 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
 
     FwdState<D> st;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) st.qf[ds] = gload16(Qg + (size_t)qrow * D + ds * 16 + hh * 8, qrow < N);
+    for (int ds = 0; ds < DS; ++ds)
+        st.qf[ds] = gload16(Qg + (size_t)qrow * dr + ds * 16 + hh * 8, qrow < N && (!PAD || ds * 16 + hh * 8 < dr));
 #pragma unroll
     for (int db = 0; db < DB; ++db) st.o[db] = zero16();
     st.m = 0.f;
@@ -522,18 +531,22 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
 
     // K and V through buffer resources covering the head's N rows: rows of a
     // ragged last tile past N read as zeros (their scores are masked).
-    const BufRes rk = make_bufres(Kg, (uint32_t)N * D * 2);
-    const BufRes rv = make_bufres(Vg, (uint32_t)N * D * 2);
+    const BufRes rk = make_bufres(Kg, (uint32_t)N * dr * 2);
+    const BufRes rv = make_bufres(Vg, (uint32_t)N * dr * 2);
     typename C::PlanK pk;
     typename C::PlanV pv;
-    pk.init(w, lane, D);
-    pv.init(w, lane, D);
+    pk.init(w, lane, dr, dr);
+    pv.init(w, lane, dr, dr);
+    if (PAD) {   // the columns no copy writes must read as zeros
+        lds_zero(Ks, C::LDS, tid, C::THREADS);
+        __syncthreads();
+    }
 
     // K tiles js, js+1 and V tile js before the loop (js = 0 without a window),
     // in the buffers the loop's index arithmetic expects for them.
-    pk.copy(rk, (uint32_t)js * kBN * D * 2, Ks + (js % 3) * C::KT, w);
-    if (nt > js + 1) pk.copy(rk, (uint32_t)(js + 1) * kBN * D * 2, Ks + ((js + 1) % 3) * C::KT, w);
-    pv.copy(rv, (uint32_t)js * kBN * D * 2, Vs + (js & 1) * C::VT, w);
+    pk.copy(rk, (uint32_t)js * kBN * dr * 2, Ks + (js % 3) * C::KT, w);
+    if (nt > js + 1) pk.copy(rk, (uint32_t)(js + 1) * kBN * dr * 2, Ks + ((js + 1) % 3) * C::KT, w);
+    pv.copy(rv, (uint32_t)js * kBN * dr * 2, Vs + (js & 1) * C::VT, w);
     wait_vmem();
     __syncthreads();
 
@@ -549,15 +562,16 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
         for (int i = 0; i < 16; ++i) st.sA[i] = fmaf(st.sA[i], sl2, -st.m);
     }
     for (int j = js; j < nt; ++j) {
-        fwd_iteration<D, WIN>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT, Vs + ((j + 1) & 1) * C::VT,
-                              Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT, Vs + (j & 1) * C::VT, kbase,
-                              vbase, wave_valid, causal, qrow, N, lastc, sl2, w, lane, wd);
+        fwd_iteration<D, WIN, PAD>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT,
+                                   Vs + ((j + 1) & 1) * C::VT, Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT,
+                                   Vs + (j & 1) * C::VT, kbase, vbase, wave_valid, causal, qrow, N, lastc, sl2, w,
+                                   lane, wd, dr);
         wait_vmem();
         __syncthreads();
     }
 
     if (wave_valid && qrow < N) {
-        uint16_t* Og = p.o + (qrow0 + qrow) * D;
+        uint16_t* Og = p.o + (qrow0 + qrow) * dr;
         // O is divided by the sum of the bf16 probabilities the P.V products
         // took, so each row's weights sum to one as used: a peaked row keeps
         // its dominant value's weight at 1 whatever that probability rounded
@@ -572,7 +586,8 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
                 u32x2 val;
                 val[0] = pack_bf16(st.o[db][u * 4 + 0] * inv, st.o[db][u * 4 + 1] * inv);
                 val[1] = pack_bf16(st.o[db][u * 4 + 2] * inv, st.o[db][u * 4 + 3] * inv);
-                *reinterpret_cast<u32x2*>(Og + db * 32 + u * 8 + hh * 4) = val;
+                if (!PAD || db * 32 + u * 8 + hh * 4 < dr)
+                    *reinterpret_cast<u32x2*>(Og + db * 32 + u * 8 + hh * 4) = val;
             }
         if (hh == 0) p.lse[qrow0 + qrow] = (st.m + __log2f(lt)) * kLn2;
     }
@@ -583,10 +598,14 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     using C = FwdCfg<D>;
     const int nqt = (p.N + C::BM - 1) / C::BM;
     const int grid = p.B * p.Hq * nqt;
-    if (p.window > 0)
-        hipLaunchKernelGGL((fwd_kernel<D, true>), dim3(grid), dim3(C::THREADS), 0, stream, p);
-    else
-        hipLaunchKernelGGL((fwd_kernel<D, false>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+    const bool pad = p.d != D;
+    if (p.window > 0) {
+        if (pad) hipLaunchKernelGGL((fwd_kernel<D, true, true>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+        else hipLaunchKernelGGL((fwd_kernel<D, true, false>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+    } else {
+        if (pad) hipLaunchKernelGGL((fwd_kernel<D, false, true>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+        else hipLaunchKernelGGL((fwd_kernel<D, false, false>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
@@ -606,12 +625,14 @@ Geometry geometry_t(int B, int Hq, int N) {
 
 Geometry fwd_geometry(int B, int Hq, int N, int d, int causal) {
     (void)causal;
-    return d == 256 ? geometry_t<256>(B, Hq, N) : d == 128 ? geometry_t<128>(B, Hq, N) : geometry_t<64>(B, Hq, N);
+    const int D = padded_dim(d);
+    return D == 256 ? geometry_t<256>(B, Hq, N) : D == 128 ? geometry_t<128>(B, Hq, N) : geometry_t<64>(B, Hq, N);
 }
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
-    if (p.d == 256) return launch_fwd_t<256>(p, stream);
-    return p.d == 128 ? launch_fwd_t<128>(p, stream) : launch_fwd_t<64>(p, stream);
+    const int D = padded_dim(p.d);
+    if (D == 256) return launch_fwd_t<256>(p, stream);
+    return D == 128 ? launch_fwd_t<128>(p, stream) : launch_fwd_t<64>(p, stream);
 }
 
 }  // namespace fa

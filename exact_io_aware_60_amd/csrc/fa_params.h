@@ -6,6 +6,11 @@
 
 namespace fa {
 
+// Padded width of a head dimension: the kernel instance that serves tensors
+// whose rows hold d values (d a multiple of 8, 8 <= d <= 256). Tiles and the
+// backward's copies hold D columns, the ones past d being zeros.
+__host__ __device__ constexpr int padded_dim(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
+
 struct FwdParams {
     const uint16_t* q;   // bf16 [B, Hq, N, d]
     const uint16_t* k;   // bf16 [B, Hkv, N, d]

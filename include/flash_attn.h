@@ -25,12 +25,15 @@
  * bfloat16, with H = Hq for q/o/dout/dq and H = Hkv for k/v/dk/dv. LSE is
  * contiguous [B, Hq, N] float32 (natural log). There are no stride arguments.
  *
- * Supported shapes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}, and also
- * d = 256 in the forward passes (flash_attn_fwd, _fwd_window, _fwd_varlen) and
- * in flash_attn_decode;
- * B*Hq*N*d < 2^62; (N + 128) * d < 2^31 and (Hq / Hkv) * (N + 128) * d * 2 <
- * 2^32 (32-bit offsets inside one head and one query-head group). scale must
- * be finite and >= 0. Other shapes return an error; there is no fallback path.
+ * Supported shapes: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d a multiple of 8 with
+ * 8 <= d <= 256 in every entry point. A d below 64, 128 or 256 runs on the
+ * kernels of that width with zero columns past d (tensors keep rows of d
+ * values; 32 and 96 are common model shapes); d above 128 in the backward runs
+ * gradient kernels that split the accumulated columns in halves of 128.
+ * With D = d rounded up to 64, 128 or 256: B*Hq*N*D < 2^62; (N + 128) * D <
+ * 2^31 and (Hq / Hkv) * (N + 128) * D * 2 < 2^32 (32-bit offsets inside one
+ * head and one query-head group). scale must be finite and >= 0. Other
+ * shapes return an error; there is no fallback path.
  *
  * Pointers are device pointers (hipMalloc'd or equivalent), 16-byte aligned.
  * `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue
@@ -60,7 +63,7 @@ enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = -1,      /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,     /* B, Hq, Hkv or N < 1, Hq % Hkv != 0, or sizes overflow */
-    FA_ERR_HEADDIM = -3,   /* d not in {64, 128} (forward passes, decode: not in {64, 128, 256}) */
+    FA_ERR_HEADDIM = -3,   /* d not a multiple of 8 in [8, 256] */
     FA_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned (int32 length arrays: 4-byte) */
     FA_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required */
     FA_ERR_HIP = -6,       /* a kernel launch failed (see flash_attn_strerror) */
@@ -123,10 +126,11 @@ int flash_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
  * shapes the backward rejects. Per head, rows are padded to Np = N rounded up
  * to a multiple of 128. The workspace holds two fp32 values per padded query
  * row (D = rowsum(dout * o) and LSE * log2(e)); fp16 copies of q, k, v and dout
- * scaled by powers of two, [.., Np, d]; transposed fp16 copies of q, dout and
- * k, [.., d, Np] (the operands of the backward's products); and a few KiB of
- * reduction scratch. In all, about 4 * |q| + 3 * |k| bytes for the bf16 sizes
- * |q| = B*Hq*N*d*2 and |k| = B*Hkv*N*d*2, plus 8 bytes per query row.
+ * scaled by powers of two, [.., Np, D]; transposed fp16 copies of q, dout and
+ * k, [.., D, Np] (the operands of the backward's products), where D is d
+ * rounded up to 64, 128 or 256 (the columns past d are zeros); and a few KiB of
+ * reduction scratch. In all, about 4 * |q| + 3 * |k| bytes for the sizes
+ * |q| = B*Hq*N*D*2 and |k| = B*Hkv*N*D*2, plus 8 bytes per query row.
  */
 size_t flash_attn_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal);
 
@@ -208,7 +212,7 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o
  * flash_attn_fwd_window), and only the cache tiles the window covers are
  * read. window = 0: no window. A row that sees no key at all (L_b = 0, or
  * L_b - Nq + i < 0) gets O = 0 and LSE = -inf.
- * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d in {64, 128, 256}; Nq <= Nk
+ * Supported: B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0; d as above (8 .. 256); Nq <= Nk
  * when causal; Nk * d * 2 < 2^31 bytes per K/V head. Any Nq is accepted; the path is made
  * for (Hq / Hkv) * Nq <= 128 query rows per K/V head, and larger counts read
  * the cache once per 128 rows. Inputs and outputs must not overlap.

@@ -72,20 +72,39 @@ def test_fwd_shape(over):
     assert fwd_call(**over) == fa.FA_ERR_SHAPE
 
 
-@pytest.mark.parametrize("d", [0, 16, 32, 63, 96, 129, 255, 257, 512])
+@pytest.mark.parametrize("d", [0, -8, 4, 12, 63, 129, 250, 255, 257, 264, 512])
 def test_fwd_headdim(d):
+    """Head dimensions are multiples of 8 from 8 to 256 in the forward passes."""
     assert fwd_call(d=d) == fa.FA_ERR_HEADDIM
 
 
-def test_d256_forward_only():
-    """d = 256 passes the forward passes' and decode's shape checks (their next
-    check, the scale, is reached) and is refused by the backward."""
+@pytest.mark.parametrize("d", [8, 16, 32, 40, 64, 80, 96, 112, 128, 136, 192, 256])
+def test_fwd_headdim_accepted(d):
+    """Multiples of 8 up to 256 pass the head-dimension check (the next check,
+    the scale, is reached); they run on the 64-, 128- or 256-wide instance."""
+    assert fwd_call(d=d, scale=-1.0) == fa.FA_ERR_SCALE
+    assert dec_call(d=d, scale=-1.0) == fa.FA_ERR_SCALE
+    assert varlen_call(d=d, scale=-1.0) == fa.FA_ERR_SCALE
+
+
+@pytest.mark.parametrize("d", [8, 16, 32, 40, 64, 80, 96, 112, 128, 136, 200, 256])
+def test_bwd_headdim_accepted(d):
+    assert bwd_call(d=d, scale=-1.0) == fa.FA_ERR_SCALE
+    pad = 64 if d <= 64 else (128 if d <= 128 else 256)
+    # the copies hold the padded width; only the reduction scratch follows d
+    ws, ws_pad = fa.bwd_workspace_size(1, 4, 2, 128, d, 1), fa.bwd_workspace_size(1, 4, 2, 128, pad, 1)
+    assert 0 < ws <= ws_pad and ws_pad - ws < 8192
+
+
+def test_d256_every_pass():
+    """d = 256 passes every entry point's shape checks (the next check, the
+    scale or the alignment, is reached)."""
     assert fwd_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert fwd_call(d=256, o=P[3] + 2) == fa.FA_ERR_ALIGN
-    assert bwd_call(d=256) == fa.FA_ERR_HEADDIM
+    assert bwd_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert dec_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert varlen_call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
-    assert fa.bwd_workspace_size(1, 4, 2, 128, 256, 1) == 0
+    assert fa.bwd_workspace_size(1, 4, 2, 128, 256, 1) > fa.bwd_workspace_size(1, 4, 2, 128, 128, 1)
 
 
 @pytest.mark.parametrize("scale", [-0.1, float("nan"), float("inf"), float("-inf")])
@@ -105,7 +124,8 @@ def test_bwd_null(name):
 
 def test_bwd_checks():
     assert bwd_call(Hq=3, Hkv=2) == fa.FA_ERR_SHAPE
-    assert bwd_call(d=96) == fa.FA_ERR_HEADDIM
+    assert bwd_call(d=100) == fa.FA_ERR_HEADDIM
+    assert bwd_call(d=264) == fa.FA_ERR_HEADDIM
     assert bwd_call(scale=float("nan")) == fa.FA_ERR_SCALE
     assert bwd_call(dk=P[7] + 8) == fa.FA_ERR_ALIGN
     assert bwd_call(ws=None) == fa.FA_ERR_WORKSPACE
@@ -145,13 +165,14 @@ def test_bwd_stages_validate(stage):
     bad[17] = need - 1
     assert fa.bwd_stage_raw(stage, *bad) == fa.FA_ERR_WORKSPACE
     bad = list(args)
-    bad[13] = 80
+    bad[13] = 84
     assert fa.bwd_stage_raw(stage, *bad) == fa.FA_ERR_HEADDIM
 
 
 def test_workspace_size_rejects_bad_shapes():
     assert fa.bwd_workspace_size(1, 3, 2, 64, 128, 1) == 0
-    assert fa.bwd_workspace_size(1, 4, 2, 64, 96, 1) == 0
+    assert fa.bwd_workspace_size(1, 4, 2, 64, 100, 1) == 0
+    assert fa.bwd_workspace_size(1, 4, 2, 64, 512, 1) == 0
 
 
 def dec_call(**over):
@@ -174,7 +195,8 @@ def test_decode_shape(over):
 
 
 def test_decode_checks():
-    assert dec_call(d=96) == fa.FA_ERR_HEADDIM
+    assert dec_call(d=97) == fa.FA_ERR_HEADDIM
+    assert dec_call(d=264) == fa.FA_ERR_HEADDIM
     assert dec_call(scale=-1.0) == fa.FA_ERR_SCALE
     assert dec_call(o=P[3] + 2) == fa.FA_ERR_ALIGN
     assert dec_call(sl=P[11] + 2) == fa.FA_ERR_ALIGN
@@ -236,7 +258,7 @@ def test_varlen_checks():
     assert varlen_call(ms=0) == fa.FA_ERR_SHAPE
     assert varlen_call(total=0) == fa.FA_ERR_SHAPE
     assert varlen_call(Hq=6, Hkv=4) == fa.FA_ERR_SHAPE
-    assert varlen_call(d=96) == fa.FA_ERR_HEADDIM
+    assert varlen_call(d=94) == fa.FA_ERR_HEADDIM
     assert varlen_call(scale=float("nan")) == fa.FA_ERR_SCALE
     assert varlen_call(cu=P[5] + 2) == fa.FA_ERR_ALIGN
     assert varlen_call(o=P[3] + 8) == fa.FA_ERR_ALIGN
@@ -252,7 +274,7 @@ def test_window_checks():
     assert call(W=0) == fa.FA_ERR_SHAPE
     assert call(W=-4) == fa.FA_ERR_SHAPE
     assert call(Hq=3) == fa.FA_ERR_SHAPE
-    assert call(d=32) == fa.FA_ERR_HEADDIM
+    assert call(d=36) == fa.FA_ERR_HEADDIM
     assert call(scale=-1.0) == fa.FA_ERR_SCALE
     assert call(d=256, scale=-1.0) == fa.FA_ERR_SCALE
     assert call(lse=P[4] + 4) == fa.FA_ERR_ALIGN

@@ -94,7 +94,7 @@ def test_decode_inflight_loads_untouched(decode_asm):
         nloads, bad = inflight_violations(lines)
         assert nloads > 0, name
         assert not bad, f"{name}: {len(bad)} instructions touch registers of LDS loads in flight, e.g. {bad[:3]}"
-    assert found == 3            # d = 64, 128, 256
+    assert found == 6            # d = 64, 128, 256, each with and without padded columns
 
 
 def test_checker_catches_a_touched_register():

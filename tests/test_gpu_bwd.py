@@ -273,3 +273,50 @@ def test_dynamic_range_of_the_fp16_operands(fa, d):
     for e in (0, -8):
         assert all(x <= TOL_GRAD for x in rel[e].values()), f"head at 2^{e}: {rel[e]}"
     assert np.max(np.abs(dq[:, 2:])) <= 2.0 ** -20 and np.max(np.abs(dk[:, 2:])) <= 2.0 ** -20
+
+
+@pytest.mark.parametrize("d", [8, 32, 40, 96, 112])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 33, 129, 300])
+def test_padded_headdim(fa, d, causal, N):
+    """Head dimensions below 64 and 128: the preparation writes the fp16 copies
+    with zero columns past d, the epilogues write d columns."""
+    inp = ai.make_case(1, 2, 2, N, d, seed=6200 + N * 3 + d + int(causal))
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"padded d={d} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("causal", [False, True])
+def test_padded_headdim_gqa(fa, d, causal):
+    inp = ai.make_case(2, 8, 2, 520, d, seed=6300 + d + int(causal))
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"padded gqa d={d} causal={causal}")
+
+
+# ------------------------------------------------------------------ head dimensions up to 256
+@pytest.mark.parametrize("d", [256, 136, 200])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 129, 300, 700])
+def test_wide_headdim(fa, d, causal, N):
+    """d above 128 runs the split gradient kernels (each half of the columns
+    in its own workgroup); every element against the oracle."""
+    inp = ai.make_case(1, 2, 2, N, d, seed=6400 + N * 3 + d + int(causal))
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"wide d={d} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_headdim_gqa(fa, causal):
+    inp = ai.make_case(2, 8, 2, 520, 256, seed=6500 + int(causal))
+    check_full(fa, inp, causal, 0.0625, f"wide gqa d=256 causal={causal}")
+
+
+def test_wide_headdim_large_logits(fa):
+    inp = ai.make_case(1, 4, 4, 1000, 256, seed=6600, dist_scale=2.0)
+    check_full(fa, inp, True, 0.2 * math.sqrt(128 / 256), "wide large logits")
+
+
+def test_wide_headdim_full_size(fa):
+    """d = 256 at a prefill size (B = 2, Hq = 16, Hkv = 4, N = 16384, causal):
+    one seeded (b, kv-head) group, every element of O, LSE, dQ, dK and dV."""
+    w = ai.WORKLOADS["gqa16k_d256"]
+    inp = ai.make_inputs(w, with_grad=True)
+    group_bwd_check(fa, w, inp, seeded_groups(w, 1))

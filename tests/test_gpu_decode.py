@@ -280,3 +280,27 @@ def test_window_many_ranges(fa):
     assert fa.decode_workspace_size(1, 4, 1, 2, 60000, 128, 1, 4096) < fa.decode_workspace_size(1, 4, 1, 2, 60000,
                                                                                                  128, 1)
     check_window(fa, inp, 4096, 0.0883883, "many ranges")
+
+
+# ------------------------------------------------------------------ head dimensions below 64 / 128 / 256
+@pytest.mark.parametrize("d", [8, 32, 96, 200])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(2, 8, 2, 1, 1000), (1, 16, 2, 5, 2049), (1, 8, 1, 16, 2500)],
+                         ids=["M4", "M40", "M128"])
+def test_padded_headdim(fa, shape, causal, d):
+    """Rows of d values on the 64-, 128- or 256-wide instance (split ranges and
+    the merge), every element against the oracle."""
+    B, Hq, Hkv, Nq, Nk = shape
+    inp = ai.make_decode_case(B, Hq, Hkv, Nq, Nk, d, seed=sum(shape) * 5 + d + int(causal))
+    check(fa, inp, causal, 1.0 / math.sqrt(d), f"padded d={d}")
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_padded_headdim_direct_and_seqlens(fa, d):
+    """One range per group (the range kernel writes O itself) and ragged lengths."""
+    B, Hq, Hkv, Nq, Nk = 64, 16, 8, 1, 200
+    assert fa.decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, 1) == 0
+    inp = ai.make_decode_case(B, Hq, Hkv, Nq, Nk, d, seed=7400 + d)
+    check(fa, inp, True, 1.0 / math.sqrt(d), f"padded direct d={d}")
+    inp = ai.make_decode_case(7, 4, 2, 3, 700, d, seed=7500 + d)
+    check_ragged(fa, inp, True, 1.0 / math.sqrt(d), [0, 1, 2, 65, 700, 5000, -3], f"padded seqlens d={d}")

@@ -228,3 +228,21 @@ def test_long_context_memory_footprint(fa):
     assert tensors == 4 * w.B * w.Hq * w.N * w.d * 2 + w.B * w.Hq * w.N * 4
     assert round(tensors / 1e9, 2) == 1.08
     assert w.B * w.Hq * w.N * w.N * 2 > 250 * tensors
+
+
+# ------------------------------------------------------------------ head dimensions below 64 / 128 / 256
+@pytest.mark.parametrize("d", [8, 32, 40, 96, 112, 200])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 64, 129, 300])
+def test_padded_headdim(fa, d, causal, N):
+    """Rows of d values run on the 64-, 128- or 256-wide instance with zero
+    columns past d: every element against the oracle at d itself."""
+    inp = ai.make_case(1, 2, 2, N, d, seed=6000 + N * 3 + d + int(causal), with_grad=False)
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"padded d={d} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [32, 96])
+def test_padded_headdim_gqa(fa, d):
+    inp = ai.make_case(2, 8, 2, 700, d, seed=6100 + d, with_grad=False)
+    check_full(fa, inp, True, 1.0 / math.sqrt(d), f"padded gqa d={d}")
+    check_full(fa, inp, False, 1.0 / math.sqrt(d), f"padded gqa d={d} noncausal")

@@ -221,3 +221,21 @@ def test_bwd_noncausal_equal_lengths_match_fixed(fa):
     for a, b_, name in ((dq, packed(gq), "dq"), (dk, packed(gk), "dk"), (dv, packed(gv), "dv")):
         err = (a.float() - b_.float()).abs().max().item()
         assert err <= 2e-2, f"{name}: {err}"
+
+
+@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("causal", [True, False])
+def test_padded_headdim(fa, d, causal):
+    """Packed sequences with head dimensions below 64 / 128: forward and backward."""
+    lens = [0, 64, 0, 513, 5]
+    inp = ai.make_varlen_case(lens, 4, 2, d, seed=7700 + d + int(causal))
+    check(fa, inp, causal, 1.0 / math.sqrt(d), f"padded d={d} lengths {lens}")
+    inp = make_grad_case([1, 17, 256, 257, 700], 4, 2, d, seed=7800 + d + int(causal))
+    check_bwd(fa, inp, 1.0 / math.sqrt(d), f"padded d={d}", causal=causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_wide_headdim_bwd(fa, causal):
+    """d = 256 packed sequences: the split gradient kernels with sequence bounds."""
+    inp = make_grad_case([1, 17, 256, 257, 700], 4, 2, 256, seed=8000 + int(causal))
+    check_bwd(fa, inp, 0.0625, "wide d=256", causal=causal)

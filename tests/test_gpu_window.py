@@ -183,3 +183,19 @@ def test_bwd_full_size_sampled(fa):
                              window=W)
     errs = {n: excess_err(g[n], ref[n]) for n in g}
     assert all(e <= TOL_GRAD for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("d", [32, 96])
+@pytest.mark.parametrize("N,W", [(300, 31), (1000, 129), (2049, 700)], ids=["N300-W31", "N1000-W129", "N2049-W700"])
+def test_padded_headdim(fa, N, W, d):
+    """Head dimensions below 64 / 128 with a window: forward and backward."""
+    inp = ai.make_case(1, 4, 2, N, d, seed=7600 + N + W + d)
+    check(fa, inp, W, 1.0 / math.sqrt(d), f"padded d={d}")
+    check_bwd(fa, inp, W, 1.0 / math.sqrt(d), f"padded d={d}")
+
+
+@pytest.mark.parametrize("N,W", [(300, 31), (1000, 129)], ids=["N300-W31", "N1000-W129"])
+def test_wide_headdim_bwd(fa, N, W):
+    """d = 256 with a window: the split gradient kernels with a bounded mask."""
+    inp = ai.make_case(1, 4, 2, N, 256, seed=7900 + N + W)
+    check_bwd(fa, inp, W, 0.0625, "wide d=256")
