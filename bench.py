@@ -23,6 +23,9 @@ workload under a sliding-window causal mask of W keys (flash_attn_fwd_window,
 flash_attn_bwd_window), counting 4*d FLOP per visible pair for the forward and
 2.5 times that for the backward: sum over rows of min(i + 1, W) pairs per head.
 
+With --fp8 NAME it measures the forward on E4M3 inputs (flash_attn_fwd_e4m3) at
+that workload's shape, against the FP8 MFMA peak (twice the bf16 one).
+
 With --decode NAME it measures instead the decode path (a few query rows over
 a long key/value cache) on one of the decode workloads, against the HBM
 roofline: the bytes the step must move (K and V once, Q, O and LSE) over the
@@ -98,6 +101,7 @@ KERNEL_SOURCES = {
     "fwd": ("fa_fwd.hip", "fa_device.h", "fa_params.h"),
     "bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_params.h"),
     "bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_params.h"),
+    "fwd8": ("fa_fwd8.hip", "fa_device.h", "fa_params.h"),
 }
 
 
@@ -124,6 +128,21 @@ def measured_traffic(kernel: str, workload: str = WORKLOAD):
             if m and m.group(1) == kernel and m.group(3) == want:
                 return int(m.group(2))
     return None
+
+
+def copy_calibration(mib: int, device) -> None:
+    """A plain device copy of `mib` MiB, 3 times (it reads and writes exactly
+    that much per launch), so that a profiled run holds the reference kernel
+    for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    if mib <= 0:
+        return
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=device)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 class ClockSampler:
@@ -329,14 +348,7 @@ def decode_main(args) -> int:
     wall = time.perf_counter() - t0
     times = [a.elapsed_time(b) for a, b in ev]
     ms = sum(times) / len(times)
-    if args.copy_calibration > 0:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device=q.device)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration, q.device)
     nbytes = decode_bytes(w)
     gbs = nbytes / (ms * 1e-3) / 1e9
     out = {
@@ -544,6 +556,94 @@ def varlen_main(args) -> int:
     return 0
 
 
+# MI355X dense FP8 (E4M3) MFMA peak: twice the bf16 rate.
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
+
+
+def fp8_main(args) -> int:
+    """The forward on E4M3 inputs (flash_attn_fwd_e4m3) at a fixed-length
+    workload's shape: quantised once before the timed region (the quantisers
+    are timed apart), then the forward kernel alone in the timed steps, against
+    the FP8 MFMA peak."""
+    import torch
+    import exact_io_aware_60_amd as fa
+
+    fa.lib()
+    w = ai.WORKLOADS[args.fp8]
+    rows = 128
+    inp = ai.make_inputs(w, with_grad=False)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp["q"]), dev(inp["k"]), dev(inp["v"])
+    del inp
+    stream = torch.cuda.current_stream()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(2):
+        e0.record(stream)
+        q8, qs = fa.quantize_e4m3(q, rows)
+        k8, ks = fa.quantize_e4m3(k, rows)
+        e1.record(stream)
+        v8t, vs = fa.quantize_e4m3_vt(v, rows)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    quant_ms = {"q_and_k": e0.elapsed_time(e1), "v_transposed": e1.elapsed_time(e2)}
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    P = [t.data_ptr() for t in (q8, qs, k8, ks, v8t, vs, o, lse)]
+    sp = stream.cuda_stream
+
+    def fwd():
+        st = fa.fwd_e4m3_raw(*P, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.scale, rows, sp)
+        if st != 0:
+            raise RuntimeError(f"fwd_e4m3: {fa.strerror(st)}")
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record(stream)
+        fwd()
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    copy_calibration(args.copy_calibration, q.device)
+    flop = algorithmic(w)["fwd"][1]
+    tflops = flop / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd TFLOP/s on E4M3 inputs (FP8 MFMA, causal) and % of MI355X FP8 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "precision": {"io": "E4M3 codes with fp32 run scales in, bf16 O, fp32 LSE",
+                      "mfma": "e4m3 x e4m3 -> fp32 (S and P.V; P rounded to e4m3)", "softmax": "fp32"},
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": w.causal,
+                   "passes": "fwd (e4m3)", "rows_per_scale": rows},
+        "quantize_ms": quant_ms,
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "roofline": {"bound": "mfma", "kernel": "fwd8_kernel", "achieved": tflops, "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_FP8_TFLOPS,
+                     "traffic": measured_traffic("fwd8", w.name),
+                     "traffic_unit": "bytes per launch (HBM read + write, rocprofv3 counters)",
+                     "avg_launch_ms": ms, "algorithmic_flop_per_launch": flop},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -568,6 +668,8 @@ def main() -> int:
                          "pass time the forward alone")
     ap.add_argument("--varlen", choices=sorted(ai.VARLEN_WORKLOADS), default=None,
                     help="measure the forward pass over this packed variable-length workload instead")
+    ap.add_argument("--fp8", choices=sorted(ai.WORKLOADS), default=None,
+                    help="measure the forward on E4M3 inputs (flash_attn_fwd_e4m3) at this workload's shape instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: the attention path here is single-GPU (asked for --gpus {args.gpus}).",
@@ -591,6 +693,12 @@ def main() -> int:
             print("bench.py needs a GPU", file=sys.stderr)
             return 2
         return varlen_main(args)
+    if args.fp8:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            return 2
+        return fp8_main(args)
 
     import torch
     import exact_io_aware_60_amd as fa
@@ -668,15 +776,7 @@ def main() -> int:
 
     clock = None if args.no_clock else sustained_clock(one_step, step_ms)
 
-    if args.copy_calibration > 0:
-        # reads and writes exactly copy_calibration MiB per launch
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device=q.device)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration, q.device)
 
     alg = algorithmic(w)
     dom = max(("fwd", "bwd_dkdv", "bwd_dq")[:3 if w.backward else 1], key=lambda n: kavg[n])

@@ -28,7 +28,8 @@ EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size",
             "flash_attn_version", "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
             "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen",
             "flash_attn_fwd_window", "flash_attn_bwd_window", "flash_attn_bwd_varlen",
-            "flash_attn_quantize_e4m3", "flash_attn_decode_noalloc", "flash_attn_decode_noalloc_max_bytes")
+            "flash_attn_quantize_e4m3", "flash_attn_decode_noalloc", "flash_attn_decode_noalloc_max_bytes",
+            "flash_attn_quantize_e4m3_vt", "flash_attn_fwd_e4m3")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_decode_workspace_size.argtypes = [_i] * 8
         L.flash_attn_quantize_e4m3.restype = _i
         L.flash_attn_quantize_e4m3.argtypes = [_vp] * 3 + [_i] * 4 + [_vp]
+        L.flash_attn_quantize_e4m3_vt.restype = _i
+        L.flash_attn_quantize_e4m3_vt.argtypes = [_vp] * 3 + [_i] * 4 + [_vp]
+        L.flash_attn_fwd_e4m3.restype = _i
+        L.flash_attn_fwd_e4m3.argtypes = [_vp] * 8 + [_i] * 6 + [ctypes.c_float, _i, _vp]
         L.flash_attn_strerror.restype = ctypes.c_char_p
         L.flash_attn_strerror.argtypes = [_i]
         L.flash_attn_version.restype = ctypes.c_char_p
@@ -168,6 +173,17 @@ def decode_noalloc_max_bytes() -> int:
 def quantize_e4m3_raw(x, codes, scales, BH, N, d, rows, stream=None) -> int:
     """flash_attn_quantize_e4m3 on raw addresses (ints); returns the status code."""
     return lib().flash_attn_quantize_e4m3(x, codes, scales, BH, N, d, rows, stream)
+
+
+def quantize_e4m3_vt_raw(x, codes_t, scales, BH, N, d, rows, stream=None) -> int:
+    """flash_attn_quantize_e4m3_vt on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_quantize_e4m3_vt(x, codes_t, scales, BH, N, d, rows, stream)
+
+
+def fwd_e4m3_raw(q8, qs, k8, ks, v8t, vs, o, lse, B, Hq, Hkv, N, d, causal, scale, rows, stream=None) -> int:
+    """flash_attn_fwd_e4m3 on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_fwd_e4m3(q8, qs, k8, ks, v8t, vs, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale),
+                                     int(rows), stream)
 
 
 def decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window: int = 0) -> int:
@@ -411,3 +427,54 @@ def quantize_e4m3(x, rows: int = 128):
     _check(quantize_e4m3_raw(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), BH, N, d, rows,
                              torch.cuda.current_stream().cuda_stream))
     return codes, scales
+
+
+def quantize_e4m3_vt(v, rows: int = 128):
+    """flash_attn_quantize_e4m3_vt: V's codes transposed for fwd_e4m3. v is a
+    contiguous bf16 [..., N, d] GPU tensor; returns (codes_t uint8
+    [..., d, Np], Np = N rounded up to 64, keys of every 64-key group in the
+    forward's operand order; scales float32 [..., ceil(N / rows)])."""
+    import torch
+    _checked(v, "v")
+    if v.dim() < 2:
+        raise ValueError("v must be [..., N, d]")
+    N, d = v.shape[-2], v.shape[-1]
+    BH = v.numel() // max(N * d, 1)
+    Np = -(-N // 64) * 64
+    codes_t = torch.empty((*v.shape[:-2], d, Np), dtype=torch.uint8, device=v.device)
+    rows = int(rows)
+    nruns = -(-N // rows) if rows > 0 else 1
+    scales = torch.empty((*v.shape[:-2], nruns), dtype=torch.float32, device=v.device)
+    _check(quantize_e4m3_vt_raw(v.data_ptr(), codes_t.data_ptr(), scales.data_ptr(), BH, N, d, rows,
+                                torch.cuda.current_stream().cuda_stream))
+    return codes_t, scales
+
+
+def fwd_e4m3(q8, q_scales, k8, k_scales, v8t, v_scales, rows: int, causal: bool = True, scale: float | None = None,
+             out=None, lse=None):
+    """Forward on 8-bit inputs (flash_attn_fwd_e4m3): q8 [B,Hq,N,d], k8
+    [B,Hkv,N,d] uint8 E4M3 codes with fp32 run scales, v8t [B,Hkv,d,Np] from
+    quantize_e4m3_vt. Returns (o bf16 [B,Hq,N,d], lse fp32 [B,Hq,N])."""
+    import torch
+    for t, name in ((q8, "q8"), (k8, "k8"), (v8t, "v8t")):
+        if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d uint8 GPU tensor")
+    for t, name in ((q_scales, "q_scales"), (k_scales, "k_scales"), (v_scales, "v_scales")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    Np = -(-N // 64) * 64
+    if tuple(k8.shape) != (B, Hkv, N, d) or tuple(v8t.shape) != (B, Hkv, d, Np):
+        raise ValueError("k8 must be [B, Hkv, N, d] and v8t [B, Hkv, d, Np]")
+    nruns = -(-N // int(rows)) if rows > 0 else 1
+    if (tuple(q_scales.shape) != (B, Hq, nruns) or tuple(k_scales.shape) != (B, Hkv, nruns)
+            or tuple(v_scales.shape) != (B, Hkv, nruns)):
+        raise ValueError("scale arrays must be [B, H, ceil(N / rows)]")
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _check(fwd_e4m3_raw(q8.data_ptr(), q_scales.data_ptr(), k8.data_ptr(), k_scales.data_ptr(), v8t.data_ptr(),
+                        v_scales.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d, causal, scale, rows,
+                        _stream(q8)))
+    return o, lse

@@ -19,6 +19,11 @@ namespace fa {
 // rows, [BH, ceil(N / rows)].
 hipError_t launch_quant_e4m3(const void* x, void* codes, float* scales, int BH, int N, int d, int rows,
                              hipStream_t stream);
+// The same codes and scales with V written transposed for the FP8 forward:
+// codes_t [BH, d, Np], Np = N rounded up to 64, keys of each 64-key group in
+// the order of the forward's P operand; rows a multiple of 64.
+hipError_t launch_quant_e4m3_vt(const void* x, void* codes_t, float* scales, int BH, int N, int d, int rows,
+                                hipStream_t stream);
 }  // namespace fa
 
 namespace {
@@ -376,6 +381,55 @@ int flash_attn_quantize_e4m3(const void* x, void* codes, float* scales, int BH, 
     if ((long double)std::min(rows, N) * d >= 2147483647.0L) return FA_ERR_SHAPE;
     if ((long double)BH * N * d >= 4.0e18L) return FA_ERR_SHAPE;
     return hip_status(fa::launch_quant_e4m3(x, codes, scales, BH, N, d, rows, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_quantize_e4m3_vt(const void* x, void* codes_t, float* scales, int BH, int N, int d, int rows,
+                                void* stream) {
+    if (!x || !codes_t || !scales) return FA_ERR_NULL;
+    if (BH < 1 || N < 1 || rows < 64 || rows % 64 != 0) return FA_ERR_SHAPE;
+    if (d < 8 || d % 8 != 0) return FA_ERR_HEADDIM;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(codes_t) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+        return FA_ERR_ALIGN;
+    const long long Np = (N + 63LL) / 64 * 64;
+    const long long runs = (N + (long long)rows - 1) / rows;
+    if ((long double)BH * runs >= 2147483647.0L) return FA_ERR_SHAPE;
+    if ((long double)std::min(rows, N) * d >= 2147483647.0L || (long double)Np * d >= 2147483647.0L)
+        return FA_ERR_SHAPE;
+    if ((long double)BH * Np * d >= 4.0e18L) return FA_ERR_SHAPE;
+    return hip_status(fa::launch_quant_e4m3_vt(x, codes_t, scales, BH, N, d, rows, static_cast<hipStream_t>(stream)));
+}
+
+int flash_attn_fwd_e4m3(const void* q8, const float* q_scales, const void* k8, const float* k_scales,
+                        const void* v8t, const float* v_scales, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                        int d, int causal, float scale, int rows, void* stream) {
+    if (!q8 || !q_scales || !k8 || !k_scales || !v8t || !v_scales || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (rows < 64 || rows % 64 != 0) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    int st = check_scale(scale);
+    if (st != FA_OK) return st;
+    const long long Np = (N + 63LL) / 64 * 64;
+    if ((long double)Np * d >= 2147483647.0L) return FA_ERR_SHAPE;            // one head's bytes, 32-bit
+    if ((long double)B * Hq * ((N + 255) / 256) >= 2147483647.0L) return FA_ERR_SHAPE;
+    if ((long double)B * Hq * Np * d >= 4.0e18L) return FA_ERR_SHAPE;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) || !aligned16(lse) ||
+        (reinterpret_cast<uintptr_t>(q_scales) & 3u) != 0 || (reinterpret_cast<uintptr_t>(k_scales) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(v_scales) & 3u) != 0)
+        return FA_ERR_ALIGN;
+    fa::Fwd8Params p;
+    p.q = static_cast<const uint8_t*>(q8);
+    p.q_scales = q_scales;
+    p.k = static_cast<const uint8_t*>(k8);
+    p.k_scales = k_scales;
+    p.vt = static_cast<const uint8_t*>(v8t);
+    p.v_scales = v_scales;
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.Np = (int)Np; p.d = d; p.G = Hq / Hkv; p.rows = rows;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    return hip_status(fa::launch_fwd8(p, static_cast<hipStream_t>(stream)));
 }
 
 int flash_attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,

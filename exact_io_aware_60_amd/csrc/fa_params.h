@@ -32,6 +32,21 @@ struct FwdParams {
     int window;
 };
 
+// Forward on 8-bit inputs (OCP E4M3 codes with one fp32 scale per run of
+// `rows` rows of each head; fa_fwd8.hip).
+struct Fwd8Params {
+    const uint8_t* q;        // E4M3 [B, Hq, N, d]
+    const float* q_scales;   // fp32 [B, Hq, ceil(N / rows)]
+    const uint8_t* k;        // E4M3 [B, Hkv, N, d]
+    const float* k_scales;   // fp32 [B, Hkv, ceil(N / rows)]
+    const uint8_t* vt;       // E4M3 [B, Hkv, d, Np]: V transposed, keys in MFMA order (flash_attn_quantize_e4m3_vt)
+    const float* v_scales;   // fp32 [B, Hkv, ceil(N / rows)]
+    uint16_t* o;             // bf16 [B, Hq, N, d]
+    float* lse;              // fp32 [B, Hq, N]
+    int B, Hq, Hkv, N, Np, d, G, rows, causal;
+    float scale_log2;        // softmax scale * log2(e)
+};
+
 struct BwdParams {
     const uint16_t* q;   // bf16 inputs, as in FwdParams
     const uint16_t* k;
@@ -125,6 +140,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 // log2-scaled LSE), 1 = dQ (and the exact row dot), 2 = dK/dV.
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, hipStream_t stream);
+hipError_t launch_fwd8(const Fwd8Params& p, hipStream_t stream);
 
 // Size of the decode's static scratch array (one per GPU; flash_attn_decode_noalloc).
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;

@@ -104,7 +104,80 @@ __global__ __launch_bounds__(kQThreads) void quant_e4m3_kernel(const uint16_t* _
     }
 }
 
+// The same quantisation of V, written transposed for the FP8 forward's
+// O^T += V^T P^T products: codes_t [BH, d, Np] with Np = N rounded up to 64,
+// and inside every group of 64 keys position p holds key
+//   ((p % 32) / 16) * 32 + ((p % 16) / 4) * 8 + (p / 32) * 4 + p % 4,
+// the key whose probability sits at the same k slot of the product's other
+// operand (byte p % 32 of lane half p / 32). Keys past N get code 0. Runs are
+// whole groups of 64 keys (rows % 64 == 0), so a workgroup owns its groups.
+__global__ __launch_bounds__(kQThreads) void quant_e4m3_vt_kernel(const uint16_t* __restrict__ x,
+                                                                  uint8_t* __restrict__ codes_t,
+                                                                  float* __restrict__ scales, int N, int Np,
+                                                                  int d, int rows, int nruns) {
+    __shared__ uint32_t red[kQThreads / 64];
+    const int run = (int)(blockIdx.x % (unsigned)nruns);
+    const long long bh = (long long)(blockIdx.x / (unsigned)nruns);
+    const long long r0 = (long long)run * rows;
+    const long long r1 = r0 + rows < N ? r0 + rows : N;
+    const long long base = (bh * N + r0) * d;
+    const int chunks = (int)((r1 - r0) * d / 8);
+    const uint4* src = reinterpret_cast<const uint4*>(x + base);
+
+    uint32_t m = 0;
+    for (int c = threadIdx.x; c < chunks; c += kQThreads) {
+        const uint4 w = src[c];
+        m = max(m, max(max(mag2(w.x), mag2(w.y)), max(mag2(w.z), mag2(w.w))));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    const bool tiny = m < (63u << 7);
+    const float up = tiny ? 0x1p64f : 1.0f;
+    const float amax = __fmul_rn(__uint_as_float(m << 16), up);
+    const float inv = m ? __fdiv_rn(448.0f, amax) : 1.0f;
+    if (threadIdx.x == 0)
+        scales[bh * nruns + run] = m ? __fmul_rn(__fdiv_rn(amax, 448.0f), tiny ? 0x1p-64f : 1.0f) : 1.0f;
+
+    // The run's key groups, every column: a thread writes 4 consecutive
+    // positions of one transposed row, one word (the keys they hold follow
+    // the map above).
+    const int g0 = (int)(r0 / 64), ng = (int)((r0 + rows < Np ? r0 + rows : Np) - r0 + 63) / 64;
+    const long long words = (long long)ng * d * 16;
+    uint8_t* dst = codes_t + bh * (long long)d * Np;
+    for (long long wi = threadIdx.x; wi < words; wi += kQThreads) {
+        const int g = g0 + (int)(wi / (d * 16));
+        const int rem = (int)(wi % (d * 16));
+        const int col = rem / 16, p0 = (rem % 16) * 4;
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int p = p0 + e;
+            const int t = ((p % 32) / 16) * 32 + ((p % 16) / 4) * 8 + (p / 32) * 4 + p % 4;
+            const long long key = (long long)g * 64 + t;
+            uint32_t c = 0;
+            if (key < N) {
+                const uint16_t b = x[(bh * N + key) * d + col];
+                c = e4m3_code(__fmul_rn(__fmul_rn(__uint_as_float((uint32_t)b << 16), up), inv));
+            }
+            word |= c << (8 * e);
+        }
+        *reinterpret_cast<uint32_t*>(dst + (long long)col * Np + (long long)g * 64 + p0) = word;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quant_e4m3_vt(const void* x, void* codes_t, float* scales, int BH, int N, int d, int rows,
+                                hipStream_t stream) {
+    const int nruns = (int)(((long long)N + rows - 1) / rows);
+    const int Np = (N + 63) / 64 * 64;
+    const long long grid = (long long)BH * nruns;
+    hipLaunchKernelGGL(quant_e4m3_vt_kernel, dim3((unsigned)grid), dim3(kQThreads), 0, stream,
+                       static_cast<const uint16_t*>(x), static_cast<uint8_t*>(codes_t), scales, N, Np, d, rows, nruns);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_e4m3(const void* x, void* codes, float* scales, int BH, int N, int d, int rows,
                              hipStream_t stream) {

@@ -329,6 +329,48 @@ int flash_attn_bwd_varlen(const void* q, const void* k, const void* v, const voi
 int flash_attn_quantize_e4m3(const void* x, void* codes, float* scales, int BH, int N, int d, int rows,
                              void* stream);
 
+/* The same quantisation of V, written for flash_attn_fwd_e4m3: codes and
+ * scales as flash_attn_quantize_e4m3 computes them, with the codes stored
+ * transposed and, inside each group of 64 keys, in the order of the FP8
+ * forward's probability operand:
+ *   x        bf16 [BH, N, d] contiguous, finite
+ *   codes_t  uint8 [BH, d, Np], Np = N rounded up to a multiple of 64: row c of
+ *            slab bh holds column c of every key; position p of key group g
+ *            holds key 64 g + ((p % 32) / 16) * 32 + ((p % 16) / 4) * 8 +
+ *            (p / 32) * 4 + p % 4 (a permutation of the group); keys past N
+ *            hold code 0
+ *   scales   fp32 [BH, ceil(N / rows)], as flash_attn_quantize_e4m3
+ * rows: a multiple of 64. d: a multiple of 8. x 16-byte aligned, codes_t and
+ * scales 4-byte. Errors as flash_attn_quantize_e4m3 (FA_ERR_SHAPE also for rows
+ * not a multiple of 64). */
+int flash_attn_quantize_e4m3_vt(const void* x, void* codes_t, float* scales, int BH, int N, int d, int rows,
+                                void* stream);
+
+/*
+ * Forward pass on 8-bit inputs: FlashAttention-3's FP8 forward with block
+ * scaling (mlapandio "FlashAttention: IO-aware exact attention",
+ * "Generations"; wishwiki "FlashAttention", "Evolution: FlashAttention-2 and
+ * -3"). The inputs are the dequantised values code * scale of
+ *   q8, q_scales    flash_attn_quantize_e4m3 of q: E4M3 [B, Hq, N, d], fp32 [B, Hq, ceil(N / rows)]
+ *   k8, k_scales    flash_attn_quantize_e4m3 of k: E4M3 [B, Hkv, N, d], fp32 [B, Hkv, ceil(N / rows)]
+ *   v8t, v_scales   flash_attn_quantize_e4m3_vt of v: E4M3 [B, Hkv, d, Np], fp32 [B, Hkv, ceil(N / rows)]
+ * and the outputs are as in flash_attn_fwd:
+ *   o    out  bf16 [B, Hq, N, d]
+ *   lse  out  fp32 [B, Hq, N]
+ * Both products run on the FP8 matrix cores; the probabilities are rounded to
+ * E4M3 for the P.V product (3 mantissa bits: the result is close to, not
+ * within bf16 rounding of, the attention of the dequantised inputs; O is
+ * normalised by the sum of the rounded probabilities, so their weights sum to
+ * one as used). Scores and softmax statistics are fp32.
+ * Supported: B, Hq, Hkv, N >= 1; Hq % Hkv == 0; d in {64, 128}; rows a
+ * multiple of 64 (the same run length for q, k and v); Np * d < 2^31.
+ * causal: 0 or 1 (row i sees keys j <= i). Code and output pointers 16-byte
+ * aligned, scale arrays 4-byte. Asynchronous on `stream`; nothing allocated.
+ */
+int flash_attn_fwd_e4m3(const void* q8, const float* q_scales, const void* k8, const float* k_scales,
+                        const void* v8t, const float* v_scales, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                        int d, int causal, float scale, int rows, void* stream);
+
 /* Static text for a status code. For FA_ERR_HIP the text also holds the HIP
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
