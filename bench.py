@@ -23,6 +23,9 @@ workload under a sliding-window causal mask of W keys (flash_attn_fwd_window,
 flash_attn_bwd_window), counting 4*d FLOP per visible pair for the forward and
 2.5 times that for the backward: sum over rows of min(i + 1, W) pairs per head.
 
+With --f32 NAME it measures the forward on fp32 inputs (flash_attn_fwd_f32) at that
+workload's shape, against the fp32 matrix peak (157.3 TFLOP/s).
+
 With --fp8 NAME it measures the forward on E4M3 inputs (flash_attn_fwd_e4m3) at
 that workload's shape, against the FP8 MFMA peak (twice the bf16 one).
 
@@ -644,6 +647,79 @@ def fp8_main(args) -> int:
     return 0
 
 
+# MI355X dense fp32 matrix peak (the rated figure; a sixteenth of the bf16 rate).
+PEAK_FP32_TFLOPS = 157.3
+
+
+def f32_main(args) -> int:
+    """The forward on fp32 inputs (flash_attn_fwd_f32) at a fixed-length
+    workload's shape (the fp32 draws, not rounded), against the fp32 matrix peak."""
+    import torch
+    import exact_io_aware_60_amd as fa
+
+    fa.lib()
+    w = ai.WORKLOADS[args.f32]
+    if w.d > 128:
+        print(f"--f32 takes head dimensions up to 128; {w.name} has d = {w.d}", file=sys.stderr)
+        return 2
+
+    def draw(t, shape):
+        return torch.from_numpy(ai.normal_f32(shape, 9100 + w.cfg_id, t)).cuda()
+
+    q = draw(0, (w.B, w.Hq, w.N, w.d))
+    k, v = draw(1, (w.B, w.Hkv, w.N, w.d)), draw(2, (w.B, w.Hkv, w.N, w.d))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    P = [t.data_ptr() for t in (q, k, v, o, lse)]
+
+    def fwd():
+        st = fa.fwd_f32_raw(*P, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.scale, sp)
+        if st != 0:
+            raise RuntimeError(f"fwd_f32: {fa.strerror(st)}")
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        ev[s_][0].record(stream)
+        fwd()
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    copy_calibration(args.copy_calibration, q.device)
+    flop = algorithmic(w)["fwd"][1]
+    tflops = flop / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd TFLOP/s on fp32 inputs (fp32 MFMA) and % of MI355X fp32 MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "precision": {"io": "fp32 q, k, v in; fp32 O and LSE out", "mfma": "fp32 x fp32 -> fp32", "softmax": "fp32"},
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": w.causal,
+                   "passes": "fwd (fp32)"},
+        "wall_ms_per_step": wall / args.steps * 1e3,
+        "roofline": {"bound": "mfma", "kernel": "fwd32_kernel", "achieved": tflops, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_TFLOPS, "traffic": None,
+                     "avg_launch_ms": ms, "algorithmic_flop_per_launch": flop},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -668,6 +744,8 @@ def main() -> int:
                          "pass time the forward alone")
     ap.add_argument("--varlen", choices=sorted(ai.VARLEN_WORKLOADS), default=None,
                     help="measure the forward pass over this packed variable-length workload instead")
+    ap.add_argument("--f32", choices=sorted(ai.WORKLOADS), default=None,
+                    help="measure the forward on fp32 inputs (flash_attn_fwd_f32) at this workload's shape instead")
     ap.add_argument("--fp8", choices=sorted(ai.WORKLOADS), default=None,
                     help="measure the forward on E4M3 inputs (flash_attn_fwd_e4m3) at this workload's shape instead")
     args = ap.parse_args()
@@ -693,6 +771,12 @@ def main() -> int:
             print("bench.py needs a GPU", file=sys.stderr)
             return 2
         return varlen_main(args)
+    if args.f32:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            return 2
+        return f32_main(args)
     if args.fp8:
         import torch
         if not torch.cuda.is_available():

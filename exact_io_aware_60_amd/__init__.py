@@ -29,7 +29,7 @@ EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size",
             "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen",
             "flash_attn_fwd_window", "flash_attn_bwd_window", "flash_attn_bwd_varlen",
             "flash_attn_quantize_e4m3", "flash_attn_decode_noalloc", "flash_attn_decode_noalloc_max_bytes",
-            "flash_attn_quantize_e4m3_vt", "flash_attn_fwd_e4m3")
+            "flash_attn_quantize_e4m3_vt", "flash_attn_fwd_e4m3", "flash_attn_fwd_f32")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_quantize_e4m3_vt.argtypes = [_vp] * 3 + [_i] * 4 + [_vp]
         L.flash_attn_fwd_e4m3.restype = _i
         L.flash_attn_fwd_e4m3.argtypes = [_vp] * 8 + [_i] * 6 + [ctypes.c_float, _i, _vp]
+        L.flash_attn_fwd_f32.restype = _i
+        L.flash_attn_fwd_f32.argtypes = [_vp] * 5 + [_i] * 6 + [ctypes.c_float, _vp]
         L.flash_attn_strerror.restype = ctypes.c_char_p
         L.flash_attn_strerror.argtypes = [_i]
         L.flash_attn_version.restype = ctypes.c_char_p
@@ -186,6 +188,11 @@ def fwd_e4m3_raw(q8, qs, k8, ks, v8t, vs, o, lse, B, Hq, Hkv, N, d, causal, scal
                                      int(rows), stream)
 
 
+def fwd_f32_raw(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, stream=None) -> int:
+    """flash_attn_fwd_f32 on raw addresses (ints); returns the status code."""
+    return lib().flash_attn_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, int(causal), float(scale), stream)
+
+
 def decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, window: int = 0) -> int:
     return int(lib().flash_attn_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(causal), int(window)))
 
@@ -230,6 +237,23 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _check(fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
                    causal, scale, _stream(q)))
+    return o, lse
+
+
+def fwd_f32(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None):
+    """Forward pass on fp32 inputs. Returns (o fp32 [B,Hq,N,d], lse fp32 [B,Hq,N])."""
+    import torch
+    B, Hq, Hkv, N, d = _dims(q, k)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor on the GPU")
+    if v.shape != k.shape:
+        raise ValueError("v must be shaped like k")
+    scale = default_scale(d) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(fwd_f32_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d,
+                       causal, scale, _stream(q)))
     return o, lse
 
 

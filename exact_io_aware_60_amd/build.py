@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libflashattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_quant.hip", "fa_fwd8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_quant.hip", "fa_fwd8.hip", "fa_fwd32.hip"]
 # Packed fp32 VALU ops are switched off on purpose: every fp32 op stays a plain
 # v_*_f32 instruction.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -107,6 +107,29 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
     return hip_status(fa::launch_fwd(p, static_cast<hipStream_t>(stream)));
 }
 
+int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq,
+                       int Hkv, int N, int d, int causal, float scale, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (!headdim_ok(d, 128)) return FA_ERR_HEADDIM;
+    int st = check_scale(scale);
+    if (st != FA_OK) return st;
+    if ((long double)B * Hq * N * d >= 4.0e18L) return FA_ERR_SHAPE;
+    if ((long double)B * Hq * ((N + 127) / 128) >= 2147483647.0L) return FA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+    log_config("fwd_f32", B, Hq, Hkv, N, d, causal);
+    fa::Fwd32Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N; p.d = d; p.G = Hq / Hkv;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = std::max(scale * 1.4426950408889634f, 1e-30f);
+    return hip_status(fa::launch_fwd32(p, static_cast<hipStream_t>(stream)));
+}
+
 int flash_attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                           int Hkv, int N, int d, int window, float scale, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;

@@ -32,6 +32,18 @@ struct FwdParams {
     int window;
 };
 
+// Forward on fp32 inputs (fa_fwd32.hip): fp32 Q, K, V in, fp32 O and LSE out.
+struct Fwd32Params {
+    const float* q;      // fp32 [B, Hq, N, d]
+    const float* k;      // fp32 [B, Hkv, N, d]
+    const float* v;      // fp32 [B, Hkv, N, d]
+    float* o;            // fp32 [B, Hq, N, d]
+    float* lse;          // fp32 [B, Hq, N]
+    int B, Hq, Hkv, N, d, G;
+    int causal;
+    float scale_log2;    // softmax scale * log2(e)
+};
+
 // Forward on 8-bit inputs (OCP E4M3 codes with one fp32 scale per run of
 // `rows` rows of each head; fa_fwd8.hip).
 struct Fwd8Params {
@@ -141,6 +153,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_stage(const BwdParams& p, int stage, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, hipStream_t stream);
 hipError_t launch_fwd8(const Fwd8Params& p, hipStream_t stream);
+hipError_t launch_fwd32(const Fwd32Params& p, hipStream_t stream);
 
 // Size of the decode's static scratch array (one per GPU; flash_attn_decode_noalloc).
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;

@@ -86,6 +86,24 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    void* stream);
 
 /*
+ * Forward pass on fp32 inputs: the computation of flash_attn_fwd (mlapandio
+ * "FlashAttention: IO-aware exact attention", "Four ideas") for Q, K and V
+ * that are fp32 and are not rounded first. Both products run on fp32 matrix
+ * instructions with fp32 accumulation, the softmax statistics in fp32.
+ *   q    in   fp32 [B, Hq,  N, d]
+ *   k    in   fp32 [B, Hkv, N, d]
+ *   v    in   fp32 [B, Hkv, N, d]
+ *   o    out  fp32 [B, Hq,  N, d]   normalised output
+ *   lse  out  fp32 [B, Hq,  N]      natural-log logsumexp of the scaled, masked scores
+ * causal: 0 or 1. d: a multiple of 8 up to 128 (else FA_ERR_HEADDIM). Other
+ * arguments and rules as in flash_attn_fwd. It runs at the fp32 matrix rate,
+ * a sixteenth of the bf16 one.
+ */
+int flash_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                       void* stream);
+
+/*
  * Forward pass with a sliding-window (local) causal mask: query row i sees keys
  * i - window < j <= i, its `window` most recent positions. Arguments, layout
  * and outputs as in flash_attn_fwd (causal is implied); window >= 1, and

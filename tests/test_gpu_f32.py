@@ -1,0 +1,138 @@
+"""GPU parity of the forward on fp32 inputs (flash_attn_fwd_f32) against the
+oracle on the same, unrounded fp32 values.
+
+Two criteria on every element:
+  * the stated tolerances (max abs error 1e-2 on O, 1e-3 on LSE);
+  * a bound derived from fp32 arithmetic (u = 2^-24), so that a product kept in
+    less than fp32 precision shows. A score is a chain of d/2 two-term matrix
+    steps, each rounding at most twice: |dS| <= (d + 4) u sum_k |q_k k_k|. With
+    the fp32 scale, the reference subtraction and exp2, a weight moves by a
+    factor e^(delta_j), delta_j = ln2 (scale log2e |dS| + 3u (|x_j| + |m|)) + 4u
+    (x in log2 units, m the row max), so LSE moves by at most max_j delta_j
+    plus the fp32 sum and log, (N + 20) u + 3u |LSE|. O moves by
+    sum_j P_j (e^(delta_j + delta_max) - 1) |v_j - O| from the weights and by
+    (2N + 40) u (sum_j P_j |v_j| + |O|) from the P.V chain, the per-tile
+    rescales and the final division.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+LOG2E = 1.0 / math.log(2.0)
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import exact_io_aware_60_amd as fa
+    fa.lib()
+    return fa
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def run_f32(fa, q, k, v, causal, scale):
+    import torch
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    o, lse = fa.fwd_f32(dev(q), dev(k), dev(v), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def f32_bounds(orc, q, k, v, causal, scale, o_ref, lse_ref):
+    """Per element bound on O and per row bound on LSE (module docstring)."""
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    P = orc.probs(q, k, causal, scale)
+    ob = np.empty_like(o_ref)
+    lb = np.empty_like(lse_ref)
+    sl2 = scale * LOG2E
+    for b in range(B):
+        for h in range(Hq):
+            qq, kk, vv = q[b, h].astype(np.float64), k[b, h // G].astype(np.float64), v[b, h // G].astype(np.float64)
+            p = P[b, h]
+            live = p > 0
+            dS = (d + 4) * U * (np.abs(qq) @ np.abs(kk).T)
+            x = sl2 * (qq @ kk.T)
+            m = np.max(np.where(live, x, -np.inf), axis=1, keepdims=True)
+            delta = np.where(live, math.log(2.0) * (sl2 * dS + 3 * U * (np.abs(x) + np.abs(m))) + 4 * U, 0.0)
+            dmax = delta.max(axis=1, keepdims=True)
+            lb[b, h] = dmax[:, 0] + (N + 20) * U + 3 * U * np.abs(lse_ref[b, h])
+            dev = np.abs(vv[None, :, :] - o_ref[b, h][:, None, :])
+            moved = np.einsum("ij,ijc->ic", p * np.expm1(delta + dmax), dev)
+            chain = (2 * N + 40) * U * (p @ np.abs(vv) + np.abs(o_ref[b, h]))
+            ob[b, h] = moved + chain
+    return ob + 1e-7, lb + 1e-7
+
+
+def check(fa, orc, q, k, v, causal, scale, tag):
+    say(f"fwd_f32 {tag}")
+    o, lse = run_f32(fa, q, k, v, causal, scale)
+    ro, rl = orc.fwd(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), causal, scale)
+    ob, lb = f32_bounds(orc, q, k, v, causal, scale, ro, rl)
+    eo, el = np.abs(o - ro), np.abs(lse - rl)
+    say(f"{tag}: max|O - ref| {eo.max():.3e} ({(eo / ob).max():.3f} of the fp32 bound), "
+        f"max|LSE - ref| {el.max():.3e} ({(el / lb).max():.3f} of it)")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert eo.max() <= 1e-2 and el.max() <= 1e-3, tag
+    assert np.all(eo <= ob), f"{tag}: O beyond the fp32 bound ({(eo / ob).max():.3f} of it)"
+    assert np.all(el <= lb), f"{tag}: LSE beyond the fp32 bound ({(el / lb).max():.3f} of it)"
+
+
+def normal(shape, cfg, t, f=1.0):
+    return ai.normal_f32(shape, cfg, t) * np.float32(f)
+
+
+def test_workload_tiny_fp32_inputs(fa, orc):
+    """The tiny workload on its fp32 draws, not rounded to bf16."""
+    w = ai.WORKLOADS["tiny"]
+    inp = ai.make_inputs(w, with_grad=False)
+    check(fa, orc, inp["q32"], inp["k32"], inp["v32"], w.causal, w.scale, "tiny, fp32 inputs")
+
+
+@pytest.mark.parametrize("d", [8, 64, 72, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 33, 128, 300])
+def test_ragged(fa, orc, d, causal, N):
+    cfg = 7000 + N * 4 + d + int(causal)
+    q, k, v = (normal((1, 2, N, d), cfg, t) for t in range(3))
+    check(fa, orc, q, k, v, causal, 1.0 / math.sqrt(d), f"N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_several_workgroups(fa, orc, causal):
+    """8 query heads over 2 K/V heads, 2 batches, N spanning 4 workgroups of rows."""
+    q = normal((2, 8, 450, 64), 7600, 0)
+    k, v = normal((2, 2, 450, 64), 7600, 1), normal((2, 2, 450, 64), 7600, 2)
+    check(fa, orc, q, k, v, causal, 0.125, f"gqa causal={causal}")
+
+
+def test_large_logits(fa, orc):
+    """Peaked rows (inputs x3): the running max moves, the rescale is exercised."""
+    q, k, v = normal((1, 2, 520, 128), 7700, 0, 3.0), normal((1, 2, 520, 128), 7700, 1, 3.0), normal((1, 2, 520, 128), 7700, 2)
+    check(fa, orc, q, k, v, True, 0.0883883, "large logits")
+
+
+def test_rejects_what_it_does_not_take(fa):
+    import torch
+    x = torch.zeros((1, 1, 64, 136), dtype=torch.float32, device="cuda")
+    st = fa.fwd_f32_raw(x.data_ptr(), x.data_ptr(), x.data_ptr(), x.data_ptr(), x.data_ptr(), 1, 1, 1, 64, 136, 0, 0.1)
+    assert st == fa.FA_ERR_HEADDIM
+    y = torch.zeros((1, 1, 64, 64), dtype=torch.float32, device="cuda")
+    st = fa.fwd_f32_raw(y.data_ptr() + 4, y.data_ptr(), y.data_ptr(), y.data_ptr(), y.data_ptr(), 1, 1, 1, 64, 64, 0, 0.1)
+    assert st == fa.FA_ERR_ALIGN
+    with pytest.raises(ValueError):
+        fa.fwd_f32(y.to(torch.bfloat16), y, y)
