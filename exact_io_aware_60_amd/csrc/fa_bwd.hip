@@ -1254,10 +1254,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
 // 128 registers, and the four accumulators of the full width 256 more: no room
 // for the scores. So each gradient pass runs two workgroups per tile, one per
 // half of the accumulated columns (kSplitDH = 128): both compute S and dP over
-// all 256 columns, and each accumulates its half of dK, dV (or dQ, PK). The
-// LDS then holds one stage (a row tile of 256 columns is 33 KiB), every step
-// runs the plain masked path, and no step overlaps the next one's copy. This
-// trades speed (S and dP are computed twice) for a register budget that fits.
+// all 256 columns, and each accumulates its half of dK, dV (or dQ, PK). This
+// trades work (S and dP are computed twice) for a register budget that fits.
+//
+// A row tile of 256 columns is 33 KiB, so the LDS holds one set of a step's
+// tiles, not two. A step has two phases that read different tiles, though:
+// S and dP (phase A) read the row tiles (and LSE, D), the gradient products
+// (phase B) the transposed tiles. So the next step's row tiles are copied as
+// soon as phase A is done everywhere, and land during phase B; the next
+// transposed tiles are copied after phase B, and land during the next phase
+// A. Loads complete in issue order, so a wave waits for the row tiles by
+// leaving only the transposed copies outstanding (vmcnt), and every step
+// runs the plain masked path.
 constexpr int kSplitDH = 128;
 
 template <int D>
@@ -1267,8 +1275,10 @@ struct KvSplitCfg {
     static constexpr int RT = padded_tile_bytes<SR, kKV_Q>();
     static constexpr int TT = kSplitDH * 2 * kKV_Q;        // Q^T, dO^T of one half: [DH][64], swizzled
     static constexpr int QR = 0, DOR = RT, QT = 2 * RT, DOT = 2 * RT + TT;
-    static constexpr int L2 = 2 * RT + 2 * TT, DD = L2 + 4 * kKV_Q;
-    static constexpr int LDS = DD + 4 * kKV_Q;             // one stage
+    // LSE and D rows (64 floats each) in two sets, by step parity: a step's
+    // set stays intact while the next step's copy fills the other one
+    static constexpr int L2 = 2 * RT + 2 * TT, DD = L2 + 4 * kKV_Q, LD2 = 8 * kKV_Q;
+    static constexpr int LDS = L2 + 2 * LD2;               // one stage of tiles
     using PlanR = CopyPlan<D, SR, kKV_Q, 4>;
     using PlanT = CopyPlanSwz<2 * kKV_Q, kSplitDH, 4>;
     using Addr = LaneAddr<SR, Swz128>;
@@ -1282,55 +1292,94 @@ struct KvSplitState {
     f32x16 dk[kSplitDH / 32], dv[kSplitDH / 32];   // dK^T, dV^T of this workgroup's half
 };
 
-// One step of 64 query rows against the wave's 32 keys, every entry masked
-// as in kv_step_masked (causal: keys above the row; bounded masks: rows
-// outside [kbeg, kend)); the transposed tiles hold this half's columns.
-template <int D, bool WIN>
+// One step of 64 query rows against the wave's 32 keys, every entry masked as
+// in kv_step_masked (causal: keys above the row; bounded masks: rows outside
+// [kbeg, kend)). Phase A: S and dP over all columns for rows 0-31, then for
+// rows 32-63 with the softmax of rows 0-31 (P, dS and their fp16 packs) spread
+// over those MFMAs, one register per two MFMAs. `mid` then runs (the
+// workgroup's hand-over between the phases). Phase B: dV^T += dO^T P and
+// dK^T += Q^T dS over this half's columns for rows 0-31 with the softmax of
+// rows 32-63 spread over them, then for rows 32-63. ld: the byte offset of
+// the step's set of LSE and D rows, which the next step's copy leaves alone.
+template <int D, bool WIN, class MID>
 __device__ __forceinline__ void kv_split_step(const FA_LDS uint8_t* __restrict__ st, KvSplitState<D>& S,
-                                              const typename KvSplitCfg<D>::Addr& la, int lbase, int q0, int key,
-                                              float sl2, float c1, int hh, bool causal, int kbeg, int kend) {
+                                              const typename KvSplitCfg<D>::Addr& la, int lbase, int ld, int q0,
+                                              int key, float sl2, float c1, int hh, bool causal, int kbeg, int kend,
+                                              const MID& mid) {
     using C = KvSplitCfg<D>;
     constexpr int DS = C::DS, DBH = C::DBH;
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = zero16();
-        dp[qb] = zero16();
-    }
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            s[qb] = mfma32h(lds_read16b(st, la.row(qb, ds) + C::QR), S.kf[ds], s[qb]);
-            dp[qb] = mfma32h(lds_read16b(st, la.row(qb, ds) + C::DOR), S.vf[ds], dp[qb]);
-        }
+    f32x4 lv[4], dv4[4];
     u32x4 pp[4], dsp[4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    auto stats = [&](int qb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const f32x4 lv = *reinterpret_cast<const FA_LDS f32x4*>(st + C::L2 + lbase + (qb * 32 + u * 8) * 4);
-            const f32x4 dv4 = *reinterpret_cast<const FA_LDS f32x4*>(st + C::DD + lbase + (qb * 32 + u * 8) * 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = u * 4 + e;
-                const int q = q0 + qb * 32 + u * 8 + hh * 4 + e;
-                float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[e]));
-                if ((causal && key > q) || (WIN && (q < kbeg || q >= kend))) x = 0.f;
-                s[qb][i] = x;
-                dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[e]);
-            }
+            lv[u] = *reinterpret_cast<const FA_LDS f32x4*>(st + C::L2 + ld + lbase + (qb * 32 + u * 8) * 4);
+            dv4[u] = *reinterpret_cast<const FA_LDS f32x4*>(st + C::DD + ld + lbase + (qb * 32 + u * 8) * 4);
         }
-#pragma unroll
-    for (int qc = 0; qc < 4; ++qc)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int i = (qc & 1) * 8 + 2 * w;
-            pp[qc][w] = pack_f16(s[qc >> 1][i], s[qc >> 1][i + 1]);
-            dsp[qc][w] = pack_f16(dp[qc >> 1][i], dp[qc >> 1][i + 1]);
+    };
+    // register i of rows qb*32..: row q0 + qb*32 + (i/4)*8 + hh*4 + i%4
+    auto soft = [&](auto qbc, auto ic) {
+        constexpr int qb = decltype(qbc)::value, i = decltype(ic)::value;
+        constexpr int u = i / 4, e = i % 4, qc = 2 * qb + i / 8, w = (i % 8) / 2;
+        const int q = q0 + qb * 32 + u * 8 + hh * 4 + e;
+        float x = fast_exp2(fmaf(s[qb][i], sl2, -lv[u][e]));
+        if ((causal && key > q) || (WIN && (q < kbeg || q >= kend))) x = 0.f;
+        s[qb][i] = x;
+        dp[qb][i] = x * fmaf(dp[qb][i], c1, -dv4[u][e]);
+        if constexpr (i & 1) {
+            pp[qc][w] = pack_f16(s[qb][i - 1], s[qb][i]);
+            dsp[qc][w] = pack_f16(dp[qb][i - 1], dp[qb][i]);
         }
+    };
+    s[0] = zero16();
+    dp[0] = zero16();
 #pragma unroll
-    for (int qc = 0; qc < 4; ++qc)
+    for (int ds = 0; ds < DS; ++ds) {
+        s[0] = mfma32h(lds_read16b(st, la.row(0, ds) + C::QR), S.kf[ds], s[0]);
+        dp[0] = mfma32h(lds_read16b(st, la.row(0, ds) + C::DOR), S.vf[ds], dp[0]);
+    }
+    s[1] = zero16();
+    dp[1] = zero16();
+    stats(0);
+    // operands read PF slots ahead of their MFMA: a scheduling barrier closes
+    // every slot, so no read could otherwise move ahead of it (one slot: the
+    // register budget has no room for a deeper ring)
+    constexpr int PF = 1;
+    u32x4 ra[PF + 1][2];
+    auto read_a = [&](auto dc) {
+        constexpr int ds = decltype(dc)::value;
+        ra[ds % (PF + 1)][0] = lds_read16b(st, la.row(1, ds) + C::QR);
+        ra[ds % (PF + 1)][1] = lds_read16b(st, la.row(1, ds) + C::DOR);
+    };
+    static_for<PF>([&](auto dc) { read_a(dc); });
+    static_for<DS>([&](auto dc) {
+        constexpr int ds = decltype(dc)::value;
+        if constexpr (ds + PF < DS) read_a(std::integral_constant<int, ds + PF>{});
+        s[1] = mfma32h(ra[ds % (PF + 1)][0], S.kf[ds], s[1]);
+        dp[1] = mfma32h(ra[ds % (PF + 1)][1], S.vf[ds], dp[1]);
+        static_for<16 / DS>([&](auto k) { soft(std::integral_constant<int, 0>{}, std::integral_constant<int, ds * (16 / DS) + decltype(k)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    mid();
+    stats(1);
+    u32x4 rb[PF + 1][2];
+    auto read_b = [&](auto mc) {
+        constexpr int m = decltype(mc)::value, qc = m / DBH, db = m % DBH;
+        rb[m % (PF + 1)][0] = la.t.read(st + C::DOT, db * 32, qc);
+        rb[m % (PF + 1)][1] = la.t.read(st + C::QT, db * 32, qc);
+    };
+    static_for<PF>([&](auto mc) { read_b(mc); });
+    static_for<2 * DBH>([&](auto mc) {
+        constexpr int m = decltype(mc)::value, qc = m / DBH, db = m % DBH;
+        if constexpr (m + PF < 2 * DBH) read_b(std::integral_constant<int, m + PF>{});
+        S.dv[db] = mfma32h(rb[m % (PF + 1)][0], pp[qc], S.dv[db]);
+        S.dk[db] = mfma32h(rb[m % (PF + 1)][1], dsp[qc], S.dk[db]);
+        static_for<16 / (2 * DBH)>([&](auto k) { soft(std::integral_constant<int, 1>{}, std::integral_constant<int, m * (16 / (2 * DBH)) + decltype(k)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int qc = 2; qc < 4; ++qc)
 #pragma unroll
         for (int db = 0; db < DBH; ++db) {
             S.dv[db] = mfma32h(la.t.read(st + C::DOT, db * 32, qc), pp[qc], S.dv[db]);
@@ -1399,22 +1448,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_split_kernel(BwdParams p
     typename C::Addr la;
     la.init(l32, hh);
     const int lbase = hh * 16;
-    for (int j = 0; j < nsteps; ++j) {
+    // step j: query head g = j % G, rows q0 = qs + (j / G) * 64
+    auto copy_rows = [&](int j) {   // Q, dO rows, LSE and D (set j & 1): 2 * NT + 1 loads per wave
         const uint32_t g = j % G;
         const int q0 = qs + (j / G) * kKV_Q;
         const uint32_t rows = (g * Np + q0) * D * 2;
-        const uint32_t tr = (g * D + half * kSplitDH) * Np * 2 + q0 * 2;   // this half's d rows
         const uint32_t row4 = (g * Np + q0) * 4;
+        const int ld = (j & 1) * C::LD2;
         pr.copy(rs.q, rows, st + C::QR, w);
         pr.copy(rs.dout, rows, st + C::DOR, w);
+        // waves 0 and 2 copy LSE, 1 and 3 copy D (the same bytes twice)
+        if ((w & 1) == 0) bload_lds4(rs.l2, lane * 4, row4, st + C::L2 + ld);
+        else bload_lds4(rs.dd, lane * 4, row4, st + C::DD + ld);
+    };
+    auto copy_tr = [&](int j) {     // this half's Q^T, dO^T: 2 * NT loads per wave
+        const uint32_t g = j % G;
+        const int q0 = qs + (j / G) * kKV_Q;
+        const uint32_t tr = (g * D + half * kSplitDH) * Np * 2 + q0 * 2;
         pt.copy(rs.qt, tr, st + C::QT, w);
         pt.copy(rs.dot, tr, st + C::DOT, w);
-        if (w == 0) bload_lds4(rs.l2, lane * 4, row4, st + C::L2);
-        if (w == 1) bload_lds4(rs.dd, lane * 4, row4, st + C::DD);
-        wait_vmem();
+    };
+    if (nsteps > 0) {
+        copy_rows(0);
+        copy_tr(0);
+    }
+    for (int j = 0; j < nsteps; ++j) {
+        const int q0 = qs + (j / G) * kKV_Q;
+        wait_vmem_n<2 * C::PlanT::NT>();   // this step's rows (its transposed tiles may be in flight)
         __syncthreads();
-        kv_split_step<D, WIN>(st, S, la, lbase, q0, key, sl2, c1, hh, causal, kbeg, kend);
-        __syncthreads();
+        kv_split_step<D, WIN>(st, S, la, lbase, (j & 1) * C::LD2, q0, key, sl2, c1, hh, causal, kbeg, kend, [&]() {
+            wait_vmem();                    // this step's transposed tiles
+            __syncthreads();                // ... everywhere, and the row tiles are free
+            if (j + 1 < nsteps) copy_rows(j + 1);
+        });
+        __syncthreads();                    // the transposed tiles are free
+        if (j + 1 < nsteps) copy_tr(j + 1);
     }
     if (key < N) {
         const int dr = p.d;
@@ -1461,49 +1529,80 @@ struct QSplitState {
 };
 
 // One tile of 64 keys, every entry masked as in dq_masked; the exact row dot
-// sums over all columns of dP, so both halves form the same value.
-template <int D, bool WIN>
+// sums over all columns of dP, so both halves form the same value. Phase A:
+// S and dP over all columns for keys 0-31, then keys 32-63 with the softmax of
+// keys 0-31 spread over those MFMAs; `mid` runs; phase B: PK^T += K^T P^T and
+// dQ^T += K^T dS^T over this half's columns for keys 0-31 with the softmax of
+// keys 32-63 spread over them, then for keys 32-63.
+template <int D, bool WIN, class MID>
 __device__ __forceinline__ void dq_split_step(QSplitState<D>& S, const FA_LDS uint8_t* __restrict__ cur,
                                               const typename QSplitCfg<D>::Addr& la, int key0, int qrow, int N,
-                                              bool causal, float sl2, float c1, int hh, int lbq, int ubq) {
+                                              bool causal, float sl2, float c1, int hh, int lbq, int ubq,
+                                              const MID& mid) {
     using C = QSplitCfg<D>;
     constexpr int DS = C::DS, DBH = C::DBH;
     f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16();
-        dp[kb] = zero16();
-    }
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = mfma32h(lds_read16b(cur, la.row(kb, ds) + C::KR), S.qf[ds], s[kb]);
-            dp[kb] = mfma32h(lds_read16b(cur, la.row(kb, ds) + C::VR), S.dof[ds], dp[kb]);
-        }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kk = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-            float x = fast_exp2(fmaf(s[kb][i], sl2, -S.l2));
-            if (kk >= N || (causal && kk > qrow) || (WIN && (kk < lbq || kk >= ubq))) x = 0.f;
-            const float dpv = dp[kb][i];
-            S.dacc = fmaf(x, dpv, S.dacc);
-            s[kb][i] = x;
-            dp[kb][i] = x * fmaf(dpv, c1, -S.dd);
-        }
     u32x4 pp[4], dsp[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int i = (kc & 1) * 8 + 2 * w;
-            pp[kc][w] = pack_f16(s[kc >> 1][i], s[kc >> 1][i + 1]);
-            dsp[kc][w] = pack_f16(dp[kc >> 1][i], dp[kc >> 1][i + 1]);
+    // register i of keys kb*32..: key key0 + kb*32 + (i/4)*8 + hh*4 + i%4
+    auto soft = [&](auto kbc, auto ic) {
+        constexpr int kb = decltype(kbc)::value, i = decltype(ic)::value;
+        constexpr int kc = 2 * kb + i / 8, w = (i % 8) / 2;
+        const int kk = key0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+        float x = fast_exp2(fmaf(s[kb][i], sl2, -S.l2));
+        if (kk >= N || (causal && kk > qrow) || (WIN && (kk < lbq || kk >= ubq))) x = 0.f;
+        const float dpv = dp[kb][i];
+        S.dacc = fmaf(x, dpv, S.dacc);
+        s[kb][i] = x;
+        dp[kb][i] = x * fmaf(dpv, c1, -S.dd);
+        if constexpr (i & 1) {
+            pp[kc][w] = pack_f16(s[kb][i - 1], s[kb][i]);
+            dsp[kc][w] = pack_f16(dp[kb][i - 1], dp[kb][i]);
         }
+    };
+    s[0] = zero16();
+    dp[0] = zero16();
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
+    for (int ds = 0; ds < DS; ++ds) {
+        s[0] = mfma32h(lds_read16b(cur, la.row(0, ds) + C::KR), S.qf[ds], s[0]);
+        dp[0] = mfma32h(lds_read16b(cur, la.row(0, ds) + C::VR), S.dof[ds], dp[0]);
+    }
+    s[1] = zero16();
+    dp[1] = zero16();
+    // operands read PF slots ahead of their MFMA (a scheduling barrier closes
+    // every slot)
+    constexpr int PF = 2;
+    u32x4 ra[PF + 1][2];
+    auto read_a = [&](auto dc) {
+        constexpr int ds = decltype(dc)::value;
+        ra[ds % (PF + 1)][0] = lds_read16b(cur, la.row(1, ds) + C::KR);
+        ra[ds % (PF + 1)][1] = lds_read16b(cur, la.row(1, ds) + C::VR);
+    };
+    static_for<PF>([&](auto dc) { read_a(dc); });
+    static_for<DS>([&](auto dc) {
+        constexpr int ds = decltype(dc)::value;
+        if constexpr (ds + PF < DS) read_a(std::integral_constant<int, ds + PF>{});
+        s[1] = mfma32h(ra[ds % (PF + 1)][0], S.qf[ds], s[1]);
+        dp[1] = mfma32h(ra[ds % (PF + 1)][1], S.dof[ds], dp[1]);
+        static_for<16 / DS>([&](auto k) { soft(std::integral_constant<int, 0>{}, std::integral_constant<int, ds * (16 / DS) + decltype(k)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    mid();
+    u32x4 rb[PF + 1];
+    auto read_b = [&](auto mc) {
+        constexpr int m = decltype(mc)::value, kc = m / DBH, db = m % DBH;
+        rb[m % (PF + 1)] = la.t.read(cur + C::KT, db * 32, kc);
+    };
+    static_for<PF>([&](auto mc) { read_b(mc); });
+    static_for<2 * DBH>([&](auto mc) {
+        constexpr int m = decltype(mc)::value, kc = m / DBH, db = m % DBH;
+        if constexpr (m + PF < 2 * DBH) read_b(std::integral_constant<int, m + PF>{});
+        S.pk[db] = mfma32h(rb[m % (PF + 1)], pp[kc], S.pk[db]);
+        S.dq[db] = mfma32h(rb[m % (PF + 1)], dsp[kc], S.dq[db]);
+        static_for<16 / (2 * DBH)>([&](auto k) { soft(std::integral_constant<int, 1>{}, std::integral_constant<int, m * (16 / (2 * DBH)) + decltype(k)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+#pragma unroll
+    for (int kc = 2; kc < 4; ++kc)
 #pragma unroll
         for (int db = 0; db < DBH; ++db) {
             const u32x4 a = la.t.read(cur + C::KT, db * 32, kc);
@@ -1569,14 +1668,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_split_kernel(BwdParams p) 
     pt.init(w, lane, Np);
     typename C::Addr la;
     la.init(l32, hh);
-    for (int j = jst; j < nt; ++j) {
+    // K, V rows of key tile j (2 * NT loads per wave), this half's K^T (NT)
+    auto copy_rows = [&](int j) {
         pr.copy(rk, (uint32_t)j * kQ_N * D * 2, cur + C::KR, w);
         pr.copy(rv, (uint32_t)j * kQ_N * D * 2, cur + C::VR, w);
-        pt.copy(rkt, (uint32_t)j * kQ_N * 2, cur + C::KT, w);
-        wait_vmem();
+    };
+    auto copy_tr = [&](int j) { pt.copy(rkt, (uint32_t)j * kQ_N * 2, cur + C::KT, w); };
+    if (jst < nt) {
+        copy_rows(jst);
+        copy_tr(jst);
+    }
+    for (int j = jst; j < nt; ++j) {
+        wait_vmem_n<C::PlanT::NT>();      // this tile's rows (its K^T may be in flight)
         __syncthreads();
-        dq_split_step<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, hh, lbq, ubq);
-        __syncthreads();
+        dq_split_step<D, WIN>(S, cur, la, j * kQ_N, qrow, N, causal, sl2, c1, hh, lbq, ubq, [&]() {
+            wait_vmem();                  // this tile's K^T
+            __syncthreads();              // ... everywhere, and the row tiles are free
+            if (j + 1 < nt) copy_rows(j + 1);
+        });
+        __syncthreads();                  // K^T is free
+        if (j + 1 < nt) copy_tr(j + 1);
     }
     const float dx = (S.dacc + swap_half(S.dacc)) * c1;
     if (qrow < N) {

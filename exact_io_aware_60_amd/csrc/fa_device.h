@@ -99,6 +99,14 @@ __device__ __forceinline__ void bload_lds4(BufRes r, uint32_t voff, uint32_t sof
 // s_waitcnt vmcnt(0): all of this wave's vector-memory loads have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): all but the N most recently issued of this wave's
+// vector-memory loads have completed (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Global 16-byte load; returns zeros when !valid (ragged tails).
 __device__ __forceinline__ u32x4 gload16(const uint16_t* p, bool valid) {
     u32x4 r = {0u, 0u, 0u, 0u};

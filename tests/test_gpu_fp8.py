@@ -76,10 +76,12 @@ def vt_key(p):
 
 # ------------------------------------------------------------------ quantiser, transposed
 @pytest.mark.parametrize("BH,N,d,rows", [(1, 1, 64, 64), (3, 300, 128, 128), (2, 64, 64, 64), (2, 777, 128, 192),
-                                         (4, 130, 24, 64), (1, 4100, 128, 256)])
+                                         (4, 130, 24, 64), (1, 4100, 128, 256), (1, 1100, 128, 512),
+                                         (2, 200, 256, 128)])
 def test_quantize_vt_matches_oracle(fa, orc, BH, N, d, rows):
     """Every code and scale bit-exact with the oracle's quantiser, placed at the
-    documented transposed position; positions past N hold 0."""
+    documented transposed position; positions past N hold 0. Runs up to 32768
+    elements take the single-read path, (1, 1100, 128, 512) the two-sweep one."""
     import torch
     say(f"quantize_e4m3_vt BH={BH} N={N} d={d} rows={rows}")
     g = torch.Generator().manual_seed(31 * N + d + rows)
