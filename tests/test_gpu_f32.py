@@ -52,30 +52,38 @@ def run_f32(fa, q, k, v, causal, scale):
     return o.double().cpu().numpy(), lse.double().cpu().numpy()
 
 
+def head_bounds(q, k, v, P, o_ref, lse_ref, scale):
+    """Per element bound on O and per row bound on LSE (module docstring) for
+    query rows q [R, d] of one head against keys k, v [N, d], given the
+    oracle's P [R, N], O [R, d] and LSE [R]."""
+    N, d = k.shape
+    q, k, v = q.astype(np.float64), k.astype(np.float64), v.astype(np.float64)
+    sl2 = scale * LOG2E
+    live = P > 0
+    dS = (d + 4) * U * (np.abs(q) @ np.abs(k).T)
+    x = sl2 * (q @ k.T)
+    m = np.max(np.where(live, x, -np.inf), axis=1, keepdims=True)
+    delta = np.where(live, math.log(2.0) * (sl2 * dS + 3 * U * (np.abs(x) + np.abs(m))) + 4 * U, 0.0)
+    dmax = delta.max(axis=1, keepdims=True)
+    lb = dmax[:, 0] + (N + 20) * U + 3 * U * np.abs(lse_ref)
+    dev = np.abs(v[None, :, :] - o_ref[:, None, :])
+    moved = np.einsum("ij,ijc->ic", P * np.expm1(delta + dmax), dev)
+    chain = (2 * N + 40) * U * (P @ np.abs(v) + np.abs(o_ref))
+    return moved + chain + 1e-7, lb + 1e-7
+
+
 def f32_bounds(orc, q, k, v, causal, scale, o_ref, lse_ref):
-    """Per element bound on O and per row bound on LSE (module docstring)."""
+    """head_bounds for every row of every head."""
     B, Hq, N, d = q.shape
     G = Hq // k.shape[1]
     P = orc.probs(q, k, causal, scale)
     ob = np.empty_like(o_ref)
     lb = np.empty_like(lse_ref)
-    sl2 = scale * LOG2E
     for b in range(B):
         for h in range(Hq):
-            qq, kk, vv = q[b, h].astype(np.float64), k[b, h // G].astype(np.float64), v[b, h // G].astype(np.float64)
-            p = P[b, h]
-            live = p > 0
-            dS = (d + 4) * U * (np.abs(qq) @ np.abs(kk).T)
-            x = sl2 * (qq @ kk.T)
-            m = np.max(np.where(live, x, -np.inf), axis=1, keepdims=True)
-            delta = np.where(live, math.log(2.0) * (sl2 * dS + 3 * U * (np.abs(x) + np.abs(m))) + 4 * U, 0.0)
-            dmax = delta.max(axis=1, keepdims=True)
-            lb[b, h] = dmax[:, 0] + (N + 20) * U + 3 * U * np.abs(lse_ref[b, h])
-            dev = np.abs(vv[None, :, :] - o_ref[b, h][:, None, :])
-            moved = np.einsum("ij,ijc->ic", p * np.expm1(delta + dmax), dev)
-            chain = (2 * N + 40) * U * (p @ np.abs(vv) + np.abs(o_ref[b, h]))
-            ob[b, h] = moved + chain
-    return ob + 1e-7, lb + 1e-7
+            ob[b, h], lb[b, h] = head_bounds(q[b, h], k[b, h // G], v[b, h // G], P[b, h], o_ref[b, h],
+                                             lse_ref[b, h], scale)
+    return ob, lb
 
 
 def check(fa, orc, q, k, v, causal, scale, tag):
@@ -136,3 +144,30 @@ def test_rejects_what_it_does_not_take(fa):
     assert st == fa.FA_ERR_ALIGN
     with pytest.raises(ValueError):
         fa.fwd_f32(y.to(torch.bfloat16), y, y)
+
+
+def test_full_size_gqa16k_sampled_rows(fa, orc):
+    """The configuration bench.py --f32 gqa16k times (B=2, Hq=32, Hkv=8,
+    N=16384, d=128, causal, the same seeded fp32 draws), checked on 24 seeded
+    rows (always 0 and N-1) of two heads in different K/V groups against the
+    oracle on all 16384 keys, to the same criteria."""
+    w = ai.WORKLOADS["gqa16k"]
+    q = ai.normal_f32((w.B, w.Hq, w.N, w.d), 9100 + w.cfg_id, 0)
+    k = ai.normal_f32((w.B, w.Hkv, w.N, w.d), 9100 + w.cfg_id, 1)
+    v = ai.normal_f32((w.B, w.Hkv, w.N, w.d), 9100 + w.cfg_id, 2)
+    say("fwd_f32 gqa16k full size")
+    o, lse = run_f32(fa, q, k, v, w.causal, w.scale)
+    rows = ai.sample_rows(w.N, 24, w.cfg_id)
+    for b, h in ((0, 0), (1, 29)):
+        hk = h // w.G
+        qh = q[b, h][rows][None, None].astype(np.float64)
+        kh, vh = k[b, hk][None, None].astype(np.float64), v[b, hk][None, None].astype(np.float64)
+        ro, rl = orc.fwd(qh, kh, vh, w.causal, w.scale, qpos=rows)
+        P = orc.probs(qh, kh, w.causal, w.scale, qpos=rows)[0, 0]
+        ob, lb = head_bounds(qh[0, 0], kh[0, 0], vh[0, 0], P, ro[0, 0], rl[0, 0], w.scale)
+        eo = np.abs(o[b, h][rows] - ro[0, 0])
+        el = np.abs(lse[b, h][rows] - rl[0, 0])
+        say(f"gqa16k head ({b}, {h}): max|O - ref| {eo.max():.3e} ({(eo / ob).max():.3f} of the fp32 bound), "
+            f"max|LSE - ref| {el.max():.3e} ({(el / lb).max():.3f} of it)")
+        assert eo.max() <= 1e-2 and el.max() <= 1e-3
+        assert np.all(eo <= ob) and np.all(el <= lb), (b, h)

@@ -147,81 +147,101 @@ def run_fp8(fa, c, rows, causal, scale, device_quant=None):
     return from_dev_bf16(o), lse.double().cpu().numpy()
 
 
+def head_reference(orc, q8, qs, k8, ks, v, rows_idx, rows, causal, scale):
+    """P', O', LSE' and per-row max |scaled score| of query rows `rows_idx`
+    of one head (codes [N, d], run scales, dequantised V [N, d]), all keys,
+    with the scores as the instruction computes them."""
+    N = k8.shape[0]
+    sq = np.repeat(qs.astype(np.float64), rows)[:N][rows_idx]
+    sk = np.repeat(ks.astype(np.float64), rows)[:N]
+    x = scale * sq[:, None] * sk[None, :] * mfma_scores(orc, q8[rows_idx], k8)
+    if causal:
+        x = np.where(np.arange(N)[None, :] <= rows_idx[:, None], x, -np.inf)
+    xabs = np.max(np.where(np.isfinite(x), np.abs(x), 0.0), axis=1)
+    mx = x.max(axis=1, keepdims=True)
+    e = np.exp(x - mx)
+    se = e.sum(axis=1, keepdims=True)
+    P = e / se
+    return P, P @ v, mx[:, 0] + np.log(se[:, 0]), xabs
+
+
 def emulated_reference(orc, c, rows, causal, scale):
-    """P', O', LSE' of the scores the instruction computes, and per row the
-    largest |scaled score| (for the fp32 slack)."""
+    """head_reference for every row of every head, stacked [B, Hq, ...]."""
     d = c["deq"]
     B, Hq, N, _ = d["q"].shape
     G = Hq // d["v"].shape[1]
     P = np.empty((B, Hq, N, N))
+    O = np.empty((B, Hq, N, d["v"].shape[3]))
     lse = np.empty((B, Hq, N))
     xabs = np.empty((B, Hq, N))
+    rows_idx = np.arange(N)
     for b in range(B):
         for h in range(Hq):
             hk = h // G
-            sq = np.repeat(c["qs"][b, h].astype(np.float64), rows)[:N]
-            sk = np.repeat(c["ks"][b, hk].astype(np.float64), rows)[:N]
-            x = scale * sq[:, None] * sk[None, :] * mfma_scores(orc, c["q8"][b, h], c["k8"][b, hk])
-            if causal:
-                x = np.where(np.arange(N)[None, :] <= np.arange(N)[:, None], x, -np.inf)
-            xabs[b, h] = np.max(np.where(np.isfinite(x), np.abs(x), 0.0), axis=1)
-            mx = x.max(axis=1, keepdims=True)
-            e = np.exp(x - mx)
-            P[b, h] = e / e.sum(axis=1, keepdims=True)
-            lse[b, h] = mx[:, 0] + np.log(e.sum(axis=1))
-    O = np.einsum("bhij,bhjc->bhic", P, np.repeat(d["v"], G, axis=1))
+            P[b, h], O[b, h], lse[b, h], xabs[b, h] = head_reference(
+                orc, c["q8"][b, h], c["qs"][b, h], c["k8"][b, hk], c["ks"][b, hk], d["v"][b, hk], rows_idx, rows,
+                causal, scale)
     return P, O, lse, xabs
 
 
-def fp8_bound(orc, c, rows, P, O, xabs):
-    """Per element bound on |O_gpu - O'| (module docstring)."""
-    d = c["deq"]
-    B, Hq, N, _ = P.shape
-    Hkv = d["v"].shape[1]
-    G = Hq // Hkv
+def head_bound(orc, v8, vs_runs, v, rows, P, O, xabs, chunk=8):
+    """Per element bound on |O_gpu - O'| (module docstring) for the rows of
+    one head whose P' [R, N], O' [R, d] and max |x| are given; V as codes
+    [N, d], run scales and dequantised values."""
+    R, N = P.shape
+    dd = O.shape[1]
     Np = -(-N // 64) * 64
-    vs = np.repeat(c["vs"].astype(np.float64), rows, axis=2)      # s_v per key, past N too
-    vs = np.concatenate([vs, np.repeat(vs[:, :, -1:], Np, axis=2)], axis=2)[:, :, :Np]
-    r = vs / vs.max(axis=2, keepdims=True)                        # V-scale ratio per key
+    vs = np.repeat(vs_runs.astype(np.float64), rows)
+    vs = np.concatenate([vs, np.full(Np, vs[-1])])[:Np]         # s_v per key, past N too
+    r = vs / vs.max()                                             # V-scale ratio per key
     order = (np.arange(Np // 64)[:, None, None] * 64 + tile_groups()[None]).reshape(-1)   # keys by group
+    r_g = r[order].reshape(-1, 8, MFMA_GROUP)[:, :, :1]          # one ratio per tile
+    v8p = np.zeros((Np, dd), dtype=np.uint8)
+    v8p[:N] = v8
+    vv = np.abs(orc.e4m3_decode(v8p)[order].reshape(-1, 8, MFMA_GROUP, dd))          # [tiles, 8, 8, d]
+    ev = np.where(vv != 0, e4m3_exp(v8p[order]).reshape(vv.shape), -1000)
+    bound = np.empty_like(O)
+    for i0 in range(0, R, chunk):
+        p = P[i0:i0 + chunk]
+        o = O[i0:i0 + chunk]
+        n = p.shape[0]
+        live = p > 0                                              # masked keys: exact zeros
+        pt = p / p.max(axis=1, keepdims=True)                     # P~ under the exact max
+        a = pt * r[None, :N]
+        D = np.where(a >= E4M3_MIN_NORMAL, E4M3_REL * a, np.minimum(a, E4M3_ABS)) / r[None, :N]
+        D = np.where(live, D, 0.0)
+        den = pt.sum(axis=1) - D.sum(axis=1)
+        dev = np.abs(v[None, :, :] - o[:, None, :])               # [n, N, d]
+        rounding = np.einsum("ij,ijc->ic", D, dev) / den[:, None]
+        # fp32 scores: relative error of the weights below 2^-20 |x| + 1e-6
+        slack = (2.0 ** -19 * xabs[i0:i0 + chunk] + 2e-6)[:, None] * np.einsum("ij,ijc->ic", p, dev)
+        # instruction truncation in P.V and in the ones-vector sum, keys in group order
+        a_up = np.zeros((n, Np))
+        a_up[:, :N] = np.where(live, a * (1 + E4M3_REL), 0.0)
+        a_up = a_up[:, order].reshape(n, -1, 8, MFMA_GROUP)       # [n, tiles, 8, 8]
+        ea = np.where(a_up > 0, np.maximum(np.floor(np.log2(np.where(a_up > 0, a_up, 1.0))), -6), -1000)
+        ones = group_loss(a_up / r_g[None], ea).sum(axis=-1) / den   # relative, per row
+        pv = np.empty((n, dd))
+        for k0 in range(n):
+            x = a_up[k0][..., None] * vv                          # [tiles, 8, 8, d]
+            ex = np.where((ea[k0][..., None] > -1000) & (ev > -1000), ea[k0][..., None] + ev, -1000)
+            pv[k0] = group_loss(np.moveaxis(x, -1, 0), np.moveaxis(ex, -1, 0)).sum(axis=-1)
+        pv *= vs.max() / den[:, None]
+        bound[i0:i0 + chunk] = rounding + slack + pv + 1.1 * np.abs(o) * ones[:, None]
+    return bound + bf16_half_ulp(O) + 1e-4
+
+
+def fp8_bound(orc, c, rows, P, O, xabs):
+    """Per element bound on |O_gpu - O'| for every row of every head."""
+    B, Hq = P.shape[:2]
+    G = Hq // c["v8"].shape[1]
     bound = np.empty_like(O)
     for b in range(B):
         for h in range(Hq):
             hk = h // G
-            p = P[b, h]
-            live = p > 0                                          # masked keys: exact zeros
-            pt = p / p.max(axis=1, keepdims=True)                 # P~ under the exact max
-            rk = r[b, hk, :N]
-            a = pt * rk[None, :]
-            D = np.where(a >= E4M3_MIN_NORMAL, E4M3_REL * a, np.minimum(a, E4M3_ABS)) / rk[None, :]
-            D = np.where(live, D, 0.0)
-            L = pt.sum(axis=1)
-            den = L - D.sum(axis=1)
-            dev = np.abs(d["v"][b, hk][None, :, :] - O[b, h][:, None, :])   # [N, N, d]
-            rounding = np.einsum("ij,ijc->ic", D, dev) / den[:, None]
-            # fp32 scores: relative error of the weights below 2^-20 |x| + 1e-6
-            slack = (2.0 ** -19 * xabs[b, h] + 2e-6)[:, None] * np.einsum("ij,ijc->ic", p, dev)
-            # instruction truncation in P.V and in the ones-vector sum, keys in group order
-            a_up = np.zeros((N, Np))
-            a_up[:, :N] = np.where(live, a * (1 + E4M3_REL), 0.0)
-            a_up = a_up[:, order].reshape(N, -1, 8, MFMA_GROUP)                     # [N, tiles, 8, 8]
-            ea = np.where(a_up > 0, np.maximum(np.floor(np.log2(np.where(a_up > 0, a_up, 1.0))), -6), -1000)
-            r_g = r[b, hk][order].reshape(-1, 8, MFMA_GROUP)[:, :, :1]              # one ratio per tile
-            ones = group_loss(a_up / r_g[None], ea).sum(axis=-1) / den                # relative, per row
-            v8 = np.zeros((Np, O.shape[3]), dtype=np.uint8)
-            v8[:N] = c["v8"][b, hk]
-            vv = orc.e4m3_decode(v8)[order].reshape(-1, 8, MFMA_GROUP, O.shape[3])  # [tiles, 8, 8, d]
-            ev = np.where(vv != 0, e4m3_exp(v8[order]).reshape(vv.shape), -1000)
-            pv = np.empty_like(O[b, h])
-            for i0 in range(0, N, 16):
-                x = a_up[i0:i0 + 16, ..., None] * np.abs(vv)[None]                  # [c, tiles, 8, 8, d]
-                ex = np.where((ea[i0:i0 + 16, ..., None] > -1000) & (ev[None] > -1000),
-                              ea[i0:i0 + 16, ..., None] + ev[None], -1000)
-                x, ex = np.moveaxis(x, -1, 1), np.moveaxis(ex, -1, 1)              # [c, d, tiles, 8, 8]
-                pv[i0:i0 + 16] = group_loss(x, ex).sum(axis=-1)
-            pv *= vs[b, hk].max() / den[:, None]
-            bound[b, h] = rounding + slack + pv + 1.1 * np.abs(O[b, h]) * ones[:, None]
-    return bound + bf16_half_ulp(O) + 1e-4
+            bound[b, h] = head_bound(orc, c["v8"][b, hk], c["vs"][b, hk], c["deq"]["v"][b, hk], rows, P[b, h],
+                                     O[b, h], xabs[b, h])
+    return bound
 
 
 def check_fp8(fa, orc, c, rows, causal, scale, tag, device_quant=None):
@@ -292,3 +312,47 @@ def test_constant_v(fa, orc):
     c["vs"][:] = 0.5
     o, _ = run_fp8(fa, c, 64, True, 0.0883883)
     assert np.max(np.abs(o - 0.6875)) == 0.0
+
+
+def test_full_size_gqa16k_sampled_rows(fa, orc):
+    """The configuration bench.py --fp8 times (gqa16k: B=2, Hq=32, Hkv=8,
+    N=16384, d=128, causal, 128-row runs, device quantisers), checked on 24
+    seeded rows (always 0 and N-1) of two heads in different K/V groups, all
+    16384 keys each, to the same bounds."""
+    import torch
+    w = ai.WORKLOADS["gqa16k"]
+    rows = 128
+    inp = ai.make_inputs(w, with_grad=False)
+    q, k, v = (to_dev(inp[t]) for t in ("q", "k", "v"))
+    q8, qs = fa.quantize_e4m3(q, rows)
+    k8, ks = fa.quantize_e4m3(k, rows)
+    v8t, vs = fa.quantize_e4m3_vt(v, rows)
+    say("fwd_e4m3 gqa16k full size")
+    o, lse = fa.fwd_e4m3(q8, qs, k8, ks, v8t, vs, rows, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    rows_idx = ai.sample_rows(w.N, 24, w.cfg_id)
+    worst = 0.0
+    for b, h in ((0, 0), (1, 29)):
+        hk = h // w.G
+        qh = ai.bf16_bits_to_f32(inp["q"][b, h])[None, None]
+        kh = ai.bf16_bits_to_f32(inp["k"][b, hk])[None, None]
+        vh = ai.bf16_bits_to_f32(inp["v"][b, hk])[None, None]
+        q8h, qsh = orc.quantize_e4m3(qh, rows)
+        k8h, ksh = orc.quantize_e4m3(kh, rows)
+        v8h, vsh = orc.quantize_e4m3(vh, rows)
+        # the device's codes and scales are the oracle's
+        assert np.array_equal(q8[b, h].cpu().numpy(), q8h[0, 0]) and np.array_equal(k8[b, hk].cpu().numpy(), k8h[0, 0])
+        assert np.array_equal(vs[b, hk].cpu().numpy().view(np.uint32), vsh[0, 0].view(np.uint32))
+        vdeq = orc.dequantize_e4m3(v8h, vsh, rows)[0, 0]
+        P, O, L, xabs = head_reference(orc, q8h[0, 0], qsh[0, 0], k8h[0, 0], ksh[0, 0], vdeq, rows_idx, rows,
+                                       w.causal, w.scale)
+        bound = head_bound(orc, v8h[0, 0], vsh[0, 0], vdeq, rows, P, O, xabs)
+        og = from_dev_bf16(o[b, h])[rows_idx]
+        lg = lse[b, h].double().cpu().numpy()[rows_idx]
+        lb = 1e-5 + 2.0 ** -19 * xabs + w.N * 2.0 ** -23
+        eo, el = np.abs(og - O), np.abs(lg - L)
+        ratio, lratio = float((eo / bound).max()), float((el / lb).max())
+        worst = max(worst, ratio)
+        say(f"gqa16k head ({b}, {h}): max|O - O'| {eo.max():.3e} ({ratio:.3f} of the bound), "
+            f"max|LSE - LSE'| {el.max():.2e} ({lratio:.3f} of its bound)")
+        assert np.all(np.isfinite(og)) and ratio <= 1.0 and lratio <= 1.0, (b, h, ratio, lratio)
