@@ -174,7 +174,7 @@ __global__ __launch_bounds__(k8Threads, 1) void fwd8_kernel(Fwd8Params p) {
     for (int db = 0; db < DB; ++db) o[db] = zero16();
     float m = 0.f, l = 0.f, lsum = 0.f;
     const uint32_t one8 = 0x38383838u;   // E4M3 1.0 in every byte
-    const i32x8 ones = {(int)one8, (int)one8, (int)one8, (int)one8, (int)one8, (int)one8, (int)one8, (int)one8};
+    i32x8 ones = {(int)one8, (int)one8, (int)one8, (int)one8, (int)one8, (int)one8, (int)one8, (int)one8};
 
     const BufRes rk = make_bufres(p.k + (size_t)bkv * N * D, (uint32_t)N * D);
     const BufRes rv = make_bufres(p.vt + (size_t)bkv * D * Np, (uint32_t)D * Np);
@@ -187,6 +187,15 @@ __global__ __launch_bounds__(k8Threads, 1) void fwd8_kernel(Fwd8Params p) {
     wait_vmem();
     __syncthreads();
 
+    // The K/V scale run of tile j: runs hold R / 64 whole tiles, so the run
+    // advances by counting, and the values derived from its scales change
+    // only at a run's first tile. The next run's scales are fetched a run
+    // ahead (uniform addresses: scalar loads).
+    const int tpr = R / k8BN;
+    int run = 0, jr = 0;
+    float sk_next = p.k_scales[(size_t)bkv * nrun], sv_next = p.v_scales[(size_t)bkv * nrun];
+    float sk = 0.f, lrv = 0.f, inv_rv = 1.f;
+
     for (int j = 0; j < nt; ++j) {
         FA_LDS uint8_t* Kt = Ks + (j & 1) * C::KT;
         FA_LDS uint8_t* Vt = Vs + (j & 1) * C::VT;
@@ -194,53 +203,24 @@ __global__ __launch_bounds__(k8Threads, 1) void fwd8_kernel(Fwd8Params p) {
             pk.copy(rk, (uint32_t)(j + 1) * k8BN * D, Ks + ((j + 1) & 1) * C::KT, w);
             pv.copy(rv, (uint32_t)(j + 1) * k8BN, Vs + ((j + 1) & 1) * C::VT, w);
         }
-        if (wave_valid && j <= last) {
-            const int run = (j * k8BN) / R;
-            const float sk = p.k_scales[(size_t)bkv * nrun + run];
-            const float sv = p.v_scales[(size_t)bkv * nrun + run];
+        if (jr == 0) {
+            sk = sk_next;
+            const float sv = sv_next;
+            lrv = __log2f(sv / svmax);       // <= 0: the run's V ratio, log2
+            inv_rv = svmax / sv;
+            if (run + 1 < nrun) {
+                sk_next = p.k_scales[(size_t)bkv * nrun + run + 1];
+                sv_next = p.v_scales[(size_t)bkv * nrun + run + 1];
+            }
+        }
+        // the tile's body; MASKED for the diagonal and the ragged last tile
+        auto tile = [&](auto masked_c) {
+            constexpr bool MASKED = decltype(masked_c)::value;
             const float cs = sq * sk * p.scale_log2;     // score code units -> log2 units
-            const float lrv = __log2f(sv / svmax);       // <= 0: the tile's V ratio, log2
-            const float inv_rv = svmax / sv;
-            f32x16 s[2];
-            s[0] = scores8<D>(Kt, 0, l32, hh, qf);
-            s[1] = scores8<D>(Kt, 1, l32, hh, qf);
-            const bool masked = (causal && j == last) || (j + 1) * k8BN > N;
-            if (masked) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = j * k8BN + h * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-                        if (key >= N || (causal && key > qrow)) s[h][i] = -INFINITY;
-                    }
-            }
-            if (j == 0) {   // the first reference: this tile's exact (masked) max
-                float mx = -INFINITY;
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
-                m = fmaxf(mx, swap_half(mx)) * cs;
-            }
-            // x = S cs - m + log2(s_v / s_vmax); P~ r = exp2(x)
-            float ls = 0.f;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    s[h][i] = fmaf(s[h][i], cs, lrv - m);
-                    const float e = fast_exp2(s[h][i]);
-                    ls += e;
-                    s[h][i] = e;
-                }
-            if (__ballot(!(ls <= k8SumMax))) {
-                // a new reference: the exact max (in units of P~), then O, l
-                // and the rounded sum rescaled and the exps redone
-                float mx = -INFINITY;
-                // recover x from the exps is not exact; recompute the scores
+                f32x16 s[2];
                 s[0] = scores8<D>(Kt, 0, l32, hh, qf);
                 s[1] = scores8<D>(Kt, 1, l32, hh, qf);
-                if (masked) {
+                if constexpr (MASKED) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -249,48 +229,95 @@ __global__ __launch_bounds__(k8Threads, 1) void fwd8_kernel(Fwd8Params p) {
                             if (key >= N || (causal && key > qrow)) s[h][i] = -INFINITY;
                         }
                 }
+                if (j == 0) {   // the first reference: this tile's exact (masked) max
+                    float mx = -INFINITY;
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
-                mx = fmaxf(mx, swap_half(mx)) * cs;
-                const float delta = fmaxf(mx - m, 0.f);
-                const float alpha = fast_exp2(-delta);
-                m += delta;
-                l *= alpha;
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-                ls = 0.f;
+                        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
+                    m = fmaxf(mx, swap_half(mx)) * cs;
+                }
+                // x = S cs - m + log2(s_v / s_vmax); P~ r = exp2(x)
+                float ls = 0.f;
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float e = fast_exp2(fmaf(s[h][i], cs, lrv - m));
+                        s[h][i] = fmaf(s[h][i], cs, lrv - m);
+                        const float e = fast_exp2(s[h][i]);
                         ls += e;
                         s[h][i] = e;
                     }
-            }
-            // P~ r rounded to E4M3: byte c * 16 + i <- half c, register i
-            i32x8 pp;
+                if (__ballot(!(ls <= k8SumMax))) {
+                    // a new reference: the exact max (in units of P~), then O, l
+                    // and the rounded sum rescaled and the exps redone
+                    float mx = -INFINITY;
+                    // recover x from the exps is not exact; recompute the scores
+                    s[0] = scores8<D>(Kt, 0, l32, hh, qf);
+                    s[1] = scores8<D>(Kt, 1, l32, hh, qf);
+                    if constexpr (MASKED) {
 #pragma unroll
-            for (int wd = 0; wd < 8; ++wd) {
-                const int h = wd >> 2, i = (wd & 3) * 4;
-                int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[h][i], s[h][i + 1], 0, false);
-                v = __builtin_amdgcn_cvt_pk_fp8_f32(s[h][i + 2], s[h][i + 3], v, true);
-                pp[wd] = v;
-            }
+                        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const FA_LDS uint8_t* a = Vt + (db * 32 + l32) * C::VS + hh * 32;
-                o[db] = mfma8(cat8(lds_read16b(a, 0), lds_read16b(a, 16)), pp, o[db]);
-            }
-            const f32x16 t = mfma8(ones, pp, zero16());
-            lsum = fmaf(t[0], inv_rv, lsum);
-            l = fmaf(ls, inv_rv, l);
+                            for (int i = 0; i < 16; ++i) {
+                                const int key = j * k8BN + h * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+                                if (key >= N || (causal && key > qrow)) s[h][i] = -INFINITY;
+                            }
+                    }
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
+                    mx = fmaxf(mx, swap_half(mx)) * cs;
+                    const float delta = fmaxf(mx - m, 0.f);
+                    const float alpha = fast_exp2(-delta);
+                    m += delta;
+                    l *= alpha;
+                    lsum *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+                    ls = 0.f;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const float e = fast_exp2(fmaf(s[h][i], cs, lrv - m));
+                            ls += e;
+                            s[h][i] = e;
+                        }
+                }
+                // P~ r rounded to E4M3: byte c * 16 + i <- half c, register i
+                i32x8 pp;
+#pragma unroll
+                for (int wd = 0; wd < 8; ++wd) {
+                    const int h = wd >> 2, i = (wd & 3) * 4;
+                    // the second conversion overwrites the other half, so the
+                    // first one may write over its own (dead) input
+                    int v = __builtin_amdgcn_cvt_pk_fp8_f32(s[h][i], s[h][i + 1], __float_as_int(s[h][i]), false);
+                    v = __builtin_amdgcn_cvt_pk_fp8_f32(s[h][i + 2], s[h][i + 3], v, true);
+                    pp[wd] = v;
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const FA_LDS uint8_t* a = Vt + (db * 32 + l32) * C::VS + hh * 32;
+                    o[db] = mfma8(cat8(lds_read16b(a, 0), lds_read16b(a, 16)), pp, o[db]);
+                }
+                const f32x16 t = mfma8(ones, pp, zero16());
+                lsum = fmaf(t[0], inv_rv, lsum);
+                l = fmaf(ls, inv_rv, l);
+        };
+        if (wave_valid && j <= last) {
+            if ((causal && j == last) || (j + 1) * k8BN > N) tile(std::true_type{});
+            else tile(std::false_type{});
         }
+        if (++jr == tpr) {
+            jr = 0;
+            ++run;
+        }
+        // keeps the ones operand resident rather than rebuilt every tile
+        asm volatile("" : "+v"(ones));
         wait_vmem();
         __syncthreads();
     }
