@@ -493,6 +493,6 @@ const char* flash_attn_strerror(int status) {
     }
 }
 
-const char* flash_attn_version(void) { return "0.6.0 gfx950"; }
+const char* flash_attn_version(void) { return "0.7.0 gfx950"; }
 
 }  // extern "C"

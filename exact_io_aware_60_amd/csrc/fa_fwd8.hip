@@ -40,7 +40,11 @@
 //    max, then a new exact max only when some lane's sum of its 32
 //    probabilities (times the V ratio) passes 2^8, so every E4M3 value stays
 //    at most 2^8 (the format's largest is 448).
-//  * 8 waves of 32 query rows, two per SIMD. 64-key tiles stream through LDS
+//  * 12 waves of 32 query rows, three per SIMD (at most 168 registers each):
+//    the kernel is bound by vector-ALU issue, and a third wave per SIMD
+//    hides more of it under the matrix instructions than two (measured on
+//    MI355X: 3.27 -> 2.86 ms on a 2 x 32-head, 16384-row causal forward,
+//    though 14 registers spill at d = 128). 64-key tiles stream through LDS
 //    with direct buffer->LDS loads into padded rows (K: D + 16 bytes, V^T: 80
 //    bytes; 16-byte reads of 16 consecutive rows then hit distinct banks),
 //    two buffers each, one barrier per tile.
@@ -54,7 +58,7 @@
 namespace fa {
 namespace {
 
-constexpr int k8Waves = 8;
+constexpr int k8Waves = 12;
 constexpr int k8Threads = 64 * k8Waves;
 constexpr int k8WM = 32;                   // query rows per wave
 constexpr int k8BM = k8WM * k8Waves;       // query rows per workgroup
@@ -316,8 +320,9 @@ __global__ __launch_bounds__(k8Threads, 1) void fwd8_kernel(Fwd8Params p) {
             jr = 0;
             ++run;
         }
-        // keeps the ones operand resident rather than rebuilt every tile
-        asm volatile("" : "+v"(ones));
+        // d = 64: keeps the ones operand resident rather than rebuilt every
+        // tile (at d = 128 its 8 registers would spill at three waves per SIMD)
+        if constexpr (D == 64) asm volatile("" : "+v"(ones));
         wait_vmem();
         __syncthreads();
     }

@@ -393,7 +393,7 @@ int flash_attn_fwd_e4m3(const void* q8, const float* q_scales, const void* k8, c
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
 
-/* Library version and the GPU target it was compiled for, e.g. "0.6.0 gfx950". */
+/* Library version and the GPU target it was compiled for, e.g. "0.7.0 gfx950". */
 const char* flash_attn_version(void);
 
 #ifdef __cplusplus
