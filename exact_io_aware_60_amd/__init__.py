@@ -29,7 +29,7 @@ EXPORTED = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size",
             "flash_attn_decode", "flash_attn_decode_workspace_size", "flash_attn_fwd_varlen",
             "flash_attn_fwd_window", "flash_attn_bwd_window", "flash_attn_bwd_varlen",
             "flash_attn_quantize_e4m3", "flash_attn_decode_noalloc", "flash_attn_decode_noalloc_max_bytes",
-            "flash_attn_quantize_e4m3_vt", "flash_attn_fwd_e4m3", "flash_attn_fwd_f32")
+            "flash_attn_quantize_e4m3_vt", "flash_attn_fwd_e4m3", "flash_attn_fwd_f32", "flash_attn_fwd_geometry")
 BWD_STAGES = ("flash_attn_bwd_preprocess", "flash_attn_bwd_dq", "flash_attn_bwd_dkdv")
 
 _lib = None
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.flash_attn_strerror.argtypes = [_i]
         L.flash_attn_version.restype = ctypes.c_char_p
         L.flash_attn_version.argtypes = []
+        L.flash_attn_fwd_geometry.restype = _i
+        L.flash_attn_fwd_geometry.argtypes = [_i] * 6 + [_vp]
         _lib = L
     return _lib
 
@@ -96,6 +98,15 @@ def strerror(status: int) -> str:
 
 def version() -> str:
     return lib().flash_attn_version().decode()
+
+
+def fwd_geometry(B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool = True) -> dict:
+    """Launch shape of flash_attn_fwd for these arguments (host logic only)."""
+    out = (ctypes.c_int * 5)()
+    st = lib().flash_attn_fwd_geometry(B, Hq, Hkv, N, d, int(causal), out)
+    if st != FA_OK:
+        raise FlashAttnError(st, strerror(st))
+    return dict(zip(("block_m", "block_n", "threads", "grid", "lds_bytes"), out))
 
 
 def _check(status: int) -> None:

@@ -493,6 +493,19 @@ const char* flash_attn_strerror(int status) {
     }
 }
 
-const char* flash_attn_version(void) { return "0.7.0 gfx950"; }
+const char* flash_attn_version(void) { return "0.8.0 gfx950"; }
+
+int flash_attn_fwd_geometry(int B, int Hq, int Hkv, int N, int d, int causal, int* out) {
+    if (!out) return FA_ERR_NULL;
+    const int st = check_shape(B, Hq, Hkv, N, d);
+    if (st != FA_OK) return st;
+    const fa::Geometry g = fa::fwd_geometry(B, Hq, N, d, causal);
+    out[0] = g.block_m;
+    out[1] = g.block_n;
+    out[2] = g.threads;
+    out[3] = g.grid;
+    out[4] = g.lds_bytes;
+    return FA_OK;
+}
 
 }  // extern "C"

@@ -13,7 +13,12 @@
 //    SIMD hides only about 2 VALU instructions under each 32x32x16 MFMA; two
 //    waves per SIMD hide most of them. So a workgroup is 8 waves (2 per SIMD),
 //    each owning 32 query rows (256 rows per workgroup, at most 256 registers
-//    per wave).
+//    per wave). At d = 64 a score costs half the MFMA work for the same
+//    softmax work, and the wave's loop fits in 152 registers: large grids take
+//    12 waves (3 per SIMD, 384 rows), 10.8% less time on a 2 x 64-head,
+//    16384-row causal forward. At d = 128 a third wave per SIMD does not fit
+//    this loop (168 registers); the loop without the cross-chunk pipelining
+//    does, and measured no faster than two pipelined waves.
 //  * Keys are streamed in tiles of 64 through LDS with direct global->LDS
 //    loads: K in 3 buffers, V in 2, one barrier per tile. Tiles are stored
 //    densely with XOR-swizzled 16-byte chunks (fa_device.h): K by row for the
@@ -51,6 +56,8 @@
 //    the ragged last chunk are masked element-wise. Workgroups run heaviest
 //    q-tile first (longest-processing-time order). Workgroups of one head set
 //    map to one XCD, so their K/V re-reads hit the same L2.
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_params.h"
 
@@ -61,24 +68,29 @@ constexpr int kWM = 32;        // query rows per wave
 constexpr int kBN = 64;        // keys per LDS tile
 constexpr float kSumMax = 256.0f;   // largest partial sum of P accepted without a new reference
 
-// d = 64 and 128: 8 waves, two per SIMD (at most 256 registers each). d = 256:
-// a wave's Q and O alone take 192 registers, so 4 waves, one per SIMD (up to
-// 512 registers), and 128 rows per workgroup; its 3 K + 2 V tiles of 32 KiB
+// d = 64 and 128: 8 waves, two per SIMD (at most 256 registers each). d = 64
+// also has a 12-wave form, three per SIMD (its pipelined loop needs 152
+// registers, within the 168 of three waves), for large grids (fwd_waves). d =
+// 256: a wave's Q and O alone take 192 registers, so 4 waves, one per SIMD (up
+// to 512 registers), and 128 rows per workgroup; its 3 K + 2 V tiles of 32 KiB
 // fill the 160 KiB of LDS.
 // PAD: the tensors' rows hold fewer than D values (a multiple of 8); the
 // tiles' columns past them stay zero (CopyPlanSwz with PAD), so every product
 // over D columns equals the product over the real ones.
-template <int D, bool PAD = false>
+template <int D, bool PAD = false, int W = (D == 256 ? 4 : 8)>
 struct FwdCfg {
     static constexpr int DS = D / 16, DB = D / 32;
-    static constexpr int WAVES = D == 256 ? 4 : 8;
+    static constexpr int WAVES = W;
+    // Waves that copy: a tile is 16 (d = 128) or 8 (d = 64) blocks of 1 KiB,
+    // so with 12 waves the first 8 copy and the other 4 only compute.
+    static constexpr int CW = W > 8 ? 8 : W;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int BM = kWM * WAVES;                       // query rows per workgroup
     static constexpr int L = 2 * D;                              // bytes per K / V row
     static constexpr int KT = kBN * L, VT = kBN * L;
     static constexpr int LDS = 3 * KT + 2 * VT;
-    using PlanK = CopyPlanSwz<L, kBN, WAVES, RowKey<L>, PAD>;
-    using PlanV = CopyPlanSwz<L, kBN, WAVES, TrKey<L>, PAD>;
+    using PlanK = CopyPlanSwz<L, kBN, CW, RowKey<L>, PAD>;
+    using PlanV = CopyPlanSwz<L, kBN, CW, TrKey<L>, PAD>;
 };
 
 // Workgroup id -> (rank, bh). Workgroups are handed to the 8 XCDs round-robin,
@@ -233,8 +245,9 @@ __device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt
 // loads before the MFMAs stalls both waves of a SIMD together right after the
 // tile barrier; spread out, each load costs about one issue slot. Otherwise
 // (the chunk is the wave's last, or past it) `bulk` issues them all at once.
-// ON = false issues nothing.
-template <int D, bool ON, bool PAD = false>
+// ON = false issues nothing. GUARD: the workgroup has more waves than copy
+// (FwdCfg::CW); the others skip their items.
+template <int D, bool ON, bool PAD = false, bool GUARD = false>
 struct FwdCopies {
     using PlanK = typename FwdCfg<D, PAD>::PlanK;
     using PlanV = typename FwdCfg<D, PAD>::PlanV;
@@ -252,6 +265,9 @@ struct FwdCopies {
         if constexpr (ON && step >= 1 && (step - 1) % SP == 0 && (step - 1) / SP < NI) {
             constexpr int i = (step - 1) / SP;
             const int ws = __builtin_amdgcn_readfirstlane(w);
+            if constexpr (GUARD) {
+                if (ws >= FwdCfg<D, PAD>::CW) return;
+            }
             if constexpr (i < NK)
                 pk->copy_one(i, rk, koff, Kw, ws);
             else
@@ -260,6 +276,9 @@ struct FwdCopies {
     }
     __device__ __forceinline__ void bulk() const {
         if constexpr (ON) {
+            if constexpr (GUARD) {
+                if (__builtin_amdgcn_readfirstlane(w) >= FwdCfg<D, PAD>::CW) return;
+            }
             pk->copy(rk, koff, Kw, w);
             pv->copy(rv, voff, Vw, w);
         }
@@ -369,14 +388,14 @@ struct Window {
 // Kc: the K tile holding this chunk; Kn: the K tile holding the next chunk;
 // Kr1: K tile j+1, which holds chunk c+2 (half H); Vt: this chunk's V tile.
 // cp carries the iteration's copies (first chunk only).
-template <int D, int H, bool CP, bool WIN, bool PAD>
+template <int D, int H, bool CP, bool WIN, bool PAD, bool GUARD>
 __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f32x16& sn,
                                           const FA_LDS uint8_t* __restrict__ Kc,
                                           const FA_LDS uint8_t* __restrict__ Kn,
                                           const FA_LDS uint8_t* __restrict__ Kr1,
                                           const FA_LDS uint8_t* __restrict__ Vt, int kbase, int vbase,
                                           bool causal, int qrow, int N, int lastc, float sl2, int hh,
-                                          const FwdCopies<D, CP, PAD>& cp, const Window& wd) {
+                                          const FwdCopies<D, CP, PAD, GUARD>& cp, const Window& wd) {
     if (c > lastc) {
         cp.bulk();
         return;
@@ -421,7 +440,7 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
 // __restrict__ qualifiers say so, which lets the compiler see that the LDS
 // reads do not touch the LDS the in-flight global->LDS copies write, so it does
 // not wait for those copies before each read.
-template <int D, bool WIN, bool PAD>
+template <int D, bool WIN, bool PAD, bool GUARD>
 __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt,
                                               const typename FwdCfg<D, PAD>::PlanK& pk,
                                               const typename FwdCfg<D, PAD>::PlanV& pv, BufRes rk, BufRes rv,
@@ -436,14 +455,15 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt,
     // Tiles j + 1 and j + 2 may lie past the last one: their copies then read
     // past the resource (zeros) into buffers no chunk reads any more (those of
     // tiles j - 1 and j - 2).
-    const FwdCopies<D, true, PAD> cp{&pk, &pv, rk, rv, (uint32_t)(j + 2) * kBN * dr * 2,
-                                     (uint32_t)(j + 1) * kBN * dr * 2, Kw, Vw, w};
+    const FwdCopies<D, true, PAD, GUARD> cp{&pk, &pv, rk, rv, (uint32_t)(j + 2) * kBN * dr * 2,
+                                            (uint32_t)(j + 1) * kBN * dr * 2, Kw, Vw, w};
     if (valid) {
         const int hh = lane >> 5;
-        fwd_chunk<D, 0, true, WIN, PAD>(st, 2 * j, st.sA, st.sB, Kr0, Kr0, Kr1, Vr, kbase, vbase, causal, qrow, N,
-                                   lastc, sl2, hh, cp, wd);
-        fwd_chunk<D, 1, false, WIN, PAD>(st, 2 * j + 1, st.sB, st.sA, Kr0, Kr1, Kr1, Vr, kbase, vbase, causal, qrow,
-                                         N, lastc, sl2, hh, FwdCopies<D, false, PAD>{}, wd);
+        fwd_chunk<D, 0, true, WIN, PAD, GUARD>(st, 2 * j, st.sA, st.sB, Kr0, Kr0, Kr1, Vr, kbase, vbase, causal,
+                                               qrow, N, lastc, sl2, hh, cp, wd);
+        fwd_chunk<D, 1, false, WIN, PAD, GUARD>(st, 2 * j + 1, st.sB, st.sA, Kr0, Kr1, Kr1, Vr, kbase, vbase,
+                                                causal, qrow, N, lastc, sl2, hh,
+                                                FwdCopies<D, false, PAD, GUARD>{}, wd);
     } else {
         cp.bulk();
     }
@@ -452,9 +472,10 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt,
 // The causal flag is a run-time argument: it only changes the tile ranges and
 // the mask of each wave's last chunk, so one instance per head dimension
 // serves both cases.
-template <int D, bool WIN, bool PAD>
-__global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p) {
-    using C = FwdCfg<D, PAD>;
+template <int D, bool WIN, bool PAD, int W>
+__global__ __launch_bounds__(64 * W, 1) void fwd_kernel(FwdParams p) {
+    using C = FwdCfg<D, PAD, W>;
+    constexpr bool GUARD = C::WAVES > C::CW;
     constexpr int DS = C::DS, DB = C::DB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
     FA_LDS uint8_t* Ks = (FA_LDS uint8_t*)smem;          // 3 K tiles
@@ -544,9 +565,11 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
 
     // K tiles js, js+1 and V tile js before the loop (js = 0 without a window),
     // in the buffers the loop's index arithmetic expects for them.
-    pk.copy(rk, (uint32_t)js * kBN * dr * 2, Ks + (js % 3) * C::KT, w);
-    if (nt > js + 1) pk.copy(rk, (uint32_t)(js + 1) * kBN * dr * 2, Ks + ((js + 1) % 3) * C::KT, w);
-    pv.copy(rv, (uint32_t)js * kBN * dr * 2, Vs + (js & 1) * C::VT, w);
+    if (!GUARD || w < C::CW) {
+        pk.copy(rk, (uint32_t)js * kBN * dr * 2, Ks + (js % 3) * C::KT, w);
+        if (nt > js + 1) pk.copy(rk, (uint32_t)(js + 1) * kBN * dr * 2, Ks + ((js + 1) % 3) * C::KT, w);
+        pv.copy(rv, (uint32_t)js * kBN * dr * 2, Vs + (js & 1) * C::VT, w);
+    }
     wait_vmem();
     __syncthreads();
 
@@ -562,7 +585,7 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
         for (int i = 0; i < 16; ++i) st.sA[i] = fmaf(st.sA[i], sl2, -st.m);
     }
     for (int j = js; j < nt; ++j) {
-        fwd_iteration<D, WIN, PAD>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT,
+        fwd_iteration<D, WIN, PAD, GUARD>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT,
                                    Vs + ((j + 1) & 1) * C::VT, Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT,
                                    Vs + (j & 1) * C::VT, kbase, vbase, wave_valid, causal, qrow, N, lastc, sl2, w,
                                    lane, wd, dr);
@@ -593,25 +616,65 @@ __global__ __launch_bounds__(FwdCfg<D>::THREADS, 1) void fwd_kernel(FwdParams p)
     }
 }
 
+// Compute units of the current GPU, read once per device.
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Waves per workgroup. d = 64 takes 12 (three per SIMD; measured on MI355X:
+// 10.8% less time on a 2 x 64-head, 16384-row causal forward, the same
+// results bit for bit) unless the grid is small: 384-row workgroups then leave
+// more of the last round of workgroups idle than the faster waves recover
+// (4 x 16 heads of 2048 rows, causal: 4.6% more time; 2 x 16 heads of 4096
+// rows, not causal: 19% more). The choice compares rounds of one workgroup per
+// CU times rows per workgroup, a 12-wave row taking 0.9 of the time.
 template <int D>
-hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-    using C = FwdCfg<D>;
+int fwd_waves(int B, int Hq, int N) {
+    if constexpr (D != 64) {
+        return FwdCfg<D>::WAVES;
+    } else {
+        const long long bh = (long long)B * Hq, cu = cu_count();
+        const long long r8 = (bh * ((N + 255) / 256) + cu - 1) / cu;
+        const long long r12 = (bh * ((N + 383) / 384) + cu - 1) / cu;
+        return r12 * 384 * 9 < r8 * 256 * 10 ? 12 : 8;
+    }
+}
+
+template <int D, int W>
+hipError_t launch_fwd_w(const FwdParams& p, hipStream_t stream) {
+    using C = FwdCfg<D, false, W>;
     const int nqt = (p.N + C::BM - 1) / C::BM;
     const int grid = p.B * p.Hq * nqt;
     const bool pad = p.d != D;
     if (p.window > 0) {
-        if (pad) hipLaunchKernelGGL((fwd_kernel<D, true, true>), dim3(grid), dim3(C::THREADS), 0, stream, p);
-        else hipLaunchKernelGGL((fwd_kernel<D, true, false>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+        if (pad) hipLaunchKernelGGL((fwd_kernel<D, true, true, W>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+        else hipLaunchKernelGGL((fwd_kernel<D, true, false, W>), dim3(grid), dim3(C::THREADS), 0, stream, p);
     } else {
-        if (pad) hipLaunchKernelGGL((fwd_kernel<D, false, true>), dim3(grid), dim3(C::THREADS), 0, stream, p);
-        else hipLaunchKernelGGL((fwd_kernel<D, false, false>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+        if (pad) hipLaunchKernelGGL((fwd_kernel<D, false, true, W>), dim3(grid), dim3(C::THREADS), 0, stream, p);
+        else hipLaunchKernelGGL((fwd_kernel<D, false, false, W>), dim3(grid), dim3(C::THREADS), 0, stream, p);
     }
     return hipGetLastError();
 }
 
 template <int D>
-Geometry geometry_t(int B, int Hq, int N) {
-    using C = FwdCfg<D>;
+hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
+    if constexpr (D == 64) {
+        if (fwd_waves<D>(p.B, p.Hq, p.N) == 12) return launch_fwd_w<D, 12>(p, stream);
+    }
+    return launch_fwd_w<D, FwdCfg<D>::WAVES>(p, stream);
+}
+
+template <int D, int W>
+Geometry geometry_w(int B, int Hq, int N) {
+    using C = FwdCfg<D, false, W>;
     Geometry g;
     g.block_m = C::BM;
     g.block_n = kBN;
@@ -619,6 +682,14 @@ Geometry geometry_t(int B, int Hq, int N) {
     g.grid = B * Hq * ((N + C::BM - 1) / C::BM);
     g.lds_bytes = C::LDS;
     return g;
+}
+
+template <int D>
+Geometry geometry_t(int B, int Hq, int N) {
+    if constexpr (D == 64) {
+        if (fwd_waves<D>(B, Hq, N) == 12) return geometry_w<D, 12>(B, Hq, N);
+    }
+    return geometry_w<D, FwdCfg<D>::WAVES>(B, Hq, N);
 }
 
 }  // namespace

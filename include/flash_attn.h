@@ -393,8 +393,22 @@ int flash_attn_fwd_e4m3(const void* q8, const float* q_scales, const void* k8, c
  * error string of the calling thread's last failed launch. Never NULL. */
 const char* flash_attn_strerror(int status);
 
-/* Library version and the GPU target it was compiled for, e.g. "0.7.0 gfx950". */
+/* Library version and the GPU target it was compiled for, e.g. "0.8.0 gfx950". */
 const char* flash_attn_version(void);
+
+/*
+ * Launch shape flash_attn_fwd would use for these arguments on the current GPU,
+ * for logging and tests of the host logic (no GPU work, nothing enqueued):
+ *   out[0] query rows per workgroup, out[1] keys per streamed tile,
+ *   out[2] threads per workgroup, out[3] workgroups, out[4] LDS bytes per
+ *   workgroup.
+ * At d <= 64 the forward takes workgroups of 8 waves (256 rows) or, for large
+ * grids, 12 waves (384 rows, three per SIMD); the choice depends on B * Hq, N
+ * and the GPU's compute-unit count (256 assumed when no GPU is current).
+ * Returns FA_ERR_NULL for a NULL out, or the status flash_attn_fwd would
+ * return for a rejected shape (out is then left unchanged).
+ */
+int flash_attn_fwd_geometry(int B, int Hq, int Hkv, int N, int d, int causal, int* out);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 """The C ABI without a GPU: the library loads, exports every function the header
 declares, and rejects bad arguments with the documented status before any HIP call."""
+import ctypes
 import os
 import re
 import subprocess
@@ -315,3 +316,35 @@ def test_bwd_varlen_checks():
     bad = list(args)
     bad[19] = need - 1
     assert fa.bwd_varlen_raw(*bad) == fa.FA_ERR_WORKSPACE
+
+
+# (B, Hq, Hkv, N, d, waves): d <= 64 takes 12-wave (384-row) workgroups when the
+# rounds of one workgroup per CU (256 when no GPU is current) times rows per
+# workgroup, at 0.9 for a 12-wave row, come out below those of 8 waves.
+WAVE_CASES = [
+    (2, 64, 16, 16384, 64, 12),   # 8192 vs 5504 workgroups: 32 vs 22 rounds
+    (4, 16, 16, 2048, 64, 8),     # 512 vs 384: 2 rounds either way, 384-row ones take longer
+    (2, 16, 16, 4096, 64, 8),
+    (1, 64, 8, 4100, 64, 12),     # 1088 vs 704: 5 vs 3 rounds
+    (1, 64, 8, 4100, 48, 12),     # a padded head dimension runs the d = 64 kernels
+    (1, 32, 8, 16384, 64, 8),     # 2048 vs 1376: 8 vs 6 rounds, 8 * 256 * 10 < 6 * 384 * 9
+    (2, 32, 8, 16384, 128, 8),    # d = 128: always 8 waves
+    (2, 16, 4, 16384, 256, 4),    # d = 256: 4 waves
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,waves", WAVE_CASES)
+def test_fwd_geometry_wave_choice(B, Hq, Hkv, N, d, waves):
+    g = fa.fwd_geometry(B, Hq, Hkv, N, d)
+    assert g["threads"] == 64 * waves and g["block_m"] == 32 * waves, g
+    assert g["block_n"] == 64
+    assert g["grid"] == B * Hq * -(-N // g["block_m"])
+    assert g["lds_bytes"] == 5 * 64 * 2 * (256 if d > 128 else 128 if d > 64 else 64)
+
+
+def test_fwd_geometry_checks():
+    out = (ctypes.c_int * 5)(*range(5))
+    assert fa.lib().flash_attn_fwd_geometry(1, 4, 2, 128, 128, 1, None) == fa.FA_ERR_NULL
+    assert fa.lib().flash_attn_fwd_geometry(1, 4, 2, 128, 132, 1, out) == fa.FA_ERR_HEADDIM
+    assert fa.lib().flash_attn_fwd_geometry(1, 4, 3, 128, 128, 1, out) == fa.FA_ERR_SHAPE
+    assert list(out) == [0, 1, 2, 3, 4]

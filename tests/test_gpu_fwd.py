@@ -246,3 +246,15 @@ def test_padded_headdim_gqa(fa, d):
     inp = ai.make_case(2, 8, 2, 700, d, seed=6100 + d, with_grad=False)
     check_full(fa, inp, True, 1.0 / math.sqrt(d), f"padded gqa d={d}")
     check_full(fa, inp, False, 1.0 / math.sqrt(d), f"padded gqa d={d} noncausal")
+
+
+@pytest.mark.parametrize("d", [64, 48])
+@pytest.mark.parametrize("causal", [False, True])
+def test_twelve_wave_workgroups(fa, d, causal):
+    """64 query heads over 8 K/V heads, N = 4100: a grid large enough for the
+    d <= 64 forward's 12-wave (384-row) workgroups, which the launch geometry
+    confirms; every row against the oracle, ragged last q-tile and key tile."""
+    g = fa.fwd_geometry(1, 64, 8, 4100, d, causal)
+    assert g["threads"] == 768 and g["block_m"] == 384, g
+    inp = ai.make_case(1, 64, 8, 4100, d, seed=4100 + d + int(causal), with_grad=False)
+    check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"12 waves d={d} causal={causal}")

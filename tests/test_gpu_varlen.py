@@ -239,3 +239,37 @@ def test_wide_headdim_bwd(fa, causal):
     """d = 256 packed sequences: the split gradient kernels with sequence bounds."""
     inp = make_grad_case([1, 17, 256, 257, 700], 4, 2, 256, seed=8000 + int(causal))
     check_bwd(fa, inp, 0.0625, "wide d=256", causal=causal)
+
+
+def test_twelve_wave_workgroups(fa):
+    """Packed sequences of up to 4100 rows with 64 query heads: the d = 64
+    forward takes 12-wave workgroups (the launch geometry for B sequences of the
+    longest length confirms it); 128 seeded rows per sequence against the
+    oracle."""
+    lens = [4100, 1, 3000, 2500, 0, 777]
+    g = fa.fwd_geometry(len(lens), 64, 8, max(lens), 64, True)
+    assert g["threads"] == 768, g
+    for causal in (True, False):
+        inp = ai.make_varlen_case(lens, 64, 8, 64, seed=12 + int(causal))
+        check(fa, inp, causal, 0.125, f"12 waves causal={causal}", rows_per_seq=128)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_equal_lengths_match_fixed_twelve_waves(fa, causal):
+    """As test_equal_lengths_match_fixed, at a size where both calls take the
+    d = 64 forward's 12-wave workgroups: bit-identical results."""
+    import torch
+    B, Hq, Hkv, N, d = 2, 64, 8, 2100, 64
+    assert fa.fwd_geometry(B, Hq, Hkv, N, d, causal)["threads"] == 768
+    inp = ai.make_varlen_case([N] * B, Hq, Hkv, d, seed=9 + int(causal))
+    say(f"varlen equal lengths vs fixed, 12 waves, causal={causal}")
+    o_v, l_v = run_varlen(fa, inp, causal, 0.125)
+
+    def fixed(x, H):
+        return np.ascontiguousarray(x.reshape(H, B, N, d).transpose(1, 0, 2, 3))
+    q, k, v = to_dev(fixed(inp["q"], Hq)), to_dev(fixed(inp["k"], Hkv)), to_dev(fixed(inp["v"], Hkv))
+    o_f, l_f = fa.fwd(q, k, v, causal=causal, scale=0.125)
+    torch.cuda.synchronize()
+    o_f = from_dev_bf16(o_f).transpose(1, 0, 2, 3).reshape(Hq, B * N, d)
+    l_f = from_dev_f32(l_f).transpose(1, 0, 2).reshape(Hq, B * N)
+    assert np.array_equal(o_v, o_f) and np.array_equal(l_v, l_f)

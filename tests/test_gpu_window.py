@@ -199,3 +199,13 @@ def test_wide_headdim_bwd(fa, N, W):
     """d = 256 with a window: the split gradient kernels with a bounded mask."""
     inp = ai.make_case(1, 4, 2, N, 256, seed=7900 + N + W)
     check_bwd(fa, inp, W, 0.0625, "wide d=256")
+
+
+@pytest.mark.parametrize("W", [33, 1000])
+def test_twelve_wave_workgroups(fa, W):
+    """A grid large enough for the d = 64 forward's 12-wave (384-row)
+    workgroups (the launch geometry confirms it), every row against the oracle."""
+    g = fa.fwd_geometry(1, 64, 8, 4100, 64, True)
+    assert g["threads"] == 768, g
+    inp = ai.make_case(1, 64, 8, 4100, 64, seed=41 + W, with_grad=False)
+    check(fa, inp, W, 0.125, f"12 waves W={W}")
