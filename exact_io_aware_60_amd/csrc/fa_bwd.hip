@@ -822,8 +822,13 @@ struct QCfg {
     static constexpr int DS = D / 16, DB = D / 32;
     static constexpr int SR = RowPad<D>::STRIDE;      // K, V rows: [64][D], padded rows
     static constexpr int RT = padded_tile_bytes<SR, kQ_N>();
-    static constexpr int ST = RowPad<kQ_N>::STRIDE;   // K^T: [D][64], padded rows
-    static constexpr int TT = padded_tile_bytes<ST, D>();
+    // K^T: [D][64]. d = 64: dense 128-byte rows, XOR-swizzled as the dK/dV
+    // kernel's transposed tiles, so that three stages (78 KiB) leave room for
+    // a second workgroup per CU (two waves per SIMD; the kernel needs at most
+    // 256 registers there). d = 128: padded rows (below).
+    static constexpr bool TSWZ = D == 64;
+    static constexpr int ST = RowPad<kQ_N>::STRIDE;
+    static constexpr int TT = TSWZ ? D * 2 * kQ_N : padded_tile_bytes<ST, D>();
     static constexpr int KR = 0, VR = RT, KT = 2 * RT;
     static constexpr int STAGE = 2 * RT + TT;
     static constexpr int LDS = 3 * STAGE;             // tiles j-1 (K^T), j, j+1
@@ -837,12 +842,14 @@ struct QCfg {
     // tile's first slots. Each group of 16 starts after its inputs are complete
     // and ends before the product that consumes it.
     static constexpr int START = 3 * DS + 1;
-    // K^T keeps padded rows here: swizzled ones, which copy no pad bytes and no
-    // duplicate blocks, measured slower in this kernel.
+    // At d = 128 K^T keeps padded rows: swizzled ones, which copy no pad bytes
+    // and no duplicate blocks, measured slower in this kernel.
     using PlanR = CopyPlan<D, SR, kQ_N, 4>;
-    using PlanT = CopyPlan<kQ_N, ST, D, 4>;
-    using Addr = LaneAddr<SR, PadRows<ST>>;
-    static_assert(LDS <= 160 * 1024, "LDS budget");
+    using PlanT = std::conditional_t<TSWZ, CopyPlanSwz<2 * kQ_N, D, 4>, CopyPlan<kQ_N, ST, D, 4>>;
+    using Addr = LaneAddr<SR, std::conditional_t<TSWZ, Swz128, PadRows<ST>>>;
+    static constexpr int PER_CU = TSWZ ? 2 : 1;       // workgroups per CU
+    static_assert(LDS * PER_CU <= 160 * 1024, "LDS budget");
+    static_assert(!TSWZ || (KT % 128 == 0 && STAGE % 128 == 0), "swizzled tiles start on 128 bytes");
 };
 
 // First softmax task of linear slot x (x counts from the tile's slot 0 and
@@ -1098,7 +1105,7 @@ __device__ __forceinline__ void dq_iteration(QState<D>& S, const typename QCfg<D
 }
 
 template <int D, bool WIN>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, QCfg<D>::PER_CU) void bwd_dq_kernel(BwdParams p) {
     using C = QCfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
