@@ -40,9 +40,11 @@
  * work on `stream` and return at once; results are valid once the stream has
  * been synchronised. The library never allocates, frees or synchronises, keeps
  * no pointer after a call returns, and holds no mutable global state apart
- * from the per-GPU address cache of flash_attn_decode_noalloc's static scratch
- * (set once per GPU under a once-flag), so calls from several host threads are
- * safe (flash_attn_decode_noalloc: see its sharing rule). Calls on one stream run in order; the
+ * from two per-GPU caches: the address of flash_attn_decode_noalloc's static
+ * scratch (set once per GPU under a once-flag) and the compute-unit count the
+ * forward's launch shape depends on (read once per GPU, atomically). Calls
+ * from several host threads are therefore safe (flash_attn_decode_noalloc:
+ * see its sharing rule). Calls on one stream run in order; the
  * caller orders calls on different streams that share buffers.
  *
  * Errors. Every entry point returns FA_OK (0) or a negative status and never
