@@ -258,3 +258,25 @@ def test_twelve_wave_workgroups(fa, d, causal):
     assert g["threads"] == 768 and g["block_m"] == 384, g
     inp = ai.make_case(1, 64, 8, 4100, d, seed=4100 + d + int(causal), with_grad=False)
     check_full(fa, inp, causal, 1.0 / math.sqrt(d), f"12 waves d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 48])
+def test_launch_shape_does_not_change_results(fa, d):
+    """Both launch shapes of the d <= 64 forward group rows into the same
+    32-row waves and walk the same chunks, so a 64-head call (12-wave
+    workgroups) and eight calls of 8 heads each (8-wave workgroups) give the
+    same bits."""
+    import torch
+    B, Hq, Hkv, N = 1, 64, 8, 4100
+    assert fa.fwd_geometry(B, Hq, Hkv, N, d, True)["threads"] == 768
+    assert fa.fwd_geometry(B, Hq // Hkv, 1, N, d, True)["threads"] == 512
+    inp = ai.make_case(B, Hq, Hkv, N, d, seed=4242 + d, with_grad=False)
+    say(f"fwd launch shapes d={d}")
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = fa.fwd(q, k, v, causal=True, scale=0.125)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        qs = q[:, g * G:(g + 1) * G].contiguous()
+        o_g, lse_g = fa.fwd(qs, k[:, g:g + 1].contiguous(), v[:, g:g + 1].contiguous(), causal=True, scale=0.125)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o[:, g * G:(g + 1) * G]) and torch.equal(lse_g, lse[:, g * G:(g + 1) * G]), g
