@@ -474,7 +474,14 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
     static_assert(SP >= 1 && 1 + (NITEM - 1) * SP < NS, "copy items fit the slots");
     f32x16 s[2], dp[2];
     u32x4 pp[4], dsp[4];
-    f32x4 lv[2][4], dv4[2][4];
+    // LSE (P tasks) or D (dS tasks) of task group g = t / 4, loaded one group
+    // ahead into lb[g % 2]. (Loading a half's 16 values at once kept up to 48
+    // of them live and pushed 51 more registers into AGPRs: 0.6% slower.)
+    f32x4 lb[2];
+    auto lse_d = [&](auto gc) {
+        constexpr int g = decltype(gc)::value, grp = g / 4, h = grp >> 1, u = g % 4;
+        lb[g % 2] = *reinterpret_cast<const FA_LDS f32x4*>(st + ((grp & 1) ? C::DD : C::L2) + lbase + h * 128 + u * 32);
+    };
     u32x4 ring[PF + 1];
     // Transposed operands: chunk pair qc of d rows db*32 + l32 lies at
     // ((st + b0) ^ (qc << 5)) + tile + db*32*128. The address of pair qc is
@@ -524,9 +531,10 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
     auto task = [&](auto tc) {
         constexpr int t = decltype(tc)::value;
         constexpr int grp = t / 16, i = t % 16, h = grp >> 1;
-        constexpr int u = i / 4, e = i % 4, qc = 2 * h + i / 8, w = (i % 8) / 2;
+        constexpr int e = i % 4, qc = 2 * h + i / 8, w = (i % 8) / 2, g = t / 4;
+        if constexpr (e == 0 && g + 1 < 16) lse_d(std::integral_constant<int, g + 1>{});
         if constexpr ((grp & 1) == 0) {
-            const float x = fast_exp2(fmaf(s[h][i], sl2, -lv[h][u][e]));
+            const float x = fast_exp2(fmaf(s[h][i], sl2, -lb[g % 2][e]));
             s[h][i] = x;
             if constexpr (i & 1) {
                 uint32_t v = pack_f16(s[h][i - 1], x);
@@ -536,7 +544,7 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
         } else {
             // dS = P (dP c1 - D): the difference in fp32, the product of the fp16
             // pair with the P pair already packed for the dV MFMA (v_pk_mul_f16)
-            const float t = fmaf(dp[h][i], c1, -dv4[h][u][e]);
+            const float t = fmaf(dp[h][i], c1, -lb[g % 2][e]);
             dp[h][i] = t;
             if constexpr (i & 1) {
                 uint32_t v = mul_f16x2(pp[qc][w], pack_f16(dp[h][i - 1], t));
@@ -547,21 +555,11 @@ __device__ __forceinline__ void kv_step(const FA_LDS uint8_t* __restrict__ st, K
     };
 
     static_for<PF>([&](auto nc) { ring[decltype(nc)::value] = frag(nc); });
+    lse_d(std::integral_constant<int, 0>{});
     static_for<NS>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
         mfma_at(nc, ring[n % (PF + 1)]);
         if constexpr (n + PF < NS) ring[(n + PF) % (PF + 1)] = frag(std::integral_constant<int, n + PF>{});
-        if constexpr (n % DS == 0 && n < 4 * DS) {
-            // LSE of a half before its P tasks, D before its dS tasks
-            constexpr int ph = n / DS, h = ph >> 1;
-            const FA_LDS uint8_t* src = st + ((ph & 1) ? C::DD : C::L2) + lbase + h * 32 * 4;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const f32x4 x = *reinterpret_cast<const FA_LDS f32x4*>(src + u * 32);
-                if constexpr (ph & 1) dv4[h][u] = x;
-                else lv[h][u] = x;
-            }
-        }
         if constexpr (COPY && n >= 1 && (n - 1) % SP == 0 && (n - 1) / SP < NITEM)
             kv_copy_item<D, (n - 1) / SP>(*nx, wst);
         constexpr int t0 = kv_task_begin<D>(n), t1 = kv_task_begin<D>(n + 1);
