@@ -36,10 +36,10 @@
 //    times P^T, one MFMA per 64 keys, divided by the tile's V scale ratio): the
 //    weights then sum to one as used, and a dominant probability's rounding
 //    cancels. The logsumexp takes the fp32 sum.
-//  * The reference max follows the bf16 forward's rule: the first tile's exact
-//    max, then a new exact max only when some lane's sum of its 32
-//    probabilities (times the V ratio) passes 2^8, so every E4M3 value stays
-//    at most 2^8 (the format's largest is 448).
+//  * The reference max follows the bf16 forward's rule with a tighter bound:
+//    the first tile's exact max, then a new exact max only when some lane's
+//    sum of its 32 probabilities (times the V ratio) passes 2^8, so every
+//    E4M3 value stays at most 2^8 (the format's largest is 448).
 //  * 12 waves of 32 query rows, three per SIMD (at most 168 registers each):
 //    the kernel is bound by vector-ALU issue, and a third wave per SIMD
 //    hides more of it under the matrix instructions than two (measured on

@@ -347,9 +347,10 @@ def pin_online_recurrence(orc):
             om, lm = online_attention(q[0, 0], k[0, 0], v[0, 0], causal, 0.6, br, bc, tau)
             _close(om, o[0, 0], what=f"online O ({br}x{bc}, tau={tau:.2f})")
             _close(lm, lse[0, 0], what=f"online LSE ({br}x{bc}, tau={tau:.2f})")
-        # the sum-triggered reference: tight (moves often), the kernel's 2^8, and
-        # loose enough that it never moves after the first block
-        for br, bc, smax in ((4, 3, 1.5), (32, 32, 256.0), (6, 5, 1e30)):
+        # the sum-triggered reference: tight (moves often), the FP8 forward's 2^8,
+        # the bf16 forward's 2^16, and loose enough that it never moves after the
+        # first block
+        for br, bc, smax in ((4, 3, 1.5), (32, 32, 256.0), (32, 32, 65536.0), (6, 5, 1e30)):
             om, lm = online_attention(q[0, 0], k[0, 0], v[0, 0], causal, 0.6, br, bc, sum_max=smax)
             _close(om, o[0, 0], what=f"online O ({br}x{bc}, sum_max={smax:g})")
             _close(lm, lse[0, 0], what=f"online LSE ({br}x{bc}, sum_max={smax:g})")
