@@ -24,6 +24,15 @@
 //    correction exp2(m_old - m_new) is applied to O and the sum at every tile.
 //  * Causal: tiles past a wave's last row are skipped; the diagonal and the
 //    ragged last tile are masked.
+//  * Several workgroups per CU (34 KiB of LDS each at d = 128, 17 KiB at
+//    d = 64): the launch bounds ask for two at d = 128 (192 registers, two
+//    waves per SIMD) and three at d = 64 (122 registers, which lets four run).
+//    Each wave's score and P.V products are chains of dependent fp32 MFMAs,
+//    so more waves per SIMD hide their latency. Measured on MI355X against one
+//    workgroup per CU (286 registers at d = 128): 61.1 -> 46.0 ms on a
+//    2 x 32-head, 16384-row causal forward, 0.613 -> 0.563 ms on 4 x 16 heads
+//    of 2048 rows at d = 64, same results bit for bit. Three per CU at
+//    d = 128 spills (168 registers): 49.3 ms.
 // Head dimensions: any multiple of 8 up to 128 (zero columns past d).
 #include "fa_device.h"
 #include "fa_params.h"
@@ -54,7 +63,7 @@ __device__ __forceinline__ f32x16 mfma_f32(float a, float b, const f32x16& c) {
 __device__ __forceinline__ int key_of(int r, int hh) { return (r >> 2) * 8 + hh * 4 + (r & 3); }
 
 template <int D>
-__global__ __launch_bounds__(k32Threads, 1) void fwd32_kernel(Fwd32Params p) {
+__global__ __launch_bounds__(k32Threads, D == 64 ? 3 : 2) void fwd32_kernel(Fwd32Params p) {
     using C = F32Cfg<D>;
     __shared__ float Kt[C::KT];
     __shared__ __attribute__((aligned(16))) float Vs[C::VT];
