@@ -280,3 +280,22 @@ def test_launch_shape_does_not_change_results(fa, d):
         o_g, lse_g = fa.fwd(qs, k[:, g:g + 1].contiguous(), v[:, g:g + 1].contiguous(), causal=True, scale=0.125)
         torch.cuda.synchronize()
         assert torch.equal(o_g, o[:, g * G:(g + 1) * G]) and torch.equal(lse_g, lse[:, g * G:(g + 1) * G]), g
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_value_scale_homogeneity(fa, d):
+    """O is homogeneous in V and the forward's arithmetic on V is exact scaling
+    by powers of two (products, sums and the final division), so V * 2^e gives
+    O * 2^e bit for bit and the same LSE, as long as nothing overflows or
+    underflows. e = +-60 with spread scores (the reference moves, and P stays
+    up to 2^16 between moves) checks the accumulators' range at both ends."""
+    import torch
+    inp = ai.make_case(1, 4, 2, 900, d, seed=31 + d, with_grad=False, dist_scale=2.0)
+    s = 0.2 * math.sqrt(128 / d)
+    say(f"fwd value-scale homogeneity d={d}")
+    o, lse = run_fwd(fa, inp, True, s)
+    for e in (60, -60):
+        v = torch.from_numpy(f64(inp["v"]) * 2.0 ** e).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        o2, lse2 = run_fwd(fa, dict(inp, v=v), True, s)
+        assert np.array_equal(o2, o * 2.0 ** e), e
+        assert np.array_equal(lse2, lse), e
