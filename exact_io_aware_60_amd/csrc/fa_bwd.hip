@@ -810,6 +810,392 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------- dK / dV, eight waves
+// The d = 128 form without a bounded mask. A workgroup owns 256 keys, 32 per
+// wave, with two waves per SIMD, and each step streams 32 query rows. Every
+// byte a step copies then serves twice as many keys as in the four-wave form,
+// so each MFMA costs half as many copy instructions, and a SIMD has a second
+// wave to issue from while one waits on a copy, an LDS read or its softmax
+// work. Two waves per SIMD allow at most 256 registers each, which the dK and
+// dV accumulators (128), the K operand (32) and one step's S, dP and packed P
+// and dS leave room for only if V is not also held in registers: it sits in
+// LDS (the workgroup's 256 rows, 68 KiB) and is read as the dP product's B
+// operand, one more 16-byte read per dP MFMA.
+constexpr int kKV8_WG = 256;     // keys per workgroup
+constexpr int kKV8_Q = 32;       // query rows per step
+constexpr int kThreads8 = 512;   // 8 waves, two per SIMD
+
+// Transposed [D x 32] tiles have 64-byte rows: 16-byte chunk c of row r sits
+// at chunk position c ^ ((r >> 2) & 3). The 16 rows that 16 lanes read at one
+// logical chunk then fill the 16 bank groups of a 256-byte line.
+struct Key64 {
+    __host__ __device__ static constexpr int key(int r) { return (r >> 2) & 3; }
+};
+
+template <int D>
+struct Kv8Cfg {
+    static constexpr int DS = D / 16, DB = D / 32;
+    static constexpr int SR = RowPad<D>::STRIDE;             // Q, dO and V rows: padded
+    static constexpr int RT = padded_tile_bytes<SR, kKV8_Q>();
+    static constexpr int TL = 2 * kKV8_Q;                    // bytes per transposed row
+    static constexpr int TT = D * TL;
+    static constexpr int QR = 0, DOR = RT, QT = 2 * RT, DOT = 2 * RT + TT;
+    static constexpr int L2 = 2 * RT + 2 * TT, DD = L2 + 256;   // 64 floats each (one 64-lane load)
+    static constexpr int STAGE = DD + 256;
+    static constexpr int VR = 2 * STAGE;                     // V rows of the workgroup's keys
+    static constexpr int LDS = VR + kKV8_WG * SR;
+    // MFMA slots of a step, DS each, in order: S = Q K^T, dP = dO V^T, then
+    // dV^T += dO^T P and dK^T += Q^T dS over the two 16-row chunks.
+    static constexpr int NS = 4 * DS;
+    // The 16 P tasks run over PSPAN slots from two slots after S is complete,
+    // the 16 dS tasks over DSPAN slots after the last P task: the tasks keep
+    // one order, which the one-group-ahead LSE / D loads rely on. P of rows
+    // 0-15 is done before the first dV slot, dS of rows 0-15 before the first
+    // dK slot.
+    static constexpr int PSTART = DS + 1, PSPAN = 10, DSTART = PSTART + PSPAN, DSPAN = 9;
+    using PlanR = CopyPlan<D, SR, kKV8_Q, 8>;
+    using PlanT = CopyPlanSwz<TL, D, 8, Key64>;
+    static_assert(D == 128, "the eight-wave form is built for d = 128");
+    static_assert(PlanR::NB == 9 && PlanR::NT == 2, "a row tile is 8 blocks of 1 KiB and a ninth, partial one");
+    static_assert(PlanT::NT == 1, "one transposed block per wave");
+    static_assert(2 * DB == DS, "the dV and dK products take DS slots each");
+    // P of rows 0-15 (tasks 0-7) ends before slot 2 DS (dV, chunk 0), of rows
+    // 16-31 before 2 DS + DB (chunk 1); dS likewise before 3 DS and 3 DS + DB.
+    static_assert(PSTART + (7 * PSPAN + 15) / 16 < 2 * DS && PSTART + PSPAN <= 2 * DS + DB, "P before dV");
+    static_assert(DSTART + (7 * DSPAN + 15) / 16 < 3 * DS && DSTART + DSPAN <= 3 * DS + DB, "dS before dK");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// First of 16 tasks spread over `span` slots from slot `start` that slot n runs.
+__host__ __device__ constexpr int kv8_task_begin(int n, int start, int span) {
+    const int t = (n - start) * 16 / span;
+    return t < 0 ? 0 : (t > 16 ? 16 : t);
+}
+
+template <int D>
+struct Kv8State {
+    u32x4 kf[D / 16];                 // K as the B operand: lane holds key l32, d = ds*16 + hh*8 .. +7
+    f32x16 dk[D / 32], dv[D / 32];    // dK^T, dV^T: lane holds key l32, d rows db*32 + (i/4)*8 + hh*4 + i%4
+};
+
+// Per-lane byte offsets: row(ds) in a row tile (row l32 of the step, d =
+// ds*16 + hh*8), tb[qc] in a transposed tile (d row l32 of a 32-row block,
+// rows qc*16 + hh*8 .. +7 of the step), V rows from vt.
+struct Kv8Addr {
+    int rbase;    // l32 * SR + hh * 16
+    int tb[2];
+    int lbase;    // hh * 16: this lane half's rows in the LSE / D arrays
+    __device__ __forceinline__ void init(int l32, int hh, int sr) {
+        rbase = l32 * sr + hh * 16;
+        const int key = Key64::key(l32);
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) tb[qc] = l32 * 64 + (((2 * qc + hh) ^ key) << 4);
+        lbase = hh * 16;
+    }
+};
+
+template <int D>
+struct Kv8Next {
+    const typename Kv8Cfg<D>::PlanR& pr;
+    const typename Kv8Cfg<D>::PlanT& pt;
+    const KvRes& rs;
+    KvSrc x;
+    int ws;     // wave index (scalar)
+    int lane;
+};
+
+// Copy item c of a step for wave ws: 0 its block of the Q rows, 1 of the dO
+// rows, 2 of Q^T, 3 of dO^T; 4 the rest, one item each for waves 0-3: the
+// last (partial) block of the Q rows, of the dO rows, the LSE and the D rows.
+template <int D, int c>
+__device__ __forceinline__ void kv8_copy_item(const Kv8Next<D>& nx, FA_LDS uint8_t* __restrict__ st) {
+    using C = Kv8Cfg<D>;
+    if constexpr (c == 0) nx.pr.copy_one(0, nx.rs.q, nx.x.rows, st + C::QR, nx.ws);
+    else if constexpr (c == 1) nx.pr.copy_one(0, nx.rs.dout, nx.x.rows, st + C::DOR, nx.ws);
+    else if constexpr (c == 2) nx.pt.copy_one(0, nx.rs.qt, nx.x.tr, st + C::QT, nx.ws);
+    else if constexpr (c == 3) nx.pt.copy_one(0, nx.rs.dot, nx.x.tr, st + C::DOT, nx.ws);
+    else {
+        if (nx.ws == 0) nx.pr.copy_one(1, nx.rs.q, nx.x.rows, st + C::QR, nx.ws);
+        else if (nx.ws == 1) nx.pr.copy_one(1, nx.rs.dout, nx.x.rows, st + C::DOR, nx.ws);
+        else if (nx.ws == 2) bload_lds4(nx.rs.l2, nx.lane * 4, nx.x.row4, st + C::L2);
+        else if (nx.ws == 3) bload_lds4(nx.rs.dd, nx.lane * 4, nx.x.row4, st + C::DD);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void kv8_copy(const Kv8Next<D>& nx, FA_LDS uint8_t* __restrict__ st) {
+    static_for<5>([&](auto c) { kv8_copy_item<D, decltype(c)::value>(nx, st); });
+}
+
+// One unmasked step, interleaved by hand: slot n issues its MFMA, starts the
+// LDS reads of slot n + 3's operands and runs its share of the softmax tasks;
+// a scheduling barrier closes every slot. With COPY, the next step's copy
+// items go out one every SP slots.
+template <int D, bool COPY>
+__device__ __forceinline__ void kv8_step(const FA_LDS uint8_t* __restrict__ st, Kv8State<D>& S, const Kv8Addr& la,
+                                         const FA_LDS uint8_t* __restrict__ vt, float sl2, float c1,
+                                         const Kv8Next<D>* nx, FA_LDS uint8_t* __restrict__ wst) {
+    using C = Kv8Cfg<D>;
+    constexpr int DS = C::DS, DB = C::DB, NS = C::NS, PF = 3, NITEM = 5, SP = NS / (NITEM + 1);
+    static_assert(SP >= 1 && 1 + (NITEM - 1) * SP < NS, "copy items fit the slots");
+    f32x16 s, dp;
+    u32x4 pp[2], dsp[2];
+    f32x4 lb[2];
+    // LSE (groups 0-3, P tasks) or D (groups 4-7, dS tasks) of task group g,
+    // rows u*8 + hh*4 + 0..3 with u = g % 4, loaded one group ahead.
+    auto lse_d = [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        lb[g % 2] = *reinterpret_cast<const FA_LDS f32x4*>(st + (g >= 4 ? C::DD : C::L2) + la.lbase + (g % 4) * 32);
+    };
+    u32x4 ra[PF + 1], rb[PF + 1];
+    auto frag = [&](auto nc) {
+        constexpr int n = decltype(nc)::value, r = n % (PF + 1);
+        if constexpr (n < DS) {
+            ra[r] = lds_read16b(st, la.rbase + C::QR + n * 32);
+        } else if constexpr (n < 2 * DS) {
+            ra[r] = lds_read16b(st, la.rbase + C::DOR + (n - DS) * 32);
+            rb[r] = lds_read16b(vt, (n - DS) * 32);
+        } else {
+            constexpr int m = n - 2 * DS, grp = m / (2 * DB), qc = (m % (2 * DB)) / DB, db = m % DB;
+            ra[r] = lds_read16b(st + la.tb[qc], (grp ? C::QT : C::DOT) + db * 32 * C::TL);
+        }
+    };
+    auto mfma_at = [&](auto nc) {
+        constexpr int n = decltype(nc)::value, r = n % (PF + 1);
+        if constexpr (n < DS) {
+            s = mfma32h(ra[r], S.kf[n], n == 0 ? zero16() : s);
+        } else if constexpr (n < 2 * DS) {
+            dp = mfma32h(ra[r], rb[r], n == DS ? zero16() : dp);
+        } else {
+            constexpr int m = n - 2 * DS, grp = m / (2 * DB), qc = (m % (2 * DB)) / DB, db = m % DB;
+            if constexpr (grp == 0)
+                S.dv[db] = mfma32h(ra[r], pp[qc], S.dv[db]);
+            else
+                S.dk[db] = mfma32h(ra[r], dsp[qc], S.dk[db]);
+        }
+    };
+    // Task t < 16: P of register i = t (row (i/4)*8 + hh*4 + i%4), P =
+    // exp2(S' sl2 - LSE log2 e); task 16 + i: dS 2^sS = P (dP' c1 - D 2^sS),
+    // the difference in fp32, the product with the packed fp16 P pair. Register
+    // pair (2w, 2w+1) of 16-row chunk qc = i / 8 is k-slot pair w of the
+    // chunk's B operand.
+    auto task = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int i = t % 16, e = i % 4, qc = i / 8, wp = (i % 8) / 2, g = t / 4;
+        if constexpr (e == 0 && g + 1 < 8) lse_d(std::integral_constant<int, g + 1>{});
+        if constexpr (t < 16) {
+            const float x = fast_exp2(fmaf(s[i], sl2, -lb[g % 2][e]));
+            s[i] = x;
+            if constexpr (i & 1) {
+                uint32_t v = pack_f16(s[i - 1], x);
+                pin(v);
+                pp[qc][wp] = v;
+            }
+        } else {
+            const float y = fmaf(dp[i], c1, -lb[g % 2][e]);
+            dp[i] = y;
+            if constexpr (i & 1) {
+                uint32_t v = mul_f16x2(pp[qc][wp], pack_f16(dp[i - 1], y));
+                pin(v);
+                dsp[qc][wp] = v;
+            }
+        }
+    };
+
+    static_for<PF>([&](auto nc) { frag(nc); });
+    lse_d(std::integral_constant<int, 0>{});
+    static_for<NS>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        mfma_at(nc);
+        if constexpr (n + PF < NS) frag(std::integral_constant<int, n + PF>{});
+        if constexpr (COPY && n >= 1 && (n - 1) % SP == 0 && (n - 1) / SP < NITEM)
+            kv8_copy_item<D, (n - 1) / SP>(*nx, wst);
+        constexpr int p0 = kv8_task_begin(n, C::PSTART, C::PSPAN), p1 = kv8_task_begin(n + 1, C::PSTART, C::PSPAN);
+        static_for<p1 - p0>([&](auto k) { task(std::integral_constant<int, p0 + decltype(k)::value>{}); });
+        constexpr int d0 = kv8_task_begin(n, C::DSTART, C::DSPAN), d1 = kv8_task_begin(n + 1, C::DSTART, C::DSPAN);
+        static_for<d1 - d0>([&](auto k) { task(std::integral_constant<int, 16 + d0 + decltype(k)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// The step on a wave's causal diagonal: keys above a row get P = 0. Unpipelined;
+// one per head and wave.
+template <int D>
+__device__ __forceinline__ void kv8_step_masked(const FA_LDS uint8_t* __restrict__ st, Kv8State<D>& S,
+                                                const Kv8Addr& la, const FA_LDS uint8_t* __restrict__ vt, int q0,
+                                                int key, float sl2, float c1, int hh) {
+    using C = Kv8Cfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+        s = mfma32h(lds_read16b(st, la.rbase + C::QR + ds * 32), S.kf[ds], s);
+        dp = mfma32h(lds_read16b(st, la.rbase + C::DOR + ds * 32), lds_read16b(vt, ds * 32), dp);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const f32x4 lv = *reinterpret_cast<const FA_LDS f32x4*>(st + C::L2 + la.lbase + u * 32);
+        const f32x4 dv4 = *reinterpret_cast<const FA_LDS f32x4*>(st + C::DD + la.lbase + u * 32);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = u * 4 + e;
+            const int q = q0 + u * 8 + hh * 4 + e;
+            float x = fast_exp2(fmaf(s[i], sl2, -lv[e]));
+            if (key > q) x = 0.f;
+            s[i] = x;
+            dp[i] = x * fmaf(dp[i], c1, -dv4[e]);
+        }
+    }
+    u32x4 pp[2], dsp[2];
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int i = qc * 8 + 2 * w;
+            pp[qc][w] = pack_f16(s[i], s[i + 1]);
+            dsp[qc][w] = pack_f16(dp[i], dp[i + 1]);
+        }
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const FA_LDS uint8_t* a = st + la.tb[qc] + db * 32 * C::TL;
+            S.dv[db] = mfma32h(lds_read16b(a, C::DOT), pp[qc], S.dv[db]);
+            S.dk[db] = mfma32h(lds_read16b(a, C::QT), dsp[qc], S.dk[db]);
+        }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads8, 1) void bwd_dkdv8_kernel(BwdParams p) {
+    using C = Kv8Cfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int N = p.N, Np = p.Np, G = p.G;
+    const bool causal = p.causal != 0;
+    int kt, bkv;
+    // kt = 0 first: the most query rows when causal
+    unmap_block_unit_major(blockIdx.x, p.B * p.Hkv, (N + kKV8_WG - 1) / kKV8_WG, kt, bkv);
+    const int k0 = kt * kKV8_WG;
+    const int kw0 = k0 + w * kKV_W;
+    const int key = kw0 + l32;
+    // Np is a multiple of 128 and kw0 of 32, so a wave's 32 keys lie all
+    // below Np or all at or past it; past it there are no copies to read
+    // (zero operands instead; such keys are never stored).
+    const bool has_keys = kw0 < Np;
+    const float sl2 = p.scales[0], c1 = p.scales[1];
+
+    Kv8State<D> S;
+    {
+        const size_t row = (size_t)bkv * Np + (has_keys ? key : 0);
+        const uint16_t* Kg = p.k16 + row * D;
+        const uint16_t* Vg = p.v16 + row * D;
+        FA_LDS uint8_t* vrow = (FA_LDS uint8_t*)smem + C::VR + (w * kKV_W + l32) * C::SR + hh * 16;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            S.kf[ds] = gload16(Kg + ds * 16 + hh * 8, has_keys);
+            *reinterpret_cast<FA_LDS u32x4*>(vrow + ds * 32) = gload16(Vg + ds * 16 + hh * 8, has_keys);
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        S.dk[db] = zero16();
+        S.dv[db] = zero16();
+    }
+
+    // Steps: 32-row blocks from the last one down to qs, all G heads per block.
+    const int qs = causal ? k0 : 0;
+    const int nrb = (N - qs + kKV8_Q - 1) / kKV8_Q;
+    const int nsteps = G * nrb;
+    const int qtop = qs + (nrb - 1) * kKV8_Q;
+    KvRes rs;
+    {
+        const size_t bh0 = (size_t)(bkv / p.Hkv) * p.Hq + (size_t)(bkv % p.Hkv) * G;   // first query head
+        const uint32_t nrow = (uint32_t)G * Np;
+        rs.q = make_bufres(p.q16 + bh0 * Np * D, nrow * D * 2);
+        rs.dout = make_bufres(p.do16 + bh0 * Np * D, nrow * D * 2);
+        rs.qt = make_bufres(p.qT16 + bh0 * D * Np, nrow * D * 2);
+        rs.dot = make_bufres(p.doT16 + bh0 * D * Np, nrow * D * 2);
+        rs.l2 = make_bufres(p.lse2 + bh0 * Np, nrow * 4);
+        rs.dd = make_bufres(p.delta + bh0 * Np, nrow * 4);
+    }
+    auto src_of = [&](int j) {
+        const uint32_t g = j % G;
+        const uint32_t q0 = qtop - (j / G) * kKV8_Q;
+        KvSrc x;
+        x.rows = (g * Np + q0) * D * 2;
+        x.tr = g * D * Np * 2 + q0 * 2;
+        x.row4 = (g * Np + q0) * 4;
+        return x;
+    };
+    typename C::PlanR pr;
+    typename C::PlanT pt;
+    pr.init(w, lane, D);
+    pt.init(w, lane, Np);
+    Kv8Addr la;
+    la.init(l32, hh, C::SR);
+    FA_LDS uint8_t* st0 = (FA_LDS uint8_t*)smem;
+    const FA_LDS uint8_t* vt = st0 + C::VR + (w * kKV_W + l32) * C::SR + hh * 16;
+
+    kv8_copy<D>(Kv8Next<D>{pr, pt, rs, src_of(0), __builtin_amdgcn_readfirstlane(w), lane}, st0);
+    wait_vmem();
+    __syncthreads();
+    // Row blocks with q0 >= k0 + 256 (all but the last eight when causal) are
+    // unmasked for every wave and run on one code path, with the next step's
+    // copy spread over the MFMA slots. A wave whose keys lie past N runs them
+    // too (zero or padding keys, never stored).
+    const int nsteady = causal ? G * max(0, nrb - kKV8_WG / kKV8_Q) : nsteps - 1;
+    for (int j = 0; j < nsteady; ++j) {
+        const Kv8Next<D> nx{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane};
+        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
+        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
+        kv8_step<D, true>(rst, S, la, vt, sl2, c1, &nx, wst);
+        wait_vmem();
+        __syncthreads();
+    }
+    // The rest: each wave is idle (rows above its keys), on its diagonal, or
+    // unmasked.
+    for (int j = nsteady; j < nsteps; ++j) {
+        const int q0 = qtop - (j / G) * kKV8_Q;
+        const bool active = kw0 < N && (!causal || q0 + kKV8_Q - 1 >= kw0);
+        const int mode = !active ? 0 : ((causal && q0 < kw0 + kKV_W - 1) ? 2 : 1);
+        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
+        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
+        if (j + 1 < nsteps) kv8_copy<D>(Kv8Next<D>{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane}, wst);
+        if (mode == 1)
+            kv8_step<D, false>(rst, S, la, vt, sl2, c1, nullptr, nullptr);
+        else if (mode == 2)
+            kv8_step_masked<D>(rst, S, la, vt, q0, key, sl2, c1, hh);
+        wait_vmem();
+        __syncthreads();
+    }
+
+    // dK^T / dV^T blocks: lane holds key l32, d rows db*32 + u*8 + hh*4 + 0..3.
+    if (key < N) {
+        const int dr = p.d;
+        uint16_t* dKg = p.dk + ((size_t)bkv * N + key) * dr;
+        uint16_t* dVg = p.dv + ((size_t)bkv * N + key) * dr;
+        const float fk = p.scales[3], fv = p.scales[2];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                u32x2 a, c;
+                a[0] = pack_bf16(S.dk[db][u * 4 + 0] * fk, S.dk[db][u * 4 + 1] * fk);
+                a[1] = pack_bf16(S.dk[db][u * 4 + 2] * fk, S.dk[db][u * 4 + 3] * fk);
+                c[0] = pack_bf16(S.dv[db][u * 4 + 0] * fv, S.dv[db][u * 4 + 1] * fv);
+                c[1] = pack_bf16(S.dv[db][u * 4 + 2] * fv, S.dv[db][u * 4 + 3] * fv);
+                if (db * 32 + u * 8 + hh * 4 < dr) {
+                    *reinterpret_cast<u32x2*>(dKg + db * 32 + u * 8 + hh * 4) = a;
+                    *reinterpret_cast<u32x2*>(dVg + db * 32 + u * 8 + hh * 4) = c;
+                }
+            }
+    }
+}
+
 // ---------------------------------------------------------------- dQ
 constexpr int kQ_WG = 128;   // query rows per workgroup
 constexpr int kQ_W = 32;     // query rows per wave
@@ -1732,8 +2118,16 @@ hipError_t launch_prep_t(const BwdParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
+    const bool bounded = p.window > 0 || p.cu_seqlens;
+    if constexpr (D == 128) {
+        if (!bounded) {
+            const int grid8 = p.B * p.Hkv * ((p.N + kKV8_WG - 1) / kKV8_WG);
+            hipLaunchKernelGGL((bwd_dkdv8_kernel<D>), dim3(grid8), dim3(kThreads8), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     const int grid = p.B * p.Hkv * ((p.N + kKV_WG - 1) / kKV_WG);
-    if (p.window > 0 || p.cu_seqlens)
+    if (bounded)
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
