@@ -1640,6 +1640,325 @@ __global__ __launch_bounds__(kThreads, QCfg<D>::PER_CU) void bwd_dq_kernel(BwdPa
     }
 }
 
+// ---------------------------------------------------------------- dQ, eight waves
+// The d = 128 form without a bounded mask, built like the eight-wave dK/dV
+// kernel: a workgroup owns 256 query rows, 32 per wave, two waves per SIMD,
+// and each step streams a tile of 32 keys. Q stays in registers; dO, the
+// other row operand, sits in LDS (the workgroup's 256 rows) and is read as the
+// dP^T product's B operand. Each tile is complete within its step (S^T, dP^T,
+// then the PK^T and dQ^T products), so two stages suffice.
+constexpr int kQ8_WG = 256;    // query rows per workgroup
+constexpr int kQ8_N = 32;      // keys per tile
+
+template <int D>
+struct Q8Cfg {
+    static constexpr int DS = D / 16, DB = D / 32;
+    static constexpr int SR = RowPad<D>::STRIDE;             // K, V and dO rows: padded
+    static constexpr int RT = padded_tile_bytes<SR, kQ8_N>();
+    static constexpr int TL = 2 * kQ8_N;                     // bytes per K^T row
+    static constexpr int TT = D * TL;
+    static constexpr int KR = 0, VR = RT, KT = 2 * RT;
+    static constexpr int STAGE = 2 * RT + TT;
+    static constexpr int DOR = 2 * STAGE;                    // dO rows of the workgroup
+    static constexpr int LDS = DOR + kQ8_WG * SR;
+    // MFMA slots of a tile, DS each: S^T = K Q^T, dP^T = V dO^T, PK^T += K^T P^T
+    // and dQ^T += K^T dS^T over the two 16-key chunks. The 16 P tasks, then the
+    // 16 dS tasks, run as in the eight-wave dK/dV step.
+    static constexpr int NS = 4 * DS;
+    static constexpr int PSTART = DS + 1, PSPAN = 10, DSTART = PSTART + PSPAN, DSPAN = 9;
+    using PlanR = CopyPlan<D, SR, kQ8_N, 8>;
+    using PlanT = CopyPlanSwz<TL, D, 8, Key64>;
+    static_assert(D == 128, "the eight-wave form is built for d = 128");
+    static_assert(PlanR::NB == 9 && PlanR::NT == 2, "a row tile is 8 blocks of 1 KiB and a ninth, partial one");
+    static_assert(PlanT::NT == 1, "one transposed block per wave");
+    static_assert(2 * DB == DS, "the PK and dQ products take DS slots each");
+    static_assert(PSTART + (7 * PSPAN + 15) / 16 < 2 * DS && PSTART + PSPAN <= 2 * DS + DB, "P before PK");
+    static_assert(DSTART + (7 * DSPAN + 15) / 16 < 3 * DS && DSTART + DSPAN <= 3 * DS + DB, "dS before dQ");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int D>
+struct Q8State {
+    u32x4 qf[D / 16];                // Q as the B operand: lane holds row l32, d = ds*16 + hh*8 ..
+    f32x16 dq[D / 32], pk[D / 32];   // dQ^T, PK^T: lane holds row l32, d rows db*32 + (i/4)*8 + hh*4 + i%4
+    float l2, dd, dacc;              // LSE log2 e, D 2^sS, running sum of P dP'
+};
+
+template <int D>
+struct Q8Next {
+    const typename Q8Cfg<D>::PlanR& pr;
+    const typename Q8Cfg<D>::PlanT& pt;
+    BufRes rk, rv, rkt;
+    uint32_t rows, tr;   // byte offsets of the tile in the row / transposed copies
+    int ws;              // wave index (scalar)
+};
+
+// Copy item c of a tile for wave ws: 0 its block of the K rows, 1 of the V
+// rows, 2 of K^T; 3 the last (partial) block of the K rows (wave 0) or of the
+// V rows (wave 1).
+template <int D, int c>
+__device__ __forceinline__ void dq8_copy_item(const Q8Next<D>& nx, FA_LDS uint8_t* __restrict__ st) {
+    using C = Q8Cfg<D>;
+    if constexpr (c == 0) nx.pr.copy_one(0, nx.rk, nx.rows, st + C::KR, nx.ws);
+    else if constexpr (c == 1) nx.pr.copy_one(0, nx.rv, nx.rows, st + C::VR, nx.ws);
+    else if constexpr (c == 2) nx.pt.copy_one(0, nx.rkt, nx.tr, st + C::KT, nx.ws);
+    else {
+        if (nx.ws == 0) nx.pr.copy_one(1, nx.rk, nx.rows, st + C::KR, nx.ws);
+        else if (nx.ws == 1) nx.pr.copy_one(1, nx.rv, nx.rows, st + C::VR, nx.ws);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void dq8_copy(const Q8Next<D>& nx, FA_LDS uint8_t* __restrict__ st) {
+    static_for<4>([&](auto c) { dq8_copy_item<D, decltype(c)::value>(nx, st); });
+}
+
+// One unmasked tile, interleaved by hand as kv8_step: slot n issues its MFMA,
+// starts the LDS reads of slot n + 3's operands and runs its share of the
+// softmax tasks. With COPY, the next tile's copy items go out one every SP slots.
+template <int D, bool COPY>
+__device__ __forceinline__ void dq8_step(const FA_LDS uint8_t* __restrict__ st, Q8State<D>& S, const Kv8Addr& la,
+                                         const FA_LDS uint8_t* __restrict__ dot, float sl2, float c1,
+                                         const Q8Next<D>* nx, FA_LDS uint8_t* __restrict__ wst) {
+    using C = Q8Cfg<D>;
+    constexpr int DS = C::DS, DB = C::DB, NS = C::NS, PF = 2, NITEM = 4, SP = NS / (NITEM + 1);
+    static_assert(SP >= 1 && 1 + (NITEM - 1) * SP < NS, "copy items fit the slots");
+    f32x16 s, dp;
+    u32x4 pp[2], dsp[2];
+    u32x4 ra[PF + 1], rb[PF + 1];
+    auto frag = [&](auto nc) {
+        constexpr int n = decltype(nc)::value, r = n % (PF + 1);
+        if constexpr (n < DS) {
+            ra[r] = lds_read16b(st, la.rbase + C::KR + n * 32);
+        } else if constexpr (n < 2 * DS) {
+            ra[r] = lds_read16b(st, la.rbase + C::VR + (n - DS) * 32);
+            rb[r] = lds_read16b(dot, (n - DS) * 32);
+        } else {
+            constexpr int m = n - 2 * DS, kc = (m % (2 * DB)) / DB, db = m % DB;
+            ra[r] = lds_read16b(st + la.tb[kc], C::KT + db * 32 * C::TL);
+        }
+    };
+    auto mfma_at = [&](auto nc) {
+        constexpr int n = decltype(nc)::value, r = n % (PF + 1);
+        if constexpr (n < DS) {
+            s = mfma32h(ra[r], S.qf[n], n == 0 ? zero16() : s);
+        } else if constexpr (n < 2 * DS) {
+            dp = mfma32h(ra[r], rb[r], n == DS ? zero16() : dp);
+        } else {
+            constexpr int m = n - 2 * DS, grp = m / (2 * DB), kc = (m % (2 * DB)) / DB, db = m % DB;
+            if constexpr (grp == 0)
+                S.pk[db] = mfma32h(ra[r], pp[kc], S.pk[db]);
+            else
+                S.dq[db] = mfma32h(ra[r], dsp[kc], S.dq[db]);
+        }
+    };
+    // Task t < 16: P^T of register i = t (key (i/4)*8 + hh*4 + i%4 of the
+    // tile), P = exp2(S' sl2 - LSE log2 e); task 16 + i: the exact row dot's
+    // term P dP' and dS 2^sS = P (dP' c1 - D 2^sS), the difference in fp32, the
+    // product with the packed fp16 P pair. Register pair (2w, 2w+1) of 16-key
+    // chunk kc = i / 8 is k-slot pair w of the chunk's B operand.
+    auto task = [&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int i = t % 16, kc = i / 8, wp = (i % 8) / 2;
+        if constexpr (t < 16) {
+            const float x = fast_exp2(fmaf(s[i], sl2, -S.l2));
+            s[i] = x;
+            if constexpr (i & 1) {
+                uint32_t v = pack_f16(s[i - 1], x);
+                pin(v);
+                pp[kc][wp] = v;
+            }
+        } else {
+            const float dpv = dp[i];
+            S.dacc = fmaf(s[i], dpv, S.dacc);
+            const float y = fmaf(dpv, c1, -S.dd);
+            dp[i] = y;
+            if constexpr (i & 1) {
+                uint32_t v = mul_f16x2(pp[kc][wp], pack_f16(dp[i - 1], y));
+                pin(v);
+                dsp[kc][wp] = v;
+            }
+        }
+    };
+
+    static_for<PF>([&](auto nc) { frag(nc); });
+    static_for<NS>([&](auto nc) {
+        constexpr int n = decltype(nc)::value;
+        mfma_at(nc);
+        if constexpr (n + PF < NS) frag(std::integral_constant<int, n + PF>{});
+        if constexpr (COPY && n >= 1 && (n - 1) % SP == 0 && (n - 1) / SP < NITEM)
+            dq8_copy_item<D, (n - 1) / SP>(*nx, wst);
+        constexpr int p0 = kv8_task_begin(n, C::PSTART, C::PSPAN), p1 = kv8_task_begin(n + 1, C::PSTART, C::PSPAN);
+        static_for<p1 - p0>([&](auto k) { task(std::integral_constant<int, p0 + decltype(k)::value>{}); });
+        constexpr int d0 = kv8_task_begin(n, C::DSTART, C::DSPAN), d1 = kv8_task_begin(n + 1, C::DSTART, C::DSPAN);
+        static_for<d1 - d0>([&](auto k) { task(std::integral_constant<int, 16 + d0 + decltype(k)::value>{}); });
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// A tile with masked entries (the causal diagonal or keys >= N), unpipelined.
+// Keys past N are zero rows in the copies but would still get P =
+// exp2(-LSE), so they are masked like the ones above the diagonal.
+template <int D>
+__device__ __forceinline__ void dq8_masked(const FA_LDS uint8_t* __restrict__ st, Q8State<D>& S, const Kv8Addr& la,
+                                           const FA_LDS uint8_t* __restrict__ dot, int key0, int qrow, int N,
+                                           bool causal, float sl2, float c1, int hh) {
+    using C = Q8Cfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+    f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+        s = mfma32h(lds_read16b(st, la.rbase + C::KR + ds * 32), S.qf[ds], s);
+        dp = mfma32h(lds_read16b(st, la.rbase + C::VR + ds * 32), lds_read16b(dot, ds * 32), dp);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int kk = key0 + (i >> 2) * 8 + hh * 4 + (i & 3);
+        float x = fast_exp2(fmaf(s[i], sl2, -S.l2));
+        if (kk >= N || (causal && kk > qrow)) x = 0.f;
+        const float dpv = dp[i];
+        S.dacc = fmaf(x, dpv, S.dacc);
+        s[i] = x;
+        dp[i] = x * fmaf(dpv, c1, -S.dd);
+    }
+    u32x4 pp[2], dsp[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int i = kc * 8 + 2 * w;
+            pp[kc][w] = pack_f16(s[i], s[i + 1]);
+            dsp[kc][w] = pack_f16(dp[i], dp[i + 1]);
+        }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const u32x4 a = lds_read16b(st + la.tb[kc], C::KT + db * 32 * C::TL);
+            S.pk[db] = mfma32h(a, pp[kc], S.pk[db]);
+            S.dq[db] = mfma32h(a, dsp[kc], S.dq[db]);
+        }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_kernel(BwdParams p) {
+    using C = Q8Cfg<D>;
+    constexpr int DS = C::DS, DB = C::DB;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int N = p.N, Np = p.Np;
+    const bool causal = p.causal != 0;
+    const int nqt = (N + kQ8_WG - 1) / kQ8_WG;
+    int rank, bh;
+    unmap_block_unit_major(blockIdx.x, p.B * p.Hq, nqt, rank, bh);
+    const int qt = causal ? nqt - 1 - rank : rank;   // heaviest first when causal
+    const int b = bh / p.Hq, hq = bh - b * p.Hq;
+    const size_t bkv = (size_t)b * p.Hkv + hq / p.G;
+    const BufRes rk = make_bufres(p.k16 + bkv * Np * D, (uint32_t)Np * D * 2);
+    const BufRes rv = make_bufres(p.v16 + bkv * Np * D, (uint32_t)Np * D * 2);
+    const BufRes rkt = make_bufres(p.kT16 + bkv * D * Np, (uint32_t)Np * D * 2);
+    const float sl2 = p.scales[0], c1 = p.scales[1];
+
+    const int q0 = qt * kQ8_WG;
+    const int r0 = q0 + w * kQ_W;
+    const int qrow = r0 + l32;
+    // Np is a multiple of 128 and r0 of 32, so a wave's 32 rows lie all below
+    // Np or all at or past it; past it they are zero operands with P = 0.
+    const bool has_rows = r0 < Np;
+    const int ntk = (N + kQ8_N - 1) / kQ8_N;
+    const int nfull = N / kQ8_N;                     // key tiles with no key >= N
+    const int nt = causal ? min(ntk, (q0 + kQ8_WG - 1) / kQ8_N + 1) : ntk;
+    // Tiles [0, jfull) are unmasked for this wave, [jfull, jlast] masked, the
+    // rest idle. jA (wave 0's jfull) <= every wave's jfull: the tiles below it
+    // run one code path on all waves, with the next tile's copy spread over
+    // the slots. A wave past N runs those too (its rows have P = 0) and then
+    // idles.
+    const int jA = causal ? min(nfull, q0 / kQ8_N) : nfull;
+    int jfull = causal ? min(nfull, r0 / kQ8_N) : nfull;
+    int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ8_N) : ntk - 1;
+    if (r0 >= N) {
+        jfull = jA;
+        jlast = -1;
+    }
+
+    Q8State<D> S;
+    {
+        const size_t ro = ((size_t)bh * Np + (has_rows ? qrow : 0)) * D;
+        FA_LDS uint8_t* drow = (FA_LDS uint8_t*)smem + C::DOR + (w * kQ_W + l32) * C::SR + hh * 16;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            S.qf[ds] = gload16(p.q16 + ro + ds * 16 + hh * 8, has_rows);
+            *reinterpret_cast<FA_LDS u32x4*>(drow + ds * 32) = gload16(p.do16 + ro + ds * 16 + hh * 8, has_rows);
+        }
+        S.l2 = has_rows ? p.lse2[(size_t)bh * Np + qrow] : INFINITY;
+        S.dd = has_rows ? p.delta[(size_t)bh * Np + qrow] : 0.f;
+        S.dacc = 0.f;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        S.dq[db] = zero16();
+        S.pk[db] = zero16();
+    }
+    typename C::PlanR pr;
+    typename C::PlanT pt;
+    pr.init(w, lane, D);
+    pt.init(w, lane, Np);
+    Kv8Addr la;
+    la.init(l32, hh, C::SR);
+    FA_LDS uint8_t* st0 = (FA_LDS uint8_t*)smem;
+    const FA_LDS uint8_t* dot = st0 + C::DOR + (w * kQ_W + l32) * C::SR + hh * 16;
+    auto next = [&](int j) {
+        return Q8Next<D>{pr, pt, rk, rv, rkt, (uint32_t)j * kQ8_N * D * 2, (uint32_t)j * kQ8_N * 2,
+                         __builtin_amdgcn_readfirstlane(w)};
+    };
+
+    dq8_copy<D>(next(0), st0);
+    wait_vmem();
+    __syncthreads();
+    const int jS = min(jA, nt - 1);   // each has a next tile to copy
+    for (int j = 0; j < jS; ++j) {
+        const Q8Next<D> nx = next(j + 1);
+        dq8_step<D, true>(st0 + (j & 1) * C::STAGE, S, la, dot, sl2, c1, &nx, st0 + ((j + 1) & 1) * C::STAGE);
+        wait_vmem();
+        __syncthreads();
+    }
+    for (int j = jS; j < nt; ++j) {
+        const FA_LDS uint8_t* cur = st0 + (j & 1) * C::STAGE;
+        if (j + 1 < nt) dq8_copy<D>(next(j + 1), st0 + ((j + 1) & 1) * C::STAGE);
+        if (j < jfull)
+            dq8_step<D, false>(cur, S, la, dot, sl2, c1, nullptr, nullptr);
+        else if (j <= jlast)
+            dq8_masked<D>(cur, S, la, dot, j * kQ8_N, qrow, N, causal, sl2, c1, hh);
+        wait_vmem();
+        __syncthreads();
+    }
+
+    // exact row dot (the lane halves hold half of the keys each), in units of 2^sS
+    const float dx = (S.dacc + swap_half(S.dacc)) * c1;
+    if (qrow < N) {
+        const int dr = p.d;   // rows of dr values (D, or fewer: padded copies)
+        uint16_t* dQg = p.dq + ((size_t)bh * N + qrow) * dr;
+        const float sc = p.scales[4];
+        const float corr = S.dd - dx;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float v4[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) v4[t] = fmaf(corr, S.pk[db][u * 4 + t], S.dq[db][u * 4 + t]) * sc;
+                u32x2 val;
+                val[0] = pack_bf16(v4[0], v4[1]);
+                val[1] = pack_bf16(v4[2], v4[3]);
+                if (db * 32 + u * 8 + hh * 4 < dr) *reinterpret_cast<u32x2*>(dQg + db * 32 + u * 8 + hh * 4) = val;
+            }
+        if (hh == 0) p.delta[(size_t)bh * Np + qrow] = dx;   // for the dK/dV kernel
+    }
+}
+
 // ---------------------------------------------------------------- d = 256: split head dimension
 // A wave's K and V (dK/dV pass) or Q and dO (dQ pass) over all 256 columns take
 // 128 registers, and the four accumulators of the full width 256 more: no room
@@ -2136,8 +2455,16 @@ hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
+    const bool bounded = p.window > 0 || p.cu_seqlens;
+    if constexpr (D == 128) {
+        if (!bounded) {
+            const int grid8 = p.B * p.Hq * ((p.N + kQ8_WG - 1) / kQ8_WG);
+            hipLaunchKernelGGL((bwd_dq8_kernel<D>), dim3(grid8), dim3(kThreads8), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     const int grid = p.B * p.Hq * ((p.N + kQ_WG - 1) / kQ_WG);
-    if (p.window > 0 || p.cu_seqlens)
+    if (bounded)
         hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
