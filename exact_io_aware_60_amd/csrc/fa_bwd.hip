@@ -1006,6 +1006,12 @@ __device__ __forceinline__ void kv8_step(const FA_LDS uint8_t* __restrict__ st, 
     lse_d(std::integral_constant<int, 0>{});
     static_for<NS>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
+        // The S and dP slots (with the P tasks) run at a raised wave priority,
+        // the products at the normal one: when both waves of a SIMD can issue,
+        // the one forming scores goes first. Measured on MI355X: 3.0% less
+        // time for dK/dV and 2.2% for dQ than equal priorities.
+        if constexpr (n == 0) __builtin_amdgcn_s_setprio(1);
+        if constexpr (n == 2 * DS) __builtin_amdgcn_s_setprio(0);
         mfma_at(nc);
         if constexpr (n + PF < NS) frag(std::integral_constant<int, n + PF>{});
         if constexpr (COPY && n >= 1 && (n - 1) % SP == 0 && (n - 1) / SP < NITEM)
@@ -1784,6 +1790,12 @@ __device__ __forceinline__ void dq8_step(const FA_LDS uint8_t* __restrict__ st, 
     static_for<PF>([&](auto nc) { frag(nc); });
     static_for<NS>([&](auto nc) {
         constexpr int n = decltype(nc)::value;
+        // The S and dP slots (with the P tasks) run at a raised wave priority,
+        // the products at the normal one: when both waves of a SIMD can issue,
+        // the one forming scores goes first. Measured on MI355X: 3.0% less
+        // time for dK/dV and 2.2% for dQ than equal priorities.
+        if constexpr (n == 0) __builtin_amdgcn_s_setprio(1);
+        if constexpr (n == 2 * DS) __builtin_amdgcn_s_setprio(0);
         mfma_at(nc);
         if constexpr (n + PF < NS) frag(std::integral_constant<int, n + PF>{});
         if constexpr (COPY && n >= 1 && (n - 1) % SP == 0 && (n - 1) / SP < NITEM)
