@@ -1024,12 +1024,15 @@ __device__ __forceinline__ void kv8_step(const FA_LDS uint8_t* __restrict__ st, 
     });
 }
 
-// The step on a wave's causal diagonal: keys above a row get P = 0. Unpipelined;
-// one per head and wave.
-template <int D>
+// A step that crosses the causal diagonal: keys above a row get P = 0. With a
+// bounded mask (WIN) so do rows at or past kend, the first row that no longer
+// sees this lane's key, and rows before kbeg, the first row that sees it.
+// Unpipelined; a few per head and wave.
+template <int D, bool WIN>
 __device__ __forceinline__ void kv8_step_masked(const FA_LDS uint8_t* __restrict__ st, Kv8State<D>& S,
                                                 const Kv8Addr& la, const FA_LDS uint8_t* __restrict__ vt, int q0,
-                                                int key, float sl2, float c1, int hh) {
+                                                int key, float sl2, float c1, int hh, bool causal, int kbeg,
+                                                int kend) {
     using C = Kv8Cfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
     f32x16 s = zero16(), dp = zero16();
@@ -1047,7 +1050,7 @@ __device__ __forceinline__ void kv8_step_masked(const FA_LDS uint8_t* __restrict
             const int i = u * 4 + e;
             const int q = q0 + u * 8 + hh * 4 + e;
             float x = fast_exp2(fmaf(s[i], sl2, -lv[e]));
-            if (key > q) x = 0.f;
+            if ((causal && key > q) || (WIN && (q < kbeg || q >= kend))) x = 0.f;
             s[i] = x;
             dp[i] = x * fmaf(dp[i], c1, -dv4[e]);
         }
@@ -1071,7 +1074,7 @@ __device__ __forceinline__ void kv8_step_masked(const FA_LDS uint8_t* __restrict
         }
 }
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads8, 1) void bwd_dkdv8_kernel(BwdParams p) {
     using C = Kv8Cfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
@@ -1112,9 +1115,18 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkdv8_kernel(BwdParams p) {
         S.dv[db] = zero16();
     }
 
-    // Steps: 32-row blocks from the last one down to qs, all G heads per block.
-    const int qs = causal ? k0 : 0;
-    const int nrb = (N - qs + kKV8_Q - 1) / kKV8_Q;
+    // Steps: 32-row blocks from the last one down to qs, all G heads per block
+    // (rows before the block's first key see none of it under the causal
+    // mask). With a bounded mask only rows below qe see a key of this
+    // workgroup, and packed sequences without the causal mask start at the
+    // first key's sequence (qs, rounded down to a row block).
+    const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
+    const int kend = WIN ? bd.row_end(key) : 0;     // this lane's key
+    const bool lbnd = WIN && !causal;
+    const int kbeg = lbnd ? bd.first_key(key) : 0;  // first row that sees this lane's key
+    const int qs = causal ? k0 : (lbnd ? bd.first_key(k0) / kKV8_Q * kKV8_Q : 0);
+    const int qe = WIN ? min(N, bd.row_end(min(k0 + kKV8_WG - 1, N - 1))) : N;
+    const int nrb = (qe - qs + kKV8_Q - 1) / kKV8_Q;
     const int nsteps = G * nrb;
     const int qtop = qs + (nrb - 1) * kKV8_Q;
     KvRes rs;
@@ -1149,12 +1161,47 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkdv8_kernel(BwdParams p) {
     kv8_copy<D>(Kv8Next<D>{pr, pt, rs, src_of(0), __builtin_amdgcn_readfirstlane(w), lane}, st0);
     wait_vmem();
     __syncthreads();
-    // Row blocks with q0 >= k0 + 256 (all but the last eight when causal) are
-    // unmasked for every wave and run on one code path, with the next step's
-    // copy spread over the MFMA slots. A wave whose keys lie past N runs them
-    // too (zero or padding keys, never stored).
-    const int nsteady = causal ? G * max(0, nrb - kKV8_WG / kKV8_Q) : nsteps - 1;
-    for (int j = 0; j < nsteady; ++j) {
+    // Row blocks t in [tnear, tfar) (q0 = qs + 32 t) are unmasked for every
+    // wave and run on one code path, with the next step's copy spread over the
+    // MFMA slots: all but the last eight blocks when causal. A wave whose keys
+    // lie past N runs them too (zero or padding keys, never stored). With a
+    // bounded mask the top blocks t >= tfar hold rows past some key's reach (the
+    // workgroup's first key reaches least far); they come first (jT steps, per
+    // wave). The bottom blocks t < tnear hold rows before some key's first row:
+    // the causal diagonal, or, for packed sequences without the causal mask,
+    // rows before the last key's sequence start.
+    const int tfar = WIN ? max(0, bd.row_end(k0) - qs) / kKV8_Q : 0;
+    const int tnear = lbnd ? (max(0, bd.first_key(min(k0 + kKV8_WG - 1, N - 1)) - qs) + kKV8_Q - 1) / kKV8_Q
+                           : kKV8_WG / kKV8_Q;
+    const int nfar = WIN ? max(0, nrb - tfar) : 0;
+    const int jT = G * nfar;
+    int nsteady = WIN ? G * max(0, min(tfar, nrb) - tnear)
+                      : (causal ? G * max(0, nrb - kKV8_WG / kKV8_Q) : nsteps - 1);   // each has a next step
+    if (lbnd) nsteady = min(nsteady, max(0, nsteps - jT - 1));
+    const int kend_w0 = WIN ? bd.row_end(kw0) : 0, kend_w31 = WIN ? bd.row_end(kw0 + kKV_W - 1) : 0;
+    const int kbeg_w0 = lbnd ? bd.first_key(kw0) : 0;
+    const int kbeg_w31 = lbnd ? bd.first_key(min(kw0 + kKV_W - 1, N - 1)) : 0;
+    // A step where each wave is idle (no row of the step sees its keys),
+    // masked or unmasked.
+    auto per_wave_step = [&](int j) {
+        const int q0 = qtop - (j / G) * kKV8_Q;
+        const bool active = kw0 < N && (!causal || q0 + kKV8_Q - 1 >= kw0) && (!WIN || q0 < kend_w31) &&
+                            (!lbnd || q0 + kKV8_Q - 1 >= kbeg_w0);
+        const int mode = !active ? 0
+                                 : (((causal && q0 < kw0 + kKV_W - 1) || (WIN && q0 + kKV8_Q - 1 >= kend_w0) ||
+                                     (lbnd && q0 < kbeg_w31)) ? 2 : 1);
+        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
+        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
+        if (j + 1 < nsteps) kv8_copy<D>(Kv8Next<D>{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane}, wst);
+        if (mode == 1)
+            kv8_step<D, false>(rst, S, la, vt, sl2, c1, nullptr, nullptr);
+        else if (mode == 2)
+            kv8_step_masked<D, WIN>(rst, S, la, vt, q0, key, sl2, c1, hh, causal, kbeg, kend);
+        wait_vmem();
+        __syncthreads();
+    };
+    for (int j = 0; j < jT; ++j) per_wave_step(j);
+    for (int j = jT; j < jT + nsteady; ++j) {
         const Kv8Next<D> nx{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane};
         FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
         const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
@@ -1162,22 +1209,7 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dkdv8_kernel(BwdParams p) {
         wait_vmem();
         __syncthreads();
     }
-    // The rest: each wave is idle (rows above its keys), on its diagonal, or
-    // unmasked.
-    for (int j = nsteady; j < nsteps; ++j) {
-        const int q0 = qtop - (j / G) * kKV8_Q;
-        const bool active = kw0 < N && (!causal || q0 + kKV8_Q - 1 >= kw0);
-        const int mode = !active ? 0 : ((causal && q0 < kw0 + kKV_W - 1) ? 2 : 1);
-        FA_LDS uint8_t* wst = st0 + ((j + 1) & 1) * C::STAGE;
-        const FA_LDS uint8_t* rst = st0 + (j & 1) * C::STAGE;
-        if (j + 1 < nsteps) kv8_copy<D>(Kv8Next<D>{pr, pt, rs, src_of(j + 1), __builtin_amdgcn_readfirstlane(w), lane}, wst);
-        if (mode == 1)
-            kv8_step<D, false>(rst, S, la, vt, sl2, c1, nullptr, nullptr);
-        else if (mode == 2)
-            kv8_step_masked<D>(rst, S, la, vt, q0, key, sl2, c1, hh);
-        wait_vmem();
-        __syncthreads();
-    }
+    for (int j = jT + nsteady; j < nsteps; ++j) per_wave_step(j);
 
     // dK^T / dV^T blocks: lane holds key l32, d rows db*32 + u*8 + hh*4 + 0..3.
     if (key < N) {
@@ -1808,13 +1840,14 @@ __device__ __forceinline__ void dq8_step(const FA_LDS uint8_t* __restrict__ st, 
     });
 }
 
-// A tile with masked entries (the causal diagonal or keys >= N), unpipelined.
-// Keys past N are zero rows in the copies but would still get P =
-// exp2(-LSE), so they are masked like the ones above the diagonal.
-template <int D>
+// A tile with masked entries (the causal diagonal, keys >= N, and with a
+// bounded mask (WIN) keys outside [lbq, ubq), this lane's row's first key and
+// end), unpipelined. Keys past N are zero rows in the copies but would still
+// get P = exp2(-LSE), so they are masked like the ones above the diagonal.
+template <int D, bool WIN>
 __device__ __forceinline__ void dq8_masked(const FA_LDS uint8_t* __restrict__ st, Q8State<D>& S, const Kv8Addr& la,
                                            const FA_LDS uint8_t* __restrict__ dot, int key0, int qrow, int N,
-                                           bool causal, float sl2, float c1, int hh) {
+                                           bool causal, float sl2, float c1, int hh, int lbq, int ubq) {
     using C = Q8Cfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
     f32x16 s = zero16(), dp = zero16();
@@ -1827,7 +1860,7 @@ __device__ __forceinline__ void dq8_masked(const FA_LDS uint8_t* __restrict__ st
     for (int i = 0; i < 16; ++i) {
         const int kk = key0 + (i >> 2) * 8 + hh * 4 + (i & 3);
         float x = fast_exp2(fmaf(s[i], sl2, -S.l2));
-        if (kk >= N || (causal && kk > qrow)) x = 0.f;
+        if (kk >= N || (causal && kk > qrow) || (WIN && (kk < lbq || kk >= ubq))) x = 0.f;
         const float dpv = dp[i];
         S.dacc = fmaf(x, dpv, S.dacc);
         s[i] = x;
@@ -1852,7 +1885,7 @@ __device__ __forceinline__ void dq8_masked(const FA_LDS uint8_t* __restrict__ st
         }
 }
 
-template <int D>
+template <int D, bool WIN>
 __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_kernel(BwdParams p) {
     using C = Q8Cfg<D>;
     constexpr int DS = C::DS, DB = C::DB;
@@ -1882,15 +1915,36 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_kernel(BwdParams p) {
     const bool has_rows = r0 < Np;
     const int ntk = (N + kQ8_N - 1) / kQ8_N;
     const int nfull = N / kQ8_N;                     // key tiles with no key >= N
-    const int nt = causal ? min(ntk, (q0 + kQ8_WG - 1) / kQ8_N + 1) : ntk;
-    // Tiles [0, jfull) are unmasked for this wave, [jfull, jlast] masked, the
-    // rest idle. jA (wave 0's jfull) <= every wave's jfull: the tiles below it
-    // run one code path on all waves, with the next tile's copy spread over
-    // the slots. A wave past N runs those too (its rows have P = 0) and then
-    // idles.
-    const int jA = causal ? min(nfull, q0 / kQ8_N) : nfull;
-    int jfull = causal ? min(nfull, r0 / kQ8_N) : nfull;
-    int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ8_N) : ntk - 1;
+    // Bounded mask (sliding window or packed sequences): a row's first key
+    // never decreases along the rows, nor does its last one for packed
+    // sequences without the causal mask (ub, the end of the row's sequence).
+    const Bounds bd{p.cu_seqlens, p.nseq, p.window, N};
+    const bool ubnd = WIN && !causal;
+    auto ub_of = [&](int r) { return bd.row_end(min(r, N - 1)); };   // keys of row r end before this
+    const int nt = causal ? min(ntk, (q0 + kQ8_WG - 1) / kQ8_N + 1)
+                          : (ubnd ? max(1, min(ntk, (ub_of(q0 + kQ8_WG - 1) + kQ8_N - 1) / kQ8_N)) : ntk);
+    // For this wave, tiles before jw0 hold no visible key, tiles [jw0, jw1)
+    // cross its rows' first keys (masked), tiles [jw1, jfull) are unmasked,
+    // tiles [jfull, jlast] masked (the causal diagonal, keys >= N, its rows'
+    // last keys), later ones idle. Without a window jw0 = jw1 = 0. jA (wave
+    // 0's jfull) <= every wave's jfull and jU (the last wave's jw1) >= every
+    // wave's jw1, so the tiles in [jU, jA) run one code path on all waves,
+    // with the next tile's copy spread over the slots. A wave past N runs
+    // those too (its rows have P = 0) and otherwise idles.
+    const int jA = causal ? min(nfull, q0 / kQ8_N) : (ubnd ? min(nfull, ub_of(q0) / kQ8_N) : nfull);
+    int jfull = causal ? min(nfull, r0 / kQ8_N) : (ubnd ? min(nfull, ub_of(r0) / kQ8_N) : nfull);
+    int jlast = causal ? min(ntk - 1, (r0 + kQ_W - 1) / kQ8_N)
+                       : (ubnd ? min(ntk - 1, max(0, ub_of(r0 + kQ_W - 1) - 1) / kQ8_N) : ntk - 1);
+    const int lbq = WIN ? bd.first_key(qrow) : 0;   // this lane's row
+    const int ubq = ubnd ? bd.row_end(qrow) : N;
+    auto jw1_of = [&](int r) {                       // first tile the wave of rows r.. sees in full
+        const int f = bd.first_key(r + kQ_W - 1);
+        return f > 0 ? (f + kQ8_N - 1) / kQ8_N : 0;
+    };
+    const int jw0 = WIN ? max(0, bd.first_key(r0)) / kQ8_N : 0;
+    const int jw1 = WIN ? jw1_of(r0) : 0;
+    const int jst = WIN ? max(0, bd.first_key(q0)) / kQ8_N : 0;      // wave 0's jw0
+    const int jU = WIN ? jw1_of(q0 + kQ8_WG - kQ_W) : 0;
     if (r0 >= N) {
         jfull = jA;
         jlast = -1;
@@ -1927,26 +1981,30 @@ __global__ __launch_bounds__(kThreads8, 1) void bwd_dq8_kernel(BwdParams p) {
                          __builtin_amdgcn_readfirstlane(w)};
     };
 
-    dq8_copy<D>(next(0), st0);
+    dq8_copy<D>(next(jst), st0 + (jst & 1) * C::STAGE);
     wait_vmem();
     __syncthreads();
+    auto per_wave_tile = [&](int j) {
+        const FA_LDS uint8_t* cur = st0 + (j & 1) * C::STAGE;
+        if (j + 1 < nt) dq8_copy<D>(next(j + 1), st0 + ((j + 1) & 1) * C::STAGE);
+        if (!(WIN && j < jw0) && j <= jlast) {
+            if (j >= jw1 && j < jfull)
+                dq8_step<D, false>(cur, S, la, dot, sl2, c1, nullptr, nullptr);
+            else
+                dq8_masked<D, WIN>(cur, S, la, dot, j * kQ8_N, qrow, N, causal, sl2, c1, hh, lbq, ubq);
+        }
+        wait_vmem();
+        __syncthreads();
+    };
     const int jS = min(jA, nt - 1);   // each has a next tile to copy
-    for (int j = 0; j < jS; ++j) {
+    for (int j = jst; j < min(jU, nt); ++j) per_wave_tile(j);
+    for (int j = max(jst, jU); j < jS; ++j) {
         const Q8Next<D> nx = next(j + 1);
         dq8_step<D, true>(st0 + (j & 1) * C::STAGE, S, la, dot, sl2, c1, &nx, st0 + ((j + 1) & 1) * C::STAGE);
         wait_vmem();
         __syncthreads();
     }
-    for (int j = jS; j < nt; ++j) {
-        const FA_LDS uint8_t* cur = st0 + (j & 1) * C::STAGE;
-        if (j + 1 < nt) dq8_copy<D>(next(j + 1), st0 + ((j + 1) & 1) * C::STAGE);
-        if (j < jfull)
-            dq8_step<D, false>(cur, S, la, dot, sl2, c1, nullptr, nullptr);
-        else if (j <= jlast)
-            dq8_masked<D>(cur, S, la, dot, j * kQ8_N, qrow, N, causal, sl2, c1, hh);
-        wait_vmem();
-        __syncthreads();
-    }
+    for (int j = max(max(jst, jU), jS); j < nt; ++j) per_wave_tile(j);
 
     // exact row dot (the lane halves hold half of the keys each), in units of 2^sS
     const float dx = (S.dacc + swap_half(S.dacc)) * c1;
@@ -2450,36 +2508,38 @@ hipError_t launch_prep_t(const BwdParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
     const bool bounded = p.window > 0 || p.cu_seqlens;
-    if constexpr (D == 128) {
-        if (!bounded) {
-            const int grid8 = p.B * p.Hkv * ((p.N + kKV8_WG - 1) / kKV8_WG);
-            hipLaunchKernelGGL((bwd_dkdv8_kernel<D>), dim3(grid8), dim3(kThreads8), 0, stream, p);
-            return hipGetLastError();
-        }
+    if constexpr (D == 128) {   // the eight-wave form
+        const int grid = p.B * p.Hkv * ((p.N + kKV8_WG - 1) / kKV8_WG);
+        if (bounded)
+            hipLaunchKernelGGL((bwd_dkdv8_kernel<D, true>), dim3(grid), dim3(kThreads8), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv8_kernel<D, false>), dim3(grid), dim3(kThreads8), 0, stream, p);
+    } else {
+        const int grid = p.B * p.Hkv * ((p.N + kKV_WG - 1) / kKV_WG);
+        if (bounded)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     }
-    const int grid = p.B * p.Hkv * ((p.N + kKV_WG - 1) / kKV_WG);
-    if (bounded)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
     const bool bounded = p.window > 0 || p.cu_seqlens;
-    if constexpr (D == 128) {
-        if (!bounded) {
-            const int grid8 = p.B * p.Hq * ((p.N + kQ8_WG - 1) / kQ8_WG);
-            hipLaunchKernelGGL((bwd_dq8_kernel<D>), dim3(grid8), dim3(kThreads8), 0, stream, p);
-            return hipGetLastError();
-        }
+    if constexpr (D == 128) {   // the eight-wave form
+        const int grid = p.B * p.Hq * ((p.N + kQ8_WG - 1) / kQ8_WG);
+        if (bounded)
+            hipLaunchKernelGGL((bwd_dq8_kernel<D, true>), dim3(grid), dim3(kThreads8), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dq8_kernel<D, false>), dim3(grid), dim3(kThreads8), 0, stream, p);
+    } else {
+        const int grid = p.B * p.Hq * ((p.N + kQ_WG - 1) / kQ_WG);
+        if (bounded)
+            hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     }
-    const int grid = p.B * p.Hq * ((p.N + kQ_WG - 1) / kQ_WG);
-    if (bounded)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid), dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
