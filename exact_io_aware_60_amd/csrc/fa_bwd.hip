@@ -58,23 +58,37 @@
 // multiple of 128 rows with zero data, D = 0 and LSE = +inf, so no tile reads
 // past an array and padding rows carry P = 0.
 //
-// Data flow (four waves per workgroup, one per SIMD):
+// Data flow at d = 128 (eight waves per workgroup, two per SIMD):
+//  * dK/dV: a workgroup owns 256 keys, 32 per wave. K stays in registers as
+//    the B operand of S = Q K^T; V, the B operand of dP = dO V^T, sits in LDS
+//    (the workgroup's 256 rows), since two waves per SIMD leave each at most
+//    256 registers. Each step streams 32 query rows of one query head of the
+//    group (Q and dO rows, their transposes, LSE and D) through two LDS
+//    stages. The steps walk the row blocks from the last one down, all heads
+//    of the group per block, so workgroups running side by side read the same
+//    rows from L2. S and dP leave one key per lane; P and dS in fp16 feed
+//    dV^T += dO^T P and dK^T += Q^T dS.
+//  * dQ: a workgroup owns 256 query rows, 32 per wave. Q stays in registers,
+//    dO sits in LDS; tiles of 32 keys (K and V rows, K^T) stream through two
+//    stages. S^T = K Q^T and dP^T = V dO^T leave one query row per lane; P^T
+//    and dS^T in fp16 feed dQ^T += K^T dS^T and PK^T += K^T P^T.
+// In both, a step's MFMAs run in four phases (the two score products, then
+// the two gradient products), with the exp / dS work interleaved by hand
+// between them and the next step's copy spread over the slots; the other wave
+// of the SIMD fills the gaps. Per MFMA a step copies half the bytes of a
+// four-wave workgroup over 128 keys or rows.
+// Data flow at d <= 64 (four waves per workgroup, one per SIMD in the
+// workgroup, two workgroups per CU):
 //  * dQ: a workgroup owns 128 query rows, 32 per wave, whose Q and dO rows
 //    stay in registers as MFMA operands. Tiles of 64 keys (K and V rows, K^T)
-//    stream through three LDS stages. S^T = K Q^T and dP^T = V dO^T leave one
-//    query row per lane; P^T and dS^T in fp16 feed dQ^T += K^T dS^T and
-//    PK^T += K^T P^T. The loop is software-pipelined across tiles: the MFMAs of
-//    tile j's scores run beside the dQ products of tile j-1, and the exp / dS
-//    work of tile j spreads over the slots in between, so the vector ALU work
-//    of one tile overlaps a whole tile of MFMAs.
+//    stream through three LDS stages. The loop is software-pipelined across
+//    tiles: the MFMAs of tile j's scores run beside the dQ products of tile
+//    j-1, and the exp / dS work of tile j spreads over the slots in between.
 //  * dK/dV: a workgroup owns 128 keys, 32 per wave, held in registers as MFMA
 //    operands. Each step streams 64 query rows of one query head of the group
-//    (Q and dO rows, their transposes, LSE and D) through two LDS stages. The
-//    steps walk the row blocks from the last one down, all heads of the group
-//    per block, so workgroups running side by side read the same rows from L2.
-//    S = Q K^T and dP = dO V^T leave one key per lane; P and dS in fp16 feed
-//    dV^T += dO^T P and dK^T += Q^T dS. Inside a step the exp / dS work is
-//    interleaved by hand with the MFMAs.
+//    through two LDS stages, in the order above. Inside a step the exp / dS
+//    work is interleaved by hand with the MFMAs.
+// (d = 256 splits the accumulated columns over two workgroups; see below.)
 // Only tiles that cross the causal diagonal (and, in dQ, the ragged last key
 // tile) take an element-wise mask, on a plain unpipelined path.
 #include "fa_device.h"
@@ -83,7 +97,7 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;   // 4 waves, one per SIMD
+constexpr int kThreads = 256;   // 4 waves
 
 // Per-lane fragment addresses in a stage of either backward kernel. Row tiles
 // ([64 x D], padded rows of SR bytes) are read at one lane base plus constants:
@@ -372,6 +386,7 @@ constexpr int kKV_WG = 128;   // keys per workgroup
 constexpr int kKV_W = 32;     // keys per wave
 constexpr int kKV_Q = 64;     // query rows per step
 
+// The four-wave dK/dV kernel: d <= 64 (D = 64); d = 128 runs the eight-wave form.
 template <int D>
 struct KvCfg {
     static constexpr int DS = D / 16, DB = D / 32;
@@ -811,8 +826,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dK / dV, eight waves
-// The d = 128 form without a bounded mask. A workgroup owns 256 keys, 32 per
-// wave, with two waves per SIMD, and each step streams 32 query rows. Every
+// The d = 128 form (every mask). A workgroup owns 256 keys, 32 per wave,
+// with two waves per SIMD, and each step streams 32 query rows. Every
 // byte a step copies then serves twice as many keys as in the four-wave form,
 // so each MFMA costs half as many copy instructions, and a SIMD has a second
 // wave to issue from while one waits on a copy, an LDS read or its softmax
@@ -1244,10 +1259,11 @@ struct QCfg {
     static constexpr int DS = D / 16, DB = D / 32;
     static constexpr int SR = RowPad<D>::STRIDE;      // K, V rows: [64][D], padded rows
     static constexpr int RT = padded_tile_bytes<SR, kQ_N>();
-    // K^T: [D][64]. d = 64: dense 128-byte rows, XOR-swizzled as the dK/dV
-    // kernel's transposed tiles, so that three stages (78 KiB) leave room for
-    // a second workgroup per CU (two waves per SIMD; the kernel needs at most
-    // 256 registers there). d = 128: padded rows (below).
+    // This four-wave kernel serves d <= 64 (D = 64); d = 128 runs the
+    // eight-wave form. K^T: [D][64]. D = 64: dense 128-byte rows, XOR-swizzled
+    // as the dK/dV kernel's transposed tiles, so that three stages (78 KiB)
+    // leave room for a second workgroup per CU (two waves per SIMD; the kernel
+    // needs at most 256 registers there). Other D: padded rows (below).
     static constexpr bool TSWZ = D == 64;
     static constexpr int ST = RowPad<kQ_N>::STRIDE;
     static constexpr int TT = TSWZ ? D * 2 * kQ_N : padded_tile_bytes<ST, D>();
@@ -1264,8 +1280,8 @@ struct QCfg {
     // tile's first slots. Each group of 16 starts after its inputs are complete
     // and ends before the product that consumes it.
     static constexpr int START = 3 * DS + 1;
-    // At d = 128 K^T keeps padded rows: swizzled ones, which copy no pad bytes
-    // and no duplicate blocks, measured slower in this kernel.
+    // Padded K^T rows: when this kernel ran d = 128, swizzled ones, which copy
+    // no pad bytes and no duplicate blocks, measured slower.
     using PlanR = CopyPlan<D, SR, kQ_N, 4>;
     using PlanT = std::conditional_t<TSWZ, CopyPlanSwz<2 * kQ_N, D, 4>, CopyPlan<kQ_N, ST, D, 4>>;
     using Addr = LaneAddr<SR, std::conditional_t<TSWZ, Swz128, PadRows<ST>>>;
@@ -1679,7 +1695,7 @@ __global__ __launch_bounds__(kThreads, QCfg<D>::PER_CU) void bwd_dq_kernel(BwdPa
 }
 
 // ---------------------------------------------------------------- dQ, eight waves
-// The d = 128 form without a bounded mask, built like the eight-wave dK/dV
+// The d = 128 form (every mask), built like the eight-wave dK/dV
 // kernel: a workgroup owns 256 query rows, 32 per wave, two waves per SIMD,
 // and each step streams a tile of 32 keys. Q stays in registers; dO, the
 // other row operand, sits in LDS (the workgroup's 256 rows) and is read as the
