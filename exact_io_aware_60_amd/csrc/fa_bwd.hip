@@ -1260,13 +1260,12 @@ struct QCfg {
     static constexpr int SR = RowPad<D>::STRIDE;      // K, V rows: [64][D], padded rows
     static constexpr int RT = padded_tile_bytes<SR, kQ_N>();
     // This four-wave kernel serves d <= 64 (D = 64); d = 128 runs the
-    // eight-wave form. K^T: [D][64]. D = 64: dense 128-byte rows, XOR-swizzled
-    // as the dK/dV kernel's transposed tiles, so that three stages (78 KiB)
-    // leave room for a second workgroup per CU (two waves per SIMD; the kernel
-    // needs at most 256 registers there). Other D: padded rows (below).
-    static constexpr bool TSWZ = D == 64;
-    static constexpr int ST = RowPad<kQ_N>::STRIDE;
-    static constexpr int TT = TSWZ ? D * 2 * kQ_N : padded_tile_bytes<ST, D>();
+    // eight-wave form. K^T: [D][64], dense 128-byte rows, XOR-swizzled as the
+    // dK/dV kernel's transposed tiles, so that three stages (78 KiB) leave room
+    // for a second workgroup per CU (two waves per SIMD; the kernel needs at
+    // most 256 registers there).
+    static_assert(D == 64, "the four-wave dQ kernel is built for d <= 64");
+    static constexpr int TT = D * 2 * kQ_N;
     static constexpr int KR = 0, VR = RT, KT = 2 * RT;
     static constexpr int STAGE = 2 * RT + TT;
     static constexpr int LDS = 3 * STAGE;             // tiles j-1 (K^T), j, j+1
@@ -1280,14 +1279,12 @@ struct QCfg {
     // tile's first slots. Each group of 16 starts after its inputs are complete
     // and ends before the product that consumes it.
     static constexpr int START = 3 * DS + 1;
-    // Padded K^T rows: when this kernel ran d = 128, swizzled ones, which copy
-    // no pad bytes and no duplicate blocks, measured slower.
     using PlanR = CopyPlan<D, SR, kQ_N, 4>;
-    using PlanT = std::conditional_t<TSWZ, CopyPlanSwz<2 * kQ_N, D, 4>, CopyPlan<kQ_N, ST, D, 4>>;
-    using Addr = LaneAddr<SR, std::conditional_t<TSWZ, Swz128, PadRows<ST>>>;
-    static constexpr int PER_CU = TSWZ ? 2 : 1;       // workgroups per CU
+    using PlanT = CopyPlanSwz<2 * kQ_N, D, 4>;
+    using Addr = LaneAddr<SR, Swz128>;
+    static constexpr int PER_CU = 2;                  // workgroups per CU
     static_assert(LDS * PER_CU <= 160 * 1024, "LDS budget");
-    static_assert(!TSWZ || (KT % 128 == 0 && STAGE % 128 == 0), "swizzled tiles start on 128 bytes");
+    static_assert(KT % 128 == 0 && STAGE % 128 == 0, "swizzled tiles start on 128 bytes");
 };
 
 // First softmax task of linear slot x (x counts from the tile's slot 0 and
