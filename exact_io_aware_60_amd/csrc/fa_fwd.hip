@@ -183,7 +183,7 @@ __device__ __forceinline__ void exp_pack_one(const f32x16& x, int pi, float& ls,
     const int kc = pi >> 2, t = pi & 3, i = kc * 8 + 2 * t;
     const float p0 = fast_exp2(x[i]);
     const float p1 = fast_exp2(x[i + 1]);
-    ls += p0 + p1;
+    ls = pi == 0 ? p0 + p1 : ls + (p0 + p1);   // the chunk's first pair starts the sum (no 0 + x)
     pp[kc][t] = pack_bf16(p0, p1);
 }
 
@@ -308,7 +308,7 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
                                                 const FA_LDS uint8_t* __restrict__ Vt, int vbase, int h,
                                                 const u32x4 (&qf)[D / 16], f32x16& sc, f32x16& sn,
                                                 float& m, float& l, f32x16& lsum, float sl2, f32x16 (&o)[D / 32],
-                                                u32x4 (&ka)[2], const CP& cp) {
+                                                u32x4 (&ka)[2], const CP& cp, const u32x4& ones) {
     constexpr int DS = D / 16, DB = D / 32, NF = 2 * DB;
     // the 8 packs of the current chunk over the DS phase-1 steps: PPS per step,
     // on every PEVERY-th step (d = 256: one pack every other step)
@@ -355,7 +355,7 @@ __device__ __forceinline__ void pipelined_chunk(const FA_LDS uint8_t* __restrict
     static_for<NF>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         o[f % DB] = mfma32(vf[f], pp[f / DB], o[f % DB]);
-        if constexpr (f == 1 || f == NF - 1) lsum = mfma32(ones_bf16(), pp[f == 1 ? 0 : 1], lsum);
+        if constexpr (f == 1 || f == NF - 1) lsum = mfma32(ones, pp[f == 1 ? 0 : 1], lsum);
 #pragma unroll
         for (int c = 0; c < EPS; ++c) sn[f * EPS + c] = fmaf(sn[f * EPS + c], sl2, -m);
         if constexpr (f == 2 || f == 3) ka[f - 2] = k_frag<D>(Knn, kbase, hnn, f - 2);
@@ -373,6 +373,7 @@ struct FwdState {
     u32x4 ka[2];               // first two K fragments of the next pipelined chunk's score MFMAs
     float m, l;                // reference (log2 units), this lane's share of the row sum
     f32x16 lsum;               // ones * P^T: the row sum of the bf16 probabilities the P.V MFMA takes
+    u32x4 ones;                // the all-ones A operand of the row-sum MFMA, held across the loop
 };
 
 // Sliding window: where a wave's keys start. A wave skips the chunks before
@@ -430,7 +431,7 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
         mask_scores<true>(sc, c * 32, qrow, N, causal, hh, wd.win);
     if (c < lastc) {
         pipelined_chunk<D, H>(Kn, kbase, H ^ 1, Kr1, H, Vt, vbase, H, st.qf, sc, sn, st.m, st.l, st.lsum, sl2,
-                              st.o, st.ka, cp);
+                              st.o, st.ka, cp, st.ones);
     } else {
         cp.bulk();
         softmax_pv<D>(Vt, vbase, H, sc, st.m, st.l, st.lsum, st.o);
@@ -552,6 +553,11 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_kernel(FwdParams p) {
     st.m = 0.f;
     st.l = 0.f;
     st.lsum = zero16();
+    // Held in registers for the whole loop (the compiler would otherwise
+    // rebuild the constant before every chunk's row-sum MFMAs: two moves per
+    // chunk; 0.6% of the forward's time with the first-pair start of the row sum).
+    st.ones = ones_bf16();
+    asm volatile("" : "+v"(st.ones));
 
     // K and V through buffer resources covering the head's N rows: rows of a
     // ragged last tile past N read as zeros (their scores are masked).
