@@ -14,7 +14,7 @@
 //    waves per SIMD hide most of them. So a workgroup is 8 waves (2 per SIMD),
 //    each owning 32 query rows (256 rows per workgroup, at most 256 registers
 //    per wave). At d = 64 a score costs half the MFMA work for the same
-//    softmax work, and the wave's loop fits in 152 registers: large grids take
+//    softmax work, and the wave's loop fits in 156 registers: large grids take
 //    12 waves (3 per SIMD, 384 rows), 10.8% less time on a 2 x 64-head,
 //    16384-row causal forward. At d = 128 a third wave per SIMD does not fit
 //    this loop (168 registers); the loop without the cross-chunk pipelining
@@ -72,7 +72,7 @@ constexpr int kBN = 64;        // keys per LDS tile
 constexpr float kSumMax = 65536.0f;   // largest partial sum of P accepted without a new reference
 
 // d = 64 and 128: 8 waves, two per SIMD (at most 256 registers each). d = 64
-// also has a 12-wave form, three per SIMD (its pipelined loop needs 152
+// also has a 12-wave form, three per SIMD (its pipelined loop needs 156
 // registers, within the 168 of three waves), for large grids (fwd_waves). d =
 // 256: a wave's Q and O alone take 192 registers, so 4 waves, one per SIMD (up
 // to 512 registers), and 128 rows per workgroup; its 3 K + 2 V tiles of 32 KiB
