@@ -386,7 +386,8 @@ constexpr int kKV_WG = 128;   // keys per workgroup
 constexpr int kKV_W = 32;     // keys per wave
 constexpr int kKV_Q = 64;     // query rows per step
 
-// The four-wave dK/dV kernel: d <= 64 (D = 64); d = 128 runs the eight-wave form.
+// The four-wave dK/dV kernel: d <= 64 (D = 64), and d = 128 on grids too small
+// for the eight-wave form (use_eight_wave).
 template <int D>
 struct KvCfg {
     static constexpr int DS = D / 16, DB = D / 32;
@@ -1259,13 +1260,14 @@ struct QCfg {
     static constexpr int DS = D / 16, DB = D / 32;
     static constexpr int SR = RowPad<D>::STRIDE;      // K, V rows: [64][D], padded rows
     static constexpr int RT = padded_tile_bytes<SR, kQ_N>();
-    // This four-wave kernel serves d <= 64 (D = 64); d = 128 runs the
-    // eight-wave form. K^T: [D][64], dense 128-byte rows, XOR-swizzled as the
-    // dK/dV kernel's transposed tiles, so that three stages (78 KiB) leave room
-    // for a second workgroup per CU (two waves per SIMD; the kernel needs at
-    // most 256 registers there).
-    static_assert(D == 64, "the four-wave dQ kernel is built for d <= 64");
-    static constexpr int TT = D * 2 * kQ_N;
+    // K^T: [D][64]. D = 64: dense 128-byte rows, XOR-swizzled as the dK/dV
+    // kernel's transposed tiles, so that three stages (78 KiB) leave room for
+    // a second workgroup per CU (two waves per SIMD; the kernel needs at most
+    // 256 registers there). D = 128 (grids too small for the eight-wave form):
+    // padded rows, which measured faster here than swizzled ones.
+    static constexpr bool TSWZ = D == 64;
+    static constexpr int ST = RowPad<kQ_N>::STRIDE;
+    static constexpr int TT = TSWZ ? D * 2 * kQ_N : padded_tile_bytes<ST, D>();
     static constexpr int KR = 0, VR = RT, KT = 2 * RT;
     static constexpr int STAGE = 2 * RT + TT;
     static constexpr int LDS = 3 * STAGE;             // tiles j-1 (K^T), j, j+1
@@ -1280,11 +1282,11 @@ struct QCfg {
     // and ends before the product that consumes it.
     static constexpr int START = 3 * DS + 1;
     using PlanR = CopyPlan<D, SR, kQ_N, 4>;
-    using PlanT = CopyPlanSwz<2 * kQ_N, D, 4>;
-    using Addr = LaneAddr<SR, Swz128>;
-    static constexpr int PER_CU = 2;                  // workgroups per CU
+    using PlanT = std::conditional_t<TSWZ, CopyPlanSwz<2 * kQ_N, D, 4>, CopyPlan<kQ_N, ST, D, 4>>;
+    using Addr = LaneAddr<SR, std::conditional_t<TSWZ, Swz128, PadRows<ST>>>;
+    static constexpr int PER_CU = TSWZ ? 2 : 1;       // workgroups per CU
     static_assert(LDS * PER_CU <= 160 * 1024, "LDS budget");
-    static_assert(KT % 128 == 0 && STAGE % 128 == 0, "swizzled tiles start on 128 bytes");
+    static_assert(!TSWZ || (KT % 128 == 0 && STAGE % 128 == 0), "swizzled tiles start on 128 bytes");
 };
 
 // First softmax task of linear slot x (x counts from the tile's slot 0 and
@@ -2518,11 +2520,28 @@ hipError_t launch_prep_t(const BwdParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// The eight-wave d = 128 gradient kernels cover 256 keys (rows) per
+// workgroup, twice the four-wave ones, and hold one workgroup per CU. Below
+// two such workgroups per compute unit the grid leaves CUs idle through the
+// causal tail, and the four-wave form (twice the workgroups) measured faster:
+// grids of 64 to 256 eight-wave workgroups ran 19-48% slower than the
+// four-wave form, while grids of 512 or more ran 3-8% faster.
+constexpr int kEightWaveMinGrid = 512;
+inline bool use_eight_wave(int grid8) { return grid8 >= kEightWaveMinGrid; }
+
 template <int D>
 hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
     const bool bounded = p.window > 0 || p.cu_seqlens;
-    if constexpr (D == 128) {   // the eight-wave form
+    if constexpr (D == 128) {   // the eight-wave form on large grids
         const int grid = p.B * p.Hkv * ((p.N + kKV8_WG - 1) / kKV8_WG);
+        if (!use_eight_wave(grid)) {
+            const int grid4 = p.B * p.Hkv * ((p.N + kKV_WG - 1) / kKV_WG);
+            if (bounded)
+                hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3(grid4), dim3(kThreads), 0, stream, p);
+            else
+                hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3(grid4), dim3(kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
         if (bounded)
             hipLaunchKernelGGL((bwd_dkdv8_kernel<D, true>), dim3(grid), dim3(kThreads8), 0, stream, p);
         else
@@ -2540,8 +2559,16 @@ hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
 template <int D>
 hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
     const bool bounded = p.window > 0 || p.cu_seqlens;
-    if constexpr (D == 128) {   // the eight-wave form
+    if constexpr (D == 128) {   // the eight-wave form on large grids
         const int grid = p.B * p.Hq * ((p.N + kQ8_WG - 1) / kQ8_WG);
+        if (!use_eight_wave(grid)) {
+            const int grid4 = p.B * p.Hq * ((p.N + kQ_WG - 1) / kQ_WG);
+            if (bounded)
+                hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(grid4), dim3(kThreads), 0, stream, p);
+            else
+                hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(grid4), dim3(kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
         if (bounded)
             hipLaunchKernelGGL((bwd_dq8_kernel<D, true>), dim3(grid), dim3(kThreads8), 0, stream, p);
         else
