@@ -82,6 +82,18 @@ def test_head_count_multiple_of_eight(fa):
     check_full(fa, inp, True, 0.0883883, "units%8==0")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv", [(8, 16, 16), (4, 32, 8), (8, 15, 15)])
+def test_d128_wave_forms(fa, B, Hq, Hkv):
+    """At d = 128 the gradient kernels come in an eight-wave form (256 keys or
+    rows per workgroup) for grids of 512 such workgroups or more and a four-wave
+    form below. N = 1000 (four 256-row blocks, ragged): 8 x 16 heads runs both
+    passes eight-wave at exactly 512 workgroups; 4 x 32 query heads over 8 K/V
+    heads runs dQ eight-wave (512) and dK/dV four-wave (128), so the row dot one
+    form writes feeds the other; 8 x 15 heads (480) runs both four-wave."""
+    inp = ai.make_case(B, Hq, Hkv, 1000, 128, seed=900 + B * Hq + Hkv)
+    check_full(fa, inp, True, 1.0 / math.sqrt(128), f"wave forms B={B} Hq={Hq} Hkv={Hkv}")
+
+
 def test_large_logits(fa):
     inp = ai.make_case(1, 4, 4, 1000, 128, seed=6, dist_scale=2.0)
     check_full(fa, inp, True, 0.2, "large logits")
