@@ -58,7 +58,8 @@
 // multiple of 128 rows with zero data, D = 0 and LSE = +inf, so no tile reads
 // past an array and padding rows carry P = 0.
 //
-// Data flow at d = 128 (eight waves per workgroup, two per SIMD):
+// Data flow at d = 128 on grids of 512 or more such workgroups (eight waves per
+// workgroup, two per SIMD; smaller grids run the four-wave form below):
 //  * dK/dV: a workgroup owns 256 keys, 32 per wave. K stays in registers as
 //    the B operand of S = Q K^T; V, the B operand of dP = dO V^T, sits in LDS
 //    (the workgroup's 256 rows), since two waves per SIMD leave each at most
@@ -77,8 +78,8 @@
 // between them and the next step's copy spread over the slots; the other wave
 // of the SIMD fills the gaps. Per MFMA a step copies half the bytes of a
 // four-wave workgroup over 128 keys or rows.
-// Data flow at d <= 64 (four waves per workgroup, one per SIMD in the
-// workgroup, two workgroups per CU):
+// Data flow at d <= 64, and at d = 128 on small grids (four waves per
+// workgroup, one per SIMD in the workgroup; two workgroups per CU at d <= 64):
 //  * dQ: a workgroup owns 128 query rows, 32 per wave, whose Q and dO rows
 //    stay in registers as MFMA operands. Tiles of 64 keys (K and V rows, K^T)
 //    stream through three LDS stages. The loop is software-pipelined across
