@@ -13,7 +13,8 @@
 //    SIMD hides only about 2 VALU instructions under each 32x32x16 MFMA; two
 //    waves per SIMD hide most of them. So a workgroup is 8 waves (2 per SIMD),
 //    each owning 32 query rows (256 rows per workgroup, at most 256 registers
-//    per wave). At d = 64 a score costs half the MFMA work for the same
+//    per wave), or at d = 128 up to 16384 rows per head and on small grids 4
+//    waves over 128 rows with two workgroups per CU (fwd_waves). At d = 64 a score costs half the MFMA work for the same
 //    softmax work, and the wave's loop fits in 156 registers: large grids take
 //    12 waves (3 per SIMD, 384 rows), 10.8% less time on a 2 x 64-head,
 //    16384-row causal forward. At d = 128 a third wave per SIMD does not fit
@@ -71,7 +72,9 @@ constexpr int kWM = 32;        // query rows per wave
 constexpr int kBN = 64;        // keys per LDS tile
 constexpr float kSumMax = 65536.0f;   // largest partial sum of P accepted without a new reference
 
-// d = 64 and 128: 8 waves, two per SIMD (at most 256 registers each). d = 64
+// d = 64 and 128: 8 waves, two per SIMD (at most 256 registers each); d = 128
+// takes 4 waves (128 rows, two workgroups per CU) up to 16384 rows per head and
+// on small grids (fwd_waves). d = 64
 // also has a 12-wave form, three per SIMD (its pipelined loop needs 156
 // registers, within the 168 of three waves), for large grids (fwd_waves). d =
 // 256: a wave's Q and O alone take 192 registers, so 4 waves, one per SIMD (up
@@ -250,10 +253,10 @@ __device__ __forceinline__ void softmax_pv(const FA_LDS uint8_t* __restrict__ Vt
 // (the chunk is the wave's last, or past it) `bulk` issues them all at once.
 // ON = false issues nothing. GUARD: the workgroup has more waves than copy
 // (FwdCfg::CW); the others skip their items.
-template <int D, bool ON, bool PAD = false, bool GUARD = false>
+template <int D, bool ON, bool PAD = false, bool GUARD = false, int W = FwdCfg<D>::WAVES>
 struct FwdCopies {
-    using PlanK = typename FwdCfg<D, PAD>::PlanK;
-    using PlanV = typename FwdCfg<D, PAD>::PlanV;
+    using PlanK = typename FwdCfg<D, PAD, W>::PlanK;
+    using PlanV = typename FwdCfg<D, PAD, W>::PlanV;
     static constexpr int NK = PlanK::NT, NI = PlanK::NT + PlanV::NT, SP = 2 * (D / 16) / NI;
     static_assert(SP >= 1, "copy items fit the steps");
     const PlanK* pk;
@@ -269,7 +272,7 @@ struct FwdCopies {
             constexpr int i = (step - 1) / SP;
             const int ws = __builtin_amdgcn_readfirstlane(w);
             if constexpr (GUARD) {
-                if (ws >= FwdCfg<D, PAD>::CW) return;
+                if (ws >= FwdCfg<D, PAD, W>::CW) return;
             }
             if constexpr (i < NK)
                 pk->copy_one(i, rk, koff, Kw, ws);
@@ -280,7 +283,7 @@ struct FwdCopies {
     __device__ __forceinline__ void bulk() const {
         if constexpr (ON) {
             if constexpr (GUARD) {
-                if (__builtin_amdgcn_readfirstlane(w) >= FwdCfg<D, PAD>::CW) return;
+                if (__builtin_amdgcn_readfirstlane(w) >= FwdCfg<D, PAD, W>::CW) return;
             }
             pk->copy(rk, koff, Kw, w);
             pv->copy(rv, voff, Vw, w);
@@ -392,14 +395,14 @@ struct Window {
 // Kc: the K tile holding this chunk; Kn: the K tile holding the next chunk;
 // Kr1: K tile j+1, which holds chunk c+2 (half H); Vt: this chunk's V tile.
 // cp carries the iteration's copies (first chunk only).
-template <int D, int H, bool CP, bool WIN, bool PAD, bool GUARD>
+template <int D, int H, bool CP, bool WIN, bool PAD, bool GUARD, int W>
 __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f32x16& sn,
                                           const FA_LDS uint8_t* __restrict__ Kc,
                                           const FA_LDS uint8_t* __restrict__ Kn,
                                           const FA_LDS uint8_t* __restrict__ Kr1,
                                           const FA_LDS uint8_t* __restrict__ Vt, int kbase, int vbase,
                                           bool causal, int qrow, int N, int lastc, float sl2, int hh,
-                                          const FwdCopies<D, CP, PAD, GUARD>& cp, const Window& wd) {
+                                          const FwdCopies<D, CP, PAD, GUARD, W>& cp, const Window& wd) {
     if (c > lastc) {
         cp.bulk();
         return;
@@ -444,10 +447,10 @@ __device__ __forceinline__ void fwd_chunk(FwdState<D>& st, int c, f32x16& sc, f3
 // __restrict__ qualifiers say so, which lets the compiler see that the LDS
 // reads do not touch the LDS the in-flight global->LDS copies write, so it does
 // not wait for those copies before each read.
-template <int D, bool WIN, bool PAD, bool GUARD>
+template <int D, bool WIN, bool PAD, bool GUARD, int W>
 __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt,
-                                              const typename FwdCfg<D, PAD>::PlanK& pk,
-                                              const typename FwdCfg<D, PAD>::PlanV& pv, BufRes rk, BufRes rv,
+                                              const typename FwdCfg<D, PAD, W>::PlanK& pk,
+                                              const typename FwdCfg<D, PAD, W>::PlanV& pv, BufRes rk, BufRes rv,
                                               FA_LDS uint8_t* __restrict__ Kw,
                                               FA_LDS uint8_t* __restrict__ Vw,
                                               const FA_LDS uint8_t* __restrict__ Kr0,
@@ -459,15 +462,15 @@ __device__ __forceinline__ void fwd_iteration(FwdState<D>& st, int j, int nt,
     // Tiles j + 1 and j + 2 may lie past the last one: their copies then read
     // past the resource (zeros) into buffers no chunk reads any more (those of
     // tiles j - 1 and j - 2).
-    const FwdCopies<D, true, PAD, GUARD> cp{&pk, &pv, rk, rv, (uint32_t)(j + 2) * kBN * dr * 2,
+    const FwdCopies<D, true, PAD, GUARD, W> cp{&pk, &pv, rk, rv, (uint32_t)(j + 2) * kBN * dr * 2,
                                             (uint32_t)(j + 1) * kBN * dr * 2, Kw, Vw, w};
     if (valid) {
         const int hh = lane >> 5;
-        fwd_chunk<D, 0, true, WIN, PAD, GUARD>(st, 2 * j, st.sA, st.sB, Kr0, Kr0, Kr1, Vr, kbase, vbase, causal,
+        fwd_chunk<D, 0, true, WIN, PAD, GUARD, W>(st, 2 * j, st.sA, st.sB, Kr0, Kr0, Kr1, Vr, kbase, vbase, causal,
                                                qrow, N, lastc, sl2, hh, cp, wd);
-        fwd_chunk<D, 1, false, WIN, PAD, GUARD>(st, 2 * j + 1, st.sB, st.sA, Kr0, Kr1, Kr1, Vr, kbase, vbase,
+        fwd_chunk<D, 1, false, WIN, PAD, GUARD, W>(st, 2 * j + 1, st.sB, st.sA, Kr0, Kr1, Kr1, Vr, kbase, vbase,
                                                 causal, qrow, N, lastc, sl2, hh,
-                                                FwdCopies<D, false, PAD, GUARD>{}, wd);
+                                                FwdCopies<D, false, PAD, GUARD, W>{}, wd);
     } else {
         cp.bulk();
     }
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(64 * W, 1) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i) st.sA[i] = fmaf(st.sA[i], sl2, -st.m);
     }
     for (int j = js; j < nt; ++j) {
-        fwd_iteration<D, WIN, PAD, GUARD>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT,
+        fwd_iteration<D, WIN, PAD, GUARD, W>(st, j, nt, pk, pv, rk, rv, Ks + ((j + 2) % 3) * C::KT,
                                    Vs + ((j + 1) & 1) * C::VT, Ks + (j % 3) * C::KT, Ks + ((j + 1) % 3) * C::KT,
                                    Vs + (j & 1) * C::VT, kbase, vbase, wave_valid, causal, qrow, N, lastc, sl2, w,
                                    lane, wd, dr);
@@ -647,7 +650,16 @@ int cu_count() {
 // CU times rows per workgroup, a 12-wave row taking 0.9 of the time.
 template <int D>
 int fwd_waves(int B, int Hq, int N) {
-    if constexpr (D != 64) {
+    if constexpr (D == 128) {
+        // 4-wave workgroups over 128 rows (two share a CU: 228-236 registers
+        // and 80 KiB of LDS each) against 8-wave ones over 256 rows, measured
+        // on MI355X: 9-17% less time on grids of fewer than two 256-row
+        // workgroups per CU, 2-3% less on larger grids up to 16384 rows per
+        // head. Longer rows on large grids keep 8 waves, which copy each K/V
+        // tile for twice the rows (2.7% faster at 65536 rows).
+        const long long g8 = (long long)B * Hq * ((N + 255) / 256);
+        return (N <= 16384 || g8 < 2 * cu_count()) ? 4 : 8;
+    } else if constexpr (D != 64) {
         return FwdCfg<D>::WAVES;
     } else {
         const long long bh = (long long)B * Hq, cu = cu_count();
@@ -678,6 +690,9 @@ hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
     if constexpr (D == 64) {
         if (fwd_waves<D>(p.B, p.Hq, p.N) == 12) return launch_fwd_w<D, 12>(p, stream);
     }
+    if constexpr (D == 128) {
+        if (fwd_waves<D>(p.B, p.Hq, p.N) == 4) return launch_fwd_w<D, 4>(p, stream);
+    }
     return launch_fwd_w<D, FwdCfg<D>::WAVES>(p, stream);
 }
 
@@ -697,6 +712,9 @@ template <int D>
 Geometry geometry_t(int B, int Hq, int N) {
     if constexpr (D == 64) {
         if (fwd_waves<D>(B, Hq, N) == 12) return geometry_w<D, 12>(B, Hq, N);
+    }
+    if constexpr (D == 128) {
+        if (fwd_waves<D>(B, Hq, N) == 4) return geometry_w<D, 4>(B, Hq, N);
     }
     return geometry_w<D, FwdCfg<D>::WAVES>(B, Hq, N);
 }

@@ -320,7 +320,9 @@ def test_bwd_varlen_checks():
 
 # (B, Hq, Hkv, N, d, waves): d <= 64 takes 12-wave (384-row) workgroups when the
 # rounds of one workgroup per CU (256 when no GPU is current) times rows per
-# workgroup, at 0.9 for a 12-wave row, come out below those of 8 waves.
+# workgroup, at 0.9 for a 12-wave row, come out below those of 8 waves. d = 128
+# takes 4-wave (128-row) workgroups up to 16384 rows per head, and beyond that
+# when 256-row ones would be fewer than two per CU.
 WAVE_CASES = [
     (2, 64, 16, 16384, 64, 12),   # 8192 vs 5504 workgroups: 32 vs 22 rounds
     (4, 16, 16, 2048, 64, 8),     # 512 vs 384: 2 rounds either way, 384-row ones take longer
@@ -328,7 +330,13 @@ WAVE_CASES = [
     (1, 64, 8, 4100, 64, 12),     # 1088 vs 704: 5 vs 3 rounds
     (1, 64, 8, 4100, 48, 12),     # a padded head dimension runs the d = 64 kernels
     (1, 32, 8, 16384, 64, 8),     # 2048 vs 1376: 8 vs 6 rounds, 8 * 256 * 10 < 6 * 384 * 9
-    (2, 32, 8, 16384, 128, 8),    # d = 128: always 8 waves
+    (2, 32, 8, 16384, 128, 4),    # d = 128: 4 waves up to 16384 rows per head
+    (1, 8, 8, 7900, 128, 4),
+    (1, 8, 8, 131072, 128, 8),    # longer rows on 4096 workgroups of 256 rows: 8 waves
+    (1, 4, 4, 65536, 128, 8),     # 1024 workgroups of 256 rows: 8 waves
+    (1, 1, 1, 65536, 128, 4),     # 256 < 2 per CU: 4 waves
+    (1, 16, 16, 1024, 128, 4),
+    (1, 16, 16, 1024, 120, 4),    # a padded head dimension runs the d = 128 kernels
     (2, 16, 4, 16384, 256, 4),    # d = 256: 4 waves
 ]
 

@@ -282,6 +282,29 @@ def test_launch_shape_does_not_change_results(fa, d):
         assert torch.equal(o_g, o[:, g * G:(g + 1) * G]) and torch.equal(lse_g, lse[:, g * G:(g + 1) * G]), g
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_d128_four_and_eight_wave_forwards_agree(fa, causal):
+    """At d = 128 the forward runs 4-wave (128-row) workgroups up to 16384 rows
+    per head and on small grids, 8-wave (256-row) ones otherwise. Both group
+    rows into the same 32-row waves and walk the same chunks, so 8 heads of
+    N = 16400 in one call (520 workgroups of 256 rows: 8 waves) and each head
+    alone (65: 4 waves) give the same bits. The small-shape tests pin the
+    4-wave form to the oracle; the long-context sample pins the 8-wave one."""
+    import torch
+    B, H, N = 1, 8, 16400
+    assert fa.fwd_geometry(B, H, H, N, 128, causal)["threads"] == 512
+    assert fa.fwd_geometry(B, 1, 1, N, 128, causal)["threads"] == 256
+    inp = ai.make_case(B, H, H, N, 128, seed=16400 + int(causal), with_grad=False)
+    say(f"fwd d=128 4- vs 8-wave causal={causal}")
+    q, k, v = to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"])
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=0.0883883)
+    for h in range(H):
+        sl = lambda t: t[:, h:h + 1].contiguous()
+        o1, lse1 = fa.fwd(sl(q), sl(k), sl(v), causal=causal, scale=0.0883883)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o[:, h:h + 1]) and torch.equal(lse1, lse[:, h:h + 1]), h
+
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_value_scale_homogeneity(fa, d):
     """O is homogeneous in V and the forward's arithmetic on V is exact scaling
